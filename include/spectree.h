@@ -1,0 +1,257 @@
+/*
+ * spectree.h - C ABI of the tree-verification step of Medusa/EAGLE-style speculative decoding,
+ * implemented as hand-written HIP kernels for AMD MI355X (gfx950).
+ *
+ * The method is described on three web pages, cited below by title and section:
+ *   [MTP]       "多トークン予測（Medusa・EAGLE）" (tech-tldr.com)
+ *   [GLOSSARY]  "Medusa（マルチヘッド投機的デコーディング）" (jisaku.com glossary)
+ *   [GUIDE]     "EAGLE-3とMedusaで実装するSpeculative Decoding実践ガイド" (qiita.com)
+ *
+ * Conventions shared by every call
+ *   - Every array argument is a DEVICE pointer unless stated otherwise, allocated and owned by
+ *     the caller, row-major with the shape given in brackets.  The library allocates no device
+ *     memory on a call path; scratch space comes in through `workspace`.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call validates its scalar
+ *     arguments on the host, enqueues its kernels on `stream` and returns without waiting.
+ *     Outputs are valid once the stream reaches the call.
+ *   - Host-checkable problems (a NULL required pointer, a size out of range, an unsupported
+ *     combination, a workspace that is too small) return a non-zero spec_status and enqueue
+ *     nothing.  A failed launch returns SPEC_EHIP.
+ *   - Problems in the DATA are found on the device and reported per sequence in an `err`
+ *     array of error words: 0 = fine, otherwise (node << 8) | code with the codes below.  When
+ *     a sequence has several problems the smallest word is reported (lowest node index, then
+ *     lowest code); sequence-level problems (node count, prefix length) take node 0 and are
+ *     checked first.  A sequence with an error gets the documented neutral outputs.
+ *   - Workspaces: query the size with the matching *_workspace() function.  A workspace must
+ *     be zero-filled before its first use; every call leaves it zero-filled again in the
+ *     regions it uses for cross-workgroup counters, so one workspace can be reused by
+ *     back-to-back calls on one stream.  Calls that run concurrently need distinct workspaces.
+ *   - Limits: N (tree nodes per sequence, padding included) <= 256.
+ */
+#ifndef SPECTREE_H
+#define SPECTREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_EINVAL = 1,        /* bad argument: NULL required pointer, size out of range     */
+  SPEC_EUNSUPPORTED = 2,  /* well-formed but unsupported: head_dim, dtype, group size   */
+  SPEC_EWORKSPACE = 3,    /* workspace NULL or smaller than the *_workspace() size      */
+  SPEC_EHIP = 4           /* a HIP runtime call or a kernel launch failed               */
+} spec_status;
+
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
+
+typedef enum {
+  SPEC_VERIFY_GREEDY = 0,   /* temperature 0: accept iff the token is the argmax          */
+  SPEC_VERIFY_TYPICAL = 1,  /* accept iff T[x] >= min(eps, delta * exp(-entropy(T)))     */
+  SPEC_VERIFY_REJECT = 2    /* accept with probability min(1, T[x] / D[x])               */
+} spec_mode;
+
+/* Per-sequence data error codes (low byte of an error word). */
+enum {
+  SPEC_ERR_ROOT = 1,       /* node 0 must have parent -1                                  */
+  SPEC_ERR_PARENT = 2,     /* node i >= 1 must have a parent in [0, i)                    */
+  SPEC_ERR_DEPTH = 3,      /* given depth disagrees with the tree, or exceeds max_depth   */
+  SPEC_ERR_NNODES = 4,     /* n_nodes[b] outside [0, N]                                   */
+  SPEC_ERR_PREFIX = 5,     /* prefix_len[b] < 0, or prefix_len[b] + n_nodes[b] > S_max     */
+  SPEC_ERR_TOKEN = 6,      /* candidate token outside [0, V)                              */
+  SPEC_ERR_DRAFTROW = 7,   /* draft_row outside [0, R)                                    */
+  SPEC_ERR_NONFINITE = 8,  /* a target-logits row that is read holds a NaN or an infinity */
+  SPEC_ERR_MAP = 9,        /* t2d entry outside [-1, Vd)                                  */
+  SPEC_ERR_RANK = 10       /* assembly: node deeper than the heads, or sibling rank >= k  */
+};
+
+#define SPEC_MAX_NODES 256
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* spec_strerror(spec_status s);
+
+/* --------------------------------------------------------------------------------------
+ * spec_tree_build - ancestor mask, depths and positions of a batch of candidate trees.
+ *
+ * [MTP] section "ツリー検証：候補を「木」に束ねて1回で確かめる" and [GUIDE] section
+ * "Tree Attention：候補を木構造で探索する": each tree node may attend only to its ancestors,
+ * which lets every candidate path share one forward pass.  [GLOSSARY] section
+ * "デプロイと運用上の考慮事項": batched requests carry their own trees, hence padding + masks.
+ *
+ *   parents    int32 [B, N]  parent of node i; node 0 is the root (parent -1); a valid tree
+ *                            is numbered topologically: parents[i] in [0, i) for i >= 1
+ *   depths_in  int32 [B, N]  optional (NULL): depths to validate (SPEC_ERR_DEPTH on mismatch)
+ *   prefix_len int32 [B]     optional (NULL = 0): committed prefix length P_b
+ *   n_nodes    int32 [B]     optional (NULL = N): valid nodes; rows >= n_nodes are padding
+ * Outputs:
+ *   mask       uint64 [B, N, W], W = ceil(N / 64): bit (j % 64) of word j / 64 of row i is set
+ *                            iff node j is an ancestor of node i or j == i
+ *   positions  int32 [B, N]  P_b + depth(i): the rotary position of node i (its KV cache slot
+ *                            is P_b + i)
+ *   depths     int32 [B, N]  number of proper ancestors
+ *   err        int32 [B]     error word
+ * Padding rows, and all rows of a sequence with an error, get mask 0, depth -1, position -1.
+ * Errors: SPEC_EINVAL if B < 1, N < 1, N > 256 or a required pointer is NULL.
+ * ------------------------------------------------------------------------------------ */
+spec_status spec_tree_build(const int32_t* parents, const int32_t* depths_in,
+                            const int32_t* prefix_len, const int32_t* n_nodes, int B, int N,
+                            uint64_t* mask, int32_t* positions, int32_t* depths, int32_t* err,
+                            void* stream);
+
+/* --------------------------------------------------------------------------------------
+ * spec_tree_assemble - candidate tokens of a predefined tree topology from per-head top-k.
+ *
+ * [GLOSSARY] section "ツリー構造の候補構築": the candidate tree combines the top candidates
+ * of each head on a predefined topology ("Medusa Tree"); e.g. top-3 x top-3 x top-2 gives
+ * 18 paths.  The r-th child (counted from 0 in node order) of a node at depth t takes the
+ * rank-r candidate of head t:  tokens[b, i] = topk_idx[b, depth(i) - 1, rank(i)].
+ *
+ *   topk_idx    int32 [B, H, k]  per-head candidates, best first (spec_medusa_heads output)
+ *   parents     int32 [N]        topology shared by the batch (same rules as above)
+ *   root_tokens int32 [B]        optional (NULL): token of the root (else -1)
+ * Outputs:
+ *   tokens      int32 [B, N]     candidate token of each node
+ *   draft_row   int32 [B, N]     depth(i) - 1: the head (draft row) that proposed node i;
+ *                                -1 for the root
+ *   err         int32 [B]        error word (the same for every b: the topology is shared);
+ *                                on error tokens and draft_row are -1
+ * Errors: SPEC_EINVAL if B, N, H, k < 1, N > 256 or a required pointer is NULL.
+ * ------------------------------------------------------------------------------------ */
+spec_status spec_tree_assemble(const int32_t* topk_idx, const int32_t* parents,
+                               const int32_t* root_tokens, int B, int N, int H, int k,
+                               int32_t* tokens, int32_t* draft_row, int32_t* err, void* stream);
+
+/* --------------------------------------------------------------------------------------
+ * spec_tree_attn - tree attention: every node's query attends to the shared committed prefix
+ * and to its own ancestors (and itself) under the ancestor mask.
+ *
+ * [MTP] section "ツリー検証：候補を「木」に束ねて1回で確かめる"; [GUIDE] sections
+ * "並列検証：ターゲットモデルの1回のforward passで一括確認する" (the KV cache lets all
+ * positions be scored in one pass) and "Tree Attention：候補を木構造で探索する".
+ *
+ *   q          [B, N, Hq, head_dim]        dtype; rotary embedding already applied
+ *   k_cache    [B, Hkv, S_max, head_dim]   dtype; slots [0, P_b) hold the prefix, slot P_b + j
+ *   v_cache    [B, Hkv, S_max, head_dim]   holds tree node j (written by the caller)
+ *   prefix_len int32 [B]                   P_b
+ *   tree_mask  uint64 [B, N, ceil(N/64)]   spec_tree_build's mask
+ *   n_nodes    int32 [B]                   optional (NULL = N)
+ *   scale      softmax scale (1/sqrt(head_dim) for standard attention)
+ *   dtype      SPEC_F32 (exact fp32 path) or SPEC_BF16 (MFMA path, fp32 accumulation)
+ * Outputs:
+ *   out        [B, N, Hq, head_dim] dtype: softmax(scale q.k) v over the visible slots;
+ *              query head h reads key/value head h / (Hq / Hkv)
+ *   lse        float [B, N, Hq]     optional (NULL): natural-log sum of exp(scale q.k) over the
+ *              visible slots (-inf for a row that sees nothing)
+ *   err        int32 [B]            optional (NULL): SPEC_ERR_NNODES / SPEC_ERR_PREFIX
+ * Rows of padding nodes, rows that see no slot and all rows of a sequence with an error are 0.
+ * Supported: head_dim 64 or 128; Hq % Hkv == 0; N <= 256.
+ * Errors: SPEC_EINVAL (sizes, NULL pointers), SPEC_EUNSUPPORTED (head_dim, dtype),
+ * SPEC_EWORKSPACE.
+ * ------------------------------------------------------------------------------------ */
+size_t spec_tree_attn_workspace(int B, int N, int Hq, int Hkv, int head_dim, int S_max,
+                                spec_dtype dtype);
+spec_status spec_tree_attn(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* prefix_len, const uint64_t* tree_mask,
+                           const int32_t* n_nodes, int B, int N, int Hq, int Hkv, int head_dim,
+                           int S_max, float scale, spec_dtype dtype, void* out, float* lse,
+                           int32_t* err, void* workspace, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------------------------------
+ * spec_verify - per-node acceptance, longest accepted root-to-node path and bonus token.
+ *
+ * [GUIDE] section "棄却サンプリング：出力品質を保証する": accept a drafted token x with
+ * probability min(1, T[x]/D[x]); on a rejection draw from norm(relu(T - D)); candidates after
+ * a rejection are dropped.  [GLOSSARY] section "Medusa-1とMedusa-2の違い": typical
+ * acceptance keeps x when T[x] reaches an entropy-based threshold.  [MTP] section
+ * "ツリー検証：候補を「木」に束ねて1回で確かめる": the path that passes the longest is kept.
+ *
+ * Row p of target_logits is the target model's logits at node p; T_p = softmax(row p) is the
+ * distribution of p's children.  Node c (parent p, token x = tokens[b, c]) is tested on T_p:
+ *   GREEDY   accept iff x == argmax T_p (lowest id on ties)
+ *   TYPICAL  accept iff T_p[x] >= min(eps, delta * exp(-H_p)), H_p the entropy of T_p in nats
+ *            (delta = +inf gives the fixed threshold eps)
+ *   REJECT   accept iff uniforms[b, c] * D[x] < T_p[x], D = draft_probs[b, draft_row[b, c]]
+ *            seen on the target vocabulary through t2d
+ * A node survives iff it and all its ancestors below the root were accepted.  m = the deepest
+ * survivor (lowest index on ties); accept_len = depth(m); path = root .. m.  Bonus token, drawn
+ * with uniforms[b, 0] by inverse CDF (smallest t whose running sum from token 0 exceeds u * Z):
+ *   GREEDY   argmax T_m
+ *   TYPICAL  a draw from T_m
+ *   REJECT   if m has children: a draw from norm(relu(T_m - D)), D the draft row of m's
+ *            lowest-index child (T_m if that residual is all zero); else a draw from T_m.
+ *
+ *   target_logits float [B, N, V]
+ *   draft_probs   float [B, R, Vd]  draft distributions (REJECT only; else may be NULL)
+ *   draft_row     int32 [B, N]      row of draft_probs that proposed node c (REJECT only)
+ *   t2d           int32 [V]         optional (NULL: identity, requires Vd == V): target id ->
+ *                                   draft id, -1 where the draft vocabulary lacks the token
+ *   tokens        int32 [B, N]      candidate token of each node (node 0's is ignored)
+ *   parents       int32 [B, N]      tree (rules as in spec_tree_build)
+ *   n_nodes       int32 [B]         optional (NULL = N)
+ *   uniforms      float [B, N]      U[0, 1) draws: column 0 for the bonus, column c for node c
+ *   max_depth     length of path minus one; a valid node deeper than this is SPEC_ERR_DEPTH
+ * Outputs:
+ *   accept_len  int32 [B]; path int32 [B, max_depth + 1] (-1 padded); bonus_token int32 [B];
+ *   node_accept uint8 [B, N] optional (NULL): per-node test result (root 1, padding 0);
+ *   err         int32 [B].
+ * A sequence with n_nodes 0, or with an error, gets accept_len 0, path all -1, bonus -1 and
+ * node_accept all 0.
+ * Errors: SPEC_EINVAL (sizes, NULL pointers, REJECT without draft arrays, t2d NULL with
+ * Vd != V), SPEC_EWORKSPACE.
+ * ------------------------------------------------------------------------------------ */
+size_t spec_verify_workspace(int B, int N, int V);
+spec_status spec_verify(const float* target_logits, const float* draft_probs,
+                        const int32_t* draft_row, const int32_t* t2d, const int32_t* tokens,
+                        const int32_t* parents, const int32_t* n_nodes, const float* uniforms,
+                        int B, int N, int V, int R, int Vd, int max_depth, spec_mode mode,
+                        float eps, float delta, int32_t* accept_len, int32_t* path,
+                        int32_t* bonus_token, uint8_t* node_accept, int32_t* err,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------------------------------
+ * spec_medusa_heads - Medusa heads on the last hidden state, shared LM head, per-head top-k.
+ *
+ * [MTP] section "Medusa：本体に複数の予測ヘッドを足す" (several light heads on the same h_t,
+ * all in one forward pass); [GUIDE] section "アーキテクチャ：複数ヘッドによる並列トークン予測"
+ * (each head: one feed-forward layer with a residual connection); [GLOSSARY] section
+ * "Medusaの基本アーキテクチャ" (heads emit vocabulary distributions whose top candidates
+ * build the tree).
+ *
+ *   z_j       = h + SiLU(W_res[j] h)      (no bias; W_res[j] stored [out, in]); kept in fp32
+ *   logits_j  = W_lm z_j                  (the shared LM head, fp32 accumulation)
+ *   D_j       = softmax(logits_j)
+ *
+ *   h        bf16 [B, Dm];  W_res bf16 [H, Dm, Dm];  W_lm bf16 [V, Dm]
+ * Outputs:
+ *   topk_idx    int32 [B, H, k]  the k largest logits of head j, descending, lower id on ties
+ *   topk_prob   float [B, H, k]  D_j at those ids
+ *   draft_probs float [B, H, V]  optional (NULL): D_j
+ * Supported: B <= 16, Dm % 256 == 0, 1 <= k <= 64, k <= V.
+ * Errors: SPEC_EINVAL, SPEC_EUNSUPPORTED, SPEC_EWORKSPACE.
+ * ------------------------------------------------------------------------------------ */
+size_t spec_medusa_heads_workspace(int B, int H, int Dm, int V, int k);
+spec_status spec_medusa_heads(const void* h, const void* W_res, const void* W_lm, int B, int H,
+                              int Dm, int V, int k, int32_t* topk_idx, float* topk_prob,
+                              float* draft_probs, void* workspace, size_t ws_bytes,
+                              void* stream);
+
+/* --------------------------------------------------------------------------------------
+ * Kernel timing.  When enabled, the library brackets each of its kernel launches with a pair
+ * of HIP events recorded on the launch stream, and accumulates the elapsed time per kernel
+ * name.  spec_prof_read() waits for the recorded events.  Host-side bookkeeping only; it
+ * changes nothing in what the kernels compute.
+ * ------------------------------------------------------------------------------------ */
+void spec_prof_enable(int on);
+void spec_prof_reset(void);
+/* Total milliseconds and launch count recorded for kernel `name` since the last reset.
+ * Returns 0 on success, -1 if the name was never launched while enabled. */
+int spec_prof_read(const char* name, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECTREE_H */

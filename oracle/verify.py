@@ -36,7 +36,9 @@ Readings taken where the pages are silent or loose:
     sum of q from token 0 upward exceeds u * Z, Z the total sum, both accumulated in float64
     in ascending token order.
   * Draft rows may live on a smaller draft vocabulary: t2d[x] maps target token x to a
-    draft index, -1 for tokens the draft cannot emit (their draft probability is 0).
+    draft index, -1 for tokens the draft cannot emit (their draft probability is 0).  A
+    candidate whose entry lies outside [-1, Vd) is an error; any other such entry is read
+    as -1.
 """
 
 import numpy as np
@@ -89,7 +91,7 @@ def _draft_on_target_vocab(draft_row_probs, t2d, V):
         return d[:V].copy()
     out = np.zeros(V, dtype=np.float64)
     for v in range(V):
-        if t2d[v] >= 0:
+        if 0 <= t2d[v] < len(d):
             out[v] = d[t2d[v]]
     return out
 

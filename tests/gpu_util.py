@@ -1,0 +1,70 @@
+"""Helpers shared by the GPU parity tests (marshalling NumPy inputs to device tensors and the
+comparison rules).  Expected values always come from ``oracle``; nothing here computes them."""
+
+import numpy as np
+import pytest
+import torch
+
+from tree_attention_verification_spec_amd import binding
+
+# Decisions whose distance from the boundary is below these are counted, not compared:
+# |u - min(1, T/D)| or |ln T - ln tau| for node tests, |u Z - C| / Z for the fp64 bonus draw.
+NODE_MARGIN = 1e-4
+BONUS_MARGIN = 1e-12
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.lib()   # raises if the library is missing: no fallback
+
+
+def dev(x, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def mask_words_np(t):
+    """Device int64 mask -> uint64 NumPy (same bits)."""
+    return host(t).view(np.uint64)
+
+
+def assert_attn_close(got, ref, dtype, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    err = float(np.abs(got - ref).max()) if ref.size else 0.0
+    if dtype == "f32":
+        assert err <= 1e-5 * max(scale, 1e-30), f"{what}: max err {err:.3e} vs 1e-5 * {scale:.3e}"
+    else:
+        assert err <= 2e-2, f"{what}: max err {err:.3e} > 2e-2"
+        assert err <= 2e-2 * max(scale, 1e-30), f"{what}: max err {err:.3e} vs 2e-2 * {scale:.3e}"
+    return err, scale
+
+
+def compare_verify(got, ref, n_nodes, node_margin=NODE_MARGIN, bonus_margin=BONUS_MARGIN,
+                   max_excused_frac=0.1):
+    """Bit-exact comparison per sequence, except sequences holding a decision within the
+    margins, which are counted separately.  Returns the number of excused sequences."""
+    B = len(ref["accept_len"])
+    excused = 0
+    for b in range(B):
+        n = int(n_nodes[b])
+        m_node = ref["margin"][b, 1:max(n, 1)]
+        near = (m_node.size and np.nanmin(m_node) < node_margin) or ref["bonus_margin"][b] < bonus_margin
+        if near and ref["err"][b] == 0:
+            excused += 1
+            continue
+        for key in ("err", "accept_len", "bonus"):
+            assert int(got[key][b]) == int(ref[key][b]), (key, b, got[key][b], ref[key][b])
+        assert np.array_equal(got["path"][b], ref["path"][b]), ("path", b, got["path"][b], ref["path"][b])
+        assert np.array_equal(got["node_accept"][b], ref["node_accept"][b]), ("node_accept", b)
+    assert excused <= max(1, int(max_excused_frac * B)), f"too many excused sequences: {excused}/{B}"
+    return excused

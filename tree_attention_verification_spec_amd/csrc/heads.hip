@@ -1,0 +1,272 @@
+// Medusa heads: z_j = h + SiLU(W_res[j] h), logits_j = W_lm z_j (shared LM head),
+// D_j = softmax(logits_j), per-head top-k.
+//
+// "多トークン予測（Medusa・EAGLE）", section "Medusa：本体に複数の予測ヘッドを足す" (light heads on
+// the same final hidden state, all in one pass); "EAGLE-3とMedusaで実装するSpeculative Decoding
+// 実践ガイド", section "アーキテクチャ：複数ヘッドによる並列トークン予測" (one feed-forward layer
+// plus a residual per head); "Medusa（マルチヘッド投機的デコーディング）", sections
+// "Medusaの基本アーキテクチャ" and "ツリー構造の候補構築" (the heads' top candidates build the
+// tree).
+//
+// Both products have a handful of columns (the batch, or batch x heads) against megabytes of
+// weights, so they are weight-streaming: each weight element is read from HBM once.  They run
+// on v_mfma_f32_16x16x32_bf16 with the weight rows as the M dimension (A operand, 16-byte loads
+// straight from HBM) and the few activation columns as N (B operand, L2-resident).  The K
+// dimension is split over the four waves of a workgroup and the partial tiles are summed in
+// LDS, so a workgroup keeps four independent load streams in flight.
+//
+// z stays fp32 (no rounding back to bf16 before the LM head).  The LM head consumes it as an
+// exact three-term bf16 split z = hi + mid + lo; each W_lm fragment is multiplied with the
+// three parts into one fp32 accumulator, which costs MFMA issue slots but no extra HBM bytes.
+#include <climits>
+
+#include "common.h"
+
+namespace spectree {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kKWaves = 4;       // K slices per workgroup
+constexpr int kLmRowBlocks = 4;  // 16-row blocks of W_lm per wave
+constexpr int kMaxCols = 64;     // B * H limit of the LM head
+
+__device__ __forceinline__ bf16x8 load8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// grid: H * Dm / 16 workgroups; workgroup = 16 output rows of one head, K split over 4 waves.
+__global__ __launch_bounds__(kThreads) void resblock_kernel(const __bf16* __restrict__ h,
+                                                            const __bf16* __restrict__ W, int B, int H,
+                                                            int Dm, __bf16* __restrict__ zsplit) {
+  __shared__ f32x4 red[kKWaves][kWave];
+  const int rows_per_head = Dm / 16;
+  const int j = blockIdx.x / rows_per_head;
+  const int row0 = (blockIdx.x - j * rows_per_head) * 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int kslice = Dm / kKWaves;
+  const int kbeg = wave * kslice;
+  const __bf16* arow = W + ((size_t)j * Dm + row0 + l16) * Dm + kbeg + 8 * lg;
+  const bool col_ok = l16 < B;
+  const __bf16* bcol = h + (size_t)(col_ok ? l16 : 0) * Dm + kbeg + 8 * lg;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int steps = kslice / 32;
+#pragma unroll 8
+  for (int s = 0; s < steps; ++s) {
+    const bf16x8 af = load8(arow + s * 32);
+    const bf16x8 bf = col_ok ? load8(bcol + s * 32) : bf16x8{};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc, 0, 0, 0);
+  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  acc = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
+  if (!col_ok) return;
+  const int b = l16;
+  const int NC = B * H;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int row = row0 + 4 * lg + e;           // output feature
+    const float a = acc[e];
+    const float z = (float)h[(size_t)b * Dm + row] + a / (1.f + expf(-a));
+    const __bf16 hi = (__bf16)z;
+    const float r1 = z - (float)hi;
+    const __bf16 mid = (__bf16)r1;
+    const __bf16 lo = (__bf16)(r1 - (float)mid);
+    const size_t col = (size_t)b * H + j;
+    zsplit[(0 * (size_t)NC + col) * Dm + row] = hi;
+    zsplit[(1 * (size_t)NC + col) * Dm + row] = mid;
+    zsplit[(2 * (size_t)NC + col) * Dm + row] = lo;
+  }
+}
+
+// grid: ceil(V / 64) workgroups; workgroup = 64 rows of W_lm (4 blocks of 16 per wave), K split
+// over the 4 waves.  logits[col, v], col = b * H + j.
+template <int CBN>
+__global__ __launch_bounds__(kThreads) void lm_head_kernel(const __bf16* __restrict__ W_lm,
+                                                           const __bf16* __restrict__ zsplit, int NC, int Dm,
+                                                           int V, float* __restrict__ logits) {
+  __shared__ f32x4 red[kKWaves][kLmRowBlocks * CBN][kWave];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int row0 = blockIdx.x * 16 * kLmRowBlocks;
+  const int kslice = Dm / kKWaves;
+  const int kbeg = wave * kslice;
+  const __bf16* arow[kLmRowBlocks];
+  bool row_ok[kLmRowBlocks];
+#pragma unroll
+  for (int rb = 0; rb < kLmRowBlocks; ++rb) {
+    const int r = row0 + rb * 16 + l16;
+    row_ok[rb] = r < V;
+    arow[rb] = W_lm + (size_t)(row_ok[rb] ? r : 0) * Dm + kbeg + 8 * lg;
+  }
+  const __bf16* bptr[3][CBN];
+  bool col_ok[CBN];
+#pragma unroll
+  for (int cb = 0; cb < CBN; ++cb) {
+    const int col = cb * 16 + l16;
+    col_ok[cb] = col < NC;
+#pragma unroll
+    for (int sp = 0; sp < 3; ++sp)
+      bptr[sp][cb] = zsplit + ((size_t)sp * NC + (col_ok[cb] ? col : 0)) * Dm + kbeg + 8 * lg;
+  }
+  f32x4 acc[kLmRowBlocks][CBN];
+#pragma unroll
+  for (int rb = 0; rb < kLmRowBlocks; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CBN; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int steps = kslice / 32;
+#pragma unroll 2
+  for (int s = 0; s < steps; ++s) {
+    bf16x8 af[kLmRowBlocks];
+#pragma unroll
+    for (int rb = 0; rb < kLmRowBlocks; ++rb) af[rb] = row_ok[rb] ? load8(arow[rb] + s * 32) : bf16x8{};
+#pragma unroll
+    for (int cb = 0; cb < CBN; ++cb) {
+#pragma unroll
+      for (int sp = 0; sp < 3; ++sp) {
+        const bf16x8 bf = col_ok[cb] ? load8(bptr[sp][cb] + s * 32) : bf16x8{};
+#pragma unroll
+        for (int rb = 0; rb < kLmRowBlocks; ++rb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rb], bf, acc[rb][cb], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < kLmRowBlocks; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CBN; ++cb) red[wave][rb * CBN + cb][lane] = acc[rb][cb];
+  __syncthreads();
+  // Every wave finishes a quarter of the tiles.
+  for (int t = wave; t < kLmRowBlocks * CBN; t += kKWaves) {
+    const f32x4 sum = red[0][t][lane] + red[1][t][lane] + red[2][t][lane] + red[3][t][lane];
+    const int rb = t / CBN, cb = t % CBN;
+    const int col = cb * 16 + l16;
+    if (col >= NC) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = row0 + rb * 16 + 4 * lg + e;
+      if (r < V) logits[(size_t)col * V + r] = sum[e];
+    }
+  }
+}
+
+// One workgroup per column (b, j): softmax and top-k (descending, lower id first on ties).
+__global__ __launch_bounds__(kThreads) void softmax_topk_kernel(const float* __restrict__ logits, int H, int V,
+                                                                int k, int32_t* __restrict__ topk_idx,
+                                                                float* __restrict__ topk_prob,
+                                                                float* __restrict__ probs) {
+  __shared__ float s_f[kThreads / kWave];
+  __shared__ int s_i[kThreads / kWave];
+  const int col = blockIdx.x;
+  const float* row = logits + (size_t)col * V;
+  const int w = threadIdx.x >> 6;
+  // max
+  float m = -INFINITY;
+  for (int v = threadIdx.x; v < V; v += kThreads) m = fmaxf(m, row[v]);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) s_f[w] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(s_f[0], s_f[1]), fmaxf(s_f[2], s_f[3]));
+  __syncthreads();
+  // normaliser
+  float s = 0.f;
+  for (int v = threadIdx.x; v < V; v += kThreads) s += expf(row[v] - m);
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) s_f[w] = s;
+  __syncthreads();
+  const float S = s_f[0] + s_f[1] + s_f[2] + s_f[3];
+  const float invS = 1.f / S;
+  __syncthreads();
+  if (probs)
+    for (int v = threadIdx.x; v < V; v += kThreads) probs[(size_t)col * V + v] = expf(row[v] - m) * invS;
+  // top-k by repeated selection below the previous pick in (value desc, id asc) order
+  float prev_v = INFINITY;
+  int prev_i = -1;
+  for (int t = 0; t < k; ++t) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    for (int v = threadIdx.x; v < V; v += kThreads) {
+      const float x = row[v];
+      const bool below = x < prev_v || (x == prev_v && v > prev_i);
+      if (below && (x > bv || (x == bv && v < bi))) { bv = x; bi = v; }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      const float v2 = __shfl_xor(bv, o);
+      const int i2 = __shfl_xor(bi, o);
+      if (v2 > bv || (v2 == bv && i2 < bi)) { bv = v2; bi = i2; }
+    }
+    if ((threadIdx.x & 63) == 0) { s_f[w] = bv; s_i[w] = bi; }
+    __syncthreads();
+    bv = s_f[0]; bi = s_i[0];
+    for (int q = 1; q < kThreads / kWave; ++q)
+      if (s_f[q] > bv || (s_f[q] == bv && s_i[q] < bi)) { bv = s_f[q]; bi = s_i[q]; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      topk_idx[(size_t)col * k + t] = bi;
+      topk_prob[(size_t)col * k + t] = expf(bv - m) * invS;
+    }
+    prev_v = bv;
+    prev_i = bi;
+  }
+}
+
+struct HeadsLayout {
+  size_t zsplit, logits, total;
+};
+
+HeadsLayout heads_layout(int B, int H, int Dm, int V) {
+  HeadsLayout L{};
+  const size_t NC = (size_t)B * H;
+  size_t off = 0;
+  L.zsplit = off; off += align_up(3 * NC * Dm * sizeof(__bf16), 256);
+  L.logits = off; off += align_up(NC * V * sizeof(float), 256);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+}  // namespace spectree
+
+using namespace spectree;
+
+extern "C" size_t spec_medusa_heads_workspace(int B, int H, int Dm, int V, int k) {
+  if (B < 1 || H < 1 || Dm < 1 || V < 1 || k < 1) return 0;
+  return heads_layout(B, H, Dm, V).total;
+}
+
+extern "C" spec_status spec_medusa_heads(const void* h, const void* W_res, const void* W_lm, int B, int H,
+                                         int Dm, int V, int k, int32_t* topk_idx, float* topk_prob,
+                                         float* draft_probs, void* workspace, size_t ws_bytes,
+                                         void* stream) {
+  if (B < 1 || H < 1 || Dm < 1 || V < 1 || k < 1) return SPEC_EINVAL;
+  if (!h || !W_res || !W_lm || !topk_idx || !topk_prob) return SPEC_EINVAL;
+  if (B > 16 || B * H > kMaxCols || Dm % 128 != 0 || k > 64 || k > V) return SPEC_EUNSUPPORTED;
+  const HeadsLayout L = heads_layout(B, H, Dm, V);
+  if (!workspace || ws_bytes < L.total) return SPEC_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(workspace);
+  __bf16* zsplit = reinterpret_cast<__bf16*>(w + L.zsplit);
+  float* logits = reinterpret_cast<float*>(w + L.logits);
+  const int NC = B * H;
+  {
+    ProfScope prof("medusa_resblock", s);
+    resblock_kernel<<<H * (Dm / 16), kThreads, 0, s>>>(static_cast<const __bf16*>(h),
+                                                       static_cast<const __bf16*>(W_res), B, H, Dm, zsplit);
+    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+  }
+  {
+    ProfScope prof("medusa_lm_head", s);
+    const int grid = (V + 16 * kLmRowBlocks - 1) / (16 * kLmRowBlocks);
+    const __bf16* wl = static_cast<const __bf16*>(W_lm);
+    const int cbn = (NC + 15) / 16;
+    if (cbn == 1) lm_head_kernel<1><<<grid, kThreads, 0, s>>>(wl, zsplit, NC, Dm, V, logits);
+    else if (cbn == 2) lm_head_kernel<2><<<grid, kThreads, 0, s>>>(wl, zsplit, NC, Dm, V, logits);
+    else if (cbn == 3) lm_head_kernel<3><<<grid, kThreads, 0, s>>>(wl, zsplit, NC, Dm, V, logits);
+    else lm_head_kernel<4><<<grid, kThreads, 0, s>>>(wl, zsplit, NC, Dm, V, logits);
+    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+  }
+  {
+    ProfScope prof("medusa_softmax_topk", s);
+    softmax_topk_kernel<<<NC, kThreads, 0, s>>>(logits, H, V, k, topk_idx, topk_prob, draft_probs);
+  }
+  return launch_status();
+}

@@ -1,0 +1,93 @@
+// Status strings and per-kernel event timing for libspectree.
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "common.h"
+
+extern "C" const char* spec_strerror(spec_status s) {
+  switch (s) {
+    case SPEC_OK: return "ok";
+    case SPEC_EINVAL: return "invalid argument";
+    case SPEC_EUNSUPPORTED: return "unsupported configuration";
+    case SPEC_EWORKSPACE: return "workspace missing or too small";
+    case SPEC_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+namespace spectree {
+namespace {
+
+struct Record {
+  std::string name;
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+
+std::mutex g_mu;
+bool g_enabled = false;
+std::vector<Record> g_records;
+
+}  // namespace
+
+int prof_begin(const char* name, hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!g_enabled) return -1;
+  Record r{name, nullptr, nullptr};
+  if (hipEventCreate(&r.start) != hipSuccess) return -1;
+  if (hipEventCreate(&r.stop) != hipSuccess) {
+    (void)hipEventDestroy(r.start);
+    return -1;
+  }
+  if (hipEventRecord(r.start, stream) != hipSuccess) {
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+    return -1;
+  }
+  g_records.push_back(r);
+  return static_cast<int>(g_records.size()) - 1;
+}
+
+void prof_end(int token, hipStream_t stream) {
+  if (token < 0) return;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (token < static_cast<int>(g_records.size())) (void)hipEventRecord(g_records[token].stop, stream);
+}
+
+}  // namespace spectree
+
+extern "C" void spec_prof_enable(int on) {
+  std::lock_guard<std::mutex> lock(spectree::g_mu);
+  spectree::g_enabled = on != 0;
+}
+
+extern "C" void spec_prof_reset(void) {
+  std::lock_guard<std::mutex> lock(spectree::g_mu);
+  for (auto& r : spectree::g_records) {
+    (void)hipEventSynchronize(r.stop);
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  spectree::g_records.clear();
+}
+
+extern "C" int spec_prof_read(const char* name, double* total_ms, int64_t* launches) {
+  std::lock_guard<std::mutex> lock(spectree::g_mu);
+  double total = 0.0;
+  int64_t n = 0;
+  for (auto& r : spectree::g_records) {
+    if (r.name != name) continue;
+    if (hipEventSynchronize(r.stop) != hipSuccess) continue;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) == hipSuccess) {
+      total += ms;
+      ++n;
+    }
+  }
+  if (total_ms) *total_ms = total;
+  if (launches) *launches = n;
+  return n > 0 ? 0 : -1;
+}

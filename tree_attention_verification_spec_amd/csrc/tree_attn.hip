@@ -1,0 +1,552 @@
+// Tree attention: every tree node's query attends to the shared committed prefix and to its
+// own ancestors only ("多トークン予測（Medusa・EAGLE）", section
+// "ツリー検証：候補を「木」に束ねて1回で確かめる"; "EAGLE-3とMedusaで実装するSpeculative
+// Decoding実践ガイド", sections "並列検証：ターゲットモデルの1回のforward passで一括確認する"
+// and "Tree Attention：候補を木構造で探索する").
+//
+// bf16 path (MFMA, gfx950).  A work unit is one (sequence b, key/value head g).  Its query rows
+// are the N tree nodes x the G query heads that share g, M = N * G rows, row r = node r / G,
+// head g * G + r % G.  All of them read the same keys, so each key/value tile is fetched from
+// HBM once per workgroup, staged in LDS and reused by every row of the workgroup.
+//
+// Each wave owns 16 * CB query rows.  Scores are computed transposed, S^T = K Q^T, with
+// v_mfma_f32_16x16x32_bf16: A = a 16-key x 32-dim slice of K from LDS, B = Q^T held in
+// registers for the whole kernel.  The accumulator layout gives lane l the query row l % 16
+// and keys 4 * (l / 16) + i, which is exactly the B-operand layout of the next product
+// O^T = V^T P^T, so the softmax weights never leave their lanes; V is written transposed into
+// LDS so its A-operand fragments are contiguous.  Every per-row quantity (running max, sum,
+// rescale factor) lives in the lanes of that row, with a two-step xor shuffle for the max.
+//
+// Work split: grid = units x row blocks x key splits.  A split covers a contiguous key range
+// of the unit (prefix and tree slots alike), computed on the device from prefix_len and
+// n_nodes.  With more than one split, each workgroup stores its unnormalised partial output
+// and (max, sum) to the workspace; the last workgroup of a (unit, row block) to arrive - found
+// with a device-scope counter - merges them and resets the counter.  Workgroups of one unit
+// are placed on one XCD (dispatch goes round-robin over the 8 XCDs), so the unit's K/V tiles,
+// Q rows and partials share that XCD's L2.
+//
+// fp32 path: a plain exact-fp32 kernel (one workgroup per query row) for small fp32 inputs.
+#include <climits>
+
+#include "common.h"
+
+namespace spectree {
+namespace {
+
+constexpr int kKT = 64;        // keys per tile
+constexpr int kWaves = 4;      // waves per workgroup (bf16 path)
+constexpr int kThreads = kWaves * kWave;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* prefix_len;
+  const uint64_t* mask;
+  const int32_t* n_nodes;
+  int B, N, Hq, Hkv, G, S_max, W;
+  float scale;                 // softmax scale
+  float scale_log2;            // scale * log2(e)
+  void* out;
+  float* lse;
+  int32_t* err;
+  // workspace
+  int* counters;               // [U * R]
+  float2* part_ml;             // [U, S, Mpad]
+  float* part_o;               // [U, S, Mpad, D]
+  int R, S, Mpad, units_per_xcd;
+};
+
+__device__ __forceinline__ bool seq_valid(int n, int P, int N, int S_max) {
+  return n >= 0 && n <= N && P >= 0 && P + n <= S_max;
+}
+
+__device__ __forceinline__ int seq_err(int n, int P, int N, int S_max) {
+  if (n < 0 || n > N) return err_word(0, SPEC_ERR_NNODES);
+  if (P < 0 || P + n > S_max) return err_word(0, SPEC_ERR_PREFIX);
+  return 0;
+}
+
+// Map the linear workgroup id to (unit, row block, split) so that all workgroups of a unit
+// land on the same XCD (hardware dispatches consecutive workgroup ids round-robin over 8
+// XCDs).  Returns false for padding workgroups.
+__device__ __forceinline__ bool decode_wg(const AttnArgs& a, int& u, int& rb, int& split) {
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7;
+  const int slot = bid >> 3;
+  const int per_unit = a.R * a.S;
+  const int lu = slot / per_unit;
+  const int w = slot - lu * per_unit;
+  u = xcd + 8 * lu;
+  rb = w % a.R;
+  split = w / a.R;
+  return u < a.B * a.Hkv;
+}
+
+template <int D, int CB>
+__global__ __launch_bounds__(kThreads) void tree_attn_bf16_kernel(AttnArgs a) {
+  constexpr int KS = D + 8;          // K tile row stride in LDS (elements)
+  constexpr int VS = kKT + 8;        // transposed V tile row stride in LDS (elements)
+  constexpr int DS = D / 32;         // 32-dim steps of the score product
+  constexpr int DB = D / 16;         // 16-dim blocks of the output
+  constexpr int ROWS_WAVE = 16 * CB;
+  constexpr int RBS = kWaves * ROWS_WAVE;
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds[kKT * KS];
+  __shared__ __attribute__((aligned(16))) __bf16 vt_lds[D * VS];
+  __shared__ int s_last;
+
+  int u, rb, split;
+  if (!decode_wg(a, u, rb, split)) return;
+  const int b = u / a.Hkv;
+  const int g = u - b * a.Hkv;
+  const int n = a.n_nodes ? a.n_nodes[b] : a.N;
+  const int P = a.prefix_len[b];
+  const int M = a.N * a.G;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int lg = lane >> 4;
+
+  const __bf16* __restrict__ qp = static_cast<const __bf16*>(a.q);
+  const __bf16* __restrict__ kp = static_cast<const __bf16*>(a.k);
+  const __bf16* __restrict__ vp = static_cast<const __bf16*>(a.v);
+  __bf16* __restrict__ op = static_cast<__bf16*>(a.out);
+
+  if (!seq_valid(n, P, a.N, a.S_max)) {
+    if (split == 0) {
+      if (a.err && g == 0 && rb == 0 && tid == 0) a.err[b] = seq_err(n, P, a.N, a.S_max);
+      for (int idx = tid; idx < RBS * D; idx += kThreads) {
+        const int r = rb * RBS + idx / D;
+        if (r >= M) continue;
+        const int i = r / a.G, h = g * a.G + r % a.G;
+        op[(((size_t)b * a.N + i) * a.Hq + h) * D + idx % D] = (__bf16)0.f;
+        if (a.lse && idx % D == 0) a.lse[((size_t)b * a.N + i) * a.Hq + h] = -INFINITY;
+      }
+    }
+    return;
+  }
+  if (a.err && g == 0 && rb == 0 && split == 0 && tid == 0) a.err[b] = 0;
+
+  // Key range of this split, tile aligned.
+  const int total = P + n;
+  int span = (total + a.S - 1) / a.S;
+  span = (span + kKT - 1) / kKT * kKT;
+  const int k0 = split * span;
+  const int k1 = min(total, k0 + span);
+
+  // Rows of this lane: r = rb * RBS + wave * ROWS_WAVE + cb * 16 + l16.
+  int row_node[CB];
+  bool row_ok[CB];
+  bf16x8 qf[CB][DS];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int r = rb * RBS + wave * ROWS_WAVE + cb * 16 + l16;
+    const int i = r / a.G;
+    row_node[cb] = i;
+    row_ok[cb] = r < M && i < n;
+    const int h = g * a.G + r % a.G;
+    const __bf16* src = qp + (((size_t)b * a.N + i) * a.Hq + h) * D + 8 * lg;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      if (row_ok[cb]) {
+        qf[cb][ds] = *reinterpret_cast<const bf16x8*>(src + ds * 32);
+      } else {
+        qf[cb][ds] = bf16x8{};
+      }
+    }
+  }
+
+  f32x4 o_acc[DB][CB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) o_acc[db][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[CB], l_run[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    m_run[cb] = -INFINITY;
+    l_run[cb] = 0.f;
+  }
+
+  const size_t kv_base = ((size_t)b * a.Hkv + g) * (size_t)a.S_max * D;
+  constexpr int CPK = D / 8;               // 16-byte chunks per key row
+  constexpr int KPP = kThreads / CPK;      // keys per load pass
+  const int ld_key = tid / CPK;
+  const int ld_chunk = tid % CPK;
+
+  for (int t0 = k0; t0 < k1; t0 += kKT) {
+    // ---- stage the tile: K row-major, V transposed; keys past the sequence are zeros.
+#pragma unroll
+    for (int pass = 0; pass < kKT / KPP; ++pass) {
+      const int key = pass * KPP + ld_key;
+      const int s = t0 + key;
+      bf16x8 kv = bf16x8{}, vv = bf16x8{};
+      if (s < total) {
+        kv = *reinterpret_cast<const bf16x8*>(kp + kv_base + (size_t)s * D + ld_chunk * 8);
+        vv = *reinterpret_cast<const bf16x8*>(vp + kv_base + (size_t)s * D + ld_chunk * 8);
+      }
+      *reinterpret_cast<bf16x8*>(&k_lds[key * KS + ld_chunk * 8]) = kv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vt_lds[(ld_chunk * 8 + e) * VS + key] = vv[e];
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T for the 64 keys of the tile.
+    f32x4 s_acc[4][CB];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) s_acc[kb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(&k_lds[(kb * 16 + l16) * KS + ds * 32 + 8 * lg]);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          s_acc[kb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[cb][ds], s_acc[kb][cb], 0, 0, 0);
+      }
+    }
+
+    // ---- mask, online softmax (base 2), pack P^T as bf16 B operands.
+    const bool tree_tile = t0 + kKT > P;         // the tile reaches tree slots
+    bf16x8 pb[2][CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      uint64_t wlo = 0, whi = 0;
+      int jw = 0;
+      if (tree_tile && row_ok[cb]) {
+        jw = (t0 - P) >> 6;                     // floor division (t0 - P may be negative)
+        const uint64_t* mrow = a.mask + ((size_t)b * a.N + row_node[cb]) * a.W;
+        if (jw >= 0 && jw < a.W) wlo = mrow[jw];
+        if (jw + 1 >= 0 && jw + 1 < a.W) whi = mrow[jw + 1];
+      }
+      float x[4][4];
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s = t0 + kb * 16 + 4 * lg + e;
+          bool vis = row_ok[cb] && s < k1;
+          if (vis && s >= P) {
+            const int j = s - P;
+            const uint64_t word = ((j >> 6) == jw) ? wlo : whi;
+            vis = (word >> (j & 63)) & 1ull;
+          }
+          x[kb][e] = vis ? s_acc[kb][cb][e] * a.scale_log2 : -INFINITY;
+          mloc = fmaxf(mloc, x[kb][e]);
+        }
+      }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      const float m_new = fmaxf(m_run[cb], mloc);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2f(m_run[cb] - m_use);
+      m_run[cb] = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[kb][e] = exp2f(x[kb][e] - m_use);
+          psum += x[kb][e];
+        }
+      l_run[cb] = l_run[cb] * alpha + psum;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o_acc[db][cb] *= alpha;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        bf16x8 p;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = (__bf16)x[2 * c][e];
+          p[4 + e] = (__bf16)x[2 * c + 1][e];
+        }
+        pb[c][cb] = p;
+      }
+    }
+
+    // ---- O^T += V^T P^T.
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const __bf16* vrow = &vt_lds[(db * 16 + l16) * VS + c * 32 + 4 * lg];
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 16);
+        const bf16x8 af = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          o_acc[db][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pb[c][cb], o_acc[db][cb], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // Row sums: lanes l16, l16+16, l16+32, l16+48 hold partial sums of the same row.
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    l_run[cb] += __shfl_xor(l_run[cb], 16);
+    l_run[cb] += __shfl_xor(l_run[cb], 32);
+  }
+
+  if (a.S == 1) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int r = rb * RBS + wave * ROWS_WAVE + cb * 16 + l16;
+      if (r >= M) continue;
+      const int i = r / a.G, h = g * a.G + r % a.G;
+      const bool live = row_ok[cb] && l_run[cb] > 0.f;
+      const float inv = live ? 1.f / l_run[cb] : 0.f;
+      __bf16* dst = op + (((size_t)b * a.N + i) * a.Hq + h) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        bf16x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(o_acc[db][cb][e] * inv);
+        *reinterpret_cast<bf16x4*>(dst + db * 16 + 4 * lg) = o4;
+      }
+      if (a.lse && lg == 0)
+        a.lse[((size_t)b * a.N + i) * a.Hq + h] = live ? (m_run[cb] + log2f(l_run[cb])) * kLn2 : -INFINITY;
+    }
+    return;
+  }
+
+  // ---- several splits: store partials, the last workgroup of the (unit, row block) merges.
+  const size_t pbase = ((size_t)u * a.S + split) * a.Mpad;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int r = rb * RBS + wave * ROWS_WAVE + cb * 16 + l16;
+    float* dst = a.part_o + (pbase + r) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(dst + db * 16 + 4 * lg) = o_acc[db][cb];
+    if (lg == 0) a.part_ml[pbase + r] = make_float2(row_ok[cb] ? m_run[cb] : -INFINITY, row_ok[cb] ? l_run[cb] : 0.f);
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const int prev = atomicAdd(&a.counters[u * a.R + rb], 1);
+    s_last = prev == a.S - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  constexpr int C4 = D / 4;
+  for (int idx = tid; idx < RBS * C4; idx += kThreads) {
+    const int rr = idx / C4;
+    const int d4 = idx - rr * C4;
+    const int r = rb * RBS + rr;
+    if (r >= M) continue;
+    const int i = r / a.G, h = g * a.G + r % a.G;
+    float mmax = -INFINITY;
+    for (int s = 0; s < a.S; ++s) mmax = fmaxf(mmax, a.part_ml[((size_t)u * a.S + s) * a.Mpad + r].x);
+    const float muse = (mmax == -INFINITY) ? 0.f : mmax;
+    float L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < a.S; ++s) {
+      const size_t pr = ((size_t)u * a.S + s) * a.Mpad + r;
+      const float2 ml = a.part_ml[pr];
+      const float wgt = exp2f(ml.x - muse);
+      L += wgt * ml.y;
+      acc += wgt * *reinterpret_cast<const f32x4*>(a.part_o + pr * D + 4 * d4);
+    }
+    const bool live = i < n && L > 0.f;
+    const float inv = live ? 1.f / L : 0.f;
+    bf16x4 o4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[e] * inv);
+    *reinterpret_cast<bf16x4*>(op + (((size_t)b * a.N + i) * a.Hq + h) * D + 4 * d4) = o4;
+    if (a.lse && d4 == 0) a.lse[((size_t)b * a.N + i) * a.Hq + h] = live ? (mmax + log2f(L)) * kLn2 : -INFINITY;
+  }
+  if (tid == 0) a.counters[u * a.R + rb] = 0;
+}
+
+// Exact fp32 path: one workgroup of 256 threads per query row (b, node, head).  Keys are taken
+// 256 at a time: each thread scores one key, the chunk is folded into a running max / sum,
+// and thread t accumulates output dimension t % D over the keys t / D, t / D + 256 / D, ...
+template <int D>
+__global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnArgs a) {
+  constexpr int SLICES = 256 / D;
+  __shared__ float q_s[D];
+  __shared__ float p_s[256];
+  __shared__ float red[256];
+  __shared__ float o_s[256];
+  const int row = blockIdx.x;
+  const int h = row % a.Hq;
+  const int i = (row / a.Hq) % a.N;
+  const int b = row / (a.Hq * a.N);
+  const int g = h / a.G;
+  const int tid = threadIdx.x;
+  const int n = a.n_nodes ? a.n_nodes[b] : a.N;
+  const int P = a.prefix_len[b];
+  const float* qp = static_cast<const float*>(a.q);
+  const float* kp = static_cast<const float*>(a.k);
+  const float* vp = static_cast<const float*>(a.v);
+  float* op = static_cast<float*>(a.out) + (((size_t)b * a.N + i) * a.Hq + h) * D;
+  const bool valid = seq_valid(n, P, a.N, a.S_max);
+  if (a.err && i == 0 && h == 0 && tid == 0) a.err[b] = seq_err(n, P, a.N, a.S_max);
+  if (!valid || i >= n) {
+    if (tid < D) op[tid] = 0.f;
+    if (a.lse && tid == 0) a.lse[((size_t)b * a.N + i) * a.Hq + h] = -INFINITY;
+    return;
+  }
+  if (tid < D) q_s[tid] = qp[(((size_t)b * a.N + i) * a.Hq + h) * D + tid];
+  const uint64_t* mrow = a.mask + ((size_t)b * a.N + i) * a.W;
+  const size_t kv_base = ((size_t)b * a.Hkv + g) * (size_t)a.S_max * D;
+  const float scale = a.scale;
+  __syncthreads();
+
+  const int total = P + n;
+  float m_run = -INFINITY, l_run = 0.f, o_run = 0.f;
+  const int dcol = tid % D, slice = tid / D;
+  for (int c0 = 0; c0 < total; c0 += 256) {
+    const int s = c0 + tid;
+    float sc = -INFINITY;
+    bool vis = s < total;
+    if (vis && s >= P) vis = (mrow[(s - P) >> 6] >> ((s - P) & 63)) & 1ull;
+    if (vis) {
+      const float* krow = kp + kv_base + (size_t)s * D;
+      float dot = 0.f;
+      for (int d = 0; d < D; ++d) dot = fmaf(q_s[d], krow[d], dot);
+      sc = dot * scale;
+    }
+    red[tid] = sc;
+    __syncthreads();
+    for (int st = 128; st > 0; st >>= 1) {
+      if (tid < st) red[tid] = fmaxf(red[tid], red[tid + st]);
+      __syncthreads();
+    }
+    const float cmax = red[0];
+    __syncthreads();
+    const float m_new = fmaxf(m_run, cmax);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = expf(m_run - m_use);
+    const float p = expf(sc - m_use);
+    p_s[tid] = p;
+    red[tid] = p;
+    __syncthreads();
+    for (int st = 128; st > 0; st >>= 1) {
+      if (tid < st) red[tid] += red[tid + st];
+      __syncthreads();
+    }
+    l_run = l_run * alpha + red[0];
+    o_run *= alpha;
+    for (int kk = slice; kk < 256; kk += SLICES) {
+      const int s2 = c0 + kk;
+      if (s2 < total && p_s[kk] != 0.f) o_run = fmaf(p_s[kk], vp[kv_base + (size_t)s2 * D + dcol], o_run);
+    }
+    m_run = m_new;
+    __syncthreads();
+  }
+  o_s[tid] = o_run;
+  __syncthreads();
+  if (tid < D) {
+    float o = 0.f;
+    for (int sl = 0; sl < SLICES; ++sl) o += o_s[sl * D + tid];
+    op[tid] = l_run > 0.f ? o / l_run : 0.f;
+  }
+  if (a.lse && tid == 0)
+    a.lse[((size_t)b * a.N + i) * a.Hq + h] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
+}
+
+struct Plan {
+  int CB, RBS, R, S, Mpad, units, wgs;
+};
+
+Plan make_plan(int B, int N, int Hq, int Hkv, int D, int S_max) {
+  Plan p{};
+  const int G = Hq / Hkv;
+  const int M = N * G;
+  p.units = B * Hkv;
+  p.CB = M >= 192 ? 4 : (M >= 96 ? 2 : 1);
+  if (D == 64 && p.CB > 2) p.CB = 2;
+  p.RBS = kWaves * 16 * p.CB;
+  p.R = (M + p.RBS - 1) / p.RBS;
+  p.Mpad = p.R * p.RBS;
+  // Enough workgroups to cover the 256 CUs about twice, but keep every split at least four
+  // tiles long so that Q loads and partial stores stay small next to the K/V stream.
+  const int want = (512 + p.units * p.R - 1) / (p.units * p.R);
+  const int max_splits = (S_max + 4 * kKT - 1) / (4 * kKT);
+  p.S = want < 1 ? 1 : want;
+  if (p.S > max_splits) p.S = max_splits;
+  if (p.S < 1) p.S = 1;
+  const int per_xcd = (p.units + 7) / 8;
+  p.wgs = 8 * per_xcd * p.R * p.S;
+  return p;
+}
+
+size_t workspace_bytes(const Plan& p, int D) {
+  if (p.S == 1) return 0;
+  size_t off = align_up((size_t)p.units * p.R * sizeof(int), 256);
+  off += align_up((size_t)p.units * p.S * p.Mpad * sizeof(float2), 256);
+  off += align_up((size_t)p.units * p.S * p.Mpad * D * sizeof(float), 256);
+  return off;
+}
+
+}  // namespace
+}  // namespace spectree
+
+using namespace spectree;
+
+extern "C" size_t spec_tree_attn_workspace(int B, int N, int Hq, int Hkv, int head_dim, int S_max,
+                                           spec_dtype dtype) {
+  if (dtype != SPEC_BF16 || B < 1 || N < 1 || Hkv < 1 || Hq < Hkv || S_max < 1) return 0;
+  return workspace_bytes(make_plan(B, N, Hq, Hkv, head_dim, S_max), head_dim);
+}
+
+extern "C" spec_status spec_tree_attn(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* prefix_len, const uint64_t* tree_mask,
+                                      const int32_t* n_nodes, int B, int N, int Hq, int Hkv,
+                                      int head_dim, int S_max, float scale, spec_dtype dtype,
+                                      void* out, float* lse, int32_t* err, void* workspace,
+                                      size_t ws_bytes, void* stream) {
+  if (B < 1 || N < 1 || N > SPEC_MAX_NODES || Hq < 1 || Hkv < 1 || S_max < 1) return SPEC_EINVAL;
+  if (!q || !k_cache || !v_cache || !prefix_len || !tree_mask || !out) return SPEC_EINVAL;
+  if (Hq % Hkv != 0) return SPEC_EUNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return SPEC_EUNSUPPORTED;
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EUNSUPPORTED;
+  if (!(scale == scale)) return SPEC_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  AttnArgs a{};
+  a.q = q; a.k = k_cache; a.v = v_cache; a.prefix_len = prefix_len; a.mask = tree_mask;
+  a.n_nodes = n_nodes; a.B = B; a.N = N; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+  a.S_max = S_max; a.W = (N + 63) / 64; a.scale = scale; a.scale_log2 = scale * kLog2e;
+  a.out = out; a.lse = lse; a.err = err;
+
+  if (dtype == SPEC_F32) {
+    ProfScope prof("tree_attn_f32", s);
+    const int grid = B * N * Hq;
+    if (head_dim == 64) tree_attn_f32_kernel<64><<<grid, 256, 0, s>>>(a);
+    else tree_attn_f32_kernel<128><<<grid, 256, 0, s>>>(a);
+    return launch_status();
+  }
+
+  const Plan p = make_plan(B, N, Hq, Hkv, head_dim, S_max);
+  const size_t need = workspace_bytes(p, head_dim);
+  if (need > 0 && (!workspace || ws_bytes < need)) return SPEC_EWORKSPACE;
+  a.R = p.R; a.S = p.S; a.Mpad = p.Mpad; a.units_per_xcd = (p.units + 7) / 8;
+  if (p.S > 1) {
+    char* w = static_cast<char*>(workspace);
+    size_t off = 0;
+    a.counters = reinterpret_cast<int*>(w + off);
+    off += align_up((size_t)p.units * p.R * sizeof(int), 256);
+    a.part_ml = reinterpret_cast<float2*>(w + off);
+    off += align_up((size_t)p.units * p.S * p.Mpad * sizeof(float2), 256);
+    a.part_o = reinterpret_cast<float*>(w + off);
+  }
+  ProfScope prof("tree_attn_bf16", s);
+  const dim3 grid(p.wgs), block(kThreads);
+  if (head_dim == 128) {
+    if (p.CB == 4) tree_attn_bf16_kernel<128, 4><<<grid, block, 0, s>>>(a);
+    else if (p.CB == 2) tree_attn_bf16_kernel<128, 2><<<grid, block, 0, s>>>(a);
+    else tree_attn_bf16_kernel<128, 1><<<grid, block, 0, s>>>(a);
+  } else {
+    if (p.CB == 2) tree_attn_bf16_kernel<64, 2><<<grid, block, 0, s>>>(a);
+    else tree_attn_bf16_kernel<64, 1><<<grid, block, 0, s>>>(a);
+  }
+  return launch_status();
+}

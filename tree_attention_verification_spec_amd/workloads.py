@@ -262,7 +262,7 @@ def verify_inputs(w, parents=None):
             r = draft_row[b, kids[p][0]]
             best = _top(draft[b, r], len(kids[p]))
             for rank, c in enumerate(kids[p]):
-                tok = int(best[rank])
+                tok = int(best[rank % len(best)])      # repeats only when Vd < #children
                 tokens[b, c] = tok if d2t is None else int(d2t[tok])
     return {"target_logits": logits, "draft_probs": draft, "draft_row": draft_row,
             "tokens": tokens, "uniforms": uniforms(w), "t2d": t2d, "d2t": d2t, "R": R, "Vd": Vd}
