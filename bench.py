@@ -1,0 +1,405 @@
+#!/usr/bin/env python3
+"""One-GPU benchmark of the tree-verification step of Medusa/EAGLE-style speculative decoding.
+
+A step is one pass of every hot-path stage the workload defines, on one batch of synthetic
+input already resident in HBM:
+    [Medusa-head workload only: heads -> tree assembly ->] tree build -> tree attention -> verify
+The default workload is the 63-node Llama-3-8B-shaped one (batch 1, 32 query / 8 key-value
+heads, head_dim 128, prefix 2048, vocabulary 128256, rejection-sampling verify).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+Timing: W warm-up steps, then exactly K steps replayed from HIP graphs (one graph per cycle
+over rotating input copies totalling more than 1 GB, so the 256 MB Infinity Cache cannot serve
+repeats), bracketed by torch.cuda.synchronize() and HIP events.  A second pass over the same K
+steps, launched eagerly with the library's kernel timing on (start/stop events stamped by each
+kernel's own dispatch), gives each kernel's average launch duration for the roofline figure.  The CPU oracle is then timed on the host on a
+bounded sample of the same workload.  Prints one JSON line on stdout; details go to stderr.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+METRIC = "tree-verify nodes/s + % HBM roofline (63/127-node tree, 8B-shaped GQA)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3
+RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload 1-5 (default 2: 63-node tree)")
+    ap.add_argument("--mode", default=None, help="verify mode (default: the workload's last listed)")
+    ap.add_argument("--rotate-gb", type=float, default=1.2, help="total size of rotating input copies")
+    ap.add_argument("--cpu-seconds", type=float, default=24.0, help="budget of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of from HIP graphs")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="also run a plain device copy of this size (for scaling --pmc byte counters)")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------------------- inputs
+
+def host_inputs(w):
+    from tree_attention_verification_spec_amd import workloads as wl
+    a = wl.attention_inputs(w)
+    if w.heads:
+        return a, None, wl.heads_inputs(w), wl.heads_target_inputs(w)
+    return a, wl.verify_inputs(w, a["parents"]), None, None
+
+
+def upload(w, a, vi, hi, ti):
+    import numpy as np
+    import torch
+    from tree_attention_verification_spec_amd import workloads as wl
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def dev(x, dt=None):
+        t = torch.from_numpy(np.ascontiguousarray(x))
+        return (t.to(dt) if dt is not None else t).cuda()
+
+    s = {"q": dev(a["q"], tdt), "k": dev(a["k_cache"], tdt), "v": dev(a["v_cache"], tdt),
+         "P": dev(a["prefix_len"]), "parents": dev(a["parents"]), "n_nodes": dev(a["n_nodes"])}
+    if w.heads:
+        s.update(h=dev(hi["h"], torch.bfloat16), W_res=dev(hi["W_res"], torch.bfloat16),
+                 W_lm=dev(hi["W_lm"], torch.bfloat16), topo=dev(wl.bfs_tree(w.tree[1], w.N)),
+                 logits=dev(ti["target_logits"]), uniforms=dev(ti["uniforms"]))
+    else:
+        s.update(logits=dev(vi["target_logits"]), uniforms=dev(vi["uniforms"]), tokens=dev(vi["tokens"]),
+                 draft=dev(vi["draft_probs"]), draft_row=dev(vi["draft_row"]))
+        if vi["t2d"] is not None:
+            s["t2d"] = dev(vi["t2d"])
+    return s
+
+
+def set_bytes(s):
+    return sum(t.numel() * t.element_size() for t in s.values())
+
+
+def alloc_outputs(w, s):
+    import torch
+    B, N = w.B, w.N
+    W = (N + 63) // 64
+    o = {"tb": {"mask": torch.empty((B, N, W), dtype=torch.int64, device="cuda"),
+                "positions": torch.empty((B, N), dtype=torch.int32, device="cuda"),
+                "depths": torch.empty((B, N), dtype=torch.int32, device="cuda"),
+                "err": torch.empty((B,), dtype=torch.int32, device="cuda")},
+         "attn_out": torch.empty_like(s["q"]),
+         "lse": torch.empty((B, N, w.Hq), dtype=torch.float32, device="cuda"),
+         "attn_err": torch.empty((B,), dtype=torch.int32, device="cuda"),
+         "ver": {"accept_len": torch.empty((B,), dtype=torch.int32, device="cuda"),
+                 "path": torch.empty((B, N), dtype=torch.int32, device="cuda"),
+                 "bonus": torch.empty((B,), dtype=torch.int32, device="cuda"),
+                 "node_accept": torch.empty((B, N), dtype=torch.uint8, device="cuda"),
+                 "err": torch.empty((B,), dtype=torch.int32, device="cuda")}}
+    if w.heads:
+        H, k, V = w.heads["H"], w.heads["k"], w.V
+        o["heads"] = {"topk_idx": torch.empty((B, H, k), dtype=torch.int32, device="cuda"),
+                      "topk_prob": torch.empty((B, H, k), dtype=torch.float32, device="cuda"),
+                      "probs": torch.empty((B, H, V), dtype=torch.float32, device="cuda")}
+        o["asm"] = {"tokens": torch.empty((B, N), dtype=torch.int32, device="cuda"),
+                    "draft_row": torch.empty((B, N), dtype=torch.int32, device="cuda"),
+                    "err": torch.empty((B,), dtype=torch.int32, device="cuda")}
+    return o
+
+
+# --------------------------------------------------------------------------- one step
+
+class Stepper:
+    def __init__(self, w, mode, sets):
+        import torch
+        from tree_attention_verification_spec_amd import binding as sb
+        self.w, self.mode, self.sets, self.sb = w, mode, sets, sb
+        self.outs = [alloc_outputs(w, s) for s in sets]
+        s0 = sets[0]
+        B, N, Hq, Hkv, d = w.B, w.N, w.Hq, w.Hkv, w.d
+        S_max = s0["k"].shape[2]
+        self.ws_attn = sb.workspace(sb.tree_attn_workspace_bytes(B, N, Hq, Hkv, d, S_max, s0["q"].dtype), "cuda")
+        self.ws_ver = sb.workspace(sb.verify_workspace_bytes(B, N, w.V), "cuda")
+        if w.heads:
+            self.ws_heads = sb.workspace(sb.medusa_heads_workspace_bytes(B, w.heads["H"], w.heads["Dm"], w.V,
+                                                                         w.heads["k"]), "cuda")
+        self.scale = d ** -0.5
+
+    def step(self, i):
+        sb, w = self.sb, self.w
+        s, o = self.sets[i], self.outs[i]
+        if w.heads:
+            sb.spec_medusa_heads(s["h"], s["W_res"], s["W_lm"], w.heads["k"], out=o["heads"], ws=self.ws_heads)
+            sb.spec_tree_assemble(o["heads"]["topk_idx"], s["topo"], out=o["asm"])
+            tokens, draft, draft_row = o["asm"]["tokens"], o["heads"]["probs"], o["asm"]["draft_row"]
+        else:
+            tokens, draft, draft_row = s["tokens"], s["draft"], s["draft_row"]
+        sb.spec_tree_build(s["parents"], prefix_len=s["P"], n_nodes=s["n_nodes"], out=o["tb"])
+        sb.spec_tree_attn(s["q"], s["k"], s["v"], s["P"], o["tb"]["mask"], n_nodes=s["n_nodes"], scale=self.scale,
+                          out=o["attn_out"], lse=o["lse"], err=o["attn_err"], ws=self.ws_attn)
+        rej = self.mode == "reject"
+        sb.spec_verify(s["logits"], tokens, s["parents"], s["uniforms"], self.mode,
+                       draft_probs=draft if rej else None, draft_row=draft_row if rej else None,
+                       t2d=s.get("t2d") if rej else None, n_nodes=s["n_nodes"], max_depth=w.N - 1,
+                       out=o["ver"], ws=self.ws_ver)
+
+
+def capture(stepper, indices):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in indices:
+            stepper.step(i)
+    return g
+
+
+# --------------------------------------------------------------------------- algorithmic work
+
+def algorithmic(w, a, parents, depths):
+    """Per-launch algorithmic bytes / FLOPs of each kernel (what the method must move or do)."""
+    import numpy as np
+    s = 2 if w.dtype == "bf16" else 4
+    B, N, Hq, Hkv, d, V = w.B, w.N, w.Hq, w.Hkv, w.d, w.V
+    P = a["prefix_len"].astype(np.int64)
+    n = a["n_nodes"].astype(np.int64)
+    W = (N + 63) // 64
+    attn_bytes = int(((P + n) * Hkv * d * 2 * s).sum() + 2 * B * N * Hq * d * s + B * N * W * 8)
+    attn_flops = 0
+    internal = 0
+    for b in range(B):
+        nb = int(n[b])
+        attn_flops += 4 * Hq * d * int((P[b] + depths[b, :nb] + 1).sum())
+        internal += len(set(int(p) for p in parents[b, 1:nb]))
+    out = {("tree_attn_bf16" if w.dtype == "bf16" else "tree_attn_f32"): (attn_bytes, attn_flops),
+           "verify_rowstats": (internal * V * 4, 0)}
+    if w.heads:
+        H, Dm = w.heads["H"], w.heads["Dm"]
+        out["medusa_resblock"] = (H * Dm * Dm * 2, 2 * B * H * Dm * Dm)
+        out["medusa_lm_head"] = (V * Dm * 2, 2 * B * H * Dm * V)
+    return out
+
+
+def roofline_entry(name, nbytes, flops, avg_ms, traffic):
+    intensity = flops / nbytes if nbytes else 0.0
+    if name.startswith("tree_attn") and intensity > RIDGE:
+        achieved = flops / (avg_ms * 1e-3) / 1e12
+        peak, unit, bound = BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        achieved = nbytes / (avg_ms * 1e-3) / 1e9
+        peak, unit, bound = HBM_PEAK_GBS, "GB/s", "hbm"
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": name,
+            "avg_us": round(avg_ms * 1e3, 3), "algorithmic_bytes": nbytes, "algorithmic_flops": flops}
+
+
+# --------------------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(w, a, vi, hi, ti, mode, budget_s):
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from tree_attention_verification_spec_amd import workloads as wl
+    modes = {"greedy": oracle.MODE_GREEDY, "typical": oracle.MODE_TYPICAL, "reject": oracle.MODE_REJECT}
+
+    def one_round(ns):
+        par = a["parents"][:1, :ns]
+        P = a["prefix_len"][:1]
+        nn = np.array([min(ns, int(a["n_nodes"][0]))])
+        if w.heads:
+            rh = oracle.medusa_heads(hi["h"][:1], hi["W_res"], hi["W_lm"], hi["k"])
+            ra = oracle.tree_assemble(rh["topk_idx"], wl.bfs_tree(w.tree[1], w.N)[:ns])
+            tokens, draft, drow, t2d = ra["tokens"], rh["probs"], ra["draft_row"], None
+            logits, unif = ti["target_logits"][:1, :ns], ti["uniforms"][:1, :ns]
+        else:
+            tokens, draft, drow, t2d = vi["tokens"][:1, :ns], vi["draft_probs"][:1], vi["draft_row"][:1, :ns], vi["t2d"]
+            logits, unif = vi["target_logits"][:1, :ns], vi["uniforms"][:1, :ns]
+        tb = oracle.tree_build(par, nn, prefix_len=P)
+        oracle.tree_attention(a["q"][:1, :ns], a["k_cache"][:1], a["v_cache"][:1], P, tb["dense"], nn, scale=a["scale"])
+        oracle.verify(logits, tokens, par, unif, modes[mode], draft_probs=draft, draft_row=drow, t2d=t2d,
+                      n_nodes=nn, max_depth=ns - 1)
+
+    with threadpool_limits(1):
+        # size the sample from two probe rounds (1 and 2 nodes): fixed cost + cost per node
+        t0 = time.perf_counter()
+        one_round(1)
+        t1 = time.perf_counter()
+        one_round(min(2, w.N))
+        t2 = time.perf_counter()
+        per_node = max(t2 - t1 - (t1 - t0), 1e-4)
+        fixed = max(t1 - t0 - per_node, 0.0)
+        ns = int(max(1, min(w.N, (budget_s / 2.0 - fixed) / per_node)))
+        rounds, start = 0, time.perf_counter()
+        while True:
+            one_round(ns)
+            rounds += 1
+            el = time.perf_counter() - start
+            if el >= budget_s / 2.0 or rounds >= 50:
+                break
+    value = rounds * ns / el
+    return {"value": round(value, 3), "unit": "tree-nodes/s", "cores": 1, "kind": "oracle",
+            "sample": (f"sequence 0 of '{w.name}': first {ns} of {w.N} tree nodes, full prefix "
+                       f"{int(a['prefix_len'][0])}; {rounds} oracle round(s) of "
+                       f"{'heads + assembly + ' if w.heads else ''}tree build + attention over all "
+                       f"{ns}x{w.Hq} query rows + {mode} verify; NumPy float64, 1 BLAS thread; "
+                       f"{el:.1f} s"),
+            "host_cpus": os.cpu_count()}
+
+
+# --------------------------------------------------------------------------- main
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (the tree-verification step of one GPU's "
+              "share); multi-GPU runs are not part of it.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from tree_attention_verification_spec_amd import binding as sb
+    from tree_attention_verification_spec_amd import profiling
+    from tree_attention_verification_spec_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    sb.lib()
+    w = wl.config(args.config)
+    mode = args.mode or w.modes[-1]
+    log(f"workload: {w.name}; verify mode {mode}")
+    t0 = time.time()
+    a, vi, hi, ti = host_inputs(w)
+    base = upload(w, a, vi, hi, ti)
+    per_set = set_bytes(base)
+    nsets = max(2, math.ceil(args.rotate_gb * 1e9 / per_set))
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+    log(f"inputs: {per_set / 1e6:.1f} MB per copy x {nsets} rotating copies ({time.time() - t0:.1f} s)")
+    st = Stepper(w, mode, sets)
+
+    # eager warm-up and a reference result for the graph check
+    for i in range(args.warmup):
+        st.step(i % nsets)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in st.outs[0]["ver"].items()}
+    ref_attn = st.outs[0]["attn_out"].clone()
+
+    K = args.steps
+    use_graph = not args.no_graph
+    if use_graph:
+        cyc = capture(st, range(nsets))
+        rem = K % nsets
+        rem_g = capture(st, range(rem)) if rem else None
+        reps = K // nsets
+
+        def run_k():
+            for _ in range(reps):
+                cyc.replay()
+            if rem_g is not None:
+                rem_g.replay()
+        run_k()   # warm the graphs
+        torch.cuda.synchronize()
+        for k, v in st.outs[0]["ver"].items():
+            assert torch.equal(v, ref[k]), f"graph replay differs from eager ({k})"
+        assert torch.equal(st.outs[0]["attn_out"], ref_attn), "graph replay differs from eager (attention)"
+    else:
+        def run_k():
+            for i in range(K):
+                st.step(i % nsets)
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    run_k()
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / K
+    err_words = torch.cat([st.outs[0]["ver"]["err"], st.outs[0]["attn_err"], st.outs[0]["tb"]["err"]])
+    assert int(err_words.abs().sum()) == 0, "a sequence reported a data error"
+
+    # per-kernel durations: the same K steps launched eagerly with the library's kernel timing
+    # on (each launch carries a start/stop event pair stamped by its own dispatch)
+    names = ("tree_build", "tree_assemble", "tree_attn_bf16", "tree_attn_f32", "verify_rowstats",
+             "verify_decide", "verify_bonus_a", "verify_bonus_b", "verify_select",
+             "medusa_resblock", "medusa_lm_head", "medusa_softmax_topk")
+    kernels = {}
+    try:
+        sb.prof_reset()
+        sb.prof_enable(True)
+        torch.cuda.synchronize()
+        for i in range(K):
+            st.step(i % nsets)
+        torch.cuda.synchronize()
+        sb.prof_enable(False)
+        for name in names:
+            ms, cnt = sb.prof_read(name)
+            if cnt:
+                kernels[name] = ms / cnt
+    finally:
+        sb.prof_enable(False)
+        sb.prof_reset()
+
+    depths = st.outs[0]["tb"]["depths"].cpu().numpy()
+    work = algorithmic(w, a, a["parents"], depths)
+    dom = max((k for k in kernels if k in work), key=lambda k: kernels[k])
+    nbytes, flops = work[dom]
+    short = {1: "tiny", 2: "tree63", 3: "tree127_b16", 4: "tree255_b4", 5: "medusa_tree127_b8"}[args.config]
+    tr = profiling.read_traffic(os.path.join(ROOT, "profiles", f"traffic_{dom}_{short}.md"))
+    roof = roofline_entry(dom, nbytes, flops, kernels[dom], None if tr is None else int(tr[0]))
+    for k in sorted(kernels, key=lambda k: -kernels[k]):
+        extra = ""
+        if k in work:
+            b_, f_ = work[k]
+            extra = f"  {b_ / (kernels[k] * 1e-3) / 1e9:8.1f} GB/s  {f_ / (kernels[k] * 1e-3) / 1e12:8.1f} TFLOP/s"
+        log(f"  {k:22s} {kernels[k] * 1e3:9.2f} us{extra}")
+    log(f"step {ms_step * 1e3:.2f} us; kernels sum {sum(kernels.values()) * 1e3:.2f} us")
+
+    if args.copy_calibration_mb:
+        nb = args.copy_calibration_mb * (1 << 20)
+        src = torch.ones(nb // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {nb} bytes x 3")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, a, vi, hi, ti, mode, args.cpu_seconds)
+
+    nodes = w.B * w.N
+    line = {
+        "metric": METRIC,
+        "value": round(nodes / (ms_step * 1e-3), 1),
+        "unit": "tree-nodes/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; shapes of the pages' Llama-3-8B-class GQA, tree sizes, vocabularies)",
+        "config": {"workload": w.name, "batch": w.B, "tree_nodes": w.N, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.d, "prefix": list(w.prefix), "vocab": w.V, "verify_mode": mode,
+                   "medusa_heads": w.heads, "rotating_copies": nsets, "hip_graphs": use_graph},
+        "rounds_per_s": round(1.0 / (ms_step * 1e-3), 1),
+        "roofline": roof,
+        "kernels_us": {k: round(v * 1e3, 3) for k, v in kernels.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -229,7 +229,7 @@ spec_status spec_verify(const float* target_logits, const float* draft_probs,
  *   topk_idx    int32 [B, H, k]  the k largest logits of head j, descending, lower id on ties
  *   topk_prob   float [B, H, k]  D_j at those ids
  *   draft_probs float [B, H, V]  optional (NULL): D_j
- * Supported: B <= 16, Dm % 256 == 0, 1 <= k <= 64, k <= V.
+ * Supported: B <= 16, B * H <= 64, Dm % 128 == 0, 1 <= k <= 64, k <= V.
  * Errors: SPEC_EINVAL, SPEC_EUNSUPPORTED, SPEC_EWORKSPACE.
  * ------------------------------------------------------------------------------------ */
 size_t spec_medusa_heads_workspace(int B, int H, int Dm, int V, int k);
@@ -239,10 +239,11 @@ spec_status spec_medusa_heads(const void* h, const void* W_res, const void* W_lm
                               void* stream);
 
 /* --------------------------------------------------------------------------------------
- * Kernel timing.  When enabled, the library brackets each of its kernel launches with a pair
- * of HIP events recorded on the launch stream, and accumulates the elapsed time per kernel
- * name.  spec_prof_read() waits for the recorded events.  Host-side bookkeeping only; it
- * changes nothing in what the kernels compute.
+ * Kernel timing.  When enabled, the library launches each kernel through hipExtLaunchKernelGGL
+ * with a start/stop HIP event pair that the kernel's own dispatch stamps on the launch stream,
+ * so each pair brackets exactly one kernel execution; elapsed times accumulate per kernel name.
+ * spec_prof_read() waits for the recorded events.  Timing must be off while a stream is being
+ * captured into a graph.  It changes nothing in what the kernels compute.
  * ------------------------------------------------------------------------------------ */
 void spec_prof_enable(int on);
 void spec_prof_reset(void);

@@ -1,0 +1,85 @@
+"""CPU checks of the C ABI: the library loads, exports every function include/spectree.h
+declares, and rejects bad host arguments before touching the GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spectree.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from tree_attention_verification_spec_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from tree_attention_verification_spec_amd import build
+        build.build()
+    return binding.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(spec_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("spec_tree_build", "spec_tree_assemble", "spec_tree_attn", "spec_tree_attn_workspace",
+              "spec_verify", "spec_verify_workspace", "spec_medusa_heads", "spec_medusa_heads_workspace",
+              "spec_strerror", "spec_prof_enable", "spec_prof_reset", "spec_prof_read"):
+        assert n in names, n
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} is declared but not exported"
+
+
+def test_status_strings(lib):
+    for code, text in ((0, "ok"), (1, "invalid argument"), (2, "unsupported configuration"),
+                       (3, "workspace missing or too small"), (4, "HIP runtime error")):
+        assert lib.spec_strerror(code).decode() == text
+
+
+def test_host_argument_checks(lib):
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: every call below returns before a launch
+    # tree build: B < 1, N > 256, NULL outputs
+    assert lib.spec_tree_build(fake, None, None, None, 0, 10, fake, fake, fake, fake, None) == 1
+    assert lib.spec_tree_build(fake, None, None, None, 1, 257, fake, fake, fake, fake, None) == 1
+    assert lib.spec_tree_build(fake, None, None, None, 1, 10, None, fake, fake, fake, None) == 1
+    # tree attention: unsupported head_dim / group, missing workspace
+    args = [fake, fake, fake, fake, fake, None]
+    assert lib.spec_tree_attn(*args, 1, 10, 8, 2, 96, 100, 0.1, 1, fake, None, None, fake, 1 << 30, None) == 2
+    assert lib.spec_tree_attn(*args, 1, 10, 6, 4, 128, 100, 0.1, 1, fake, None, None, fake, 1 << 30, None) == 2
+    assert lib.spec_tree_attn(*args, 1, 10, 8, 2, 128, 100, 0.1, 7, fake, None, None, fake, 1 << 30, None) == 2
+    need = lib.spec_tree_attn_workspace(1, 63, 32, 8, 128, 2111, 1)
+    assert need > 0
+    assert lib.spec_tree_attn(*args, 1, 63, 32, 8, 128, 2111, 0.1, 1, fake, None, None, None, 0, None) == 3
+    assert lib.spec_tree_attn(*args, 1, 63, 32, 8, 128, 2111, 0.1, 1, fake, None, None, fake, need - 1, None) == 3
+    # verify: reject without draft rows, t2d missing with Vd != V, bad mode, small workspace
+    vargs = [fake, None, None, None, fake, fake, None, fake, 2, 10, 100]
+    outs = [fake, fake, fake, None, fake]
+    wsz = lib.spec_verify_workspace(2, 10, 100)
+    assert lib.spec_verify(*vargs, 0, 0, 9, 2, 0.1, 0.3, *outs, fake, wsz, None) == 1
+    vargs2 = [fake, fake, fake, None, fake, fake, None, fake, 2, 10, 100]
+    assert lib.spec_verify(*vargs2, 3, 50, 9, 2, 0.1, 0.3, *outs, fake, wsz, None) == 1
+    assert lib.spec_verify(*vargs2, 3, 100, 9, 5, 0.1, 0.3, *outs, fake, wsz, None) == 1
+    assert lib.spec_verify(*vargs2, 3, 100, 9, 2, 0.1, 0.3, *outs, fake, wsz - 1, None) == 3
+    # heads: unsupported shapes
+    hw = lib.spec_medusa_heads_workspace(4, 2, 256, 1000, 8)
+    assert lib.spec_medusa_heads(fake, fake, fake, 17, 2, 256, 1000, 8, fake, fake, None, fake, hw, None) == 2
+    assert lib.spec_medusa_heads(fake, fake, fake, 4, 2, 200, 1000, 8, fake, fake, None, fake, hw, None) == 2
+    assert lib.spec_medusa_heads(fake, fake, fake, 4, 2, 256, 1000, 65, fake, fake, None, fake, hw, None) == 2
+    assert lib.spec_medusa_heads(fake, fake, fake, 4, 2, 256, 1000, 8, fake, fake, None, fake, hw - 1, None) == 3
+
+
+def test_workspace_sizes_are_monotone(lib):
+    small = lib.spec_verify_workspace(1, 63, 128256)
+    big = lib.spec_verify_workspace(16, 127, 128256)
+    assert 0 < small < big
+    assert lib.spec_medusa_heads_workspace(8, 4, 4096, 32000, 8) > 8 * 4 * 32000 * 4
+    assert lib.spec_tree_attn_workspace(1, 10, 4, 1, 64, 266, 0) == 0   # fp32 path needs none

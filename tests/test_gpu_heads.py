@@ -1,8 +1,9 @@
 """GPU parity: spec_medusa_heads against the oracle, and the end-to-end Medusa round
 (heads -> assembly -> tree build -> tree attention -> verify) of the 4-head workload.
 
-topk_idx is compared exactly except for a (batch, head) whose oracle ranking has two of its
-k + 1 best logits within 1e-4 (counted separately); probabilities within 1e-5 relative."""
+topk_idx is compared position by position: the same token id, or a token whose oracle logit is
+within 1e-4 of the oracle's choice (a near-tie that fp32 rounding may order differently; such
+positions are counted).  Probabilities agree within 1e-5 relative."""
 
 import numpy as np
 import pytest
@@ -26,19 +27,25 @@ def _heads(hi):
     return {k: host(v) for k, v in out.items()}
 
 
-def _compare_heads(got, ref, max_excused_frac=0.25):
+def _compare_heads(got, ref):
+    """Position by position the GPU's top-k must name the oracle's token, or a token whose
+    oracle logit is within 1e-4 of it (a near-tie whose order fp32 rounding may flip).
+    Returns the number of positions that differed within that margin."""
     B, H, k = ref["topk_idx"].shape
-    excused = 0
+    swapped = 0
     for b in range(B):
         for j in range(H):
-            if ref["topk_margin"][b, j] < TOPK_MARGIN:
-                excused += 1
-                continue
-            assert list(got["topk_idx"][b, j]) == list(ref["topk_idx"][b, j]), (b, j)
-    np.testing.assert_allclose(got["topk_prob"], ref["topk_prob"], rtol=1e-5, atol=1e-9)
+            g, r = got["topk_idx"][b, j], ref["topk_idx"][b, j]
+            assert len(set(g.tolist())) == k and (g >= 0).all() and (g < ref["logits"].shape[2]).all()
+            lg = ref["logits"][b, j]
+            for t in range(k):
+                if g[t] != r[t]:
+                    assert abs(lg[g[t]] - lg[r[t]]) < TOPK_MARGIN, (b, j, t, g[t], r[t])
+                    swapped += 1
+    probs_at = np.take_along_axis(ref["probs"], got["topk_idx"].astype(np.int64), axis=2)
+    np.testing.assert_allclose(got["topk_prob"], probs_at, rtol=1e-5, atol=1e-9)
     np.testing.assert_allclose(got["probs"], ref["probs"], rtol=1e-5, atol=1e-9)
-    assert excused <= max(1, int(max_excused_frac * B * H))
-    return excused
+    return swapped
 
 
 SMALL = [dict(B=4, H=3, Dm=256, V=1000, k=8), dict(B=1, H=1, Dm=128, V=77, k=5),
@@ -69,8 +76,8 @@ def test_full_size_heads():
     hi = wl.heads_inputs(w)
     got = _heads(hi)
     ref = oracle.medusa_heads(hi["h"], hi["W_res"], hi["W_lm"], hi["k"])
-    ex = _compare_heads(got, ref)
-    print(f"heads: excused {ex} of {w.B * w.heads['H']} rankings")
+    sw = _compare_heads(got, ref)
+    print(f"heads: {sw} near-tie positions swapped out of {w.B * w.heads['H'] * w.heads['k']}")
 
 
 def test_medusa_round_end_to_end():
@@ -99,8 +106,9 @@ def test_medusa_round_end_to_end():
     # --- oracle, on its own intermediate results
     rh = oracle.medusa_heads(hi["h"], hi["W_res"], hi["W_lm"], hi["k"])
     ra = oracle.tree_assemble(rh["topk_idx"], topo)
-    if (rh["topk_margin"] < TOPK_MARGIN).any():
-        pytest.skip("a top-k ranking is within the margin; downstream steps are excused")
+    if not np.array_equal(host(heads["topk_idx"]), rh["topk_idx"]):
+        _compare_heads({k: host(v) for k, v in heads.items()}, rh)   # only near-ties may differ
+        pytest.skip("a near-tie in the top-k ranking flipped; the downstream steps are excused")
     assert np.array_equal(host(asm["tokens"]), ra["tokens"])
     assert np.array_equal(host(asm["draft_row"]), ra["draft_row"])
     rtb = oracle.tree_build(np.tile(topo, (w.B, 1)), prefix_len=a["prefix_len"])

@@ -1,6 +1,7 @@
 // Internal helpers shared by the HIP sources of libspectree (gfx950 only).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -45,16 +46,21 @@ __device__ __forceinline__ int wave_max(int v) {
 
 // ---------------------------------------------------------------- host side
 
-// Kernel timing hooks (runtime.hip).  prof_begin returns an opaque token passed to prof_end.
-int prof_begin(const char* name, hipStream_t stream);
-void prof_end(int token, hipStream_t stream);
+// Kernel timing (runtime.hip).  When timing is on, prof_pair() creates a start/stop event pair
+// registered under `name` and returns true; the launch then goes through
+// hipExtLaunchKernelGGL, whose events are stamped by the kernel's own dispatch, so they bracket
+// exactly that kernel's execution on `stream`.
+bool prof_pair(const char* name, hipEvent_t* start, hipEvent_t* stop);
 
-struct ProfScope {
-  int token;
-  hipStream_t stream;
-  ProfScope(const char* name, hipStream_t s) : token(prof_begin(name, s)), stream(s) {}
-  ~ProfScope() { prof_end(token, stream); }
-};
+template <typename F, typename... Args>
+inline void launch(const char* name, F kernel, dim3 grid, dim3 block, hipStream_t stream, Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (prof_pair(name, &e0, &e1)) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, e0, e1, 0, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+  }
+}
 
 inline spec_status launch_status() {
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;

@@ -247,26 +247,19 @@ extern "C" spec_status spec_medusa_heads(const void* h, const void* W_res, const
   __bf16* zsplit = reinterpret_cast<__bf16*>(w + L.zsplit);
   float* logits = reinterpret_cast<float*>(w + L.logits);
   const int NC = B * H;
-  {
-    ProfScope prof("medusa_resblock", s);
-    resblock_kernel<<<H * (Dm / 16), kThreads, 0, s>>>(static_cast<const __bf16*>(h),
-                                                       static_cast<const __bf16*>(W_res), B, H, Dm, zsplit);
-    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-  }
-  {
-    ProfScope prof("medusa_lm_head", s);
-    const int grid = (V + 16 * kLmRowBlocks - 1) / (16 * kLmRowBlocks);
-    const __bf16* wl = static_cast<const __bf16*>(W_lm);
-    const int cbn = (NC + 15) / 16;
-    if (cbn == 1) lm_head_kernel<1><<<grid, kThreads, 0, s>>>(wl, zsplit, NC, Dm, V, logits);
-    else if (cbn == 2) lm_head_kernel<2><<<grid, kThreads, 0, s>>>(wl, zsplit, NC, Dm, V, logits);
-    else if (cbn == 3) lm_head_kernel<3><<<grid, kThreads, 0, s>>>(wl, zsplit, NC, Dm, V, logits);
-    else lm_head_kernel<4><<<grid, kThreads, 0, s>>>(wl, zsplit, NC, Dm, V, logits);
-    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-  }
-  {
-    ProfScope prof("medusa_softmax_topk", s);
-    softmax_topk_kernel<<<NC, kThreads, 0, s>>>(logits, H, V, k, topk_idx, topk_prob, draft_probs);
-  }
+  const dim3 blk(kThreads);
+  launch("medusa_resblock", resblock_kernel, dim3(H * (Dm / 16)), blk, s, static_cast<const __bf16*>(h),
+         static_cast<const __bf16*>(W_res), B, H, Dm, zsplit);
+  const dim3 grid_lm((V + 16 * kLmRowBlocks - 1) / (16 * kLmRowBlocks));
+  const __bf16* wl = static_cast<const __bf16*>(W_lm);
+  const __bf16* zs = zsplit;
+  const char* nm = "medusa_lm_head";
+  const int cbn = (NC + 15) / 16;
+  if (cbn == 1) launch(nm, lm_head_kernel<1>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
+  else if (cbn == 2) launch(nm, lm_head_kernel<2>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
+  else if (cbn == 3) launch(nm, lm_head_kernel<3>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
+  else launch(nm, lm_head_kernel<4>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
+  launch("medusa_softmax_topk", softmax_topk_kernel, dim3(NC), blk, s, static_cast<const float*>(logits), H, V,
+         k, topk_idx, topk_prob, draft_probs);
   return launch_status();
 }

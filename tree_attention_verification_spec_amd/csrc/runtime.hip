@@ -33,28 +33,19 @@ std::vector<Record> g_records;
 
 }  // namespace
 
-int prof_begin(const char* name, hipStream_t stream) {
+bool prof_pair(const char* name, hipEvent_t* start, hipEvent_t* stop) {
   std::lock_guard<std::mutex> lock(g_mu);
-  if (!g_enabled) return -1;
+  if (!g_enabled) return false;
   Record r{name, nullptr, nullptr};
-  if (hipEventCreate(&r.start) != hipSuccess) return -1;
+  if (hipEventCreate(&r.start) != hipSuccess) return false;
   if (hipEventCreate(&r.stop) != hipSuccess) {
     (void)hipEventDestroy(r.start);
-    return -1;
-  }
-  if (hipEventRecord(r.start, stream) != hipSuccess) {
-    (void)hipEventDestroy(r.start);
-    (void)hipEventDestroy(r.stop);
-    return -1;
+    return false;
   }
   g_records.push_back(r);
-  return static_cast<int>(g_records.size()) - 1;
-}
-
-void prof_end(int token, hipStream_t stream) {
-  if (token < 0) return;
-  std::lock_guard<std::mutex> lock(g_mu);
-  if (token < static_cast<int>(g_records.size())) (void)hipEventRecord(g_records[token].stop, stream);
+  *start = r.start;
+  *stop = r.stop;
+  return true;
 }
 
 }  // namespace spectree

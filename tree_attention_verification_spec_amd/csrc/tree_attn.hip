@@ -518,10 +518,9 @@ extern "C" spec_status spec_tree_attn(const void* q, const void* k_cache, const 
   a.out = out; a.lse = lse; a.err = err;
 
   if (dtype == SPEC_F32) {
-    ProfScope prof("tree_attn_f32", s);
-    const int grid = B * N * Hq;
-    if (head_dim == 64) tree_attn_f32_kernel<64><<<grid, 256, 0, s>>>(a);
-    else tree_attn_f32_kernel<128><<<grid, 256, 0, s>>>(a);
+    const dim3 grid(B * N * Hq);
+    if (head_dim == 64) launch("tree_attn_f32", tree_attn_f32_kernel<64>, grid, dim3(256), s, a);
+    else launch("tree_attn_f32", tree_attn_f32_kernel<128>, grid, dim3(256), s, a);
     return launch_status();
   }
 
@@ -538,15 +537,15 @@ extern "C" spec_status spec_tree_attn(const void* q, const void* k_cache, const 
     off += align_up((size_t)p.units * p.S * p.Mpad * sizeof(float2), 256);
     a.part_o = reinterpret_cast<float*>(w + off);
   }
-  ProfScope prof("tree_attn_bf16", s);
   const dim3 grid(p.wgs), block(kThreads);
+  const char* nm = "tree_attn_bf16";
   if (head_dim == 128) {
-    if (p.CB == 4) tree_attn_bf16_kernel<128, 4><<<grid, block, 0, s>>>(a);
-    else if (p.CB == 2) tree_attn_bf16_kernel<128, 2><<<grid, block, 0, s>>>(a);
-    else tree_attn_bf16_kernel<128, 1><<<grid, block, 0, s>>>(a);
+    if (p.CB == 4) launch(nm, tree_attn_bf16_kernel<128, 4>, grid, block, s, a);
+    else if (p.CB == 2) launch(nm, tree_attn_bf16_kernel<128, 2>, grid, block, s, a);
+    else launch(nm, tree_attn_bf16_kernel<128, 1>, grid, block, s, a);
   } else {
-    if (p.CB == 2) tree_attn_bf16_kernel<64, 2><<<grid, block, 0, s>>>(a);
-    else tree_attn_bf16_kernel<64, 1><<<grid, block, 0, s>>>(a);
+    if (p.CB == 2) launch(nm, tree_attn_bf16_kernel<64, 2>, grid, block, s, a);
+    else launch(nm, tree_attn_bf16_kernel<64, 1>, grid, block, s, a);
   }
   return launch_status();
 }

@@ -153,9 +153,8 @@ extern "C" spec_status spec_tree_build(const int32_t* parents, const int32_t* de
   if (!parents || !mask || !positions || !depths || !err) return SPEC_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int W = (N + 63) / 64;
-  ProfScope prof("tree_build", s);
-  tree_build_kernel<<<B, SPEC_MAX_NODES, 0, s>>>(parents, depths_in, prefix_len, n_nodes, N, W,
-                                                 mask, positions, depths, err);
+  launch("tree_build", tree_build_kernel, dim3(B), dim3(SPEC_MAX_NODES), s, parents, depths_in, prefix_len,
+         n_nodes, N, W, mask, positions, depths, err);
   return launch_status();
 }
 
@@ -166,8 +165,7 @@ extern "C" spec_status spec_tree_assemble(const int32_t* topk_idx, const int32_t
   if (B < 1 || N < 1 || N > SPEC_MAX_NODES || H < 1 || k < 1) return SPEC_EINVAL;
   if (!topk_idx || !parents || !tokens || !draft_row || !err) return SPEC_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  ProfScope prof("tree_assemble", s);
-  tree_assemble_kernel<<<B, SPEC_MAX_NODES, 0, s>>>(topk_idx, parents, root_tokens, N, H, k,
-                                                    tokens, draft_row, err);
+  launch("tree_assemble", tree_assemble_kernel, dim3(B), dim3(SPEC_MAX_NODES), s, topk_idx, parents,
+         root_tokens, N, H, k, tokens, draft_row, err);
   return launch_status();
 }

@@ -594,31 +594,13 @@ extern "C" spec_status spec_verify(const float* target_logits, const float* draf
   a.plans = reinterpret_cast<BonusPlan*>(w + L.plans);
   a.bparts = reinterpret_cast<BonusPart*>(w + L.bparts);
 
-  {
-    ProfScope prof("verify_rowstats", s);
-    const dim3 grid((unsigned)((size_t)L.C * N * B));
-    if (V % 4 == 0) rowstats_kernel<4><<<grid, kThreads, 0, s>>>(a);
-    else rowstats_kernel<1><<<grid, kThreads, 0, s>>>(a);
-    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-  }
-  {
-    ProfScope prof("verify_decide", s);
-    decide_kernel<<<B, kThreads, 0, s>>>(a);
-    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-  }
-  {
-    ProfScope prof("verify_bonus_a", s);
-    bonus_a_kernel<<<dim3((unsigned)((size_t)L.C * B)), kThreads, 0, s>>>(a);
-    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-  }
-  {
-    ProfScope prof("verify_bonus_b", s);
-    bonus_b_kernel<<<dim3((unsigned)((size_t)L.C * B)), kThreads, 0, s>>>(a);
-    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-  }
-  {
-    ProfScope prof("verify_select", s);
-    select_kernel<<<B, kThreads, 0, s>>>(a);
-  }
+  const dim3 blk(kThreads);
+  const dim3 grid_rows((unsigned)((size_t)L.C * N * B)), grid_chunks((unsigned)((size_t)L.C * B));
+  if (V % 4 == 0) launch("verify_rowstats", rowstats_kernel<4>, grid_rows, blk, s, a);
+  else launch("verify_rowstats", rowstats_kernel<1>, grid_rows, blk, s, a);
+  launch("verify_decide", decide_kernel, dim3(B), blk, s, a);
+  launch("verify_bonus_a", bonus_a_kernel, grid_chunks, blk, s, a);
+  launch("verify_bonus_b", bonus_b_kernel, grid_chunks, blk, s, a);
+  launch("verify_select", select_kernel, dim3(B), blk, s, a);
   return launch_status();
 }
