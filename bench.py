@@ -181,7 +181,7 @@ def algorithmic(w, a, parents, depths):
         attn_flops += 4 * Hq * d * int((P[b] + depths[b, :nb] + 1).sum())
         internal += len(set(int(p) for p in parents[b, 1:nb]))
     out = {("tree_attn_bf16" if w.dtype == "bf16" else "tree_attn_f32"): (attn_bytes, attn_flops),
-           "verify_rowstats": (internal * V * 4, 0)}
+           "verify_rows": (internal * V * 4, 0)}
     if w.heads:
         H, Dm = w.heads["H"], w.heads["Dm"]
         out["medusa_resblock"] = (H * Dm * Dm * 2, 2 * B * H * Dm * Dm)
@@ -328,9 +328,9 @@ def main():
 
     # per-kernel durations: the same K steps launched eagerly with the library's kernel timing
     # on (each launch carries a start/stop event pair stamped by its own dispatch)
-    names = ("tree_build", "tree_assemble", "tree_attn_bf16", "tree_attn_f32", "verify_rowstats",
-             "verify_decide", "verify_bonus_a", "verify_bonus_b", "verify_select",
-             "medusa_resblock", "medusa_lm_head", "medusa_softmax_topk")
+    names = ("tree_build", "tree_assemble", "tree_attn_bf16", "tree_attn_merge", "tree_attn_f32", "verify_rows",
+             "verify_decide", "verify_bonus", "verify_select", "medusa_resblock", "medusa_lm_head",
+             "medusa_softmax_topk")
     kernels = {}
     try:
         sb.prof_reset()

@@ -1,7 +1,7 @@
 """GPU parity: spec_verify against the oracle.  accept_len, path, bonus token, per-node results and
 error words are bit-exact; a sequence holding a decision within the stated margins of its
-boundary (|u - min(1, T/D)| or |ln T - ln tau| below 1e-4, or an fp64 bonus draw within
-1e-12 of a CDF step) is counted separately."""
+boundary (|u - min(1, T/D)| or |ln T - ln tau| below 1e-4, or a bonus draw within 1e-9
+(relative) of a CDF step) is counted separately."""
 
 import numpy as np
 import pytest

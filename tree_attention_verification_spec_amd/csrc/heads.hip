@@ -149,8 +149,84 @@ __global__ __launch_bounds__(kThreads) void lm_head_kernel(const __bf16* __restr
   }
 }
 
-// One workgroup per column (b, j): softmax and top-k (descending, lower id first on ties).
+// One workgroup per column (b, j): the whole logits row is held in registers (PER values per
+// thread, loaded branch-free and all in flight), then max, normaliser, probabilities, and k
+// rounds of a block arg-max below the previous pick in (value desc, id asc) order.
+template <int PER>
 __global__ __launch_bounds__(kThreads) void softmax_topk_kernel(const float* __restrict__ logits, int H, int V,
+                                                                int k, int32_t* __restrict__ topk_idx,
+                                                                float* __restrict__ topk_prob,
+                                                                float* __restrict__ probs) {
+  __shared__ float s_f[kThreads / kWave];
+  __shared__ int s_i[kThreads / kWave];
+  const int col = blockIdx.x;
+  const int t = threadIdx.x;
+  const int w = t >> 6;
+  const float* row = logits + (size_t)col * V;
+  float x[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int v = i * kThreads + t;
+    const float val = row[v < V ? v : 0];
+    x[i] = v < V ? val : -INFINITY;
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) m = fmaxf(m, x[i]);
+  m = wave_max(m);
+  if ((t & 63) == 0) s_f[w] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(s_f[0], s_f[1]), fmaxf(s_f[2], s_f[3]));
+  __syncthreads();
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) sum += expf(x[i] - m);   // exp(-inf) = 0 past the row
+  sum = wave_sum(sum);
+  if ((t & 63) == 0) s_f[w] = sum;
+  __syncthreads();
+  const float invS = 1.f / (s_f[0] + s_f[1] + s_f[2] + s_f[3]);
+  __syncthreads();
+  if (probs) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int v = i * kThreads + t;
+      if (v < V) probs[(size_t)col * V + v] = expf(x[i] - m) * invS;
+    }
+  }
+  float prev_v = INFINITY;
+  int prev_i = -1;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int v = i * kThreads + t;
+      const bool below = x[i] < prev_v || (x[i] == prev_v && v > prev_i);
+      if (v < V && below && (x[i] > bv || (x[i] == bv && v < bi))) { bv = x[i]; bi = v; }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      const float v2 = __shfl_xor(bv, o);
+      const int i2 = __shfl_xor(bi, o);
+      if (v2 > bv || (v2 == bv && i2 < bi)) { bv = v2; bi = i2; }
+    }
+    if ((t & 63) == 0) { s_f[w] = bv; s_i[w] = bi; }
+    __syncthreads();
+    bv = s_f[0]; bi = s_i[0];
+    for (int q = 1; q < kThreads / kWave; ++q)
+      if (s_f[q] > bv || (s_f[q] == bv && s_i[q] < bi)) { bv = s_f[q]; bi = s_i[q]; }
+    __syncthreads();
+    if (t == 0) {
+      topk_idx[(size_t)col * k + r] = bi;
+      topk_prob[(size_t)col * k + r] = expf(bv - m) * invS;
+    }
+    prev_v = bv;
+    prev_i = bi;
+  }
+}
+
+// Large vocabularies (V > 256 * 128): one workgroup per column (b, j), the row re-read from L2
+// for each pass; softmax and top-k (descending, lower id first on ties).
+__global__ __launch_bounds__(kThreads) void softmax_topk_big_kernel(const float* __restrict__ logits, int H, int V,
                                                                 int k, int32_t* __restrict__ topk_idx,
                                                                 float* __restrict__ topk_prob,
                                                                 float* __restrict__ probs) {
@@ -259,7 +335,12 @@ extern "C" spec_status spec_medusa_heads(const void* h, const void* W_res, const
   else if (cbn == 2) launch(nm, lm_head_kernel<2>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
   else if (cbn == 3) launch(nm, lm_head_kernel<3>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
   else launch(nm, lm_head_kernel<4>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
-  launch("medusa_softmax_topk", softmax_topk_kernel, dim3(NC), blk, s, static_cast<const float*>(logits), H, V,
-         k, topk_idx, topk_prob, draft_probs);
+  const float* lg = logits;
+  const char* nt = "medusa_softmax_topk";
+  if (V <= 16 * kThreads) launch(nt, softmax_topk_kernel<16>, dim3(NC), blk, s, lg, H, V, k, topk_idx, topk_prob, draft_probs);
+  else if (V <= 32 * kThreads) launch(nt, softmax_topk_kernel<32>, dim3(NC), blk, s, lg, H, V, k, topk_idx, topk_prob, draft_probs);
+  else if (V <= 64 * kThreads) launch(nt, softmax_topk_kernel<64>, dim3(NC), blk, s, lg, H, V, k, topk_idx, topk_prob, draft_probs);
+  else if (V <= 128 * kThreads) launch(nt, softmax_topk_kernel<128>, dim3(NC), blk, s, lg, H, V, k, topk_idx, topk_prob, draft_probs);
+  else launch(nt, softmax_topk_big_kernel, dim3(NC), blk, s, lg, H, V, k, topk_idx, topk_prob, draft_probs);
   return launch_status();
 }

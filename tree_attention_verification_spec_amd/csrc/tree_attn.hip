@@ -6,27 +6,37 @@
 //
 // bf16 path (MFMA, gfx950).  A work unit is one (sequence b, key/value head g).  Its query rows
 // are the N tree nodes x the G query heads that share g, M = N * G rows, row r = node r / G,
-// head g * G + r % G.  All of them read the same keys, so each key/value tile is fetched from
-// HBM once per workgroup, staged in LDS and reused by every row of the workgroup.
+// head g * G + r % G.  All of them read the same keys, so each 64-key tile is fetched from HBM
+// once per workgroup (16-byte loads, 16 lanes per 256-byte key row), staged in LDS and reused
+// by every row of the workgroup.
 //
 // Each wave owns 16 * CB query rows.  Scores are computed transposed, S^T = K Q^T, with
-// v_mfma_f32_16x16x32_bf16: A = a 16-key x 32-dim slice of K from LDS, B = Q^T held in
+// v_mfma_f32_16x16x32_bf16: A = a 16-key x 32-dim slice of K read from LDS, B = Q^T held in
 // registers for the whole kernel.  The accumulator layout gives lane l the query row l % 16
-// and keys 4 * (l / 16) + i, which is exactly the B-operand layout of the next product
-// O^T = V^T P^T, so the softmax weights never leave their lanes; V is written transposed into
-// LDS so its A-operand fragments are contiguous.  Every per-row quantity (running max, sum,
-// rescale factor) lives in the lanes of that row, with a two-step xor shuffle for the max.
+// and keys 4 * (l / 16) + i, which is the B-operand layout of the next product
+// O^T = V^T P^T, so the softmax weights never leave their lanes.  V stays row-major in LDS; its
+// A-operand fragments (one output dimension per lane, 8 keys in the slots) come from the LDS
+// transpose read ds_read_b64_tr_b16: within each 16-lane group, lane L reads 4 dimensions of
+// key key0 + L / 4 and lane j receives dimension j of those 4 keys.  Every per-row quantity
+// (running max, sum, rescale) lives in the lanes of that row; the O rescale is skipped for a
+// tile in which no row's max moved.
+//
+// Tiles are double-buffered: the next tile's global loads are issued into registers before
+// the current tile is computed and written to the other LDS buffer afterwards, so there is
+// one barrier per tile and the HBM latency hides behind the MFMA work.  Tiles that lie wholly
+// in the prefix and inside the split skip all masking.
 //
 // Work split: grid = units x row blocks x key splits.  A split covers a contiguous key range
 // of the unit (prefix and tree slots alike), computed on the device from prefix_len and
 // n_nodes.  With more than one split, each workgroup stores its unnormalised partial output
-// and (max, sum) to the workspace; the last workgroup of a (unit, row block) to arrive - found
-// with a device-scope counter - merges them and resets the counter.  Workgroups of one unit
-// are placed on one XCD (dispatch goes round-robin over the 8 XCDs), so the unit's K/V tiles,
-// Q rows and partials share that XCD's L2.
+// and (max, sum) to the workspace and a second kernel merges them (the kernel boundary orders
+// the two; no workgroup waits on another).  Workgroups of one unit are placed on one XCD
+// (dispatch goes round-robin over the 8 XCDs) in both kernels, so the unit's K/V tiles, Q rows
+// and partials share that XCD's L2.
 //
 // fp32 path: a plain exact-fp32 kernel (one workgroup per query row) for small fp32 inputs.
 #include <climits>
+#include <cstdlib>
 
 #include "common.h"
 
@@ -38,6 +48,9 @@ constexpr int kWaves = 4;      // waves per workgroup (bf16 path)
 constexpr int kThreads = kWaves * kWave;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4;
 
 struct AttnArgs {
   const void* q;
@@ -53,10 +66,9 @@ struct AttnArgs {
   float* lse;
   int32_t* err;
   // workspace
-  int* counters;               // [U * R]
   float2* part_ml;             // [U, S, Mpad]
   float* part_o;               // [U, S, Mpad, D]
-  int R, S, Mpad, units_per_xcd;
+  int R, S, Mpad;
 };
 
 __device__ __forceinline__ bool seq_valid(int n, int P, int N, int S_max) {
@@ -85,18 +97,32 @@ __device__ __forceinline__ bool decode_wg(const AttnArgs& a, int& u, int& rb, in
   return u < a.B * a.Hkv;
 }
 
+// A-operand fragment of V^T for output dims [d0, d0 + 16) and keys c32 + {4 lg + s, 16 + 4 lg + s}.
+template <int VS>
+__device__ __forceinline__ bf16x8 v_fragment(const __bf16* vt, int d0, int c32, int lg, int l16) {
+  const __bf16* p0 = vt + (c32 + 4 * lg + (l16 >> 2)) * VS + d0 + 4 * (l16 & 3);
+  const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p0);
+  const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p0 + 16 * VS));
+  typedef short short8_t __attribute__((ext_vector_type(8)));
+  const short8_t both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, both);
+}
+
 template <int D, int CB>
 __global__ __launch_bounds__(kThreads) void tree_attn_bf16_kernel(AttnArgs a) {
-  constexpr int KS = D + 8;          // K tile row stride in LDS (elements)
-  constexpr int VS = kKT + 8;        // transposed V tile row stride in LDS (elements)
+  // LDS row strides (elements): K rows 4 banks apart, V rows 8 banks apart, so the 16-byte K
+  // reads and the 8-byte transpose reads of V meet no bank conflicts within a pass.
+  constexpr int KS = D + 8;
+  constexpr int VS = D + 16;
   constexpr int DS = D / 32;         // 32-dim steps of the score product
   constexpr int DB = D / 16;         // 16-dim blocks of the output
   constexpr int ROWS_WAVE = 16 * CB;
   constexpr int RBS = kWaves * ROWS_WAVE;
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[kKT * KS];
-  __shared__ __attribute__((aligned(16))) __bf16 vt_lds[D * VS];
-  __shared__ int s_last;
-
+  constexpr int CPK = D / 8;         // 16-byte chunks per key row
+  constexpr int KPP = kThreads / CPK;// keys per load pass
+  constexpr int PASSES = kKT / KPP;
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][kKT * KS];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][kKT * VS];
   int u, rb, split;
   if (!decode_wg(a, u, rb, split)) return;
   const int b = u / a.Hkv;
@@ -150,13 +176,8 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16_kernel(AttnArgs a) {
     const int h = g * a.G + r % a.G;
     const __bf16* src = qp + (((size_t)b * a.N + i) * a.Hq + h) * D + 8 * lg;
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      if (row_ok[cb]) {
-        qf[cb][ds] = *reinterpret_cast<const bf16x8*>(src + ds * 32);
-      } else {
-        qf[cb][ds] = bf16x8{};
-      }
-    }
+    for (int ds = 0; ds < DS; ++ds)
+      qf[cb][ds] = row_ok[cb] ? *reinterpret_cast<const bf16x8*>(src + ds * 32) : bf16x8{};
   }
 
   f32x4 o_acc[DB][CB];
@@ -172,27 +193,57 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16_kernel(AttnArgs a) {
   }
 
   const size_t kv_base = ((size_t)b * a.Hkv + g) * (size_t)a.S_max * D;
-  constexpr int CPK = D / 8;               // 16-byte chunks per key row
-  constexpr int KPP = kThreads / CPK;      // keys per load pass
   const int ld_key = tid / CPK;
   const int ld_chunk = tid % CPK;
-
-  for (int t0 = k0; t0 < k1; t0 += kKT) {
-    // ---- stage the tile: K row-major, V transposed; keys past the sequence are zeros.
+  bf16x8 kreg[PASSES], vreg[PASSES];
+  // Next tile into registers, consumed only by the next stage(), so the loads stay in flight
+  // while this tile is computed.  A key past the sequence loads the last valid key instead
+  // (total >= 1 whenever a tile exists): finite data whose score is masked to -inf, so its
+  // weight is exactly 0.
+  auto fetch = [&](int t0) {
 #pragma unroll
-    for (int pass = 0; pass < kKT / KPP; ++pass) {
-      const int key = pass * KPP + ld_key;
-      const int s = t0 + key;
-      bf16x8 kv = bf16x8{}, vv = bf16x8{};
-      if (s < total) {
-        kv = *reinterpret_cast<const bf16x8*>(kp + kv_base + (size_t)s * D + ld_chunk * 8);
-        vv = *reinterpret_cast<const bf16x8*>(vp + kv_base + (size_t)s * D + ld_chunk * 8);
-      }
-      *reinterpret_cast<bf16x8*>(&k_lds[key * KS + ld_chunk * 8]) = kv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vt_lds[(ld_chunk * 8 + e) * VS + key] = vv[e];
+    for (int pass = 0; pass < PASSES; ++pass) {
+      const int s = min(t0 + pass * KPP + ld_key, total - 1);
+      const size_t at = kv_base + (size_t)s * D + ld_chunk * 8;
+      kreg[pass] = *reinterpret_cast<const bf16x8*>(kp + at);
+      vreg[pass] = *reinterpret_cast<const bf16x8*>(vp + at);
     }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+      const int key = pass * KPP + ld_key;
+      *reinterpret_cast<bf16x8*>(&k_lds[buf][key * KS + ld_chunk * 8]) = kreg[pass];
+      *reinterpret_cast<bf16x8*>(&v_lds[buf][key * VS + ld_chunk * 8]) = vreg[pass];
+    }
+  };
+
+  if (k0 < k1) fetch(k0);
+  int buf = 0;
+  for (int t0 = k0; t0 < k1; t0 += kKT) {
+    stage(buf);
     __syncthreads();
+    // Ancestor words for tiles that reach the tree part, issued before the prefetch: the
+    // memory counter drains in order, so a load issued after the prefetch could only be
+    // waited for together with it.  Word indices are clamped; a clamped word is never read
+    // below, since a tree key j always lies in word jw or jw + 1 and j < n <= 64 W.
+    const int jw = (t0 - P) >> 6;                 // floor division (t0 - P may be negative)
+    uint64_t wlo[CB], whi[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) wlo[cb] = whi[cb] = 0;
+    if (t0 + kKT > P) {
+      const int j0 = min(max(jw, 0), a.W - 1), j1 = min(max(jw + 1, 0), a.W - 1);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const uint64_t* mrow = a.mask + ((size_t)b * a.N + min(row_node[cb], a.N - 1)) * a.W;
+        wlo[cb] = mrow[j0];
+        whi[cb] = mrow[j1];
+      }
+    }
+    fetch(t0 + kKT);   // unconditional (past the end it reloads the last key) so no branch
+                       // leaves the compiler unsure how many loads are still in flight
+    const __bf16* kt = k_lds[buf];
+    const __bf16* vt = v_lds[buf];
 
     // ---- S^T = K Q^T for the 64 keys of the tile.
     f32x4 s_acc[4][CB];
@@ -202,49 +253,55 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16_kernel(AttnArgs a) {
       for (int cb = 0; cb < CB; ++cb) s_acc[kb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
-        const bf16x8 af = *reinterpret_cast<const bf16x8*>(&k_lds[(kb * 16 + l16) * KS + ds * 32 + 8 * lg]);
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(&kt[(kb * 16 + l16) * KS + ds * 32 + 8 * lg]);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
           s_acc[kb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[cb][ds], s_acc[kb][cb], 0, 0, 0);
       }
     }
 
-    // ---- mask, online softmax (base 2), pack P^T as bf16 B operands.
-    const bool tree_tile = t0 + kKT > P;         // the tile reaches tree slots
+    // ---- mask (only where needed), online softmax in base 2, P^T packed as bf16.
+    const bool plain = t0 + kKT <= k1 && t0 + kKT <= P;   // wholly prefix, wholly in the split
     bf16x8 pb[2][CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      uint64_t wlo = 0, whi = 0;
-      int jw = 0;
-      if (tree_tile && row_ok[cb]) {
-        jw = (t0 - P) >> 6;                     // floor division (t0 - P may be negative)
-        const uint64_t* mrow = a.mask + ((size_t)b * a.N + row_node[cb]) * a.W;
-        if (jw >= 0 && jw < a.W) wlo = mrow[jw];
-        if (jw + 1 >= 0 && jw + 1 < a.W) whi = mrow[jw + 1];
-      }
       float x[4][4];
+      if (plain) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[kb][e] = row_ok[cb] ? s_acc[kb][cb][e] * a.scale_log2 : -INFINITY;
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int s = t0 + kb * 16 + 4 * lg + e;
+            bool vis = row_ok[cb] && s < k1;
+            if (vis && s >= P) {
+              const int j = s - P;
+              const uint64_t word = ((j >> 6) == jw) ? wlo[cb] : whi[cb];
+              vis = (word >> (j & 63)) & 1ull;
+            }
+            x[kb][e] = vis ? s_acc[kb][cb][e] * a.scale_log2 : -INFINITY;
+          }
+      }
       float mloc = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int s = t0 + kb * 16 + 4 * lg + e;
-          bool vis = row_ok[cb] && s < k1;
-          if (vis && s >= P) {
-            const int j = s - P;
-            const uint64_t word = ((j >> 6) == jw) ? wlo : whi;
-            vis = (word >> (j & 63)) & 1ull;
-          }
-          x[kb][e] = vis ? s_acc[kb][cb][e] * a.scale_log2 : -INFINITY;
-          mloc = fmaxf(mloc, x[kb][e]);
-        }
-      }
+        for (int e = 0; e < 4; ++e) mloc = fmaxf(mloc, x[kb][e]);
       mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
       const float m_new = fmaxf(m_run[cb], mloc);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2f(m_run[cb] - m_use);
-      m_run[cb] = m_new;
+      if (__ballot(m_new > m_run[cb])) {         // some row's max moved: rescale
+        const float alpha = exp2f(m_run[cb] - m_use);
+        l_run[cb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o_acc[db][cb] *= alpha;
+        m_run[cb] = m_new;
+      }
       float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -253,9 +310,7 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16_kernel(AttnArgs a) {
           x[kb][e] = exp2f(x[kb][e] - m_use);
           psum += x[kb][e];
         }
-      l_run[cb] = l_run[cb] * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o_acc[db][cb] *= alpha;
+      l_run[cb] += psum;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         bf16x8 p;
@@ -273,16 +328,13 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16_kernel(AttnArgs a) {
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const __bf16* vrow = &vt_lds[(db * 16 + l16) * VS + c * 32 + 4 * lg];
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 16);
-        const bf16x8 af = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const bf16x8 af = v_fragment<VS>(vt, db * 16, c * 32, lg, l16);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
           o_acc[db][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pb[c][cb], o_acc[db][cb], 0, 0, 0);
       }
     }
-    __syncthreads();
+    buf ^= 1;
   }
 
   // Row sums: lanes l16, l16+16, l16+32, l16+48 hold partial sums of the same row.
@@ -314,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16_kernel(AttnArgs a) {
     return;
   }
 
-  // ---- several splits: store partials, the last workgroup of the (unit, row block) merges.
+  // ---- several splits: store the unnormalised partials; the merge kernel combines them.
   const size_t pbase = ((size_t)u * a.S + split) * a.Mpad;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
@@ -324,44 +376,63 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16_kernel(AttnArgs a) {
     for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(dst + db * 16 + 4 * lg) = o_acc[db][cb];
     if (lg == 0) a.part_ml[pbase + r] = make_float2(row_ok[cb] ? m_run[cb] : -INFINITY, row_ok[cb] ? l_run[cb] : 0.f);
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = atomicAdd(&a.counters[u * a.R + rb], 1);
-    s_last = prev == a.S - 1;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+}
 
+// Merge of the key splits.  One workgroup per (unit, 16 query rows); thread -> (row, 4 output
+// dims); the splits are folded with a running max, loads for 8 splits issued together.
+// Workgroups of a unit run on the unit's XCD (as in the main kernel), where its partials sit
+// in L2.
+template <int D>
+__global__ __launch_bounds__(kThreads) void tree_attn_merge_kernel(AttnArgs a) {
   constexpr int C4 = D / 4;
-  for (int idx = tid; idx < RBS * C4; idx += kThreads) {
-    const int rr = idx / C4;
-    const int d4 = idx - rr * C4;
-    const int r = rb * RBS + rr;
-    if (r >= M) continue;
-    const int i = r / a.G, h = g * a.G + r % a.G;
-    float mmax = -INFINITY;
-    for (int s = 0; s < a.S; ++s) mmax = fmaxf(mmax, a.part_ml[((size_t)u * a.S + s) * a.Mpad + r].x);
-    const float muse = (mmax == -INFINITY) ? 0.f : mmax;
-    float L = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < a.S; ++s) {
-      const size_t pr = ((size_t)u * a.S + s) * a.Mpad + r;
-      const float2 ml = a.part_ml[pr];
-      const float wgt = exp2f(ml.x - muse);
-      L += wgt * ml.y;
-      acc += wgt * *reinterpret_cast<const f32x4*>(a.part_o + pr * D + 4 * d4);
-    }
-    const bool live = i < n && L > 0.f;
-    const float inv = live ? 1.f / L : 0.f;
-    bf16x4 o4;
+  constexpr int ROWS = kThreads / C4;          // rows per workgroup (8 at D = 128)
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7;
+  const int slot = bid >> 3;
+  const int per_unit = a.Mpad / ROWS;
+  const int lu = slot / per_unit;
+  const int u = xcd + 8 * lu;
+  if (u >= a.B * a.Hkv) return;
+  const int r = (slot - lu * per_unit) * ROWS + threadIdx.x / C4;
+  const int d4 = threadIdx.x % C4;
+  const int M = a.N * a.G;
+  if (r >= M) return;
+  const int b = u / a.Hkv, g = u - b * a.Hkv;
+  const int n = a.n_nodes ? a.n_nodes[b] : a.N;
+  const int P = a.prefix_len[b];
+  if (!seq_valid(n, P, a.N, a.S_max)) return;  // the main kernel wrote zeros and the error
+  const int i = r / a.G, h = g * a.G + r % a.G;
+  float mrun = -INFINITY, L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < a.S; s0 += 8) {
+    float2 ml[8];
+    f32x4 po[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[e] * inv);
-    *reinterpret_cast<bf16x4*>(op + (((size_t)b * a.N + i) * a.Hq + h) * D + 4 * d4) = o4;
-    if (a.lse && d4 == 0) a.lse[((size_t)b * a.N + i) * a.Hq + h] = live ? (mmax + log2f(L)) * kLn2 : -INFINITY;
+    for (int k = 0; k < 8; ++k) {
+      const int s = s0 + k < a.S ? s0 + k : 0;
+      const size_t pr = ((size_t)u * a.S + s) * a.Mpad + r;
+      ml[k] = a.part_ml[pr];
+      po[k] = *reinterpret_cast<const f32x4*>(a.part_o + pr * D + 4 * d4);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (s0 + k >= a.S || ml[k].x == -INFINITY) continue;
+      const float mn = fmaxf(mrun, ml[k].x);
+      const float sc_old = exp2f(mrun - mn);   // 0 when mrun = -inf
+      const float sc_new = exp2f(ml[k].x - mn);
+      L = L * sc_old + ml[k].y * sc_new;
+      acc = acc * sc_old + po[k] * sc_new;
+      mrun = mn;
+    }
   }
-  if (tid == 0) a.counters[u * a.R + rb] = 0;
+  const bool live = i < n && L > 0.f;
+  const float inv = live ? 1.f / L : 0.f;
+  bf16x4 o4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[e] * inv);
+  __bf16* op = static_cast<__bf16*>(a.out);
+  *reinterpret_cast<bf16x4*>(op + (((size_t)b * a.N + i) * a.Hq + h) * D + 4 * d4) = o4;
+  if (a.lse && d4 == 0) a.lse[((size_t)b * a.N + i) * a.Hq + h] = live ? (mrun + log2f(L)) * kLn2 : -INFINITY;
 }
 
 // Exact fp32 path: one workgroup of 256 threads per query row (b, node, head).  Keys are taken
@@ -456,23 +527,36 @@ struct Plan {
   int CB, RBS, R, S, Mpad, units, wgs;
 };
 
+int env_int(const char* name, int fallback) {
+  const char* v = std::getenv(name);
+  return (v && *v) ? std::atoi(v) : fallback;
+}
+
+// Launch shape.  Few (sequence, KV head) units -> 16-row waves and more key splits so that all
+// CUs work; many units -> 64-row waves (the K/V tile in LDS serves 4x more rows per read) and
+// few splits.  Every split keeps at least two tiles.  SPECTREE_ATTN_CB / SPECTREE_ATTN_SPLITS
+// override the choice (tuning knobs; results do not depend on them).
 Plan make_plan(int B, int N, int Hq, int Hkv, int D, int S_max) {
   Plan p{};
   const int G = Hq / Hkv;
   const int M = N * G;
   p.units = B * Hkv;
-  p.CB = M >= 192 ? 4 : (M >= 96 ? 2 : 1);
+  const int big = p.units * ((M + 255) / 256) >= 64;
+  p.CB = big ? 4 : 1;
   if (D == 64 && p.CB > 2) p.CB = 2;
+  p.CB = env_int("SPECTREE_ATTN_CB", p.CB);
+  if (p.CB != 1 && p.CB != 2 && p.CB != 4) p.CB = 1;
+  if (D == 64 && p.CB == 4) p.CB = 2;
   p.RBS = kWaves * 16 * p.CB;
   p.R = (M + p.RBS - 1) / p.RBS;
   p.Mpad = p.R * p.RBS;
-  // Enough workgroups to cover the 256 CUs about twice, but keep every split at least four
-  // tiles long so that Q loads and partial stores stay small next to the K/V stream.
-  const int want = (512 + p.units * p.R - 1) / (p.units * p.R);
-  const int max_splits = (S_max + 4 * kKT - 1) / (4 * kKT);
-  p.S = want < 1 ? 1 : want;
-  if (p.S > max_splits) p.S = max_splits;
-  if (p.S < 1) p.S = 1;
+  const int target = big ? 512 : 256;
+  const int tiles = (S_max + kKT - 1) / kKT;
+  int S = (target + p.units * p.R - 1) / (p.units * p.R);
+  S = env_int("SPECTREE_ATTN_SPLITS", S);
+  if (S > tiles / 2) S = tiles / 2;
+  if (S < 1) S = 1;
+  p.S = S;
   const int per_xcd = (p.units + 7) / 8;
   p.wgs = 8 * per_xcd * p.R * p.S;
   return p;
@@ -480,8 +564,7 @@ Plan make_plan(int B, int N, int Hq, int Hkv, int D, int S_max) {
 
 size_t workspace_bytes(const Plan& p, int D) {
   if (p.S == 1) return 0;
-  size_t off = align_up((size_t)p.units * p.R * sizeof(int), 256);
-  off += align_up((size_t)p.units * p.S * p.Mpad * sizeof(float2), 256);
+  size_t off = align_up((size_t)p.units * p.S * p.Mpad * sizeof(float2), 256);
   off += align_up((size_t)p.units * p.S * p.Mpad * D * sizeof(float), 256);
   return off;
 }
@@ -527,12 +610,10 @@ extern "C" spec_status spec_tree_attn(const void* q, const void* k_cache, const 
   const Plan p = make_plan(B, N, Hq, Hkv, head_dim, S_max);
   const size_t need = workspace_bytes(p, head_dim);
   if (need > 0 && (!workspace || ws_bytes < need)) return SPEC_EWORKSPACE;
-  a.R = p.R; a.S = p.S; a.Mpad = p.Mpad; a.units_per_xcd = (p.units + 7) / 8;
+  a.R = p.R; a.S = p.S; a.Mpad = p.Mpad;
   if (p.S > 1) {
     char* w = static_cast<char*>(workspace);
     size_t off = 0;
-    a.counters = reinterpret_cast<int*>(w + off);
-    off += align_up((size_t)p.units * p.R * sizeof(int), 256);
     a.part_ml = reinterpret_cast<float2*>(w + off);
     off += align_up((size_t)p.units * p.S * p.Mpad * sizeof(float2), 256);
     a.part_o = reinterpret_cast<float*>(w + off);
@@ -546,6 +627,12 @@ extern "C" spec_status spec_tree_attn(const void* q, const void* k_cache, const 
   } else {
     if (p.CB == 2) launch(nm, tree_attn_bf16_kernel<64, 2>, grid, block, s, a);
     else launch(nm, tree_attn_bf16_kernel<64, 1>, grid, block, s, a);
+  }
+  if (p.S > 1) {
+    const int rows_per_wg = kThreads / (head_dim / 4);
+    const dim3 mgrid(8 * ((p.units + 7) / 8) * (p.Mpad / rows_per_wg));
+    if (head_dim == 128) launch("tree_attn_merge", tree_attn_merge_kernel<128>, mgrid, block, s, a);
+    else launch("tree_attn_merge", tree_attn_merge_kernel<64>, mgrid, block, s, a);
   }
   return launch_status();
 }
