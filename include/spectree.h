@@ -138,7 +138,7 @@ spec_status spec_tree_assemble(const int32_t* topk_idx, const int32_t* parents,
  *   prefix_len int32 [B]                   P_b
  *   tree_mask  uint64 [B, N, ceil(N/64)]   spec_tree_build's mask
  *   n_nodes    int32 [B]                   optional (NULL = N)
- *   scale      softmax scale (1/sqrt(head_dim) for standard attention)
+ *   scale      softmax scale, positive and finite (1/sqrt(head_dim) for standard attention)
  *   dtype      SPEC_F32 (exact fp32 path) or SPEC_BF16 (MFMA path, fp32 accumulation)
  * Outputs:
  *   out        [B, N, Hq, head_dim] dtype: softmax(scale q.k) v over the visible slots;
@@ -148,8 +148,8 @@ spec_status spec_tree_assemble(const int32_t* topk_idx, const int32_t* parents,
  *   err        int32 [B]            optional (NULL): SPEC_ERR_NNODES / SPEC_ERR_PREFIX
  * Rows of padding nodes, rows that see no slot and all rows of a sequence with an error are 0.
  * Supported: head_dim 64 or 128; Hq % Hkv == 0; N <= 256.
- * Errors: SPEC_EINVAL (sizes, NULL pointers), SPEC_EUNSUPPORTED (head_dim, dtype),
- * SPEC_EWORKSPACE.
+ * Errors: SPEC_EINVAL (sizes, NULL pointers, scale not positive and finite),
+ * SPEC_EUNSUPPORTED (head_dim, dtype), SPEC_EWORKSPACE.
  * ------------------------------------------------------------------------------------ */
 size_t spec_tree_attn_workspace(int B, int N, int Hq, int Hkv, int head_dim, int S_max,
                                 spec_dtype dtype);

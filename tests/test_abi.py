@@ -56,6 +56,8 @@ def test_host_argument_checks(lib):
     assert lib.spec_tree_attn(*args, 1, 10, 8, 2, 96, 100, 0.1, 1, fake, None, None, fake, 1 << 30, None) == 2
     assert lib.spec_tree_attn(*args, 1, 10, 6, 4, 128, 100, 0.1, 1, fake, None, None, fake, 1 << 30, None) == 2
     assert lib.spec_tree_attn(*args, 1, 10, 8, 2, 128, 100, 0.1, 7, fake, None, None, fake, 1 << 30, None) == 2
+    for bad in (0.0, -0.1, float("inf"), float("nan")):   # the scale must be positive and finite
+        assert lib.spec_tree_attn(*args, 1, 10, 8, 2, 128, 100, bad, 1, fake, None, None, fake, 1 << 30, None) == 1
     need = lib.spec_tree_attn_workspace(1, 63, 32, 8, 128, 2111, 1)
     assert need > 0
     assert lib.spec_tree_attn(*args, 1, 63, 32, 8, 128, 2111, 0.1, 1, fake, None, None, None, 0, None) == 3

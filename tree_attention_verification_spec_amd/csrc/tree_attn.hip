@@ -44,8 +44,7 @@ namespace spectree {
 namespace {
 
 constexpr int kKT = 64;        // keys per tile
-constexpr int kWaves = 4;      // waves per workgroup (bf16 path)
-constexpr int kThreads = kWaves * kWave;
+constexpr int kThreads = 256;  // merge kernel workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -108,8 +107,13 @@ __device__ __forceinline__ bf16x8 v_fragment(const __bf16* vt, int d0, int c32, 
   return __builtin_bit_cast(bf16x8, both);
 }
 
-template <int D, int CB>
-__global__ __launch_bounds__(kThreads) void tree_attn_bf16_kernel(AttnArgs a) {
+// WAVES waves per workgroup, 16 * CB query rows per wave.  Two waves per SIMD are requested
+// (at most 256 registers per lane): while one wave runs its softmax on the VALU the other
+// keeps the matrix cores busy.
+template <int D, int CB, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void tree_attn_bf16_kernel(AttnArgs a) {
+  constexpr int THREADS = WAVES * kWave;
   // LDS row strides (elements): K rows 4 banks apart, V rows 8 banks apart, so the 16-byte K
   // reads and the 8-byte transpose reads of V meet no bank conflicts within a pass.
   constexpr int KS = D + 8;
@@ -117,9 +121,9 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16_kernel(AttnArgs a) {
   constexpr int DS = D / 32;         // 32-dim steps of the score product
   constexpr int DB = D / 16;         // 16-dim blocks of the output
   constexpr int ROWS_WAVE = 16 * CB;
-  constexpr int RBS = kWaves * ROWS_WAVE;
+  constexpr int RBS = WAVES * ROWS_WAVE;
   constexpr int CPK = D / 8;         // 16-byte chunks per key row
-  constexpr int KPP = kThreads / CPK;// keys per load pass
+  constexpr int KPP = THREADS / CPK; // keys per load pass
   constexpr int PASSES = kKT / KPP;
   __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][kKT * KS];
   __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][kKT * VS];
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16_kernel(AttnArgs a) {
   if (!seq_valid(n, P, a.N, a.S_max)) {
     if (split == 0) {
       if (a.err && g == 0 && rb == 0 && tid == 0) a.err[b] = seq_err(n, P, a.N, a.S_max);
-      for (int idx = tid; idx < RBS * D; idx += kThreads) {
+      for (int idx = tid; idx < RBS * D; idx += THREADS) {
         const int r = rb * RBS + idx / D;
         if (r >= M) continue;
         const int i = r / a.G, h = g * a.G + r % a.G;
@@ -260,18 +264,20 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16_kernel(AttnArgs a) {
       }
     }
 
-    // ---- mask (only where needed), online softmax in base 2, P^T packed as bf16.
+    // ---- mask (only where needed), online softmax in base 2, P^T packed as bf16.  The max is
+    // taken on raw scores (the scale is positive, so it commutes with the max) and each weight
+    // is exp2(s * scale_log2 - m) with one FMA.  Rows past the workload have Q = 0 and are
+    // discarded at the end, so wholly-prefix tiles need no per-score select.
     const bool plain = t0 + kKT <= k1 && t0 + kKT <= P;   // wholly prefix, wholly in the split
     bf16x8 pb[2][CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       float x[4][4];
-      if (plain) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[kb][e] = row_ok[cb] ? s_acc[kb][cb][e] * a.scale_log2 : -INFINITY;
-      } else {
+        for (int e = 0; e < 4; ++e) x[kb][e] = s_acc[kb][cb][e];
+      if (!plain) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -283,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16_kernel(AttnArgs a) {
               const uint64_t word = ((j >> 6) == jw) ? wlo[cb] : whi[cb];
               vis = (word >> (j & 63)) & 1ull;
             }
-            x[kb][e] = vis ? s_acc[kb][cb][e] * a.scale_log2 : -INFINITY;
+            if (!vis) x[kb][e] = -INFINITY;
           }
       }
       float mloc = -INFINITY;
@@ -293,10 +299,10 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16_kernel(AttnArgs a) {
         for (int e = 0; e < 4; ++e) mloc = fmaxf(mloc, x[kb][e]);
       mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const float m_new = fmaxf(m_run[cb], mloc);
+      const float m_new = fmaxf(m_run[cb], mloc * a.scale_log2);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       if (__ballot(m_new > m_run[cb])) {         // some row's max moved: rescale
-        const float alpha = exp2f(m_run[cb] - m_use);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_use);
         l_run[cb] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) o_acc[db][cb] *= alpha;
@@ -307,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16_kernel(AttnArgs a) {
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          x[kb][e] = exp2f(x[kb][e] - m_use);
+          x[kb][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][e], a.scale_log2, -m_use));
           psum += x[kb][e];
         }
       l_run[cb] += psum;
@@ -418,8 +424,8 @@ __global__ __launch_bounds__(kThreads) void tree_attn_merge_kernel(AttnArgs a) {
     for (int k = 0; k < 8; ++k) {
       if (s0 + k >= a.S || ml[k].x == -INFINITY) continue;
       const float mn = fmaxf(mrun, ml[k].x);
-      const float sc_old = exp2f(mrun - mn);   // 0 when mrun = -inf
-      const float sc_new = exp2f(ml[k].x - mn);
+      const float sc_old = __builtin_amdgcn_exp2f(mrun - mn);   // 0 when mrun = -inf
+      const float sc_new = __builtin_amdgcn_exp2f(ml[k].x - mn);
       L = L * sc_old + ml[k].y * sc_new;
       acc = acc * sc_old + po[k] * sc_new;
       mrun = mn;
@@ -524,7 +530,7 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnArgs a) {
 }
 
 struct Plan {
-  int CB, RBS, R, S, Mpad, units, wgs;
+  int CB, WAVES, RBS, R, S, Mpad, units, wgs;
 };
 
 int env_int(const char* name, int fallback) {
@@ -532,22 +538,22 @@ int env_int(const char* name, int fallback) {
   return (v && *v) ? std::atoi(v) : fallback;
 }
 
-// Launch shape.  Few (sequence, KV head) units -> 16-row waves and more key splits so that all
-// CUs work; many units -> 64-row waves (the K/V tile in LDS serves 4x more rows per read) and
-// few splits.  Every split keeps at least two tiles.  SPECTREE_ATTN_CB / SPECTREE_ATTN_SPLITS
-// override the choice (tuning knobs; results do not depend on them).
+// Launch shape.  Few (sequence, KV head) units -> 64-row workgroups (4 waves of 16 rows) and
+// more key splits so that all CUs work; many units -> 256-row workgroups (8 waves of 32 rows:
+// the K/V tile in LDS serves 4x more rows per read) and few splits.  Every split keeps at
+// least two tiles.  SPECTREE_ATTN_CB, SPECTREE_ATTN_WAVES and SPECTREE_ATTN_SPLITS override the
+// choice (tuning knobs; results do not depend on them).
 Plan make_plan(int B, int N, int Hq, int Hkv, int D, int S_max) {
   Plan p{};
   const int G = Hq / Hkv;
   const int M = N * G;
   p.units = B * Hkv;
   const int big = p.units * ((M + 255) / 256) >= 64;
-  p.CB = big ? 4 : 1;
-  if (D == 64 && p.CB > 2) p.CB = 2;
-  p.CB = env_int("SPECTREE_ATTN_CB", p.CB);
-  if (p.CB != 1 && p.CB != 2 && p.CB != 4) p.CB = 1;
-  if (D == 64 && p.CB == 4) p.CB = 2;
-  p.RBS = kWaves * 16 * p.CB;
+  p.CB = env_int("SPECTREE_ATTN_CB", big ? 2 : 1);
+  p.WAVES = env_int("SPECTREE_ATTN_WAVES", big ? 8 : 4);
+  if (p.CB != 1 && p.CB != 2) p.CB = 1;
+  if (p.WAVES != 4 && p.WAVES != 8) p.WAVES = 4;
+  p.RBS = p.WAVES * 16 * p.CB;
   p.R = (M + p.RBS - 1) / p.RBS;
   p.Mpad = p.R * p.RBS;
   const int target = big ? 512 : 256;
@@ -560,6 +566,19 @@ Plan make_plan(int B, int N, int Hq, int Hkv, int D, int S_max) {
   const int per_xcd = (p.units + 7) / 8;
   p.wgs = 8 * per_xcd * p.R * p.S;
   return p;
+}
+
+template <int D>
+void launch_bf16(const Plan& p, const AttnArgs& a, hipStream_t s) {
+  const dim3 grid(p.wgs);
+  const char* nm = "tree_attn_bf16";
+  if (p.WAVES == 8) {
+    if (p.CB == 2) launch(nm, tree_attn_bf16_kernel<D, 2, 8>, grid, dim3(8 * kWave), s, a);
+    else launch(nm, tree_attn_bf16_kernel<D, 1, 8>, grid, dim3(8 * kWave), s, a);
+  } else {
+    if (p.CB == 2) launch(nm, tree_attn_bf16_kernel<D, 2, 4>, grid, dim3(4 * kWave), s, a);
+    else launch(nm, tree_attn_bf16_kernel<D, 1, 4>, grid, dim3(4 * kWave), s, a);
+  }
 }
 
 size_t workspace_bytes(const Plan& p, int D) {
@@ -591,7 +610,7 @@ extern "C" spec_status spec_tree_attn(const void* q, const void* k_cache, const 
   if (Hq % Hkv != 0) return SPEC_EUNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return SPEC_EUNSUPPORTED;
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EUNSUPPORTED;
-  if (!(scale == scale)) return SPEC_EINVAL;
+  if (!(scale > 0.f) || !(scale < INFINITY)) return SPEC_EINVAL;   // positive and finite
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   AttnArgs a{};
@@ -618,21 +637,13 @@ extern "C" spec_status spec_tree_attn(const void* q, const void* k_cache, const 
     off += align_up((size_t)p.units * p.S * p.Mpad * sizeof(float2), 256);
     a.part_o = reinterpret_cast<float*>(w + off);
   }
-  const dim3 grid(p.wgs), block(kThreads);
-  const char* nm = "tree_attn_bf16";
-  if (head_dim == 128) {
-    if (p.CB == 4) launch(nm, tree_attn_bf16_kernel<128, 4>, grid, block, s, a);
-    else if (p.CB == 2) launch(nm, tree_attn_bf16_kernel<128, 2>, grid, block, s, a);
-    else launch(nm, tree_attn_bf16_kernel<128, 1>, grid, block, s, a);
-  } else {
-    if (p.CB == 2) launch(nm, tree_attn_bf16_kernel<64, 2>, grid, block, s, a);
-    else launch(nm, tree_attn_bf16_kernel<64, 1>, grid, block, s, a);
-  }
+  if (head_dim == 128) launch_bf16<128>(p, a, s);
+  else launch_bf16<64>(p, a, s);
   if (p.S > 1) {
     const int rows_per_wg = kThreads / (head_dim / 4);
     const dim3 mgrid(8 * ((p.units + 7) / 8) * (p.Mpad / rows_per_wg));
-    if (head_dim == 128) launch("tree_attn_merge", tree_attn_merge_kernel<128>, mgrid, block, s, a);
-    else launch("tree_attn_merge", tree_attn_merge_kernel<64>, mgrid, block, s, a);
+    if (head_dim == 128) launch("tree_attn_merge", tree_attn_merge_kernel<128>, mgrid, dim3(kThreads), s, a);
+    else launch("tree_attn_merge", tree_attn_merge_kernel<64>, mgrid, dim3(kThreads), s, a);
   }
   return launch_status();
 }
