@@ -87,54 +87,78 @@ struct VerifyArgs {
 };
 
 // ------------------------------------------------------------------ reductions
+//
+// Every sum of exponentials is formed against a maximum that is known first, so no reduction
+// step needs an exponential: block max (lowest index among equal maxima) in fp32, then fp32
+// exp(x - max) summed in fp64.
 
-__device__ __forceinline__ void combine(double& S, double& A, float& m, int& am, double S2, double A2,
-                                        float m2, int am2) {
-  if (m2 > m || (m2 == m && am2 < am)) {
-    const double sc = (m == -INFINITY) ? 0.0 : exp((double)m - (double)m2);
-    const double d = (m == -INFINITY) ? 0.0 : (double)m - (double)m2;
-    A = sc * (A + d * S) + A2;
-    S = sc * S + S2;
-    m = m2;
-    am = am2;
-  } else {
-    const double sc = (m2 == -INFINITY) ? 0.0 : exp((double)m2 - (double)m);
-    const double d = (m2 == -INFINITY) ? 0.0 : (double)m2 - (double)m;
-    A = A + sc * (A2 + d * S2);
-    S = S + sc * S2;
-  }
-}
+constexpr int kWavesPB = kThreads / kWave;
 
-// Block-wide reduction of (S, A, m, argmax, nonfinite); the result is returned to every thread.
-__device__ void block_combine(double& S, double& A, float& m, int& am, int& nf) {
-  __shared__ double sS[kThreads / kWave], sA[kThreads / kWave];
-  __shared__ float sm[kThreads / kWave];
-  __shared__ int sam[kThreads / kWave], snf[kThreads / kWave];
+// Max with the lowest index among equal maxima, and OR of the nonfinite flags, over the block;
+// the result is returned to every thread.  NaN never compares greater, so it never wins (the
+// nonfinite flag reports it).
+__device__ void block_argmax(float& m, int& am, int& nf) {
+  __shared__ float sm[kWavesPB];
+  __shared__ int sam[kWavesPB], snf[kWavesPB];
+#pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    const double S2 = __shfl_xor(S, o), A2 = __shfl_xor(A, o);
     const float m2 = __shfl_xor(m, o);
     const int am2 = __shfl_xor(am, o), nf2 = __shfl_xor(nf, o);
-    combine(S, A, m, am, S2, A2, m2, am2);
+    if (m2 > m || (m2 == m && am2 < am)) { m = m2; am = am2; }
     nf |= nf2;
   }
   const int w = threadIdx.x >> 6;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) { sS[w] = S; sA[w] = A; sm[w] = m; sam[w] = am; snf[w] = nf; }
+  if ((threadIdx.x & 63) == 0) { sm[w] = m; sam[w] = am; snf[w] = nf; }
   __syncthreads();
-  S = sS[0]; A = sA[0]; m = sm[0]; am = sam[0]; nf = snf[0];
-  for (int k = 1; k < kThreads / kWave; ++k) {
-    combine(S, A, m, am, sS[k], sA[k], sm[k], sam[k]);
+  m = sm[0]; am = sam[0]; nf = snf[0];
+#pragma unroll
+  for (int k = 1; k < kWavesPB; ++k) {
+    if (sm[k] > m || (sm[k] == m && sam[k] < am)) { m = sm[k]; am = sam[k]; }
     nf |= snf[k];
   }
 }
 
+// Block sums of two fp64 values, returned to every thread.
+__device__ void block_sum2(double& x, double& y) {
+  __shared__ double sx[kWavesPB], sy[kWavesPB];
+  x = wave_sum(x);
+  y = wave_sum(y);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) { sx[w] = x; sy[w] = y; }
+  __syncthreads();
+  x = sx[0]; y = sy[0];
+#pragma unroll
+  for (int k = 1; k < kWavesPB; ++k) { x += sx[k]; y += sy[k]; }
+}
+
 __device__ double block_sum(double v) {
-  __shared__ double s[kThreads / kWave];
-  v = wave_sum(v);
+  double dummy = 0.0;
+  block_sum2(v, dummy);
+  return v;
+}
+
+// Inclusive prefix sum in thread order (fp64); `total` receives the block sum.
+__device__ double block_scan(double v, double& total) {
+  __shared__ double sw[kWavesPB];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = v;
+  if (lane == kWave - 1) sw[w] = v;
   __syncthreads();
-  return s[0] + s[1] + s[2] + s[3];
+  double off = 0.0;
+  total = 0.0;
+#pragma unroll
+  for (int k = 0; k < kWavesPB; ++k) {
+    if (k < w) off += sw[k];
+    total += sw[k];
+  }
+  return v + off;
 }
 
 // ------------------------------------------------------------------ chunk loads
@@ -188,6 +212,7 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(VerifyArgs a) {
   const int hi = min(a.V, lo + kRowChunk);
   float x[kRowPer];
   load_chunk<VEC>(row, lo, hi, x);
+  // chunk max (lowest index: a thread's slots run in increasing token order), nonfinite flag
   float m = -INFINITY;
   int am = INT_MAX, nf = 0;
 #pragma unroll
@@ -195,9 +220,10 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(VerifyArgs a) {
     const int idx = chunk_index<VEC>(lo, k);
     if (idx < hi) {
       nf |= !isfinite(x[k]);
-      if (x[k] > m || (x[k] == m && idx < am)) { m = x[k]; am = idx; }
+      if (x[k] > m) { m = x[k]; am = idx; }
     }
   }
+  block_argmax(m, am, nf);
   double S = 0.0, A = 0.0;
   if (m != -INFINITY && !nf) {
 #pragma unroll
@@ -208,8 +234,8 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(VerifyArgs a) {
       A += (ex > 0.f) ? (double)ex * (double)d : 0.0;
     }
   }
+  block_sum2(S, A);
   if (am == INT_MAX) m = -INFINITY;
-  block_combine(S, A, m, am, nf);
   if (t == 0) a.rowparts[((size_t)b * a.N + p) * a.CR + c] = RowPart{S, A, m, am, nf, 0};
 }
 
@@ -298,27 +324,47 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
     s_dep[c] = depth;
   }
 
-  // ---- statistics of the rows that have children: merge their chunks
+  // ---- statistics of the rows that have children: merge their chunks.  Max first, then
+  // S = sum_c S_c e^(m_c - M) and A = sum_c e^(m_c - M) (A_c + (m_c - M) S_c); the chunk
+  // exponentials are independent of one another.
   if (has) {
-    double S = 0.0, A = 0.0;
+    const RowPart* rp = a.rowparts + ((size_t)b * a.N + c) * a.CR;
     float m = -INFINITY;
     int am = INT_MAX, nf = 0;
+    auto upd = [&](const RowPart& r) {
+      nf |= r.nonfinite;
+      if (r.m > m || (r.m == m && r.argmax < am)) { m = r.m; am = r.argmax; }
+    };
 #pragma unroll
-    for (int k = 0; k < kMaxRowChunks; ++k) {
-      if (k >= a.CR) break;
-      nf |= q[k].nonfinite;
-      combine(S, A, m, am, q[k].S, q[k].A, q[k].m, q[k].argmax);
+    for (int k = 0; k < kMaxRowChunks; ++k)
+      if (k < a.CR) upd(q[k]);
+    for (int k0 = kMaxRowChunks; k0 < a.CR; k0 += kMaxRowChunks) {   // V > 8 chunks: further batches
+      RowPart r[kMaxRowChunks];
+#pragma unroll
+      for (int k = 0; k < kMaxRowChunks; ++k) r[k] = rp[k0 + k < a.CR ? k0 + k : 0];
+#pragma unroll
+      for (int k = 0; k < kMaxRowChunks; ++k)
+        if (k0 + k < a.CR) upd(r[k]);
     }
-    // vocabularies beyond kMaxRowChunks * kRowChunk: further batches
-    const RowPart* rp = a.rowparts + ((size_t)b * a.N + c) * a.CR;
-    for (int k0 = kMaxRowChunks; k0 < a.CR; k0 += kMaxRowChunks) {
+    double S = 0.0, A = 0.0;
+    auto add = [&](const RowPart& r) {
+      if (r.m == -INFINITY) return;
+      const double d = (double)r.m - (double)m;
+      const double sc = exp(d);
+      S += sc * r.S;
+      A += sc * (r.A + d * r.S);
+    };
+    if (m != -INFINITY && !nf) {
 #pragma unroll
-      for (int k = 0; k < kMaxRowChunks; ++k) q[k] = rp[k0 + k < a.CR ? k0 + k : 0];
+      for (int k = 0; k < kMaxRowChunks; ++k)
+        if (k < a.CR) add(q[k]);
+      for (int k0 = kMaxRowChunks; k0 < a.CR; k0 += kMaxRowChunks) {
+        RowPart r[kMaxRowChunks];
 #pragma unroll
-      for (int k = 0; k < kMaxRowChunks; ++k) {
-        if (k0 + k >= a.CR) break;
-        nf |= q[k].nonfinite;
-        combine(S, A, m, am, q[k].S, q[k].A, q[k].m, q[k].argmax);
+        for (int k = 0; k < kMaxRowChunks; ++k) r[k] = rp[k0 + k < a.CR ? k0 + k : 0];
+#pragma unroll
+        for (int k = 0; k < kMaxRowChunks; ++k)
+          if (k0 + k < a.CR) add(r[k]);
       }
     }
     if (nf) atomicMin(&s_err, err_word(c, SPEC_ERR_NONFINITE));
@@ -411,6 +457,7 @@ __device__ __forceinline__ double draft_at(const VerifyArgs& a, int b, int r, in
   return (double)a.draft[((size_t)b * a.R + r) * a.Vd + v];
 }
 
+template <int VEC>
 __global__ __launch_bounds__(kThreads) void bonus_kernel(VerifyArgs a) {
   const int c = blockIdx.x % a.C, b = blockIdx.x / a.C;
   const BonusPlan pl = a.plans[b];
@@ -418,48 +465,44 @@ __global__ __launch_bounds__(kThreads) void bonus_kernel(VerifyArgs a) {
   const float* row = a.logits + ((size_t)b * a.N + pl.m) * a.V;
   const int lo = c * a.CS, hi = min(a.V, lo + a.CS);
   float x[kPer];
-  load_chunk<1>(row, lo, hi, x);
+  load_chunk<VEC>(row, lo, hi, x);
+  double dr[kPer];
+  if (pl.kind == 3) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int v = chunk_index<VEC>(lo, k);
+      dr[k] = draft_at(a, b, pl.r, v < hi ? v : lo);
+    }
+  }
   float m = -INFINITY;
   int am = INT_MAX, nf = 0;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const int idx = chunk_index<1>(lo, k);
+    const int idx = chunk_index<VEC>(lo, k);
     if (idx < hi) {
       nf |= !isfinite(x[k]);
-      if (x[k] > m || (x[k] == m && idx < am)) { m = x[k]; am = idx; }
+      if (x[k] > m) { m = x[k]; am = idx; }
     }
   }
-  double S = 0.0, Q = 0.0, dummy = 0.0;
-  if (pl.kind == 3) {
+  block_argmax(m, am, nf);                 // chunk max / argmax / nonfinite, in every thread
+  double S = 0.0, Q = 0.0;
+  if (!nf && pl.kind == 3) {
     // exp(x - M) with the row max, and relu(T - D) with T normalised by the row statistics
-    m = pl.M;
-    double d[kPer];
+    const double inv = 1.0 / pl.S;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-      const int v = chunk_index<1>(lo, k);
-      d[k] = draft_at(a, b, pl.r, v < hi ? v : lo);
-    }
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int v = chunk_index<1>(lo, k);
-      if (v < hi && !nf) {
-        const double e = exp((double)x[k] - (double)m);
+      if (chunk_index<VEC>(lo, k) < hi) {
+        const double e = exp((double)x[k] - (double)pl.M);
         S += e;
-        Q += fmax(e / pl.S - d[k], 0.0);
+        Q += fmax(e * inv - dr[k], 0.0);
       }
     }
-    Q = block_sum(Q);
-    S = block_sum(S);
-    int nf2 = nf;
-    nf = __syncthreads_or(nf2);
-  } else {
-    block_combine(S, dummy, m, am, nf);    // chunk max / argmax / nonfinite, in every thread
-    if (!nf && pl.kind == 2 && m != -INFINITY) {
+  } else if (!nf && pl.kind == 2 && m != -INFINITY) {
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) S += (x[k] == -INFINITY) ? 0.0 : exp((double)x[k] - (double)m);
-    }
-    S = block_sum(S);
+    for (int k = 0; k < kPer; ++k) S += (x[k] == -INFINITY) ? 0.0 : exp((double)x[k] - (double)m);
   }
+  block_sum2(S, Q);
+  if (pl.kind == 3) m = pl.M;              // S is relative to the row max
   if (threadIdx.x == 0) a.bparts[(size_t)b * a.C + c] = BonusPart{S, Q, m, am, nf, 0};
 }
 
@@ -473,20 +516,29 @@ __device__ __forceinline__ double draw_weight(const VerifyArgs& a, int b, int ki
 }
 
 // Smallest token of chunk [lo, hi) whose running sum (from `base`, fp64, ascending token order)
-// exceeds thr; -1 if none.  Thread t owns a contiguous run of the chunk.
+// exceeds thr; -1 if none.  Thread t owns a contiguous run of `per` tokens (a multiple of VEC,
+// so the run is read with VEC-wide loads).
+template <int VEC>
 __device__ int scan_chunk(const VerifyArgs& a, int b, int kind, int r, const float* row, int lo, int hi,
                           float M, double S, double base, double thr) {
-  __shared__ double s_pre[kThreads];
   __shared__ int s_hit;
-  const int per = (hi - lo + kThreads - 1) / kThreads;   // <= kPer
+  const int per = (hi - lo + kThreads * VEC - 1) / (kThreads * VEC) * VEC;   // <= kPer
   const int my_lo = lo + (int)threadIdx.x * per;
   float xv[kPer];
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
+  for (int k = 0; k < kPer; k += VEC) {
     const int v = my_lo + k;
     const bool in = k < per && v < hi;
-    const float val = row[in ? v : lo];
-    xv[k] = val;
+    const int at = in ? v : lo;
+    if (VEC == 4) {
+      const float4 v4 = *reinterpret_cast<const float4*>(row + at);
+      xv[k] = v4.x;
+      xv[k + (VEC > 1 ? 1 : 0)] = v4.y;
+      xv[k + (VEC > 2 ? 2 : 0)] = v4.z;
+      xv[k + (VEC > 3 ? 3 : 0)] = v4.w;
+    } else {
+      xv[k] = row[at];
+    }
   }
   double w[kPer];
   double mine = 0.0;
@@ -496,18 +548,9 @@ __device__ int scan_chunk(const VerifyArgs& a, int b, int kind, int r, const flo
     w[k] = (k < per && v < hi) ? draw_weight(a, b, kind, r, xv[k], v, M, S) : 0.0;
     mine += w[k];
   }
-  __syncthreads();
   if (threadIdx.x == 0) s_hit = INT_MAX;
-  s_pre[threadIdx.x] = mine;
-  __syncthreads();
-  // inclusive scan of the per-thread sums in thread order
-  for (int o = 1; o < kThreads; o <<= 1) {
-    const double add = (int)threadIdx.x >= o ? s_pre[threadIdx.x - o] : 0.0;
-    __syncthreads();
-    s_pre[threadIdx.x] += add;
-    __syncthreads();
-  }
-  const double before = base + (threadIdx.x ? s_pre[threadIdx.x - 1] : 0.0);
+  double total;
+  const double before = base + (block_scan(mine, total) - mine);   // barriers inside
   if (before + mine > thr) {
     double run = before;
 #pragma unroll
@@ -522,33 +565,33 @@ __device__ int scan_chunk(const VerifyArgs& a, int b, int kind, int r, const flo
   return hit == INT_MAX ? -1 : hit;
 }
 
-// Chunk holding thr among the fp64 chunk sums q[0..C), and the sum before it.
-__device__ int pick_chunk(const double* q, int C, double thr, double& base) {
-  double acc = 0.0, acc_last = 0.0;
-  int last = 0;
-  for (int k = 0; k < C; ++k) {
-    if (acc + q[k] > thr) { base = acc; return k; }
-    if (q[k] > 0.0) { last = k; acc_last = acc; }
-    acc += q[k];
-  }
-  base = acc_last;                          // rounding put thr past the end
-  return last;
-}
-
-// Inverse-CDF draw with u = uniforms[b, 0] over the weights of `kind`, given their chunk sums.
-__device__ int draw(const VerifyArgs& a, int b, int kind, int r, const float* row, const double* q, float M,
+// Inverse-CDF draw with u = uniforms[b, 0] over the weights of `kind`; thread t < C holds the
+// sum q of chunk t.  The chunk is the first whose inclusive prefix exceeds u * Z (if rounding
+// puts u * Z past the end: the last chunk of positive mass), then the token inside it.
+template <int VEC>
+__device__ int draw(const VerifyArgs& a, int b, int kind, int r, const float* row, double q, float M,
                     double S) {
-  __shared__ int s_tok;
-  double Z = 0.0;
-  for (int k = 0; k < a.C; ++k) Z += q[k];
-  const double u = (double)a.uniforms[(size_t)b * a.N];
-  const double thr = u * Z;
-  double base;
-  const int cs = pick_chunk(q, a.C, thr, base);
+  __shared__ int s_pick, s_last, s_tok;
+  __shared__ double s_base[2];
+  const int t = threadIdx.x;
+  if (t >= a.C) q = 0.0;
+  if (t == 0) { s_pick = INT_MAX; s_last = -1; }
+  double Z;
+  const double incl = block_scan(q, Z);                           // barriers inside
+  const double thr = (double)a.uniforms[(size_t)b * a.N] * Z;
+  if (t < a.C && incl > thr) atomicMin(&s_pick, t);
+  if (t < a.C && q > 0.0) atomicMax(&s_last, t);
+  __syncthreads();
+  const int pick = s_pick, last = s_last;
+  if (t == pick) s_base[0] = incl - q;
+  if (t == last) s_base[1] = incl - q;
+  __syncthreads();
+  const int cs = pick != INT_MAX ? pick : (last >= 0 ? last : 0);
+  const double base = pick != INT_MAX ? s_base[0] : (last >= 0 ? s_base[1] : 0.0);
   const int lo = cs * a.CS, hi = min(a.V, lo + a.CS);
-  int tok = scan_chunk(a, b, kind, r, row, lo, hi, M, S, base, thr);
+  int tok = scan_chunk<VEC>(a, b, kind, r, row, lo, hi, M, S, base, thr);
   if (tok < 0) {                            // rounding put thr at the chunk's end
-    if (threadIdx.x == 0) {
+    if (t == 0) {
       s_tok = -1;
       for (int v = hi - 1; v >= lo; --v)
         if (draw_weight(a, b, kind, r, row[v], v, M, S) > 0.0) { s_tok = v; break; }
@@ -559,23 +602,23 @@ __device__ int draw(const VerifyArgs& a, int b, int kind, int r, const float* ro
   return tok;
 }
 
+template <int VEC>
 __global__ __launch_bounds__(kThreads) void select_kernel(VerifyArgs a) {
-  __shared__ double s_q[kThreads];
   const int b = blockIdx.x;
   const BonusPlan pl = a.plans[b];
   if (pl.kind == 0) return;
   const int t = threadIdx.x;
-  // merge the chunk parts (one per thread)
-  double S = 0.0, dummy = 0.0, Qc = 0.0;
-  float m = -INFINITY;
-  int am = INT_MAX, nf = 0;
+  // merge the chunk parts (one per thread): row max / argmax / nonfinite
+  double Sc = 0.0, Qc = 0.0;
+  float mc = -INFINITY;
+  int amc = INT_MAX, nf = 0;
   if (t < a.C) {
     const BonusPart bp = a.bparts[(size_t)b * a.C + t];
-    S = bp.S; Qc = bp.Q; m = bp.m; am = bp.argmax; nf = bp.nonfinite;
+    Sc = bp.S; Qc = bp.Q; mc = bp.m; amc = bp.argmax; nf = bp.nonfinite;
   }
-  const double Sc = S;
-  const float mc = m;
-  block_combine(S, dummy, m, am, nf);
+  float m = mc;
+  int am = amc;
+  block_argmax(m, am, nf);
   if (nf) {
     write_neutral(a, b, err_word(pl.m, SPEC_ERR_NONFINITE));
     return;
@@ -587,22 +630,12 @@ __global__ __launch_bounds__(kThreads) void select_kernel(VerifyArgs a) {
   const float* row = a.logits + ((size_t)b * a.N + pl.m) * a.V;
   int tok;
   if (pl.kind == 2) {
-    if (t < a.C) s_q[t] = (mc == -INFINITY) ? 0.0 : Sc * exp((double)mc - (double)m);
-    __syncthreads();
-    tok = draw(a, b, 2, pl.r, row, s_q, m, S);
+    const double q = (mc == -INFINITY) ? 0.0 : Sc * exp((double)mc - (double)m);
+    tok = draw<VEC>(a, b, 2, pl.r, row, q, m, 0.0);
   } else {
-    if (t < a.C) s_q[t] = Qc;
-    __syncthreads();
-    double Z = 0.0;
-    for (int k = 0; k < a.C; ++k) Z += s_q[k];
-    if (Z > 0.0) {
-      tok = draw(a, b, 3, pl.r, row, s_q, pl.M, pl.S);
-    } else {                                // residual of zero mass: draw from T_m
-      __syncthreads();
-      if (t < a.C) s_q[t] = Sc;             // chunk sums of exp(x - M), M the row max
-      __syncthreads();
-      tok = draw(a, b, 2, pl.r, row, s_q, pl.M, pl.S);
-    }
+    const double Z = block_sum(t < a.C ? Qc : 0.0);
+    if (Z > 0.0) tok = draw<VEC>(a, b, 3, pl.r, row, Qc, pl.M, pl.S);
+    else tok = draw<VEC>(a, b, 2, pl.r, row, Sc, pl.M, pl.S);   // residual of zero mass: T_m
   }
   if (t == 0) a.bonus[b] = tok;
 }
@@ -673,10 +706,17 @@ extern "C" spec_status spec_verify(const float* target_logits, const float* draf
 
   const dim3 blk(kThreads);
   const dim3 grid_rows((unsigned)((size_t)L.CR * N * B)), grid_chunks((unsigned)((size_t)L.C * B));
-  if (V % 4 == 0) launch("verify_rows", rows_kernel<4>, grid_rows, blk, s, a);
+  // 16-byte loads need rows that start on 16-byte boundaries
+  const bool vec4 = V % 4 == 0 && (reinterpret_cast<uintptr_t>(target_logits) & 15) == 0;
+  if (vec4) launch("verify_rows", rows_kernel<4>, grid_rows, blk, s, a);
   else launch("verify_rows", rows_kernel<1>, grid_rows, blk, s, a);
   launch("verify_decide", decide_kernel, dim3(B), blk, s, a);
-  launch("verify_bonus", bonus_kernel, grid_chunks, blk, s, a);
-  launch("verify_select", select_kernel, dim3(B), blk, s, a);
+  if (vec4) {
+    launch("verify_bonus", bonus_kernel<4>, grid_chunks, blk, s, a);
+    launch("verify_select", select_kernel<4>, dim3(B), blk, s, a);
+  } else {
+    launch("verify_bonus", bonus_kernel<1>, grid_chunks, blk, s, a);
+    launch("verify_select", select_kernel<1>, dim3(B), blk, s, a);
+  }
   return launch_status();
 }
