@@ -149,140 +149,225 @@ __global__ __launch_bounds__(kThreads) void lm_head_kernel(const __bf16* __restr
   }
 }
 
-// One workgroup per column (b, j): the whole logits row is held in registers (PER values per
-// thread, loaded branch-free and all in flight), then max, normaliser, probabilities, and k
-// rounds of a block arg-max below the previous pick in (value desc, id asc) order.
-template <int PER>
-__global__ __launch_bounds__(kThreads) void softmax_topk_kernel(const float* __restrict__ logits, int H, int V,
-                                                                int k, int32_t* __restrict__ topk_idx,
-                                                                float* __restrict__ topk_prob,
-                                                                float* __restrict__ probs) {
-  __shared__ float s_f[kThreads / kWave];
-  __shared__ int s_i[kThreads / kWave];
-  const int col = blockIdx.x;
+// ---------------------------------------------------------------- softmax and top-k
+//
+// One workgroup per column (b, j).  Top-k in (value desc, id asc) order without k selection
+// rounds: the k-th largest of the 256 per-thread maxima is a lower bound tau of the row's k-th
+// largest value (the k threads ranked above it each hold an element at least that large), so
+// every top-k element is >= tau.  Those candidates (typically a few more than k) are gathered
+// in LDS and each one's rank among them, which equals its rank in the row, is counted
+// directly.  More than kCand candidates (heavy ties) falls back to k selection rounds.
+// Weights are exp2(x log2 e - m log2 e) with the hardware exp2; the shared rounding of
+// m log2 e cancels in the normalised probabilities.
+
+constexpr int kCand = 512;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float weight(float x, float mL) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, -mL));
+}
+
+struct __attribute__((aligned(16))) TopkShared {   // tmax is read as float4
+  float tmax[kThreads];
+  float cv[kCand];
+  int ci[kCand];
+  float red[kThreads / kWave];
+  int redi[kThreads / kWave];
+  float tau, m;
+  int n;
+};
+
+// Row max and tau from the per-thread maxima (written to sh.tmax by the caller).
+__device__ __forceinline__ void row_max_and_tau(TopkShared& sh, float tm, int k) {
   const int t = threadIdx.x;
-  const int w = t >> 6;
-  const float* row = logits + (size_t)col * V;
-  float x[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int v = i * kThreads + t;
-    const float val = row[v < V ? v : 0];
-    x[i] = v < V ? val : -INFINITY;
-  }
+  if (t == 0) sh.n = 0;
+  __syncthreads();
+  int rank = 0;
   float m = -INFINITY;
+  const float4* tm4 = reinterpret_cast<const float4*>(sh.tmax);
+#pragma unroll 4
+  for (int j4 = 0; j4 < kThreads / 4; ++j4) {
+    const float4 o = tm4[j4];
+    const int j = 4 * j4;
+    rank += (o.x > tm || (o.x == tm && j < t)) + (o.y > tm || (o.y == tm && j + 1 < t)) +
+            (o.z > tm || (o.z == tm && j + 2 < t)) + (o.w > tm || (o.w == tm && j + 3 < t));
+    m = fmaxf(m, fmaxf(fmaxf(o.x, o.y), fmaxf(o.z, o.w)));
+  }
+  if (rank == k - 1) sh.tau = tm;     // the ranks are a permutation of 0..255 and k <= 64
+  if (t == 0) sh.m = m;
+  __syncthreads();
+}
+
+__device__ __forceinline__ void push_candidate(TopkShared& sh, float x, int v) {
+  const int slot = atomicAdd(&sh.n, 1);
+  if (slot < kCand) { sh.cv[slot] = x; sh.ci[slot] = v; }
+}
+
+__device__ __forceinline__ float block_sum_f(TopkShared& sh, float v) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) m = fmaxf(m, x[i]);
-  m = wave_max(m);
-  if ((t & 63) == 0) s_f[w] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(s_f[0], s_f[1]), fmaxf(s_f[2], s_f[3]));
-  __syncthreads();
-  float sum = 0.f;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) sum += expf(x[i] - m);   // exp(-inf) = 0 past the row
-  sum = wave_sum(sum);
-  if ((t & 63) == 0) s_f[w] = sum;
-  __syncthreads();
-  const float invS = 1.f / (s_f[0] + s_f[1] + s_f[2] + s_f[3]);
-  __syncthreads();
-  if (probs) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int v = i * kThreads + t;
-      if (v < V) probs[(size_t)col * V + v] = expf(x[i] - m) * invS;
+  for (int q = 0; q < kThreads / kWave; ++q) s += sh.red[q];
+  return s;
+}
+
+// Ranks of the gathered candidates; the k first go to the outputs.
+__device__ __forceinline__ void rank_candidates(const TopkShared& sh, int nc, int k, float mL, float invS,
+                                                int32_t* idx_out, float* prob_out) {
+  for (int c = threadIdx.x; c < nc; c += kThreads) {
+    const float cv = sh.cv[c];
+    const int ci = sh.ci[c];
+    int r = 0;
+    for (int j = 0; j < nc; ++j) r += (sh.cv[j] > cv || (sh.cv[j] == cv && sh.ci[j] < ci)) ? 1 : 0;
+    if (r < k) {
+      idx_out[r] = ci;
+      prob_out[r] = weight(cv, mL) * invS;
     }
   }
+}
+
+// k selection rounds over the row in memory, each the largest element below the previous pick
+// in (value desc, id asc) order.  Branch-free selects; used when the candidates overflow.
+__device__ void select_rounds(TopkShared& sh, const float* row, int V, int k, float mL, float invS,
+                              int32_t* idx_out, float* prob_out) {
   float prev_v = INFINITY;
   int prev_i = -1;
   for (int r = 0; r < k; ++r) {
     float bv = -INFINITY;
     int bi = INT_MAX;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int v = i * kThreads + t;
-      const bool below = x[i] < prev_v || (x[i] == prev_v && v > prev_i);
-      if (v < V && below && (x[i] > bv || (x[i] == bv && v < bi))) { bv = x[i]; bi = v; }
+    for (int v = threadIdx.x; v < V; v += kThreads) {
+      const float x = row[v];
+      const bool below = (x < prev_v) | ((x == prev_v) & (v > prev_i));
+      const bool better = (x > bv) | ((x == bv) & (v < bi));
+      const bool take = below & better;
+      bv = take ? x : bv;
+      bi = take ? v : bi;
     }
+#pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const float v2 = __shfl_xor(bv, o);
       const int i2 = __shfl_xor(bi, o);
-      if (v2 > bv || (v2 == bv && i2 < bi)) { bv = v2; bi = i2; }
+      const bool take = (v2 > bv) | ((v2 == bv) & (i2 < bi));
+      bv = take ? v2 : bv;
+      bi = take ? i2 : bi;
     }
-    if ((t & 63) == 0) { s_f[w] = bv; s_i[w] = bi; }
     __syncthreads();
-    bv = s_f[0]; bi = s_i[0];
+    if ((threadIdx.x & 63) == 0) { sh.red[threadIdx.x >> 6] = bv; sh.redi[threadIdx.x >> 6] = bi; }
+    __syncthreads();
+    bv = sh.red[0];
+    bi = sh.redi[0];
+#pragma unroll
     for (int q = 1; q < kThreads / kWave; ++q)
-      if (s_f[q] > bv || (s_f[q] == bv && s_i[q] < bi)) { bv = s_f[q]; bi = s_i[q]; }
-    __syncthreads();
-    if (t == 0) {
-      topk_idx[(size_t)col * k + r] = bi;
-      topk_prob[(size_t)col * k + r] = expf(bv - m) * invS;
+      if (sh.red[q] > bv || (sh.red[q] == bv && sh.redi[q] < bi)) { bv = sh.red[q]; bi = sh.redi[q]; }
+    if (threadIdx.x == 0) {
+      idx_out[r] = bi;
+      prob_out[r] = weight(bv, mL) * invS;
     }
     prev_v = bv;
     prev_i = bi;
   }
 }
 
-// Large vocabularies (V > 256 * 128): one workgroup per column (b, j), the row re-read from L2
-// for each pass; softmax and top-k (descending, lower id first on ties).
-__global__ __launch_bounds__(kThreads) void softmax_topk_big_kernel(const float* __restrict__ logits, int H, int V,
-                                                                int k, int32_t* __restrict__ topk_idx,
+// Rows of up to 256 * PER logits, held in registers: element (i / VEC) * 256 * VEC + t * VEC +
+// i % VEC of the row in slot i of thread t (VEC = 4: 16-byte loads, V % 4 == 0).
+template <int PER, int VEC>
+__global__ __launch_bounds__(kThreads) void softmax_topk_kernel(const float* __restrict__ logits, int V, int k,
+                                                                int32_t* __restrict__ topk_idx,
                                                                 float* __restrict__ topk_prob,
                                                                 float* __restrict__ probs) {
-  __shared__ float s_f[kThreads / kWave];
-  __shared__ int s_i[kThreads / kWave];
+  __shared__ TopkShared sh;
   const int col = blockIdx.x;
+  const int t = threadIdx.x;
   const float* row = logits + (size_t)col * V;
-  const int w = threadIdx.x >> 6;
-  // max
-  float m = -INFINITY;
-  for (int v = threadIdx.x; v < V; v += kThreads) m = fmaxf(m, row[v]);
-  m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) s_f[w] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(s_f[0], s_f[1]), fmaxf(s_f[2], s_f[3]));
-  __syncthreads();
-  // normaliser
-  float s = 0.f;
-  for (int v = threadIdx.x; v < V; v += kThreads) s += expf(row[v] - m);
-  s = wave_sum(s);
-  if ((threadIdx.x & 63) == 0) s_f[w] = s;
-  __syncthreads();
-  const float S = s_f[0] + s_f[1] + s_f[2] + s_f[3];
-  const float invS = 1.f / S;
-  __syncthreads();
-  if (probs)
-    for (int v = threadIdx.x; v < V; v += kThreads) probs[(size_t)col * V + v] = expf(row[v] - m) * invS;
-  // top-k by repeated selection below the previous pick in (value desc, id asc) order
-  float prev_v = INFINITY;
-  int prev_i = -1;
-  for (int t = 0; t < k; ++t) {
-    float bv = -INFINITY;
-    int bi = INT_MAX;
-    for (int v = threadIdx.x; v < V; v += kThreads) {
-      const float x = row[v];
-      const bool below = x < prev_v || (x == prev_v && v > prev_i);
-      if (below && (x > bv || (x == bv && v < bi))) { bv = x; bi = v; }
+  auto index = [&](int i) { return ((i / VEC) * kThreads + t) * VEC + i % VEC; };
+  float x[PER];
+#pragma unroll
+  for (int i = 0; i < PER; i += VEC) {
+    const int v = index(i);
+    const int at = v < V ? v : 0;
+    if (VEC == 4) {
+      const float4 q = *reinterpret_cast<const float4*>(row + at);
+      x[i] = q.x;
+      x[i + (VEC > 1 ? 1 : 0)] = q.y;
+      x[i + (VEC > 2 ? 2 : 0)] = q.z;
+      x[i + (VEC > 3 ? 3 : 0)] = q.w;
+    } else {
+      x[i] = row[at];
     }
-    for (int o = 32; o > 0; o >>= 1) {
-      const float v2 = __shfl_xor(bv, o);
-      const int i2 = __shfl_xor(bi, o);
-      if (v2 > bv || (v2 == bv && i2 < bi)) { bv = v2; bi = i2; }
-    }
-    if ((threadIdx.x & 63) == 0) { s_f[w] = bv; s_i[w] = bi; }
-    __syncthreads();
-    bv = s_f[0]; bi = s_i[0];
-    for (int q = 1; q < kThreads / kWave; ++q)
-      if (s_f[q] > bv || (s_f[q] == bv && s_i[q] < bi)) { bv = s_f[q]; bi = s_i[q]; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      topk_idx[(size_t)col * k + t] = bi;
-      topk_prob[(size_t)col * k + t] = expf(bv - m) * invS;
-    }
-    prev_v = bv;
-    prev_i = bi;
   }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) x[i] = index(i) < V ? x[i] : -INFINITY;
+  float tm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) tm = fmaxf(tm, x[i]);
+  sh.tmax[t] = tm;
+  row_max_and_tau(sh, tm, k);
+  const float tau = sh.tau;
+  const float mL = sh.m * kLog2e;
+  // candidates, then the weights (x is overwritten by its weight)
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (x[i] >= tau && index(i) < V) push_candidate(sh, x[i], index(i));
+    x[i] = weight(x[i], mL);                     // 0 past the row
+    sum += x[i];
+  }
+  const float invS = 1.f / block_sum_f(sh, sum);  // barriers inside: the candidates are in
+  const int nc = sh.n;
+  int32_t* io = topk_idx + (size_t)col * k;
+  float* po = topk_prob + (size_t)col * k;
+  if (nc <= kCand) rank_candidates(sh, nc, k, mL, invS, io, po);
+  else select_rounds(sh, row, V, k, mL, invS, io, po);
+  if (probs) {
+    float* pr = probs + (size_t)col * V;
+#pragma unroll
+    for (int i = 0; i < PER; i += VEC) {
+      const int v = index(i);
+      if (v < V) {
+        if (VEC == 4) {
+          *reinterpret_cast<float4*>(pr + v) =
+              make_float4(x[i] * invS, x[i + (VEC > 1 ? 1 : 0)] * invS, x[i + (VEC > 2 ? 2 : 0)] * invS,
+                          x[i + (VEC > 3 ? 3 : 0)] * invS);
+        } else {
+          pr[v] = x[i] * invS;
+        }
+      }
+    }
+  }
+}
+
+// Larger vocabularies: the same steps with the row re-read (from L2) in each pass.
+__global__ __launch_bounds__(kThreads) void softmax_topk_big_kernel(const float* __restrict__ logits, int V,
+                                                                    int k, int32_t* __restrict__ topk_idx,
+                                                                    float* __restrict__ topk_prob,
+                                                                    float* __restrict__ probs) {
+  __shared__ TopkShared sh;
+  const int col = blockIdx.x;
+  const int t = threadIdx.x;
+  const float* row = logits + (size_t)col * V;
+  float tm = -INFINITY;
+  for (int v = t; v < V; v += kThreads) tm = fmaxf(tm, row[v]);
+  sh.tmax[t] = tm;
+  row_max_and_tau(sh, tm, k);
+  const float tau = sh.tau;
+  const float mL = sh.m * kLog2e;
+  float sum = 0.f;
+  for (int v = t; v < V; v += kThreads) {
+    const float x = row[v];
+    if (x >= tau) push_candidate(sh, x, v);
+    sum += weight(x, mL);
+  }
+  const float invS = 1.f / block_sum_f(sh, sum);
+  const int nc = sh.n;
+  int32_t* io = topk_idx + (size_t)col * k;
+  float* po = topk_prob + (size_t)col * k;
+  if (nc <= kCand) rank_candidates(sh, nc, k, mL, invS, io, po);
+  else select_rounds(sh, row, V, k, mL, invS, io, po);
+  if (probs)
+    for (int v = t; v < V; v += kThreads) probs[(size_t)col * V + v] = weight(row[v], mL) * invS;
 }
 
 struct HeadsLayout {
@@ -337,10 +422,17 @@ extern "C" spec_status spec_medusa_heads(const void* h, const void* W_res, const
   else launch(nm, lm_head_kernel<4>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
   const float* lg = logits;
   const char* nt = "medusa_softmax_topk";
-  if (V <= 16 * kThreads) launch(nt, softmax_topk_kernel<16>, dim3(NC), blk, s, lg, H, V, k, topk_idx, topk_prob, draft_probs);
-  else if (V <= 32 * kThreads) launch(nt, softmax_topk_kernel<32>, dim3(NC), blk, s, lg, H, V, k, topk_idx, topk_prob, draft_probs);
-  else if (V <= 64 * kThreads) launch(nt, softmax_topk_kernel<64>, dim3(NC), blk, s, lg, H, V, k, topk_idx, topk_prob, draft_probs);
-  else if (V <= 128 * kThreads) launch(nt, softmax_topk_kernel<128>, dim3(NC), blk, s, lg, H, V, k, topk_idx, topk_prob, draft_probs);
-  else launch(nt, softmax_topk_big_kernel, dim3(NC), blk, s, lg, H, V, k, topk_idx, topk_prob, draft_probs);
+  // logits rows start on 16-byte boundaries when V % 4 == 0 (the workspace is 256-byte aligned)
+  if (V % 4 == 0) {
+    if (V <= 16 * kThreads) launch(nt, softmax_topk_kernel<16, 4>, dim3(NC), blk, s, lg, V, k, topk_idx, topk_prob, draft_probs);
+    else if (V <= 32 * kThreads) launch(nt, softmax_topk_kernel<32, 4>, dim3(NC), blk, s, lg, V, k, topk_idx, topk_prob, draft_probs);
+    else if (V <= 64 * kThreads) launch(nt, softmax_topk_kernel<64, 4>, dim3(NC), blk, s, lg, V, k, topk_idx, topk_prob, draft_probs);
+    else if (V <= 128 * kThreads) launch(nt, softmax_topk_kernel<128, 4>, dim3(NC), blk, s, lg, V, k, topk_idx, topk_prob, draft_probs);
+    else launch(nt, softmax_topk_big_kernel, dim3(NC), blk, s, lg, V, k, topk_idx, topk_prob, draft_probs);
+  } else {
+    if (V <= 16 * kThreads) launch(nt, softmax_topk_kernel<16, 1>, dim3(NC), blk, s, lg, V, k, topk_idx, topk_prob, draft_probs);
+    else if (V <= 64 * kThreads) launch(nt, softmax_topk_kernel<64, 1>, dim3(NC), blk, s, lg, V, k, topk_idx, topk_prob, draft_probs);
+    else launch(nt, softmax_topk_big_kernel, dim3(NC), blk, s, lg, V, k, topk_idx, topk_prob, draft_probs);
+  }
   return launch_status();
 }
