@@ -199,8 +199,9 @@ spec_status spec_tree_attn(const void* q, const void* k_cache, const void* v_cac
  *   err         int32 [B].
  * A sequence with n_nodes 0, or with an error, gets accept_len 0, path all -1, bonus -1 and
  * node_accept all 0.
+ * Supported: V <= 1048576 (256 chunks of 4096 logits in the bonus draw).
  * Errors: SPEC_EINVAL (sizes, NULL pointers, REJECT without draft arrays, t2d NULL with
- * Vd != V), SPEC_EWORKSPACE.
+ * Vd != V, TYPICAL with a NaN eps or delta), SPEC_EUNSUPPORTED (V), SPEC_EWORKSPACE.
  * ------------------------------------------------------------------------------------ */
 size_t spec_verify_workspace(int B, int N, int V);
 spec_status spec_verify(const float* target_logits, const float* draft_probs,

@@ -47,13 +47,39 @@ __global__ __launch_bounds__(kThreads) void resblock_kernel(const __bf16* __rest
   const __bf16* arow = W + ((size_t)j * Dm + row0 + l16) * Dm + kbeg + 8 * lg;
   const bool col_ok = l16 < B;
   const __bf16* bcol = h + (size_t)(col_ok ? l16 : 0) * Dm + kbeg + 8 * lg;
+  // Loads are branch-free (a column past B reads column 0 and is never stored) and the next
+  // step's fragments are requested before this step's product, so loads stay in flight.
+  // Buffers of four steps in a ring of NB, one buffer requested ahead of the products (deeper
+  // rings measured slower here); the ring index is static inside the unrolled body (a
+  // register copy would wait for the loads it copies).
+  // Step indices are clamped to the slice, so every load stays inside it; steps past the slice
+  // are loaded (L2 hits) but not multiplied.
+  constexpr int U = 4, NB = 2;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const int steps = kslice / 32;
-#pragma unroll 8
-  for (int s = 0; s < steps; ++s) {
-    const bf16x8 af = load8(arow + s * 32);
-    const bf16x8 bf = col_ok ? load8(bcol + s * 32) : bf16x8{};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc, 0, 0, 0);
+  const int steps = kslice / 32;             // >= 1 (Dm % 128 == 0, 4 K slices)
+  bf16x8 a[NB][U], bv[NB][U];
+  auto fetch = [&](bf16x8 (&ar)[U], bf16x8 (&br)[U], int s0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int st = min(s0 + u, steps - 1);
+      ar[u] = load8(arow + st * 32);
+      br[u] = load8(bcol + st * 32);
+    }
+  };
+  auto products = [&](const bf16x8 (&ar)[U], const bf16x8 (&br)[U], int valid) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (u < valid) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[u], br[u], acc, 0, 0, 0);
+  };
+#pragma unroll
+  for (int q = 0; q < NB - 1; ++q) fetch(a[q], bv[q], q * U);
+  for (int s = 0; s < steps; s += NB * U) {
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      fetch(a[(q + NB - 1) % NB], bv[(q + NB - 1) % NB], s + (q + NB - 1) * U);
+      __builtin_amdgcn_sched_barrier(0);    // keep the prefetch ahead of the products
+      products(a[q], bv[q], steps - (s + q * U));
+    }
   }
   red[wave][lane] = acc;
   __syncthreads();
@@ -113,21 +139,46 @@ __global__ __launch_bounds__(kThreads) void lm_head_kernel(const __bf16* __restr
   for (int rb = 0; rb < kLmRowBlocks; ++rb)
 #pragma unroll
     for (int cb = 0; cb < CBN; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Loads are branch-free (rows past V and columns past NC read row / column 0 and are never
+  // stored).  All fragments of the next step (W_lm from HBM, z from L2) are requested before
+  // this step's products: the memory counter drains in issue order, so a load issued after
+  // the prefetch could only be waited for together with it.
   const int steps = kslice / 32;
-#pragma unroll 2
-  for (int s = 0; s < steps; ++s) {
-    bf16x8 af[kLmRowBlocks];
+  struct Frags {
+    bf16x8 a[kLmRowBlocks];
+    bf16x8 b[3][CBN];
+  };
+  auto fetch = [&](Frags& f, int s) {
 #pragma unroll
-    for (int rb = 0; rb < kLmRowBlocks; ++rb) af[rb] = row_ok[rb] ? load8(arow[rb] + s * 32) : bf16x8{};
+    for (int rb = 0; rb < kLmRowBlocks; ++rb) f.a[rb] = load8(arow[rb] + s * 32);
 #pragma unroll
-    for (int cb = 0; cb < CBN; ++cb) {
+    for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
-      for (int sp = 0; sp < 3; ++sp) {
-        const bf16x8 bf = col_ok[cb] ? load8(bptr[sp][cb] + s * 32) : bf16x8{};
+      for (int cb = 0; cb < CBN; ++cb) f.b[sp][cb] = load8(bptr[sp][cb] + s * 32);
+  };
+  auto products = [&](const Frags& f) {
+#pragma unroll
+    for (int cb = 0; cb < CBN; ++cb)
+#pragma unroll
+      for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
         for (int rb = 0; rb < kLmRowBlocks; ++rb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rb], bf, acc[rb][cb], 0, 0, 0);
-      }
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[rb], f.b[sp][cb], acc[rb][cb], 0, 0, 0);
+  };
+  // A ring of NB buffers, NB - 1 steps requested ahead of the products (deeper rings measured
+  // slower here).  The ring index is static inside the unrolled body (a register copy would
+  // wait for the loads it copies).  Step indices are
+  // clamped, so the loads past the last step re-read it (L2 hits) and stay inside the slice.
+  constexpr int NB = 2;
+  Frags f[NB];
+#pragma unroll
+  for (int u = 0; u < NB - 1; ++u) fetch(f[u], min(u, steps - 1));
+  for (int s = 0; s < steps; s += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      fetch(f[(u + NB - 1) % NB], min(s + u + NB - 1, steps - 1));
+      __builtin_amdgcn_sched_barrier(0);    // keep the prefetch ahead of the products
+      if (s + u < steps) products(f[u]);
     }
   }
 #pragma unroll
