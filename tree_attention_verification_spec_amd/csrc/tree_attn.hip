@@ -68,6 +68,7 @@ struct AttnArgs {
   float2* part_ml;             // [U, S, Mpad]
   float* part_o;               // [U, S, Mpad, D]
   int R, S, Mpad;
+  int prio;                    // raise wave priority around the MFMA blocks
 };
 
 __device__ __forceinline__ bool seq_valid(int n, int P, int N, int S_max) {
@@ -249,7 +250,10 @@ void tree_attn_bf16_kernel(AttnArgs a) {
     const __bf16* kt = k_lds[buf];
     const __bf16* vt = v_lds[buf];
 
-    // ---- S^T = K Q^T for the 64 keys of the tile.
+    // ---- S^T = K Q^T for the 64 keys of the tile.  The MFMA blocks run at raised wave
+    // priority: a wave that reaches one gets the issue slot first, so the two waves of a SIMD
+    // drift apart and one's softmax (VALU) overlaps the other's products.
+    if (a.prio) __builtin_amdgcn_s_setprio(1);
     f32x4 s_acc[4][CB];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -264,6 +268,7 @@ void tree_attn_bf16_kernel(AttnArgs a) {
       }
     }
 
+    if (a.prio) __builtin_amdgcn_s_setprio(0);
     // ---- mask (only where needed), online softmax in base 2, P^T packed as bf16.  The max is
     // taken on raw scores (the scale is positive, so it commutes with the max) and each weight
     // is exp2(s * scale_log2 - m) with one FMA.  Rows past the workload have Q = 0 and are
@@ -330,6 +335,7 @@ void tree_attn_bf16_kernel(AttnArgs a) {
     }
 
     // ---- O^T += V^T P^T.
+    if (a.prio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -340,6 +346,7 @@ void tree_attn_bf16_kernel(AttnArgs a) {
           o_acc[db][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pb[c][cb], o_acc[db][cb], 0, 0, 0);
       }
     }
+    if (a.prio) __builtin_amdgcn_s_setprio(0);
     buf ^= 1;
   }
 
@@ -540,8 +547,9 @@ int env_int(const char* name, int fallback) {
 
 // Launch shape.  Few (sequence, KV head) units -> 64-row workgroups (4 waves of 16 rows) and
 // more key splits so that all CUs work; many units -> 256-row workgroups (8 waves of 32 rows:
-// the K/V tile in LDS serves 4x more rows per read) and few splits.  Every split keeps at
-// least two tiles.  SPECTREE_ATTN_CB, SPECTREE_ATTN_WAVES and SPECTREE_ATTN_SPLITS override the
+// the K/V tile in LDS serves 4x more rows per read) and few splits.  Splits are chosen for
+// about 256 workgroups (one round; an unsplit problem needs no merge), and every split keeps
+// at least two tiles.  SPECTREE_ATTN_CB, SPECTREE_ATTN_WAVES and SPECTREE_ATTN_SPLITS override the
 // choice (tuning knobs; results do not depend on them).
 Plan make_plan(int B, int N, int Hq, int Hkv, int D, int S_max) {
   Plan p{};
@@ -556,7 +564,7 @@ Plan make_plan(int B, int N, int Hq, int Hkv, int D, int S_max) {
   p.RBS = p.WAVES * 16 * p.CB;
   p.R = (M + p.RBS - 1) / p.RBS;
   p.Mpad = p.R * p.RBS;
-  const int target = big ? 512 : 256;
+  const int target = 256;   // one workgroup per CU, all in one round (measured best)
   const int tiles = (S_max + kKT - 1) / kKT;
   int S = (target + p.units * p.R - 1) / (p.units * p.R);
   S = env_int("SPECTREE_ATTN_SPLITS", S);
@@ -630,6 +638,7 @@ extern "C" spec_status spec_tree_attn(const void* q, const void* k_cache, const 
   const size_t need = workspace_bytes(p, head_dim);
   if (need > 0 && (!workspace || ws_bytes < need)) return SPEC_EWORKSPACE;
   a.R = p.R; a.S = p.S; a.Mpad = p.Mpad;
+  a.prio = env_int("SPECTREE_ATTN_PRIO", 1);
   if (p.S > 1) {
     char* w = static_cast<char*>(workspace);
     size_t off = 0;
