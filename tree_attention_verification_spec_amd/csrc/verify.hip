@@ -10,7 +10,7 @@
 // Four kernels, in stream order; no kernel synchronises workgroups (the kernel boundaries
 // order their results), and every global load is issued before it is needed.
 //   rows    grid (seq, node, chunk): rows of nodes with children are split into chunks of
-//           16K logits; each workgroup streams its chunk once (float4 loads held in registers)
+//           8K logits; each workgroup streams its chunk once (float4 loads held in registers)
 //           into (max, lowest argmax, sum exp(x - max), sum exp(x - max)(x - max)), fp32 exp
 //           with fp64 sums.  Workgroups of leaf rows leave after a 1 KB look at the parents.
 //   decide  one workgroup per sequence, one thread per node: merge of the row chunks,
@@ -23,6 +23,7 @@
 //           inside it for the smallest token whose running sum exceeds u * Z.
 #include <cfloat>
 #include <climits>
+#include <cstdlib>
 
 #include "common.h"
 
@@ -30,11 +31,9 @@ namespace spectree {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowChunk = 16384;             // logits per workgroup in the row pass
-constexpr int kRowPer = kRowChunk / kThreads;
 constexpr int kBonusChunk = 4096;            // logits per workgroup in the bonus pass
 constexpr int kPer = kBonusChunk / kThreads;
-constexpr int kMaxRowChunks = 8;             // decide merges a row's chunks in batches of 8
+constexpr int kPartsPerLane = 8;             // row-chunk partials per merging lane and batch
 
 struct RowPart {      // one chunk of one logits row
   double S;           // sum exp(x - m)
@@ -79,7 +78,8 @@ struct VerifyArgs {
   int32_t* bonus;
   uint8_t* node_accept;
   int32_t* err;
-  int CR;               // row-pass chunks per row (kRowChunk logits each)
+  int CR;               // row-pass chunks per row
+  int RC;               // logits per row-pass chunk
   int CS, C;            // bonus-pass chunk size (kBonusChunk) and chunks per row
   RowPart* rowparts;    // [B, N, CR]
   BonusPlan* plans;     // [B]
@@ -194,7 +194,7 @@ __device__ __forceinline__ int chunk_index(int lo, int k) {
 
 // ------------------------------------------------------------------ kernel 1: row chunks
 
-template <int VEC>
+template <int VEC, int PER>
 __global__ __launch_bounds__(kThreads) void rows_kernel(VerifyArgs a) {
   // 1-D grid over (seq, node, chunk): grid y/z are limited to 65536.
   const int c = blockIdx.x % a.CR;
@@ -208,15 +208,15 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(VerifyArgs a) {
   if (!__syncthreads_or(named)) return;
 
   const float* row = a.logits + ((size_t)b * a.N + p) * a.V;
-  const int lo = c * kRowChunk;
-  const int hi = min(a.V, lo + kRowChunk);
-  float x[kRowPer];
+  const int lo = c * a.RC;                 // a.RC == PER * kThreads
+  const int hi = min(a.V, lo + a.RC);
+  float x[PER];
   load_chunk<VEC>(row, lo, hi, x);
   // chunk max (lowest index: a thread's slots run in increasing token order), nonfinite flag
   float m = -INFINITY;
   int am = INT_MAX, nf = 0;
 #pragma unroll
-  for (int k = 0; k < kRowPer; ++k) {
+  for (int k = 0; k < PER; ++k) {
     const int idx = chunk_index<VEC>(lo, k);
     if (idx < hi) {
       nf |= !isfinite(x[k]);
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(VerifyArgs a) {
   double S = 0.0, A = 0.0;
   if (m != -INFINITY && !nf) {
 #pragma unroll
-    for (int k = 0; k < kRowPer; ++k) {
+    for (int k = 0; k < PER; ++k) {
       const float d = x[k] - m;            // -inf past the chunk -> exp 0
       const float ex = __expf(d);
       S += (double)ex;
@@ -281,14 +281,18 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
     if (p >= 0 && p < c) s_has[p] = 1;
   }
   __syncthreads();
-  // this thread's loads, all issued before any is used: its own token / uniform / draft row,
-  // and the chunk partials of its row if it has children
-  RowPart q[kMaxRowChunks];
-  const bool has = c < n && s_has[c];
-  {
-    const RowPart* rp = a.rowparts + ((size_t)b * a.N + (has ? c : 0)) * a.CR;
+  // Chunk partials of the rows that have children, merged by L lanes per node (4, 2 or 1 for
+  // up to 64, 128 or 256 nodes), each lane a strided subset of the chunks.  They are loaded
+  // before this thread's own token / uniform / draft row.
+  const int L = a.N <= 64 ? 4 : (a.N <= 128 ? 2 : 1);
+  const int mn = c / L, sub = c % L;
+  const bool mhas = mn < n && s_has[mn];
+  const RowPart* rp = a.rowparts + ((size_t)b * a.N + (mhas ? mn : 0)) * a.CR;
+  RowPart q[kPartsPerLane];
 #pragma unroll
-    for (int k = 0; k < kMaxRowChunks; ++k) q[k] = rp[k < a.CR ? k : 0];
+  for (int k = 0; k < kPartsPerLane; ++k) {
+    const int ck = sub + k * L;
+    q[k] = rp[ck < a.CR ? ck : 0];
   }
   int code = 0, depth = 0, tok = -1, drow = -1, dx = -1;
   float u = 0.f;
@@ -326,25 +330,37 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
 
   // ---- statistics of the rows that have children: merge their chunks.  Max first, then
   // S = sum_c S_c e^(m_c - M) and A = sum_c e^(m_c - M) (A_c + (m_c - M) S_c); the chunk
-  // exponentials are independent of one another.
-  if (has) {
-    const RowPart* rp = a.rowparts + ((size_t)b * a.N + c) * a.CR;
+  // exponentials are independent of one another.  Chunks past the first kPartsPerLane per
+  // lane are read in further batches.
+  {
     float m = -INFINITY;
     int am = INT_MAX, nf = 0;
     auto upd = [&](const RowPart& r) {
       nf |= r.nonfinite;
       if (r.m > m || (r.m == m && r.argmax < am)) { m = r.m; am = r.argmax; }
     };
+    const int per_lane = kPartsPerLane * L;
+    if (mhas) {
 #pragma unroll
-    for (int k = 0; k < kMaxRowChunks; ++k)
-      if (k < a.CR) upd(q[k]);
-    for (int k0 = kMaxRowChunks; k0 < a.CR; k0 += kMaxRowChunks) {   // V > 8 chunks: further batches
-      RowPart r[kMaxRowChunks];
+      for (int k = 0; k < kPartsPerLane; ++k)
+        if (sub + k * L < a.CR) upd(q[k]);
+      for (int k0 = per_lane; k0 < a.CR; k0 += per_lane) {
+        RowPart r[kPartsPerLane];
 #pragma unroll
-      for (int k = 0; k < kMaxRowChunks; ++k) r[k] = rp[k0 + k < a.CR ? k0 + k : 0];
+        for (int k = 0; k < kPartsPerLane; ++k) {
+          const int ck = k0 + sub + k * L;
+          r[k] = rp[ck < a.CR ? ck : 0];
+        }
 #pragma unroll
-      for (int k = 0; k < kMaxRowChunks; ++k)
-        if (k0 + k < a.CR) upd(r[k]);
+        for (int k = 0; k < kPartsPerLane; ++k)
+          if (k0 + sub + k * L < a.CR) upd(r[k]);
+      }
+    }
+    for (int o = 1; o < L; o <<= 1) {            // the L lanes of a node are adjacent
+      const float m2 = __shfl_xor(m, o);
+      const int am2 = __shfl_xor(am, o), nf2 = __shfl_xor(nf, o);
+      if (m2 > m || (m2 == m && am2 < am)) { m = m2; am = am2; }
+      nf |= nf2;
     }
     double S = 0.0, A = 0.0;
     auto add = [&](const RowPart& r) {
@@ -354,24 +370,33 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
       S += sc * r.S;
       A += sc * (r.A + d * r.S);
     };
-    if (m != -INFINITY && !nf) {
+    if (mhas && m != -INFINITY && !nf) {
 #pragma unroll
-      for (int k = 0; k < kMaxRowChunks; ++k)
-        if (k < a.CR) add(q[k]);
-      for (int k0 = kMaxRowChunks; k0 < a.CR; k0 += kMaxRowChunks) {
-        RowPart r[kMaxRowChunks];
+      for (int k = 0; k < kPartsPerLane; ++k)
+        if (sub + k * L < a.CR) add(q[k]);
+      for (int k0 = per_lane; k0 < a.CR; k0 += per_lane) {
+        RowPart r[kPartsPerLane];
 #pragma unroll
-        for (int k = 0; k < kMaxRowChunks; ++k) r[k] = rp[k0 + k < a.CR ? k0 + k : 0];
+        for (int k = 0; k < kPartsPerLane; ++k) {
+          const int ck = k0 + sub + k * L;
+          r[k] = rp[ck < a.CR ? ck : 0];
+        }
 #pragma unroll
-        for (int k = 0; k < kMaxRowChunks; ++k)
-          if (k0 + k < a.CR) add(r[k]);
+        for (int k = 0; k < kPartsPerLane; ++k)
+          if (k0 + sub + k * L < a.CR) add(r[k]);
       }
     }
-    if (nf) atomicMin(&s_err, err_word(c, SPEC_ERR_NONFINITE));
-    s_mx[c] = m;
-    s_am[c] = am;
-    s_S[c] = S;
-    s_H[c] = log(S) - A / S;
+    for (int o = 1; o < L; o <<= 1) {
+      S += __shfl_xor(S, o);
+      A += __shfl_xor(A, o);
+    }
+    if (mhas && sub == 0) {
+      if (nf) atomicMin(&s_err, err_word(mn, SPEC_ERR_NONFINITE));
+      s_mx[mn] = m;
+      s_am[mn] = am;
+      s_S[mn] = S;
+      s_H[mn] = log(S) - A / S;
+    }
   }
   if (code) atomicMin(&s_err, err_word(c, code));
   __syncthreads();
@@ -643,13 +668,26 @@ __global__ __launch_bounds__(kThreads) void select_kernel(VerifyArgs a) {
 // ------------------------------------------------------------------ host
 
 struct VerifyLayout {
-  int CR, CS, C;
+  int RC, CR, CS, C;
   size_t rowparts, plans, bparts, total;
 };
 
+// Row-pass chunk: 8K logits (measured faster than 4K and 16K at batch 1 and 16).
+// SPECTREE_VERIFY_CHUNK (4096, 8192 or 16384) overrides the choice (a tuning knob).
+int row_chunk(int B, int N, int V) {
+  int rc = 8192;
+  const char* e = std::getenv("SPECTREE_VERIFY_CHUNK");
+  if (e && *e) {
+    const int v = std::atoi(e);
+    if (v == 4096 || v == 8192 || v == 16384) rc = v;
+  }
+  return rc;
+}
+
 VerifyLayout layout(int B, int N, int V) {
   VerifyLayout L{};
-  L.CR = (V + kRowChunk - 1) / kRowChunk;
+  L.RC = row_chunk(B, N, V);
+  L.CR = (V + L.RC - 1) / L.RC;
   L.CS = kBonusChunk;
   L.C = (V + L.CS - 1) / L.CS;
   size_t off = 0;
@@ -698,7 +736,7 @@ extern "C" spec_status spec_verify(const float* target_logits, const float* draf
   a.tokens = tokens; a.parents = parents; a.n_nodes = n_nodes; a.uniforms = uniforms;
   a.B = B; a.N = N; a.V = V; a.R = R; a.Vd = Vd; a.max_depth = max_depth; a.mode = mode;
   a.eps = eps; a.delta = delta; a.accept_len = accept_len; a.path = path; a.bonus = bonus_token;
-  a.node_accept = node_accept; a.err = err; a.CR = L.CR; a.CS = L.CS; a.C = L.C;
+  a.node_accept = node_accept; a.err = err; a.CR = L.CR; a.RC = L.RC; a.CS = L.CS; a.C = L.C;
   char* w = static_cast<char*>(workspace);
   a.rowparts = reinterpret_cast<RowPart*>(w + L.rowparts);
   a.plans = reinterpret_cast<BonusPlan*>(w + L.plans);
@@ -708,8 +746,17 @@ extern "C" spec_status spec_verify(const float* target_logits, const float* draf
   const dim3 grid_rows((unsigned)((size_t)L.CR * N * B)), grid_chunks((unsigned)((size_t)L.C * B));
   // 16-byte loads need rows that start on 16-byte boundaries
   const bool vec4 = V % 4 == 0 && (reinterpret_cast<uintptr_t>(target_logits) & 15) == 0;
-  if (vec4) launch("verify_rows", rows_kernel<4>, grid_rows, blk, s, a);
-  else launch("verify_rows", rows_kernel<1>, grid_rows, blk, s, a);
+  const char* nr = "verify_rows";
+  if (L.RC == 16384) {
+    if (vec4) launch(nr, rows_kernel<4, 64>, grid_rows, blk, s, a);
+    else launch(nr, rows_kernel<1, 64>, grid_rows, blk, s, a);
+  } else if (L.RC == 8192) {
+    if (vec4) launch(nr, rows_kernel<4, 32>, grid_rows, blk, s, a);
+    else launch(nr, rows_kernel<1, 32>, grid_rows, blk, s, a);
+  } else {
+    if (vec4) launch(nr, rows_kernel<4, 16>, grid_rows, blk, s, a);
+    else launch(nr, rows_kernel<1, 16>, grid_rows, blk, s, a);
+  }
   launch("verify_decide", decide_kernel, dim3(B), blk, s, a);
   if (vec4) {
     launch("verify_bonus", bonus_kernel<4>, grid_chunks, blk, s, a);
