@@ -190,12 +190,19 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) o_acc[db][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[CB], l_run[CB];
+  // Row sums of the weights are a 17th output block: A = ones in its first row, so element 0
+  // of lanes 0..15 accumulates sum_k P[k][row l16] on the matrix cores, with the same bf16
+  // weights as the product and the same rescaling.
+  f32x4 o_sum[CB];
+  float m_run[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     m_run[cb] = -INFINITY;
-    l_run[cb] = 0.f;
+    o_sum[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  bf16x8 ones_frag;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones_frag[e] = (__bf16)(l16 == 0 ? 1.f : 0.f);
 
   const size_t kv_base = ((size_t)b * a.Hkv + g) * (size_t)a.S_max * D;
   const int ld_key = tid / CPK;
@@ -308,20 +315,15 @@ void tree_attn_bf16_kernel(AttnArgs a) {
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       if (__ballot(m_new > m_run[cb])) {         // some row's max moved: rescale
         const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_use);
-        l_run[cb] *= alpha;
+        o_sum[cb] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) o_acc[db][cb] *= alpha;
         m_run[cb] = m_new;
       }
-      float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[kb][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][e], a.scale_log2, -m_use));
-          psum += x[kb][e];
-        }
-      l_run[cb] += psum;
+        for (int e = 0; e < 4; ++e) x[kb][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][e], a.scale_log2, -m_use));
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         bf16x8 p;
@@ -346,16 +348,19 @@ void tree_attn_bf16_kernel(AttnArgs a) {
           o_acc[db][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pb[c][cb], o_acc[db][cb], 0, 0, 0);
       }
     }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        o_sum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_frag, pb[c][cb], o_sum[cb], 0, 0, 0);
     if (a.prio) __builtin_amdgcn_s_setprio(0);
     buf ^= 1;
   }
 
-  // Row sums: lanes l16, l16+16, l16+32, l16+48 hold partial sums of the same row.
+  // Row sums: element 0 of lane l16 (the first 16 lanes) holds the sum of row l16.
+  float l_run[CB];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    l_run[cb] += __shfl_xor(l_run[cb], 16);
-    l_run[cb] += __shfl_xor(l_run[cb], 32);
-  }
+  for (int cb = 0; cb < CB; ++cb) l_run[cb] = __shfl(o_sum[cb][0], l16);
 
   if (a.S == 1) {
 #pragma unroll
