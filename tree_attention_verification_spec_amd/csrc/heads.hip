@@ -19,6 +19,7 @@
 // exact three-term bf16 split z = hi + mid + lo; each W_lm fragment is multiplied with the
 // three parts into one fp32 accumulator, which costs MFMA issue slots but no extra HBM bytes.
 #include <climits>
+#include <cstdlib>
 
 #include "common.h"
 
@@ -27,7 +28,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kKWaves = 4;       // K slices per workgroup
-constexpr int kLmRowBlocks = 4;  // 16-row blocks of W_lm per wave
 constexpr int kMaxCols = 64;     // B * H limit of the LM head
 
 __device__ __forceinline__ bf16x8 load8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
@@ -104,22 +104,22 @@ __global__ __launch_bounds__(kThreads) void resblock_kernel(const __bf16* __rest
   }
 }
 
-// grid: ceil(V / 64) workgroups; workgroup = 64 rows of W_lm (4 blocks of 16 per wave), K split
-// over the 4 waves.  logits[col, v], col = b * H + j.
-template <int CBN>
+// grid: ceil(V / (16 RB)) workgroups; workgroup = 16 RB rows of W_lm (RB blocks of 16 per wave),
+// K split over the 4 waves.  logits[col, v], col = b * H + j.
+template <int CBN, int RB>
 __global__ __launch_bounds__(kThreads) void lm_head_kernel(const __bf16* __restrict__ W_lm,
                                                            const __bf16* __restrict__ zsplit, int NC, int Dm,
                                                            int V, float* __restrict__ logits) {
-  __shared__ f32x4 red[kKWaves][kLmRowBlocks * CBN][kWave];
+  __shared__ f32x4 red[kKWaves][RB * CBN][kWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int row0 = blockIdx.x * 16 * kLmRowBlocks;
+  const int row0 = blockIdx.x * 16 * RB;
   const int kslice = Dm / kKWaves;
   const int kbeg = wave * kslice;
-  const __bf16* arow[kLmRowBlocks];
-  bool row_ok[kLmRowBlocks];
+  const __bf16* arow[RB];
+  bool row_ok[RB];
 #pragma unroll
-  for (int rb = 0; rb < kLmRowBlocks; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     const int r = row0 + rb * 16 + l16;
     row_ok[rb] = r < V;
     arow[rb] = W_lm + (size_t)(row_ok[rb] ? r : 0) * Dm + kbeg + 8 * lg;
@@ -134,9 +134,9 @@ __global__ __launch_bounds__(kThreads) void lm_head_kernel(const __bf16* __restr
     for (int sp = 0; sp < 3; ++sp)
       bptr[sp][cb] = zsplit + ((size_t)sp * NC + (col_ok[cb] ? col : 0)) * Dm + kbeg + 8 * lg;
   }
-  f32x4 acc[kLmRowBlocks][CBN];
+  f32x4 acc[RB][CBN];
 #pragma unroll
-  for (int rb = 0; rb < kLmRowBlocks; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < CBN; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   // Loads are branch-free (rows past V and columns past NC read row / column 0 and are never
@@ -145,12 +145,12 @@ __global__ __launch_bounds__(kThreads) void lm_head_kernel(const __bf16* __restr
   // the prefetch could only be waited for together with it.
   const int steps = kslice / 32;
   struct Frags {
-    bf16x8 a[kLmRowBlocks];
+    bf16x8 a[RB];
     bf16x8 b[3][CBN];
   };
   auto fetch = [&](Frags& f, int s) {
 #pragma unroll
-    for (int rb = 0; rb < kLmRowBlocks; ++rb) f.a[rb] = load8(arow[rb] + s * 32);
+    for (int rb = 0; rb < RB; ++rb) f.a[rb] = load8(arow[rb] + s * 32);
 #pragma unroll
     for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
@@ -162,14 +162,15 @@ __global__ __launch_bounds__(kThreads) void lm_head_kernel(const __bf16* __restr
 #pragma unroll
       for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
-        for (int rb = 0; rb < kLmRowBlocks; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[rb], f.b[sp][cb], acc[rb][cb], 0, 0, 0);
   };
-  // A ring of NB buffers, NB - 1 steps requested ahead of the products (deeper rings measured
-  // slower here).  The ring index is static inside the unrolled body (a register copy would
-  // wait for the loads it copies).  Step indices are
+  // A ring of NB buffers, NB - 1 steps requested ahead of the products: three with 8 row
+  // blocks (one wave per SIMD, so the registers cost no occupancy), two otherwise (deeper rings
+  // measured slower there).  The ring index is static inside the unrolled body (a register
+  // copy would wait for the loads it copies).  Step indices are
   // clamped, so the loads past the last step re-read it (L2 hits) and stay inside the slice.
-  constexpr int NB = 2;
+  constexpr int NB = (RB == 8 && CBN <= 2) ? 3 : 2;
   Frags f[NB];
 #pragma unroll
   for (int u = 0; u < NB - 1; ++u) fetch(f[u], min(u, steps - 1));
@@ -182,12 +183,12 @@ __global__ __launch_bounds__(kThreads) void lm_head_kernel(const __bf16* __restr
     }
   }
 #pragma unroll
-  for (int rb = 0; rb < kLmRowBlocks; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < CBN; ++cb) red[wave][rb * CBN + cb][lane] = acc[rb][cb];
   __syncthreads();
   // Every wave finishes a quarter of the tiles.
-  for (int t = wave; t < kLmRowBlocks * CBN; t += kKWaves) {
+  for (int t = wave; t < RB * CBN; t += kKWaves) {
     const f32x4 sum = red[0][t][lane] + red[1][t][lane] + red[2][t][lane] + red[3][t][lane];
     const int rb = t / CBN, cb = t % CBN;
     const int col = cb * 16 + l16;
@@ -462,15 +463,25 @@ extern "C" spec_status spec_medusa_heads(const void* h, const void* W_res, const
   const dim3 blk(kThreads);
   launch("medusa_resblock", resblock_kernel, dim3(H * (Dm / 16)), blk, s, static_cast<const __bf16*>(h),
          static_cast<const __bf16*>(W_res), B, H, Dm, zsplit);
-  const dim3 grid_lm((V + 16 * kLmRowBlocks - 1) / (16 * kLmRowBlocks));
+  // 16-row blocks of W_lm per wave (RB): 8 by default, 4 with SPECTREE_LM_ROWBLOCKS=4 (tuning).
+  const char* rbe = std::getenv("SPECTREE_LM_ROWBLOCKS");
+  const int RBv = (rbe && std::atoi(rbe) == 4) ? 4 : 8;
+  const dim3 grid_lm((V + 16 * RBv - 1) / (16 * RBv));
   const __bf16* wl = static_cast<const __bf16*>(W_lm);
   const __bf16* zs = zsplit;
   const char* nm = "medusa_lm_head";
   const int cbn = (NC + 15) / 16;
-  if (cbn == 1) launch(nm, lm_head_kernel<1>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
-  else if (cbn == 2) launch(nm, lm_head_kernel<2>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
-  else if (cbn == 3) launch(nm, lm_head_kernel<3>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
-  else launch(nm, lm_head_kernel<4>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
+  if (RBv == 8) {
+    if (cbn == 1) launch(nm, lm_head_kernel<1, 8>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
+    else if (cbn == 2) launch(nm, lm_head_kernel<2, 8>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
+    else if (cbn == 3) launch(nm, lm_head_kernel<3, 8>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
+    else launch(nm, lm_head_kernel<4, 8>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
+  } else {
+    if (cbn == 1) launch(nm, lm_head_kernel<1, 4>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
+    else if (cbn == 2) launch(nm, lm_head_kernel<2, 4>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
+    else if (cbn == 3) launch(nm, lm_head_kernel<3, 4>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
+    else launch(nm, lm_head_kernel<4, 4>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
+  }
   const float* lg = logits;
   const char* nt = "medusa_softmax_topk";
   // logits rows start on 16-byte boundaries when V % 4 == 0 (the workspace is 256-byte aligned)
