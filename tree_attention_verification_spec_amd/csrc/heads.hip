@@ -32,14 +32,17 @@ constexpr int kMaxCols = 64;     // B * H limit of the LM head
 
 __device__ __forceinline__ bf16x8 load8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-// grid: H * Dm / 16 workgroups; workgroup = 16 output rows of one head, K split over 4 waves.
+// grid: H * Dm / (16 RB) workgroups; workgroup = RB blocks of 16 output rows of one head, K
+// split over 4 waves (each wave all RB blocks of its K slice, so one h fragment serves RB
+// products and h is re-read from L2 once per workgroup).
+template <int RB>
 __global__ __launch_bounds__(kThreads) void resblock_kernel(const __bf16* __restrict__ h,
                                                             const __bf16* __restrict__ W, int B, int H,
                                                             int Dm, __bf16* __restrict__ zsplit) {
-  __shared__ f32x4 red[kKWaves][kWave];
-  const int rows_per_head = Dm / 16;
-  const int j = blockIdx.x / rows_per_head;
-  const int row0 = (blockIdx.x - j * rows_per_head) * 16;
+  __shared__ f32x4 red[kKWaves][RB][kWave];
+  const int blocks_per_head = Dm / (16 * RB);
+  const int j = blockIdx.x / blocks_per_head;
+  const int row0 = (blockIdx.x - j * blocks_per_head) * 16 * RB;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int kslice = Dm / kKWaves;
@@ -48,28 +51,33 @@ __global__ __launch_bounds__(kThreads) void resblock_kernel(const __bf16* __rest
   const bool col_ok = l16 < B;
   const __bf16* bcol = h + (size_t)(col_ok ? l16 : 0) * Dm + kbeg + 8 * lg;
   // Loads are branch-free (a column past B reads column 0 and is never stored) and the next
-  // step's fragments are requested before this step's product, so loads stay in flight.
-  // Buffers of four steps in a ring of NB, one buffer requested ahead of the products (deeper
-  // rings measured slower here); the ring index is static inside the unrolled body (a
-  // register copy would wait for the loads it copies).
-  // Step indices are clamped to the slice, so every load stays inside it; steps past the slice
-  // are loaded (L2 hits) but not multiplied.
+  // steps' fragments are requested before this step's products, so loads stay in flight.
+  // Buffers of four steps in a ring of NB, one buffer requested ahead of the products; the
+  // ring index is static inside the unrolled body (a register copy would wait for the loads
+  // it copies).  Step indices are clamped to the slice, so every load stays inside it; steps
+  // past the slice are loaded (L2 hits) but not multiplied.
   constexpr int U = 4, NB = 2;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int steps = kslice / 32;             // >= 1 (Dm % 128 == 0, 4 K slices)
-  bf16x8 a[NB][U], bv[NB][U];
-  auto fetch = [&](bf16x8 (&ar)[U], bf16x8 (&br)[U], int s0) {
+  bf16x8 a[NB][U][RB], bv[NB][U];
+  auto fetch = [&](bf16x8 (&ar)[U][RB], bf16x8 (&br)[U], int s0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int st = min(s0 + u, steps - 1);
-      ar[u] = load8(arow + st * 32);
+#pragma unroll
+      for (int r = 0; r < RB; ++r) ar[u][r] = load8(arow + (size_t)r * 16 * Dm + st * 32);
       br[u] = load8(bcol + st * 32);
     }
   };
-  auto products = [&](const bf16x8 (&ar)[U], const bf16x8 (&br)[U], int valid) {
+  auto products = [&](const bf16x8 (&ar)[U][RB], const bf16x8 (&br)[U], int valid) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (u < valid) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[u], br[u], acc, 0, 0, 0);
+      if (u < valid) {
+#pragma unroll
+        for (int r = 0; r < RB; ++r) acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[u][r], br[u], acc[r], 0, 0, 0);
+      }
   };
 #pragma unroll
   for (int q = 0; q < NB - 1; ++q) fetch(a[q], bv[q], q * U);
@@ -81,26 +89,29 @@ __global__ __launch_bounds__(kThreads) void resblock_kernel(const __bf16* __rest
       products(a[q], bv[q], steps - (s + q * U));
     }
   }
-  red[wave][lane] = acc;
+#pragma unroll
+  for (int r = 0; r < RB; ++r) red[wave][r][lane] = acc[r];
   __syncthreads();
-  if (wave != 0) return;
-  acc = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
   if (!col_ok) return;
   const int b = l16;
   const int NC = B * H;
+  // Every wave finishes a share of the row blocks: z = h + SiLU(W h), as an exact bf16 split.
+  for (int r = wave; r < RB; r += kKWaves) {
+    const f32x4 sum = red[0][r][lane] + red[1][r][lane] + red[2][r][lane] + red[3][r][lane];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int row = row0 + 4 * lg + e;           // output feature
-    const float a = acc[e];
-    const float z = (float)h[(size_t)b * Dm + row] + a / (1.f + expf(-a));
-    const __bf16 hi = (__bf16)z;
-    const float r1 = z - (float)hi;
-    const __bf16 mid = (__bf16)r1;
-    const __bf16 lo = (__bf16)(r1 - (float)mid);
-    const size_t col = (size_t)b * H + j;
-    zsplit[(0 * (size_t)NC + col) * Dm + row] = hi;
-    zsplit[(1 * (size_t)NC + col) * Dm + row] = mid;
-    zsplit[(2 * (size_t)NC + col) * Dm + row] = lo;
+    for (int e = 0; e < 4; ++e) {
+      const int row = row0 + r * 16 + 4 * lg + e;   // output feature
+      const float av = sum[e];
+      const float z = (float)h[(size_t)b * Dm + row] + av / (1.f + expf(-av));
+      const __bf16 hi = (__bf16)z;
+      const float r1 = z - (float)hi;
+      const __bf16 mid = (__bf16)r1;
+      const __bf16 lo = (__bf16)(r1 - (float)mid);
+      const size_t col = (size_t)b * H + j;
+      zsplit[(0 * (size_t)NC + col) * Dm + row] = hi;
+      zsplit[(1 * (size_t)NC + col) * Dm + row] = mid;
+      zsplit[(2 * (size_t)NC + col) * Dm + row] = lo;
+    }
   }
 }
 
@@ -461,8 +472,16 @@ extern "C" spec_status spec_medusa_heads(const void* h, const void* W_res, const
   float* logits = reinterpret_cast<float*>(w + L.logits);
   const int NC = B * H;
   const dim3 blk(kThreads);
-  launch("medusa_resblock", resblock_kernel, dim3(H * (Dm / 16)), blk, s, static_cast<const __bf16*>(h),
-         static_cast<const __bf16*>(W_res), B, H, Dm, zsplit);
+  // Row blocks per ResBlock workgroup: 2 (Dm % 32 == 0 always holds here), or as set by
+  // SPECTREE_RES_ROWBLOCKS (1, 2 or 4; tuning).
+  const char* rre = std::getenv("SPECTREE_RES_ROWBLOCKS");
+  int rrb = rre && *rre ? std::atoi(rre) : 2;
+  if (rrb != 1 && rrb != 2 && rrb != 4) rrb = 2;
+  const __bf16* hb = static_cast<const __bf16*>(h);
+  const __bf16* wr = static_cast<const __bf16*>(W_res);
+  if (rrb == 4) launch("medusa_resblock", resblock_kernel<4>, dim3(H * (Dm / 64)), blk, s, hb, wr, B, H, Dm, zsplit);
+  else if (rrb == 2) launch("medusa_resblock", resblock_kernel<2>, dim3(H * (Dm / 32)), blk, s, hb, wr, B, H, Dm, zsplit);
+  else launch("medusa_resblock", resblock_kernel<1>, dim3(H * (Dm / 16)), blk, s, hb, wr, B, H, Dm, zsplit);
   // 16-row blocks of W_lm per wave (RB): 8 by default, 4 with SPECTREE_LM_ROWBLOCKS=4 (tuning).
   const char* rbe = std::getenv("SPECTREE_LM_ROWBLOCKS");
   const int RBv = (rbe && std::atoi(rbe) == 4) ? 4 : 8;
