@@ -201,10 +201,13 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(VerifyArgs a) {
   const int p = (blockIdx.x / a.CR) % a.N;
   const int b = blockIdx.x / (a.CR * a.N);
   const int t = threadIdx.x;
+  // n_nodes and the parent entries are requested together (the parent load does not wait for
+  // n; its index is clamped into the row, and entries past n are ignored below)
   const int n = a.n_nodes ? a.n_nodes[b] : a.N;
+  const int par = a.parents[(size_t)b * a.N + min(max(t, 1), a.N - 1)];
   if (n < 0 || n > a.N || p >= n) return;
   // only rows of nodes that some node names as its parent are read
-  const int named = (t >= 1 && t < n && a.parents[(size_t)b * a.N + t] == p) ? 1 : 0;
+  const int named = (t >= 1 && t < n && par == p) ? 1 : 0;
   if (!__syncthreads_or(named)) return;
 
   const float* row = a.logits + ((size_t)b * a.N + p) * a.V;
@@ -264,9 +267,17 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
   __shared__ int s_err, s_best, s_minchild;
   const int b = blockIdx.x;
   const int c = threadIdx.x;
+  // Every load that does not depend on another is requested here, together: n_nodes, the
+  // parent, token, uniform and draft row of this thread's node (index clamped into the row;
+  // values of threads past n are ignored).
   const int n = a.n_nodes ? a.n_nodes[b] : a.N;
+  const size_t ci = (size_t)b * a.N + min(c, a.N - 1);
+  const int par_c = a.parents[ci];
+  const int tok_c = a.tokens[ci];
+  const float u_c = a.uniforms[ci];
+  const int drow_c = a.mode == SPEC_VERIFY_REJECT ? a.draft_row[ci] : -1;
   if (c == 0) { s_err = INT_MAX; s_best = -1; s_minchild = INT_MAX; }
-  if (c < a.N) { s_par[c] = a.parents[(size_t)b * a.N + c]; s_has[c] = 0; s_acc[c] = 0; }
+  if (c < a.N) { s_par[c] = par_c; s_has[c] = 0; s_acc[c] = 0; }
   __syncthreads();
   BonusPlan* plan = a.plans + b;
   if (n < 0 || n > a.N || n == 0) {
@@ -303,9 +314,9 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
     } else if (p < 0 || p >= c) {
       code = SPEC_ERR_PARENT;
     } else {
-      tok = a.tokens[(size_t)b * a.N + c];
-      u = a.uniforms[(size_t)b * a.N + c];
-      if (a.mode == SPEC_VERIFY_REJECT) drow = a.draft_row[(size_t)b * a.N + c];
+      tok = tok_c;
+      u = u_c;
+      drow = drow_c;
       int j = c;
       while (j > 0) {
         const int pj = s_par[j];
