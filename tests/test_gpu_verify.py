@@ -76,6 +76,18 @@ def test_small(case, mode):
             break
 
 
+@pytest.mark.parametrize("chunk", ["4096", "16384"])
+@pytest.mark.parametrize("case", [0, 2, 6])
+def test_row_chunk_sizes(monkeypatch, chunk, case):
+    """The row pass at each chunk size its tuning variable allows (8192 is the default)."""
+    monkeypatch.setenv("SPECTREE_VERIFY_CHUNK", chunk)
+    w = wl.custom(seed=3000 + case, **SMALL[case])
+    parents, n_nodes, vi = _case(w)
+    for mode in ("greedy", "typical", "reject"):
+        got, ref = _run(w, mode, vi, parents, n_nodes)
+        compare_verify(got, ref, n_nodes)
+
+
 def test_max_depth_and_errors():
     need_gpu()
     w = wl.custom(seed=41, B=8, N=20, V=64, tree=("random", 6))
