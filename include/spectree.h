@@ -22,10 +22,10 @@
  *     a sequence has several problems the smallest word is reported (lowest node index, then
  *     lowest code); sequence-level problems (node count, prefix length) take node 0 and are
  *     checked first.  A sequence with an error gets the documented neutral outputs.
- *   - Workspaces: query the size with the matching *_workspace() function.  A workspace must
- *     be zero-filled before its first use; every call leaves it zero-filled again in the
- *     regions it uses for cross-workgroup counters, so one workspace can be reused by
- *     back-to-back calls on one stream.  Calls that run concurrently need distinct workspaces.
+ *   - Workspaces: query the size with the matching *_workspace() function.  A workspace needs
+ *     no initialisation: every call writes each workspace byte it later reads (no call keeps
+ *     cross-workgroup counters), so one workspace can be reused by back-to-back calls on one
+ *     stream.  Calls that run concurrently need distinct workspaces.
  *   - Limits: N (tree nodes per sequence, padding included) <= 256.
  */
 #ifndef SPECTREE_H
