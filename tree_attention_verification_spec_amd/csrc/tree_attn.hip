@@ -28,11 +28,12 @@
 //
 // Work split: grid = units x row blocks x key splits.  A split covers a contiguous key range
 // of the unit (prefix and tree slots alike), computed on the device from prefix_len and
-// n_nodes.  With more than one split, each workgroup stores its unnormalised partial output
-// and (max, sum) to the workspace and a second kernel merges them (the kernel boundary orders
-// the two; no workgroup waits on another).  Workgroups of one unit are placed on one XCD
-// (dispatch goes round-robin over the 8 XCDs) in both kernels, so the unit's K/V tiles, Q rows
-// and partials share that XCD's L2.
+// n_nodes.  With more than one split, each workgroup stores its output normalised by its own
+// sum (bf16) and its (max, sum) to the workspace and a second kernel merges them as a convex
+// combination (the kernel boundary orders the two; no workgroup waits on another).  Workgroups
+// of one unit are placed on one XCD (dispatch goes round-robin over the 8 XCDs) in both
+// kernels, so the unit's K/V tiles, Q rows and partials share that XCD's L2; in a batch the
+// sequences are dispatched longest first.
 //
 // fp32 path: a plain exact-fp32 kernel (one workgroup per query row) for small fp32 inputs.
 #include <climits>
@@ -45,6 +46,7 @@ namespace {
 
 constexpr int kKT = 64;        // keys per tile
 constexpr int kThreads = 256;  // merge kernel workgroup
+constexpr int kMaxLptSeqs = 256;  // longest-first ordering for batches up to this size
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -65,10 +67,11 @@ struct AttnArgs {
   float* lse;
   int32_t* err;
   // workspace
-  float2* part_ml;             // [U, S, Mpad]
-  float* part_o;               // [U, S, Mpad, D]
+  float2* part_ml;             // [U, S, Mpad]: (max, sum) of each split
+  __bf16* part_o;              // [U, S, Mpad, D]: each split's output normalised by its own sum
   int R, S, Mpad;
   int prio;                    // raise wave priority around the MFMA blocks
+  int lpt;                     // dispatch sequences longest first (batches of 2..256)
 };
 
 __device__ __forceinline__ bool seq_valid(int n, int P, int N, int S_max) {
@@ -83,7 +86,10 @@ __device__ __forceinline__ int seq_err(int n, int P, int N, int S_max) {
 
 // Map the linear workgroup id to (unit, row block, split) so that all workgroups of a unit
 // land on the same XCD (hardware dispatches consecutive workgroup ids round-robin over 8
-// XCDs).  Returns false for padding workgroups.
+// XCDs).  With a.lpt, sequences are taken longest first (prefix + nodes, ties by index): every
+// workgroup ranks the B lengths in LDS, and since each XCD takes its workgroups in id order,
+// the longest sequences' splits start first and the short ones fill in behind them.  Returns
+// false for padding workgroups.
 __device__ __forceinline__ bool decode_wg(const AttnArgs& a, int& u, int& rb, int& split) {
   const int bid = blockIdx.x;
   const int xcd = bid & 7;
@@ -94,7 +100,27 @@ __device__ __forceinline__ bool decode_wg(const AttnArgs& a, int& u, int& rb, in
   u = xcd + 8 * lu;
   rb = w % a.R;
   split = w / a.R;
-  return u < a.B * a.Hkv;
+  if (u >= a.B * a.Hkv) return false;
+  if (a.lpt) {
+    __shared__ int s_len[kMaxLptSeqs];
+    __shared__ int s_order[kMaxLptSeqs];
+    for (int t = threadIdx.x; t < a.B; t += blockDim.x) {
+      const int n = a.n_nodes ? a.n_nodes[t] : a.N;
+      const int P = a.prefix_len[t];
+      s_len[t] = (n >= 0 && n <= a.N && P >= 0 && P + n <= a.S_max) ? P + n : 0;
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < a.B; t += blockDim.x) {
+      const int lt = s_len[t];
+      int r = 0;
+      for (int j = 0; j < a.B; ++j) r += (s_len[j] > lt || (s_len[j] == lt && j < t)) ? 1 : 0;
+      s_order[r] = t;
+    }
+    __syncthreads();
+    const int seq = u / a.Hkv;                   // rank of the sequence this workgroup takes
+    u = s_order[seq] * a.Hkv + (u - seq * a.Hkv);
+  }
+  return true;
 }
 
 // A-operand fragment of V^T for output dims [d0, d0 + 16) and keys c32 + {4 lg + s, 16 + 4 lg + s}.
@@ -384,26 +410,35 @@ void tree_attn_bf16_kernel(AttnArgs a) {
     return;
   }
 
-  // ---- several splits: store the unnormalised partials; the merge kernel combines them.
+  // ---- several splits: store each split's output normalised by its own sum (bf16, like the
+  // final output; the merge takes a convex combination of them) and its (max, sum) in fp32.
   const size_t pbase = ((size_t)u * a.S + split) * a.Mpad;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const int r = rb * RBS + wave * ROWS_WAVE + cb * 16 + l16;
-    float* dst = a.part_o + (pbase + r) * D;
+    const bool live = row_ok[cb] && l_run[cb] > 0.f;
+    const float inv = live ? 1.f / l_run[cb] : 0.f;
+    __bf16* dst = a.part_o + (pbase + r) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(dst + db * 16 + 4 * lg) = o_acc[db][cb];
-    if (lg == 0) a.part_ml[pbase + r] = make_float2(row_ok[cb] ? m_run[cb] : -INFINITY, row_ok[cb] ? l_run[cb] : 0.f);
+    for (int db = 0; db < DB; ++db) {
+      bf16x4 o4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(o_acc[db][cb][e] * inv);
+      *reinterpret_cast<bf16x4*>(dst + db * 16 + 4 * lg) = o4;
+    }
+    if (lg == 0) a.part_ml[pbase + r] = make_float2(live ? m_run[cb] : -INFINITY, live ? l_run[cb] : 0.f);
   }
 }
 
-// Merge of the key splits.  One workgroup per (unit, 16 query rows); thread -> (row, 4 output
-// dims); the splits are folded with a running max, loads for 8 splits issued together.
-// Workgroups of a unit run on the unit's XCD (as in the main kernel), where its partials sit
-// in L2.
-template <int D>
+// Merge of the key splits.  Thread -> (row, 8 output dims), 16-byte loads; a workgroup covers
+// 256 / (D / 8) rows of one unit.  The splits are folded with a running max, SB splits' loads
+// issued together (SB >= S up to 8, so no load is repeated); the partial loads do not wait for
+// the sequence's validity, which only decides the store.  Workgroups of a unit run on the
+// unit's XCD (as in the main kernel), where its partials sit in L2.
+template <int D, int SB>
 __global__ __launch_bounds__(kThreads) void tree_attn_merge_kernel(AttnArgs a) {
-  constexpr int C4 = D / 4;
-  constexpr int ROWS = kThreads / C4;          // rows per workgroup (8 at D = 128)
+  constexpr int C8 = D / 8;
+  constexpr int ROWS = kThreads / C8;          // rows per workgroup (16 at D = 128)
   const int bid = blockIdx.x;
   const int xcd = bid & 7;
   const int slot = bid >> 3;
@@ -411,46 +446,56 @@ __global__ __launch_bounds__(kThreads) void tree_attn_merge_kernel(AttnArgs a) {
   const int lu = slot / per_unit;
   const int u = xcd + 8 * lu;
   if (u >= a.B * a.Hkv) return;
-  const int r = (slot - lu * per_unit) * ROWS + threadIdx.x / C4;
-  const int d4 = threadIdx.x % C4;
+  const int r = (slot - lu * per_unit) * ROWS + threadIdx.x / C8;
+  const int d8 = threadIdx.x % C8;
   const int M = a.N * a.G;
   if (r >= M) return;
   const int b = u / a.Hkv, g = u - b * a.Hkv;
   const int n = a.n_nodes ? a.n_nodes[b] : a.N;
   const int P = a.prefix_len[b];
-  if (!seq_valid(n, P, a.N, a.S_max)) return;  // the main kernel wrote zeros and the error
-  const int i = r / a.G, h = g * a.G + r % a.G;
   float mrun = -INFINITY, L = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < a.S; s0 += 8) {
-    float2 ml[8];
-    f32x4 po[8];
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  for (int s0 = 0; s0 < a.S; s0 += SB) {
+    float2 ml[SB];
+    bf16x8 po[SB];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int s = s0 + k < a.S ? s0 + k : 0;
+    for (int k = 0; k < SB; ++k) {
+      const int s = min(s0 + k, a.S - 1);
       const size_t pr = ((size_t)u * a.S + s) * a.Mpad + r;
       ml[k] = a.part_ml[pr];
-      po[k] = *reinterpret_cast<const f32x4*>(a.part_o + pr * D + 4 * d4);
+      po[k] = *reinterpret_cast<const bf16x8*>(a.part_o + pr * D + 8 * d8);
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < SB; ++k) {
       if (s0 + k >= a.S || ml[k].x == -INFINITY) continue;
       const float mn = fmaxf(mrun, ml[k].x);
       const float sc_old = __builtin_amdgcn_exp2f(mrun - mn);   // 0 when mrun = -inf
-      const float sc_new = __builtin_amdgcn_exp2f(ml[k].x - mn);
-      L = L * sc_old + ml[k].y * sc_new;
-      acc = acc * sc_old + po[k] * sc_new;
+      const float w = ml[k].y * __builtin_amdgcn_exp2f(ml[k].x - mn);   // this split's weight
+      L = L * sc_old + w;
+      f32x4 p0, p1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p0[e] = (float)po[k][e];
+        p1[e] = (float)po[k][4 + e];
+      }
+      acc0 = acc0 * sc_old + p0 * w;
+      acc1 = acc1 * sc_old + p1 * w;
       mrun = mn;
     }
   }
+  if (!seq_valid(n, P, a.N, a.S_max)) return;  // the main kernel wrote zeros and the error
+  const int i = r / a.G, h = g * a.G + r % a.G;
   const bool live = i < n && L > 0.f;
   const float inv = live ? 1.f / L : 0.f;
-  bf16x4 o4;
+  bf16x8 o8;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[e] * inv);
+  for (int e = 0; e < 4; ++e) {
+    o8[e] = (__bf16)(acc0[e] * inv);
+    o8[4 + e] = (__bf16)(acc1[e] * inv);
+  }
   __bf16* op = static_cast<__bf16*>(a.out);
-  *reinterpret_cast<bf16x4*>(op + (((size_t)b * a.N + i) * a.Hq + h) * D + 4 * d4) = o4;
-  if (a.lse && d4 == 0) a.lse[((size_t)b * a.N + i) * a.Hq + h] = live ? (mrun + log2f(L)) * kLn2 : -INFINITY;
+  *reinterpret_cast<bf16x8*>(op + (((size_t)b * a.N + i) * a.Hq + h) * D + 8 * d8) = o8;
+  if (a.lse && d8 == 0) a.lse[((size_t)b * a.N + i) * a.Hq + h] = live ? (mrun + log2f(L)) * kLn2 : -INFINITY;
 }
 
 // Exact fp32 path: one workgroup of 256 threads per query row (b, node, head).  Keys are taken
@@ -542,7 +587,7 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnArgs a) {
 }
 
 struct Plan {
-  int CB, WAVES, RBS, R, S, Mpad, units, wgs;
+  int CB, WAVES, RBS, R, S, Mpad, units, wgs, lpt;
 };
 
 int env_int(const char* name, int fallback) {
@@ -553,8 +598,9 @@ int env_int(const char* name, int fallback) {
 // Launch shape.  Few (sequence, KV head) units -> 64-row workgroups (4 waves of 16 rows) and
 // more key splits so that all CUs work; many units -> 256-row workgroups (8 waves of 32 rows:
 // the K/V tile in LDS serves 4x more rows per read) and few splits.  Splits are chosen for
-// about 256 workgroups (one round; an unsplit problem needs no merge), and every split keeps
-// at least two tiles.  SPECTREE_ATTN_CB, SPECTREE_ATTN_WAVES and SPECTREE_ATTN_SPLITS override the
+// about 256 workgroups (one round; an unsplit problem needs no merge), at least two for a large
+// batch (its sequences may differ in length), and every split keeps at least two tiles.
+// SPECTREE_ATTN_LPT=0/1 turns the longest-first order off or on (tuning).  SPECTREE_ATTN_CB, SPECTREE_ATTN_WAVES and SPECTREE_ATTN_SPLITS override the
 // choice (tuning knobs; results do not depend on them).
 Plan make_plan(int B, int N, int Hq, int Hkv, int D, int S_max) {
   Plan p{};
@@ -572,7 +618,12 @@ Plan make_plan(int B, int N, int Hq, int Hkv, int D, int S_max) {
   const int target = 256;   // one workgroup per CU, all in one round (measured best)
   const int tiles = (S_max + kKT - 1) / kKT;
   int S = (target + p.units * p.R - 1) / (p.units * p.R);
+  // Batches may mix prefix lengths: at least two splits, taken longest sequence first, so that
+  // the halves of long sequences are not left running alone at the end.
+  p.lpt = B >= 2 && B <= kMaxLptSeqs;
+  if (big && p.lpt && S < 2) S = 2;
   S = env_int("SPECTREE_ATTN_SPLITS", S);
+  p.lpt = env_int("SPECTREE_ATTN_LPT", p.lpt) != 0 && B >= 2 && B <= kMaxLptSeqs;
   if (S > tiles / 2) S = tiles / 2;
   if (S < 1) S = 1;
   p.S = S;
@@ -597,7 +648,7 @@ void launch_bf16(const Plan& p, const AttnArgs& a, hipStream_t s) {
 size_t workspace_bytes(const Plan& p, int D) {
   if (p.S == 1) return 0;
   size_t off = align_up((size_t)p.units * p.S * p.Mpad * sizeof(float2), 256);
-  off += align_up((size_t)p.units * p.S * p.Mpad * D * sizeof(float), 256);
+  off += align_up((size_t)p.units * p.S * p.Mpad * D * sizeof(__bf16), 256);
   return off;
 }
 
@@ -644,20 +695,30 @@ extern "C" spec_status spec_tree_attn(const void* q, const void* k_cache, const 
   if (need > 0 && (!workspace || ws_bytes < need)) return SPEC_EWORKSPACE;
   a.R = p.R; a.S = p.S; a.Mpad = p.Mpad;
   a.prio = env_int("SPECTREE_ATTN_PRIO", 1);
+  a.lpt = p.lpt;
   if (p.S > 1) {
     char* w = static_cast<char*>(workspace);
     size_t off = 0;
     a.part_ml = reinterpret_cast<float2*>(w + off);
     off += align_up((size_t)p.units * p.S * p.Mpad * sizeof(float2), 256);
-    a.part_o = reinterpret_cast<float*>(w + off);
+    a.part_o = reinterpret_cast<__bf16*>(w + off);
   }
   if (head_dim == 128) launch_bf16<128>(p, a, s);
   else launch_bf16<64>(p, a, s);
   if (p.S > 1) {
-    const int rows_per_wg = kThreads / (head_dim / 4);
+    const int rows_per_wg = kThreads / (head_dim / 8);
     const dim3 mgrid(8 * ((p.units + 7) / 8) * (p.Mpad / rows_per_wg));
-    if (head_dim == 128) launch("tree_attn_merge", tree_attn_merge_kernel<128>, mgrid, dim3(kThreads), s, a);
-    else launch("tree_attn_merge", tree_attn_merge_kernel<64>, mgrid, dim3(kThreads), s, a);
+    const char* mn = "tree_attn_merge";
+    const dim3 mb(kThreads);
+    if (head_dim == 128) {
+      if (p.S <= 2) launch(mn, tree_attn_merge_kernel<128, 2>, mgrid, mb, s, a);
+      else if (p.S <= 4) launch(mn, tree_attn_merge_kernel<128, 4>, mgrid, mb, s, a);
+      else launch(mn, tree_attn_merge_kernel<128, 8>, mgrid, mb, s, a);
+    } else {
+      if (p.S <= 2) launch(mn, tree_attn_merge_kernel<64, 2>, mgrid, mb, s, a);
+      else if (p.S <= 4) launch(mn, tree_attn_merge_kernel<64, 4>, mgrid, mb, s, a);
+      else launch(mn, tree_attn_merge_kernel<64, 8>, mgrid, mb, s, a);
+    }
   }
   return launch_status();
 }
