@@ -641,15 +641,17 @@ __device__ int draw(const VerifyArgs& a, int b, int kind, int r, const float* ro
 template <int VEC>
 __global__ __launch_bounds__(kThreads) void select_kernel(VerifyArgs a) {
   const int b = blockIdx.x;
-  const BonusPlan pl = a.plans[b];
-  if (pl.kind == 0) return;
   const int t = threadIdx.x;
+  // the plan and this thread's chunk part are requested together (the part's index does not
+  // depend on the plan; threads past C read part 0 and ignore it)
+  const BonusPlan pl = a.plans[b];
+  const BonusPart bp = a.bparts[(size_t)b * a.C + (t < a.C ? t : 0)];
+  if (pl.kind == 0) return;
   // merge the chunk parts (one per thread): row max / argmax / nonfinite
   double Sc = 0.0, Qc = 0.0;
   float mc = -INFINITY;
   int amc = INT_MAX, nf = 0;
   if (t < a.C) {
-    const BonusPart bp = a.bparts[(size_t)b * a.C + t];
     Sc = bp.S; Qc = bp.Q; mc = bp.m; amc = bp.argmax; nf = bp.nonfinite;
   }
   float m = mc;
