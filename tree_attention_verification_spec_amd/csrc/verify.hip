@@ -227,14 +227,21 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(VerifyArgs a) {
     }
   }
   block_argmax(m, am, nf);
+  // sum exp(x - max); the entropy term sum exp(x - max)(x - max) only in typical mode (the
+  // other modes never read it)
   double S = 0.0, A = 0.0;
   if (m != -INFINITY && !nf) {
+    if (a.mode == SPEC_VERIFY_TYPICAL) {
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const float d = x[k] - m;            // -inf past the chunk -> exp 0
-      const float ex = __expf(d);
-      S += (double)ex;
-      A += (ex > 0.f) ? (double)ex * (double)d : 0.0;
+      for (int k = 0; k < PER; ++k) {
+        const float d = x[k] - m;          // -inf past the chunk -> exp 0
+        const float ex = __expf(d);
+        S += (double)ex;
+        A += (ex > 0.f) ? (double)ex * (double)d : 0.0;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < PER; ++k) S += (double)__expf(x[k] - m);
     }
   }
   block_sum2(S, A);
