@@ -88,6 +88,19 @@ def test_row_chunk_sizes(monkeypatch, chunk, case):
         compare_verify(got, ref, n_nodes)
 
 
+@pytest.mark.parametrize("store", ["0", "1"])
+@pytest.mark.parametrize("case", [0, 1, 3, 6])
+def test_draw_weights_stored_or_recomputed(monkeypatch, store, case):
+    """The bonus draw scans weights stored by the bonus pass (small batches by default) or
+    recomputes them (large batches): both paths, forced, on every mode."""
+    monkeypatch.setenv("SPECTREE_VERIFY_STORE_W", store)
+    w = wl.custom(seed=3000 + case, **SMALL[case])
+    parents, n_nodes, vi = _case(w)
+    for mode in ("greedy", "typical", "reject"):
+        got, ref = _run(w, mode, vi, parents, n_nodes)
+        compare_verify(got, ref, n_nodes)
+
+
 def test_max_depth_and_errors():
     need_gpu()
     w = wl.custom(seed=41, B=8, N=20, V=64, tree=("random", 6))

@@ -33,6 +33,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBonusChunk = 4096;            // logits per workgroup in the bonus pass
 constexpr int kPer = kBonusChunk / kThreads;
+constexpr int kStoreWeightsMaxB = 8;          // batches that keep the bonus pass's weights
 constexpr int kPartsPerLane = 8;             // row-chunk partials per merging lane and batch
 
 struct RowPart {      // one chunk of one logits row
@@ -84,6 +85,8 @@ struct VerifyArgs {
   RowPart* rowparts;    // [B, N, CR]
   BonusPlan* plans;     // [B]
   BonusPart* bparts;    // [B, C]
+  double* weights;      // [B, C * CS]: the bonus pass's per-token weights (kinds 2 and 3),
+                        // kept only for small batches (NULL otherwise)
 };
 
 // ------------------------------------------------------------------ reductions
@@ -528,7 +531,14 @@ __global__ __launch_bounds__(kThreads) void bonus_kernel(VerifyArgs a) {
     }
   }
   block_argmax(m, am, nf);                 // chunk max / argmax / nonfinite, in every thread
+  // For small batches each token's weight of the draw (kind 3: relu(T - D); kind 2:
+  // exp(x - chunk max)) is also stored, so that the draw scans exactly these values instead of
+  // re-gathering and recomputing them (one dependent round trip less on a latency-bound path;
+  // for large batches writing B x V fp64 weights costs more than it saves).
   double S = 0.0, Q = 0.0;
+  double w[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) w[k] = 0.0;
   if (!nf && pl.kind == 3) {
     // exp(x - M) with the row max, and relu(T - D) with T normalised by the row statistics
     const double inv = 1.0 / pl.S;
@@ -537,12 +547,29 @@ __global__ __launch_bounds__(kThreads) void bonus_kernel(VerifyArgs a) {
       if (chunk_index<VEC>(lo, k) < hi) {
         const double e = exp((double)x[k] - (double)pl.M);
         S += e;
-        Q += fmax(e * inv - dr[k], 0.0);
+        w[k] = fmax(e * inv - dr[k], 0.0);
+        Q += w[k];
       }
     }
   } else if (!nf && pl.kind == 2 && m != -INFINITY) {
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) S += (x[k] == -INFINITY) ? 0.0 : exp((double)x[k] - (double)m);
+    for (int k = 0; k < kPer; ++k) {
+      w[k] = (x[k] == -INFINITY) ? 0.0 : exp((double)x[k] - (double)m);
+      S += w[k];
+    }
+  }
+  if (a.weights && pl.kind >= 2) {
+    double* wrow = a.weights + (size_t)b * a.C * a.CS;
+#pragma unroll
+    for (int k = 0; k < kPer; k += 2) {       // chunk_index(k + 1) == chunk_index(k) + 1 for even k
+      const int v = chunk_index<VEC>(lo, k);
+      if (VEC >= 2) {
+        *reinterpret_cast<double2*>(wrow + v) = make_double2(w[k], w[k + 1]);
+      } else {
+        wrow[v] = w[k];
+        wrow[chunk_index<VEC>(lo, k + 1)] = w[k + 1];
+      }
+    }
   }
   block_sum2(S, Q);
   if (pl.kind == 3) m = pl.M;              // S is relative to the row max
@@ -645,6 +672,80 @@ __device__ int draw(const VerifyArgs& a, int b, int kind, int r, const float* ro
   return tok;
 }
 
+// Smallest token of chunk [lo, hi) whose running sum of the stored weights (times scale, from
+// `base`, fp64, ascending token order) exceeds thr; -1 if none.  Thread t owns a contiguous run
+// of `per` tokens (even, so the run is read with 16-byte loads).
+__device__ int scan_stored(const double* wrow, int lo, int hi, double scale, double base, double thr) {
+  __shared__ int s_hit;
+  const int per = (hi - lo + kThreads * 2 - 1) / (kThreads * 2) * 2;   // <= kPer
+  const int my_lo = lo + (int)threadIdx.x * per;
+  double w[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; k += 2) {
+    const int v = my_lo + k;
+    const bool in = k < per && v < hi;
+    const double2 p = *reinterpret_cast<const double2*>(wrow + (in ? v : lo));
+    w[k] = in ? p.x * scale : 0.0;
+    w[k + 1] = (in && v + 1 < hi) ? p.y * scale : 0.0;
+  }
+  double mine = 0.0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) mine += w[k];
+  if (threadIdx.x == 0) s_hit = INT_MAX;
+  double total;
+  const double before = base + (block_scan(mine, total) - mine);   // barriers inside
+  if (before + mine > thr) {
+    double run = before;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      run += w[k];
+      if (k < per && my_lo + k < hi && run > thr) { atomicMin(&s_hit, my_lo + k); break; }
+    }
+  }
+  __syncthreads();
+  const int hit = s_hit;
+  __syncthreads();
+  return hit == INT_MAX ? -1 : hit;
+}
+
+// Inverse-CDF draw over the weights stored by the bonus pass: thread t < C holds chunk t's sum
+// q and the factor that scales its stored weights (1 for a residual draw; exp(chunk max - row
+// max) for a draw from T).  Same chunk choice and rounding fallbacks as draw().
+__device__ int draw_stored(const VerifyArgs& a, int b, double q, double scale) {
+  __shared__ int s_pick, s_last, s_tok;
+  __shared__ double s_base[2], s_scale[2];
+  const int t = threadIdx.x;
+  if (t >= a.C) q = 0.0;
+  if (t == 0) { s_pick = INT_MAX; s_last = -1; }
+  double Z;
+  const double incl = block_scan(q, Z);                           // barriers inside
+  const double thr = (double)a.uniforms[(size_t)b * a.N] * Z;
+  if (t < a.C && incl > thr) atomicMin(&s_pick, t);
+  if (t < a.C && q > 0.0) atomicMax(&s_last, t);
+  __syncthreads();
+  const int pick = s_pick, last = s_last;
+  if (t == pick) { s_base[0] = incl - q; s_scale[0] = scale; }
+  if (t == last) { s_base[1] = incl - q; s_scale[1] = scale; }
+  __syncthreads();
+  const int k = pick != INT_MAX ? 0 : 1;
+  const int cs = pick != INT_MAX ? pick : (last >= 0 ? last : 0);
+  const double base = (pick != INT_MAX || last >= 0) ? s_base[k] : 0.0;
+  const double sc = (pick != INT_MAX || last >= 0) ? s_scale[k] : 1.0;
+  const int lo = cs * a.CS, hi = min(a.V, lo + a.CS);
+  const double* wrow = a.weights + (size_t)b * a.C * a.CS;
+  int tok = scan_stored(wrow, lo, hi, sc, base, thr);
+  if (tok < 0) {                            // rounding put thr at the chunk's end
+    if (t == 0) {
+      s_tok = -1;
+      for (int v = hi - 1; v >= lo; --v)
+        if (wrow[v] * sc > 0.0) { s_tok = v; break; }
+    }
+    __syncthreads();
+    tok = s_tok;
+  }
+  return tok;
+}
+
 template <int VEC>
 __global__ __launch_bounds__(kThreads) void select_kernel(VerifyArgs a) {
   const int b = blockIdx.x;
@@ -675,11 +776,12 @@ __global__ __launch_bounds__(kThreads) void select_kernel(VerifyArgs a) {
   const float* row = a.logits + ((size_t)b * a.N + pl.m) * a.V;
   int tok;
   if (pl.kind == 2) {
-    const double q = (mc == -INFINITY) ? 0.0 : Sc * exp((double)mc - (double)m);
-    tok = draw<VEC>(a, b, 2, pl.r, row, q, m, 0.0);
+    const double sc = (mc == -INFINITY) ? 0.0 : exp((double)mc - (double)m);
+    if (a.weights) tok = draw_stored(a, b, Sc * sc, sc);
+    else tok = draw<VEC>(a, b, 2, pl.r, row, Sc * sc, m, 0.0);
   } else {
     const double Z = block_sum(t < a.C ? Qc : 0.0);
-    if (Z > 0.0) tok = draw<VEC>(a, b, 3, pl.r, row, Qc, pl.M, pl.S);
+    if (Z > 0.0) tok = a.weights ? draw_stored(a, b, Qc, 1.0) : draw<VEC>(a, b, 3, pl.r, row, Qc, pl.M, pl.S);
     else tok = draw<VEC>(a, b, 2, pl.r, row, Sc, pl.M, pl.S);   // residual of zero mass: T_m
   }
   if (t == 0) a.bonus[b] = tok;
@@ -689,7 +791,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(VerifyArgs a) {
 
 struct VerifyLayout {
   int RC, CR, CS, C;
-  size_t rowparts, plans, bparts, total;
+  bool store_w;
+  size_t rowparts, plans, bparts, weights, total;
 };
 
 // Row-pass chunk: 8K logits (measured faster than 4K and 16K at batch 1 and 16).
@@ -715,6 +818,12 @@ VerifyLayout layout(int B, int N, int V) {
   L.rowparts = take((size_t)B * N * L.CR * sizeof(RowPart));
   L.plans = take((size_t)B * sizeof(BonusPlan));
   L.bparts = take((size_t)B * L.C * sizeof(BonusPart));
+  // Stored draw weights are used for batches up to kStoreWeightsMaxB (SPECTREE_VERIFY_STORE_W=0/1
+  // overrides); their region is always reserved, so that the workspace size grows with B and a
+  // workspace sized for a batch also serves every smaller one.
+  const char* sw = std::getenv("SPECTREE_VERIFY_STORE_W");
+  L.store_w = (sw && *sw) ? std::atoi(sw) != 0 : B <= kStoreWeightsMaxB;
+  L.weights = take((size_t)B * L.C * L.CS * sizeof(double));
   L.total = off;
   return L;
 }
@@ -761,6 +870,7 @@ extern "C" spec_status spec_verify(const float* target_logits, const float* draf
   a.rowparts = reinterpret_cast<RowPart*>(w + L.rowparts);
   a.plans = reinterpret_cast<BonusPlan*>(w + L.plans);
   a.bparts = reinterpret_cast<BonusPart*>(w + L.bparts);
+  a.weights = L.store_w ? reinterpret_cast<double*>(w + L.weights) : nullptr;
 
   const dim3 blk(kThreads);
   const dim3 grid_rows((unsigned)((size_t)L.CR * N * B)), grid_chunks((unsigned)((size_t)L.C * B));
