@@ -11,16 +11,18 @@
 // order their results), and every global load is issued before it is needed.
 //   rows    grid (seq, node, chunk): rows of nodes with children are split into chunks of
 //           8K logits; each workgroup streams its chunk once (float4 loads held in registers)
-//           into (max, lowest argmax, sum exp(x - max), sum exp(x - max)(x - max)), fp32 exp
-//           with fp64 sums.  Workgroups of leaf rows leave after a 1 KB look at the parents.
-//   decide  one workgroup per sequence, one thread per node: merge of the row chunks,
+//           into (max, lowest argmax, sum exp(x - max) and, for typical acceptance,
+//           sum exp(x - max)(x - max)), fp32 exp with fp64 sums.  Workgroups of leaf rows leave
+//           after a 1 KB look at the parents.
+//   decide  one workgroup per sequence: merge of the row chunks (1-4 lanes per node),
 //           validation, node tests in fp64, survival = AND over the parent chain, the deepest
 //           survivor (LDS max on depth, -index), the path, and the plan of the bonus draw.
 //   bonus   grid (seq, chunk) over the kept row m: chunk max / argmax, and fp64 chunk sums of
 //           exp(x - max) and, for a residual draw, of relu(T - D) with T normalised by the row
-//           statistics of the first kernel.
-//   select  one workgroup per sequence: the chunk holding u * Z, then an in-order fp64 scan
-//           inside it for the smallest token whose running sum exceeds u * Z.
+//           statistics of the first kernel; small batches also keep each token's weight.
+//   select  one workgroup per sequence: the chunk holding u * Z (shuffle scan of the chunk
+//           sums), then an in-order fp64 scan inside it (of the kept weights, or recomputed
+//           ones) for the smallest token whose running sum exceeds u * Z.
 #include <cfloat>
 #include <climits>
 #include <cstdlib>
