@@ -276,20 +276,45 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
   __shared__ int s_am[SPEC_MAX_NODES];
   __shared__ double s_S[SPEC_MAX_NODES];
   __shared__ double s_H[SPEC_MAX_NODES];
+  __shared__ int s_drow[SPEC_MAX_NODES];
   __shared__ int s_err, s_best, s_minchild;
   const int b = blockIdx.x;
   const int c = threadIdx.x;
   // Every load that does not depend on another is requested here, together: n_nodes, the
-  // parent, token, uniform and draft row of this thread's node (index clamped into the row;
-  // values of threads past n are ignored).
+  // parent, token, uniform and draft row of this thread's node, and the chunk partials this
+  // lane merges (L lanes per node: 4, 2 or 1 for up to 64, 128 or 256 nodes, each lane a
+  // strided subset of the chunks).  Indices are clamped into their arrays; what a thread reads
+  // for a node past n, or for a row without children (whose partials were never written), is
+  // ignored.
   const int n = a.n_nodes ? a.n_nodes[b] : a.N;
   const size_t ci = (size_t)b * a.N + min(c, a.N - 1);
   const int par_c = a.parents[ci];
   const int tok_c = a.tokens[ci];
   const float u_c = a.uniforms[ci];
   const int drow_c = a.mode == SPEC_VERIFY_REJECT ? a.draft_row[ci] : -1;
+  const int L = a.N <= 64 ? 4 : (a.N <= 128 ? 2 : 1);
+  const int mn = c / L, sub = c % L;
+  const RowPart* rp = a.rowparts + ((size_t)b * a.N + min(mn, a.N - 1)) * a.CR;
+  RowPart q[kPartsPerLane];
+#pragma unroll
+  for (int k = 0; k < kPartsPerLane; ++k) {
+    const int ck = sub + k * L;
+    q[k] = rp[ck < a.CR ? ck : 0];
+  }
+  // Second round, in flight during the merge: the target logit of this node's token in its
+  // parent's row and, for rejection sampling, either the draft probability of that token (one
+  // vocabulary) or its draft-vocabulary index (the probability is then gathered after the
+  // merge).  Both loads are unconditional, from a pointer chosen per launch, so that no branch
+  // makes the merge wait for them; their values are used only once the node is validated.
+  const int pc = min(max(par_c, 0), a.N - 1);
+  const int tc = min(max(tok_c, 0), a.V - 1);
+  const float lpx_c = a.logits[((size_t)b * a.N + pc) * a.V + tc];
+  const bool rej = a.mode == SPEC_VERIFY_REJECT;
+  const size_t drow_off = rej ? ((size_t)b * a.R + min(max(drow_c, 0), a.R - 1)) * a.Vd : 0;
+  const float dval_c = *((rej && !a.t2d) ? a.draft + drow_off + tc : a.logits);
+  const int dx_c = *((rej && a.t2d) ? a.t2d + tc : a.parents);
   if (c == 0) { s_err = INT_MAX; s_best = -1; s_minchild = INT_MAX; }
-  if (c < a.N) { s_par[c] = par_c; s_has[c] = 0; s_acc[c] = 0; }
+  if (c < a.N) { s_par[c] = par_c; s_has[c] = 0; s_acc[c] = 0; s_drow[c] = drow_c; }
   __syncthreads();
   BonusPlan* plan = a.plans + b;
   if (n < 0 || n > a.N || n == 0) {
@@ -304,19 +329,7 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
     if (p >= 0 && p < c) s_has[p] = 1;
   }
   __syncthreads();
-  // Chunk partials of the rows that have children, merged by L lanes per node (4, 2 or 1 for
-  // up to 64, 128 or 256 nodes), each lane a strided subset of the chunks.  They are loaded
-  // before this thread's own token / uniform / draft row.
-  const int L = a.N <= 64 ? 4 : (a.N <= 128 ? 2 : 1);
-  const int mn = c / L, sub = c % L;
   const bool mhas = mn < n && s_has[mn];
-  const RowPart* rp = a.rowparts + ((size_t)b * a.N + (mhas ? mn : 0)) * a.CR;
-  RowPart q[kPartsPerLane];
-#pragma unroll
-  for (int k = 0; k < kPartsPerLane; ++k) {
-    const int ck = sub + k * L;
-    q[k] = rp[ck < a.CR ? ck : 0];
-  }
   int code = 0, depth = 0, tok = -1, drow = -1, dx = -1;
   float u = 0.f;
   if (c < n) {
@@ -340,12 +353,7 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
       else if (tok < 0 || tok >= a.V) code = SPEC_ERR_TOKEN;
       if (code == 0 && a.mode == SPEC_VERIFY_REJECT) {
         if (drow < 0 || drow >= a.R) code = SPEC_ERR_DRAFTROW;
-        else if (a.t2d) {
-          dx = a.t2d[tok];
-          if (dx < -1 || dx >= a.Vd) code = SPEC_ERR_MAP;
-        } else {
-          dx = tok;
-        }
+        else dx = tok;                          // mapped (and checked) after the merge
       }
     }
     s_dep[c] = depth;
@@ -421,6 +429,10 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
       s_H[mn] = log(S) - A / S;
     }
   }
+  if (code == 0 && dx >= 0 && a.t2d) {
+    dx = dx_c;
+    if (dx < -1 || dx >= a.Vd) code = SPEC_ERR_MAP;
+  }
   if (code) atomicMin(&s_err, err_word(c, code));
   __syncthreads();
   if (s_err != INT_MAX) {
@@ -432,8 +444,7 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
   // ---- per-node tests (fp64)
   if (c >= 1 && c < n) {
     const int p = s_par[c];
-    const float lpx = a.logits[((size_t)b * a.N + p) * a.V + tok];
-    const double T = exp((double)lpx - (double)s_mx[p]) / s_S[p];
+    const double T = exp((double)lpx_c - (double)s_mx[p]) / s_S[p];
     bool acc;
     if (a.mode == SPEC_VERIFY_GREEDY) {
       acc = tok == s_am[p];
@@ -441,7 +452,8 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
       const double tau = fmin((double)a.eps, (double)a.delta * exp(-s_H[p]));
       acc = T >= tau;
     } else {
-      const double d = dx >= 0 ? (double)a.draft[((size_t)b * a.R + drow) * a.Vd + dx] : 0.0;
+      double d = 0.0;
+      if (dx >= 0) d = a.t2d ? (double)a.draft[drow_off + dx] : (double)dval_c;
       acc = (double)u * d < T;
     }
     s_acc[c] = acc ? 1 : 0;
@@ -483,7 +495,7 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
       pl.kind = 2;
     } else if (s_minchild != INT_MAX) {
       pl.kind = 3;
-      pl.r = a.draft_row[(size_t)b * a.N + s_minchild];
+      pl.r = s_drow[s_minchild];
       pl.M = s_mx[m];
       pl.S = s_S[m];
     } else {
@@ -642,7 +654,7 @@ __device__ int scan_chunk(const VerifyArgs& a, int b, int kind, int r, const flo
 // puts u * Z past the end: the last chunk of positive mass), then the token inside it.
 template <int VEC>
 __device__ int draw(const VerifyArgs& a, int b, int kind, int r, const float* row, double q, float M,
-                    double S) {
+                    double S, float u) {
   __shared__ int s_pick, s_last, s_tok;
   __shared__ double s_base[2];
   const int t = threadIdx.x;
@@ -650,7 +662,7 @@ __device__ int draw(const VerifyArgs& a, int b, int kind, int r, const float* ro
   if (t == 0) { s_pick = INT_MAX; s_last = -1; }
   double Z;
   const double incl = block_scan(q, Z);                           // barriers inside
-  const double thr = (double)a.uniforms[(size_t)b * a.N] * Z;
+  const double thr = (double)u * Z;
   if (t < a.C && incl > thr) atomicMin(&s_pick, t);
   if (t < a.C && q > 0.0) atomicMax(&s_last, t);
   __syncthreads();
@@ -713,7 +725,7 @@ __device__ int scan_stored(const double* wrow, int lo, int hi, double scale, dou
 // Inverse-CDF draw over the weights stored by the bonus pass: thread t < C holds chunk t's sum
 // q and the factor that scales its stored weights (1 for a residual draw; exp(chunk max - row
 // max) for a draw from T).  Same chunk choice and rounding fallbacks as draw().
-__device__ int draw_stored(const VerifyArgs& a, int b, double q, double scale) {
+__device__ int draw_stored(const VerifyArgs& a, int b, double q, double scale, float u) {
   __shared__ int s_pick, s_last, s_tok;
   __shared__ double s_base[2], s_scale[2];
   const int t = threadIdx.x;
@@ -721,7 +733,7 @@ __device__ int draw_stored(const VerifyArgs& a, int b, double q, double scale) {
   if (t == 0) { s_pick = INT_MAX; s_last = -1; }
   double Z;
   const double incl = block_scan(q, Z);                           // barriers inside
-  const double thr = (double)a.uniforms[(size_t)b * a.N] * Z;
+  const double thr = (double)u * Z;
   if (t < a.C && incl > thr) atomicMin(&s_pick, t);
   if (t < a.C && q > 0.0) atomicMax(&s_last, t);
   __syncthreads();
@@ -752,10 +764,12 @@ template <int VEC>
 __global__ __launch_bounds__(kThreads) void select_kernel(VerifyArgs a) {
   const int b = blockIdx.x;
   const int t = threadIdx.x;
-  // the plan and this thread's chunk part are requested together (the part's index does not
-  // depend on the plan; threads past C read part 0 and ignore it)
+  // the plan, this thread's chunk part and the draw's uniform u = uniforms[b, 0] are requested
+  // together (none of their indices depends on the plan; threads past C read part 0 and ignore
+  // it)
   const BonusPlan pl = a.plans[b];
   const BonusPart bp = a.bparts[(size_t)b * a.C + (t < a.C ? t : 0)];
+  const float u = a.uniforms[(size_t)b * a.N];
   if (pl.kind == 0) return;
   // merge the chunk parts (one per thread): row max / argmax / nonfinite
   double Sc = 0.0, Qc = 0.0;
@@ -779,12 +793,12 @@ __global__ __launch_bounds__(kThreads) void select_kernel(VerifyArgs a) {
   int tok;
   if (pl.kind == 2) {
     const double sc = (mc == -INFINITY) ? 0.0 : exp((double)mc - (double)m);
-    if (a.weights) tok = draw_stored(a, b, Sc * sc, sc);
-    else tok = draw<VEC>(a, b, 2, pl.r, row, Sc * sc, m, 0.0);
+    if (a.weights) tok = draw_stored(a, b, Sc * sc, sc, u);
+    else tok = draw<VEC>(a, b, 2, pl.r, row, Sc * sc, m, 0.0, u);
   } else {
     const double Z = block_sum(t < a.C ? Qc : 0.0);
-    if (Z > 0.0) tok = a.weights ? draw_stored(a, b, Qc, 1.0) : draw<VEC>(a, b, 3, pl.r, row, Qc, pl.M, pl.S);
-    else tok = draw<VEC>(a, b, 2, pl.r, row, Sc, pl.M, pl.S);   // residual of zero mass: T_m
+    if (Z > 0.0) tok = a.weights ? draw_stored(a, b, Qc, 1.0, u) : draw<VEC>(a, b, 3, pl.r, row, Qc, pl.M, pl.S, u);
+    else tok = draw<VEC>(a, b, 2, pl.r, row, Sc, pl.M, pl.S, u);   // residual of zero mass: T_m
   }
   if (t == 0) a.bonus[b] = tok;
 }
