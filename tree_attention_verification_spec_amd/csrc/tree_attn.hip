@@ -47,6 +47,7 @@ namespace {
 constexpr int kKT = 64;        // keys per tile
 constexpr int kThreads = 256;  // merge kernel workgroup
 constexpr int kMaxLptSeqs = 256;  // longest-first ordering for batches up to this size
+constexpr int kMaxWords = (SPEC_MAX_NODES + 63) / 64;   // ancestor words per tree node
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -210,6 +211,16 @@ void tree_attn_bf16_kernel(AttnArgs a) {
     for (int ds = 0; ds < DS; ++ds)
       qf[cb][ds] = row_ok[cb] ? *reinterpret_cast<const bf16x8*>(src + ds * 32) : bf16x8{};
   }
+  // The ancestor words of this lane's rows (W <= kMaxWords), requested with Q so that no tile
+  // loads mask words behind the prefetch (the memory counter drains in issue order).  Word
+  // indices are clamped into the row; a clamped word is never selected below.
+  uint64_t mw[CB][kMaxWords];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const uint64_t* mrow = a.mask + ((size_t)b * a.N + min(row_node[cb], a.N - 1)) * a.W;
+#pragma unroll
+    for (int w = 0; w < kMaxWords; ++w) mw[cb][w] = mrow[min(w, a.W - 1)];
+  }
 
   f32x4 o_acc[DB][CB];
 #pragma unroll
@@ -233,15 +244,15 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   const size_t kv_base = ((size_t)b * a.Hkv + g) * (size_t)a.S_max * D;
   const int ld_key = tid / CPK;
   const int ld_chunk = tid % CPK;
-  bf16x8 kreg[PASSES], vreg[PASSES];
   // Next tile into registers, consumed only by the next stage(), so the loads stay in flight
-  // while this tile is computed.  A key past the sequence loads the last valid key instead
-  // (total >= 1 whenever a tile exists): finite data whose score is masked to -inf, so its
-  // weight is exactly 0.
+  // while this tile is computed.  A key past the split loads the split's last key instead
+  // (k1 >= 1 whenever a tile exists): finite data whose score is masked to -inf, so its weight
+  // is exactly 0, and all lanes then read one address.
+  bf16x8 kreg[PASSES], vreg[PASSES];
   auto fetch = [&](int t0) {
 #pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
-      const int s = min(t0 + pass * KPP + ld_key, total - 1);
+      const int s = min(t0 + pass * KPP + ld_key, k1 - 1);
       const size_t at = kv_base + (size_t)s * D + ld_chunk * 8;
       kreg[pass] = *reinterpret_cast<const bf16x8*>(kp + at);
       vreg[pass] = *reinterpret_cast<const bf16x8*>(vp + at);
@@ -256,30 +267,45 @@ void tree_attn_bf16_kernel(AttnArgs a) {
     }
   };
 
-  if (k0 < k1) fetch(k0);
+  // Q and the ancestor words pass through an empty asm once the first tile is requested: the
+  // compiler waits for their loads there, where it still counts exactly (they precede the
+  // tile's loads, which stay in flight), and inside the loop they are plain registers.
+  // Without it the loop's merged load state makes a tile re-wait for them at a count that
+  // also drains the prefetch.
+  auto settle = [&]() {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) asm volatile("" : "+v"(qf[cb][ds]));
+#pragma unroll
+      for (int w = 0; w < kMaxWords; ++w) asm volatile("" : "+v"(mw[cb][w]));
+    }
+  };
+  if (k0 < k1) {
+    fetch(k0);
+    settle();
+  } else {
+    settle();
+  }
   int buf = 0;
   for (int t0 = k0; t0 < k1; t0 += kKT) {
     stage(buf);
     __syncthreads();
-    // Ancestor words for tiles that reach the tree part, issued before the prefetch: the
-    // memory counter drains in order, so a load issued after the prefetch could only be
-    // waited for together with it.  Word indices are clamped; a clamped word is never read
-    // below, since a tree key j always lies in word jw or jw + 1 and j < n <= 64 W.
+    fetch(t0 + kKT);   // unconditional (past the split it reloads its last key) so no branch
+                       // leaves the compiler unsure how many loads are still in flight
+    // Ancestor words of tree keys j = s - P in this tile: word jw or jw + 1 (j < n <= 64 W).
     const int jw = (t0 - P) >> 6;                 // floor division (t0 - P may be negative)
     uint64_t wlo[CB], whi[CB];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) wlo[cb] = whi[cb] = 0;
-    if (t0 + kKT > P) {
-      const int j0 = min(max(jw, 0), a.W - 1), j1 = min(max(jw + 1, 0), a.W - 1);
+    for (int cb = 0; cb < CB; ++cb) {
+      wlo[cb] = mw[cb][0];
+      whi[cb] = mw[cb][0];
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const uint64_t* mrow = a.mask + ((size_t)b * a.N + min(row_node[cb], a.N - 1)) * a.W;
-        wlo[cb] = mrow[j0];
-        whi[cb] = mrow[j1];
+      for (int w = 1; w < kMaxWords; ++w) {
+        wlo[cb] = jw == w ? mw[cb][w] : wlo[cb];
+        whi[cb] = jw + 1 == w ? mw[cb][w] : whi[cb];
       }
     }
-    fetch(t0 + kKT);   // unconditional (past the end it reloads the last key) so no branch
-                       // leaves the compiler unsure how many loads are still in flight
     const __bf16* kt = k_lds[buf];
     const __bf16* vt = v_lds[buf];
 
