@@ -7,19 +7,20 @@
 // entropy-based threshold); "多トークン予測（Medusa・EAGLE）", section
 // "ツリー検証：候補を「木」に束ねて1回で確かめる" (keep the path that passes the longest).
 //
-// Four kernels, in stream order; no kernel synchronises workgroups (the kernel boundaries
+// Three kernels, in stream order; no kernel synchronises workgroups (the kernel boundaries
 // order their results), and every global load is issued before it is needed.
 //   rows    grid (seq, node, chunk): rows of nodes with children are split into chunks of
 //           8K logits; each workgroup streams its chunk once (float4 loads held in registers)
 //           into (max, lowest argmax, sum exp(x - max) and, for typical acceptance,
 //           sum exp(x - max)(x - max)), fp32 exp with fp64 sums.  Workgroups of leaf rows leave
 //           after a 1 KB look at the parents.
-//   decide  one workgroup per sequence: merge of the row chunks (1-4 lanes per node),
-//           validation, node tests in fp64, survival = AND over the parent chain, the deepest
-//           survivor (LDS max on depth, -index), the path, and the plan of the bonus draw.
-//   bonus   grid (seq, chunk) over the kept row m: chunk max / argmax, and fp64 chunk sums of
-//           exp(x - max) and, for a residual draw, of relu(T - D) with T normalised by the row
-//           statistics of the first kernel; small batches also keep each token's weight.
+//   decide_bonus  grid (seq, chunk).  First the decision, derived by every workgroup of the
+//           sequence (outputs written by chunk 0's): merge of the row chunks (1-4 lanes per
+//           node), validation, node tests in fp64, survival = AND over the parent chain, the
+//           deepest survivor (LDS max on depth, -index), the path, and the plan of the bonus
+//           draw.  Then this chunk of the kept row m: chunk max / argmax, and fp64 chunk sums
+//           of exp(x - max) and, for a residual draw, of relu(T - D) with T normalised by the
+//           row statistics of the first kernel; small batches also keep each token's weight.
 //   select  one workgroup per sequence: the chunk holding u * Z (shuffle scan of the chunk
 //           sums), then an in-order fp64 scan inside it (of the kept weights, or recomputed
 //           ones) for the smallest token whose running sum exceeds u * Z.
@@ -267,7 +268,11 @@ __device__ void write_neutral(const VerifyArgs& a, int b, int e) {
   }
 }
 
-__global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
+// The decision for sequence b, in every thread of the workgroup.  Each workgroup of the bonus
+// pass derives it for itself (a few KB of chunk partials and one gather per node, read from
+// L2 by all chunks of the sequence) instead of waiting for a kernel of its own; only the
+// workgroup with `out` set writes the outputs and the plan for the draw.
+__device__ BonusPlan decide(const VerifyArgs& a, int b, bool out) {
   __shared__ int s_par[SPEC_MAX_NODES];
   __shared__ int s_dep[SPEC_MAX_NODES];
   __shared__ int s_acc[SPEC_MAX_NODES];
@@ -278,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
   __shared__ double s_H[SPEC_MAX_NODES];
   __shared__ int s_drow[SPEC_MAX_NODES];
   __shared__ int s_err, s_best, s_minchild;
-  const int b = blockIdx.x;
+  __shared__ BonusPlan s_plan;
   const int c = threadIdx.x;
   // Every load that does not depend on another is requested here, together: n_nodes, the
   // parent, token, uniform and draft row of this thread's node, and the chunk partials this
@@ -318,9 +323,11 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
   __syncthreads();
   BonusPlan* plan = a.plans + b;
   if (n < 0 || n > a.N || n == 0) {
-    write_neutral(a, b, n == 0 ? 0 : err_word(0, SPEC_ERR_NNODES));
-    if (c == 0) *plan = BonusPlan{0, 0, 0, 0.f, 0.0};
-    return;
+    if (out) {
+      write_neutral(a, b, n == 0 ? 0 : err_word(0, SPEC_ERR_NNODES));
+      if (c == 0) *plan = BonusPlan{0, 0, 0, 0.f, 0.0};
+    }
+    return BonusPlan{0, 0, 0, 0.f, 0.0};
   }
 
   // rows read: nodes named as a parent by some valid child
@@ -436,9 +443,11 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
   if (code) atomicMin(&s_err, err_word(c, code));
   __syncthreads();
   if (s_err != INT_MAX) {
-    write_neutral(a, b, s_err);
-    if (c == 0) *plan = BonusPlan{0, 0, 0, 0.f, 0.0};
-    return;
+    if (out) {
+      write_neutral(a, b, s_err);
+      if (c == 0) *plan = BonusPlan{0, 0, 0, 0.f, 0.0};
+    }
+    return BonusPlan{0, 0, 0, 0.f, 0.0};
   }
 
   // ---- per-node tests (fp64)
@@ -471,26 +480,32 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
     }
     if (ok) atomicMax(&s_best, (s_dep[c] << 9) | (511 - c));
   }
-  if (c < a.N && a.node_accept) a.node_accept[(size_t)b * a.N + c] = (c < n) ? (uint8_t)s_acc[c] : 0;
+  if (out && c < a.N && a.node_accept) a.node_accept[(size_t)b * a.N + c] = (c < n) ? (uint8_t)s_acc[c] : 0;
   __syncthreads();
   const int m = 511 - (s_best & 511);
   const int dm = s_best >> 9;
   if (c >= 1 && c < n && s_par[c] == m) atomicMin(&s_minchild, c);
-  for (int j = c; j <= a.max_depth; j += kThreads)
-    if (j > dm) a.path[(size_t)b * (a.max_depth + 1) + j] = -1;
+  if (out)
+    for (int j = c; j <= a.max_depth; j += kThreads)
+      if (j > dm) a.path[(size_t)b * (a.max_depth + 1) + j] = -1;
   __syncthreads();
   if (c == 0) {
-    int j = m;
-    for (int d = dm; d >= 0; --d) {
-      a.path[(size_t)b * (a.max_depth + 1) + d] = j;
-      j = s_par[j];
+    if (out) {
+      int j = m;
+      for (int d = dm; d >= 0; --d) {
+        a.path[(size_t)b * (a.max_depth + 1) + d] = j;
+        j = s_par[j];
+      }
+      a.accept_len[b] = dm;
+      a.err[b] = 0;
     }
-    a.accept_len[b] = dm;
-    a.err[b] = 0;
     BonusPlan pl{m, 0, 0, 0.f, 0.0};
     if (a.mode == SPEC_VERIFY_GREEDY) {
-      if (s_has[m]) a.bonus[b] = s_am[m];
-      else pl.kind = 1;
+      if (s_has[m]) {
+        if (out) a.bonus[b] = s_am[m];
+      } else {
+        pl.kind = 1;
+      }
     } else if (a.mode == SPEC_VERIFY_TYPICAL) {
       pl.kind = 2;
     } else if (s_minchild != INT_MAX) {
@@ -501,8 +516,11 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
     } else {
       pl.kind = 2;
     }
-    *plan = pl;
+    if (out) *plan = pl;
+    s_plan = pl;
   }
+  __syncthreads();
+  return s_plan;
 }
 
 // ------------------------------------------------------------------ kernels 3-4: bonus draw
@@ -518,10 +536,7 @@ __device__ __forceinline__ double draft_at(const VerifyArgs& a, int b, int r, in
 }
 
 template <int VEC>
-__global__ __launch_bounds__(kThreads) void bonus_kernel(VerifyArgs a) {
-  const int c = blockIdx.x % a.C, b = blockIdx.x / a.C;
-  const BonusPlan pl = a.plans[b];
-  if (pl.kind == 0) return;
+__device__ void bonus_chunk(const VerifyArgs& a, int b, int c, const BonusPlan& pl) {
   const float* row = a.logits + ((size_t)b * a.N + pl.m) * a.V;
   const int lo = c * a.CS, hi = min(a.V, lo + a.CS);
   float x[kPer];
@@ -588,6 +603,16 @@ __global__ __launch_bounds__(kThreads) void bonus_kernel(VerifyArgs a) {
   block_sum2(S, Q);
   if (pl.kind == 3) m = pl.M;              // S is relative to the row max
   if (threadIdx.x == 0) a.bparts[(size_t)b * a.C + c] = BonusPart{S, Q, m, am, nf, 0};
+}
+
+// Grid (seq, chunk): the decision of the sequence (outputs written by chunk 0's workgroup),
+// then this chunk of the kept row's bonus pass.
+template <int VEC>
+__global__ __launch_bounds__(kThreads) void decide_bonus_kernel(VerifyArgs a) {
+  const int c = blockIdx.x % a.C, b = blockIdx.x / a.C;
+  const BonusPlan pl = decide(a, b, c == 0);
+  if (pl.kind == 0) return;
+  bonus_chunk<VEC>(a, b, c, pl);
 }
 
 // Weight of token v for draw `kind`: 2 -> exp(x - M) (T up to the common factor 1/S),
@@ -903,12 +928,11 @@ extern "C" spec_status spec_verify(const float* target_logits, const float* draf
     if (vec4) launch(nr, rows_kernel<4, 16>, grid_rows, blk, s, a);
     else launch(nr, rows_kernel<1, 16>, grid_rows, blk, s, a);
   }
-  launch("verify_decide", decide_kernel, dim3(B), blk, s, a);
   if (vec4) {
-    launch("verify_bonus", bonus_kernel<4>, grid_chunks, blk, s, a);
+    launch("verify_decide_bonus", decide_bonus_kernel<4>, grid_chunks, blk, s, a);
     launch("verify_select", select_kernel<4>, dim3(B), blk, s, a);
   } else {
-    launch("verify_bonus", bonus_kernel<1>, grid_chunks, blk, s, a);
+    launch("verify_decide_bonus", decide_bonus_kernel<1>, grid_chunks, blk, s, a);
     launch("verify_select", select_kernel<1>, dim3(B), blk, s, a);
   }
   return launch_status();
