@@ -165,7 +165,7 @@ def capture(stepper, indices):
 
 # --------------------------------------------------------------------------- algorithmic work
 
-def algorithmic(w, a, parents, depths):
+def algorithmic(w, a, parents, depths, mode):
     """Per-launch algorithmic bytes / FLOPs of each kernel (what the method must move or do)."""
     import numpy as np
     s = 2 if w.dtype == "bf16" else 4
@@ -180,8 +180,11 @@ def algorithmic(w, a, parents, depths):
         nb = int(n[b])
         attn_flops += 4 * Hq * d * int((P[b] + depths[b, :nb] + 1).sum())
         internal += len(set(int(p) for p in parents[b, 1:nb]))
+    # the bonus pass reads the kept row once more, and a residual draw the draft row beside it
+    kept = B * V * 4 * (2 if mode == "reject" else 1)
     out = {("tree_attn_bf16" if w.dtype == "bf16" else "tree_attn_f32"): (attn_bytes, attn_flops),
-           "verify_rows": (internal * V * 4, 0)}
+           "verify_rows": (internal * V * 4, 0),
+           "verify_decide_bonus": (kept, 0)}
     if w.heads:
         H, Dm = w.heads["H"], w.heads["Dm"]
         out["medusa_resblock"] = (H * Dm * Dm * 2, 2 * B * H * Dm * Dm)
@@ -349,7 +352,7 @@ def main():
         sb.prof_reset()
 
     depths = st.outs[0]["tb"]["depths"].cpu().numpy()
-    work = algorithmic(w, a, a["parents"], depths)
+    work = algorithmic(w, a, a["parents"], depths, mode)
     dom = max((k for k in kernels if k in work), key=lambda k: kernels[k])
     nbytes, flops = work[dom]
     short = {1: "tiny", 2: "tree63", 3: "tree127_b16", 4: "tree255_b4", 5: "medusa_tree127_b8"}[args.config]

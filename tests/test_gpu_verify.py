@@ -101,6 +101,21 @@ def test_draw_weights_stored_or_recomputed(monkeypatch, store, case):
         compare_verify(got, ref, n_nodes)
 
 
+@pytest.mark.parametrize("store", ["0", "1"])
+def test_zero_residual_draws_from_target(monkeypatch, store):
+    """Draft probabilities of 2 everywhere: each node test accepts with T/D <= 1/2 and every
+    residual relu(T - D) is zero, so a rejection's bonus token is drawn from T at the kept node
+    (the zero-mass reading), on both draw kernels."""
+    monkeypatch.setenv("SPECTREE_VERIFY_STORE_W", store)
+    w = wl.custom(seed=3100, B=6, N=40, V=9000, tree=("random", 5))
+    parents, n_nodes, vi = _case(w)
+    vi = dict(vi)
+    vi["draft_probs"] = np.full_like(vi["draft_probs"], 2.0)
+    got, ref = _run(w, "reject", vi, parents, n_nodes)
+    assert (ref["accept_len"] < 5).sum() >= 3          # rejections happened
+    compare_verify(got, ref, n_nodes)
+
+
 def test_max_depth_and_errors():
     need_gpu()
     w = wl.custom(seed=41, B=8, N=20, V=64, tree=("random", 6))

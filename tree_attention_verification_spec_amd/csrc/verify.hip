@@ -828,6 +828,137 @@ __global__ __launch_bounds__(kThreads) void select_kernel(VerifyArgs a) {
   if (t == 0) a.bonus[b] = tok;
 }
 
+// One-wave draw for the common case of stored weights and at most 64 chunks: lane t holds
+// chunk t's part, and inside the chosen chunk lane t owns a contiguous run of 64 tokens, so
+// every reduction and scan is a wave shuffle and the kernel has no barrier.  Same chunk choice,
+// token choice and rounding fallbacks as select_kernel.
+
+// Inclusive prefix sum over the wave in lane order (fp64).
+__device__ __forceinline__ double wave_scan(double v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
+__device__ void write_neutral_wave(const VerifyArgs& a, int b, int e) {
+  const int t = threadIdx.x;
+  if (a.node_accept)
+    for (int i = t; i < a.N; i += kWave) a.node_accept[(size_t)b * a.N + i] = 0;
+  for (int j = t; j <= a.max_depth; j += kWave) a.path[(size_t)b * (a.max_depth + 1) + j] = -1;
+  if (t == 0) {
+    a.accept_len[b] = 0;
+    a.bonus[b] = -1;
+    a.err[b] = e;
+  }
+}
+
+constexpr int kRun = kBonusChunk / kWave;    // tokens per lane inside a chunk
+
+template <int VEC>
+__global__ __launch_bounds__(kWave) void select_wave_kernel(VerifyArgs a) {
+  const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  const BonusPlan pl = a.plans[b];
+  const BonusPart bp = a.bparts[(size_t)b * a.C + (t < a.C ? t : 0)];
+  const float u = a.uniforms[(size_t)b * a.N];
+  if (pl.kind == 0) return;
+  double Sc = 0.0, Qc = 0.0;
+  float mc = -INFINITY;
+  int amc = INT_MAX, nf = 0;
+  if (t < a.C) {
+    Sc = bp.S; Qc = bp.Q; mc = bp.m; amc = bp.argmax; nf = bp.nonfinite;
+  }
+  float m = mc;
+  int am = amc;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {           // row max / lowest argmax / nonfinite
+    const float m2 = __shfl_xor(m, o);
+    const int am2 = __shfl_xor(am, o), nf2 = __shfl_xor(nf, o);
+    if (m2 > m || (m2 == m && am2 < am)) { m = m2; am = am2; }
+    nf |= nf2;
+  }
+  if (nf) {
+    write_neutral_wave(a, b, err_word(pl.m, SPEC_ERR_NONFINITE));
+    return;
+  }
+  if (pl.kind == 1) {
+    if (t == 0) a.bonus[b] = am;
+    return;
+  }
+  // chunk weights: q = this chunk's sum, scale = factor of its stored weights; a residual of
+  // zero mass draws from T_m instead, recomputed from the logits (stored weights are zero)
+  double q, scale = 1.0;
+  bool stored = true;
+  if (pl.kind == 2) {
+    scale = (mc == -INFINITY) ? 0.0 : exp((double)mc - (double)m);
+    q = Sc * scale;
+  } else if (wave_sum(Qc) > 0.0) {
+    q = Qc;
+  } else {
+    q = Sc;                                    // relative to the row max pl.M
+    stored = false;
+  }
+  if (t >= a.C) q = 0.0;
+  const double incl = wave_scan(q);
+  const double Z = __shfl(incl, kWave - 1);
+  const double thr = (double)u * Z;
+  const unsigned long long over = __ballot(t < a.C && incl > thr);
+  const unsigned long long mass = __ballot(t < a.C && q > 0.0);
+  const int cs = over ? __ffsll(over) - 1 : (mass ? 63 - __clzll(mass) : 0);
+  const double base = (over || mass) ? __shfl(incl - q, cs) : 0.0;
+  const double sc = (over || mass) ? __shfl(scale, cs) : 1.0;
+  const int lo = cs * a.CS, hi = min(a.V, lo + a.CS);
+  const int my_lo = lo + t * kRun;
+  double w[kRun];
+  if (stored) {
+    const double* wrow = a.weights + (size_t)b * a.C * a.CS;
+#pragma unroll
+    for (int k = 0; k < kRun; k += 2) {
+      const int v = my_lo + k;
+      const double2 p = *reinterpret_cast<const double2*>(wrow + (v < hi ? v : lo));
+      w[k] = v < hi ? p.x * sc : 0.0;
+      w[k + 1] = v + 1 < hi ? p.y * sc : 0.0;
+    }
+  } else {
+    const float* row = a.logits + ((size_t)b * a.N + pl.m) * a.V;
+#pragma unroll
+    for (int k = 0; k < kRun; ++k) {
+      const int v = my_lo + k;
+      w[k] = v < hi ? exp((double)row[v] - (double)pl.M) : 0.0;
+    }
+  }
+  double mine = 0.0;
+#pragma unroll
+  for (int k = 0; k < kRun; ++k) mine += w[k];
+  const double before = base + (wave_scan(mine) - mine);
+  // every lane whose run crosses thr finds its first token past thr; the smallest wins
+  int mt = INT_MAX;
+  if (before + mine > thr) {
+    double run = before;
+#pragma unroll
+    for (int k = 0; k < kRun; ++k) {
+      run += w[k];
+      if (mt == INT_MAX && my_lo + k < hi && run > thr) mt = my_lo + k;
+    }
+  }
+  int tok = wave_min(mt);
+  if (tok == INT_MAX) tok = -1;
+  if (tok < 0) {                               // rounding put thr at the chunk's end: the
+    int lastpos = -1;                          // last token of positive weight
+#pragma unroll
+    for (int k = 0; k < kRun; ++k)
+      if (my_lo + k < hi && w[k] > 0.0) lastpos = my_lo + k;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) lastpos = max(lastpos, __shfl_xor(lastpos, o));
+    tok = lastpos;
+  }
+  if (t == 0) a.bonus[b] = tok;
+}
+
 // ------------------------------------------------------------------ host
 
 struct VerifyLayout {
@@ -928,12 +1059,16 @@ extern "C" spec_status spec_verify(const float* target_logits, const float* draf
     if (vec4) launch(nr, rows_kernel<4, 16>, grid_rows, blk, s, a);
     else launch(nr, rows_kernel<1, 16>, grid_rows, blk, s, a);
   }
+  // the draw: one wave per sequence when the weights are stored and a wave holds the chunks
+  const bool wave_draw = a.weights && L.C <= kWave;
   if (vec4) {
     launch("verify_decide_bonus", decide_bonus_kernel<4>, grid_chunks, blk, s, a);
-    launch("verify_select", select_kernel<4>, dim3(B), blk, s, a);
+    if (wave_draw) launch("verify_select", select_wave_kernel<4>, dim3(B), dim3(kWave), s, a);
+    else launch("verify_select", select_kernel<4>, dim3(B), blk, s, a);
   } else {
     launch("verify_decide_bonus", decide_bonus_kernel<1>, grid_chunks, blk, s, a);
-    launch("verify_select", select_kernel<1>, dim3(B), blk, s, a);
+    if (wave_draw) launch("verify_select", select_wave_kernel<1>, dim3(B), dim3(kWave), s, a);
+    else launch("verify_select", select_kernel<1>, dim3(B), blk, s, a);
   }
   return launch_status();
 }
