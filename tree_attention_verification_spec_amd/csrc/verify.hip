@@ -34,8 +34,12 @@ namespace spectree {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBonusChunk = 4096;            // logits per workgroup in the bonus pass
-constexpr int kPer = kBonusChunk / kThreads;
+// Logits per workgroup in the bonus pass: 2048 for batches up to kSmallChunkMaxB whose rows fit
+// in one wave's worth of chunks (the decision is derived per workgroup, so more, shorter chunks
+// pay off while they are few), 4096 otherwise.
+constexpr int kChunkSmall = 2048;
+constexpr int kChunkLarge = 4096;
+constexpr int kSmallChunkMaxB = 8;
 constexpr int kStoreWeightsMaxB = 8;          // batches that keep the bonus pass's weights
 constexpr int kPartsPerLane = 8;             // row-chunk partials per merging lane and batch
 
@@ -84,7 +88,7 @@ struct VerifyArgs {
   int32_t* err;
   int CR;               // row-pass chunks per row
   int RC;               // logits per row-pass chunk
-  int CS, C;            // bonus-pass chunk size (kBonusChunk) and chunks per row
+  int CS, C;            // bonus-pass chunk size (kChunkSmall or kChunkLarge) and chunks per row
   RowPart* rowparts;    // [B, N, CR]
   BonusPlan* plans;     // [B]
   BonusPart* bparts;    // [B, C]
@@ -535,8 +539,9 @@ __device__ __forceinline__ double draft_at(const VerifyArgs& a, int b, int r, in
   return (double)a.draft[((size_t)b * a.R + r) * a.Vd + v];
 }
 
-template <int VEC>
+template <int VEC, int CS>
 __device__ void bonus_chunk(const VerifyArgs& a, int b, int c, const BonusPlan& pl) {
+  constexpr int kPer = CS / kThreads;
   const float* row = a.logits + ((size_t)b * a.N + pl.m) * a.V;
   const int lo = c * a.CS, hi = min(a.V, lo + a.CS);
   float x[kPer];
@@ -607,12 +612,12 @@ __device__ void bonus_chunk(const VerifyArgs& a, int b, int c, const BonusPlan& 
 
 // Grid (seq, chunk): the decision of the sequence (outputs written by chunk 0's workgroup),
 // then this chunk of the kept row's bonus pass.
-template <int VEC>
+template <int VEC, int CS>
 __global__ __launch_bounds__(kThreads) void decide_bonus_kernel(VerifyArgs a) {
   const int c = blockIdx.x % a.C, b = blockIdx.x / a.C;
   const BonusPlan pl = decide(a, b, c == 0);
   if (pl.kind == 0) return;
-  bonus_chunk<VEC>(a, b, c, pl);
+  bonus_chunk<VEC, CS>(a, b, c, pl);
 }
 
 // Weight of token v for draw `kind`: 2 -> exp(x - M) (T up to the common factor 1/S),
@@ -627,9 +632,10 @@ __device__ __forceinline__ double draw_weight(const VerifyArgs& a, int b, int ki
 // Smallest token of chunk [lo, hi) whose running sum (from `base`, fp64, ascending token order)
 // exceeds thr; -1 if none.  Thread t owns a contiguous run of `per` tokens (a multiple of VEC,
 // so the run is read with VEC-wide loads).
-template <int VEC>
+template <int VEC, int CS>
 __device__ int scan_chunk(const VerifyArgs& a, int b, int kind, int r, const float* row, int lo, int hi,
                           float M, double S, double base, double thr) {
+  constexpr int kPer = CS / kThreads;
   __shared__ int s_hit;
   const int per = (hi - lo + kThreads * VEC - 1) / (kThreads * VEC) * VEC;   // <= kPer
   const int my_lo = lo + (int)threadIdx.x * per;
@@ -677,7 +683,7 @@ __device__ int scan_chunk(const VerifyArgs& a, int b, int kind, int r, const flo
 // Inverse-CDF draw with u = uniforms[b, 0] over the weights of `kind`; thread t < C holds the
 // sum q of chunk t.  The chunk is the first whose inclusive prefix exceeds u * Z (if rounding
 // puts u * Z past the end: the last chunk of positive mass), then the token inside it.
-template <int VEC>
+template <int VEC, int CS>
 __device__ int draw(const VerifyArgs& a, int b, int kind, int r, const float* row, double q, float M,
                     double S, float u) {
   __shared__ int s_pick, s_last, s_tok;
@@ -698,7 +704,7 @@ __device__ int draw(const VerifyArgs& a, int b, int kind, int r, const float* ro
   const int cs = pick != INT_MAX ? pick : (last >= 0 ? last : 0);
   const double base = pick != INT_MAX ? s_base[0] : (last >= 0 ? s_base[1] : 0.0);
   const int lo = cs * a.CS, hi = min(a.V, lo + a.CS);
-  int tok = scan_chunk<VEC>(a, b, kind, r, row, lo, hi, M, S, base, thr);
+  int tok = scan_chunk<VEC, CS>(a, b, kind, r, row, lo, hi, M, S, base, thr);
   if (tok < 0) {                            // rounding put thr at the chunk's end
     if (t == 0) {
       s_tok = -1;
@@ -714,7 +720,9 @@ __device__ int draw(const VerifyArgs& a, int b, int kind, int r, const float* ro
 // Smallest token of chunk [lo, hi) whose running sum of the stored weights (times scale, from
 // `base`, fp64, ascending token order) exceeds thr; -1 if none.  Thread t owns a contiguous run
 // of `per` tokens (even, so the run is read with 16-byte loads).
+template <int CS>
 __device__ int scan_stored(const double* wrow, int lo, int hi, double scale, double base, double thr) {
+  constexpr int kPer = CS / kThreads;
   __shared__ int s_hit;
   const int per = (hi - lo + kThreads * 2 - 1) / (kThreads * 2) * 2;   // <= kPer
   const int my_lo = lo + (int)threadIdx.x * per;
@@ -750,6 +758,7 @@ __device__ int scan_stored(const double* wrow, int lo, int hi, double scale, dou
 // Inverse-CDF draw over the weights stored by the bonus pass: thread t < C holds chunk t's sum
 // q and the factor that scales its stored weights (1 for a residual draw; exp(chunk max - row
 // max) for a draw from T).  Same chunk choice and rounding fallbacks as draw().
+template <int CS>
 __device__ int draw_stored(const VerifyArgs& a, int b, double q, double scale, float u) {
   __shared__ int s_pick, s_last, s_tok;
   __shared__ double s_base[2], s_scale[2];
@@ -772,7 +781,7 @@ __device__ int draw_stored(const VerifyArgs& a, int b, double q, double scale, f
   const double sc = (pick != INT_MAX || last >= 0) ? s_scale[k] : 1.0;
   const int lo = cs * a.CS, hi = min(a.V, lo + a.CS);
   const double* wrow = a.weights + (size_t)b * a.C * a.CS;
-  int tok = scan_stored(wrow, lo, hi, sc, base, thr);
+  int tok = scan_stored<CS>(wrow, lo, hi, sc, base, thr);
   if (tok < 0) {                            // rounding put thr at the chunk's end
     if (t == 0) {
       s_tok = -1;
@@ -785,7 +794,7 @@ __device__ int draw_stored(const VerifyArgs& a, int b, double q, double scale, f
   return tok;
 }
 
-template <int VEC>
+template <int VEC, int CS>
 __global__ __launch_bounds__(kThreads) void select_kernel(VerifyArgs a) {
   const int b = blockIdx.x;
   const int t = threadIdx.x;
@@ -818,18 +827,18 @@ __global__ __launch_bounds__(kThreads) void select_kernel(VerifyArgs a) {
   int tok;
   if (pl.kind == 2) {
     const double sc = (mc == -INFINITY) ? 0.0 : exp((double)mc - (double)m);
-    if (a.weights) tok = draw_stored(a, b, Sc * sc, sc, u);
-    else tok = draw<VEC>(a, b, 2, pl.r, row, Sc * sc, m, 0.0, u);
+    if (a.weights) tok = draw_stored<CS>(a, b, Sc * sc, sc, u);
+    else tok = draw<VEC, CS>(a, b, 2, pl.r, row, Sc * sc, m, 0.0, u);
   } else {
     const double Z = block_sum(t < a.C ? Qc : 0.0);
-    if (Z > 0.0) tok = a.weights ? draw_stored(a, b, Qc, 1.0, u) : draw<VEC>(a, b, 3, pl.r, row, Qc, pl.M, pl.S, u);
-    else tok = draw<VEC>(a, b, 2, pl.r, row, Sc, pl.M, pl.S, u);   // residual of zero mass: T_m
+    if (Z > 0.0) tok = a.weights ? draw_stored<CS>(a, b, Qc, 1.0, u) : draw<VEC, CS>(a, b, 3, pl.r, row, Qc, pl.M, pl.S, u);
+    else tok = draw<VEC, CS>(a, b, 2, pl.r, row, Sc, pl.M, pl.S, u);   // residual of zero mass: T_m
   }
   if (t == 0) a.bonus[b] = tok;
 }
 
 // One-wave draw for the common case of stored weights and at most 64 chunks: lane t holds
-// chunk t's part, and inside the chosen chunk lane t owns a contiguous run of 64 tokens, so
+// chunk t's part, and inside the chosen chunk lane t owns a contiguous run of CS / 64 tokens, so
 // every reduction and scan is a wave shuffle and the kernel has no barrier.  Same chunk choice,
 // token choice and rounding fallbacks as select_kernel.
 
@@ -856,10 +865,9 @@ __device__ void write_neutral_wave(const VerifyArgs& a, int b, int e) {
   }
 }
 
-constexpr int kRun = kBonusChunk / kWave;    // tokens per lane inside a chunk
-
-template <int VEC>
+template <int VEC, int CS>
 __global__ __launch_bounds__(kWave) void select_wave_kernel(VerifyArgs a) {
+  constexpr int kRun = CS / kWave;             // tokens per lane inside a chunk
   const int b = blockIdx.x;
   const int t = threadIdx.x;
   const BonusPlan pl = a.plans[b];
@@ -979,23 +987,35 @@ int row_chunk(int B, int N, int V) {
   return rc;
 }
 
+// The decision + bonus pass and the draw, for chunks of CS logits.
+template <int VEC, int CS>
+void launch_tail(const VerifyArgs& a, int B, bool wave_draw, hipStream_t s) {
+  launch("verify_decide_bonus", decide_bonus_kernel<VEC, CS>, dim3((unsigned)((size_t)a.C * B)), dim3(kThreads), s, a);
+  if (wave_draw) launch("verify_select", select_wave_kernel<VEC, CS>, dim3(B), dim3(kWave), s, a);
+  else launch("verify_select", select_kernel<VEC, CS>, dim3(B), dim3(kThreads), s, a);
+}
+
 VerifyLayout layout(int B, int N, int V) {
   VerifyLayout L{};
   L.RC = row_chunk(B, N, V);
   L.CR = (V + L.RC - 1) / L.RC;
-  L.CS = kBonusChunk;
-  L.C = (V + L.CS - 1) / L.CS;
+  const int c_small = (V + kChunkSmall - 1) / kChunkSmall;
+  const int c_large = (V + kChunkLarge - 1) / kChunkLarge;
+  L.CS = (B <= kSmallChunkMaxB && c_small <= kWave) ? kChunkSmall : kChunkLarge;
+  L.C = L.CS == kChunkSmall ? c_small : c_large;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t at = off; off += align_up(bytes, 256); return at; };
   L.rowparts = take((size_t)B * N * L.CR * sizeof(RowPart));
   L.plans = take((size_t)B * sizeof(BonusPlan));
-  L.bparts = take((size_t)B * L.C * sizeof(BonusPart));
+  // the chunk parts and weights regions are sized for either chunking (the more chunks, the
+  // longer padded row), so the workspace size grows with B whichever chunk size B selects
+  L.bparts = take((size_t)B * c_small * sizeof(BonusPart));
   // Stored draw weights are used for batches up to kStoreWeightsMaxB (SPECTREE_VERIFY_STORE_W=0/1
   // overrides); their region is always reserved, so that the workspace size grows with B and a
   // workspace sized for a batch also serves every smaller one.
   const char* sw = std::getenv("SPECTREE_VERIFY_STORE_W");
   L.store_w = (sw && *sw) ? std::atoi(sw) != 0 : B <= kStoreWeightsMaxB;
-  L.weights = take((size_t)B * L.C * L.CS * sizeof(double));
+  L.weights = take((size_t)B * c_large * kChunkLarge * sizeof(double));
   L.total = off;
   return L;
 }
@@ -1045,7 +1065,7 @@ extern "C" spec_status spec_verify(const float* target_logits, const float* draf
   a.weights = L.store_w ? reinterpret_cast<double*>(w + L.weights) : nullptr;
 
   const dim3 blk(kThreads);
-  const dim3 grid_rows((unsigned)((size_t)L.CR * N * B)), grid_chunks((unsigned)((size_t)L.C * B));
+  const dim3 grid_rows((unsigned)((size_t)L.CR * N * B));
   // 16-byte loads need rows that start on 16-byte boundaries
   const bool vec4 = V % 4 == 0 && (reinterpret_cast<uintptr_t>(target_logits) & 15) == 0;
   const char* nr = "verify_rows";
@@ -1062,13 +1082,11 @@ extern "C" spec_status spec_verify(const float* target_logits, const float* draf
   // the draw: one wave per sequence when the weights are stored and a wave holds the chunks
   const bool wave_draw = a.weights && L.C <= kWave;
   if (vec4) {
-    launch("verify_decide_bonus", decide_bonus_kernel<4>, grid_chunks, blk, s, a);
-    if (wave_draw) launch("verify_select", select_wave_kernel<4>, dim3(B), dim3(kWave), s, a);
-    else launch("verify_select", select_kernel<4>, dim3(B), blk, s, a);
+    if (L.CS == kChunkSmall) launch_tail<4, kChunkSmall>(a, B, wave_draw, s);
+    else launch_tail<4, kChunkLarge>(a, B, wave_draw, s);
   } else {
-    launch("verify_decide_bonus", decide_bonus_kernel<1>, grid_chunks, blk, s, a);
-    if (wave_draw) launch("verify_select", select_wave_kernel<1>, dim3(B), dim3(kWave), s, a);
-    else launch("verify_select", select_kernel<1>, dim3(B), blk, s, a);
+    if (L.CS == kChunkSmall) launch_tail<1, kChunkSmall>(a, B, wave_draw, s);
+    else launch_tail<1, kChunkLarge>(a, B, wave_draw, s);
   }
   return launch_status();
 }
