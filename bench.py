@@ -331,7 +331,7 @@ def main():
 
     # per-kernel durations: the same K steps launched eagerly with the library's kernel timing
     # on (each launch carries a start/stop event pair stamped by its own dispatch)
-    names = ("tree_build", "tree_assemble", "tree_attn_bf16", "tree_attn_merge", "tree_attn_f32", "verify_rows",
+    names = ("tree_build", "tree_assemble", "tree_attn_bf16", "tree_attn_merge", "tree_attn_f32", "verify_rows_list", "verify_rows",
              "verify_decide_bonus", "verify_select", "medusa_resblock", "medusa_lm_head",
              "medusa_softmax_topk")
     kernels = {}

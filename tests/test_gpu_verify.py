@@ -88,6 +88,20 @@ def test_row_chunk_sizes(monkeypatch, chunk, case):
         compare_verify(got, ref, n_nodes)
 
 
+@pytest.mark.parametrize("listed", ["0", "1"])
+@pytest.mark.parametrize("case", [0, 2, 3, 4, 6])
+def test_row_pass_listed_or_per_chunk(monkeypatch, listed, case):
+    """The row pass as one workgroup per (sequence, node, chunk), or as a listing of the rows
+    with children followed by one workgroup per listed (row, chunk) item (large problems by
+    default): both, forced, on every mode."""
+    monkeypatch.setenv("SPECTREE_VERIFY_ROWS_LIST", listed)
+    w = wl.custom(seed=3000 + case, **SMALL[case])
+    parents, n_nodes, vi = _case(w)
+    for mode in ("greedy", "typical", "reject"):
+        got, ref = _run(w, mode, vi, parents, n_nodes)
+        compare_verify(got, ref, n_nodes)
+
+
 @pytest.mark.parametrize("store", ["0", "1"])
 @pytest.mark.parametrize("case", [0, 1, 3, 6])
 def test_draw_weights_stored_or_recomputed(monkeypatch, store, case):
@@ -116,8 +130,10 @@ def test_zero_residual_draws_from_target(monkeypatch, store):
     compare_verify(got, ref, n_nodes)
 
 
-def test_max_depth_and_errors():
+@pytest.mark.parametrize("listed", ["0", "1"])
+def test_max_depth_and_errors(monkeypatch, listed):
     need_gpu()
+    monkeypatch.setenv("SPECTREE_VERIFY_ROWS_LIST", listed)
     w = wl.custom(seed=41, B=8, N=20, V=64, tree=("random", 6))
     parents, n_nodes, vi = _case(w)
     vi = dict(vi)

@@ -24,6 +24,7 @@
 //   select  one workgroup per sequence: the chunk holding u * Z (shuffle scan of the chunk
 //           sums), then an in-order fp64 scan inside it (of the kept weights, or recomputed
 //           ones) for the smallest token whose running sum exceeds u * Z.
+#include <algorithm>
 #include <cfloat>
 #include <climits>
 #include <cstdlib>
@@ -90,6 +91,8 @@ struct VerifyArgs {
   int RC;               // logits per row-pass chunk
   int CS, C;            // bonus-pass chunk size (kChunkSmall or kChunkLarge) and chunks per row
   RowPart* rowparts;    // [B, N, CR]
+  int32_t* row_list;    // [B * N]: b * N + p of each row with children (large problems)
+  int32_t* row_count;   // [1]: entries of row_list
   BonusPlan* plans;     // [B]
   BonusPart* bparts;    // [B, C]
   double* weights;      // [B, C * CS]: the bonus pass's per-token weights (kinds 2 and 3),
@@ -204,27 +207,22 @@ __device__ __forceinline__ int chunk_index(int lo, int k) {
 
 // ------------------------------------------------------------------ kernel 1: row chunks
 
+// Chunk c of row p of sequence b: (max, lowest argmax, sum exp(x - max) and, in typical mode,
+// sum exp(x - max)(x - max)) into rowparts.  row_load requests the chunk (all loads at once),
+// row_reduce reduces it.
 template <int VEC, int PER>
-__global__ __launch_bounds__(kThreads) void rows_kernel(VerifyArgs a) {
-  // 1-D grid over (seq, node, chunk): grid y/z are limited to 65536.
-  const int c = blockIdx.x % a.CR;
-  const int p = (blockIdx.x / a.CR) % a.N;
-  const int b = blockIdx.x / (a.CR * a.N);
-  const int t = threadIdx.x;
-  // n_nodes and the parent entries are requested together (the parent load does not wait for
-  // n; its index is clamped into the row, and entries past n are ignored below)
-  const int n = a.n_nodes ? a.n_nodes[b] : a.N;
-  const int par = a.parents[(size_t)b * a.N + min(max(t, 1), a.N - 1)];
-  if (n < 0 || n > a.N || p >= n) return;
-  // only rows of nodes that some node names as its parent are read
-  const int named = (t >= 1 && t < n && par == p) ? 1 : 0;
-  if (!__syncthreads_or(named)) return;
-
+__device__ __forceinline__ void row_load(const VerifyArgs& a, int b, int p, int c, float (&x)[PER]) {
   const float* row = a.logits + ((size_t)b * a.N + p) * a.V;
   const int lo = c * a.RC;                 // a.RC == PER * kThreads
+  load_chunk<VEC>(row, lo, min(a.V, lo + a.RC), x);
+}
+
+// Reduction of a chunk loaded by row_load.
+template <int VEC, int PER>
+__device__ void row_reduce(const VerifyArgs& a, int b, int p, int c, const float (&x)[PER]) {
+  const int t = threadIdx.x;
+  const int lo = c * a.RC;
   const int hi = min(a.V, lo + a.RC);
-  float x[PER];
-  load_chunk<VEC>(row, lo, hi, x);
   // chunk max (lowest index: a thread's slots run in increasing token order), nonfinite flag
   float m = -INFINITY;
   int am = INT_MAX, nf = 0;
@@ -257,6 +255,94 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(VerifyArgs a) {
   block_sum2(S, A);
   if (am == INT_MAX) m = -INFINITY;
   if (t == 0) a.rowparts[((size_t)b * a.N + p) * a.CR + c] = RowPart{S, A, m, am, nf, 0};
+}
+
+template <int VEC, int PER>
+__global__ __launch_bounds__(kThreads) void rows_kernel(VerifyArgs a) {
+  // 1-D grid over (seq, node, chunk): grid y/z are limited to 65536.
+  const int c = blockIdx.x % a.CR;
+  const int p = (blockIdx.x / a.CR) % a.N;
+  const int b = blockIdx.x / (a.CR * a.N);
+  const int t = threadIdx.x;
+  // n_nodes and the parent entries are requested together (the parent load does not wait for
+  // n; its index is clamped into the row, and entries past n are ignored below)
+  const int n = a.n_nodes ? a.n_nodes[b] : a.N;
+  const int par = a.parents[(size_t)b * a.N + min(max(t, 1), a.N - 1)];
+  if (n < 0 || n > a.N || p >= n) return;
+  // only rows of nodes that some node names as its parent are read
+  const int named = (t >= 1 && t < n && par == p) ? 1 : 0;
+  if (!__syncthreads_or(named)) return;
+  float x[PER];
+  row_load<VEC>(a, b, p, c, x);
+  row_reduce<VEC>(a, b, p, c, x);
+}
+
+// Large problems: most (sequence, node, chunk) workgroups of rows_kernel only look at the
+// parents and leave, and on large grids those empty workgroups, interleaved with the ones that
+// stream, cost about a fifth of the pass.  So one workgroup first lists the rows with children,
+// in (sequence, node) order, and the row pass then maps workgroup i to the i-th (listed row,
+// chunk) item.  Used for B * N <= kListMax.
+constexpr int kListMax = 4096;
+constexpr int kListPer = kListMax / kThreads;
+
+// Thread t owns the contiguous entries [t * per, t * per + per) of the B x N (sequence, node)
+// table in both passes; its parent and n_nodes loads are all requested at once.
+__global__ __launch_bounds__(kThreads) void rows_list_kernel(VerifyArgs a) {
+  __shared__ unsigned char s_named[kListMax];
+  const int t = threadIdx.x;
+  const int total = a.B * a.N;
+  const int per = (total + kThreads - 1) / kThreads;   // <= kListPer
+  const int i0 = t * per;
+  int par[kListPer], nn[kListPer];
+#pragma unroll
+  for (int k = 0; k < kListPer; ++k) {
+    const int i = min(i0 + k, total - 1);
+    par[k] = a.parents[i];
+    nn[k] = a.n_nodes ? a.n_nodes[i / a.N] : a.N;
+  }
+#pragma unroll
+  for (int k = 0; k < kListPer; ++k)
+    if (k < per && i0 + k < total) s_named[i0 + k] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kListPer; ++k) {
+    const int i = i0 + k;
+    if (k < per && i < total) {
+      // a valid child's parent (invalid sequences list nothing; their error comes from the
+      // decision)
+      const int b = i / a.N, c = i - b * a.N, n = nn[k], p = par[k];
+      if (n >= 1 && n <= a.N && c >= 1 && c < n && p >= 0 && p < c) s_named[b * a.N + p] = 1;
+    }
+  }
+  __syncthreads();
+  // ordered compaction over the same runs
+  int cnt = 0;
+#pragma unroll
+  for (int k = 0; k < kListPer; ++k)
+    if (k < per && i0 + k < total) cnt += s_named[i0 + k];
+  double all;
+  int at = (int)(block_scan((double)cnt, all) - cnt);   // counts are exact in fp64
+#pragma unroll
+  for (int k = 0; k < kListPer; ++k)
+    if (k < per && i0 + k < total && s_named[i0 + k]) a.row_list[at++] = i0 + k;
+  if (t == 0) *a.row_count = (int)all;
+}
+
+// Workgroup i takes the i-th (listed row, chunk) item, so the workgroups with work come first
+// and back to back; the rest leave after one look at the count.  The count and the list entry
+// are requested together (the entry's index is clamped into the list).
+template <int VEC, int PER>
+__global__ __launch_bounds__(kThreads) void rows_listed_kernel(VerifyArgs a) {
+  const int it = blockIdx.x;
+  const int count = *a.row_count;
+  const int idx = a.row_list[min(it / a.CR, a.B * a.N - 1)];
+  if (it >= count * a.CR) return;
+  const int b = idx / a.N;
+  const int p = idx - b * a.N;
+  const int c = it - (it / a.CR) * a.CR;
+  float x[PER];
+  row_load<VEC>(a, b, p, c, x);
+  row_reduce<VEC>(a, b, p, c, x);
 }
 
 // ------------------------------------------------------------------ kernel 2: decision
@@ -971,9 +1057,14 @@ __global__ __launch_bounds__(kWave) void select_wave_kernel(VerifyArgs a) {
 
 struct VerifyLayout {
   int RC, CR, CS, C;
-  bool store_w;
-  size_t rowparts, plans, bparts, weights, total;
+  bool store_w, listed;
+  size_t rowparts, plans, bparts, weights, row_list, row_count, total;
 };
+
+// The listed row pass pays one more launch, so it is used from this many (sequence, node,
+// chunk) items of the plain grid up (SPECTREE_VERIFY_ROWS_LIST=0/1 forces either path; a
+// tuning knob).
+constexpr size_t kListMinItems = 8192;
 
 // Row-pass chunk: 8K logits (measured faster than 4K and 16K at batch 1 and 16).
 // SPECTREE_VERIFY_CHUNK (4096, 8192 or 16384) overrides the choice (a tuning knob).
@@ -1016,6 +1107,11 @@ VerifyLayout layout(int B, int N, int V) {
   const char* sw = std::getenv("SPECTREE_VERIFY_STORE_W");
   L.store_w = (sw && *sw) ? std::atoi(sw) != 0 : B <= kStoreWeightsMaxB;
   L.weights = take((size_t)B * c_large * kChunkLarge * sizeof(double));
+  L.row_list = take((size_t)B * N * sizeof(int32_t));
+  L.row_count = take(sizeof(int32_t));
+  const char* rl = std::getenv("SPECTREE_VERIFY_ROWS_LIST");
+  const bool fits = (size_t)B * N <= (size_t)kListMax;
+  L.listed = fits && ((rl && *rl) ? std::atoi(rl) != 0 : (size_t)B * N * L.CR >= kListMinItems);
   L.total = off;
   return L;
 }
@@ -1063,13 +1159,27 @@ extern "C" spec_status spec_verify(const float* target_logits, const float* draf
   a.plans = reinterpret_cast<BonusPlan*>(w + L.plans);
   a.bparts = reinterpret_cast<BonusPart*>(w + L.bparts);
   a.weights = L.store_w ? reinterpret_cast<double*>(w + L.weights) : nullptr;
+  a.row_list = reinterpret_cast<int32_t*>(w + L.row_list);
+  a.row_count = reinterpret_cast<int32_t*>(w + L.row_count);
 
   const dim3 blk(kThreads);
   const dim3 grid_rows((unsigned)((size_t)L.CR * N * B));
   // 16-byte loads need rows that start on 16-byte boundaries
   const bool vec4 = V % 4 == 0 && (reinterpret_cast<uintptr_t>(target_logits) & 15) == 0;
   const char* nr = "verify_rows";
-  if (L.RC == 16384) {
+  if (L.listed) {
+    launch("verify_rows_list", rows_list_kernel, dim3(1), blk, s, a);
+    if (L.RC == 16384) {
+      if (vec4) launch(nr, rows_listed_kernel<4, 64>, grid_rows, blk, s, a);
+      else launch(nr, rows_listed_kernel<1, 64>, grid_rows, blk, s, a);
+    } else if (L.RC == 8192) {
+      if (vec4) launch(nr, rows_listed_kernel<4, 32>, grid_rows, blk, s, a);
+      else launch(nr, rows_listed_kernel<1, 32>, grid_rows, blk, s, a);
+    } else {
+      if (vec4) launch(nr, rows_listed_kernel<4, 16>, grid_rows, blk, s, a);
+      else launch(nr, rows_listed_kernel<1, 16>, grid_rows, blk, s, a);
+    }
+  } else if (L.RC == 16384) {
     if (vec4) launch(nr, rows_kernel<4, 64>, grid_rows, blk, s, a);
     else launch(nr, rows_kernel<1, 64>, grid_rows, blk, s, a);
   } else if (L.RC == 8192) {
