@@ -7,23 +7,27 @@
 // entropy-based threshold); "多トークン予測（Medusa・EAGLE）", section
 // "ツリー検証：候補を「木」に束ねて1回で確かめる" (keep the path that passes the longest).
 //
-// Three kernels, in stream order; no kernel synchronises workgroups (the kernel boundaries
-// order their results), and every global load is issued before it is needed.
-//   rows    grid (seq, node, chunk): rows of nodes with children are split into chunks of
-//           8K logits; each workgroup streams its chunk once (float4 loads held in registers)
-//           into (max, lowest argmax, sum exp(x - max) and, for typical acceptance,
-//           sum exp(x - max)(x - max)), fp32 exp with fp64 sums.  Workgroups of leaf rows leave
-//           after a 1 KB look at the parents.
+// Three kernels in stream order (four with the row listing of large problems); no kernel
+// synchronises workgroups (the kernel boundaries order their results), and every global load is
+// issued before it is needed.
+//   rows    rows of nodes with children are split into chunks of 8K logits; each workgroup
+//           streams one chunk once (float4 loads held in registers) into (max, lowest argmax,
+//           sum exp(x - max) and, for typical acceptance, sum exp(x - max)(x - max)), fp32 exp
+//           with fp64 sums.  Small problems: grid (seq, node, chunk), workgroups of leaf rows
+//           leave after a 1 KB look at the parents.  Large ones: one workgroup first lists the
+//           rows with children and workgroup i takes the i-th listed (row, chunk) item.
 //   decide_bonus  grid (seq, chunk).  First the decision, derived by every workgroup of the
 //           sequence (outputs written by chunk 0's): merge of the row chunks (1-4 lanes per
 //           node), validation, node tests in fp64, survival = AND over the parent chain, the
 //           deepest survivor (LDS max on depth, -index), the path, and the plan of the bonus
-//           draw.  Then this chunk of the kept row m: chunk max / argmax, and fp64 chunk sums
-//           of exp(x - max) and, for a residual draw, of relu(T - D) with T normalised by the
-//           row statistics of the first kernel; small batches also keep each token's weight.
-//   select  one workgroup per sequence: the chunk holding u * Z (shuffle scan of the chunk
-//           sums), then an in-order fp64 scan inside it (of the kept weights, or recomputed
-//           ones) for the smallest token whose running sum exceeds u * Z.
+//           draw.  Then this chunk (2K or 4K logits) of the kept row m: chunk max / argmax, and
+//           fp64 chunk sums of exp(x - max) and, for a residual draw, of relu(T - D) with T
+//           normalised by the row statistics of the first kernel; small batches also keep
+//           each token's weight.
+//   select  per sequence: the chunk holding u * Z (scan of the chunk sums), then an in-order
+//           fp64 scan inside it (of the kept weights, or recomputed ones) for the smallest
+//           token whose running sum exceeds u * Z.  With kept weights and at most 64 chunks,
+//           one wave does all of it with shuffles; otherwise a 256-thread workgroup.
 #include <algorithm>
 #include <cfloat>
 #include <climits>
