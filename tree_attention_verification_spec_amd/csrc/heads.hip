@@ -35,6 +35,16 @@ __device__ __forceinline__ bf16x8 load8(const __bf16* p) { return *reinterpret_c
 // grid: H * Dm / (16 RB) workgroups; workgroup = RB blocks of 16 output rows of one head, K
 // split over 4 waves (each wave all RB blocks of its K slice, so one h fragment serves RB
 // products and h is re-read from L2 once per workgroup).
+// Layout of each part of the z split in the workspace: [Dm / 8][NC][8], i.e. element (col, k)
+// at ((k / 8) * NC + col) * 8 + k % 8.  The LM head's B fragment (lane l: column l % 16,
+// k = 8 (l / 16) + [0, 8)) is then four 256-byte runs with consecutive lanes on consecutive 16
+// bytes, instead of 16 columns x 64 bytes scattered over the part (measured 18 us of the LM
+// head's 84 on the Medusa workload went to those fragment loads).
+__device__ __forceinline__ size_t zsplit_index(int NC, int Dm, int col, int k) {
+  (void)Dm;
+  return ((size_t)(k >> 3) * NC + col) * 8 + (k & 7);
+}
+
 template <int RB>
 __global__ __launch_bounds__(kThreads) void resblock_kernel(const __bf16* __restrict__ h,
                                                             const __bf16* __restrict__ W, int B, int H,
@@ -108,9 +118,10 @@ __global__ __launch_bounds__(kThreads) void resblock_kernel(const __bf16* __rest
       const __bf16 mid = (__bf16)r1;
       const __bf16 lo = (__bf16)(r1 - (float)mid);
       const size_t col = (size_t)b * H + j;
-      zsplit[(0 * (size_t)NC + col) * Dm + row] = hi;
-      zsplit[(1 * (size_t)NC + col) * Dm + row] = mid;
-      zsplit[(2 * (size_t)NC + col) * Dm + row] = lo;
+      const size_t at = zsplit_index(NC, Dm, col, row);
+      zsplit[at] = hi;
+      zsplit[(size_t)NC * Dm + at] = mid;
+      zsplit[2 * (size_t)NC * Dm + at] = lo;
     }
   }
 }
@@ -143,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void lm_head_kernel(const __bf16* __restr
     col_ok[cb] = col < NC;
 #pragma unroll
     for (int sp = 0; sp < 3; ++sp)
-      bptr[sp][cb] = zsplit + ((size_t)sp * NC + (col_ok[cb] ? col : 0)) * Dm + kbeg + 8 * lg;
+      bptr[sp][cb] = zsplit + (size_t)sp * NC * Dm + zsplit_index(NC, Dm, col_ok[cb] ? col : 0, kbeg + 8 * lg);
   }
   f32x4 acc[RB][CBN];
 #pragma unroll
@@ -165,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void lm_head_kernel(const __bf16* __restr
 #pragma unroll
     for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
-      for (int cb = 0; cb < CBN; ++cb) f.b[sp][cb] = load8(bptr[sp][cb] + s * 32);
+      for (int cb = 0; cb < CBN; ++cb) f.b[sp][cb] = load8(bptr[sp][cb] + (size_t)s * 32 * NC);
   };
   auto products = [&](const Frags& f) {
 #pragma unroll
