@@ -312,8 +312,8 @@ __global__ __launch_bounds__(kThreads) void rows_list_kernel(VerifyArgs a) {
   for (int k = 0; k < kListPer; ++k) {
     const int i = i0 + k;
     if (k < per && i < total) {
-      // a valid child's parent (invalid sequences list nothing; their error comes from the
-      // decision)
+      // a valid child's parent: entries of sequences with an invalid n_nodes, and invalid
+      // parent entries, list nothing (the decision reports those errors)
       const int b = i / a.N, c = i - b * a.N, n = nn[k], p = par[k];
       if (n >= 1 && n <= a.N && c >= 1 && c < n && p >= 0 && p < c) s_named[b * a.N + p] = 1;
     }
