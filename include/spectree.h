@@ -213,6 +213,38 @@ spec_status spec_verify(const float* target_logits, const float* draft_probs,
                         void* workspace, size_t ws_bytes, void* stream);
 
 /* --------------------------------------------------------------------------------------
+ * spec_kv_compact - KV-cache compaction that closes a verification round.
+ *
+ * [GUIDE] section "Speculative Decodingの動作原理を理解する": decoding repeats draft, one
+ * verifying pass of the target model over the KV cache, and rejection sampling; every
+ * candidate after a rejected one is discarded.  With tree node i's K/V at cache slot P + i
+ * (P = prefix_len[b], node 0 the root), the root and the accepted path are committed: for
+ * j = 1..accept_len[b], node path[b, j] moves from slot P + path[b, j] to slot P + j, in every
+ * layer, KV head and both caches, and the new prefix length is P + accept_len[b] + 1.  Other
+ * slots keep their contents.  A sequence with err[b] != 0, or whose path is not a root-first
+ * chain of increasing node indices ending inside the cache (path[b, 0] == 0,
+ * path[b, j] > path[b, j - 1], P + path[b, accept_len] < S_max, 0 <= accept_len <= max_depth),
+ * is left unchanged (its new prefix length is P); this is not reported as an error.
+ *
+ *   k_cache, v_cache  L layers of [B, Hkv, S_max, head_dim] elements of `dtype`, layer l at
+ *                     element offset l * layer_stride (ignored when L == 1); updated in place
+ *   prefix_len        int32 [B]
+ *   prefix_len_out    int32 [B] new prefix lengths, or NULL; must not alias prefix_len
+ *   path, accept_len  as written by spec_verify (path rows of max_depth + 1 entries)
+ *   err               int32 [B] as written by spec_verify, or NULL (no errors)
+ * All pointers are device memory.  No workspace.
+ * Supported: dtype BF16 or F32 with head_dim * element size a multiple of 16 bytes and at most
+ * 1024; 16-byte aligned caches and layer stride.
+ * Errors: SPEC_EINVAL (NULL pointers, sizes, layer_stride below one layer when L > 1,
+ * prefix_len_out == prefix_len), SPEC_EUNSUPPORTED (dtype, head_dim, alignment).
+ * ------------------------------------------------------------------------------------ */
+spec_status spec_kv_compact(void* k_cache, void* v_cache, size_t layer_stride, int L,
+                            const int32_t* prefix_len, int32_t* prefix_len_out,
+                            const int32_t* path, const int32_t* accept_len, const int32_t* err,
+                            int B, int Hkv, int S_max, int head_dim, int max_depth,
+                            spec_dtype dtype, void* stream);
+
+/* --------------------------------------------------------------------------------------
  * spec_medusa_heads - Medusa heads on the last hidden state, shared LM head, per-head top-k.
  *
  * [MTP] section "Medusa：本体に複数の予測ヘッドを足す" (several light heads on the same h_t,

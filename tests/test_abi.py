@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("spec_tree_build", "spec_tree_assemble", "spec_tree_attn", "spec_tree_attn_workspace",
               "spec_verify", "spec_verify_workspace", "spec_medusa_heads", "spec_medusa_heads_workspace",
-              "spec_strerror", "spec_prof_enable", "spec_prof_reset", "spec_prof_read"):
+              "spec_kv_compact", "spec_strerror", "spec_prof_enable", "spec_prof_reset",
+              "spec_prof_read"):
         assert n in names, n
 
 
@@ -77,6 +78,27 @@ def test_host_argument_checks(lib):
     assert lib.spec_medusa_heads(fake, fake, fake, 4, 2, 200, 1000, 8, fake, fake, None, fake, hw, None) == 2
     assert lib.spec_medusa_heads(fake, fake, fake, 4, 2, 256, 1000, 65, fake, fake, None, fake, hw, None) == 2
     assert lib.spec_medusa_heads(fake, fake, fake, 4, 2, 256, 1000, 8, fake, fake, None, fake, hw - 1, None) == 3
+
+
+def test_kv_compact_host_checks(lib):
+    fake = ctypes.c_void_p(0x1000)     # 16-byte aligned; never dereferenced (no call launches)
+    other = ctypes.c_void_p(0x2000)
+    odd = ctypes.c_void_p(0x1008)      # 8-byte aligned only
+    one = 1 * 8 * 100 * 128            # elements of one layer at B 1, Hkv 8, S_max 100, d 128
+
+    def call(k=fake, v=fake, stride=one, L=1, pl=fake, plo=other, path=fake, acc=fake, err=None,
+             B=1, H=8, S=100, d=128, md=8, dt=1):
+        return lib.spec_kv_compact(k, v, stride, L, pl, plo, path, acc, err, B, H, S, d, md, dt, None)
+
+    assert call(k=None) == 1 and call(path=None) == 1 and call(acc=None) == 1
+    assert call(L=0) == 1 and call(B=0) == 1 and call(md=-1) == 1
+    assert call(plo=fake) == 1                           # prefix_len_out aliases prefix_len
+    assert call(L=2, stride=one - 1) == 1                # layers overlap
+    assert call(dt=7) == 2                               # dtype
+    assert call(d=100) == 2                              # 200-byte rows: not a multiple of 16
+    assert call(d=512, dt=0) == 2                        # 2 KB rows: longer than a wave's pass
+    assert call(k=odd) == 2                              # alignment
+    assert call(L=2, stride=one + 4) == 2                # 8-byte layer stride in bf16
 
 
 def test_workspace_sizes_are_monotone(lib):

@@ -58,6 +58,8 @@ def lib():
     L.spec_medusa_heads_workspace.argtypes = [_I, _I, _I, _I, _I]
     L.spec_medusa_heads.restype = _I
     L.spec_medusa_heads.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _Z, _P]
+    L.spec_kv_compact.restype = _I
+    L.spec_kv_compact.argtypes = [_P, _P, _Z, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
     L.spec_prof_enable.restype = None
     L.spec_prof_enable.argtypes = [_I]
     L.spec_prof_reset.restype = None
@@ -95,7 +97,8 @@ def _stream(stream=None):
 
 
 def workspace(nbytes, device):
-    """A zero-filled workspace (the library requires zeros before first use)."""
+    """A workspace buffer of ``nbytes`` bytes on ``device`` (zero-filled, although the library
+    needs no initialisation: every call writes each workspace byte it later reads)."""
     return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
@@ -241,6 +244,38 @@ def spec_medusa_heads(h, W_res, W_lm, k, out=None, want_probs=True, ws=None, str
         _ptr(out["probs"], torch.float32, (B, H, V), "probs"),
         _ptr(ws, None, None, "workspace"), ws.numel(), _stream(stream)), "spec_medusa_heads")
     return out
+
+
+# ----------------------------------------------------------------------------- KV compaction
+
+def spec_kv_compact(k_cache, v_cache, prefix_len, path, accept_len, err=None, prefix_len_out=None,
+                    stream=None):
+    """Compact the accepted path's K/V after the prefix, in place, in every layer.
+
+    k_cache, v_cache: [L, B, Hkv, S_max, d] or [B, Hkv, S_max, d] (one layer), bf16 or f32,
+    contiguous.  path / accept_len / err: spec_verify's outputs.  Returns the new prefix
+    lengths (``prefix_len_out``, allocated when None; it must not be ``prefix_len``)."""
+    if k_cache.dim() == 4:
+        L, (B, Hkv, S_max, d) = 1, k_cache.shape
+    else:
+        L, B, Hkv, S_max, d = k_cache.shape
+    dt = k_cache.dtype
+    code = {torch.bfloat16: SPEC_BF16, torch.float32: SPEC_F32}.get(dt)
+    if code is None:
+        raise SpecError("k_cache must be bfloat16 or float32")
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise SpecError("v_cache must have the shape of k_cache")
+    max_depth = path.shape[1] - 1
+    if prefix_len_out is None:
+        prefix_len_out = torch.empty_like(prefix_len)
+    _check(lib().spec_kv_compact(
+        _ptr(k_cache, dt, None, "k_cache"), _ptr(v_cache, dt, None, "v_cache"), B * Hkv * S_max * d, L,
+        _ptr(prefix_len, torch.int32, (B,), "prefix_len"),
+        _ptr(prefix_len_out, torch.int32, (B,), "prefix_len_out"),
+        _ptr(path, torch.int32, (B, max_depth + 1), "path"), _ptr(accept_len, torch.int32, (B,), "accept_len"),
+        _ptr(err, torch.int32, (B,), "err"), B, Hkv, S_max, d, max_depth, code, _stream(stream)),
+        "spec_kv_compact")
+    return prefix_len_out
 
 
 # ----------------------------------------------------------------------------- timing
