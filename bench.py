@@ -192,6 +192,44 @@ def algorithmic(w, a, parents, depths, mode):
     return out
 
 
+def kv_compact_timing(st, layers_max=32, cap_bytes=8 << 30, reps=50):
+    """The KV-cache compaction that closes a round (a row after the verification step, measured
+    outside it): a cache of the workload's KV shape with up to `layers_max` layers (32 for a
+    Llama-3-8B-class model; fewer when the cache would pass `cap_bytes`), compacted with the
+    step's own verification outputs.  The cache contents do not matter to the copy's time."""
+    import torch
+    from tree_attention_verification_spec_amd import binding as sb
+    s0, ver = st.sets[0], st.outs[0]["ver"]
+    B, Hkv, S_max, d = s0["k"].shape
+    per_layer = 2 * B * Hkv * S_max * d * s0["k"].element_size()
+    layers = int(max(1, min(layers_max, cap_bytes // per_layer)))
+    k = torch.empty((layers, B, Hkv, S_max, d), dtype=s0["k"].dtype, device="cuda")
+    v = torch.empty_like(k)
+    P_out = torch.empty_like(s0["P"])
+    call = lambda: sb.spec_kv_compact(k, v, s0["P"], ver["path"], ver["accept_len"], err=ver["err"],
+                                      prefix_len_out=P_out)
+    call()
+    torch.cuda.synchronize()
+    try:
+        sb.prof_reset()
+        sb.prof_enable(True)
+        for _ in range(reps):
+            call()
+        torch.cuda.synchronize()
+        sb.prof_enable(False)
+        ms, cnt = sb.prof_read("kv_compact")
+    finally:
+        sb.prof_enable(False)
+        sb.prof_reset()
+    acc, err = ver["accept_len"].cpu().numpy(), ver["err"].cpu().numpy()
+    rows = int(acc[err == 0].clip(min=0).sum())
+    nbytes = 2 * rows * Hkv * d * k.element_size() * 2 * layers     # read + write, K and V
+    del k, v
+    us = ms / cnt * 1e3
+    return {"layers": layers, "us": round(us, 3), "algorithmic_bytes": nbytes,
+            "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 2) if us > 0 else None}
+
+
 def roofline_entry(name, nbytes, flops, avg_ms, traffic):
     intensity = flops / nbytes if nbytes else 0.0
     if name.startswith("tree_attn") and intensity > RIDGE:
@@ -365,6 +403,11 @@ def main():
             extra = f"  {b_ / (kernels[k] * 1e-3) / 1e9:8.1f} GB/s  {f_ / (kernels[k] * 1e-3) / 1e12:8.1f} TFLOP/s"
         log(f"  {k:22s} {kernels[k] * 1e3:9.2f} us{extra}")
     log(f"step {ms_step * 1e3:.2f} us; kernels sum {sum(kernels.values()) * 1e3:.2f} us")
+    kvc = None
+    if w.dtype == "bf16":
+        kvc = kv_compact_timing(st)
+        log(f"kv_compact (after the step, not in it): {kvc['layers']} layers, {kvc['us']:.2f} us, "
+            f"{kvc['algorithmic_bytes']} bytes moved")
 
     if args.copy_calibration_mb:
         nb = args.copy_calibration_mb * (1 << 20)
@@ -400,6 +443,7 @@ def main():
         "roofline": roof,
         "kernels_us": {k: round(v * 1e3, 3) for k, v in kernels.items()},
         "cpu_baseline": cpu,
+        "next_rows": {"kv_compact": kvc},
     }
     print(json.dumps(line), flush=True)
 
