@@ -23,7 +23,8 @@ from .errors import (ERR_ROOT, ERR_PARENT, ERR_DEPTH, ERR_NNODES, ERR_PREFIX, ER
                      ERR_DRAFTROW, ERR_NONFINITE, ERR_MAP, ERR_RANK, encode_err, decode_err)
 from .tree import tree_build, pack_mask, unpack_mask
 from .attention import tree_attention, tree_attention_row
-from .verify import verify, MODE_GREEDY, MODE_TYPICAL, MODE_REJECT, sample_inverse_cdf
+from .verify import (verify, MODE_GREEDY, MODE_TYPICAL, MODE_REJECT, MODE_WALK,
+                     sample_inverse_cdf, residual_after_rejections)
 from .heads import medusa_heads
 from .assemble import tree_assemble
 from .kv import kv_compact
@@ -32,6 +33,7 @@ __all__ = [
     "ERR_ROOT", "ERR_PARENT", "ERR_DEPTH", "ERR_NNODES", "ERR_PREFIX", "ERR_TOKEN",
     "ERR_DRAFTROW", "ERR_NONFINITE", "ERR_MAP", "ERR_RANK", "encode_err", "decode_err",
     "tree_build", "pack_mask", "unpack_mask", "tree_attention", "tree_attention_row",
-    "verify", "MODE_GREEDY", "MODE_TYPICAL", "MODE_REJECT", "sample_inverse_cdf",
+    "verify", "MODE_GREEDY", "MODE_TYPICAL", "MODE_REJECT", "MODE_WALK", "sample_inverse_cdf",
+    "residual_after_rejections",
     "medusa_heads", "tree_assemble", "kv_compact",
 ]

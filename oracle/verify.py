@@ -35,6 +35,19 @@ Readings taken where the pages are silent or loose:
   * Draws use uniforms[b, 0] and inverse-CDF sampling: the smallest token t whose running
     sum of q from token 0 upward exceeds u * Z, Z the total sum, both accumulated in float64
     in ascending token order.
+  * WALK (the tree-lossless variant of REJECT): the tree is walked from the root.  At node p
+    the children are tried in index order against a running distribution R, first R = T_p;
+    child c (token x, uniform u_c, draft row D) is accepted iff u_c * D[x] < R[x]; on a
+    rejection R becomes norm(relu(R - D)) before the next sibling is tried, which is the
+    guide's residual rule applied once per rejected sibling, so every sibling is a fresh
+    draw against what the earlier rejections left.  The first accepted child becomes the new
+    p; when every child of p is rejected, or p has none, the walk stops at m = p and the
+    bonus is drawn from R (from T_m when m has no child, or when R has summed to zero, after
+    which every later sibling counts as rejected).  With children drawn i.i.d. from D this
+    keeps the law of the emitted tokens equal to the target's on any tree (the residual
+    argument applied sibling after sibling); REJECT is exact only on chains.  The children of
+    one node must share a draft row (as in both layouts above): a child whose row differs
+    from its first sibling's is ERR_DRAFTROW.  node_accept marks the walk's path.
   * Draft rows may live on a smaller draft vocabulary: t2d[x] maps target token x to a
     draft index, -1 for tokens the draft cannot emit (their draft probability is 0).  A
     candidate whose entry lies outside [-1, Vd) is an error; any other such entry is read
@@ -49,6 +62,7 @@ from .errors import (ERR_ROOT, ERR_PARENT, ERR_DEPTH, ERR_NNODES, ERR_TOKEN, ERR
 MODE_GREEDY = 0
 MODE_TYPICAL = 1
 MODE_REJECT = 2
+MODE_WALK = 3
 
 
 def sample_inverse_cdf(q, u):
@@ -96,6 +110,59 @@ def _draft_on_target_vocab(draft_row_probs, t2d, V):
     return out
 
 
+def _residual_step(Rv, D):
+    """One rejected sibling: (norm(relu(R - D)), its normaliser); None for a zero residual."""
+    Rn = np.maximum(Rv - D, 0.0)
+    z = float(Rn.sum())
+    return (Rn / z if z > 0 else None), z
+
+
+def residual_after_rejections(T, D, j):
+    """The running distribution after j rejected siblings that share draft row D: R_0 = T and
+    R_i = norm(relu(R_(i-1) - D)); None once a residual has summed to zero."""
+    Rv = np.asarray(T, dtype=np.float64).copy()
+    D = np.asarray(D, dtype=np.float64)
+    for _ in range(j):
+        Rv, _ = _residual_step(Rv, D)
+        if Rv is None:
+            return None
+    return Rv
+
+
+def _walk(b, n, children, stats, logits, tokens, uniforms, draft_probs, draft_row, t2d, V, margin):
+    """WALK mode for one sequence (see the module's readings).  Returns the path root..m and
+    the distribution of the bonus draw (None: T_m).  Fills margin[b, c] for every tested
+    child with the distance of its test from the boundary, relative to the magnitudes that
+    enter it: writing R = relu(T - c D) / s (c, s follow from the normalisers of the earlier
+    rejections), |u D[x] s - (T[x] - c D[x])| / (T[x] + c D[x] + u D[x] s)."""
+    cur, chain = 0, [0]
+    while True:
+        kids = children[cur]
+        if not kids:
+            return chain, None
+        T = stats[cur]["T"]
+        D = _draft_on_target_vocab(draft_probs[b, int(draft_row[b, kids[0]])], t2d, V)
+        Rv = T.copy()
+        c_sc, s_sc = 0.0, 1.0
+        live, nxt = True, None
+        for c in kids:
+            x, u = int(tokens[b, c]), float(uniforms[b, c])
+            if live:
+                if D[x] > 0:
+                    num = abs(u * D[x] * s_sc - (T[x] - c_sc * D[x]))
+                    margin[b, c] = num / (T[x] + c_sc * D[x] + u * D[x] * s_sc)
+                if u * D[x] < Rv[x]:
+                    nxt = c
+                    break
+                Rv, z = _residual_step(Rv, D)
+                c_sc, s_sc = c_sc + s_sc, s_sc * z
+                live = Rv is not None
+        if nxt is None:
+            return chain, (Rv if live else None)
+        chain.append(nxt)
+        cur = nxt
+
+
 def verify(target_logits, tokens, parents, uniforms, mode, *, draft_probs=None, draft_row=None,
            t2d=None, n_nodes=None, eps=0.09, delta=0.3, max_depth=None):
     """target_logits [B, N, V] (row p = target logits at node p); tokens, parents [B, N];
@@ -111,7 +178,8 @@ def verify(target_logits, tokens, parents, uniforms, mode, *, draft_probs=None, 
     if max_depth is None:
         max_depth = N - 1
     n_nodes = np.full(B, N, dtype=np.int64) if n_nodes is None else np.asarray(n_nodes, np.int64)
-    if mode == MODE_REJECT:
+    drafted = mode in (MODE_REJECT, MODE_WALK)
+    if drafted:
         R, Vd = draft_probs.shape[1], draft_probs.shape[2]
 
     accept_len = np.zeros(B, dtype=np.int32)
@@ -150,7 +218,7 @@ def verify(target_logits, tokens, parents, uniforms, mode, *, draft_probs=None, 
             x = int(tokens[b, c])
             if not 0 <= x < V:
                 problems.append((c, ERR_TOKEN))
-            if mode == MODE_REJECT:
+            if drafted:
                 if not 0 <= int(draft_row[b, c]) < R:
                     problems.append((c, ERR_DRAFTROW))
                 if t2d is not None and 0 <= x < V and not -1 <= int(t2d[x]) < Vd:
@@ -160,6 +228,12 @@ def verify(target_logits, tokens, parents, uniforms, mode, *, draft_probs=None, 
             if 0 <= par[c] < c:
                 children[par[c]].append(c)
         internal = [p for p in range(n) if children[p]]
+        if mode == MODE_WALK:
+            for p in internal:
+                r0 = int(draft_row[b, children[p][0]])
+                for c in children[p][1:]:
+                    if 0 <= r0 < R and 0 <= int(draft_row[b, c]) < R and int(draft_row[b, c]) != r0:
+                        problems.append((c, ERR_DRAFTROW))
         for p in internal:
             if not np.all(np.isfinite(logits[b, p])):
                 problems.append((p, ERR_NONFINITE))
@@ -169,9 +243,16 @@ def verify(target_logits, tokens, parents, uniforms, mode, *, draft_probs=None, 
 
         stats = {p: _row_stats(logits[b, p]) for p in internal}
 
-        # Per-node tests.
-        accepted = [True] * n
-        for c in range(1, n):
+        walk_q = None
+        if mode == MODE_WALK:
+            chain, walk_q = _walk(b, n, children, stats, logits, tokens, uniforms, draft_probs,
+                                  draft_row, t2d, V, margin)
+            m = chain[-1]
+            accepted = [c in chain for c in range(n)]
+        else:
+            accepted = [True] * n
+        # Per-node tests (the walk tests its nodes as it goes).
+        for c in range(1, n if mode != MODE_WALK else 1):
             p, x = par[c], int(tokens[b, c])
             st = stats[p]
             t_px = st["T"][x]
@@ -195,27 +276,28 @@ def verify(target_logits, tokens, parents, uniforms, mode, *, draft_probs=None, 
             else:
                 raise ValueError("unknown mode")
 
-        # A node survives iff every node on its chain below the root was accepted
-        # (candidates after a rejection are dropped).
-        survives = [False] * n
-        for c in range(n):
-            ok, j = True, c
-            while j > 0:
-                ok = ok and accepted[j]
-                j = par[j]
-            survives[c] = ok
+        if mode != MODE_WALK:
+            # A node survives iff every node on its chain below the root was accepted
+            # (candidates after a rejection are dropped).
+            survives = [False] * n
+            for c in range(n):
+                ok, j = True, c
+                while j > 0:
+                    ok = ok and accepted[j]
+                    j = par[j]
+                survives[c] = ok
 
-        # Deepest survivor, smallest index on ties.
-        m = 0
-        for c in range(1, n):
-            if survives[c] and depth[c] > depth[m]:
-                m = c
-        chain = []
-        j = m
-        while j != -1:
-            chain.append(j)
-            j = par[j] if j > 0 else -1
-        chain.reverse()
+            # Deepest survivor, smallest index on ties.
+            m = 0
+            for c in range(1, n):
+                if survives[c] and depth[c] > depth[m]:
+                    m = c
+            chain = []
+            j = m
+            while j != -1:
+                chain.append(j)
+                j = par[j] if j > 0 else -1
+            chain.reverse()
 
         # Bonus token from row m.
         row_m = logits[b, m]
@@ -228,6 +310,8 @@ def verify(target_logits, tokens, parents, uniforms, mode, *, draft_probs=None, 
             tok, bm = st_m["argmax"], st_m["gap"]
         elif mode == MODE_TYPICAL:
             tok, bm = sample_inverse_cdf(st_m["T"], u0)
+        elif mode == MODE_WALK:
+            tok, bm = sample_inverse_cdf(st_m["T"] if walk_q is None else walk_q, u0)
         else:
             q = st_m["T"]
             if children[m]:
