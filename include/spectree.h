@@ -51,7 +51,8 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
 typedef enum {
   SPEC_VERIFY_GREEDY = 0,   /* temperature 0: accept iff the token is the argmax          */
   SPEC_VERIFY_TYPICAL = 1,  /* accept iff T[x] >= min(eps, delta * exp(-entropy(T)))     */
-  SPEC_VERIFY_REJECT = 2    /* accept with probability min(1, T[x] / D[x])               */
+  SPEC_VERIFY_REJECT = 2,   /* accept with probability min(1, T[x] / D[x])               */
+  SPEC_VERIFY_WALK = 3      /* REJECT made lossless on trees: siblings tried in order      */
 } spec_mode;
 
 /* Per-sequence data error codes (low byte of an error word). */
@@ -176,16 +177,27 @@ spec_status spec_tree_attn(const void* q, const void* k_cache, const void* v_cac
  *   REJECT   accept iff uniforms[b, c] * D[x] < T_p[x], D = draft_probs[b, draft_row[b, c]]
  *            seen on the target vocabulary through t2d
  * A node survives iff it and all its ancestors below the root were accepted.  m = the deepest
- * survivor (lowest index on ties); accept_len = depth(m); path = root .. m.  Bonus token, drawn
+ * survivor (lowest index on ties); accept_len = depth(m); path = root .. m.
+ *   WALK     the same section's residual rule applied per rejected sibling, which keeps the
+ *            output law equal to the target's on branching trees (REJECT keeps it on chains
+ *            only).  From p = root: the children of p, in index order, are tested against a
+ *            running R (first T_p): accept iff uniforms[b, c] * D[x] < R[x]; a rejection sets
+ *            R = norm(relu(R - D)) (zero mass: every later sibling is rejected).  The first
+ *            accepted child becomes p; the walk ends at m when all children of m (or none)
+ *            are rejected.  All children of a node must share one draft row (else
+ *            SPEC_ERR_DRAFTROW at the first child that differs).  node_accept marks the path.
+ * Bonus token, drawn
  * with uniforms[b, 0] by inverse CDF (smallest t whose running sum from token 0 exceeds u * Z):
  *   GREEDY   argmax T_m
  *   TYPICAL  a draw from T_m
  *   REJECT   if m has children: a draw from norm(relu(T_m - D)), D the draft row of m's
  *            lowest-index child (T_m if that residual is all zero); else a draw from T_m.
+ *   WALK     the running R of m after all its children were rejected (T_m if it has summed
+ *            to zero, or if m has no child).
  *
  *   target_logits float [B, N, V]
- *   draft_probs   float [B, R, Vd]  draft distributions (REJECT only; else may be NULL)
- *   draft_row     int32 [B, N]      row of draft_probs that proposed node c (REJECT only)
+ *   draft_probs   float [B, R, Vd]  draft distributions (REJECT, WALK; else may be NULL)
+ *   draft_row     int32 [B, N]      row of draft_probs that proposed node c (REJECT, WALK)
  *   t2d           int32 [V]         optional (NULL: identity, requires Vd == V): target id ->
  *                                   draft id, -1 where the draft vocabulary lacks the token
  *   tokens        int32 [B, N]      candidate token of each node (node 0's is ignored)
@@ -195,7 +207,8 @@ spec_status spec_tree_attn(const void* q, const void* k_cache, const void* v_cac
  *   max_depth     length of path minus one; a valid node deeper than this is SPEC_ERR_DEPTH
  * Outputs:
  *   accept_len  int32 [B]; path int32 [B, max_depth + 1] (-1 padded); bonus_token int32 [B];
- *   node_accept uint8 [B, N] optional (NULL): per-node test result (root 1, padding 0);
+ *   node_accept uint8 [B, N] optional (NULL): per-node test result (root 1, padding 0;
+ *               WALK: 1 on the path);
  *   err         int32 [B].
  * A sequence with n_nodes 0, or with an error, gets accept_len 0, path all -1, bonus -1 and
  * node_accept all 0.

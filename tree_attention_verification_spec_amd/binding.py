@@ -15,8 +15,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libspectree.so")
 
 SPEC_F32, SPEC_BF16 = 0, 1
-GREEDY, TYPICAL, REJECT = 0, 1, 2
-MODES = {"greedy": GREEDY, "typical": TYPICAL, "reject": REJECT}
+GREEDY, TYPICAL, REJECT, WALK = 0, 1, 2, 3
+MODES = {"greedy": GREEDY, "typical": TYPICAL, "reject": REJECT, "walk": WALK}
 
 _lib = None
 _P = ctypes.c_void_p

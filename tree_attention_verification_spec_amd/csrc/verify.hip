@@ -63,6 +63,7 @@ struct BonusPlan {
   int r;              // draft row of the residual
   float M;            // row max of m (residual draws)
   double S;           // sum exp(x - M) over row m (residual draws)
+  double cs;          // the residual is relu(T_m - cs * D): 1, or after the walk's rejections
 };
 
 struct BonusPart {
@@ -101,6 +102,9 @@ struct VerifyArgs {
   BonusPart* bparts;    // [B, C]
   double* weights;      // [B, C * CS]: the bonus pass's per-token weights (kinds 2 and 3),
                         // kept only for small batches (NULL otherwise)
+  double* wc;           // [B, N] walk: child c is tested against relu(T_p - wc D) / wf
+  double* wf;           // [B, N]
+  double* wend;         // [B, N] walk: residual scale after every child of node p is rejected
 };
 
 // ------------------------------------------------------------------ reductions
@@ -376,6 +380,9 @@ __device__ BonusPlan decide(const VerifyArgs& a, int b, bool out) {
   __shared__ double s_S[SPEC_MAX_NODES];
   __shared__ double s_H[SPEC_MAX_NODES];
   __shared__ int s_drow[SPEC_MAX_NODES];
+  __shared__ int s_first[SPEC_MAX_NODES];      // lowest-index child of each node
+  __shared__ int s_fpass[SPEC_MAX_NODES];      // walk: lowest-index child that passes its test
+  __shared__ double s_wend[SPEC_MAX_NODES];
   __shared__ int s_err, s_best, s_minchild;
   __shared__ BonusPlan s_plan;
   const int c = threadIdx.x;
@@ -390,7 +397,13 @@ __device__ BonusPlan decide(const VerifyArgs& a, int b, bool out) {
   const int par_c = a.parents[ci];
   const int tok_c = a.tokens[ci];
   const float u_c = a.uniforms[ci];
-  const int drow_c = a.mode == SPEC_VERIFY_REJECT ? a.draft_row[ci] : -1;
+  const bool walk = a.mode == SPEC_VERIFY_WALK;
+  const bool rej = a.mode == SPEC_VERIFY_REJECT || walk;
+  const int drow_c = rej ? a.draft_row[ci] : -1;
+  // walk: this node's test constants and its residual scale as a parent (a.wc, a.wf, a.wend
+  // always point into the workspace; other modes read and ignore them)
+  const size_t wi = walk ? ci : 0;
+  const double wc_c = a.wc[wi], wf_c = a.wf[wi], wend_c = a.wend[wi];
   const int L = a.N <= 64 ? 4 : (a.N <= 128 ? 2 : 1);
   const int mn = c / L, sub = c % L;
   const RowPart* rp = a.rowparts + ((size_t)b * a.N + min(mn, a.N - 1)) * a.CR;
@@ -408,12 +421,14 @@ __device__ BonusPlan decide(const VerifyArgs& a, int b, bool out) {
   const int pc = min(max(par_c, 0), a.N - 1);
   const int tc = min(max(tok_c, 0), a.V - 1);
   const float lpx_c = a.logits[((size_t)b * a.N + pc) * a.V + tc];
-  const bool rej = a.mode == SPEC_VERIFY_REJECT;
   const size_t drow_off = rej ? ((size_t)b * a.R + min(max(drow_c, 0), a.R - 1)) * a.Vd : 0;
   const float dval_c = *((rej && !a.t2d) ? a.draft + drow_off + tc : a.logits);
   const int dx_c = *((rej && a.t2d) ? a.t2d + tc : a.parents);
   if (c == 0) { s_err = INT_MAX; s_best = -1; s_minchild = INT_MAX; }
-  if (c < a.N) { s_par[c] = par_c; s_has[c] = 0; s_acc[c] = 0; s_drow[c] = drow_c; }
+  if (c < a.N) {
+    s_par[c] = par_c; s_has[c] = 0; s_acc[c] = 0; s_drow[c] = drow_c;
+    s_first[c] = INT_MAX; s_fpass[c] = INT_MAX; s_wend[c] = wend_c;
+  }
   __syncthreads();
   BonusPlan* plan = a.plans + b;
   if (n < 0 || n > a.N || n == 0) {
@@ -427,7 +442,10 @@ __device__ BonusPlan decide(const VerifyArgs& a, int b, bool out) {
   // rows read: nodes named as a parent by some valid child
   if (c >= 1 && c < n) {
     const int p = s_par[c];
-    if (p >= 0 && p < c) s_has[p] = 1;
+    if (p >= 0 && p < c) {
+      s_has[p] = 1;
+      if (walk) atomicMin(&s_first[p], c);
+    }
   }
   __syncthreads();
   const bool mhas = mn < n && s_has[mn];
@@ -452,8 +470,11 @@ __device__ BonusPlan decide(const VerifyArgs& a, int b, bool out) {
       }
       if (depth > a.max_depth) code = SPEC_ERR_DEPTH;
       else if (tok < 0 || tok >= a.V) code = SPEC_ERR_TOKEN;
-      if (code == 0 && a.mode == SPEC_VERIFY_REJECT) {
+      if (code == 0 && rej) {
+        // the walk needs the children of a node on one draft row (its first child's)
+        const int r0 = walk ? s_drow[s_first[s_par[c]]] : drow;
         if (drow < 0 || drow >= a.R) code = SPEC_ERR_DRAFTROW;
+        else if (r0 >= 0 && r0 < a.R && r0 != drow) code = SPEC_ERR_DRAFTROW;
         else dx = tok;                          // mapped (and checked) after the merge
       }
     }
@@ -557,16 +578,27 @@ __device__ BonusPlan decide(const VerifyArgs& a, int b, bool out) {
     } else {
       double d = 0.0;
       if (dx >= 0) d = a.t2d ? (double)a.draft[drow_off + dx] : (double)dval_c;
-      acc = (double)u * d < T;
+      // walk: u D[x] < R[x] with R = relu(T - wc D) / wf, the running residual after the
+      // earlier siblings' rejections (none left once it has summed to zero)
+      acc = walk ? (wf_c > 0.0 && (double)u * d * wf_c < T - wc_c * d) : (double)u * d < T;
     }
     s_acc[c] = acc ? 1 : 0;
   }
   if (c == 0) s_acc[0] = 1;
   __syncthreads();
+  if (walk) {
+    // siblings are tried in index order: only the first child that passes is taken
+    if (c >= 1 && c < n && s_acc[c]) atomicMin(&s_fpass[s_par[c]], c);
+    __syncthreads();
+    const int keep = (c >= 1 && c < n) ? (s_acc[c] && s_fpass[s_par[c]] == c) : 0;
+    __syncthreads();
+    if (c >= 1 && c < n) s_acc[c] = keep;
+    __syncthreads();
+  }
 
-  // ---- survival and the deepest survivor
+  // ---- survival and the deepest survivor (walk: the survivors are the walk's path)
+  bool ok = true;
   if (c < n) {
-    bool ok = true;
     int j = c;
     while (j > 0) {
       ok = ok && s_acc[j];
@@ -574,7 +606,8 @@ __device__ BonusPlan decide(const VerifyArgs& a, int b, bool out) {
     }
     if (ok) atomicMax(&s_best, (s_dep[c] << 9) | (511 - c));
   }
-  if (out && c < a.N && a.node_accept) a.node_accept[(size_t)b * a.N + c] = (c < n) ? (uint8_t)s_acc[c] : 0;
+  if (out && c < a.N && a.node_accept)
+    a.node_accept[(size_t)b * a.N + c] = (c < n) ? (uint8_t)(walk ? ok : s_acc[c]) : 0;
   __syncthreads();
   const int m = 511 - (s_best & 511);
   const int dm = s_best >> 9;
@@ -593,7 +626,7 @@ __device__ BonusPlan decide(const VerifyArgs& a, int b, bool out) {
       a.accept_len[b] = dm;
       a.err[b] = 0;
     }
-    BonusPlan pl{m, 0, 0, 0.f, 0.0};
+    BonusPlan pl{m, 0, 0, 0.f, 0.0, 1.0};
     if (a.mode == SPEC_VERIFY_GREEDY) {
       if (s_has[m]) {
         if (out) a.bonus[b] = s_am[m];
@@ -607,6 +640,7 @@ __device__ BonusPlan decide(const VerifyArgs& a, int b, bool out) {
       pl.r = s_drow[s_minchild];
       pl.M = s_mx[m];
       pl.S = s_S[m];
+      if (walk) pl.cs = s_wend[m];
     } else {
       pl.kind = 2;
     }
@@ -627,6 +661,94 @@ __device__ __forceinline__ double draft_at(const VerifyArgs& a, int b, int r, in
     return (dx >= 0 && dx < a.Vd) ? (double)a.draft[((size_t)b * a.R + r) * a.Vd + dx] : 0.0;
   }
   return (double)a.draft[((size_t)b * a.R + r) * a.Vd + v];
+}
+
+// ------------------------------------------------------------------ walk: residual chains
+//
+// The walk tries the children c_1 < c_2 < ... of a node p (one draft row D) against a running
+// distribution: R_0 = T_p, and R_j = norm(relu(R_(j-1) - D)) after the j-th rejection.  Since
+// relu(relu(y) - z) = relu(y - z) for z >= 0, R_j = relu(T_p - c_j D) / f(c_j) with
+// f(c) = sum_x relu(T_p[x] - c D[x]), c_0 = 0, f(c_0) = 1 and c_(j+1) = c_j + f(c_j).  None of
+// this depends on which children pass, so the chain of every node is computed ahead of the
+// decision, all nodes at once: the workgroup of node p writes (c_(j-1), f(c_(j-1))) for its
+// j-th child and c_k (k children) for a residual bonus draw at p.  Each f is one pass over the
+// row: fp32 exp(x - M) as in the row pass, scaled by 1/S and reduced against c D in fp64.
+// Grid (seq, node); nodes with fewer than two children need no pass.
+constexpr int kChainUnroll = 8;
+
+__global__ __launch_bounds__(kThreads) void walk_chain_kernel(VerifyArgs a) {
+  __shared__ int s_kids[SPEC_MAX_NODES];
+  __shared__ int s_wcnt[kWavesPB];
+  __shared__ float s_M;
+  __shared__ double s_invS;
+  const int b = blockIdx.x / a.N, p = blockIdx.x - b * a.N;
+  const int t = threadIdx.x, lane = t & (kWave - 1), wv = t >> 6;
+  const int n = a.n_nodes ? a.n_nodes[b] : a.N;
+  if (n < 1 || n > a.N || p >= n) return;
+  const size_t base = (size_t)b * a.N;
+  // the children of p in index order (N <= kThreads: one candidate node per thread)
+  const int i = p + 1 + t;
+  const bool kid = i < n && a.parents[base + i] == p;
+  const unsigned long long bal = __ballot(kid);
+  if (lane == 0) s_wcnt[wv] = __popcll(bal);
+  __syncthreads();
+  int off = 0, k = 0;
+#pragma unroll
+  for (int q = 0; q < kWavesPB; ++q) {
+    off += q < wv ? s_wcnt[q] : 0;
+    k += s_wcnt[q];
+  }
+  if (kid) s_kids[off + __popcll(bal & ((1ull << lane) - 1))] = i;
+  __syncthreads();
+  if (k == 0) return;
+  if (t == 0) {
+    a.wc[base + s_kids[0]] = 0.0;
+    a.wf[base + s_kids[0]] = 1.0;
+    if (k == 1) a.wend[base + p] = 1.0;
+  }
+  if (k == 1) return;
+  if (t == 0) {                            // row statistics of p from its row-pass chunks
+    const RowPart* rp = a.rowparts + (base + p) * a.CR;
+    float M = -INFINITY;
+    for (int q = 0; q < a.CR; ++q) M = fmaxf(M, rp[q].m);
+    double S = 0.0;
+    for (int q = 0; q < a.CR; ++q)
+      if (rp[q].m != -INFINITY) S += rp[q].S * exp((double)rp[q].m - (double)M);
+    s_M = M;
+    s_invS = 1.0 / S;
+  }
+  __syncthreads();
+  const float M = s_M;
+  const double invS = s_invS;
+  const int r = min(max(a.draft_row[base + s_kids[0]], 0), a.R - 1);
+  const float* row = a.logits + (base + p) * a.V;
+  double cj = 1.0;
+  for (int j = 1; j < k; ++j) {
+    double f = 0.0;
+    for (int v0 = 0; v0 < a.V; v0 += kThreads * kChainUnroll) {
+      float x[kChainUnroll];
+      double d[kChainUnroll];
+#pragma unroll
+      for (int u = 0; u < kChainUnroll; ++u) {
+        const int v = v0 + u * kThreads + t;
+        const int at = v < a.V ? v : 0;
+        x[u] = row[at];
+        d[u] = draft_at(a, b, r, at);
+      }
+#pragma unroll
+      for (int u = 0; u < kChainUnroll; ++u) {
+        const double q = (double)__expf(x[u] - M) * invS - cj * d[u];
+        f += (v0 + u * kThreads + t < a.V && q > 0.0) ? q : 0.0;
+      }
+    }
+    f = block_sum(f);
+    if (t == 0) {
+      a.wc[base + s_kids[j]] = cj;
+      a.wf[base + s_kids[j]] = f;
+    }
+    cj += f;
+  }
+  if (t == 0) a.wend[base + p] = cj;
 }
 
 template <int VEC, int CS>
@@ -671,7 +793,7 @@ __device__ void bonus_chunk(const VerifyArgs& a, int b, int c, const BonusPlan& 
       if (chunk_index<VEC>(lo, k) < hi) {
         const double e = exp((double)x[k] - (double)pl.M);
         S += e;
-        w[k] = fmax(e * inv - dr[k], 0.0);
+        w[k] = fmax(e * inv - pl.cs * dr[k], 0.0);
         Q += w[k];
       }
     }
@@ -711,12 +833,12 @@ __global__ __launch_bounds__(kThreads) void decide_bonus_kernel(VerifyArgs a) {
 }
 
 // Weight of token v for draw `kind`: 2 -> exp(x - M) (T up to the common factor 1/S),
-// 3 -> relu(exp(x - M) / S - D[v]).
+// 3 -> relu(exp(x - M) / S - cs D[v]).
 __device__ __forceinline__ double draw_weight(const VerifyArgs& a, int b, int kind, int r, float x, int v,
-                                              float M, double S) {
+                                              float M, double S, double cs) {
   const double e = exp((double)x - (double)M);
   if (kind == 2) return e;
-  return fmax(e / S - draft_at(a, b, r, v), 0.0);
+  return fmax(e / S - cs * draft_at(a, b, r, v), 0.0);
 }
 
 // Smallest token of chunk [lo, hi) whose running sum (from `base`, fp64, ascending token order)
@@ -724,7 +846,7 @@ __device__ __forceinline__ double draw_weight(const VerifyArgs& a, int b, int ki
 // so the run is read with VEC-wide loads).
 template <int VEC, int CS>
 __device__ int scan_chunk(const VerifyArgs& a, int b, int kind, int r, const float* row, int lo, int hi,
-                          float M, double S, double base, double thr) {
+                          float M, double S, double cs, double base, double thr) {
   constexpr int kPer = CS / kThreads;
   __shared__ int s_hit;
   const int per = (hi - lo + kThreads * VEC - 1) / (kThreads * VEC) * VEC;   // <= kPer
@@ -750,7 +872,7 @@ __device__ int scan_chunk(const VerifyArgs& a, int b, int kind, int r, const flo
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int v = my_lo + k;
-    w[k] = (k < per && v < hi) ? draw_weight(a, b, kind, r, xv[k], v, M, S) : 0.0;
+    w[k] = (k < per && v < hi) ? draw_weight(a, b, kind, r, xv[k], v, M, S, cs) : 0.0;
     mine += w[k];
   }
   if (threadIdx.x == 0) s_hit = INT_MAX;
@@ -770,12 +892,13 @@ __device__ int scan_chunk(const VerifyArgs& a, int b, int kind, int r, const flo
   return hit == INT_MAX ? -1 : hit;
 }
 
-// Inverse-CDF draw with u = uniforms[b, 0] over the weights of `kind`; thread t < C holds the
-// sum q of chunk t.  The chunk is the first whose inclusive prefix exceeds u * Z (if rounding
-// puts u * Z past the end: the last chunk of positive mass), then the token inside it.
+// Inverse-CDF draw with u = uniforms[b, 0] over the weights of `kind` (rcs: the residual's
+// scale of D); thread t < C holds the sum q of chunk t.  The chunk is the first whose inclusive
+// prefix exceeds u * Z (if rounding puts u * Z past the end: the last chunk of positive mass),
+// then the token inside it.
 template <int VEC, int CS>
 __device__ int draw(const VerifyArgs& a, int b, int kind, int r, const float* row, double q, float M,
-                    double S, float u) {
+                    double S, double rcs, float u) {
   __shared__ int s_pick, s_last, s_tok;
   __shared__ double s_base[2];
   const int t = threadIdx.x;
@@ -794,12 +917,12 @@ __device__ int draw(const VerifyArgs& a, int b, int kind, int r, const float* ro
   const int cs = pick != INT_MAX ? pick : (last >= 0 ? last : 0);
   const double base = pick != INT_MAX ? s_base[0] : (last >= 0 ? s_base[1] : 0.0);
   const int lo = cs * a.CS, hi = min(a.V, lo + a.CS);
-  int tok = scan_chunk<VEC, CS>(a, b, kind, r, row, lo, hi, M, S, base, thr);
+  int tok = scan_chunk<VEC, CS>(a, b, kind, r, row, lo, hi, M, S, rcs, base, thr);
   if (tok < 0) {                            // rounding put thr at the chunk's end
     if (t == 0) {
       s_tok = -1;
       for (int v = hi - 1; v >= lo; --v)
-        if (draw_weight(a, b, kind, r, row[v], v, M, S) > 0.0) { s_tok = v; break; }
+        if (draw_weight(a, b, kind, r, row[v], v, M, S, rcs) > 0.0) { s_tok = v; break; }
     }
     __syncthreads();
     tok = s_tok;
@@ -918,11 +1041,11 @@ __global__ __launch_bounds__(kThreads) void select_kernel(VerifyArgs a) {
   if (pl.kind == 2) {
     const double sc = (mc == -INFINITY) ? 0.0 : exp((double)mc - (double)m);
     if (a.weights) tok = draw_stored<CS>(a, b, Sc * sc, sc, u);
-    else tok = draw<VEC, CS>(a, b, 2, pl.r, row, Sc * sc, m, 0.0, u);
+    else tok = draw<VEC, CS>(a, b, 2, pl.r, row, Sc * sc, m, 0.0, 1.0, u);
   } else {
     const double Z = block_sum(t < a.C ? Qc : 0.0);
-    if (Z > 0.0) tok = a.weights ? draw_stored<CS>(a, b, Qc, 1.0, u) : draw<VEC, CS>(a, b, 3, pl.r, row, Qc, pl.M, pl.S, u);
-    else tok = draw<VEC, CS>(a, b, 2, pl.r, row, Sc, pl.M, pl.S, u);   // residual of zero mass: T_m
+    if (Z > 0.0) tok = a.weights ? draw_stored<CS>(a, b, Qc, 1.0, u) : draw<VEC, CS>(a, b, 3, pl.r, row, Qc, pl.M, pl.S, pl.cs, u);
+    else tok = draw<VEC, CS>(a, b, 2, pl.r, row, Sc, pl.M, pl.S, 1.0, u);   // residual of zero mass: T_m
   }
   if (t == 0) a.bonus[b] = tok;
 }
@@ -1062,7 +1185,7 @@ __global__ __launch_bounds__(kWave) void select_wave_kernel(VerifyArgs a) {
 struct VerifyLayout {
   int RC, CR, CS, C;
   bool store_w, listed;
-  size_t rowparts, plans, bparts, weights, row_list, row_count, total;
+  size_t rowparts, plans, bparts, weights, row_list, row_count, walk, total;
 };
 
 // The listed row pass pays one more launch, so it is used from this many (sequence, node,
@@ -1113,6 +1236,7 @@ VerifyLayout layout(int B, int N, int V) {
   L.weights = take((size_t)B * c_large * kChunkLarge * sizeof(double));
   L.row_list = take((size_t)B * N * sizeof(int32_t));
   L.row_count = take(sizeof(int32_t));
+  L.walk = take((size_t)3 * B * N * sizeof(double));
   const char* rl = std::getenv("SPECTREE_VERIFY_ROWS_LIST");
   const bool fits = (size_t)B * N <= (size_t)kListMax;
   L.listed = fits && ((rl && *rl) ? std::atoi(rl) != 0 : (size_t)B * N * L.CR >= kListMinItems);
@@ -1141,8 +1265,10 @@ extern "C" spec_status spec_verify(const float* target_logits, const float* draf
   if (B < 1 || N < 1 || N > SPEC_MAX_NODES || V < 1 || max_depth < 0) return SPEC_EINVAL;
   if (!target_logits || !tokens || !parents || !uniforms || !accept_len || !path || !bonus_token || !err)
     return SPEC_EINVAL;
-  if (mode != SPEC_VERIFY_GREEDY && mode != SPEC_VERIFY_TYPICAL && mode != SPEC_VERIFY_REJECT) return SPEC_EINVAL;
-  if (mode == SPEC_VERIFY_REJECT) {
+  if (mode != SPEC_VERIFY_GREEDY && mode != SPEC_VERIFY_TYPICAL && mode != SPEC_VERIFY_REJECT &&
+      mode != SPEC_VERIFY_WALK)
+    return SPEC_EINVAL;
+  if (mode == SPEC_VERIFY_REJECT || mode == SPEC_VERIFY_WALK) {
     if (!draft_probs || !draft_row || R < 1 || Vd < 1) return SPEC_EINVAL;
     if (!t2d && Vd != V) return SPEC_EINVAL;
   }
@@ -1165,6 +1291,9 @@ extern "C" spec_status spec_verify(const float* target_logits, const float* draf
   a.weights = L.store_w ? reinterpret_cast<double*>(w + L.weights) : nullptr;
   a.row_list = reinterpret_cast<int32_t*>(w + L.row_list);
   a.row_count = reinterpret_cast<int32_t*>(w + L.row_count);
+  a.wc = reinterpret_cast<double*>(w + L.walk);
+  a.wf = a.wc + (size_t)B * N;
+  a.wend = a.wf + (size_t)B * N;
 
   const dim3 blk(kThreads);
   const dim3 grid_rows((unsigned)((size_t)L.CR * N * B));
@@ -1193,6 +1322,8 @@ extern "C" spec_status spec_verify(const float* target_logits, const float* draf
     if (vec4) launch(nr, rows_kernel<4, 16>, grid_rows, blk, s, a);
     else launch(nr, rows_kernel<1, 16>, grid_rows, blk, s, a);
   }
+  if (mode == SPEC_VERIFY_WALK)
+    launch("verify_walk_chain", walk_chain_kernel, dim3((unsigned)((size_t)B * N)), blk, s, a);
   // the draw: one wave per sequence when the weights are stored and a wave holds the chunks
   const bool wave_draw = a.weights && L.C <= kWave;
   if (vec4) {
