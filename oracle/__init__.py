@@ -20,7 +20,7 @@ Pins (tests that tie these functions to something other than themselves) live in
 """
 
 from .errors import (ERR_ROOT, ERR_PARENT, ERR_DEPTH, ERR_NNODES, ERR_PREFIX, ERR_TOKEN,
-                     ERR_DRAFTROW, ERR_NONFINITE, ERR_MAP, ERR_RANK, encode_err, decode_err)
+                     ERR_DRAFTROW, ERR_NONFINITE, ERR_MAP, ERR_RANK, ERR_PROB, encode_err, decode_err)
 from .tree import tree_build, pack_mask, unpack_mask
 from .attention import tree_attention, tree_attention_row
 from .verify import (verify, MODE_GREEDY, MODE_TYPICAL, MODE_REJECT, MODE_WALK,
@@ -28,12 +28,13 @@ from .verify import (verify, MODE_GREEDY, MODE_TYPICAL, MODE_REJECT, MODE_WALK,
 from .heads import medusa_heads
 from .assemble import tree_assemble
 from .kv import kv_compact
+from .select import tree_select, path_value
 
 __all__ = [
     "ERR_ROOT", "ERR_PARENT", "ERR_DEPTH", "ERR_NNODES", "ERR_PREFIX", "ERR_TOKEN",
-    "ERR_DRAFTROW", "ERR_NONFINITE", "ERR_MAP", "ERR_RANK", "encode_err", "decode_err",
+    "ERR_DRAFTROW", "ERR_NONFINITE", "ERR_MAP", "ERR_RANK", "ERR_PROB", "encode_err", "decode_err",
     "tree_build", "pack_mask", "unpack_mask", "tree_attention", "tree_attention_row",
     "verify", "MODE_GREEDY", "MODE_TYPICAL", "MODE_REJECT", "MODE_WALK", "sample_inverse_cdf",
     "residual_after_rejections",
-    "medusa_heads", "tree_assemble", "kv_compact",
+    "medusa_heads", "tree_assemble", "kv_compact", "tree_select", "path_value",
 ]

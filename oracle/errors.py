@@ -19,6 +19,7 @@ ERR_DRAFTROW = 7    # draft row index outside [0, R)
 ERR_NONFINITE = 8   # a logits row that is read holds a NaN or an infinity
 ERR_MAP = 9         # target->draft map entry outside [-1, Vd)
 ERR_RANK = 10       # tree assembly: a node's depth or sibling rank exceeds the heads' top-k
+ERR_PROB = 11       # tree selection: a candidate's draft probability is not a number in [0, 1]
 
 
 def encode_err(node, code):
