@@ -147,7 +147,7 @@ class Stepper:
         sb.spec_tree_build(s["parents"], prefix_len=s["P"], n_nodes=s["n_nodes"], out=o["tb"])
         sb.spec_tree_attn(s["q"], s["k"], s["v"], s["P"], o["tb"]["mask"], n_nodes=s["n_nodes"], scale=self.scale,
                           out=o["attn_out"], lse=o["lse"], err=o["attn_err"], ws=self.ws_attn)
-        rej = self.mode == "reject"
+        rej = self.mode in ("reject", "walk")
         sb.spec_verify(s["logits"], tokens, s["parents"], s["uniforms"], self.mode,
                        draft_probs=draft if rej else None, draft_row=draft_row if rej else None,
                        t2d=s.get("t2d") if rej else None, n_nodes=s["n_nodes"], max_depth=w.N - 1,
@@ -175,16 +175,23 @@ def algorithmic(w, a, parents, depths, mode):
     W = (N + 63) // 64
     attn_bytes = int(((P + n) * Hkv * d * 2 * s).sum() + 2 * B * N * Hq * d * s + B * N * W * 8)
     attn_flops = 0
-    internal = 0
+    internal = branching = 0
     for b in range(B):
         nb = int(n[b])
         attn_flops += 4 * Hq * d * int((P[b] + depths[b, :nb] + 1).sum())
-        internal += len(set(int(p) for p in parents[b, 1:nb]))
+        kids = np.bincount(parents[b, 1:nb].clip(min=0), minlength=N)
+        internal += int((kids > 0).sum())
+        branching += int((kids > 1).sum())
     # the bonus pass reads the kept row once more, and a residual draw the draft row beside it
-    kept = B * V * 4 * (2 if mode == "reject" else 1)
+    kept = B * V * 4 * (2 if mode in ("reject", "walk") else 1)
     out = {("tree_attn_bf16" if w.dtype == "bf16" else "tree_attn_f32"): (attn_bytes, attn_flops),
            "verify_rows": (internal * V * 4, 0),
            "verify_decide_bonus": (kept, 0)}
+    if mode == "walk":
+        # the walk's residual chains: each node with two or more children reads its logits row
+        # and its children's draft row once (the passes after the first are served by the caches)
+        Vd = w.Vd or V
+        out["verify_walk_chain"] = (branching * (V + Vd) * 4, 0)
     if w.heads:
         H, Dm = w.heads["H"], w.heads["Dm"]
         out["medusa_resblock"] = (H * Dm * Dm * 2, 2 * B * H * Dm * Dm)
@@ -250,7 +257,8 @@ def cpu_baseline(w, a, vi, hi, ti, mode, budget_s):
     from threadpoolctl import threadpool_limits
     import oracle
     from tree_attention_verification_spec_amd import workloads as wl
-    modes = {"greedy": oracle.MODE_GREEDY, "typical": oracle.MODE_TYPICAL, "reject": oracle.MODE_REJECT}
+    modes = {"greedy": oracle.MODE_GREEDY, "typical": oracle.MODE_TYPICAL, "reject": oracle.MODE_REJECT,
+             "walk": oracle.MODE_WALK}
 
     def one_round(ns):
         par = a["parents"][:1, :ns]
@@ -370,7 +378,7 @@ def main():
     # per-kernel durations: the same K steps launched eagerly with the library's kernel timing
     # on (each launch carries a start/stop event pair stamped by its own dispatch)
     names = ("tree_build", "tree_assemble", "tree_attn_bf16", "tree_attn_merge", "tree_attn_f32", "verify_rows_list", "verify_rows",
-             "verify_decide_bonus", "verify_select", "medusa_resblock", "medusa_lm_head",
+             "verify_walk_chain", "verify_decide_bonus", "verify_select", "medusa_resblock", "medusa_lm_head",
              "medusa_softmax_topk")
     kernels = {}
     try:
