@@ -237,6 +237,35 @@ def kv_compact_timing(st, layers_max=32, cap_bytes=8 << 30, reps=50):
             "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 2) if us > 0 else None}
 
 
+def tree_select_timing(w, C=1024, reps=50):
+    """Dynamic tree selection (a row before the step, measured outside it): per sequence of the
+    workload's batch, a seeded pool of C drafted candidates (depth < 8) is cut to the workload's
+    tree size."""
+    import torch
+    from tree_attention_verification_spec_amd import binding as sb
+    from tree_attention_verification_spec_amd import workloads as wl
+    pool = wl.random_pool(seed=5, B=w.B, C=C)
+    d = {k: torch.from_numpy(v).cuda() for k, v in pool.items()}
+    out = None
+    call = lambda: sb.spec_tree_select(d["cand_parents"], d["cand_prob"], w.N, cand_tokens=d["cand_tokens"],
+                                       cand_row=d["cand_row"], out=out)
+    out = call()
+    torch.cuda.synchronize()
+    assert int(out["err"].abs().sum()) == 0
+    try:
+        sb.prof_reset()
+        sb.prof_enable(True)
+        for _ in range(reps):
+            call()
+        torch.cuda.synchronize()
+        sb.prof_enable(False)
+        ms, cnt = sb.prof_read("tree_select")
+    finally:
+        sb.prof_enable(False)
+        sb.prof_reset()
+    return {"pool": f"B{w.B} x {C} candidates -> {w.N} nodes", "us": round(ms / cnt * 1e3, 3)}
+
+
 def roofline_entry(name, nbytes, flops, avg_ms, traffic):
     intensity = flops / nbytes if nbytes else 0.0
     if name.startswith("tree_attn") and intensity > RIDGE:
@@ -416,6 +445,8 @@ def main():
         kvc = kv_compact_timing(st)
         log(f"kv_compact (after the step, not in it): {kvc['layers']} layers, {kvc['us']:.2f} us, "
             f"{kvc['algorithmic_bytes']} bytes moved")
+    tsel = tree_select_timing(w)
+    log(f"tree_select (before the step, not in it): {tsel['pool']}, {tsel['us']:.2f} us")
 
     if args.copy_calibration_mb:
         nb = args.copy_calibration_mb * (1 << 20)
@@ -451,7 +482,7 @@ def main():
         "roofline": roof,
         "kernels_us": {k: round(v * 1e3, 3) for k, v in kernels.items()},
         "cpu_baseline": cpu,
-        "next_rows": {"kv_compact": kvc},
+        "next_rows": {"kv_compact": kvc, "tree_select": tsel},
     }
     print(json.dumps(line), flush=True)
 

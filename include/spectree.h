@@ -66,10 +66,12 @@ enum {
   SPEC_ERR_DRAFTROW = 7,   /* draft_row outside [0, R)                                    */
   SPEC_ERR_NONFINITE = 8,  /* a target-logits row that is read holds a NaN or an infinity */
   SPEC_ERR_MAP = 9,        /* t2d entry outside [-1, Vd)                                  */
-  SPEC_ERR_RANK = 10       /* assembly: node deeper than the heads, or sibling rank >= k  */
+  SPEC_ERR_RANK = 10,      /* assembly: node deeper than the heads, or sibling rank >= k  */
+  SPEC_ERR_PROB = 11       /* selection: a candidate's draft probability is not in [0, 1] */
 };
 
 #define SPEC_MAX_NODES 256
+#define SPEC_MAX_CANDIDATES 4096
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* spec_strerror(spec_status s);
@@ -224,6 +226,48 @@ spec_status spec_verify(const float* target_logits, const float* draft_probs,
                         float eps, float delta, int32_t* accept_len, int32_t* path,
                         int32_t* bonus_token, uint8_t* node_accept, int32_t* err,
                         void* workspace, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------------------------------
+ * spec_tree_select - dynamic tree: keep the best N-node subtree of a drafted candidate tree.
+ *
+ * [MTP] section "ツリー検証：候補を「木」に束ねて1回で確かめる": a larger tree raises the
+ * expected accepted length but costs verification work; EAGLE-2's dynamic tree shapes the tree
+ * by the context's confidence.  [GLOSSARY] section "EAGLE: Medusaの発展形" and [GUIDE] section
+ * "EAGLE-1/2からの進化" name the same context-aware tree.  The rule taken: a candidate's value
+ * is the product of the draft probabilities on its path from the root (the root counts 1;
+ * float64 products of the float32 inputs, multiplied root first); the root and the N - 1 other
+ * candidates of largest value are kept, ties to the lower candidate index.  With every
+ * probability in [0, 1] the kept set contains each member's parent.  Kept candidates are
+ * written in candidate order (so the output is numbered topologically) with renumbered parents.
+ *
+ *   cand_parents int32 [B, C]  candidate tree: candidate 0 the root (parent -1), parents[i] in
+ *                              [0, i) for i >= 1
+ *   cand_prob    float [B, C]  draft probability of each candidate's token (root entry unused)
+ *   n_cand       int32 [B]     optional (NULL = C): valid candidates per sequence
+ *   cand_tokens  int32 [B, C]  optional (NULL): carried to `tokens`
+ *   cand_row     int32 [B, C]  optional (NULL): carried to `draft_row` unchanged (the draft rows
+ *                              stay those of the candidate pool)
+ * Outputs (every entry written; entries j >= n_nodes[b] are -1):
+ *   sel          int32 [B, N]  candidate index of output node j
+ *   parents      int32 [B, N]  parent of output node j among the output nodes (-1: root)
+ *   tokens       int32 [B, N]  given iff cand_tokens is given
+ *   draft_row    int32 [B, N]  given iff cand_row is given
+ *   n_nodes      int32 [B]     min(n_cand[b], N), 0 on error
+ *   err          int32 [B]     error word: SPEC_ERR_NNODES (n_cand outside [0, C], at node 0),
+ *                              SPEC_ERR_ROOT, SPEC_ERR_PARENT, SPEC_ERR_PROB (a non-root
+ *                              probability that is NaN or outside [0, 1]); a sequence with an
+ *                              error keeps nothing
+ * The outputs feed spec_tree_build (parents, n_nodes) and spec_verify (tokens, draft_row).
+ * All pointers are device memory; no workspace.
+ * Supported: 1 <= C <= 4096, 1 <= N <= 256.
+ * Errors: SPEC_EINVAL (sizes, NULL required pointer, exactly one of cand_tokens / tokens or of
+ * cand_row / draft_row NULL).
+ * ------------------------------------------------------------------------------------ */
+spec_status spec_tree_select(const int32_t* cand_parents, const float* cand_prob,
+                             const int32_t* n_cand, const int32_t* cand_tokens,
+                             const int32_t* cand_row, int B, int C, int N, int32_t* sel,
+                             int32_t* parents, int32_t* tokens, int32_t* draft_row,
+                             int32_t* n_nodes, int32_t* err, void* stream);
 
 /* --------------------------------------------------------------------------------------
  * spec_kv_compact - KV-cache compaction that closes a verification round.

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("spec_tree_build", "spec_tree_assemble", "spec_tree_attn", "spec_tree_attn_workspace",
               "spec_verify", "spec_verify_workspace", "spec_medusa_heads", "spec_medusa_heads_workspace",
-              "spec_kv_compact", "spec_strerror", "spec_prof_enable", "spec_prof_reset",
+              "spec_kv_compact", "spec_tree_select", "spec_strerror", "spec_prof_enable", "spec_prof_reset",
               "spec_prof_read"):
         assert n in names, n
 
@@ -107,3 +107,19 @@ def test_workspace_sizes_are_monotone(lib):
     assert 0 < small < big
     assert lib.spec_medusa_heads_workspace(8, 4, 4096, 32000, 8) > 8 * 4 * 32000 * 4
     assert lib.spec_tree_attn_workspace(1, 10, 4, 1, 64, 266, 0) == 0   # fp32 path needs none
+
+
+def test_tree_select_argument_checks(lib):
+    fake = ctypes.c_void_p(0x1000)     # never dereferenced: every call below returns before a launch
+
+    def call(par=fake, prob=fake, tok_in=None, row_in=None, B=2, C=100, N=63, sel=fake, parents=fake,
+             tok=None, row=None, nn=fake, err=fake):
+        return lib.spec_tree_select(par, prob, None, tok_in, row_in, B, C, N, sel, parents, tok, row, nn, err,
+                                    None)
+
+    assert call(par=None) == 1 and call(prob=None) == 1 and call(sel=None) == 1
+    assert call(parents=None) == 1 and call(nn=None) == 1 and call(err=None) == 1
+    assert call(B=0) == 1 and call(C=0) == 1 and call(C=4097) == 1
+    assert call(N=0) == 1 and call(N=257) == 1
+    assert call(tok_in=fake) == 1 and call(tok=fake) == 1          # tokens in without out, and back
+    assert call(row_in=fake) == 1 and call(row=fake) == 1

@@ -44,6 +44,8 @@ def lib():
     L.spec_tree_build.argtypes = [_P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P]
     L.spec_tree_assemble.restype = _I
     L.spec_tree_assemble.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P]
+    L.spec_tree_select.restype = _I
+    L.spec_tree_select.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]
     L.spec_tree_attn_workspace.restype = _Z
     L.spec_tree_attn_workspace.argtypes = [_I, _I, _I, _I, _I, _I, _I]
     L.spec_tree_attn.restype = _I
@@ -137,6 +139,29 @@ def spec_tree_assemble(topk_idx, parents, root_tokens=None, out=None, stream=Non
         _ptr(out["tokens"], torch.int32, (B, N), "tokens"),
         _ptr(out["draft_row"], torch.int32, (B, N), "draft_row"),
         _ptr(out["err"], torch.int32, (B,), "err"), _stream(stream)), "spec_tree_assemble")
+    return out
+
+
+def spec_tree_select(cand_parents, cand_prob, N, n_cand=None, cand_tokens=None, cand_row=None, out=None,
+                     stream=None):
+    B, C = cand_parents.shape
+    dev = cand_parents.device
+    if out is None:
+        out = {"sel": torch.empty((B, N), dtype=torch.int32, device=dev),
+               "parents": torch.empty((B, N), dtype=torch.int32, device=dev),
+               "tokens": torch.empty((B, N), dtype=torch.int32, device=dev) if cand_tokens is not None else None,
+               "draft_row": torch.empty((B, N), dtype=torch.int32, device=dev) if cand_row is not None else None,
+               "n_nodes": torch.empty((B,), dtype=torch.int32, device=dev),
+               "err": torch.empty((B,), dtype=torch.int32, device=dev)}
+    _check(lib().spec_tree_select(
+        _ptr(cand_parents, torch.int32, (B, C), "cand_parents"), _ptr(cand_prob, torch.float32, (B, C), "cand_prob"),
+        _ptr(n_cand, torch.int32, (B,), "n_cand"), _ptr(cand_tokens, torch.int32, (B, C), "cand_tokens"),
+        _ptr(cand_row, torch.int32, (B, C), "cand_row"), B, C, int(N),
+        _ptr(out["sel"], torch.int32, (B, N), "sel"), _ptr(out["parents"], torch.int32, (B, N), "parents"),
+        _ptr(out.get("tokens"), torch.int32, (B, N), "tokens"),
+        _ptr(out.get("draft_row"), torch.int32, (B, N), "draft_row"),
+        _ptr(out["n_nodes"], torch.int32, (B,), "n_nodes"), _ptr(out["err"], torch.int32, (B,), "err"),
+        _stream(stream)), "spec_tree_select")
     return out
 
 

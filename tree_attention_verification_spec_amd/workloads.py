@@ -287,3 +287,46 @@ def heads_target_inputs(w):
     """Target logits and uniforms for a Medusa-head workload (drafts come from the heads)."""
     logits = np.stack([target_logits(w, b) for b in range(w.B)])
     return {"target_logits": logits, "uniforms": uniforms(w)}
+
+
+# ----------------------------------------------------------------------------- tree selection
+
+def select_inputs(w, vi=None, parents=None):
+    """A candidate pool from a workload's tree: parents, tokens and draft rows as drafted, and
+    each candidate's draft probability looked up in its draft row (through the target->draft
+    map when the drafter has its own vocabulary).  The root's entry is 1."""
+    if parents is None:
+        parents, _ = trees(w)
+    if vi is None:
+        vi = verify_inputs(w, parents)
+    B, N = w.B, w.N
+    prob = np.ones((B, N), dtype=np.float32)
+    for b in range(B):
+        for c in range(1, N):
+            tok = int(vi["tokens"][b, c])
+            x = tok if vi["t2d"] is None else int(vi["t2d"][tok])
+            prob[b, c] = vi["draft_probs"][b, vi["draft_row"][b, c], x]
+    return {"cand_parents": np.asarray(parents, dtype=np.int32), "cand_prob": prob,
+            "cand_tokens": vi["tokens"], "cand_row": vi["draft_row"]}
+
+
+def random_pool(seed, B, C, max_depth=8, power=2.0):
+    """Seeded random candidate pools: candidate i attaches to a uniform earlier candidate of depth
+    < max_depth; probabilities U(0,1)^power as float32 (skewed towards small values, as the
+    draft probabilities of lower-ranked candidates are); tokens and rows are distinct tags."""
+    par = np.full((B, C), -1, dtype=np.int32)
+    prob = np.ones((B, C), dtype=np.float32)
+    for b in range(B):
+        g = rng(seed, S_TREE, b)
+        depth = np.zeros(C, dtype=np.int64)
+        ok = [0]
+        for i in range(1, C):
+            p = ok[int(g.integers(0, len(ok)))]
+            par[b, i] = p
+            depth[i] = depth[p] + 1
+            if depth[i] < max_depth:
+                ok.append(i)
+        prob[b, 1:] = (g.random(C - 1) ** power).astype(np.float32)
+    tokens = (np.arange(C, dtype=np.int32)[None, :] * 7 + 1000 * np.arange(B, dtype=np.int32)[:, None])
+    rows = np.maximum(par, 0).astype(np.int32)
+    return {"cand_parents": par, "cand_prob": prob, "cand_tokens": tokens.astype(np.int32), "cand_row": rows}
