@@ -671,14 +671,127 @@ __device__ __forceinline__ double draft_at(const VerifyArgs& a, int b, int r, in
 // f(c) = sum_x relu(T_p[x] - c D[x]), c_0 = 0, f(c_0) = 1 and c_(j+1) = c_j + f(c_j).  None of
 // this depends on which children pass, so the chain of every node is computed ahead of the
 // decision, all nodes at once: the workgroup of node p writes (c_(j-1), f(c_(j-1))) for its
-// j-th child and c_k (k children) for a residual bonus draw at p.  Each f is one pass over the
-// row: fp32 exp(x - M) as in the row pass, scaled by 1/S and reduced against c D in fp64.
-// Grid (seq, node); nodes with fewer than two children need no pass.
-constexpr int kChainUnroll = 8;
+// j-th child and c_k (k children) for a residual bonus draw at p.
+//
+// Each f is a pass over the row with T = fp32 exp(x - M) / S (as in the row pass) reduced against
+// c D in fp64; the passes are sequential, so one 1024-thread workgroup per node streams the row
+// with 32 elements per thread in flight.  Tokens with D = 0 add T at every c (their sum is kept
+// apart), and a token with D > 0 that adds nothing at c adds nothing at any larger c, since
+// exp(x - M) / S - c D only falls as c grows.  So each streaming pass also collects, in LDS, the
+// tokens with D != 0 that still add something; once they fit (the chain's c grows by f each step
+// and the set shrinks fast), every later pass reads only that list.  Grid (seq, node); nodes with
+// fewer than two children need no pass.
+constexpr int kChainThreads = 512;
+constexpr int kChainWaves = kChainThreads / kWave;
+constexpr int kChainPer = 24;                 // elements per thread per streaming step
+constexpr int kChainCap = 16384;              // LDS list: (exp(x - M), D) pairs, 128 KB
 
-__global__ __launch_bounds__(kThreads) void walk_chain_kernel(VerifyArgs a) {
+__device__ __forceinline__ double chain_sum(double v, double* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x >> 6;
+  if (lane == 0) red[wv] = v;
+  __syncthreads();
+  double r = 0.0;
+#pragma unroll
+  for (int q = 0; q < kChainWaves; ++q) r += red[q];
+  __syncthreads();
+  return r;
+}
+
+// One streaming pass of a chain at c: fp = sum over tokens with D != 0 of relu(T - c D), z = sum
+// of T over tokens with D = 0, cnt = this thread's tokens with D != 0 and T - c D > 0; with BUILD
+// they are also appended to the LDS list as (exp(x - M), D) (one LDS atomic per wave and step).
+template <int VEC, bool BUILD>
+__device__ __forceinline__ void chain_stream(const VerifyArgs& a, const float* row, const float* drow,
+                                             bool dvec, float M, double invS, double cj, double& fp,
+                                             double& z, int& cnt, float2* list, int* list_n) {
+  const int t = threadIdx.x, lane = t & (kWave - 1);
+  for (int v0 = 0; v0 < a.V; v0 += kChainThreads * kChainPer) {
+    float x[kChainPer], d[kChainPer];
+#pragma unroll
+    for (int u = 0; u < kChainPer / VEC; ++u) {
+      const int vb = v0 + (u * kChainThreads + t) * VEC;
+      const int at = vb < a.V ? vb : 0;
+      if (VEC == 4) {
+        const float4 x4 = *reinterpret_cast<const float4*>(row + at);
+        x[u * VEC] = x4.x;
+        x[u * VEC + (VEC > 1 ? 1 : 0)] = x4.y;
+        x[u * VEC + (VEC > 2 ? 2 : 0)] = x4.z;
+        x[u * VEC + (VEC > 3 ? 3 : 0)] = x4.w;
+      } else {
+        x[u] = row[at];
+      }
+    }
+    if (a.t2d) {
+#pragma unroll
+      for (int u = 0; u < kChainPer; ++u) {
+        const int v = v0 + ((u / VEC) * kChainThreads + t) * VEC + u % VEC;
+        const int dx = a.t2d[v < a.V ? v : 0];
+        const bool mapped = dx >= 0 && dx < a.Vd;
+        const float dv = drow[mapped ? dx : 0];
+        d[u] = mapped ? dv : 0.f;
+      }
+    } else if (dvec) {
+#pragma unroll
+      for (int u = 0; u < kChainPer / VEC; ++u) {
+        const int vb = v0 + (u * kChainThreads + t) * VEC;
+        const float4 d4 = *reinterpret_cast<const float4*>(drow + (vb < a.V ? vb : 0));
+        d[u * VEC] = d4.x;
+        d[u * VEC + (VEC > 1 ? 1 : 0)] = d4.y;
+        d[u * VEC + (VEC > 2 ? 2 : 0)] = d4.z;
+        d[u * VEC + (VEC > 3 ? 3 : 0)] = d4.w;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kChainPer; ++u) {
+        const int v = v0 + ((u / VEC) * kChainThreads + t) * VEC + u % VEC;
+        d[u] = drow[v < a.V ? v : 0];
+      }
+    }
+    int mine = 0;
+#pragma unroll
+    for (int u = 0; u < kChainPer; ++u) x[u] = __expf(x[u] - M);    // x now holds exp(x - M)
+#pragma unroll
+    for (int u = 0; u < kChainPer; ++u) {
+      const int v = v0 + ((u / VEC) * kChainThreads + t) * VEC + u % VEC;
+      const bool in = v < a.V;
+      const double tv = (double)x[u] * invS;
+      const double q = tv - cj * (double)d[u];
+      z += (in && d[u] == 0.f) ? tv : 0.0;
+      const bool keep = in && d[u] != 0.f && q > 0.0;
+      fp += keep ? q : 0.0;
+      mine += keep ? 1 : 0;
+      d[u] = keep ? d[u] : 0.f;            // 0 marks a token that is not appended
+    }
+    cnt += mine;
+    if (BUILD) {
+      int incl = mine;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      int at = 0;
+      if (lane == kWave - 1 && incl) at = atomicAdd(list_n, incl);
+      int pos = __shfl(at, kWave - 1) + incl - mine;
+#pragma unroll
+      for (int u = 0; u < kChainPer; ++u) {
+        if (d[u] != 0.f) {
+          if (pos < kChainCap) list[pos] = make_float2(x[u], d[u]);
+          ++pos;
+        }
+      }
+    }
+  }
+}
+
+template <int VEC>
+__global__ __launch_bounds__(kChainThreads) void walk_chain_kernel(VerifyArgs a) {
+  __shared__ float2 s_list[kChainCap];
   __shared__ int s_kids[SPEC_MAX_NODES];
-  __shared__ int s_wcnt[kWavesPB];
+  __shared__ int s_wcnt[kChainWaves];
+  __shared__ double s_red[kChainWaves];
+  __shared__ int s_n;
   __shared__ float s_M;
   __shared__ double s_invS;
   const int b = blockIdx.x / a.N, p = blockIdx.x - b * a.N;
@@ -686,7 +799,7 @@ __global__ __launch_bounds__(kThreads) void walk_chain_kernel(VerifyArgs a) {
   const int n = a.n_nodes ? a.n_nodes[b] : a.N;
   if (n < 1 || n > a.N || p >= n) return;
   const size_t base = (size_t)b * a.N;
-  // the children of p in index order (N <= kThreads: one candidate node per thread)
+  // the children of p in index order (one candidate node per thread)
   const int i = p + 1 + t;
   const bool kid = i < n && a.parents[base + i] == p;
   const unsigned long long bal = __ballot(kid);
@@ -694,7 +807,7 @@ __global__ __launch_bounds__(kThreads) void walk_chain_kernel(VerifyArgs a) {
   __syncthreads();
   int off = 0, k = 0;
 #pragma unroll
-  for (int q = 0; q < kWavesPB; ++q) {
+  for (int q = 0; q < kChainWaves; ++q) {
     off += q < wv ? s_wcnt[q] : 0;
     k += s_wcnt[q];
   }
@@ -722,26 +835,37 @@ __global__ __launch_bounds__(kThreads) void walk_chain_kernel(VerifyArgs a) {
   const double invS = s_invS;
   const int r = min(max(a.draft_row[base + s_kids[0]], 0), a.R - 1);
   const float* row = a.logits + (base + p) * a.V;
-  double cj = 1.0;
+  const float* drow = a.draft + ((size_t)b * a.R + r) * a.Vd;
+  // 16-byte draft loads when the draft row is the target vocabulary and aligned like the logits
+  const bool dvec = VEC == 4 && !a.t2d && (reinterpret_cast<uintptr_t>(drow) & 15) == 0;
+  double cj = 1.0, zero_part = 0.0;
+  int listed = -1;        // entries of s_list once it holds every token that can still add
+  int prev = INT_MAX;     // tokens with D != 0 that added something in the previous pass
   for (int j = 1; j < k; ++j) {
-    double f = 0.0;
-    for (int v0 = 0; v0 < a.V; v0 += kThreads * kChainUnroll) {
-      float x[kChainUnroll];
-      double d[kChainUnroll];
-#pragma unroll
-      for (int u = 0; u < kChainUnroll; ++u) {
-        const int v = v0 + u * kThreads + t;
-        const int at = v < a.V ? v : 0;
-        x[u] = row[at];
-        d[u] = draft_at(a, b, r, at);
+    double f;
+    if (listed < 0) {
+      // the contributors at c_j are a subset of those at c_(j-1): collect them only when their
+      // previous count shows that they fit
+      const bool build = prev <= kChainCap;
+      if (t == 0) s_n = 0;
+      __syncthreads();
+      double fp = 0.0, z = 0.0;
+      int cnt = 0;
+      if (build) chain_stream<VEC, true>(a, row, drow, dvec, M, invS, cj, fp, z, cnt, s_list, &s_n);
+      else chain_stream<VEC, false>(a, row, drow, dvec, M, invS, cj, fp, z, cnt, s_list, &s_n);
+      zero_part = chain_sum(z, s_red);
+      f = zero_part + chain_sum(fp, s_red);
+      prev = (int)chain_sum((double)cnt, s_red);
+      if (build) listed = prev;
+    } else {
+      double fp = 0.0;
+      for (int e = t; e < listed; e += kChainThreads) {
+        const float2 ed = s_list[e];
+        const double q = (double)ed.x * invS - cj * (double)ed.y;
+        fp += q > 0.0 ? q : 0.0;
       }
-#pragma unroll
-      for (int u = 0; u < kChainUnroll; ++u) {
-        const double q = (double)__expf(x[u] - M) * invS - cj * d[u];
-        f += (v0 + u * kThreads + t < a.V && q > 0.0) ? q : 0.0;
-      }
+      f = zero_part + chain_sum(fp, s_red);
     }
-    f = block_sum(f);
     if (t == 0) {
       a.wc[base + s_kids[j]] = cj;
       a.wf[base + s_kids[j]] = f;
@@ -1322,8 +1446,11 @@ extern "C" spec_status spec_verify(const float* target_logits, const float* draf
     if (vec4) launch(nr, rows_kernel<4, 16>, grid_rows, blk, s, a);
     else launch(nr, rows_kernel<1, 16>, grid_rows, blk, s, a);
   }
-  if (mode == SPEC_VERIFY_WALK)
-    launch("verify_walk_chain", walk_chain_kernel, dim3((unsigned)((size_t)B * N)), blk, s, a);
+  if (mode == SPEC_VERIFY_WALK) {
+    const dim3 gw((unsigned)((size_t)B * N)), bw(kChainThreads);
+    if (vec4) launch("verify_walk_chain", walk_chain_kernel<4>, gw, bw, s, a);
+    else launch("verify_walk_chain", walk_chain_kernel<1>, gw, bw, s, a);
+  }
   // the draw: one wave per sequence when the weights are stored and a wave holds the chunks
   const bool wave_draw = a.weights && L.C <= kWave;
   if (vec4) {
