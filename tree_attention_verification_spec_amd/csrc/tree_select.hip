@@ -17,7 +17,9 @@
 //   2. values level by level: a candidate whose parent's value is known takes parent * p; one
 //      round per tree level, two barriers per round (reads, then writes);
 //   3. a bitonic sort of (value desc, index asc) over the candidates padded to a power of two
-//      (the root gets key 2, above every value; padding -1, below every value);
+//      (the root gets key 2, above every value; padding -1, below every value), held in
+//      registers: wave shuffles for strides below 64, LDS for strides 64-512, and in-thread
+//      swaps for larger ones, so only 10-18 stages of the sort need a barrier;
 //   4. the first N sorted entries are flagged, a block scan over the flags in candidate order
 //      numbers the kept candidates, and threads j < N write output node j.
 // Pools that already fit (n_cand <= N) keep everything and skip steps 2-3.
@@ -37,14 +39,41 @@ __device__ __forceinline__ bool precedes(double ka, int ia, double kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
+// One compare-exchange of a bitonic stage seen from one position: (k, i) is this position's
+// entry and (ok, oi) its partner's; `lo` says this is the lower position of the pair, `up` that
+// the pair's block is sorted in precedence order.  The lower position of an up block (and the
+// upper of a down block) takes the entry that comes first.
+__device__ __forceinline__ void bitonic_pick(double& k, int& i, double ok, int oi, bool lo, bool up) {
+  const bool mine_first = precedes(k, i, ok, oi);
+  if ((lo == up) != mine_first) {
+    k = ok;
+    i = oi;
+  }
+}
+
+// Both positions of the pair in one thread (strides of 1024 and more): a at the lower one.
+__device__ __forceinline__ void bitonic_in_thread(double& ka, int& ia, double& kb, int& ib, bool up) {
+  const bool a_first = precedes(ka, ia, kb, ib);
+  if (a_first != up) {
+    const double tk = ka;
+    const int ti = ia;
+    ka = kb;
+    ia = ib;
+    kb = tk;
+    ib = ti;
+  }
+}
+
 __global__ __launch_bounds__(kSelThreads) void tree_select_kernel(
     const int32_t* __restrict__ cand_parents, const float* __restrict__ cand_prob,
     const int32_t* __restrict__ n_cand, const int32_t* __restrict__ cand_tokens,
     const int32_t* __restrict__ cand_row, int C, int N, int32_t* __restrict__ sel,
     int32_t* __restrict__ parents, int32_t* __restrict__ tokens, int32_t* __restrict__ draft_row,
     int32_t* __restrict__ n_nodes, int32_t* __restrict__ err) {
-  __shared__ double s_key[SPEC_MAX_CANDIDATES];   // values, then sort keys
-  __shared__ short s_idx[SPEC_MAX_CANDIDATES];    // sort payload, then new index (-1: dropped)
+  __shared__ double s_key[SPEC_MAX_CANDIDATES];   // values, then sort exchange buffer 0
+  __shared__ double s_key2[SPEC_MAX_CANDIDATES];  // sort exchange buffer 1
+  __shared__ short s_idx[SPEC_MAX_CANDIDATES];    // sort exchange, then new index (-1: dropped)
+  __shared__ short s_idx2[SPEC_MAX_CANDIDATES];
   __shared__ short s_par[SPEC_MAX_CANDIDATES];
   __shared__ unsigned char s_keep[SPEC_MAX_CANDIDATES];
   __shared__ int s_sel[SPEC_MAX_NODES];
@@ -137,40 +166,66 @@ __global__ __launch_bounds__(kSelThreads) void tree_select_kernel(
       if (!more) break;
     }
 
-    // ---- 3. bitonic sort over E = 2^ceil(log2 n) entries: the root first, then value desc,
-    // index asc; padding (-1) last
+    // ---- 3. bitonic sort over E = 2^ceil(log2 n) positions: the root first, then value desc,
+    // index asc; padding (-1) last.  Position r * 1024 + t lives in register slot r of thread t:
+    // strides below 64 exchange by wave shuffles, strides of 1024 and more stay inside a thread,
+    // the others go through LDS (two buffers in turn: one barrier per stage).
     int E = 1;
     while (E < n) E <<= 1;
+    const int R = E > kSelThreads ? E / kSelThreads : 1;
+    double key[kSelPer];
+    int idx[kSelPer];
 #pragma unroll
-    for (int k = 0; k < kSelPer; ++k) {
-      const int i = t + k * kSelThreads;
-      if (i < E) {
-        if (i == 0) s_key[0] = 2.0;
-        else if (i >= n) s_key[i] = -1.0;
-        s_idx[i] = (short)i;
-      }
+    for (int r = 0; r < kSelPer; ++r) {
+      const int q = r * kSelThreads + t;
+      key[r] = q == 0 ? 2.0 : (q < n ? s_key[q] : -1.0);
+      idx[r] = q;
     }
-    __syncthreads();
+    int buf = 0;
     for (int size = 2; size <= E; size <<= 1) {
       for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int q = t; q < (E >> 1); q += kSelThreads) {
-          const int lo = 2 * q - (q & (stride - 1));
-          const int hi = lo + stride;
-          const double ka = s_key[lo], kb = s_key[hi];
-          const int ia = s_idx[lo], ib = s_idx[hi];
-          const bool up = (lo & size) == 0;
-          const bool swap = up ? precedes(kb, ib, ka, ia) : precedes(ka, ia, kb, ib);
-          if (swap) {
-            s_key[lo] = kb;
-            s_key[hi] = ka;
-            s_idx[lo] = (short)ib;
-            s_idx[hi] = (short)ia;
+        if (stride >= kSelThreads) {
+          if (stride == kSelThreads) {
+            bitonic_in_thread(key[0], idx[0], key[1], idx[1], (0 * kSelThreads & size) == 0);
+            if (R == 4) bitonic_in_thread(key[2], idx[2], key[3], idx[3], (2 * kSelThreads & size) == 0);
+          } else {
+            bitonic_in_thread(key[0], idx[0], key[2], idx[2], (0 * kSelThreads & size) == 0);
+            bitonic_in_thread(key[1], idx[1], key[3], idx[3], (1 * kSelThreads & size) == 0);
+          }
+        } else if (stride >= kWave) {
+          double* kb = buf ? s_key2 : s_key;
+          short* ib = buf ? s_idx2 : s_idx;
+#pragma unroll
+          for (int r = 0; r < kSelPer; ++r) {
+            if (r < R) {
+              kb[r * kSelThreads + t] = key[r];
+              ib[r * kSelThreads + t] = (short)idx[r];
+            }
+          }
+          __syncthreads();
+#pragma unroll
+          for (int r = 0; r < kSelPer; ++r) {
+            if (r < R) {
+              const int q = r * kSelThreads + t;
+              bitonic_pick(key[r], idx[r], kb[q ^ stride], ib[q ^ stride], (q & stride) == 0,
+                           (q & size) == 0);
+            }
+          }
+          buf ^= 1;
+        } else {
+#pragma unroll
+          for (int r = 0; r < kSelPer; ++r) {
+            if (r < R) {
+              const int q = r * kSelThreads + t;
+              const double ok = __shfl_xor(key[r], stride);
+              const int oi = __shfl_xor(idx[r], stride);
+              bitonic_pick(key[r], idx[r], ok, oi, (q & stride) == 0, (q & size) == 0);
+            }
           }
         }
-        __syncthreads();
       }
     }
-    for (int r = t; r < N; r += kSelThreads) s_keep[s_idx[r]] = 1;
+    if (t < N) s_keep[idx[0]] = 1;           // positions 0 .. N-1 (N <= 256 < 1024: slot 0)
   }
   __syncthreads();
 
