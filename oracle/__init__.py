@@ -29,6 +29,7 @@ from .heads import medusa_heads
 from .assemble import tree_assemble
 from .kv import kv_compact
 from .select import tree_select, path_value
+from .lm_head import lm_head_stats, row_statistics
 
 __all__ = [
     "ERR_ROOT", "ERR_PARENT", "ERR_DEPTH", "ERR_NNODES", "ERR_PREFIX", "ERR_TOKEN",
@@ -36,5 +37,5 @@ __all__ = [
     "tree_build", "pack_mask", "unpack_mask", "tree_attention", "tree_attention_row",
     "verify", "MODE_GREEDY", "MODE_TYPICAL", "MODE_REJECT", "MODE_WALK", "sample_inverse_cdf",
     "residual_after_rejections",
-    "medusa_heads", "tree_assemble", "kv_compact", "tree_select", "path_value",
+    "medusa_heads", "tree_assemble", "kv_compact", "tree_select", "path_value", "lm_head_stats", "row_statistics",
 ]
