@@ -266,6 +266,48 @@ def tree_select_timing(w, C=1024, reps=50):
     return {"pool": f"B{w.B} x {C} candidates -> {w.N} nodes", "us": round(ms / cnt * 1e3, 3)}
 
 
+def lm_head_stats_timing(w, reps=20, Dm=4096):
+    """The target LM head fused with the row statistics (a row beside the step, measured outside
+    it) at the workload's batch and tree size when B * N <= 64: hidden 4096, the workload's
+    vocabulary.  Seeded random device inputs (their values do not change the time)."""
+    import numpy as np
+    import torch
+    from tree_attention_verification_spec_amd import binding as sb
+    from tree_attention_verification_spec_amd import workloads as wl
+    B, N, V = w.B, w.N, w.V
+    if B * N > 64 or w.dtype != "bf16":
+        return None
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    h = torch.randn((B, N, Dm), generator=g, device="cuda").to(torch.bfloat16)
+    W = (torch.randn((V, Dm), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    par = torch.from_numpy(np.stack(wl.trees(w)[0])).to(torch.int32).cuda()
+    tok = torch.randint(0, V, (B, N), generator=g, device="cuda", dtype=torch.int32)
+    out = sb.spec_lm_head_stats(h, W, par, tok)
+    torch.cuda.synchronize()
+    assert int(out["err"].abs().sum()) == 0
+    try:
+        sb.prof_reset()
+        sb.prof_enable(True)
+        for _ in range(reps):
+            sb.spec_lm_head_stats(h, W, par, tok, out=out)
+        torch.cuda.synchronize()
+        sb.prof_enable(False)
+        ms, cnt = sb.prof_read("lm_head_stats")
+        ms2, cnt2 = sb.prof_read("lm_head_merge")
+    finally:
+        sb.prof_enable(False)
+        sb.prof_reset()
+    us, us_merge = ms / cnt * 1e3, ms2 / cnt2 * 1e3
+    nbytes = V * Dm * 2 + B * N * Dm * 2
+    flops = 2 * B * N * Dm * V
+    del W
+    return {"shape": f"[{B * N} x {Dm}] x [{Dm} x {V}]", "us": round(us, 3), "merge_us": round(us_merge, 3),
+            "algorithmic_bytes": nbytes, "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (us * 1e-6) / 8e12, 4),
+            "achieved_TFLOPs": round(flops / (us * 1e-6) / 1e12, 1)}
+
+
 def roofline_entry(name, nbytes, flops, avg_ms, traffic):
     intensity = flops / nbytes if nbytes else 0.0
     if name.startswith("tree_attn") and intensity > RIDGE:
@@ -447,6 +489,10 @@ def main():
             f"{kvc['algorithmic_bytes']} bytes moved")
     tsel = tree_select_timing(w)
     log(f"tree_select (before the step, not in it): {tsel['pool']}, {tsel['us']:.2f} us")
+    lmh = lm_head_stats_timing(w)
+    if lmh:
+        log(f"lm_head_stats (beside the step, not in it): {lmh['shape']}, {lmh['us']:.2f} us + merge "
+            f"{lmh['merge_us']:.2f} us, {lmh['achieved_GBs']:.0f} GB/s")
 
     if args.copy_calibration_mb:
         nb = args.copy_calibration_mb * (1 << 20)
@@ -482,7 +528,7 @@ def main():
         "roofline": roof,
         "kernels_us": {k: round(v * 1e3, 3) for k, v in kernels.items()},
         "cpu_baseline": cpu,
-        "next_rows": {"kv_compact": kvc, "tree_select": tsel},
+        "next_rows": {"kv_compact": kvc, "tree_select": tsel, "lm_head_stats": lmh},
     }
     print(json.dumps(line), flush=True)
 

@@ -270,6 +270,40 @@ spec_status spec_tree_select(const int32_t* cand_parents, const float* cand_prob
                              int32_t* n_nodes, int32_t* err, void* stream);
 
 /* --------------------------------------------------------------------------------------
+ * spec_lm_head_stats - the target's LM head fused with the row statistics verification reads.
+ *
+ * [GUIDE] section "並列検証：ターゲットモデルの1回のforward passで一括確認する": one target pass
+ * gives every tree node's distribution T_p = softmax(W h_p); [GUIDE] section
+ * "ドラフトヘッドの構成と学習手順" gives the shapes (hidden 4096, vocabulary 128256).  Only a few
+ * numbers of each row are read by verification, so the logits are reduced as they are produced
+ * and never written:
+ *   l_p[v]      = sum_k W[v, k] h_p[k]      (bf16 inputs, fp32 accumulation)
+ *   row_max     = max_v l_p[v],  row_argmax = the lowest v holding it
+ *   row_sum     = sum_v exp(l_p[v] - row_max)                     (T_p[x] = exp(l_p[x] - max) / S)
+ *   row_ent     = sum_v exp(l_p[v] - row_max) (l_p[v] - row_max)  (entropy = ln S - row_ent / S)
+ *   cand_logit  = l_parent(c)[tokens[c]] for every non-root node c (NaN for the root)
+ *
+ *   hidden   bf16 [B, N, Dm]  the target's last hidden state at each tree node (16-byte aligned)
+ *   W        bf16 [V, Dm]     the target's LM head ([out, in]; 16-byte aligned)
+ *   parents  int32 [B, N], tokens int32 [B, N] (node c's candidate token), n_nodes int32 [B]
+ *            (optional, NULL = N): the same tree rules as spec_tree_build
+ * Outputs: row_max float [B, N], row_argmax int32 [B, N], row_sum, row_ent double [B, N],
+ *   cand_logit float [B, N], err int32 [B]: SPEC_ERR_NNODES, SPEC_ERR_ROOT, SPEC_ERR_PARENT,
+ *   SPEC_ERR_TOKEN (a non-root token outside [0, V)).  Rows past n_nodes and every row of a
+ *   sequence with an error get NaN (argmax -1).
+ * The workspace (spec_lm_head_stats_workspace bytes) holds one partial per (row, 64 tokens).
+ * Supported: B * N <= 64, Dm a multiple of 128.
+ * Errors: SPEC_EINVAL (sizes, NULL pointers), SPEC_EUNSUPPORTED (B * N, Dm, alignment),
+ * SPEC_EWORKSPACE.
+ * ------------------------------------------------------------------------------------ */
+size_t spec_lm_head_stats_workspace(int B, int N, int V);
+spec_status spec_lm_head_stats(const void* hidden, const void* W, const int32_t* parents,
+                               const int32_t* tokens, const int32_t* n_nodes, int B, int N, int Dm,
+                               int V, float* row_max, int32_t* row_argmax, double* row_sum,
+                               double* row_ent, float* cand_logit, int32_t* err, void* workspace,
+                               size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------------------------------
  * spec_kv_compact - KV-cache compaction that closes a verification round.
  *
  * [GUIDE] section "Speculative Decodingの動作原理を理解する": decoding repeats draft, one

@@ -70,10 +70,10 @@ def lm_head_stats(hidden, W, parents, tokens, n_nodes=None):
         if problems:
             out["err"][b] = encode_err(*min(problems))
             continue
+        if n > 0:
+            out["logits"][b, :n] = hidden[b, :n] @ W64.T      # l_i[v] = sum_k W[v, k] h_i[k]
         for i in range(n):
-            row = W64 @ hidden[b, i]                  # l_i[v] = sum_k W[v, k] h_i[k]
-            out["logits"][b, i] = row
-            m, am, S, A = row_statistics(row)
+            m, am, S, A = row_statistics(out["logits"][b, i])
             out["row_max"][b, i], out["row_argmax"][b, i] = m, am
             out["row_sum"][b, i], out["row_ent"][b, i] = S, A
         for c in range(1, n):

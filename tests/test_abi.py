@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("spec_tree_build", "spec_tree_assemble", "spec_tree_attn", "spec_tree_attn_workspace",
               "spec_verify", "spec_verify_workspace", "spec_medusa_heads", "spec_medusa_heads_workspace",
-              "spec_kv_compact", "spec_tree_select", "spec_strerror", "spec_prof_enable", "spec_prof_reset",
+              "spec_kv_compact", "spec_tree_select", "spec_lm_head_stats", "spec_lm_head_stats_workspace",
+              "spec_strerror", "spec_prof_enable", "spec_prof_reset",
               "spec_prof_read"):
         assert n in names, n
 
@@ -123,3 +124,21 @@ def test_tree_select_argument_checks(lib):
     assert call(N=0) == 1 and call(N=257) == 1
     assert call(tok_in=fake) == 1 and call(tok=fake) == 1          # tokens in without out, and back
     assert call(row_in=fake) == 1 and call(row=fake) == 1
+
+
+def test_lm_head_stats_argument_checks(lib):
+    fake = ctypes.c_void_p(0x1000)     # 16-byte aligned; never dereferenced (no call launches)
+    odd = ctypes.c_void_p(0x1008)
+    ws = lib.spec_lm_head_stats_workspace(1, 63, 128256)
+    assert ws >= 63 * 2004 * 24
+
+    def call(h=fake, W=fake, B=1, N=63, Dm=4096, V=128256, out=fake, wsz=ws, wsp=fake):
+        return lib.spec_lm_head_stats(h, W, fake, fake, None, B, N, Dm, V, out, fake, fake, fake, fake, fake,
+                                      wsp, wsz, None)
+
+    assert call(h=None) == 1 and call(W=None) == 1 and call(out=None) == 1
+    assert call(B=0) == 1 and call(V=0) == 1
+    assert call(B=2, N=33) == 2                          # more than 64 rows
+    assert call(Dm=4000) == 2                            # not a multiple of 128
+    assert call(h=odd) == 2 and call(W=odd) == 2         # alignment
+    assert call(wsz=ws - 1) == 3 and call(wsp=None) == 3

@@ -1,0 +1,110 @@
+"""GPU parity of spec_lm_head_stats (the target LM head fused with the verify row statistics)
+against oracle.lm_head_stats.
+
+Tolerance, derived from the arithmetic: bf16 x bf16 products are exact in fp32 and the GPU sums
+Dm of them in fp32 in some order, so every logit is within
+    delta_p = (Dm + 2) * 2^-24 * max_v sum_k |h_p[k]| |W[v, k]|
+of the exact one (the standard bound for a sum of Dm terms in any order, with slack).  Then
+row_max and cand_logit are within delta_p; the lowest argmax is exact unless the oracle's two
+best logits are within 2 delta_p (then the GPU's choice must hold a logit within 2 delta_p of
+the max); S = sum exp(l - max) is within a factor exp(+-2 delta_p) (+ fp32 exp rounding); the
+entropy ln S - A / S within 4 delta_p (H + 1).  Error words and NaN patterns are exact."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tree_attention_verification_spec_amd import binding as sb
+from tree_attention_verification_spec_amd import workloads as wl
+
+from gpu_util import dev, host, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def bound(h, W):
+    """delta per (b, i): (Dm + 2) 2^-24 max_v sum_k |h||W| (fp32 product, inflated by 1 %)."""
+    B, N, Dm = h.shape
+    absW = torch.from_numpy(np.abs(W)).float()
+    s = torch.from_numpy(np.abs(h).reshape(B * N, Dm)).float() @ absW.T
+    return ((Dm + 2) * 2.0 ** -24 * 1.01 * s.max(dim=1).values.double().numpy()).reshape(B, N)
+
+
+def run_both(inp, n_nodes=None, what=""):
+    need_gpu()
+    h, W, par, tok = inp["hidden"], inp["W"], inp["parents"], inp["tokens"]
+    B, N, Dm = h.shape
+    print(f"lm_head_stats {what}: B={B} N={N} Dm={Dm} V={W.shape[0]}", flush=True)
+    got = sb.spec_lm_head_stats(dev(h, torch.bfloat16), dev(W, torch.bfloat16), dev(par), dev(tok),
+                                n_nodes=None if n_nodes is None else dev(n_nodes))
+    torch.cuda.synchronize()
+    got = {k: host(v) for k, v in got.items()}
+    ref = oracle.lm_head_stats(h, W, par, tok, n_nodes=n_nodes)
+    assert np.array_equal(got["err"], ref["err"]), f"{what}: err {got['err']} vs {ref['err']}"
+    ok = np.isfinite(ref["row_max"])
+    for key in ("row_max", "row_sum", "row_ent", "cand_logit"):
+        assert np.array_equal(np.isnan(got[key]), np.isnan(ref[key])), f"{what}: {key} NaN pattern"
+    assert np.array_equal(got["row_argmax"][~ok], ref["row_argmax"][~ok])
+    d = bound(h, W)
+    worst = {}
+    for b, i in zip(*np.nonzero(ok)):
+        dl = d[b, i]
+        row = ref["logits"][b, i]
+        m = ref["row_max"][b, i]
+        e_max = abs(got["row_max"][b, i] - m)
+        assert e_max <= dl, f"{what}: row_max ({b},{i}) off by {e_max:.3e} > {dl:.3e}"
+        ga, ra = int(got["row_argmax"][b, i]), int(ref["row_argmax"][b, i])
+        if ga != ra:
+            second = np.partition(row, -2)[-2]
+            assert m - second <= 2 * dl and row[ga] >= m - 2 * dl, f"{what}: argmax ({b},{i}) {ga} vs {ra}"
+        S, A = ref["row_sum"][b, i], ref["row_ent"][b, i]
+        gS, gA = got["row_sum"][b, i], got["row_ent"][b, i]
+        assert abs(gS - S) <= (np.expm1(2 * dl) + 1e-6) * S, f"{what}: row_sum ({b},{i}) {gS} vs {S}"
+        H, gH = np.log(S) - A / S, np.log(gS) - gA / gS
+        assert abs(gH - H) <= 4 * dl * (H + 1) + 1e-6, f"{what}: entropy ({b},{i}) {gH} vs {H}"
+        if i > 0:
+            e_c = abs(got["cand_logit"][b, i] - ref["cand_logit"][b, i])
+            assert e_c <= dl, f"{what}: cand_logit ({b},{i}) off by {e_c:.3e} > {dl:.3e}"
+            worst["cand"] = max(worst.get("cand", 0.0), e_c)
+        worst["max"] = max(worst.get("max", 0.0), e_max)
+        worst["bound"] = max(worst.get("bound", 0.0), dl)
+    print(f"  worst |d max| {worst.get('max', 0):.2e}, |d cand| {worst.get('cand', 0):.2e}, "
+          f"bound {worst.get('bound', 0):.2e}", flush=True)
+    return got, ref
+
+
+@pytest.mark.parametrize("B,N,Dm,V", [(1, 1, 128, 1), (1, 5, 128, 37), (1, 16, 128, 64), (1, 17, 256, 65),
+                                      (2, 16, 256, 1000), (3, 11, 128, 5000), (4, 16, 384, 2048),
+                                      (1, 64, 512, 4099)])
+def test_small(B, N, Dm, V):
+    inp = wl.lm_head_inputs(seed=40 + B + N + V, B=B, N=N, Dm=Dm, V=V)
+    run_both(inp, what=f"small {B}x{N} Dm{Dm} V{V}")
+
+
+def test_ragged_and_errors():
+    inp = wl.lm_head_inputs(seed=9, B=4, N=12, Dm=256, V=3000)
+    inp["parents"][1, 0] = 0
+    inp["parents"][2, 5] = 9
+    inp["tokens"][3, 4] = 3000
+    run_both(inp, n_nodes=np.array([7, 12, 12, 12], dtype=np.int32), what="errors")
+    inp = wl.lm_head_inputs(seed=10, B=4, N=12, Dm=256, V=3000)
+    run_both(inp, n_nodes=np.array([12, 0, 1, 13], dtype=np.int32), what="ragged")
+
+
+def test_ties():
+    """Columns of W that repeat the best logit: the lowest id wins, on the GPU as in the oracle."""
+    inp = wl.lm_head_inputs(seed=12, B=1, N=8, Dm=128, V=700)
+    W = inp["W"]
+    W[[13, 200, 511, 699]] = W[600]
+    inp["hidden"][0, :] = np.sign(W[600])[None, :] * np.abs(inp["hidden"][0, :])   # make row 600 win
+    got, ref = run_both(inp, what="ties")
+    assert (ref["row_argmax"][0] == 13).all()
+    assert np.isin(got["row_argmax"][0], [13, 200, 511, 600, 699]).all()
+    print(f"  GPU argmax on the tied rows: {got['row_argmax'][0].tolist()}", flush=True)
+
+
+def test_llama3_8b_shape():
+    """The 63-node batch-1 workload's shapes: hidden 4096, vocabulary 128256 (a 1 GB LM head)."""
+    inp = wl.lm_head_inputs(seed=2, B=1, N=63, Dm=4096, V=128256)
+    run_both(inp, what="llama3-8b B1 N63")

@@ -46,6 +46,10 @@ def lib():
     L.spec_tree_assemble.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P]
     L.spec_tree_select.restype = _I
     L.spec_tree_select.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]
+    L.spec_lm_head_stats_workspace.restype = _Z
+    L.spec_lm_head_stats_workspace.argtypes = [_I, _I, _I]
+    L.spec_lm_head_stats.restype = _I
+    L.spec_lm_head_stats.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P]
     L.spec_tree_attn_workspace.restype = _Z
     L.spec_tree_attn_workspace.argtypes = [_I, _I, _I, _I, _I, _I, _I]
     L.spec_tree_attn.restype = _I
@@ -241,6 +245,39 @@ def spec_verify(target_logits, tokens, parents, uniforms, mode, draft_probs=None
         _ptr(out["node_accept"], torch.uint8, (B, N), "node_accept"),
         _ptr(out["err"], torch.int32, (B,), "err"), _ptr(ws, None, None, "workspace"), ws.numel(),
         _stream(stream)), "spec_verify")
+    return out
+
+
+# ----------------------------------------------------------------------------- target LM head + row statistics
+
+def lm_head_stats_workspace_bytes(B, N, V):
+    return int(lib().spec_lm_head_stats_workspace(B, N, V))
+
+
+def spec_lm_head_stats(hidden, W, parents, tokens, n_nodes=None, out=None, ws=None, stream=None):
+    B, N, Dm = hidden.shape
+    V = W.shape[0]
+    dev = hidden.device
+    if out is None:
+        out = {"row_max": torch.empty((B, N), dtype=torch.float32, device=dev),
+               "row_argmax": torch.empty((B, N), dtype=torch.int32, device=dev),
+               "row_sum": torch.empty((B, N), dtype=torch.float64, device=dev),
+               "row_ent": torch.empty((B, N), dtype=torch.float64, device=dev),
+               "cand_logit": torch.empty((B, N), dtype=torch.float32, device=dev),
+               "err": torch.empty((B,), dtype=torch.int32, device=dev)}
+    if ws is None:
+        ws = workspace(lm_head_stats_workspace_bytes(B, N, V), dev)
+    _check(lib().spec_lm_head_stats(
+        _ptr(hidden, torch.bfloat16, (B, N, Dm), "hidden"), _ptr(W, torch.bfloat16, (V, Dm), "W"),
+        _ptr(parents, torch.int32, (B, N), "parents"), _ptr(tokens, torch.int32, (B, N), "tokens"),
+        _ptr(n_nodes, torch.int32, (B,), "n_nodes"), B, N, Dm, V,
+        _ptr(out["row_max"], torch.float32, (B, N), "row_max"),
+        _ptr(out["row_argmax"], torch.int32, (B, N), "row_argmax"),
+        _ptr(out["row_sum"], torch.float64, (B, N), "row_sum"),
+        _ptr(out["row_ent"], torch.float64, (B, N), "row_ent"),
+        _ptr(out["cand_logit"], torch.float32, (B, N), "cand_logit"),
+        _ptr(out["err"], torch.int32, (B,), "err"), _ptr(ws, None, None, "workspace"), ws.numel(),
+        _stream(stream)), "spec_lm_head_stats")
     return out
 
 

@@ -1,0 +1,341 @@
+// The target model's LM head fused with the row statistics that verification reads.
+//
+// "EAGLE-3とMedusaで実装するSpeculative Decoding実践ガイド", section "並列検証：ターゲットモデルの
+// 1回のforward passで一括確認する": one target pass gives the distribution T_p = softmax(W h_p) at
+// every tree node ("多トークン予測（Medusa・EAGLE）", section "ツリー検証：候補を「木」に束ねて1回で
+// 確かめる"); the guide's section "ドラフトヘッドの構成と学習手順" gives the Llama-3.1-8B-class
+// shapes (hidden 4096, vocabulary 128256).  Verification reads only a few numbers per row -
+// max, lowest argmax, S = sum exp(l - max), A = sum exp(l - max)(l - max) - and each child's
+// logit in its parent's row, so the logits are reduced where they are produced and the
+// B x N x V logits array is never written.
+//
+// lmhead_stats_kernel: grid ceil(V / 64); a workgroup multiplies 64 rows of W (four 16-row
+// blocks, A operand of v_mfma_f32_16x16x32_bf16, 16-byte loads streamed from HBM) with all
+// M = B * N <= 64 hidden states (up to four 16-column blocks, B operand, L2-resident), K split
+// over the four waves and summed in LDS.  The 64 x M logits tile then stays in LDS: per column,
+// four threads reduce (max, lowest argmax) and then fp64 sums of fp32 exp(l - max), and the
+// candidates whose token falls in the tile pick their parent's logit.  Partials go to the
+// workspace, one per (column, tile).
+// lmhead_merge_kernel: one workgroup per column; block max first, then the partials' sums
+// rescaled by exp(m_j - max) in fp64 (no sequential rescaling), validation of the sequence's
+// tree, and the outputs.
+//
+// Weight-streaming: W (1.05 GB at V = 128256, Dm = 4096) is read from HBM once; the hidden
+// states (512 KB) are re-read from L2 by every workgroup.
+#include <climits>
+
+#include "common.h"
+
+namespace spectree {
+namespace {
+
+constexpr int kLThreads = 256;
+constexpr int kLKWaves = 4;                 // K slices per workgroup
+constexpr int kLRB = 4;                     // 16-row blocks of W per workgroup
+constexpr int kLRows = 16 * kLRB;           // vocabulary rows per workgroup
+constexpr int kLMaxCols = 64;               // B * N limit
+
+struct LmPart {       // one 64-token tile of one row
+  double S;           // sum exp(l - m)
+  double A;           // sum exp(l - m) (l - m)
+  float m;            // tile max
+  int argmax;         // lowest token id of the tile max (INT_MAX: none)
+};
+
+__device__ __forceinline__ bf16x8 ld8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+template <int CBN>
+__global__ __launch_bounds__(kLThreads) void lmhead_stats_kernel(
+    const __bf16* __restrict__ W, const __bf16* __restrict__ X, int M, int Dm, int V, int N,
+    const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
+    LmPart* __restrict__ parts, float* __restrict__ gath) {
+  // the K-slice partials and, once they are summed, the logits tile share one LDS block, so
+  // two workgroups fit a CU
+  constexpr size_t kRedBytes = sizeof(f32x4) * kLKWaves * kLRB * CBN * kWave;
+  constexpr size_t kTileBytes = sizeof(float) * kLRows * (kLMaxCols + 1);
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kRedBytes > kTileBytes ? kRedBytes : kTileBytes];
+  auto red = reinterpret_cast<f32x4 (*)[kLRB * CBN][kWave]>(lds);
+  auto tile = reinterpret_cast<float (*)[kLMaxCols + 1]>(lds);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int row0 = blockIdx.x * kLRows;
+  const int kslice = Dm / kLKWaves;
+  const int kbeg = wave * kslice;
+  // branch-free loads: rows past V and columns past M read the last valid one (never stored)
+  const __bf16* arow[kLRB];
+#pragma unroll
+  for (int rb = 0; rb < kLRB; ++rb)
+    arow[rb] = W + (size_t)min(row0 + rb * 16 + l16, V - 1) * Dm + kbeg + 8 * lg;
+  const __bf16* bptr[CBN];
+#pragma unroll
+  for (int cb = 0; cb < CBN; ++cb) bptr[cb] = X + (size_t)min(cb * 16 + l16, M - 1) * Dm + kbeg + 8 * lg;
+  f32x4 acc[kLRB][CBN];
+#pragma unroll
+  for (int rb = 0; rb < kLRB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CBN; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  struct Frags {
+    bf16x8 a[kLRB];
+    bf16x8 b[CBN];
+  };
+  auto fetch = [&](Frags& f, int s) {
+#pragma unroll
+    for (int rb = 0; rb < kLRB; ++rb) f.a[rb] = ld8(arow[rb] + s * 32);
+#pragma unroll
+    for (int cb = 0; cb < CBN; ++cb) f.b[cb] = ld8(bptr[cb] + s * 32);
+  };
+  auto products = [&](const Frags& f) {
+#pragma unroll
+    for (int cb = 0; cb < CBN; ++cb)
+#pragma unroll
+      for (int rb = 0; rb < kLRB; ++rb)
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[rb], f.b[cb], acc[rb][cb], 0, 0, 0);
+  };
+  // a two-slot ring: the next step's fragments are requested before this step's products;
+  // step indices are clamped, so the loads past the last step re-read it inside the slice
+  const int steps = kslice / 32;
+  Frags f[2];
+  fetch(f[0], 0);
+  for (int s = 0; s < steps; s += 2) {
+    fetch(f[1], min(s + 1, steps - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    products(f[0]);
+    fetch(f[0], min(s + 2, steps - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    if (s + 1 < steps) products(f[1]);
+  }
+#pragma unroll
+  for (int rb = 0; rb < kLRB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CBN; ++cb) red[wave][rb * CBN + cb][lane] = acc[rb][cb];
+  __syncthreads();
+  // the K slices summed (wave w takes the 16 x 16 blocks w, w + 4, ...), then written over the
+  // partials as the logits tile (lane: column l16 of the block, rows 4 lg + e)
+  constexpr int kPerWave = (kLRB * CBN + kLKWaves - 1) / kLKWaves;
+  f32x4 sums[kPerWave];
+#pragma unroll
+  for (int j = 0; j < kPerWave; ++j) {
+    const int t = wave + j * kLKWaves;
+    if (t < kLRB * CBN) sums[j] = red[0][t][lane] + red[1][t][lane] + red[2][t][lane] + red[3][t][lane];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPerWave; ++j) {
+    const int t = wave + j * kLKWaves;
+    if (t < kLRB * CBN) {
+      const int rb = t / CBN, cb = t % CBN;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tile[rb * 16 + 4 * lg + e][cb * 16 + l16] = sums[j][e];
+    }
+  }
+  __syncthreads();
+
+  // per column: four consecutive threads share the tile's 64 rows, 16 each
+  const int col = threadIdx.x >> 2, q = threadIdx.x & 3;
+  float m = -INFINITY;
+  int am = INT_MAX;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int vr = q * 16 + j;
+    const float x = tile[vr][col];
+    if (row0 + vr < V && x > m) {          // ascending ids: strict > keeps the lowest
+      m = x;
+      am = row0 + vr;
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 4; o <<= 1) {
+    const float m2 = __shfl_xor(m, o);
+    const int a2 = __shfl_xor(am, o);
+    if (m2 > m || (m2 == m && a2 < am)) {
+      m = m2;
+      am = a2;
+    }
+  }
+  double S = 0.0, A = 0.0;
+  if (m != -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int vr = q * 16 + j;
+      if (row0 + vr < V) {
+        const float d = tile[vr][col] - m;
+        const double e = (double)expf(d);
+        S += e;
+        A += e * (double)d;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 4; o <<= 1) {
+    S += __shfl_xor(S, o);
+    A += __shfl_xor(A, o);
+  }
+  if (q == 0 && col < M) parts[(size_t)col * gridDim.x + blockIdx.x] = LmPart{S, A, m, am};
+
+  // the candidates whose token lies in this tile take their parent's logit
+  for (int c = threadIdx.x; c < M; c += kLThreads) {
+    const int i = c % N;
+    if (i == 0) continue;
+    const int p = parents[c], x = tokens[c];
+    if (p >= 0 && p < i && x >= row0 && x < row0 + kLRows && x < V) gath[c] = tile[x - row0][c - i + p];
+  }
+}
+
+__global__ __launch_bounds__(kLThreads) void lmhead_merge_kernel(
+    const LmPart* __restrict__ parts, const float* __restrict__ gath, int nblk, int N, int V,
+    const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
+    const int32_t* __restrict__ n_nodes, float* __restrict__ row_max, int32_t* __restrict__ row_argmax,
+    double* __restrict__ row_sum, double* __restrict__ row_ent, float* __restrict__ cand_logit,
+    int32_t* __restrict__ err) {
+  __shared__ float s_m[kLThreads / kWave];
+  __shared__ int s_a[kLThreads / kWave];
+  __shared__ double s_S[kLThreads / kWave], s_A[kLThreads / kWave];
+  __shared__ int s_err;
+  const int col = blockIdx.x;
+  const int b = col / N, i = col - b * N;
+  const int t = threadIdx.x, lane = t & (kWave - 1), wv = t >> 6;
+  if (t == 0) s_err = INT_MAX;
+  __syncthreads();
+  // the sequence's tree, validated by every column of the sequence (N <= 64)
+  const int n = n_nodes ? n_nodes[b] : N;
+  const bool bad_n = n < 0 || n > N;
+  if (!bad_n && t < n) {
+    const int p = parents[(size_t)b * N + t], x = tokens[(size_t)b * N + t];
+    int code = 0;
+    if (t == 0) {
+      if (p != -1) code = SPEC_ERR_ROOT;
+    } else if (p < 0 || p >= t) {
+      code = SPEC_ERR_PARENT;
+    } else if (x < 0 || x >= V) {
+      code = SPEC_ERR_TOKEN;
+    }
+    if (code) atomicMin(&s_err, err_word(t, code));
+  }
+  // block max, lowest argmax among the tiles holding it
+  const LmPart* pp = parts + (size_t)col * nblk;
+  float m = -INFINITY;
+  int am = INT_MAX;
+  for (int j = t; j < nblk; j += kLThreads) {
+    const float mj = pp[j].m;
+    const int aj = pp[j].argmax;
+    if (mj > m || (mj == m && aj < am)) {
+      m = mj;
+      am = aj;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o);
+    const int a2 = __shfl_xor(am, o);
+    if (m2 > m || (m2 == m && a2 < am)) {
+      m = m2;
+      am = a2;
+    }
+  }
+  if (lane == 0) {
+    s_m[wv] = m;
+    s_a[wv] = am;
+  }
+  __syncthreads();
+  m = s_m[0];
+  am = s_a[0];
+#pragma unroll
+  for (int w = 1; w < kLThreads / kWave; ++w) {
+    if (s_m[w] > m || (s_m[w] == m && s_a[w] < am)) {
+      m = s_m[w];
+      am = s_a[w];
+    }
+  }
+  // sums rescaled to the row max: A_j is relative to m_j, so A += e (A_j + (m_j - M) S_j)
+  double S = 0.0, A = 0.0;
+  for (int j = t; j < nblk; j += kLThreads) {
+    const LmPart pj = pp[j];
+    if (pj.m != -INFINITY) {
+      const double d = (double)pj.m - (double)m;
+      const double e = exp(d);
+      S += e * pj.S;
+      A += e * (pj.A + d * pj.S);
+    }
+  }
+  S = wave_sum(S);
+  A = wave_sum(A);
+  if (lane == 0) {
+    s_S[wv] = S;
+    s_A[wv] = A;
+  }
+  __syncthreads();
+  if (t == 0) {
+    S = 0.0;
+    A = 0.0;
+    for (int w = 0; w < kLThreads / kWave; ++w) {
+      S += s_S[w];
+      A += s_A[w];
+    }
+    const int e = bad_n ? err_word(0, SPEC_ERR_NNODES) : (s_err == INT_MAX ? 0 : s_err);
+    const bool ok = e == 0 && i < n;
+    row_max[col] = ok ? m : NAN;
+    row_argmax[col] = ok ? am : -1;
+    row_sum[col] = ok ? S : NAN;
+    row_ent[col] = ok ? A : NAN;
+    cand_logit[col] = (ok && i > 0) ? gath[col] : NAN;
+    if (i == 0) err[b] = e;
+  }
+}
+
+}  // namespace
+}  // namespace spectree
+
+using namespace spectree;
+
+namespace {
+struct LmLayout {
+  int nblk;
+  size_t parts, gath, total;
+};
+LmLayout lm_layout(int B, int N, int V) {
+  LmLayout L{};
+  L.nblk = (V + kLRows - 1) / kLRows;
+  const size_t M = (size_t)B * N;
+  L.parts = 0;
+  L.gath = align_up(M * L.nblk * sizeof(LmPart), 256);
+  L.total = L.gath + align_up(M * sizeof(float), 256);
+  return L;
+}
+}  // namespace
+
+extern "C" size_t spec_lm_head_stats_workspace(int B, int N, int V) {
+  if (B < 1 || N < 1 || V < 1) return 0;
+  return lm_layout(B, N, V).total;
+}
+
+extern "C" spec_status spec_lm_head_stats(const void* hidden, const void* W, const int32_t* parents,
+                                          const int32_t* tokens, const int32_t* n_nodes, int B, int N,
+                                          int Dm, int V, float* row_max, int32_t* row_argmax,
+                                          double* row_sum, double* row_ent, float* cand_logit,
+                                          int32_t* err, void* workspace, size_t ws_bytes, void* stream) {
+  if (B < 1 || N < 1 || Dm < 1 || V < 1) return SPEC_EINVAL;
+  if (!hidden || !W || !parents || !tokens || !row_max || !row_argmax || !row_sum || !row_ent ||
+      !cand_logit || !err)
+    return SPEC_EINVAL;
+  const int M = B * N;
+  if (M > kLMaxCols || Dm % 128 != 0) return SPEC_EUNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(hidden) & 15) || (reinterpret_cast<uintptr_t>(W) & 15))
+    return SPEC_EUNSUPPORTED;
+  const LmLayout L = lm_layout(B, N, V);
+  if (!workspace || ws_bytes < L.total) return SPEC_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(workspace);
+  LmPart* parts = reinterpret_cast<LmPart*>(w + L.parts);
+  float* gath = reinterpret_cast<float*>(w + L.gath);
+  const __bf16* Wb = static_cast<const __bf16*>(W);
+  const __bf16* X = static_cast<const __bf16*>(hidden);
+  const dim3 g1((unsigned)L.nblk), blk(kLThreads);
+  const char* nm = "lm_head_stats";
+  if (M <= 16) launch(nm, lmhead_stats_kernel<1>, g1, blk, s, Wb, X, M, Dm, V, N, parents, tokens, parts, gath);
+  else if (M <= 32) launch(nm, lmhead_stats_kernel<2>, g1, blk, s, Wb, X, M, Dm, V, N, parents, tokens, parts, gath);
+  else if (M <= 48) launch(nm, lmhead_stats_kernel<3>, g1, blk, s, Wb, X, M, Dm, V, N, parents, tokens, parts, gath);
+  else launch(nm, lmhead_stats_kernel<4>, g1, blk, s, Wb, X, M, Dm, V, N, parents, tokens, parts, gath);
+  launch("lm_head_merge", lmhead_merge_kernel, dim3((unsigned)M), blk, s, parts, gath, L.nblk, N, V,
+         parents, tokens, n_nodes, row_max, row_argmax, row_sum, row_ent, cand_logit, err);
+  return launch_status();
+}

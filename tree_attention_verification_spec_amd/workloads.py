@@ -330,3 +330,19 @@ def random_pool(seed, B, C, max_depth=8, power=2.0):
     tokens = (np.arange(C, dtype=np.int32)[None, :] * 7 + 1000 * np.arange(B, dtype=np.int32)[:, None])
     rows = np.maximum(par, 0).astype(np.int32)
     return {"cand_parents": par, "cand_prob": prob, "cand_tokens": tokens.astype(np.int32), "cand_row": rows}
+
+
+# ----------------------------------------------------------------------------- target LM head
+
+def lm_head_inputs(seed, B, N, Dm, V, parents=None, max_depth=4):
+    """The target's last hidden states at the tree nodes, h ~ N(0, 1), and its LM head
+    W ~ N(0, 0.02) [V, Dm], both rounded to bf16 (fp32 arrays holding bf16 values); a tree per
+    sequence (node i attaches to a uniform earlier node of depth < max_depth, unless given) and
+    uniform candidate tokens."""
+    h = round_bf16(np.stack([rng(seed, S_H, b).standard_normal((N, Dm), dtype=np.float32) for b in range(B)]))
+    W = round_bf16(rng(seed, S_WLM).standard_normal((V, Dm), dtype=np.float32) * np.float32(0.02))
+    if parents is None:
+        parents = np.stack([random_tree(rng(seed, S_TREE, b), N, max_depth) for b in range(B)]).astype(np.int32)
+    tokens = np.stack([rng(seed, S_LOGITS, b).integers(0, V, size=N) for b in range(B)]).astype(np.int32)
+    tokens[:, 0] = -1
+    return {"hidden": h, "W": W, "parents": np.asarray(parents, dtype=np.int32), "tokens": tokens}
