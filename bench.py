@@ -295,14 +295,16 @@ def lm_head_stats_timing(w, reps=20, Dm=4096):
         sb.prof_enable(False)
         ms, cnt = sb.prof_read("lm_head_stats")
         ms2, cnt2 = sb.prof_read("lm_head_merge")
+        ms3, cnt3 = sb.prof_read("lm_head_xperm")
     finally:
         sb.prof_enable(False)
         sb.prof_reset()
-    us, us_merge = ms / cnt * 1e3, ms2 / cnt2 * 1e3
+    us, us_merge, us_perm = ms / cnt * 1e3, ms2 / cnt2 * 1e3, ms3 / cnt3 * 1e3
     nbytes = V * Dm * 2 + B * N * Dm * 2
     flops = 2 * B * N * Dm * V
     del W
     return {"shape": f"[{B * N} x {Dm}] x [{Dm} x {V}]", "us": round(us, 3), "merge_us": round(us_merge, 3),
+            "xperm_us": round(us_perm, 3),
             "algorithmic_bytes": nbytes, "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
             "hbm_frac": round(nbytes / (us * 1e-6) / 8e12, 4),
             "achieved_TFLOPs": round(flops / (us * 1e-6) / 1e12, 1)}
@@ -491,8 +493,8 @@ def main():
     log(f"tree_select (before the step, not in it): {tsel['pool']}, {tsel['us']:.2f} us")
     lmh = lm_head_stats_timing(w)
     if lmh:
-        log(f"lm_head_stats (beside the step, not in it): {lmh['shape']}, {lmh['us']:.2f} us + merge "
-            f"{lmh['merge_us']:.2f} us, {lmh['achieved_GBs']:.0f} GB/s")
+        log(f"lm_head_stats (beside the step, not in it): {lmh['shape']}, {lmh['xperm_us']:.2f} us permute + "
+            f"{lmh['us']:.2f} us + merge {lmh['merge_us']:.2f} us, {lmh['achieved_GBs']:.0f} GB/s")
 
     if args.copy_calibration_mb:
         nb = args.copy_calibration_mb * (1 << 20)

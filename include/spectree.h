@@ -291,12 +291,13 @@ spec_status spec_tree_select(const int32_t* cand_parents, const float* cand_prob
  *   cand_logit float [B, N], err int32 [B]: SPEC_ERR_NNODES, SPEC_ERR_ROOT, SPEC_ERR_PARENT,
  *   SPEC_ERR_TOKEN (a non-root token outside [0, V)).  Rows past n_nodes and every row of a
  *   sequence with an error get NaN (argmax -1).
- * The workspace (spec_lm_head_stats_workspace bytes) holds one partial per (row, 64 tokens).
+ * The workspace (spec_lm_head_stats_workspace bytes) holds one partial per (row, 64 tokens) and
+ * a copy of the hidden states in the order the matrix-core fragments read them.
  * Supported: B * N <= 64, Dm a multiple of 128.
  * Errors: SPEC_EINVAL (sizes, NULL pointers), SPEC_EUNSUPPORTED (B * N, Dm, alignment),
  * SPEC_EWORKSPACE.
  * ------------------------------------------------------------------------------------ */
-size_t spec_lm_head_stats_workspace(int B, int N, int V);
+size_t spec_lm_head_stats_workspace(int B, int N, int Dm, int V);
 spec_status spec_lm_head_stats(const void* hidden, const void* W, const int32_t* parents,
                                const int32_t* tokens, const int32_t* n_nodes, int B, int N, int Dm,
                                int V, float* row_max, int32_t* row_argmax, double* row_sum,

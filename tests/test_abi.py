@@ -129,8 +129,8 @@ def test_tree_select_argument_checks(lib):
 def test_lm_head_stats_argument_checks(lib):
     fake = ctypes.c_void_p(0x1000)     # 16-byte aligned; never dereferenced (no call launches)
     odd = ctypes.c_void_p(0x1008)
-    ws = lib.spec_lm_head_stats_workspace(1, 63, 128256)
-    assert ws >= 63 * 2004 * 24
+    ws = lib.spec_lm_head_stats_workspace(1, 63, 4096, 128256)
+    assert ws >= 63 * 2004 * 24 + 63 * 4096 * 2
 
     def call(h=fake, W=fake, B=1, N=63, Dm=4096, V=128256, out=fake, wsz=ws, wsp=fake):
         return lib.spec_lm_head_stats(h, W, fake, fake, None, B, N, Dm, V, out, fake, fake, fake, fake, fake,

@@ -47,7 +47,7 @@ def lib():
     L.spec_tree_select.restype = _I
     L.spec_tree_select.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]
     L.spec_lm_head_stats_workspace.restype = _Z
-    L.spec_lm_head_stats_workspace.argtypes = [_I, _I, _I]
+    L.spec_lm_head_stats_workspace.argtypes = [_I, _I, _I, _I]
     L.spec_lm_head_stats.restype = _I
     L.spec_lm_head_stats.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P]
     L.spec_tree_attn_workspace.restype = _Z
@@ -250,8 +250,8 @@ def spec_verify(target_logits, tokens, parents, uniforms, mode, draft_probs=None
 
 # ----------------------------------------------------------------------------- target LM head + row statistics
 
-def lm_head_stats_workspace_bytes(B, N, V):
-    return int(lib().spec_lm_head_stats_workspace(B, N, V))
+def lm_head_stats_workspace_bytes(B, N, Dm, V):
+    return int(lib().spec_lm_head_stats_workspace(B, N, Dm, V))
 
 
 def spec_lm_head_stats(hidden, W, parents, tokens, n_nodes=None, out=None, ws=None, stream=None):
@@ -266,7 +266,7 @@ def spec_lm_head_stats(hidden, W, parents, tokens, n_nodes=None, out=None, ws=No
                "cand_logit": torch.empty((B, N), dtype=torch.float32, device=dev),
                "err": torch.empty((B,), dtype=torch.int32, device=dev)}
     if ws is None:
-        ws = workspace(lm_head_stats_workspace_bytes(B, N, V), dev)
+        ws = workspace(lm_head_stats_workspace_bytes(B, N, Dm, V), dev)
     _check(lib().spec_lm_head_stats(
         _ptr(hidden, torch.bfloat16, (B, N, Dm), "hidden"), _ptr(W, torch.bfloat16, (V, Dm), "W"),
         _ptr(parents, torch.int32, (B, N), "parents"), _ptr(tokens, torch.int32, (B, N), "tokens"),

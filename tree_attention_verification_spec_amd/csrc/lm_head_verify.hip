@@ -21,7 +21,8 @@
 // tree, and the outputs.
 //
 // Weight-streaming: W (1.05 GB at V = 128256, Dm = 4096) is read from HBM once; the hidden
-// states (512 KB) are re-read from L2 by every workgroup.
+// states (512 KB) are re-read from L2 by every workgroup, from a copy in fragment order
+// (lmhead_xperm_kernel) so that each B-fragment load is four 256-byte runs.
 #include <climits>
 
 #include "common.h"
@@ -34,6 +35,7 @@ constexpr int kLKWaves = 4;                 // K slices per workgroup
 constexpr int kLRB = 4;                     // 16-row blocks of W per workgroup
 constexpr int kLRows = 16 * kLRB;           // vocabulary rows per workgroup
 constexpr int kLMaxCols = 64;               // B * N limit
+constexpr int kMergePer = 8;                // partials per merging thread held in registers
 
 struct LmPart {       // one 64-token tile of one row
   double S;           // sum exp(l - m)
@@ -46,7 +48,7 @@ __device__ __forceinline__ bf16x8 ld8(const __bf16* p) { return *reinterpret_cas
 
 template <int CBN>
 __global__ __launch_bounds__(kLThreads) void lmhead_stats_kernel(
-    const __bf16* __restrict__ W, const __bf16* __restrict__ X, int M, int Dm, int V, int N,
+    const __bf16* __restrict__ W, const __bf16* __restrict__ Xp, int M, int Dm, int V, int N,
     const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
     LmPart* __restrict__ parts, float* __restrict__ gath) {
   // the K-slice partials and, once they are summed, the logits tile share one LDS block, so
@@ -66,9 +68,12 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_kernel(
 #pragma unroll
   for (int rb = 0; rb < kLRB; ++rb)
     arow[rb] = W + (size_t)min(row0 + rb * 16 + l16, V - 1) * Dm + kbeg + 8 * lg;
+  // Xp is the hidden states in fragment order, element (col, k) at ((k / 8) M + col) 8 + k % 8:
+  // a B fragment (lane l: column l % 16, k = 8 (l / 16) + [0, 8)) is four 256-byte runs
   const __bf16* bptr[CBN];
 #pragma unroll
-  for (int cb = 0; cb < CBN; ++cb) bptr[cb] = X + (size_t)min(cb * 16 + l16, M - 1) * Dm + kbeg + 8 * lg;
+  for (int cb = 0; cb < CBN; ++cb)
+    bptr[cb] = Xp + ((size_t)(kbeg / 8 + lg) * M + min(cb * 16 + l16, M - 1)) * 8;
   f32x4 acc[kLRB][CBN];
 #pragma unroll
   for (int rb = 0; rb < kLRB; ++rb)
@@ -82,7 +87,7 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_kernel(
 #pragma unroll
     for (int rb = 0; rb < kLRB; ++rb) f.a[rb] = ld8(arow[rb] + s * 32);
 #pragma unroll
-    for (int cb = 0; cb < CBN; ++cb) f.b[cb] = ld8(bptr[cb] + s * 32);
+    for (int cb = 0; cb < CBN; ++cb) f.b[cb] = ld8(bptr[cb] + (size_t)s * 32 * M);
   };
   auto products = [&](const Frags& f) {
 #pragma unroll
@@ -91,18 +96,21 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_kernel(
       for (int rb = 0; rb < kLRB; ++rb)
         acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[rb], f.b[cb], acc[rb][cb], 0, 0, 0);
   };
-  // a two-slot ring: the next step's fragments are requested before this step's products;
-  // step indices are clamped, so the loads past the last step re-read it inside the slice
+  // a three-slot ring: two steps' fragments are in flight while a step's products run (the
+  // ring index is static inside the unrolled body); step indices are clamped, so the loads past
+  // the last step re-read it inside the slice
+  constexpr int NB = 3;
   const int steps = kslice / 32;
-  Frags f[2];
-  fetch(f[0], 0);
-  for (int s = 0; s < steps; s += 2) {
-    fetch(f[1], min(s + 1, steps - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    products(f[0]);
-    fetch(f[0], min(s + 2, steps - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    if (s + 1 < steps) products(f[1]);
+  Frags f[NB];
+#pragma unroll
+  for (int u = 0; u < NB - 1; ++u) fetch(f[u], min(u, steps - 1));
+  for (int s = 0; s < steps; s += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      fetch(f[(u + NB - 1) % NB], min(s + u + NB - 1, steps - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + u < steps) products(f[u]);
+    }
   }
 #pragma unroll
   for (int rb = 0; rb < kLRB; ++rb)
@@ -181,6 +189,16 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_kernel(
   }
 }
 
+// The hidden states [M, Dm] into fragment order (see lmhead_stats_kernel), 16 bytes per thread.
+__global__ __launch_bounds__(kLThreads) void lmhead_xperm_kernel(const __bf16* __restrict__ X, int M, int Dm,
+                                                                 __bf16* __restrict__ Xp) {
+  const int id = blockIdx.x * kLThreads + threadIdx.x;     // (k / 8) * M + col
+  const int K8 = Dm / 8;
+  if (id >= K8 * M) return;
+  const int k8 = id / M, col = id - k8 * M;
+  *reinterpret_cast<bf16x8*>(Xp + (size_t)id * 8) = ld8(X + (size_t)col * Dm + (size_t)k8 * 8);
+}
+
 __global__ __launch_bounds__(kLThreads) void lmhead_merge_kernel(
     const LmPart* __restrict__ parts, const float* __restrict__ gath, int nblk, int N, int V,
     const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
@@ -211,16 +229,34 @@ __global__ __launch_bounds__(kLThreads) void lmhead_merge_kernel(
     }
     if (code) atomicMin(&s_err, err_word(t, code));
   }
-  // block max, lowest argmax among the tiles holding it
+  // block max, lowest argmax among the tiles holding it; up to kMergePer partials per thread
+  // are requested at once and kept for the sums (more than that: a strided loop)
   const LmPart* pp = parts + (size_t)col * nblk;
+  const bool held = nblk <= kLThreads * kMergePer;
+  LmPart mine[kMergePer];
   float m = -INFINITY;
   int am = INT_MAX;
-  for (int j = t; j < nblk; j += kLThreads) {
-    const float mj = pp[j].m;
-    const int aj = pp[j].argmax;
-    if (mj > m || (mj == m && aj < am)) {
-      m = mj;
-      am = aj;
+  if (held) {
+#pragma unroll
+    for (int u = 0; u < kMergePer; ++u) {
+      const int j = t + u * kLThreads;
+      mine[u] = j < nblk ? pp[j] : LmPart{0.0, 0.0, -INFINITY, INT_MAX};
+    }
+#pragma unroll
+    for (int u = 0; u < kMergePer; ++u) {
+      if (mine[u].m > m || (mine[u].m == m && mine[u].argmax < am)) {
+        m = mine[u].m;
+        am = mine[u].argmax;
+      }
+    }
+  } else {
+    for (int j = t; j < nblk; j += kLThreads) {
+      const float mj = pp[j].m;
+      const int aj = pp[j].argmax;
+      if (mj > m || (mj == m && aj < am)) {
+        m = mj;
+        am = aj;
+      }
     }
   }
 #pragma unroll
@@ -248,14 +284,19 @@ __global__ __launch_bounds__(kLThreads) void lmhead_merge_kernel(
   }
   // sums rescaled to the row max: A_j is relative to m_j, so A += e (A_j + (m_j - M) S_j)
   double S = 0.0, A = 0.0;
-  for (int j = t; j < nblk; j += kLThreads) {
-    const LmPart pj = pp[j];
+  auto add = [&](const LmPart& pj) {
     if (pj.m != -INFINITY) {
       const double d = (double)pj.m - (double)m;
       const double e = exp(d);
       S += e * pj.S;
       A += e * (pj.A + d * pj.S);
     }
+  };
+  if (held) {
+#pragma unroll
+    for (int u = 0; u < kMergePer; ++u) add(mine[u]);
+  } else {
+    for (int j = t; j < nblk; j += kLThreads) add(pp[j]);
   }
   S = wave_sum(S);
   A = wave_sum(A);
@@ -290,22 +331,23 @@ using namespace spectree;
 namespace {
 struct LmLayout {
   int nblk;
-  size_t parts, gath, total;
+  size_t parts, gath, xperm, total;
 };
-LmLayout lm_layout(int B, int N, int V) {
+LmLayout lm_layout(int B, int N, int V, int Dm) {
   LmLayout L{};
   L.nblk = (V + kLRows - 1) / kLRows;
   const size_t M = (size_t)B * N;
   L.parts = 0;
   L.gath = align_up(M * L.nblk * sizeof(LmPart), 256);
-  L.total = L.gath + align_up(M * sizeof(float), 256);
+  L.xperm = L.gath + align_up(M * sizeof(float), 256);
+  L.total = L.xperm + align_up(M * (size_t)Dm * 2, 256);
   return L;
 }
 }  // namespace
 
-extern "C" size_t spec_lm_head_stats_workspace(int B, int N, int V) {
-  if (B < 1 || N < 1 || V < 1) return 0;
-  return lm_layout(B, N, V).total;
+extern "C" size_t spec_lm_head_stats_workspace(int B, int N, int Dm, int V) {
+  if (B < 1 || N < 1 || Dm < 1 || V < 1) return 0;
+  return lm_layout(B, N, V, Dm).total;
 }
 
 extern "C" spec_status spec_lm_head_stats(const void* hidden, const void* W, const int32_t* parents,
@@ -321,20 +363,24 @@ extern "C" spec_status spec_lm_head_stats(const void* hidden, const void* W, con
   if (M > kLMaxCols || Dm % 128 != 0) return SPEC_EUNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(hidden) & 15) || (reinterpret_cast<uintptr_t>(W) & 15))
     return SPEC_EUNSUPPORTED;
-  const LmLayout L = lm_layout(B, N, V);
+  const LmLayout L = lm_layout(B, N, V, Dm);
   if (!workspace || ws_bytes < L.total) return SPEC_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(workspace);
   LmPart* parts = reinterpret_cast<LmPart*>(w + L.parts);
   float* gath = reinterpret_cast<float*>(w + L.gath);
+  __bf16* Xp = reinterpret_cast<__bf16*>(w + L.xperm);
   const __bf16* Wb = static_cast<const __bf16*>(W);
   const __bf16* X = static_cast<const __bf16*>(hidden);
   const dim3 g1((unsigned)L.nblk), blk(kLThreads);
+  const int nchunk = M * (Dm / 8);
+  launch("lm_head_xperm", lmhead_xperm_kernel, dim3((unsigned)((nchunk + kLThreads - 1) / kLThreads)), blk, s, X,
+         M, Dm, Xp);
   const char* nm = "lm_head_stats";
-  if (M <= 16) launch(nm, lmhead_stats_kernel<1>, g1, blk, s, Wb, X, M, Dm, V, N, parents, tokens, parts, gath);
-  else if (M <= 32) launch(nm, lmhead_stats_kernel<2>, g1, blk, s, Wb, X, M, Dm, V, N, parents, tokens, parts, gath);
-  else if (M <= 48) launch(nm, lmhead_stats_kernel<3>, g1, blk, s, Wb, X, M, Dm, V, N, parents, tokens, parts, gath);
-  else launch(nm, lmhead_stats_kernel<4>, g1, blk, s, Wb, X, M, Dm, V, N, parents, tokens, parts, gath);
+  if (M <= 16) launch(nm, lmhead_stats_kernel<1>, g1, blk, s, Wb, Xp, M, Dm, V, N, parents, tokens, parts, gath);
+  else if (M <= 32) launch(nm, lmhead_stats_kernel<2>, g1, blk, s, Wb, Xp, M, Dm, V, N, parents, tokens, parts, gath);
+  else if (M <= 48) launch(nm, lmhead_stats_kernel<3>, g1, blk, s, Wb, Xp, M, Dm, V, N, parents, tokens, parts, gath);
+  else launch(nm, lmhead_stats_kernel<4>, g1, blk, s, Wb, Xp, M, Dm, V, N, parents, tokens, parts, gath);
   launch("lm_head_merge", lmhead_merge_kernel, dim3((unsigned)M), blk, s, parts, gath, L.nblk, N, V,
          parents, tokens, n_nodes, row_max, row_argmax, row_sum, row_ent, cand_logit, err);
   return launch_status();
