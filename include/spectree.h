@@ -305,6 +305,31 @@ spec_status spec_lm_head_stats(const void* hidden, const void* W, const int32_t*
                                size_t ws_bytes, void* stream);
 
 /* --------------------------------------------------------------------------------------
+ * spec_verify_greedy_stats - greedy verification from spec_lm_head_stats' statistics, so that a
+ * temperature-0 round never materialises the N x V logits.
+ *
+ * The GREEDY rule of spec_verify on the row arg-maxima alone ([GUIDE] section "結論・成果"
+ * quotes speed-ups at temperature 0, where T_p collapses to its lowest-id argmax): node c
+ * (parent p, token x) is accepted iff x == row_argmax[b, p]; a node survives iff every node on
+ * its path below the root was accepted; m = the deepest survivor (lowest index on ties);
+ * accept_len = depth(m), path = root .. m, bonus_token = row_argmax[b, m].
+ *
+ *   row_argmax  int32 [B, N]  spec_lm_head_stats' output; tokens, parents int32 [B, N];
+ *   n_nodes     int32 [B] optional (NULL = N); max_depth and V as for spec_verify
+ * Outputs: accept_len [B], path [B, max_depth + 1], bonus_token [B], node_accept uint8 [B, N]
+ *   (optional, NULL), err [B] - exactly as spec_verify in GREEDY mode (errors SPEC_ERR_NNODES,
+ *   ROOT, PARENT, DEPTH, TOKEN; a sequence with n_nodes 0 or an error gets accept_len 0,
+ *   path -1, bonus -1, node_accept 0).  No workspace.
+ * Supported: N <= 256.
+ * Errors: SPEC_EINVAL (sizes, NULL required pointers).
+ * ------------------------------------------------------------------------------------ */
+spec_status spec_verify_greedy_stats(const int32_t* row_argmax, const int32_t* tokens,
+                                     const int32_t* parents, const int32_t* n_nodes, int B, int N,
+                                     int V, int max_depth, int32_t* accept_len, int32_t* path,
+                                     int32_t* bonus_token, uint8_t* node_accept, int32_t* err,
+                                     void* stream);
+
+/* --------------------------------------------------------------------------------------
  * spec_kv_compact - KV-cache compaction that closes a verification round.
  *
  * [GUIDE] section "Speculative Decodingの動作原理を理解する": decoding repeats draft, one

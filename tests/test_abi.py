@@ -31,6 +31,7 @@ def test_header_declares_the_entry_points():
     for n in ("spec_tree_build", "spec_tree_assemble", "spec_tree_attn", "spec_tree_attn_workspace",
               "spec_verify", "spec_verify_workspace", "spec_medusa_heads", "spec_medusa_heads_workspace",
               "spec_kv_compact", "spec_tree_select", "spec_lm_head_stats", "spec_lm_head_stats_workspace",
+              "spec_verify_greedy_stats",
               "spec_strerror", "spec_prof_enable", "spec_prof_reset",
               "spec_prof_read"):
         assert n in names, n
@@ -142,3 +143,13 @@ def test_lm_head_stats_argument_checks(lib):
     assert call(Dm=4000) == 2                            # not a multiple of 128
     assert call(h=odd) == 2 and call(W=odd) == 2         # alignment
     assert call(wsz=ws - 1) == 3 and call(wsp=None) == 3
+
+
+def test_verify_greedy_stats_argument_checks(lib):
+    fake = ctypes.c_void_p(0x1000)     # never dereferenced: every call below returns before a launch
+
+    def call(am=fake, B=1, N=63, V=100, md=62, acc=fake, err=fake):
+        return lib.spec_verify_greedy_stats(am, fake, fake, None, B, N, V, md, acc, fake, fake, None, err, None)
+
+    assert call(am=None) == 1 and call(acc=None) == 1 and call(err=None) == 1
+    assert call(B=0) == 1 and call(N=257) == 1 and call(V=0) == 1 and call(md=-1) == 1

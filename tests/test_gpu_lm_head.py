@@ -108,3 +108,83 @@ def test_llama3_8b_shape():
     """The 63-node batch-1 workload's shapes: hidden 4096, vocabulary 128256 (a 1 GB LM head)."""
     inp = wl.lm_head_inputs(seed=2, B=1, N=63, Dm=4096, V=128256)
     run_both(inp, what="llama3-8b B1 N63")
+
+
+@pytest.mark.parametrize("seed,B,N,Dm,V", [(21, 1, 63, 4096, 128256), (22, 4, 16, 512, 3000), (23, 2, 30, 256, 777)])
+def test_greedy_round_from_statistics(seed, B, N, Dm, V):
+    """LM head statistics then greedy verification, both on the GPU, against the oracle's logits
+    through oracle.verify (GREEDY).  Candidate tokens are the oracle's argmax of the parent's row
+    for about 70 % of the nodes, so paths are long.  Greedy outcomes depend on the row arg-maxima
+    only: a sequence whose GPU arg-maxima all equal the oracle's must match exactly; one where
+    an arg-maximum differs (allowed only within the fp32 accumulation bound, checked here) is
+    counted, not compared."""
+    need_gpu()
+    inp = wl.lm_head_inputs(seed=seed, B=B, N=N, Dm=Dm, V=V, max_depth=6)
+    ref_stats = oracle.lm_head_stats(inp["hidden"], inp["W"], inp["parents"], inp["tokens"])
+    g = np.random.default_rng(seed)
+    tok = inp["tokens"].copy()
+    for b in range(B):
+        for c in range(1, N):
+            if g.random() < 0.7:
+                tok[b, c] = ref_stats["row_argmax"][b, inp["parents"][b, c]]
+    inp["tokens"] = tok
+    n_nodes = np.array([N - (b % 3) for b in range(B)], dtype=np.int32)
+    print(f"greedy round B={B} N={N} Dm={Dm} V={V}", flush=True)
+    st = sb.spec_lm_head_stats(dev(inp["hidden"], torch.bfloat16), dev(inp["W"], torch.bfloat16),
+                               dev(inp["parents"]), dev(tok), n_nodes=dev(n_nodes))
+    ver = sb.spec_verify_greedy_stats(st["row_argmax"], dev(tok), dev(inp["parents"]), V, n_nodes=dev(n_nodes))
+    torch.cuda.synchronize()
+    ref = oracle.lm_head_stats(inp["hidden"], inp["W"], inp["parents"], tok, n_nodes=n_nodes)
+    logits = np.nan_to_num(ref["logits"], nan=0.0)
+    rv = oracle.verify(logits, tok, inp["parents"], np.zeros((B, N), np.float32), oracle.MODE_GREEDY,
+                       n_nodes=n_nodes)
+    d = bound(inp["hidden"], inp["W"])
+    got = {k: host(v) for k, v in ver.items()}
+    gam = host(st["row_argmax"])
+    compared = 0
+    for b in range(B):
+        nb = int(n_nodes[b])
+        differ = np.flatnonzero(gam[b, :nb] != ref["row_argmax"][b, :nb])
+        for i in differ:                    # a different argmax only within the accumulation bound
+            row = ref["logits"][b, i]
+            assert row[gam[b, i]] >= row.max() - 2 * d[b, i], f"sequence {b} row {i}: argmax off"
+        if differ.size:
+            continue
+        compared += 1
+        assert int(got["err"][b]) == int(rv["err"][b])
+        assert int(got["accept_len"][b]) == int(rv["accept_len"][b]), f"sequence {b}: accept_len"
+        assert np.array_equal(got["path"][b], rv["path"][b]), f"sequence {b}: path"
+        assert int(got["bonus"][b]) == int(rv["bonus"][b]), f"sequence {b}: bonus"
+        assert np.array_equal(got["node_accept"][b], rv["node_accept"][b]), f"sequence {b}: node_accept"
+    print(f"  compared {compared} of {B} sequences; accept_len {got['accept_len'].tolist()}", flush=True)
+    assert compared >= 1
+
+
+def test_greedy_stats_errors():
+    """Error words and the empty sequence, from arg-maxima given directly."""
+    need_gpu()
+    B, N, V = 6, 8, 50
+    par = np.tile(np.array([-1, 0, 0, 1, 1, 2, 3, 6], np.int32), (B, 1))
+    tok = np.tile(np.array([-1, 5, 7, 9, 5, 1, 2, 3], np.int32), (B, 1))
+    am = np.tile(np.array([5, 9, 1, 2, 0, 0, 3, 4], np.int32), (B, 1))
+    par[1, 0] = 3
+    par[2] = np.arange(-1, 7, dtype=np.int32)          # a chain: node 5 is deeper than max_depth
+    par[2, 4] = 4
+    tok[3, 5] = 50
+    n_nodes = np.array([8, 8, 8, 8, 0, 9], np.int32)
+    got = sb.spec_verify_greedy_stats(dev(am), dev(tok), dev(par), V, n_nodes=dev(n_nodes), max_depth=4)
+    torch.cuda.synchronize()
+    got = {k: host(v) for k, v in got.items()}
+    # the oracle on logits whose argmax is am (one-hot rows)
+    logits = np.zeros((B, N, V))
+    for b in range(B):
+        for i in range(N):
+            logits[b, i, am[b, i]] = 1.0
+    rv = oracle.verify(logits, tok, par, np.zeros((B, N), np.float32), oracle.MODE_GREEDY, n_nodes=n_nodes,
+                       max_depth=4)
+    for key in ("err", "accept_len", "bonus"):
+        assert np.array_equal(got[key], rv[key]), f"{key}: {got[key]} vs {rv[key]}"
+    assert np.array_equal(got["path"], rv["path"]) and np.array_equal(got["node_accept"], rv["node_accept"])
+    assert [oracle.decode_err(e) for e in rv["err"]] == [(0, 0), (0, oracle.ERR_ROOT), (4, oracle.ERR_PARENT),
+                                                         (5, oracle.ERR_TOKEN), (0, 0), (0, oracle.ERR_NNODES)]
+    assert int(rv["accept_len"][0]) == 4 and int(rv["bonus"][0]) == 4   # path 0 -> 1 -> 3 -> 6 -> 7

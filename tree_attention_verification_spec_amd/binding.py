@@ -50,6 +50,8 @@ def lib():
     L.spec_lm_head_stats_workspace.argtypes = [_I, _I, _I, _I]
     L.spec_lm_head_stats.restype = _I
     L.spec_lm_head_stats.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P]
+    L.spec_verify_greedy_stats.restype = _I
+    L.spec_verify_greedy_stats.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
     L.spec_tree_attn_workspace.restype = _Z
     L.spec_tree_attn_workspace.argtypes = [_I, _I, _I, _I, _I, _I, _I]
     L.spec_tree_attn.restype = _I
@@ -278,6 +280,29 @@ def spec_lm_head_stats(hidden, W, parents, tokens, n_nodes=None, out=None, ws=No
         _ptr(out["cand_logit"], torch.float32, (B, N), "cand_logit"),
         _ptr(out["err"], torch.int32, (B,), "err"), _ptr(ws, None, None, "workspace"), ws.numel(),
         _stream(stream)), "spec_lm_head_stats")
+    return out
+
+
+def spec_verify_greedy_stats(row_argmax, tokens, parents, V, n_nodes=None, max_depth=None, out=None, stream=None):
+    B, N = tokens.shape
+    dev = tokens.device
+    if max_depth is None:
+        max_depth = N - 1
+    if out is None:
+        out = {"accept_len": torch.empty((B,), dtype=torch.int32, device=dev),
+               "path": torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev),
+               "bonus": torch.empty((B,), dtype=torch.int32, device=dev),
+               "node_accept": torch.empty((B, N), dtype=torch.uint8, device=dev),
+               "err": torch.empty((B,), dtype=torch.int32, device=dev)}
+    _check(lib().spec_verify_greedy_stats(
+        _ptr(row_argmax, torch.int32, (B, N), "row_argmax"), _ptr(tokens, torch.int32, (B, N), "tokens"),
+        _ptr(parents, torch.int32, (B, N), "parents"), _ptr(n_nodes, torch.int32, (B,), "n_nodes"),
+        B, N, int(V), int(max_depth),
+        _ptr(out["accept_len"], torch.int32, (B,), "accept_len"),
+        _ptr(out["path"], torch.int32, (B, max_depth + 1), "path"),
+        _ptr(out["bonus"], torch.int32, (B,), "bonus"),
+        _ptr(out.get("node_accept"), torch.uint8, (B, N), "node_accept"),
+        _ptr(out["err"], torch.int32, (B,), "err"), _stream(stream)), "spec_verify_greedy_stats")
     return out
 
 

@@ -323,6 +323,80 @@ __global__ __launch_bounds__(kLThreads) void lmhead_merge_kernel(
   }
 }
 
+
+// Greedy verification from the fused statistics: node c (parent p, token x) is accepted iff
+// x == row_argmax[p]; a node survives iff every node on its path below the root was accepted;
+// m = the deepest survivor (lowest index on ties); bonus = row_argmax[m].  One workgroup per
+// sequence, one thread per node; validation as spec_verify's (node count, root, parent, depth,
+// token), smallest error word first.
+__global__ __launch_bounds__(SPEC_MAX_NODES) void verify_greedy_stats_kernel(
+    const int32_t* __restrict__ row_argmax, const int32_t* __restrict__ tokens,
+    const int32_t* __restrict__ parents, const int32_t* __restrict__ n_nodes, int N, int V,
+    int max_depth, int32_t* __restrict__ accept_len, int32_t* __restrict__ path,
+    int32_t* __restrict__ bonus, uint8_t* __restrict__ node_accept, int32_t* __restrict__ err) {
+  __shared__ int s_par[SPEC_MAX_NODES];
+  __shared__ unsigned char s_acc[SPEC_MAX_NODES];
+  __shared__ int s_err, s_best;
+  const int b = blockIdx.x, c = threadIdx.x;
+  const size_t base = (size_t)b * N;
+  const int n_raw = n_nodes ? n_nodes[b] : N;
+  const bool bad_n = n_raw < 0 || n_raw > N;
+  const int n = bad_n ? 0 : n_raw;
+  if (c == 0) {
+    s_err = INT_MAX;
+    s_best = -1;
+  }
+  if (c < N) s_par[c] = parents[base + c];
+  __syncthreads();
+  int depth = 0;
+  bool acc = false;
+  if (c < n) {
+    const int p = s_par[c];
+    int code = 0;
+    if (c == 0) {
+      if (p != -1) code = SPEC_ERR_ROOT;
+      acc = true;
+    } else if (p < 0 || p >= c) {
+      code = SPEC_ERR_PARENT;
+    } else {
+      int j = c;
+      while (j > 0 && s_par[j] >= 0 && s_par[j] < j) {   // parents strictly decrease: ends
+        j = s_par[j];
+        ++depth;
+      }
+      const int x = tokens[base + c];
+      if (depth > max_depth) code = SPEC_ERR_DEPTH;
+      else if (x < 0 || x >= V) code = SPEC_ERR_TOKEN;
+      else acc = x == row_argmax[base + p];
+    }
+    if (code) atomicMin(&s_err, err_word(c, code));
+    s_acc[c] = acc ? 1 : 0;
+  }
+  __syncthreads();
+  const int e = bad_n ? err_word(0, SPEC_ERR_NNODES) : (s_err == INT_MAX ? 0 : s_err);
+  if (e == 0 && c < n) {
+    bool live = true;
+    for (int j = c; j > 0; j = s_par[j]) live = live && s_acc[j];
+    if (live) atomicMax(&s_best, (depth << 9) | (511 - c));
+  }
+  __syncthreads();
+  if (c < N && node_accept) node_accept[base + c] = (e == 0 && c < n) ? s_acc[c] : 0;
+  if (c == 0) {
+    int32_t* pr = path + (size_t)b * (max_depth + 1);
+    for (int k = 0; k <= max_depth; ++k) pr[k] = -1;
+    int len = 0, tok = -1;
+    if (e == 0 && n > 0) {
+      const int m = 511 - (s_best & 511);
+      len = s_best >> 9;
+      for (int j = m, k = len; k >= 0; --k, j = s_par[j]) pr[k] = j;
+      tok = row_argmax[base + m];
+    }
+    accept_len[b] = len;
+    bonus[b] = tok;
+    err[b] = e;
+  }
+}
+
 }  // namespace
 }  // namespace spectree
 
@@ -383,5 +457,18 @@ extern "C" spec_status spec_lm_head_stats(const void* hidden, const void* W, con
   else launch(nm, lmhead_stats_kernel<4>, g1, blk, s, Wb, Xp, M, Dm, V, N, parents, tokens, parts, gath);
   launch("lm_head_merge", lmhead_merge_kernel, dim3((unsigned)M), blk, s, parts, gath, L.nblk, N, V,
          parents, tokens, n_nodes, row_max, row_argmax, row_sum, row_ent, cand_logit, err);
+  return launch_status();
+}
+
+extern "C" spec_status spec_verify_greedy_stats(const int32_t* row_argmax, const int32_t* tokens,
+                                                const int32_t* parents, const int32_t* n_nodes, int B,
+                                                int N, int V, int max_depth, int32_t* accept_len,
+                                                int32_t* path, int32_t* bonus_token,
+                                                uint8_t* node_accept, int32_t* err, void* stream) {
+  if (B < 1 || N < 1 || N > SPEC_MAX_NODES || V < 1 || max_depth < 0) return SPEC_EINVAL;
+  if (!row_argmax || !tokens || !parents || !accept_len || !path || !bonus_token || !err) return SPEC_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  launch("verify_greedy_stats", verify_greedy_stats_kernel, dim3(B), dim3(SPEC_MAX_NODES), s, row_argmax, tokens,
+         parents, n_nodes, N, V, max_depth, accept_len, path, bonus_token, node_accept, err);
   return launch_status();
 }
