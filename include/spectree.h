@@ -293,8 +293,8 @@ spec_status spec_tree_select(const int32_t* cand_parents, const float* cand_prob
  *   sequence with an error get NaN (argmax -1).
  * The workspace (spec_lm_head_stats_workspace bytes) holds one partial per (row, 64 tokens) and
  * a copy of the hidden states in the order the matrix-core fragments read them.
- * Supported: B * N <= 64, Dm a multiple of 128.
- * Errors: SPEC_EINVAL (sizes, NULL pointers), SPEC_EUNSUPPORTED (B * N, Dm, alignment),
+ * Supported: N <= 256, B * N <= 4096, Dm a multiple of 128.
+ * Errors: SPEC_EINVAL (sizes, NULL pointers), SPEC_EUNSUPPORTED (N, B * N, Dm, alignment),
  * SPEC_EWORKSPACE.
  * ------------------------------------------------------------------------------------ */
 size_t spec_lm_head_stats_workspace(int B, int N, int Dm, int V);

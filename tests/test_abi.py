@@ -139,7 +139,8 @@ def test_lm_head_stats_argument_checks(lib):
 
     assert call(h=None) == 1 and call(W=None) == 1 and call(out=None) == 1
     assert call(B=0) == 1 and call(V=0) == 1
-    assert call(B=2, N=33) == 2                          # more than 64 rows
+    assert call(B=17, N=256) == 2                        # more than 4096 rows
+    assert call(B=1, N=257) == 2                         # more than 256 nodes
     assert call(Dm=4000) == 2                            # not a multiple of 128
     assert call(h=odd) == 2 and call(W=odd) == 2         # alignment
     assert call(wsz=ws - 1) == 3 and call(wsp=None) == 3

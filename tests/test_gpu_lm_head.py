@@ -76,7 +76,8 @@ def run_both(inp, n_nodes=None, what=""):
 
 @pytest.mark.parametrize("B,N,Dm,V", [(1, 1, 128, 1), (1, 5, 128, 37), (1, 16, 128, 64), (1, 17, 256, 65),
                                       (2, 16, 256, 1000), (3, 11, 128, 5000), (4, 16, 384, 2048),
-                                      (1, 64, 512, 4099)])
+                                      (1, 64, 512, 4099), (1, 65, 128, 700), (2, 256, 256, 1500),
+                                      (8, 127, 512, 4099), (16, 127, 256, 3000)])
 def test_small(B, N, Dm, V):
     inp = wl.lm_head_inputs(seed=40 + B + N + V, B=B, N=N, Dm=Dm, V=V)
     run_both(inp, what=f"small {B}x{N} Dm{Dm} V{V}")
@@ -110,7 +111,8 @@ def test_llama3_8b_shape():
     run_both(inp, what="llama3-8b B1 N63")
 
 
-@pytest.mark.parametrize("seed,B,N,Dm,V", [(21, 1, 63, 4096, 128256), (22, 4, 16, 512, 3000), (23, 2, 30, 256, 777)])
+@pytest.mark.parametrize("seed,B,N,Dm,V", [(21, 1, 63, 4096, 128256), (22, 4, 16, 512, 3000), (23, 2, 30, 256, 777),
+                                            (24, 16, 127, 256, 2000)])
 def test_greedy_round_from_statistics(seed, B, N, Dm, V):
     """LM head statistics then greedy verification, both on the GPU, against the oracle's logits
     through oracle.verify (GREEDY).  Candidate tokens are the oracle's argmax of the parent's row

@@ -9,10 +9,11 @@
 // logit in its parent's row, so the logits are reduced where they are produced and the
 // B x N x V logits array is never written.
 //
-// lmhead_stats_kernel: grid ceil(V / 64); a workgroup multiplies 64 rows of W (four 16-row
-// blocks, A operand of v_mfma_f32_16x16x32_bf16, 16-byte loads streamed from HBM) with all
-// M = B * N <= 64 hidden states (up to four 16-column blocks, B operand, L2-resident), K split
-// over the four waves and summed in LDS.  The 64 x M logits tile then stays in LDS: per column,
+// lmhead_stats_kernel: grid ceil(V / 64) x ceil(M / 64); a workgroup multiplies 64 rows of W
+// (four 16-row blocks, A operand of v_mfma_f32_16x16x32_bf16, 16-byte loads) with up to 64 of
+// the M = B * N hidden states (up to four 16-column blocks, B operand, L2-resident), K split over
+// the four waves and summed in LDS.  With more than 64 hidden states the column blocks of one W
+// tile are placed on one XCD, so the tile comes from HBM once and from that XCD's L2 after.  The 64 x M logits tile then stays in LDS: per column,
 // four threads reduce (max, lowest argmax) and then fp64 sums of fp32 exp(l - max), and the
 // candidates whose token falls in the tile pick their parent's logit.  Partials go to the
 // workspace, one per (column, tile).
@@ -34,7 +35,8 @@ constexpr int kLThreads = 256;
 constexpr int kLKWaves = 4;                 // K slices per workgroup
 constexpr int kLRB = 4;                     // 16-row blocks of W per workgroup
 constexpr int kLRows = 16 * kLRB;           // vocabulary rows per workgroup
-constexpr int kLMaxCols = 64;               // B * N limit
+constexpr int kLMaxCols = 64;               // hidden states (columns) per workgroup
+constexpr int kLMaxRows = 4096;             // B * N limit
 constexpr int kMergePer = 8;                // partials per merging thread held in registers
 
 struct LmPart {       // one 64-token tile of one row
@@ -49,7 +51,7 @@ __device__ __forceinline__ bf16x8 ld8(const __bf16* p) { return *reinterpret_cas
 template <int CBN>
 __global__ __launch_bounds__(kLThreads) void lmhead_stats_kernel(
     const __bf16* __restrict__ W, const __bf16* __restrict__ Xp, int M, int Dm, int V, int N,
-    const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
+    int nblk, int ncb, const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
     LmPart* __restrict__ parts, float* __restrict__ gath) {
   // the K-slice partials and, once they are summed, the logits tile share one LDS block, so
   // two workgroups fit a CU
@@ -60,7 +62,12 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_kernel(
   auto tile = reinterpret_cast<float (*)[kLMaxCols + 1]>(lds);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int row0 = blockIdx.x * kLRows;
+  // Workgroup id -> (W tile, column block): the ncb column blocks of a tile share id % 8, so
+  // they run on one XCD (dispatch is round-robin over the 8) and read the tile through its L2.
+  const int grp = blockIdx.x / (8 * ncb), rem = blockIdx.x - grp * 8 * ncb;
+  const int tidx = grp * 8 + (rem & 7), cblk = rem >> 3;
+  if (tidx >= nblk) return;
+  const int row0 = tidx * kLRows, col0 = cblk * kLMaxCols;
   const int kslice = Dm / kLKWaves;
   const int kbeg = wave * kslice;
   // branch-free loads: rows past V and columns past M read the last valid one (never stored)
@@ -73,7 +80,7 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_kernel(
   const __bf16* bptr[CBN];
 #pragma unroll
   for (int cb = 0; cb < CBN; ++cb)
-    bptr[cb] = Xp + ((size_t)(kbeg / 8 + lg) * M + min(cb * 16 + l16, M - 1)) * 8;
+    bptr[cb] = Xp + ((size_t)(kbeg / 8 + lg) * M + min(col0 + cb * 16 + l16, M - 1)) * 8;
   f32x4 acc[kLRB][CBN];
 #pragma unroll
   for (int rb = 0; rb < kLRB; ++rb)
@@ -178,14 +185,18 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_kernel(
     S += __shfl_xor(S, o);
     A += __shfl_xor(A, o);
   }
-  if (q == 0 && col < M) parts[(size_t)col * gridDim.x + blockIdx.x] = LmPart{S, A, m, am};
+  if (q == 0 && col0 + col < M) parts[(size_t)(col0 + col) * nblk + tidx] = LmPart{S, A, m, am};
 
-  // the candidates whose token lies in this tile take their parent's logit
-  for (int c = threadIdx.x; c < M; c += kLThreads) {
+  // the candidates whose parent's column is in this block and whose token lies in this tile take
+  // their parent's logit (only the sequences overlapping the block are scanned)
+  const int c_lo = (col0 / N) * N, c_hi = min(M, (min(col0 + kLMaxCols, M) - 1) / N * N + N);
+  for (int c = c_lo + threadIdx.x; c < c_hi; c += kLThreads) {
     const int i = c % N;
     if (i == 0) continue;
     const int p = parents[c], x = tokens[c];
-    if (p >= 0 && p < i && x >= row0 && x < row0 + kLRows && x < V) gath[c] = tile[x - row0][c - i + p];
+    const int pc = c - i + p;
+    if (p >= 0 && p < i && pc >= col0 && pc < col0 + kLMaxCols && x >= row0 && x < row0 + kLRows && x < V)
+      gath[c] = tile[x - row0][pc - col0];
   }
 }
 
@@ -433,8 +444,9 @@ extern "C" spec_status spec_lm_head_stats(const void* hidden, const void* W, con
   if (!hidden || !W || !parents || !tokens || !row_max || !row_argmax || !row_sum || !row_ent ||
       !cand_logit || !err)
     return SPEC_EINVAL;
+  if (N > SPEC_MAX_NODES || (size_t)B * N > (size_t)kLMaxRows) return SPEC_EUNSUPPORTED;
   const int M = B * N;
-  if (M > kLMaxCols || Dm % 128 != 0) return SPEC_EUNSUPPORTED;
+  if (Dm % 128 != 0) return SPEC_EUNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(hidden) & 15) || (reinterpret_cast<uintptr_t>(W) & 15))
     return SPEC_EUNSUPPORTED;
   const LmLayout L = lm_layout(B, N, V, Dm);
@@ -446,15 +458,17 @@ extern "C" spec_status spec_lm_head_stats(const void* hidden, const void* W, con
   __bf16* Xp = reinterpret_cast<__bf16*>(w + L.xperm);
   const __bf16* Wb = static_cast<const __bf16*>(W);
   const __bf16* X = static_cast<const __bf16*>(hidden);
-  const dim3 g1((unsigned)L.nblk), blk(kLThreads);
+  const int ncb = (M + kLMaxCols - 1) / kLMaxCols;
+  const dim3 g1((unsigned)((L.nblk + 7) / 8 * 8 * ncb)), blk(kLThreads);
   const int nchunk = M * (Dm / 8);
   launch("lm_head_xperm", lmhead_xperm_kernel, dim3((unsigned)((nchunk + kLThreads - 1) / kLThreads)), blk, s, X,
          M, Dm, Xp);
   const char* nm = "lm_head_stats";
-  if (M <= 16) launch(nm, lmhead_stats_kernel<1>, g1, blk, s, Wb, Xp, M, Dm, V, N, parents, tokens, parts, gath);
-  else if (M <= 32) launch(nm, lmhead_stats_kernel<2>, g1, blk, s, Wb, Xp, M, Dm, V, N, parents, tokens, parts, gath);
-  else if (M <= 48) launch(nm, lmhead_stats_kernel<3>, g1, blk, s, Wb, Xp, M, Dm, V, N, parents, tokens, parts, gath);
-  else launch(nm, lmhead_stats_kernel<4>, g1, blk, s, Wb, Xp, M, Dm, V, N, parents, tokens, parts, gath);
+  const int nb = L.nblk;
+  if (M <= 16) launch(nm, lmhead_stats_kernel<1>, g1, blk, s, Wb, Xp, M, Dm, V, N, nb, ncb, parents, tokens, parts, gath);
+  else if (M <= 32) launch(nm, lmhead_stats_kernel<2>, g1, blk, s, Wb, Xp, M, Dm, V, N, nb, ncb, parents, tokens, parts, gath);
+  else if (M <= 48) launch(nm, lmhead_stats_kernel<3>, g1, blk, s, Wb, Xp, M, Dm, V, N, nb, ncb, parents, tokens, parts, gath);
+  else launch(nm, lmhead_stats_kernel<4>, g1, blk, s, Wb, Xp, M, Dm, V, N, nb, ncb, parents, tokens, parts, gath);
   launch("lm_head_merge", lmhead_merge_kernel, dim3((unsigned)M), blk, s, parts, gath, L.nblk, N, V,
          parents, tokens, n_nodes, row_max, row_argmax, row_sum, row_ent, cand_logit, err);
   return launch_status();
