@@ -200,6 +200,111 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_kernel(
   }
 }
 
+// More than 64 hidden states: every 64-row W tile meets all of them, so what bounds the kernel
+// above is re-reading the hidden states (16 MB at 2032 rows) once per 64 W rows.  Here a
+// workgroup covers 256 W rows x 64 columns: each wave owns 64 W rows over the whole K (no K
+// split, no LDS reduction) and the four waves read the same B fragments, so the column block is
+// fetched into the CU once per 256 W rows.  The tiles are then written to LDS (one 64 x 64 tile
+// per wave) and reduced per column by the wave's 64 lanes, with the same partials and gathers
+// as above.
+constexpr int kWRowsPerWave = 64;
+constexpr int kWRows = kWRowsPerWave * kLKWaves;   // W rows per workgroup
+
+__global__ __launch_bounds__(kLThreads) void lmhead_stats_wide_kernel(
+    const __bf16* __restrict__ W, const __bf16* __restrict__ Xp, int M, int Dm, int V, int N,
+    int nblk, int ntile, int ncb, const int32_t* __restrict__ parents,
+    const int32_t* __restrict__ tokens, LmPart* __restrict__ parts, float* __restrict__ gath) {
+  __shared__ float tile[kLKWaves][kWRowsPerWave][kLMaxCols + 1];
+  constexpr int RB = kWRowsPerWave / 16, CBN = kLMaxCols / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int grp = blockIdx.x / (8 * ncb), rem = blockIdx.x - grp * 8 * ncb;
+  const int tidx = grp * 8 + (rem & 7), cblk = rem >> 3;
+  if (tidx >= ntile) return;
+  const int wrow0 = tidx * kWRows + wave * kWRowsPerWave, col0 = cblk * kLMaxCols;
+  const __bf16* arow[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+    arow[rb] = W + (size_t)min(wrow0 + rb * 16 + l16, V - 1) * Dm + 8 * lg;
+  const __bf16* bptr[CBN];
+#pragma unroll
+  for (int cb = 0; cb < CBN; ++cb) bptr[cb] = Xp + ((size_t)lg * M + min(col0 + cb * 16 + l16, M - 1)) * 8;
+  f32x4 acc[RB][CBN];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CBN; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  struct Frags {
+    bf16x8 a[RB];
+    bf16x8 b[CBN];
+  };
+  auto fetch = [&](Frags& f, int s) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) f.a[rb] = ld8(arow[rb] + s * 32);
+#pragma unroll
+    for (int cb = 0; cb < CBN; ++cb) f.b[cb] = ld8(bptr[cb] + (size_t)s * 32 * M);
+  };
+  auto products = [&](const Frags& f) {
+#pragma unroll
+    for (int cb = 0; cb < CBN; ++cb)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[rb], f.b[cb], acc[rb][cb], 0, 0, 0);
+  };
+  constexpr int NB = 3;
+  const int steps = Dm / 32;
+  Frags f[NB];
+#pragma unroll
+  for (int u = 0; u < NB - 1; ++u) fetch(f[u], min(u, steps - 1));
+  for (int s = 0; s < steps; s += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      fetch(f[(u + NB - 1) % NB], min(s + u + NB - 1, steps - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + u < steps) products(f[u]);
+    }
+  }
+  float (*tw)[kLMaxCols + 1] = tile[wave];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CBN; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tw[rb * 16 + 4 * lg + e][cb * 16 + l16] = acc[rb][cb][e];
+  __syncthreads();
+  // lane = column: max and lowest argmax over the wave's 64 rows, then fp64 sums
+  const int col = lane;
+  float m = -INFINITY;
+  int am = INT_MAX;
+  for (int vr = 0; vr < kWRowsPerWave; ++vr) {
+    const float x = tw[vr][col];
+    if (wrow0 + vr < V && x > m) {
+      m = x;
+      am = wrow0 + vr;
+    }
+  }
+  double S = 0.0, A = 0.0;
+  if (m != -INFINITY) {
+    for (int vr = 0; vr < kWRowsPerWave && wrow0 + vr < V; ++vr) {
+      const float d = tw[vr][col] - m;
+      const double e = (double)expf(d);
+      S += e;
+      A += e * (double)d;
+    }
+  }
+  const int wt = tidx * kLKWaves + wave;          // this wave's 64-row tile among the nblk
+  if (col0 + col < M && wt < nblk) parts[(size_t)(col0 + col) * nblk + wt] = LmPart{S, A, m, am};
+  const int c_lo = (col0 / N) * N, c_hi = min(M, (min(col0 + kLMaxCols, M) - 1) / N * N + N);
+  for (int c = c_lo + lane; c < c_hi; c += kWave) {
+    const int i = c % N;
+    if (i == 0) continue;
+    const int p = parents[c], x = tokens[c];
+    const int pc = c - i + p;
+    if (p >= 0 && p < i && pc >= col0 && pc < col0 + kLMaxCols && x >= wrow0 && x < wrow0 + kWRowsPerWave && x < V)
+      gath[c] = tw[x - wrow0][pc - col0];
+  }
+}
+
 // The hidden states [M, Dm] into fragment order (see lmhead_stats_kernel), 16 bytes per thread.
 __global__ __launch_bounds__(kLThreads) void lmhead_xperm_kernel(const __bf16* __restrict__ X, int M, int Dm,
                                                                  __bf16* __restrict__ Xp) {
@@ -465,7 +570,11 @@ extern "C" spec_status spec_lm_head_stats(const void* hidden, const void* W, con
          M, Dm, Xp);
   const char* nm = "lm_head_stats";
   const int nb = L.nblk;
-  if (M <= 16) launch(nm, lmhead_stats_kernel<1>, g1, blk, s, Wb, Xp, M, Dm, V, N, nb, ncb, parents, tokens, parts, gath);
+  if (M > kLMaxCols) {
+    const int ntile = (V + kWRows - 1) / kWRows;
+    const dim3 gw((unsigned)((ntile + 7) / 8 * 8 * ncb));
+    launch(nm, lmhead_stats_wide_kernel, gw, blk, s, Wb, Xp, M, Dm, V, N, nb, ntile, ncb, parents, tokens, parts, gath);
+  } else if (M <= 16) launch(nm, lmhead_stats_kernel<1>, g1, blk, s, Wb, Xp, M, Dm, V, N, nb, ncb, parents, tokens, parts, gath);
   else if (M <= 32) launch(nm, lmhead_stats_kernel<2>, g1, blk, s, Wb, Xp, M, Dm, V, N, nb, ncb, parents, tokens, parts, gath);
   else if (M <= 48) launch(nm, lmhead_stats_kernel<3>, g1, blk, s, Wb, Xp, M, Dm, V, N, nb, ncb, parents, tokens, parts, gath);
   else launch(nm, lmhead_stats_kernel<4>, g1, blk, s, Wb, Xp, M, Dm, V, N, nb, ncb, parents, tokens, parts, gath);
