@@ -305,6 +305,131 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_wide_kernel(
   }
 }
 
+// More than 128 hidden states: a 128 x 128 tile per workgroup (waves in 2 x 2, each 64 W rows x
+// 64 columns), both operands staged through LDS once per workgroup and K step (16-byte global
+// loads for the next step requested before this step's products, two LDS buffers in turn, one
+// barrier per step).  Per 32-wide K step a workgroup moves 16 KB for 64 products instead of the
+// 32 KB the 256-row kernel's waves fetch separately.
+constexpr int kGT = 128;                 // tile edge (W rows and columns)
+constexpr int kGS = 40;                  // LDS row stride in bf16 (32 + 8: rows 80 bytes apart)
+
+__global__ __launch_bounds__(kLThreads) void lmhead_stats_gemm_kernel(
+    const __bf16* __restrict__ W, const __bf16* __restrict__ Xp, int M, int Dm, int V, int N,
+    int nblk, int ntile, int ncb, const int32_t* __restrict__ parents,
+    const int32_t* __restrict__ tokens, LmPart* __restrict__ parts, float* __restrict__ gath) {
+  constexpr size_t kStageBytes = sizeof(__bf16) * 2 * 2 * kGT * kGS;               // [buf][A|B]
+  constexpr size_t kTileBytes = sizeof(float) * kLKWaves * 64 * (kLMaxCols + 1);
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kStageBytes > kTileBytes ? kStageBytes : kTileBytes];
+  auto stage = reinterpret_cast<__bf16 (*)[2][kGT][kGS]>(lds);                        // [buf][0 A / 1 B]
+  auto tiles = reinterpret_cast<float (*)[64][kLMaxCols + 1]>(lds);
+  constexpr int RB = 4, CBN = 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int grp = blockIdx.x / (8 * ncb), rem = blockIdx.x - grp * 8 * ncb;
+  const int tidx = grp * 8 + (rem & 7), cblk = rem >> 3;
+  if (tidx >= ntile) return;
+  const int row0 = tidx * kGT, col0 = cblk * kGT;
+  // staging: thread t moves chunks q = t and t + 256 of A (row q / 4, k chunk q % 4) and of B
+  // (k chunk q / 128, column q % 128), 16 bytes each
+  const __bf16* ga[2];
+  const __bf16* gb[2];
+  int ar[2], ak[2], bc[2], bk[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int q = threadIdx.x + j * kLThreads;
+    ar[j] = q >> 2;
+    ak[j] = (q & 3) * 8;
+    ga[j] = W + (size_t)min(row0 + ar[j], V - 1) * Dm + ak[j];
+    bk[j] = q >> 7;
+    bc[j] = q & 127;
+    gb[j] = Xp + ((size_t)bk[j] * M + min(col0 + bc[j], M - 1)) * 8;
+  }
+  bf16x8 ra[2], rb[2];
+  auto load = [&](int s) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      ra[j] = ld8(ga[j] + (size_t)s * 32);
+      rb[j] = ld8(gb[j] + (size_t)s * 4 * M * 8);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      *reinterpret_cast<bf16x8*>(&stage[buf][0][ar[j]][ak[j]]) = ra[j];
+      *reinterpret_cast<bf16x8*>(&stage[buf][1][bc[j]][bk[j] * 8]) = rb[j];
+    }
+  };
+  f32x4 acc[RB][CBN];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int cb = 0; cb < CBN; ++cb) acc[i][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int steps = Dm / 32;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int s = 0; s < steps; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < steps) load(s + 1);
+    bf16x8 fa[RB], fb[CBN];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(&stage[buf][0][wr * 64 + i * 16 + l16][8 * lg]);
+#pragma unroll
+    for (int cb = 0; cb < CBN; ++cb)
+      fb[cb] = *reinterpret_cast<const bf16x8*>(&stage[buf][1][wc * 64 + cb * 16 + l16][8 * lg]);
+#pragma unroll
+    for (int cb = 0; cb < CBN; ++cb)
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+        acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[cb], acc[i][cb], 0, 0, 0);
+    if (s + 1 < steps) store(buf ^ 1);
+    __syncthreads();
+  }
+  // each wave's 64 x 64 tile to LDS (over the staging buffers, after the last barrier)
+  float (*tw)[kLMaxCols + 1] = tiles[wave];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int cb = 0; cb < CBN; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tw[i * 16 + 4 * lg + e][cb * 16 + l16] = acc[i][cb][e];
+  __syncthreads();
+  const int wrow0 = row0 + wr * 64, wcol0 = col0 + wc * 64;
+  const int col = lane;
+  float m = -INFINITY;
+  int am = INT_MAX;
+  for (int vr = 0; vr < 64; ++vr) {
+    const float x = tw[vr][col];
+    if (wrow0 + vr < V && x > m) {
+      m = x;
+      am = wrow0 + vr;
+    }
+  }
+  double S = 0.0, A = 0.0;
+  if (m != -INFINITY) {
+    for (int vr = 0; vr < 64 && wrow0 + vr < V; ++vr) {
+      const float d = tw[vr][col] - m;
+      const double e = (double)expf(d);
+      S += e;
+      A += e * (double)d;
+    }
+  }
+  const int wt = wrow0 / 64;
+  if (wcol0 + col < M && wt < nblk) parts[(size_t)(wcol0 + col) * nblk + wt] = LmPart{S, A, m, am};
+  if (wcol0 < M) {
+    const int c_lo = (wcol0 / N) * N, c_hi = min(M, (min(wcol0 + kLMaxCols, M) - 1) / N * N + N);
+    for (int c = c_lo + lane; c < c_hi; c += kWave) {
+      const int i = c % N;
+      if (i == 0) continue;
+      const int p = parents[c], x = tokens[c];
+      const int pc = c - i + p;
+      if (p >= 0 && p < i && pc >= wcol0 && pc < wcol0 + kLMaxCols && x >= wrow0 && x < wrow0 + 64 && x < V)
+        gath[c] = tw[x - wrow0][pc - wcol0];
+    }
+  }
+}
+
 // The hidden states [M, Dm] into fragment order (see lmhead_stats_kernel), 16 bytes per thread.
 __global__ __launch_bounds__(kLThreads) void lmhead_xperm_kernel(const __bf16* __restrict__ X, int M, int Dm,
                                                                  __bf16* __restrict__ Xp) {
@@ -570,7 +695,11 @@ extern "C" spec_status spec_lm_head_stats(const void* hidden, const void* W, con
          M, Dm, Xp);
   const char* nm = "lm_head_stats";
   const int nb = L.nblk;
-  if (M > kLMaxCols) {
+  if (M > 2 * kLMaxCols) {
+    const int ntile = (V + kGT - 1) / kGT, ncb2 = (M + kGT - 1) / kGT;
+    const dim3 gg((unsigned)((ntile + 7) / 8 * 8 * ncb2));
+    launch(nm, lmhead_stats_gemm_kernel, gg, blk, s, Wb, Xp, M, Dm, V, N, nb, ntile, ncb2, parents, tokens, parts, gath);
+  } else if (M > kLMaxCols) {
     const int ntile = (V + kWRows - 1) / kWRows;
     const dim3 gw((unsigned)((ntile + 7) / 8 * 8 * ncb));
     launch(nm, lmhead_stats_wide_kernel, gw, blk, s, Wb, Xp, M, Dm, V, N, nb, ntile, ncb, parents, tokens, parts, gath);
