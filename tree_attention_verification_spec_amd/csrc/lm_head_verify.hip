@@ -365,13 +365,19 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_gemm_kernel(
   for (int i = 0; i < RB; ++i)
 #pragma unroll
     for (int cb = 0; cb < CBN; ++cb) acc[i][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Step s: the registers (step s + 1, requested a whole step earlier) go to the other LDS
+  // buffer first, then step s + 2 is requested, then step s's products run.  Storing before
+  // requesting keeps the wait for the stored loads exact (the memory counter drains in issue
+  // order, so a wait issued behind newer loads would wait for those too).
   const int steps = Dm / 32;
   load(0);
   store(0);
+  load(min(1, steps - 1));
   __syncthreads();
   for (int s = 0; s < steps; ++s) {
     const int buf = s & 1;
-    if (s + 1 < steps) load(s + 1);
+    if (s + 1 < steps) store(buf ^ 1);
+    if (s + 2 < steps) load(s + 2);
     bf16x8 fa[RB], fb[CBN];
 #pragma unroll
     for (int i = 0; i < RB; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(&stage[buf][0][wr * 64 + i * 16 + l16][8 * lg]);
@@ -383,7 +389,6 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_gemm_kernel(
 #pragma unroll
       for (int i = 0; i < RB; ++i)
         acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[cb], acc[i][cb], 0, 0, 0);
-    if (s + 1 < steps) store(buf ^ 1);
     __syncthreads();
   }
   // each wave's 64 x 64 tile to LDS (over the staging buffers, after the last barrier)
