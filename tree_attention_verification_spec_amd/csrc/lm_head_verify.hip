@@ -305,6 +305,48 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_wide_kernel(
   }
 }
 
+// Per-column reduction of one wave's 64 x 64 logits tile in LDS (lane = column): the (row,
+// 64-row tile) partial and the gathers of the candidates whose parent's column and token fall in
+// the tile.
+__device__ __forceinline__ void wave_tile_epilogue(float (*tw)[kLMaxCols + 1], int wrow0, int wcol0, int M,
+                                                   int V, int N, int nblk, const int32_t* __restrict__ parents,
+                                                   const int32_t* __restrict__ tokens, LmPart* __restrict__ parts,
+                                                   float* __restrict__ gath) {
+  const int lane = threadIdx.x & 63;
+  const int col = lane;
+  float m = -INFINITY;
+  int am = INT_MAX;
+  for (int vr = 0; vr < 64; ++vr) {
+    const float x = tw[vr][col];
+    if (wrow0 + vr < V && x > m) {
+      m = x;
+      am = wrow0 + vr;
+    }
+  }
+  double S = 0.0, A = 0.0;
+  if (m != -INFINITY) {
+    for (int vr = 0; vr < 64 && wrow0 + vr < V; ++vr) {
+      const float d = tw[vr][col] - m;
+      const double e = (double)expf(d);
+      S += e;
+      A += e * (double)d;
+    }
+  }
+  const int wt = wrow0 / 64;
+  if (wcol0 + col < M && wt < nblk) parts[(size_t)(wcol0 + col) * nblk + wt] = LmPart{S, A, m, am};
+  if (wcol0 < M) {
+    const int c_lo = (wcol0 / N) * N, c_hi = min(M, (min(wcol0 + kLMaxCols, M) - 1) / N * N + N);
+    for (int c = c_lo + lane; c < c_hi; c += kWave) {
+      const int i = c % N;
+      if (i == 0) continue;
+      const int p = parents[c], x = tokens[c];
+      const int pc = c - i + p;
+      if (p >= 0 && p < i && pc >= wcol0 && pc < wcol0 + kLMaxCols && x >= wrow0 && x < wrow0 + 64 && x < V)
+        gath[c] = tw[x - wrow0][pc - wcol0];
+    }
+  }
+}
+
 // More than 128 hidden states: a 128 x 128 tile per workgroup (waves in 2 x 2, each 64 W rows x
 // 64 columns), both operands staged through LDS once per workgroup and K step (16-byte global
 // loads for the next step requested before this step's products, two LDS buffers in turn, one
@@ -318,7 +360,7 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_gemm_kernel(
     int nblk, int ntile, int ncb, const int32_t* __restrict__ parents,
     const int32_t* __restrict__ tokens, LmPart* __restrict__ parts, float* __restrict__ gath) {
   constexpr size_t kStageBytes = sizeof(__bf16) * 2 * 2 * kGT * kGS;               // [buf][A|B]
-  constexpr size_t kTileBytes = sizeof(float) * kLKWaves * 64 * (kLMaxCols + 1);
+  constexpr size_t kTileBytes = sizeof(float) * 2 * 64 * (kLMaxCols + 1);          // two waves at a time
   __shared__ __attribute__((aligned(16))) unsigned char lds[kStageBytes > kTileBytes ? kStageBytes : kTileBytes];
   auto stage = reinterpret_cast<__bf16 (*)[2][kGT][kGS]>(lds);                        // [buf][0 A / 1 B]
   auto tiles = reinterpret_cast<float (*)[64][kLMaxCols + 1]>(lds);
@@ -391,47 +433,22 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_gemm_kernel(
         acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[cb], acc[i][cb], 0, 0, 0);
     __syncthreads();
   }
-  // each wave's 64 x 64 tile to LDS (over the staging buffers, after the last barrier)
-  float (*tw)[kLMaxCols + 1] = tiles[wave];
+  // each wave's 64 x 64 tile to LDS (over the staging buffers, after the last barrier), two
+  // waves at a time so that the block stays at the staging size (three workgroups per CU)
+  float (*tw)[kLMaxCols + 1] = tiles[wave & 1];
+  for (int half = 0; half < 2; ++half) {
+    if ((wave >> 1) == half) {
 #pragma unroll
-  for (int i = 0; i < RB; ++i)
+      for (int i = 0; i < RB; ++i)
 #pragma unroll
-    for (int cb = 0; cb < CBN; ++cb)
+        for (int cb = 0; cb < CBN; ++cb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) tw[i * 16 + 4 * lg + e][cb * 16 + l16] = acc[i][cb][e];
-  __syncthreads();
-  const int wrow0 = row0 + wr * 64, wcol0 = col0 + wc * 64;
-  const int col = lane;
-  float m = -INFINITY;
-  int am = INT_MAX;
-  for (int vr = 0; vr < 64; ++vr) {
-    const float x = tw[vr][col];
-    if (wrow0 + vr < V && x > m) {
-      m = x;
-      am = wrow0 + vr;
+          for (int e = 0; e < 4; ++e) tw[i * 16 + 4 * lg + e][cb * 16 + l16] = acc[i][cb][e];
     }
-  }
-  double S = 0.0, A = 0.0;
-  if (m != -INFINITY) {
-    for (int vr = 0; vr < 64 && wrow0 + vr < V; ++vr) {
-      const float d = tw[vr][col] - m;
-      const double e = (double)expf(d);
-      S += e;
-      A += e * (double)d;
-    }
-  }
-  const int wt = wrow0 / 64;
-  if (wcol0 + col < M && wt < nblk) parts[(size_t)(wcol0 + col) * nblk + wt] = LmPart{S, A, m, am};
-  if (wcol0 < M) {
-    const int c_lo = (wcol0 / N) * N, c_hi = min(M, (min(wcol0 + kLMaxCols, M) - 1) / N * N + N);
-    for (int c = c_lo + lane; c < c_hi; c += kWave) {
-      const int i = c % N;
-      if (i == 0) continue;
-      const int p = parents[c], x = tokens[c];
-      const int pc = c - i + p;
-      if (p >= 0 && p < i && pc >= wcol0 && pc < wcol0 + kLMaxCols && x >= wrow0 && x < wrow0 + 64 && x < V)
-        gath[c] = tw[x - wrow0][pc - wcol0];
-    }
+    __syncthreads();
+    if ((wave >> 1) == half) wave_tile_epilogue(tw, row0 + wr * 64, col0 + wc * 64, M, V, N, nblk, parents,
+                                                tokens, parts, gath);
+    __syncthreads();
   }
 }
 
