@@ -1,0 +1,99 @@
+"""The entry points inside a captured HIP graph: a verification step (tree build, tree attention,
+rejection and walk verification), a tree selection and a fused LM head with greedy verification
+are captured once with preallocated outputs and workspaces, replayed three times with unrelated
+eager work and synchronisations in between, and every replay's outputs must equal the eager
+call's bit for bit (the kernels are deterministic: no atomics decide a floating-point sum)."""
+
+import pytest
+import torch
+
+from tree_attention_verification_spec_amd import binding as sb
+from tree_attention_verification_spec_amd import workloads as wl
+
+from gpu_util import dev, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def snapshot(outs):
+    flat = {}
+    for name, d in outs.items():
+        for k, v in d.items():
+            if isinstance(v, torch.Tensor):
+                flat[f"{name}.{k}"] = v.clone()
+    return flat
+
+
+def test_graph_replays_match_eager():
+    need_gpu()
+    torch.cuda.set_device(0)
+    w = wl.custom(seed=31, B=2, N=37, Hq=8, Hkv=2, d=128, prefix=("uniform", 60, 333), tree=("random", 5), V=5000)
+    a = wl.attention_inputs(w)
+    vi = wl.verify_inputs(w, a["parents"])
+    pool = wl.random_pool(seed=32, B=2, C=300)
+    lm = wl.lm_head_inputs(seed=33, B=2, N=40, Dm=256, V=3000)
+
+    P, par, nn = dev(a["prefix_len"]), dev(a["parents"]), dev(a["n_nodes"])
+    q, k, v = (dev(a[x], torch.bfloat16) for x in ("q", "k_cache", "v_cache"))
+    logits, toks, unif = dev(vi["target_logits"]), dev(vi["tokens"]), dev(vi["uniforms"])
+    draft, drow = dev(vi["draft_probs"]), dev(vi["draft_row"])
+    cp, cprob, ct, cr = (dev(pool[x]) for x in ("cand_parents", "cand_prob", "cand_tokens", "cand_row"))
+    h, W = dev(lm["hidden"], torch.bfloat16), dev(lm["W"], torch.bfloat16)
+    lpar, ltok = dev(lm["parents"]), dev(lm["tokens"])
+    B, N = w.B, w.N
+    S_max = a["k_cache"].shape[2]
+    ws_attn = sb.workspace(sb.tree_attn_workspace_bytes(B, N, w.Hq, w.Hkv, w.d, S_max, torch.bfloat16), "cuda")
+    ws_ver = sb.workspace(sb.verify_workspace_bytes(B, N, w.V), "cuda")
+    ws_walk = sb.workspace(sb.verify_workspace_bytes(B, N, w.V), "cuda")
+    ws_lm = sb.workspace(sb.lm_head_stats_workspace_bytes(2, 40, 256, 3000), "cuda")
+
+    def run(o):
+        o["tb"] = sb.spec_tree_build(par, prefix_len=P, n_nodes=nn, out=o.get("tb"))
+        prev = o.get("att", {})
+        o["att"] = sb.spec_tree_attn(q, k, v, P, o["tb"]["mask"], n_nodes=nn, scale=w.d ** -0.5,
+                                     out=prev.get("out"), lse=prev.get("lse"), err=prev.get("err"), ws=ws_attn)
+        o["rej"] = sb.spec_verify(logits, toks, par, unif, "reject", draft_probs=draft, draft_row=drow,
+                                  n_nodes=nn, out=o.get("rej"), ws=ws_ver)
+        o["walk"] = sb.spec_verify(logits, toks, par, unif, "walk", draft_probs=draft, draft_row=drow,
+                                   n_nodes=nn, out=o.get("walk"), ws=ws_walk)
+        o["sel"] = sb.spec_tree_select(cp, cprob, 64, cand_tokens=ct, cand_row=cr, out=o.get("sel"))
+        o["lm"] = sb.spec_lm_head_stats(h, W, lpar, ltok, out=o.get("lm"), ws=ws_lm)
+        o["gr"] = sb.spec_verify_greedy_stats(o["lm"]["row_argmax"], ltok, lpar, 3000, out=o.get("gr"))
+        return o
+
+    eager = run({})
+    torch.cuda.synchronize()
+    ref = snapshot({k: v for k, v in eager.items() if isinstance(v, dict)})
+
+    outs = run({})                      # the graph's own output buffers, allocated eagerly
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            run(outs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    scratch = torch.empty(1 << 22, device="cuda")
+    for rep in range(3):
+        for d in outs.values():         # poison the outputs: the replay must rewrite them
+            if isinstance(d, dict):
+                for t in d.values():
+                    if isinstance(t, torch.Tensor) and t.dtype.is_floating_point:
+                        t.fill_(float("nan"))
+                    elif isinstance(t, torch.Tensor):
+                        t.fill_(-7)
+        scratch.uniform_()              # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snapshot({k: v for k, v in outs.items() if isinstance(v, dict)})
+        for key, want in ref.items():
+            have = got[key]
+            if want.dtype.is_floating_point:
+                same = torch.equal(torch.nan_to_num(have, nan=1.5e38), torch.nan_to_num(want, nan=1.5e38))
+            else:
+                same = torch.equal(have, want)
+            assert same, f"replay {rep}: {key} differs from the eager call"
+        print(f"replay {rep}: {len(ref)} outputs equal to the eager call", flush=True)
