@@ -33,10 +33,29 @@ namespace {
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kSelPer = SPEC_MAX_CANDIDATES / kSelThreads;  // candidates per thread
+constexpr int kSelLog2Max = 12;                                // log2 of SPEC_MAX_CANDIDATES
 
 // true if (ka, ia) comes before (kb, ib): larger value first, then lower index
 __device__ __forceinline__ bool precedes(double ka, int ia, double kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
+}
+
+// The value of lane (lane ^ m) for m < 64; m is a constant after unrolling.  Quad permutes
+// (DPP) for 1 and 2, the swizzle's bit mode (and 0x1f, xor m, inside 32 lanes) for 4 to 16,
+// ds_bpermute for 32.
+__device__ __forceinline__ int lane_xor(int v, int m) {
+  if (m == 1) return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad 1 0 3 2
+  if (m == 2) return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad 2 3 0 1
+  if (m == 4) return __builtin_amdgcn_ds_swizzle(v, 0x1F | (4 << 10));
+  if (m == 8) return __builtin_amdgcn_ds_swizzle(v, 0x1F | (8 << 10));
+  if (m == 16) return __builtin_amdgcn_ds_swizzle(v, 0x1F | (16 << 10));
+  return __shfl_xor(v, m);
+}
+__device__ __forceinline__ double lane_xor(double v, int m) {
+  const long long b = __double_as_longlong(v);
+  const int lo = lane_xor((int)(b & 0xffffffffll), m);
+  const int hi = lane_xor((int)(b >> 32), m);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
 // One compare-exchange of a bitonic stage seen from one position: (k, i) is this position's
@@ -182,8 +201,15 @@ __global__ __launch_bounds__(kSelThreads) void tree_select_kernel(
       idx[r] = q;
     }
     int buf = 0;
-    for (int size = 2; size <= E; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+    // both loops unrolled, so every stage's stride is a constant: strides 1 and 2 exchange by
+    // DPP, 4 to 16 by ds_swizzle, 32 by ds_bpermute
+#pragma unroll
+    for (int ls = 1; ls <= kSelLog2Max; ++ls) {
+      const int size = 1 << ls;
+      if (size > E) break;
+#pragma unroll
+      for (int lt = ls - 1; lt >= 0; --lt) {
+        const int stride = 1 << lt;
         if (stride >= kSelThreads) {
           if (stride == kSelThreads) {
             bitonic_in_thread(key[0], idx[0], key[1], idx[1], (0 * kSelThreads & size) == 0);
@@ -217,8 +243,8 @@ __global__ __launch_bounds__(kSelThreads) void tree_select_kernel(
           for (int r = 0; r < kSelPer; ++r) {
             if (r < R) {
               const int q = r * kSelThreads + t;
-              const double ok = __shfl_xor(key[r], stride);
-              const int oi = __shfl_xor(idx[r], stride);
+              const double ok = lane_xor(key[r], stride);
+              const int oi = lane_xor(idx[r], stride);
               bitonic_pick(key[r], idx[r], ok, oi, (q & stride) == 0, (q & size) == 0);
             }
           }
