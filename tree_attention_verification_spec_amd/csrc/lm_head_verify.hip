@@ -9,21 +9,24 @@
 // logit in its parent's row, so the logits are reduced where they are produced and the
 // B x N x V logits array is never written.
 //
-// lmhead_stats_kernel: grid ceil(V / 64) x ceil(M / 64); a workgroup multiplies 64 rows of W
-// (four 16-row blocks, A operand of v_mfma_f32_16x16x32_bf16, 16-byte loads) with up to 64 of
-// the M = B * N hidden states (up to four 16-column blocks, B operand, L2-resident), K split over
-// the four waves and summed in LDS.  With more than 64 hidden states the column blocks of one W
-// tile are placed on one XCD, so the tile comes from HBM once and from that XCD's L2 after.  The 64 x M logits tile then stays in LDS: per column,
-// four threads reduce (max, lowest argmax) and then fp64 sums of fp32 exp(l - max), and the
-// candidates whose token falls in the tile pick their parent's logit.  Partials go to the
-// workspace, one per (column, tile).
-// lmhead_merge_kernel: one workgroup per column; block max first, then the partials' sums
-// rescaled by exp(m_j - max) in fp64 (no sequential rescaling), validation of the sequence's
-// tree, and the outputs.
+// lmhead_stats_kernel (M <= 64 hidden states): grid ceil(V / 64); a workgroup multiplies 64
+// rows of W (four 16-row blocks, A operand of v_mfma_f32_16x16x32_bf16, 16-byte loads streamed
+// from HBM) with all M hidden states (up to four 16-column blocks, B operand, L2-resident), K
+// split over the four waves and summed in LDS.  The 64 x M logits tile then stays in LDS: per
+// column, four threads reduce (max, lowest argmax) and then fp64 sums of fp32 exp(l - max), and
+// the candidates whose token falls in the tile pick their parent's logit.  Partials go to the
+// workspace, one per (row, 64 W rows).
+// lmhead_stats_wide_kernel (65-128) and lmhead_stats_gemm_kernel (129-4096): every W tile must
+// meet all hidden states, so these cover 256 W rows x 64 columns, or 128 x 128 tiles staged
+// through LDS; the column blocks of one W tile get workgroup ids with the same residue mod 8, so
+// they run on one XCD and read the tile through its L2.  Same partials and gathers.
+// lmhead_merge_kernel: one workgroup per row; block max first, then the partials' sums rescaled
+// by exp(m_j - max) in fp64 (no sequential rescaling), validation of the sequence's tree, and
+// the outputs.
 //
-// Weight-streaming: W (1.05 GB at V = 128256, Dm = 4096) is read from HBM once; the hidden
-// states (512 KB) are re-read from L2 by every workgroup, from a copy in fragment order
-// (lmhead_xperm_kernel) so that each B-fragment load is four 256-byte runs.
+// At small M this is weight-streaming: W (1.05 GB at V = 128256, Dm = 4096) is read from HBM
+// once; the hidden states (512 KB at 63 rows) are re-read from L2 by every workgroup, from a copy
+// in fragment order (lmhead_xperm_kernel) so that each B-fragment load is four 256-byte runs.
 #include <climits>
 
 #include "common.h"
