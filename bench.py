@@ -285,8 +285,11 @@ def lm_head_stats_timing(w, reps=20, Dm=4096):
     tok = torch.randint(0, V, (B, N), generator=g, device="cuda", dtype=torch.int32)
     out = sb.spec_lm_head_stats(h, W, par, tok)
     ver = sb.spec_verify_greedy_stats(out["row_argmax"], tok, par, V)
+    uni = torch.rand((B, N), generator=g, device="cuda")
+    vtyp = sb.spec_verify_lm_head(h, W, tok, par, uni, "typical")
     torch.cuda.synchronize()
     assert int(out["err"].abs().sum()) == 0 and int(ver["err"].abs().sum()) == 0
+    assert int(vtyp["err"].abs().sum()) == 0
     try:
         sb.prof_reset()
         sb.prof_enable(True)
@@ -294,20 +297,26 @@ def lm_head_stats_timing(w, reps=20, Dm=4096):
             sb.spec_lm_head_stats(h, W, par, tok, out=out)
             sb.spec_verify_greedy_stats(out["row_argmax"], tok, par, V, out=ver)
         torch.cuda.synchronize()
-        sb.prof_enable(False)
         ms, cnt = sb.prof_read("lm_head_stats")
         ms2, cnt2 = sb.prof_read("lm_head_merge")
         ms3, cnt3 = sb.prof_read("lm_head_xperm")
         ms4, cnt4 = sb.prof_read("verify_greedy_stats")
+        for _ in range(reps):
+            sb.spec_verify_lm_head(h, W, tok, par, uni, "typical", out=vtyp)
+        torch.cuda.synchronize()
+        sb.prof_enable(False)
+        ms5, cnt5 = sb.prof_read("verify_lm")
     finally:
         sb.prof_enable(False)
         sb.prof_reset()
     us, us_merge, us_perm, us_greedy = ms / cnt * 1e3, ms2 / cnt2 * 1e3, ms3 / cnt3 * 1e3, ms4 / cnt4 * 1e3
+    us_typ = ms5 / cnt5 * 1e3
     nbytes = V * Dm * 2 + B * N * Dm * 2
     flops = 2 * B * N * Dm * V
     del W
     return {"shape": f"[{B * N} x {Dm}] x [{Dm} x {V}]", "us": round(us, 3), "merge_us": round(us_merge, 3),
             "xperm_us": round(us_perm, 3), "greedy_verify_us": round(us_greedy, 3),
+            "typical_verify_us": round(us_typ, 3),
             "algorithmic_bytes": nbytes, "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
             "hbm_frac": round(nbytes / (us * 1e-6) / 8e12, 4),
             "achieved_TFLOPs": round(flops / (us * 1e-6) / 1e12, 1)}
@@ -502,7 +511,8 @@ def main():
     if lmh:
         log(f"lm_head_stats (beside the step, not in it): {lmh['shape']}, {lmh['xperm_us']:.2f} us permute + "
             f"{lmh['us']:.2f} us + merge {lmh['merge_us']:.2f} us, {lmh['achieved_GBs']:.0f} GB/s; greedy verify "
-            f"from the statistics {lmh['greedy_verify_us']:.2f} us")
+            f"from the statistics {lmh['greedy_verify_us']:.2f} us, typical with its bonus draw "
+            f"{lmh['typical_verify_us']:.2f} us")
 
     if args.copy_calibration_mb:
         nb = args.copy_calibration_mb * (1 << 20)

@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     for n in ("spec_tree_build", "spec_tree_assemble", "spec_tree_attn", "spec_tree_attn_workspace",
               "spec_verify", "spec_verify_workspace", "spec_medusa_heads", "spec_medusa_heads_workspace",
               "spec_kv_compact", "spec_tree_select", "spec_lm_head_stats", "spec_lm_head_stats_workspace",
-              "spec_verify_greedy_stats",
+              "spec_verify_greedy_stats", "spec_verify_lm_head", "spec_verify_lm_head_workspace",
               "spec_strerror", "spec_prof_enable", "spec_prof_reset",
               "spec_prof_read"):
         assert n in names, n
@@ -154,3 +154,18 @@ def test_verify_greedy_stats_argument_checks(lib):
 
     assert call(am=None) == 1 and call(acc=None) == 1 and call(err=None) == 1
     assert call(B=0) == 1 and call(N=257) == 1 and call(V=0) == 1 and call(md=-1) == 1
+
+
+def test_verify_lm_head_argument_checks(lib):
+    fake = ctypes.c_void_p(0x1000)     # never dereferenced: every call below returns before a launch
+    ws = lib.spec_verify_lm_head_workspace(1, 63, 4096, 128256)
+    assert ws > lib.spec_lm_head_stats_workspace(1, 63, 4096, 128256)
+
+    def call(mode=0, eps=0.09, delta=0.3, uni=fake, wsz=ws, B=1, N=63, Dm=4096):
+        return lib.spec_verify_lm_head(fake, fake, fake, fake, None, uni, B, N, Dm, 128256, N - 1, mode, eps, delta,
+                                       fake, fake, fake, None, fake, fake, wsz, None)
+
+    assert call(uni=None) == 1 and call(B=0) == 1
+    assert call(mode=2) == 2 and call(mode=3) == 2       # REJECT / WALK need the whole row m
+    assert call(mode=1, eps=float("nan")) == 1
+    assert call(Dm=4000) == 2 and call(wsz=ws - 1) == 3

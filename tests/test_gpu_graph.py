@@ -4,6 +4,7 @@ are captured once with preallocated outputs and workspaces, replayed three times
 eager work and synchronisations in between, and every replay's outputs must equal the eager
 call's bit for bit (the kernels are deterministic: no atomics decide a floating-point sum)."""
 
+import numpy as np
 import pytest
 import torch
 
@@ -46,6 +47,8 @@ def test_graph_replays_match_eager():
     ws_ver = sb.workspace(sb.verify_workspace_bytes(B, N, w.V), "cuda")
     ws_walk = sb.workspace(sb.verify_workspace_bytes(B, N, w.V), "cuda")
     ws_lm = sb.workspace(sb.lm_head_stats_workspace_bytes(2, 40, 256, 3000), "cuda")
+    ws_vlm = sb.workspace(sb.verify_lm_head_workspace_bytes(2, 40, 256, 3000), "cuda")
+    lunif = dev(np.random.default_rng(34).random((2, 40), dtype=np.float32))
 
     def run(o):
         o["tb"] = sb.spec_tree_build(par, prefix_len=P, n_nodes=nn, out=o.get("tb"))
@@ -59,6 +62,7 @@ def test_graph_replays_match_eager():
         o["sel"] = sb.spec_tree_select(cp, cprob, 64, cand_tokens=ct, cand_row=cr, out=o.get("sel"))
         o["lm"] = sb.spec_lm_head_stats(h, W, lpar, ltok, out=o.get("lm"), ws=ws_lm)
         o["gr"] = sb.spec_verify_greedy_stats(o["lm"]["row_argmax"], ltok, lpar, 3000, out=o.get("gr"))
+        o["vlm"] = sb.spec_verify_lm_head(h, W, ltok, lpar, lunif, "typical", out=o.get("vlm"), ws=ws_vlm)
         return o
 
     eager = run({})

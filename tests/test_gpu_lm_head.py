@@ -190,3 +190,83 @@ def test_greedy_stats_errors():
     assert [oracle.decode_err(e) for e in rv["err"]] == [(0, 0), (0, oracle.ERR_ROOT), (4, oracle.ERR_PARENT),
                                                          (5, oracle.ERR_TOKEN), (0, 0), (0, oracle.ERR_NNODES)]
     assert int(rv["accept_len"][0]) == 4 and int(rv["bonus"][0]) == 4   # path 0 -> 1 -> 3 -> 6 -> 7
+
+
+@pytest.mark.parametrize("mode", ["greedy", "typical"])
+@pytest.mark.parametrize("seed,B,N,Dm,V,hscale", [(41, 2, 40, 256, 3000, 8.0), (42, 4, 16, 128, 700, 12.0),
+                                                   (43, 1, 63, 4096, 128256, 1.0), (44, 8, 127, 256, 2000, 8.0)])
+def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
+    """spec_verify_lm_head against oracle.verify on the oracle's exact logits.  Typical node tests
+    within the accumulation bound of their boundary (|ln T - ln tau| below 6 delta (H + 1), delta
+    the sequence's logit bound) are counted, not compared, and so is everything downstream.  The TYPICAL bonus must be a
+    token the oracle's inverse CDF gives for some u' within 4 delta_m of u (the GPU's CDF is
+    exact up to the fp32 logits).  Greedy sequences are compared whenever the GPU's row arg-maxima
+    (read through spec_lm_head_stats, the same kernels) equal the oracle's."""
+    need_gpu()
+    inp = wl.lm_head_inputs(seed=seed, B=B, N=N, Dm=Dm, V=V, max_depth=6)
+    inp["hidden"] = wl.round_bf16(inp["hidden"] * np.float32(hscale))
+    ref0 = oracle.lm_head_stats(inp["hidden"], inp["W"], inp["parents"], inp["tokens"])
+    g = np.random.default_rng(seed)
+    tok = inp["tokens"].copy()
+    for b in range(B):
+        for c in range(1, N):
+            if g.random() < 0.6:
+                tok[b, c] = ref0["row_argmax"][b, inp["parents"][b, c]]
+    unif = g.random((B, N), dtype=np.float32)
+    n_nodes = np.array([N - (b % 2) for b in range(B)], dtype=np.int32)
+    eps, delta = float(np.float32(0.09)), float(np.float32(0.3))
+    print(f"verify_lm_head {mode} B={B} N={N} Dm={Dm} V={V}", flush=True)
+    got = sb.spec_verify_lm_head(dev(inp["hidden"], torch.bfloat16), dev(inp["W"], torch.bfloat16), dev(tok),
+                                 dev(inp["parents"]), dev(unif), mode, n_nodes=dev(n_nodes), eps=eps, delta=delta)
+    torch.cuda.synchronize()
+    got = {k: host(v) for k, v in got.items()}
+    ref = oracle.lm_head_stats(inp["hidden"], inp["W"], inp["parents"], tok, n_nodes=n_nodes)
+    logits = np.nan_to_num(ref["logits"], nan=0.0)
+    m_id = oracle.MODE_GREEDY if mode == "greedy" else oracle.MODE_TYPICAL
+    rv = oracle.verify(logits, tok, inp["parents"], unif, m_id, n_nodes=n_nodes, eps=eps, delta=delta)
+    d = bound(inp["hidden"], inp["W"])
+    # greedy outcomes depend on the row arg-maxima only: the GPU's (same kernels) are read here
+    st = sb.spec_lm_head_stats(dev(inp["hidden"], torch.bfloat16), dev(inp["W"], torch.bfloat16), dev(inp["parents"]),
+                               dev(tok), n_nodes=dev(n_nodes))
+    torch.cuda.synchronize()
+    gam = host(st["row_argmax"])
+    compared = bonus_checked = 0
+    for b in range(B):
+        nb = int(n_nodes[b])
+        assert int(got["err"][b]) == int(rv["err"][b])
+        dmax = float(d[b, :nb].max())
+        if mode == "greedy":
+            differ = np.flatnonzero(gam[b, :nb] != ref["row_argmax"][b, :nb])
+            for i in differ:
+                row = ref["logits"][b, i]
+                assert row[gam[b, i]] >= row.max() - 2 * d[b, i], f"sequence {b} row {i}: argmax off"
+            if differ.size:
+                continue
+        else:
+            H = np.log(ref["row_sum"][b, :nb]) - ref["row_ent"][b, :nb] / ref["row_sum"][b, :nb]
+            if np.any(rv["margin"][b, 1:nb] < 6 * dmax * (H.max() + 1)):
+                continue
+        compared += 1
+        assert np.array_equal(got["node_accept"][b], rv["node_accept"][b]), f"sequence {b}: node_accept"
+        assert int(got["accept_len"][b]) == int(rv["accept_len"][b]), f"sequence {b}: accept_len"
+        assert np.array_equal(got["path"][b], rv["path"][b]), f"sequence {b}: path"
+        if mode == "greedy":
+            assert int(got["bonus"][b]) == int(rv["bonus"][b]), f"sequence {b}: bonus"
+        else:
+            m = int(rv["m"][b])
+            row = logits[b, m]
+            T = np.exp(row - row.max())
+            C = np.cumsum(T) / T.sum()
+            t = int(got["bonus"][b])
+            assert 0 <= t < V
+            lo = C[t - 1] if t > 0 else 0.0
+            tol = 4 * float(d[b, m]) + 1e-12
+            assert lo <= unif[b, 0] + tol and C[t] >= unif[b, 0] - tol, \
+                f"sequence {b}: bonus {t} outside the oracle's CDF step (u {unif[b, 0]}, [{lo}, {C[t]}])"
+            bonus_checked += 1
+            if int(rv["bonus"][b]) != t:
+                print(f"  sequence {b}: bonus {t} vs oracle {int(rv['bonus'][b])} (u within {tol:.1e} of a step)")
+    print(f"  compared {compared} of {B} sequences; accept_len {got['accept_len'].tolist()}; "
+          f"oracle {rv['accept_len'].tolist()}", flush=True)
+    # at Dm = 4096 the typical margin bound (~1e-2 in ln T) can excuse a whole sequence
+    assert compared >= 1 or (mode == "typical" and Dm > 512)

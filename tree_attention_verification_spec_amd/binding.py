@@ -52,6 +52,11 @@ def lib():
     L.spec_lm_head_stats.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P]
     L.spec_verify_greedy_stats.restype = _I
     L.spec_verify_greedy_stats.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
+    L.spec_verify_lm_head_workspace.restype = _Z
+    L.spec_verify_lm_head_workspace.argtypes = [_I, _I, _I, _I]
+    L.spec_verify_lm_head.restype = _I
+    L.spec_verify_lm_head.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F,
+                                      _P, _P, _P, _P, _P, _P, _Z, _P]
     L.spec_tree_attn_workspace.restype = _Z
     L.spec_tree_attn_workspace.argtypes = [_I, _I, _I, _I, _I, _I, _I]
     L.spec_tree_attn.restype = _I
@@ -303,6 +308,40 @@ def spec_verify_greedy_stats(row_argmax, tokens, parents, V, n_nodes=None, max_d
         _ptr(out["bonus"], torch.int32, (B,), "bonus"),
         _ptr(out.get("node_accept"), torch.uint8, (B, N), "node_accept"),
         _ptr(out["err"], torch.int32, (B,), "err"), _stream(stream)), "spec_verify_greedy_stats")
+    return out
+
+
+def verify_lm_head_workspace_bytes(B, N, Dm, V):
+    return int(lib().spec_verify_lm_head_workspace(B, N, Dm, V))
+
+
+def spec_verify_lm_head(hidden, W, tokens, parents, uniforms, mode, n_nodes=None, eps=0.09, delta=0.3,
+                        max_depth=None, out=None, ws=None, stream=None):
+    B, N, Dm = hidden.shape
+    V = W.shape[0]
+    dev = hidden.device
+    mode = MODES.get(mode, mode)
+    if max_depth is None:
+        max_depth = N - 1
+    if out is None:
+        out = {"accept_len": torch.empty((B,), dtype=torch.int32, device=dev),
+               "path": torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev),
+               "bonus": torch.empty((B,), dtype=torch.int32, device=dev),
+               "node_accept": torch.empty((B, N), dtype=torch.uint8, device=dev),
+               "err": torch.empty((B,), dtype=torch.int32, device=dev)}
+    if ws is None:
+        ws = workspace(verify_lm_head_workspace_bytes(B, N, Dm, V), dev)
+    _check(lib().spec_verify_lm_head(
+        _ptr(hidden, torch.bfloat16, (B, N, Dm), "hidden"), _ptr(W, torch.bfloat16, (V, Dm), "W"),
+        _ptr(tokens, torch.int32, (B, N), "tokens"), _ptr(parents, torch.int32, (B, N), "parents"),
+        _ptr(n_nodes, torch.int32, (B,), "n_nodes"), _ptr(uniforms, torch.float32, (B, N), "uniforms"),
+        B, N, Dm, V, int(max_depth), int(mode), float(eps), float(delta),
+        _ptr(out["accept_len"], torch.int32, (B,), "accept_len"),
+        _ptr(out["path"], torch.int32, (B, max_depth + 1), "path"),
+        _ptr(out["bonus"], torch.int32, (B,), "bonus"),
+        _ptr(out.get("node_accept"), torch.uint8, (B, N), "node_accept"),
+        _ptr(out["err"], torch.int32, (B,), "err"), _ptr(ws, None, None, "workspace"), ws.numel(),
+        _stream(stream)), "spec_verify_lm_head")
     return out
 
 

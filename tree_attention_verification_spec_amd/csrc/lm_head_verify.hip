@@ -590,6 +590,193 @@ __global__ __launch_bounds__(kLThreads) void lmhead_merge_kernel(
 }
 
 
+// Greedy or typical verification straight from the LM head's statistics, with the bonus token.
+// One workgroup per sequence.  Node c (parent p, token x): GREEDY accepts iff x is p's lowest
+// argmax; TYPICAL iff T_p[x] = exp(l_p[x] - max_p) / S_p >= min(eps, delta exp(-H_p)), with
+// H_p = ln S_p - A_p / S_p (fp64, T from the same fp32 exponential the sums were built from).
+// Survival, the deepest survivor m and the path as spec_verify.  The bonus: GREEDY the argmax of
+// row m; TYPICAL a draw from T_m by inverse CDF with u = uniforms[b, 0]: the 64-token tile
+// holding u Z is found from the per-tile sums the LM head left in the workspace (Z = sum_j
+// S_j e^(m_j - M)), the tile's 64 logits are recomputed (fp32 dot products), and the token is
+// the first whose running weight exceeds the remainder (scaled to the recomputed tile's total,
+// which differs from the stored sum only by fp32 rounding).
+__global__ __launch_bounds__(SPEC_MAX_NODES) void verify_lm_kernel(
+    const float* __restrict__ row_max, const int32_t* __restrict__ row_argmax,
+    const double* __restrict__ row_sum, const double* __restrict__ row_ent,
+    const float* __restrict__ cand, const LmPart* __restrict__ parts, int nblk,
+    const __bf16* __restrict__ X, const __bf16* __restrict__ W, int Dm,
+    const int32_t* __restrict__ tokens, const int32_t* __restrict__ parents,
+    const int32_t* __restrict__ n_nodes, const float* __restrict__ uniforms, int N, int V,
+    int max_depth, int mode, float eps, float delta, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ path, int32_t* __restrict__ bonus, uint8_t* __restrict__ node_accept,
+    int32_t* __restrict__ err) {
+  __shared__ int s_par[SPEC_MAX_NODES];
+  __shared__ unsigned char s_acc[SPEC_MAX_NODES];
+  __shared__ int s_err, s_best;
+  __shared__ double s_wsum[SPEC_MAX_NODES / kWave];
+  __shared__ int s_tile;
+  __shared__ double s_pre, s_scale;
+  __shared__ float s_logit[kLRows];
+  const int b = blockIdx.x, c = threadIdx.x;
+  const int lane = c & (kWave - 1), wv = c >> 6;
+  const size_t base = (size_t)b * N;
+  const int n_raw = n_nodes ? n_nodes[b] : N;
+  const bool bad_n = n_raw < 0 || n_raw > N;
+  const int n = bad_n ? 0 : n_raw;
+  if (c == 0) {
+    s_err = INT_MAX;
+    s_best = -1;
+  }
+  if (c < N) s_par[c] = parents[base + c];
+  __syncthreads();
+  int depth = 0;
+  bool acc = false;
+  if (c < n) {
+    const int p = s_par[c];
+    int code = 0;
+    if (c == 0) {
+      if (p != -1) code = SPEC_ERR_ROOT;
+      acc = true;
+    } else if (p < 0 || p >= c) {
+      code = SPEC_ERR_PARENT;
+    } else {
+      int j = c;
+      while (j > 0 && s_par[j] >= 0 && s_par[j] < j) {
+        j = s_par[j];
+        ++depth;
+      }
+      const int x = tokens[base + c];
+      if (depth > max_depth) code = SPEC_ERR_DEPTH;
+      else if (x < 0 || x >= V) code = SPEC_ERR_TOKEN;
+      else if (mode == SPEC_VERIFY_GREEDY) acc = x == row_argmax[base + p];
+      else {
+        const double S = row_sum[base + p];
+        const double T = (double)expf(cand[base + c] - row_max[base + p]) / S;
+        const double H = log(S) - row_ent[base + p] / S;
+        acc = T >= fmin((double)eps, (double)delta * exp(-H));
+      }
+    }
+    if (code) atomicMin(&s_err, err_word(c, code));
+    s_acc[c] = acc ? 1 : 0;
+  }
+  __syncthreads();
+  const int e = bad_n ? err_word(0, SPEC_ERR_NNODES) : (s_err == INT_MAX ? 0 : s_err);
+  if (e == 0 && c < n) {
+    bool live = true;
+    for (int j = c; j > 0; j = s_par[j]) live = live && s_acc[j];
+    if (live) atomicMax(&s_best, (depth << 9) | (511 - c));
+  }
+  __syncthreads();
+  if (c < N && node_accept) node_accept[base + c] = (e == 0 && c < n) ? s_acc[c] : 0;
+  const bool ok = e == 0 && n > 0;
+  const int m = ok ? 511 - (s_best & 511) : 0;
+  if (c == 0) {
+    int32_t* pr = path + (size_t)b * (max_depth + 1);
+    for (int k = 0; k <= max_depth; ++k) pr[k] = -1;
+    int len = 0;
+    if (ok) {
+      len = s_best >> 9;
+      for (int j = m, k = len; k >= 0; --k, j = s_par[j]) pr[k] = j;
+    }
+    accept_len[b] = len;
+    err[b] = e;
+    if (!ok) bonus[b] = -1;
+    else if (mode == SPEC_VERIFY_GREEDY) bonus[b] = row_argmax[base + m];
+  }
+  if (!ok || mode == SPEC_VERIFY_GREEDY) return;            // uniform across the workgroup
+
+  // ---- TYPICAL bonus: the tile of row m holding u Z, from the per-tile partials
+  const LmPart* pp = parts + (base + m) * nblk;
+  const float M = row_max[base + m];
+  const double Z = row_sum[base + m];
+  const double target = (double)uniforms[base] * Z;
+  // tiles in chunks of 256: each thread's weight, a block scan, the first crossing
+  if (c == 0) {
+    s_tile = -1;
+    s_pre = 0.0;
+  }
+  __syncthreads();
+  double carry = 0.0;
+  for (int j0 = 0; j0 < nblk; j0 += SPEC_MAX_NODES) {
+    const int j = j0 + c;
+    double wj = 0.0;
+    if (j < nblk) {
+      const LmPart q = pp[j];
+      if (q.m != -INFINITY) wj = q.S * exp((double)q.m - (double)M);
+    }
+    double incl = wj;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const double y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == kWave - 1) s_wsum[wv] = incl;
+    __syncthreads();
+    double off = carry;
+    for (int q = 0; q < wv; ++q) off += s_wsum[q];
+    const double before = off + incl - wj, after = off + incl;
+    if (j < nblk && wj > 0.0 && before <= target && target < after) {
+      s_tile = j;                            // one thread at most: the ranges are disjoint
+      s_pre = before;
+    }
+    double tot = 0.0;
+    for (int q = 0; q < SPEC_MAX_NODES / kWave; ++q) tot += s_wsum[q];
+    carry += tot;
+    __syncthreads();
+    if (s_tile >= 0) break;                  // uniform: read after the barrier
+  }
+  int tile = s_tile;
+  if (tile < 0) {                            // u Z at or past the rounded total: the last tile
+    if (c == 0) {                            // with weight
+      int last = nblk - 1;
+      while (last > 0 && !(pp[last].m != -INFINITY && pp[last].S > 0.0)) --last;
+      s_tile = last;
+      s_pre = -1.0;                          // take its last token
+    }
+    __syncthreads();
+    tile = s_tile;
+  }
+  // the tile's 64 logits of row m: four threads per token, Dm / 4 products each
+  {
+    const int v_local = c >> 2, part = c & 3;
+    const int v = tile * kLRows + v_local;
+    float acc32 = 0.f;
+    if (v < V) {
+      const __bf16* wr = W + (size_t)v * Dm;
+      const __bf16* hr = X + (base + m) * (size_t)Dm;
+      for (int k = part * 8; k < Dm; k += 32) {
+        const bf16x8 a8 = ld8(wr + k), h8 = ld8(hr + k);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc32 = fmaf((float)a8[i], (float)h8[i], acc32);
+      }
+    }
+    acc32 += __shfl_xor(acc32, 1);
+    acc32 += __shfl_xor(acc32, 2);
+    if (part == 0) s_logit[v_local] = v < V ? acc32 : -INFINITY;
+  }
+  __syncthreads();
+  if (c == 0) {
+    const double mj = (double)pp[tile].m;
+    const double sc = exp(mj - (double)M);
+    double tw = 0.0;
+    for (int i = 0; i < kLRows; ++i)
+      if (s_logit[i] != -INFINITY) tw += (double)expf(s_logit[i] - (float)mj) * sc;
+    const double stored = pp[tile].S * sc;
+    // the remainder inside the tile, scaled to the recomputed total
+    double r = s_pre < 0.0 ? tw : (target - s_pre) * (stored > 0.0 ? tw / stored : 1.0);
+    int tok = -1;
+    double run = 0.0;
+    for (int i = 0; i < kLRows; ++i) {
+      if (s_logit[i] == -INFINITY) continue;
+      const double wi = (double)expf(s_logit[i] - (float)mj) * sc;
+      run += wi;
+      if (wi > 0.0) tok = tile * kLRows + i;  // the last token with weight, if r is never passed
+      if (run > r && wi > 0.0) break;
+    }
+    bonus[b] = tok;
+  }
+}
+
 // Greedy verification from the fused statistics: node c (parent p, token x) is accepted iff
 // x == row_argmax[p]; a node survives iff every node on its path below the root was accepted;
 // m = the deepest survivor (lowest index on ties); bonus = row_argmax[m].  One workgroup per
@@ -690,29 +877,26 @@ extern "C" size_t spec_lm_head_stats_workspace(int B, int N, int Dm, int V) {
   return lm_layout(B, N, V, Dm).total;
 }
 
-extern "C" spec_status spec_lm_head_stats(const void* hidden, const void* W, const int32_t* parents,
-                                          const int32_t* tokens, const int32_t* n_nodes, int B, int N,
-                                          int Dm, int V, float* row_max, int32_t* row_argmax,
-                                          double* row_sum, double* row_ent, float* cand_logit,
-                                          int32_t* err, void* workspace, size_t ws_bytes, void* stream) {
+namespace {
+spec_status check_lm(const void* hidden, const void* W, int B, int N, int Dm, int V) {
   if (B < 1 || N < 1 || Dm < 1 || V < 1) return SPEC_EINVAL;
-  if (!hidden || !W || !parents || !tokens || !row_max || !row_argmax || !row_sum || !row_ent ||
-      !cand_logit || !err)
-    return SPEC_EINVAL;
+  if (!hidden || !W) return SPEC_EINVAL;
   if (N > SPEC_MAX_NODES || (size_t)B * N > (size_t)kLMaxRows) return SPEC_EUNSUPPORTED;
-  const int M = B * N;
   if (Dm % 128 != 0) return SPEC_EUNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(hidden) & 15) || (reinterpret_cast<uintptr_t>(W) & 15))
     return SPEC_EUNSUPPORTED;
-  const LmLayout L = lm_layout(B, N, V, Dm);
-  if (!workspace || ws_bytes < L.total) return SPEC_EWORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* w = static_cast<char*>(workspace);
+  return SPEC_OK;
+}
+
+// permutation, tile kernel for the size, merge: the statistics into the given arrays
+void launch_lm(const __bf16* X, const __bf16* Wb, const int32_t* parents, const int32_t* tokens,
+               const int32_t* n_nodes, int B, int N, int Dm, int V, const LmLayout& L, char* w,
+               float* row_max, int32_t* row_argmax, double* row_sum, double* row_ent, float* cand_logit,
+               int32_t* err, hipStream_t s) {
+  const int M = B * N;
   LmPart* parts = reinterpret_cast<LmPart*>(w + L.parts);
   float* gath = reinterpret_cast<float*>(w + L.gath);
   __bf16* Xp = reinterpret_cast<__bf16*>(w + L.xperm);
-  const __bf16* Wb = static_cast<const __bf16*>(W);
-  const __bf16* X = static_cast<const __bf16*>(hidden);
   const int ncb = (M + kLMaxCols - 1) / kLMaxCols;
   const dim3 g1((unsigned)((L.nblk + 7) / 8 * 8 * ncb)), blk(kLThreads);
   const int nchunk = M * (Dm / 8);
@@ -734,6 +918,79 @@ extern "C" spec_status spec_lm_head_stats(const void* hidden, const void* W, con
   else launch(nm, lmhead_stats_kernel<4>, g1, blk, s, Wb, Xp, M, Dm, V, N, nb, ncb, parents, tokens, parts, gath);
   launch("lm_head_merge", lmhead_merge_kernel, dim3((unsigned)M), blk, s, parts, gath, L.nblk, N, V,
          parents, tokens, n_nodes, row_max, row_argmax, row_sum, row_ent, cand_logit, err);
+}
+
+// spec_verify_lm_head's own part of the workspace, after the LM head's: the statistics
+struct VlLayout {
+  size_t mx, am, sum, ent, cand, err, total;
+};
+VlLayout vl_layout(const LmLayout& L, int B, int N) {
+  const size_t M = (size_t)B * N;
+  VlLayout v{};
+  v.mx = L.total;
+  v.am = v.mx + align_up(M * sizeof(float), 256);
+  v.sum = v.am + align_up(M * sizeof(int32_t), 256);
+  v.ent = v.sum + align_up(M * sizeof(double), 256);
+  v.cand = v.ent + align_up(M * sizeof(double), 256);
+  v.err = v.cand + align_up(M * sizeof(float), 256);
+  v.total = v.err + align_up((size_t)B * sizeof(int32_t), 256);
+  return v;
+}
+}  // namespace
+
+extern "C" spec_status spec_lm_head_stats(const void* hidden, const void* W, const int32_t* parents,
+                                          const int32_t* tokens, const int32_t* n_nodes, int B, int N,
+                                          int Dm, int V, float* row_max, int32_t* row_argmax,
+                                          double* row_sum, double* row_ent, float* cand_logit,
+                                          int32_t* err, void* workspace, size_t ws_bytes, void* stream) {
+  const spec_status st = check_lm(hidden, W, B, N, Dm, V);
+  if (st != SPEC_OK) return st;
+  if (!parents || !tokens || !row_max || !row_argmax || !row_sum || !row_ent || !cand_logit || !err)
+    return SPEC_EINVAL;
+  const LmLayout L = lm_layout(B, N, V, Dm);
+  if (!workspace || ws_bytes < L.total) return SPEC_EWORKSPACE;
+  launch_lm(static_cast<const __bf16*>(hidden), static_cast<const __bf16*>(W), parents, tokens, n_nodes, B, N, Dm,
+            V, L, static_cast<char*>(workspace), row_max, row_argmax, row_sum, row_ent, cand_logit, err,
+            static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+extern "C" size_t spec_verify_lm_head_workspace(int B, int N, int Dm, int V) {
+  if (B < 1 || N < 1 || Dm < 1 || V < 1) return 0;
+  return vl_layout(lm_layout(B, N, V, Dm), B, N).total;
+}
+
+extern "C" spec_status spec_verify_lm_head(const void* hidden, const void* W, const int32_t* tokens,
+                                           const int32_t* parents, const int32_t* n_nodes,
+                                           const float* uniforms, int B, int N, int Dm, int V,
+                                           int max_depth, spec_mode mode, float eps, float delta,
+                                           int32_t* accept_len, int32_t* path, int32_t* bonus_token,
+                                           uint8_t* node_accept, int32_t* err, void* workspace,
+                                           size_t ws_bytes, void* stream) {
+  const spec_status st = check_lm(hidden, W, B, N, Dm, V);
+  if (st != SPEC_OK) return st;
+  if (!tokens || !parents || !uniforms || !accept_len || !path || !bonus_token || !err || max_depth < 0)
+    return SPEC_EINVAL;
+  if (mode != SPEC_VERIFY_GREEDY && mode != SPEC_VERIFY_TYPICAL) return SPEC_EUNSUPPORTED;
+  if (mode == SPEC_VERIFY_TYPICAL && (!(eps == eps) || !(delta == delta))) return SPEC_EINVAL;
+  const LmLayout L = lm_layout(B, N, V, Dm);
+  const VlLayout VL = vl_layout(L, B, N);
+  if (!workspace || ws_bytes < VL.total) return SPEC_EWORKSPACE;
+  char* w = static_cast<char*>(workspace);
+  float* mx = reinterpret_cast<float*>(w + VL.mx);
+  int32_t* am = reinterpret_cast<int32_t*>(w + VL.am);
+  double* sum = reinterpret_cast<double*>(w + VL.sum);
+  double* ent = reinterpret_cast<double*>(w + VL.ent);
+  float* cand = reinterpret_cast<float*>(w + VL.cand);
+  int32_t* lerr = reinterpret_cast<int32_t*>(w + VL.err);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const __bf16* X = static_cast<const __bf16*>(hidden);
+  const __bf16* Wb = static_cast<const __bf16*>(W);
+  launch_lm(X, Wb, parents, tokens, n_nodes, B, N, Dm, V, L, w, mx, am, sum, ent, cand, lerr, s);
+  launch("verify_lm", verify_lm_kernel, dim3(B), dim3(SPEC_MAX_NODES), s, (const float*)mx, (const int32_t*)am,
+         (const double*)sum, (const double*)ent, (const float*)cand,
+         (const LmPart*)reinterpret_cast<LmPart*>(w + L.parts), L.nblk, X, Wb, Dm, tokens, parents, n_nodes,
+         uniforms, N, V, max_depth, (int)mode, eps, delta, accept_len, path, bonus_token, node_accept, err);
   return launch_status();
 }
 
