@@ -41,6 +41,7 @@ constexpr int kLRows = 16 * kLRB;           // vocabulary rows per workgroup
 constexpr int kLMaxCols = 64;               // hidden states (columns) per workgroup
 constexpr int kLMaxRows = 4096;             // B * N limit
 constexpr int kMergePer = 8;                // partials per merging thread held in registers
+constexpr int kScanPer = 8;                 // tiles per thread in the typical bonus's scan
 
 struct LmPart {       // one 64-token tile of one row
   double S;           // sum exp(l - m)
@@ -690,12 +691,46 @@ __global__ __launch_bounds__(SPEC_MAX_NODES) void verify_lm_kernel(
   const float M = row_max[base + m];
   const double Z = row_sum[base + m];
   const double target = (double)uniforms[base] * Z;
-  // tiles in chunks of 256: each thread's weight, a block scan, the first crossing
   if (c == 0) {
     s_tile = -1;
     s_pre = 0.0;
   }
   __syncthreads();
+  if (nblk <= SPEC_MAX_NODES * kScanPer) {
+    // thread c owns tiles 8c .. 8c + 7 (all requested at once): its weight, a block scan of the
+    // threads' totals, and the owner of the crossing scans its own tiles
+    double wj[kScanPer];
+    double mine = 0.0;
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+      const int j = c * kScanPer + k;
+      const LmPart q = pp[j < nblk ? j : 0];
+      wj[k] = (j < nblk && q.m != -INFINITY) ? q.S * exp((double)q.m - (double)M) : 0.0;
+      mine += wj[k];
+    }
+    double incl = mine;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const double y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == kWave - 1) s_wsum[wv] = incl;
+    __syncthreads();
+    double run = incl - mine;
+    for (int q = 0; q < wv; ++q) run += s_wsum[q];
+    if (mine > 0.0 && run <= target && target < run + mine) {
+#pragma unroll
+      for (int k = 0; k < kScanPer; ++k) {
+        if (wj[k] > 0.0 && run <= target && target < run + wj[k] && s_tile < 0) {
+          s_tile = c * kScanPer + k;         // one thread: the ranges are disjoint
+          s_pre = run;
+        }
+        run += wj[k];
+      }
+    }
+    __syncthreads();
+  } else {
+  // more tiles: chunks of 256, each thread's weight, a block scan, the first crossing
   double carry = 0.0;
   for (int j0 = 0; j0 < nblk; j0 += SPEC_MAX_NODES) {
     const int j = j0 + c;
@@ -725,6 +760,7 @@ __global__ __launch_bounds__(SPEC_MAX_NODES) void verify_lm_kernel(
     __syncthreads();
     if (s_tile >= 0) break;                  // uniform: read after the barrier
   }
+  }
   int tile = s_tile;
   if (tile < 0) {                            // u Z at or past the rounded total: the last tile
     if (c == 0) {                            // with weight
@@ -742,12 +778,22 @@ __global__ __launch_bounds__(SPEC_MAX_NODES) void verify_lm_kernel(
     const int v = tile * kLRows + v_local;
     float acc32 = 0.f;
     if (v < V) {
-      const __bf16* wr = W + (size_t)v * Dm;
-      const __bf16* hr = X + (base + m) * (size_t)Dm;
-      for (int k = part * 8; k < Dm; k += 32) {
-        const bf16x8 a8 = ld8(wr + k), h8 = ld8(hr + k);
+      const __bf16* wr = W + (size_t)v * Dm + part * 8;
+      const __bf16* hr = X + (base + m) * (size_t)Dm + part * 8;
+      const int nk = Dm / 32;
+      for (int k0 = 0; k0 < nk; k0 += 8) {   // eight 16-byte pairs requested at once
+        bf16x8 a8[8], h8[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc32 = fmaf((float)a8[i], (float)h8[i], acc32);
+        for (int i = 0; i < 8; ++i) {
+          const int k = (k0 + i < nk ? k0 + i : 0) * 32;
+          a8[i] = ld8(wr + k);
+          h8[i] = ld8(hr + k);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (k0 + i < nk)
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2) acc32 = fmaf((float)a8[i][e2], (float)h8[i][e2], acc32);
       }
     }
     acc32 += __shfl_xor(acc32, 1);
