@@ -330,37 +330,40 @@ spec_status spec_verify_greedy_stats(const int32_t* row_argmax, const int32_t* t
                                      void* stream);
 
 /* --------------------------------------------------------------------------------------
- * spec_verify_lm_head - greedy or typical verification straight from the target's hidden
- * states: spec_lm_head_stats' statistics, then spec_verify's GREEDY or TYPICAL rule on them,
+ * spec_verify_lm_head - greedy, typical or rejection-sampling verification straight from the
+ * target's hidden states: spec_lm_head_stats' statistics, then spec_verify's rule on them,
  * without the N x V logits.
  *
  * The rules are spec_verify's: GREEDY accepts node c (parent p, token x) iff x is p's lowest
  * argmax; TYPICAL iff T_p[x] = exp(l_p[x] - max_p) / S_p >= min(eps, delta exp(-H_p)) with
- * H_p = ln S_p - A_p / S_p; survival, the deepest survivor m and the path as spec_verify.
- * Bonus token: GREEDY the argmax of row m; TYPICAL a draw from T_m with u = uniforms[b, 0] by
- * inverse CDF (smallest t whose running sum from token 0 exceeds u Z): the 64-token tile that
- * holds u Z is found from the per-tile sums of the statistics pass, and that tile's logits are
- * recomputed (fp32 dot products) to place the token inside it.  [GUIDE] section
- * "並列検証：ターゲットモデルの1回のforward passで一括確認する" (one target pass scores every
- * node); [GLOSSARY] section "Medusa-1とMedusa-2の違い" (typical acceptance).
+ * H_p = ln S_p - A_p / S_p; REJECT iff uniforms[b, c] * D[x] < T_p[x]; survival, the deepest
+ * survivor m and the path as spec_verify.  Bonus token, by inverse CDF with u = uniforms[b, 0]
+ * (smallest t whose running sum from token 0 exceeds u Z): GREEDY the argmax of row m; TYPICAL,
+ * and REJECT when m has no child, a draw from T_m - the 64-token tile holding u Z is found from
+ * the per-tile sums of the statistics pass and only that tile's logits are recomputed; REJECT
+ * when m has children, a draw from norm(relu(T_m - D)), D the draft row of m's lowest-index
+ * child (T_m if that residual is zero) - row m is recomputed whole for it (one more pass over
+ * W).  [GUIDE] sections "並列検証：ターゲットモデルの1回のforward passで一括確認する" and
+ * "棄却サンプリング：出力品質を保証する"; [GLOSSARY] section "Medusa-1とMedusa-2の違い".
  *
  *   hidden, W, parents, tokens, n_nodes, B, N, Dm, V  as spec_lm_head_stats
- *   uniforms float [B, N] (column 0 for the bonus draw); max_depth, eps, delta as spec_verify
+ *   uniforms float [B, N]; draft_probs, draft_row, t2d, R, Vd (REJECT only; else may be NULL),
+ *   max_depth, eps, delta  as spec_verify
  * Outputs: accept_len [B], path [B, max_depth + 1], bonus_token [B], node_accept uint8 [B, N]
- *   (optional), err [B]: as spec_verify (SPEC_ERR_NNODES, ROOT, PARENT, DEPTH, TOKEN).
- * Workspace: spec_verify_lm_head_workspace bytes.
- * Supported: mode GREEDY or TYPICAL (the residual draw of REJECT needs row m whole: not
- * supported), N <= 256, B * N <= 4096, Dm a multiple of 128.
- * Errors: SPEC_EINVAL (sizes, NULL pointers, NaN eps or delta), SPEC_EUNSUPPORTED (mode, sizes,
- * alignment), SPEC_EWORKSPACE.
+ *   (optional), err [B]: as spec_verify (SPEC_ERR_NNODES, ROOT, PARENT, DEPTH, TOKEN, DRAFTROW,
+ *   MAP).  Workspace: spec_verify_lm_head_workspace bytes.
+ * Supported: GREEDY, TYPICAL, REJECT (not WALK), N <= 256, B * N <= 4096, Dm a multiple of 128.
+ * Errors: SPEC_EINVAL (sizes, NULL pointers, NaN eps or delta, REJECT without draft arrays, t2d
+ * NULL with Vd != V), SPEC_EUNSUPPORTED (mode, sizes, alignment), SPEC_EWORKSPACE.
  * ------------------------------------------------------------------------------------ */
 size_t spec_verify_lm_head_workspace(int B, int N, int Dm, int V);
 spec_status spec_verify_lm_head(const void* hidden, const void* W, const int32_t* tokens,
                                 const int32_t* parents, const int32_t* n_nodes, const float* uniforms,
-                                int B, int N, int Dm, int V, int max_depth, spec_mode mode, float eps,
-                                float delta, int32_t* accept_len, int32_t* path, int32_t* bonus_token,
-                                uint8_t* node_accept, int32_t* err, void* workspace, size_t ws_bytes,
-                                void* stream);
+                                const float* draft_probs, const int32_t* draft_row, const int32_t* t2d,
+                                int B, int N, int Dm, int V, int R, int Vd, int max_depth,
+                                spec_mode mode, float eps, float delta, int32_t* accept_len,
+                                int32_t* path, int32_t* bonus_token, uint8_t* node_accept,
+                                int32_t* err, void* workspace, size_t ws_bytes, void* stream);
 
 /* --------------------------------------------------------------------------------------
  * spec_kv_compact - KV-cache compaction that closes a verification round.

@@ -161,11 +161,13 @@ def test_verify_lm_head_argument_checks(lib):
     ws = lib.spec_verify_lm_head_workspace(1, 63, 4096, 128256)
     assert ws > lib.spec_lm_head_stats_workspace(1, 63, 4096, 128256)
 
-    def call(mode=0, eps=0.09, delta=0.3, uni=fake, wsz=ws, B=1, N=63, Dm=4096):
-        return lib.spec_verify_lm_head(fake, fake, fake, fake, None, uni, B, N, Dm, 128256, N - 1, mode, eps, delta,
-                                       fake, fake, fake, None, fake, fake, wsz, None)
+    def call(mode=0, eps=0.09, delta=0.3, uni=fake, wsz=ws, B=1, N=63, Dm=4096, draft=None, drow=None, R=0, Vd=0):
+        return lib.spec_verify_lm_head(fake, fake, fake, fake, None, uni, draft, drow, None, B, N, Dm, 128256, R, Vd,
+                                       N - 1, mode, eps, delta, fake, fake, fake, None, fake, fake, wsz, None)
 
     assert call(uni=None) == 1 and call(B=0) == 1
-    assert call(mode=2) == 2 and call(mode=3) == 2       # REJECT / WALK need the whole row m
+    assert call(mode=3) == 2                             # WALK is not supported here
+    assert call(mode=2) == 1                             # REJECT without draft arrays
+    assert call(mode=2, draft=fake, drow=fake, R=4, Vd=1000) == 1   # no t2d: Vd must be V
     assert call(mode=1, eps=float("nan")) == 1
     assert call(Dm=4000) == 2 and call(wsz=ws - 1) == 3

@@ -1,6 +1,6 @@
 """The entry points inside a captured HIP graph: a verification step (tree build, tree attention,
-rejection and walk verification), a tree selection and a fused LM head with greedy verification
-are captured once with preallocated outputs and workspaces, replayed three times with unrelated
+rejection and walk verification), a tree selection and a fused LM head with greedy, typical and
+rejection verification are captured once with preallocated outputs and workspaces, replayed three times with unrelated
 eager work and synchronisations in between, and every replay's outputs must equal the eager
 call's bit for bit (the kernels are deterministic: no atomics decide a floating-point sum)."""
 
@@ -48,7 +48,12 @@ def test_graph_replays_match_eager():
     ws_walk = sb.workspace(sb.verify_workspace_bytes(B, N, w.V), "cuda")
     ws_lm = sb.workspace(sb.lm_head_stats_workspace_bytes(2, 40, 256, 3000), "cuda")
     ws_vlm = sb.workspace(sb.verify_lm_head_workspace_bytes(2, 40, 256, 3000), "cuda")
-    lunif = dev(np.random.default_rng(34).random((2, 40), dtype=np.float32))
+    ws_vrj = sb.workspace(sb.verify_lm_head_workspace_bytes(2, 40, 256, 3000), "cuda")
+    lg = np.random.default_rng(34)
+    lunif = dev(lg.random((2, 40), dtype=np.float32))
+    ldraft = lg.random((2, 40, 3000)).astype(np.float32) ** 8
+    ldraft = dev(ldraft / ldraft.sum(axis=2, keepdims=True))
+    ldrow = dev(np.maximum(lm["parents"], 0).astype(np.int32))
 
     def run(o):
         o["tb"] = sb.spec_tree_build(par, prefix_len=P, n_nodes=nn, out=o.get("tb"))
@@ -63,6 +68,8 @@ def test_graph_replays_match_eager():
         o["lm"] = sb.spec_lm_head_stats(h, W, lpar, ltok, out=o.get("lm"), ws=ws_lm)
         o["gr"] = sb.spec_verify_greedy_stats(o["lm"]["row_argmax"], ltok, lpar, 3000, out=o.get("gr"))
         o["vlm"] = sb.spec_verify_lm_head(h, W, ltok, lpar, lunif, "typical", out=o.get("vlm"), ws=ws_vlm)
+        o["vrj"] = sb.spec_verify_lm_head(h, W, ltok, lpar, lunif, "reject", draft_probs=ldraft,
+                                          draft_row=ldrow, out=o.get("vrj"), ws=ws_vrj)
         return o
 
     eager = run({})

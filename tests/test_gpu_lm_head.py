@@ -192,7 +192,7 @@ def test_greedy_stats_errors():
     assert int(rv["accept_len"][0]) == 4 and int(rv["bonus"][0]) == 4   # path 0 -> 1 -> 3 -> 6 -> 7
 
 
-@pytest.mark.parametrize("mode", ["greedy", "typical"])
+@pytest.mark.parametrize("mode", ["greedy", "typical", "reject"])
 @pytest.mark.parametrize("seed,B,N,Dm,V,hscale", [(41, 2, 40, 256, 3000, 8.0), (42, 4, 16, 128, 700, 12.0),
                                                    (43, 1, 63, 4096, 128256, 1.0), (44, 8, 127, 256, 2000, 8.0)])
 def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
@@ -215,15 +215,25 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
     unif = g.random((B, N), dtype=np.float32)
     n_nodes = np.array([N - (b % 2) for b in range(B)], dtype=np.int32)
     eps, delta = float(np.float32(0.09)), float(np.float32(0.3))
+    draft = drow = None
+    if mode == "reject":
+        # per-parent draft rows: D_p = softmax(l_p + N(0, 0.5)) of the oracle's logits (inputs only)
+        x = np.nan_to_num(ref0["logits"], nan=0.0) + g.standard_normal(ref0["logits"].shape) * 0.5
+        e = np.exp(x - x.max(axis=2, keepdims=True))
+        draft = (e / e.sum(axis=2, keepdims=True)).astype(np.float32)
+        drow = np.maximum(inp["parents"], 0).astype(np.int32)
     print(f"verify_lm_head {mode} B={B} N={N} Dm={Dm} V={V}", flush=True)
     got = sb.spec_verify_lm_head(dev(inp["hidden"], torch.bfloat16), dev(inp["W"], torch.bfloat16), dev(tok),
-                                 dev(inp["parents"]), dev(unif), mode, n_nodes=dev(n_nodes), eps=eps, delta=delta)
+                                 dev(inp["parents"]), dev(unif), mode, n_nodes=dev(n_nodes), eps=eps, delta=delta,
+                                 draft_probs=None if draft is None else dev(draft),
+                                 draft_row=None if drow is None else dev(drow))
     torch.cuda.synchronize()
     got = {k: host(v) for k, v in got.items()}
     ref = oracle.lm_head_stats(inp["hidden"], inp["W"], inp["parents"], tok, n_nodes=n_nodes)
     logits = np.nan_to_num(ref["logits"], nan=0.0)
-    m_id = oracle.MODE_GREEDY if mode == "greedy" else oracle.MODE_TYPICAL
-    rv = oracle.verify(logits, tok, inp["parents"], unif, m_id, n_nodes=n_nodes, eps=eps, delta=delta)
+    m_id = {"greedy": oracle.MODE_GREEDY, "typical": oracle.MODE_TYPICAL, "reject": oracle.MODE_REJECT}[mode]
+    rv = oracle.verify(logits, tok, inp["parents"], unif, m_id, n_nodes=n_nodes, eps=eps, delta=delta,
+                       draft_probs=draft, draft_row=drow)
     d = bound(inp["hidden"], inp["W"])
     # greedy outcomes depend on the row arg-maxima only: the GPU's (same kernels) are read here
     st = sb.spec_lm_head_stats(dev(inp["hidden"], torch.bfloat16), dev(inp["W"], torch.bfloat16), dev(inp["parents"]),
@@ -242,10 +252,12 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
                 assert row[gam[b, i]] >= row.max() - 2 * d[b, i], f"sequence {b} row {i}: argmax off"
             if differ.size:
                 continue
-        else:
+        elif mode == "typical":
             H = np.log(ref["row_sum"][b, :nb]) - ref["row_ent"][b, :nb] / ref["row_sum"][b, :nb]
             if np.any(rv["margin"][b, 1:nb] < 6 * dmax * (H.max() + 1)):
                 continue
+        elif np.any(rv["margin"][b, 1:nb] < 3 * dmax + 1e-9):     # |u - min(1, T/D)|, T within 2 delta
+            continue
         compared += 1
         assert np.array_equal(got["node_accept"][b], rv["node_accept"][b]), f"sequence {b}: node_accept"
         assert int(got["accept_len"][b]) == int(rv["accept_len"][b]), f"sequence {b}: accept_len"
@@ -256,11 +268,17 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
             m = int(rv["m"][b])
             row = logits[b, m]
             T = np.exp(row - row.max())
-            C = np.cumsum(T) / T.sum()
+            T = T / T.sum()
+            q, tol = T, 4 * float(d[b, m]) + 1e-12
+            kids = [c for c in range(1, nb) if inp["parents"][b, c] == m]
+            if mode == "reject" and kids:
+                res = np.maximum(T - draft[b, drow[b, kids[0]]].astype(np.float64), 0.0)
+                if res.sum() > 0:
+                    q, tol = res, 4 * float(d[b, m]) / res.sum() + 1e-12
+            C = np.cumsum(q) / q.sum()
             t = int(got["bonus"][b])
             assert 0 <= t < V
             lo = C[t - 1] if t > 0 else 0.0
-            tol = 4 * float(d[b, m]) + 1e-12
             assert lo <= unif[b, 0] + tol and C[t] >= unif[b, 0] - tol, \
                 f"sequence {b}: bonus {t} outside the oracle's CDF step (u {unif[b, 0]}, [{lo}, {C[t]}])"
             bonus_checked += 1
@@ -269,4 +287,4 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
     print(f"  compared {compared} of {B} sequences; accept_len {got['accept_len'].tolist()}; "
           f"oracle {rv['accept_len'].tolist()}", flush=True)
     # at Dm = 4096 the typical margin bound (~1e-2 in ln T) can excuse a whole sequence
-    assert compared >= 1 or (mode == "typical" and Dm > 512)
+    assert compared >= 1 or (mode != "greedy" and Dm > 512)

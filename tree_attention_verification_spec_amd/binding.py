@@ -55,8 +55,8 @@ def lib():
     L.spec_verify_lm_head_workspace.restype = _Z
     L.spec_verify_lm_head_workspace.argtypes = [_I, _I, _I, _I]
     L.spec_verify_lm_head.restype = _I
-    L.spec_verify_lm_head.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F,
-                                      _P, _P, _P, _P, _P, _P, _Z, _P]
+    L.spec_verify_lm_head.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                                      _F, _F, _P, _P, _P, _P, _P, _P, _Z, _P]
     L.spec_tree_attn_workspace.restype = _Z
     L.spec_tree_attn_workspace.argtypes = [_I, _I, _I, _I, _I, _I, _I]
     L.spec_tree_attn.restype = _I
@@ -315,10 +315,13 @@ def verify_lm_head_workspace_bytes(B, N, Dm, V):
     return int(lib().spec_verify_lm_head_workspace(B, N, Dm, V))
 
 
-def spec_verify_lm_head(hidden, W, tokens, parents, uniforms, mode, n_nodes=None, eps=0.09, delta=0.3,
-                        max_depth=None, out=None, ws=None, stream=None):
+def spec_verify_lm_head(hidden, W, tokens, parents, uniforms, mode, n_nodes=None, draft_probs=None, draft_row=None,
+                        t2d=None, eps=0.09, delta=0.3, max_depth=None, out=None, ws=None, stream=None):
     B, N, Dm = hidden.shape
     V = W.shape[0]
+    R = Vd = 0
+    if draft_probs is not None:
+        _, R, Vd = draft_probs.shape
     dev = hidden.device
     mode = MODES.get(mode, mode)
     if max_depth is None:
@@ -335,7 +338,8 @@ def spec_verify_lm_head(hidden, W, tokens, parents, uniforms, mode, n_nodes=None
         _ptr(hidden, torch.bfloat16, (B, N, Dm), "hidden"), _ptr(W, torch.bfloat16, (V, Dm), "W"),
         _ptr(tokens, torch.int32, (B, N), "tokens"), _ptr(parents, torch.int32, (B, N), "parents"),
         _ptr(n_nodes, torch.int32, (B,), "n_nodes"), _ptr(uniforms, torch.float32, (B, N), "uniforms"),
-        B, N, Dm, V, int(max_depth), int(mode), float(eps), float(delta),
+        _ptr(draft_probs, torch.float32, (B, R, Vd), "draft_probs"), _ptr(draft_row, torch.int32, (B, N), "draft_row"),
+        _ptr(t2d, torch.int32, (V,), "t2d"), B, N, Dm, V, R, Vd, int(max_depth), int(mode), float(eps), float(delta),
         _ptr(out["accept_len"], torch.int32, (B,), "accept_len"),
         _ptr(out["path"], torch.int32, (B, max_depth + 1), "path"),
         _ptr(out["bonus"], torch.int32, (B,), "bonus"),

@@ -591,6 +591,128 @@ __global__ __launch_bounds__(kLThreads) void lmhead_merge_kernel(
 }
 
 
+// Rejection-sampling arguments of verify_lm_kernel and the plan it leaves for the residual draw:
+// plan[3b] = 1 when sequence b's bonus is a residual draw (else 0), plan[3b + 1] its draft row,
+// plan[3b + 2] the kept node m.
+struct LmDraft {
+  const float* draft;       // [B, R, Vd]
+  const int32_t* draft_row; // [B, N]
+  const int32_t* t2d;       // [V] or NULL
+  int R, Vd;
+  int32_t* plan;            // [B, 3]
+};
+
+// Row m of a sequence whose bonus is a residual draw, recomputed: grid (64-token tile, sequence),
+// four threads per token, eight 16-byte pairs in flight per thread.
+__global__ __launch_bounds__(kLThreads) void lm_row_kernel(const __bf16* __restrict__ X, const __bf16* __restrict__ W,
+                                                           int N, int Dm, int V, const int32_t* __restrict__ plan,
+                                                           float* __restrict__ rowbuf) {
+  const int b = blockIdx.y, tile = blockIdx.x;
+  if (plan[3 * b] != 1) return;
+  const int m = plan[3 * b + 2];
+  const int c = threadIdx.x, v = tile * kLRows + (c >> 2), part = c & 3;
+  float acc32 = 0.f;
+  if (v < V) {
+    const __bf16* wr = W + (size_t)v * Dm + part * 8;
+    const __bf16* hr = X + ((size_t)b * N + m) * Dm + part * 8;
+    const int nk = Dm / 32;
+    for (int k0 = 0; k0 < nk; k0 += 8) {
+      bf16x8 a8[8], h8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int k = (k0 + i < nk ? k0 + i : 0) * 32;
+        a8[i] = ld8(wr + k);
+        h8[i] = ld8(hr + k);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (k0 + i < nk)
+#pragma unroll
+          for (int e2 = 0; e2 < 8; ++e2) acc32 = fmaf((float)a8[i][e2], (float)h8[i][e2], acc32);
+    }
+  }
+  acc32 += __shfl_xor(acc32, 1);
+  acc32 += __shfl_xor(acc32, 2);
+  if (part == 0 && v < V) rowbuf[(size_t)b * V + v] = acc32;
+}
+
+// The residual draw: q_v = relu(exp(l_v - M) / S - D[v]) over the recomputed row (fp64 weights,
+// M and S the row's statistics), u Q placed by inverse CDF; a residual of zero mass draws from
+// T_m.  One workgroup per sequence; thread t owns a contiguous run of tokens.
+__global__ __launch_bounds__(kLThreads) void lm_residual_kernel(
+    const float* __restrict__ rowbuf, const float* __restrict__ row_max, const double* __restrict__ row_sum,
+    const float* __restrict__ uniforms, int N, int V, LmDraft dr, int32_t* __restrict__ bonus) {
+  __shared__ double s_w[kLThreads / kWave];
+  __shared__ int s_tok;
+  const int b = blockIdx.x, t = threadIdx.x, lane = t & (kWave - 1), wv = t >> 6;
+  if (dr.plan[3 * b] != 1) return;
+  const int r = dr.plan[3 * b + 1], m = dr.plan[3 * b + 2];
+  const float M = row_max[(size_t)b * N + m];
+  const double invS = 1.0 / row_sum[(size_t)b * N + m];
+  const float* row = rowbuf + (size_t)b * V;
+  const float* drow = dr.draft + ((size_t)b * dr.R + r) * dr.Vd;
+  const int per = (V + kLThreads - 1) / kLThreads;
+  const int lo = min(V, t * per), hi = min(V, lo + per);
+  auto weight = [&](int v, bool resid) -> double {
+    const double e = (double)expf(row[v] - M) * invS;
+    if (!resid) return e;
+    int dx = v;
+    if (dr.t2d) dx = dr.t2d[v];
+    const double d = (dx >= 0 && dx < dr.Vd) ? (double)drow[dx] : 0.0;
+    return fmax(e - d, 0.0);
+  };
+  auto block_scan = [&](double mine, double& before, double& total) {
+    double incl = mine;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const double y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == kWave - 1) s_w[wv] = incl;
+    __syncthreads();
+    before = incl - mine;
+    total = 0.0;
+    for (int q = 0; q < kLThreads / kWave; ++q) {
+      if (q < wv) before += s_w[q];
+      total += s_w[q];
+    }
+    __syncthreads();
+  };
+  double mine = 0.0;
+  for (int v = lo; v < hi; ++v) mine += weight(v, true);
+  double before, Q;
+  block_scan(mine, before, Q);
+  const bool resid = Q > 0.0;
+  if (!resid) {                              // zero residual: a draw from T_m
+    mine = 0.0;
+    for (int v = lo; v < hi; ++v) mine += weight(v, false);
+    block_scan(mine, before, Q);
+  }
+  if (t == 0) s_tok = -1;
+  __syncthreads();
+  const double target = (double)uniforms[(size_t)b * N] * Q;
+  if (mine > 0.0 && before <= target && target < before + mine) {
+    double run = before;
+    int tok = -1;
+    for (int v = lo; v < hi; ++v) {
+      const double w = weight(v, resid);
+      if (w > 0.0) tok = v;
+      run += w;
+      if (run > target && w > 0.0) break;
+    }
+    s_tok = tok;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int tok = s_tok;
+    if (tok < 0) {                           // u Q at the rounded total: the last token with weight
+      for (int v = V - 1; v >= 0 && tok < 0; --v)
+        if (weight(v, resid) > 0.0) tok = v;
+    }
+    bonus[b] = tok;
+  }
+}
+
 // Greedy or typical verification straight from the LM head's statistics, with the bonus token.
 // One workgroup per sequence.  Node c (parent p, token x): GREEDY accepts iff x is p's lowest
 // argmax; TYPICAL iff T_p[x] = exp(l_p[x] - max_p) / S_p >= min(eps, delta exp(-H_p)), with
@@ -608,12 +730,12 @@ __global__ __launch_bounds__(SPEC_MAX_NODES) void verify_lm_kernel(
     const __bf16* __restrict__ X, const __bf16* __restrict__ W, int Dm,
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ parents,
     const int32_t* __restrict__ n_nodes, const float* __restrict__ uniforms, int N, int V,
-    int max_depth, int mode, float eps, float delta, int32_t* __restrict__ accept_len,
+    int max_depth, int mode, float eps, float delta, LmDraft dr, int32_t* __restrict__ accept_len,
     int32_t* __restrict__ path, int32_t* __restrict__ bonus, uint8_t* __restrict__ node_accept,
     int32_t* __restrict__ err) {
   __shared__ int s_par[SPEC_MAX_NODES];
   __shared__ unsigned char s_acc[SPEC_MAX_NODES];
-  __shared__ int s_err, s_best;
+  __shared__ int s_err, s_best, s_kid;
   __shared__ double s_wsum[SPEC_MAX_NODES / kWave];
   __shared__ int s_tile;
   __shared__ double s_pre, s_scale;
@@ -627,6 +749,7 @@ __global__ __launch_bounds__(SPEC_MAX_NODES) void verify_lm_kernel(
   if (c == 0) {
     s_err = INT_MAX;
     s_best = -1;
+    s_kid = INT_MAX;
   }
   if (c < N) s_par[c] = parents[base + c];
   __syncthreads();
@@ -653,8 +776,19 @@ __global__ __launch_bounds__(SPEC_MAX_NODES) void verify_lm_kernel(
       else {
         const double S = row_sum[base + p];
         const double T = (double)expf(cand[base + c] - row_max[base + p]) / S;
-        const double H = log(S) - row_ent[base + p] / S;
-        acc = T >= fmin((double)eps, (double)delta * exp(-H));
+        if (mode == SPEC_VERIFY_TYPICAL) {
+          const double H = log(S) - row_ent[base + p] / S;
+          acc = T >= fmin((double)eps, (double)delta * exp(-H));
+        } else {                              // REJECT: u D[x] < T[x]
+          const int r = dr.draft_row[base + c];
+          const int dx = dr.t2d ? dr.t2d[x] : x;
+          if (r < 0 || r >= dr.R) code = SPEC_ERR_DRAFTROW;
+          else if (dx < -1 || dx >= dr.Vd) code = SPEC_ERR_MAP;
+          else {
+            const double D = dx >= 0 ? (double)dr.draft[((size_t)b * dr.R + r) * dr.Vd + dx] : 0.0;
+            acc = (double)uniforms[base + c] * D < T;
+          }
+        }
       }
     }
     if (code) atomicMin(&s_err, err_word(c, code));
@@ -684,7 +818,21 @@ __global__ __launch_bounds__(SPEC_MAX_NODES) void verify_lm_kernel(
     if (!ok) bonus[b] = -1;
     else if (mode == SPEC_VERIFY_GREEDY) bonus[b] = row_argmax[base + m];
   }
+  if (mode == SPEC_VERIFY_REJECT && c == 0) dr.plan[3 * b] = 0;
   if (!ok || mode == SPEC_VERIFY_GREEDY) return;            // uniform across the workgroup
+  if (mode == SPEC_VERIFY_REJECT) {
+    // m with children: a residual draw over the whole row (lm_row_kernel, lm_residual_kernel)
+    if (c < n && c > 0 && s_par[c] == m) atomicMin(&s_kid, c);
+    __syncthreads();
+    if (s_kid != INT_MAX) {
+      if (c == 0) {
+        dr.plan[3 * b] = 1;
+        dr.plan[3 * b + 1] = dr.draft_row[base + s_kid];
+        dr.plan[3 * b + 2] = m;
+      }
+      return;                                // uniform: s_kid read after the barrier
+    }
+  }
 
   // ---- TYPICAL bonus: the tile of row m holding u Z, from the per-tile partials
   const LmPart* pp = parts + (base + m) * nblk;
@@ -968,9 +1116,9 @@ void launch_lm(const __bf16* X, const __bf16* Wb, const int32_t* parents, const 
 
 // spec_verify_lm_head's own part of the workspace, after the LM head's: the statistics
 struct VlLayout {
-  size_t mx, am, sum, ent, cand, err, total;
+  size_t mx, am, sum, ent, cand, err, plan, rowbuf, total;
 };
-VlLayout vl_layout(const LmLayout& L, int B, int N) {
+VlLayout vl_layout(const LmLayout& L, int B, int N, int V) {
   const size_t M = (size_t)B * N;
   VlLayout v{};
   v.mx = L.total;
@@ -979,7 +1127,9 @@ VlLayout vl_layout(const LmLayout& L, int B, int N) {
   v.ent = v.sum + align_up(M * sizeof(double), 256);
   v.cand = v.ent + align_up(M * sizeof(double), 256);
   v.err = v.cand + align_up(M * sizeof(float), 256);
-  v.total = v.err + align_up((size_t)B * sizeof(int32_t), 256);
+  v.plan = v.err + align_up((size_t)B * sizeof(int32_t), 256);
+  v.rowbuf = v.plan + align_up((size_t)B * 3 * sizeof(int32_t), 256);
+  v.total = v.rowbuf + align_up((size_t)B * V * sizeof(float), 256);     // row m, residual draws
   return v;
 }
 }  // namespace
@@ -1003,24 +1153,30 @@ extern "C" spec_status spec_lm_head_stats(const void* hidden, const void* W, con
 
 extern "C" size_t spec_verify_lm_head_workspace(int B, int N, int Dm, int V) {
   if (B < 1 || N < 1 || Dm < 1 || V < 1) return 0;
-  return vl_layout(lm_layout(B, N, V, Dm), B, N).total;
+  return vl_layout(lm_layout(B, N, V, Dm), B, N, V).total;
 }
 
 extern "C" spec_status spec_verify_lm_head(const void* hidden, const void* W, const int32_t* tokens,
                                            const int32_t* parents, const int32_t* n_nodes,
-                                           const float* uniforms, int B, int N, int Dm, int V,
-                                           int max_depth, spec_mode mode, float eps, float delta,
-                                           int32_t* accept_len, int32_t* path, int32_t* bonus_token,
-                                           uint8_t* node_accept, int32_t* err, void* workspace,
-                                           size_t ws_bytes, void* stream) {
+                                           const float* uniforms, const float* draft_probs,
+                                           const int32_t* draft_row, const int32_t* t2d, int B, int N,
+                                           int Dm, int V, int R, int Vd, int max_depth, spec_mode mode,
+                                           float eps, float delta, int32_t* accept_len, int32_t* path,
+                                           int32_t* bonus_token, uint8_t* node_accept, int32_t* err,
+                                           void* workspace, size_t ws_bytes, void* stream) {
   const spec_status st = check_lm(hidden, W, B, N, Dm, V);
   if (st != SPEC_OK) return st;
   if (!tokens || !parents || !uniforms || !accept_len || !path || !bonus_token || !err || max_depth < 0)
     return SPEC_EINVAL;
-  if (mode != SPEC_VERIFY_GREEDY && mode != SPEC_VERIFY_TYPICAL) return SPEC_EUNSUPPORTED;
+  if (mode != SPEC_VERIFY_GREEDY && mode != SPEC_VERIFY_TYPICAL && mode != SPEC_VERIFY_REJECT)
+    return SPEC_EUNSUPPORTED;
   if (mode == SPEC_VERIFY_TYPICAL && (!(eps == eps) || !(delta == delta))) return SPEC_EINVAL;
+  if (mode == SPEC_VERIFY_REJECT) {
+    if (!draft_probs || !draft_row || R < 1 || Vd < 1) return SPEC_EINVAL;
+    if (!t2d && Vd != V) return SPEC_EINVAL;
+  }
   const LmLayout L = lm_layout(B, N, V, Dm);
-  const VlLayout VL = vl_layout(L, B, N);
+  const VlLayout VL = vl_layout(L, B, N, V);
   if (!workspace || ws_bytes < VL.total) return SPEC_EWORKSPACE;
   char* w = static_cast<char*>(workspace);
   float* mx = reinterpret_cast<float*>(w + VL.mx);
@@ -1029,6 +1185,10 @@ extern "C" spec_status spec_verify_lm_head(const void* hidden, const void* W, co
   double* ent = reinterpret_cast<double*>(w + VL.ent);
   float* cand = reinterpret_cast<float*>(w + VL.cand);
   int32_t* lerr = reinterpret_cast<int32_t*>(w + VL.err);
+  LmDraft dr{};
+  dr.draft = draft_probs; dr.draft_row = draft_row; dr.t2d = t2d; dr.R = R; dr.Vd = Vd;
+  dr.plan = reinterpret_cast<int32_t*>(w + VL.plan);
+  float* rowbuf = reinterpret_cast<float*>(w + VL.rowbuf);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const __bf16* X = static_cast<const __bf16*>(hidden);
   const __bf16* Wb = static_cast<const __bf16*>(W);
@@ -1036,7 +1196,13 @@ extern "C" spec_status spec_verify_lm_head(const void* hidden, const void* W, co
   launch("verify_lm", verify_lm_kernel, dim3(B), dim3(SPEC_MAX_NODES), s, (const float*)mx, (const int32_t*)am,
          (const double*)sum, (const double*)ent, (const float*)cand,
          (const LmPart*)reinterpret_cast<LmPart*>(w + L.parts), L.nblk, X, Wb, Dm, tokens, parents, n_nodes,
-         uniforms, N, V, max_depth, (int)mode, eps, delta, accept_len, path, bonus_token, node_accept, err);
+         uniforms, N, V, max_depth, (int)mode, eps, delta, dr, accept_len, path, bonus_token, node_accept, err);
+  if (mode == SPEC_VERIFY_REJECT) {
+    launch("verify_lm_row", lm_row_kernel, dim3((unsigned)L.nblk, (unsigned)B), dim3(kLThreads), s, X, Wb, N, Dm, V,
+           (const int32_t*)dr.plan, rowbuf);
+    launch("verify_lm_residual", lm_residual_kernel, dim3(B), dim3(kLThreads), s, (const float*)rowbuf,
+           (const float*)mx, (const double*)sum, uniforms, N, V, dr, bonus_token);
+  }
   return launch_status();
 }
 
