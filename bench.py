@@ -287,9 +287,17 @@ def lm_head_stats_timing(w, reps=20, Dm=4096):
     ver = sb.spec_verify_greedy_stats(out["row_argmax"], tok, par, V)
     uni = torch.rand((B, N), generator=g, device="cuda")
     vtyp = sb.spec_verify_lm_head(h, W, tok, par, uni, "typical")
+    # draft rows that put most of their mass on the drafted tokens: the root's children are
+    # rejected, so the residual draw takes the recomputed-row path (the costly case)
+    drow = par.clamp(min=0)
+    draft = torch.rand((B, N, V), generator=g, device="cuda") ** 8
+    bi = torch.arange(B, device="cuda").unsqueeze(1).expand(B, N)
+    draft[bi[:, 1:], drow[:, 1:].long(), tok[:, 1:].long()] += 1e4
+    draft /= draft.sum(dim=2, keepdim=True)
+    vrej = sb.spec_verify_lm_head(h, W, tok, par, uni, "reject", draft_probs=draft, draft_row=drow)
     torch.cuda.synchronize()
     assert int(out["err"].abs().sum()) == 0 and int(ver["err"].abs().sum()) == 0
-    assert int(vtyp["err"].abs().sum()) == 0
+    assert int(vtyp["err"].abs().sum()) == 0 and int(vrej["err"].abs().sum()) == 0
     try:
         sb.prof_reset()
         sb.prof_enable(True)
@@ -304,19 +312,27 @@ def lm_head_stats_timing(w, reps=20, Dm=4096):
         for _ in range(reps):
             sb.spec_verify_lm_head(h, W, tok, par, uni, "typical", out=vtyp)
         torch.cuda.synchronize()
-        sb.prof_enable(False)
         ms5, cnt5 = sb.prof_read("verify_lm")
+        sb.prof_reset()
+        for _ in range(reps):
+            sb.spec_verify_lm_head(h, W, tok, par, uni, "reject", draft_probs=draft, draft_row=drow, out=vrej)
+        torch.cuda.synchronize()
+        sb.prof_enable(False)
+        rej = [sb.prof_read(k) for k in ("verify_lm", "verify_lm_row", "verify_lm_residual")]
     finally:
         sb.prof_enable(False)
         sb.prof_reset()
     us, us_merge, us_perm, us_greedy = ms / cnt * 1e3, ms2 / cnt2 * 1e3, ms3 / cnt3 * 1e3, ms4 / cnt4 * 1e3
     us_typ = ms5 / cnt5 * 1e3
+    us_rej = [m / c * 1e3 for m, c in rej]
     nbytes = V * Dm * 2 + B * N * Dm * 2
     flops = 2 * B * N * Dm * V
-    del W
+    del W, draft
     return {"shape": f"[{B * N} x {Dm}] x [{Dm} x {V}]", "us": round(us, 3), "merge_us": round(us_merge, 3),
             "xperm_us": round(us_perm, 3), "greedy_verify_us": round(us_greedy, 3),
             "typical_verify_us": round(us_typ, 3),
+            "reject_verify_us": {"decide": round(us_rej[0], 3), "row": round(us_rej[1], 3),
+                                 "residual": round(us_rej[2], 3)},
             "algorithmic_bytes": nbytes, "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
             "hbm_frac": round(nbytes / (us * 1e-6) / 8e12, 4),
             "achieved_TFLOPs": round(flops / (us * 1e-6) / 1e12, 1)}

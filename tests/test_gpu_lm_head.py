@@ -192,7 +192,7 @@ def test_greedy_stats_errors():
     assert int(rv["accept_len"][0]) == 4 and int(rv["bonus"][0]) == 4   # path 0 -> 1 -> 3 -> 6 -> 7
 
 
-@pytest.mark.parametrize("mode", ["greedy", "typical", "reject"])
+@pytest.mark.parametrize("mode", ["greedy", "typical", "reject", "reject_row"])
 @pytest.mark.parametrize("seed,B,N,Dm,V,hscale", [(41, 2, 40, 256, 3000, 8.0), (42, 4, 16, 128, 700, 12.0),
                                                    (43, 1, 63, 4096, 128256, 1.0), (44, 8, 127, 256, 2000, 8.0)])
 def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
@@ -201,7 +201,11 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
     the sequence's logit bound) are counted, not compared, and so is everything downstream.  The TYPICAL bonus must be a
     token the oracle's inverse CDF gives for some u' within 4 delta_m of u (the GPU's CDF is
     exact up to the fp32 logits).  Greedy sequences are compared whenever the GPU's row arg-maxima
-    (read through spec_lm_head_stats, the same kernels) equal the oracle's."""
+    (read through spec_lm_head_stats, the same kernels) equal the oracle's.  REJECT decisions within
+    3 delta of u are excused; its bonus must lie within the tolerance of the oracle's residual CDF
+    step (or of T_m's at a leaf).  reject_row drafts random tokens with draft rows peaked on them
+    and node uniforms in [0.1, 1), so the root's children are rejected and the bonus is a residual
+    draw over a recomputed row."""
     need_gpu()
     inp = wl.lm_head_inputs(seed=seed, B=B, N=N, Dm=Dm, V=V, max_depth=6)
     inp["hidden"] = wl.round_bf16(inp["hidden"] * np.float32(hscale))
@@ -210,28 +214,36 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
     tok = inp["tokens"].copy()
     for b in range(B):
         for c in range(1, N):
-            if g.random() < 0.6:
+            if g.random() < 0.6 and mode != "reject_row":
                 tok[b, c] = ref0["row_argmax"][b, inp["parents"][b, c]]
     unif = g.random((B, N), dtype=np.float32)
     n_nodes = np.array([N - (b % 2) for b in range(B)], dtype=np.int32)
     eps, delta = float(np.float32(0.09)), float(np.float32(0.3))
     draft = drow = None
-    if mode == "reject":
+    if mode.startswith("reject"):
         # per-parent draft rows: D_p = softmax(l_p + N(0, 0.5)) of the oracle's logits (inputs only)
         x = np.nan_to_num(ref0["logits"], nan=0.0) + g.standard_normal(ref0["logits"].shape) * 0.5
         e = np.exp(x - x.max(axis=2, keepdims=True))
-        draft = (e / e.sum(axis=2, keepdims=True)).astype(np.float32)
+        draft = e / e.sum(axis=2, keepdims=True)
         drow = np.maximum(inp["parents"], 0).astype(np.int32)
+        if mode == "reject_row":
+            unif[:, 1:] = np.float32(0.1) + np.float32(0.9) * unif[:, 1:]   # clear of T/D ~ 0
+            for b in range(B):
+                for c in range(1, N):
+                    draft[b, drow[b, c], tok[b, c]] += 1.0
+            draft /= draft.sum(axis=2, keepdims=True)
+        draft = draft.astype(np.float32)
     print(f"verify_lm_head {mode} B={B} N={N} Dm={Dm} V={V}", flush=True)
     got = sb.spec_verify_lm_head(dev(inp["hidden"], torch.bfloat16), dev(inp["W"], torch.bfloat16), dev(tok),
-                                 dev(inp["parents"]), dev(unif), mode, n_nodes=dev(n_nodes), eps=eps, delta=delta,
+                                 dev(inp["parents"]), dev(unif), mode.split("_")[0], n_nodes=dev(n_nodes),
+                                 eps=eps, delta=delta,
                                  draft_probs=None if draft is None else dev(draft),
                                  draft_row=None if drow is None else dev(drow))
     torch.cuda.synchronize()
     got = {k: host(v) for k, v in got.items()}
     ref = oracle.lm_head_stats(inp["hidden"], inp["W"], inp["parents"], tok, n_nodes=n_nodes)
     logits = np.nan_to_num(ref["logits"], nan=0.0)
-    m_id = {"greedy": oracle.MODE_GREEDY, "typical": oracle.MODE_TYPICAL, "reject": oracle.MODE_REJECT}[mode]
+    m_id = {"greedy": oracle.MODE_GREEDY, "typical": oracle.MODE_TYPICAL, "reject": oracle.MODE_REJECT}[mode.split("_")[0]]
     rv = oracle.verify(logits, tok, inp["parents"], unif, m_id, n_nodes=n_nodes, eps=eps, delta=delta,
                        draft_probs=draft, draft_row=drow)
     d = bound(inp["hidden"], inp["W"])
@@ -240,7 +252,7 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
                                dev(tok), n_nodes=dev(n_nodes))
     torch.cuda.synchronize()
     gam = host(st["row_argmax"])
-    compared = bonus_checked = 0
+    compared = bonus_checked = resid_checked = 0
     for b in range(B):
         nb = int(n_nodes[b])
         assert int(got["err"][b]) == int(rv["err"][b])
@@ -271,10 +283,11 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
             T = T / T.sum()
             q, tol = T, 4 * float(d[b, m]) + 1e-12
             kids = [c for c in range(1, nb) if inp["parents"][b, c] == m]
-            if mode == "reject" and kids:
+            if mode.startswith("reject") and kids:
                 res = np.maximum(T - draft[b, drow[b, kids[0]]].astype(np.float64), 0.0)
                 if res.sum() > 0:
                     q, tol = res, 4 * float(d[b, m]) / res.sum() + 1e-12
+                    resid_checked += 1
             C = np.cumsum(q) / q.sum()
             t = int(got["bonus"][b])
             assert 0 <= t < V
@@ -288,3 +301,6 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
           f"oracle {rv['accept_len'].tolist()}", flush=True)
     # at Dm = 4096 the typical margin bound (~1e-2 in ln T) can excuse a whole sequence
     assert compared >= 1 or (mode != "greedy" and Dm > 512)
+    if mode == "reject_row":
+        print(f"  residual draws checked: {resid_checked}", flush=True)
+        assert resid_checked >= 1

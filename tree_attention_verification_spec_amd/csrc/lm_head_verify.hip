@@ -38,6 +38,7 @@ constexpr int kLThreads = 256;
 constexpr int kLKWaves = 4;                 // K slices per workgroup
 constexpr int kLRB = 4;                     // 16-row blocks of W per workgroup
 constexpr int kLRows = 16 * kLRB;           // vocabulary rows per workgroup
+static_assert(kLRows == kWave && kLThreads == 4 * kLRows, "one token per lane, four threads per token");
 constexpr int kLMaxCols = 64;               // hidden states (columns) per workgroup
 constexpr int kLMaxRows = 4096;             // B * N limit
 constexpr int kMergePer = 8;                // partials per merging thread held in registers
@@ -602,15 +603,30 @@ struct LmDraft {
   int32_t* plan;            // [B, 3]
 };
 
+// Weight of token v in a residual draw from row m (logit l, statistics M and 1/S): the residual
+// relu(T[v] - D[v]) with T[v] = exp(l - M) / S, or T[v] itself when the residual has no mass.
+// Draft ids come through t2d when the draft vocabulary differs; an id outside it has D = 0.
+__device__ __forceinline__ double draw_weight(float l, float M, double invS, const float* __restrict__ drow,
+                                              const LmDraft& dr, int v, bool resid) {
+  const double e = (double)expf(l - M) * invS;
+  if (!resid) return e;
+  const int dx = dr.t2d ? dr.t2d[v] : v;
+  const double d = (dx >= 0 && dx < dr.Vd) ? (double)drow[dx] : 0.0;
+  return fmax(e - d, 0.0);
+}
+
 // Row m of a sequence whose bonus is a residual draw, recomputed: grid (64-token tile, sequence),
-// four threads per token, eight 16-byte pairs in flight per thread.
-__global__ __launch_bounds__(kLThreads) void lm_row_kernel(const __bf16* __restrict__ X, const __bf16* __restrict__ W,
-                                                           int N, int Dm, int V, const int32_t* __restrict__ plan,
-                                                           float* __restrict__ rowbuf) {
+// four threads per token, eight 16-byte pairs in flight per thread.  Besides the row, each tile
+// leaves its fp64 (residual, target) weight sums for the draw's scan.
+__global__ __launch_bounds__(kLThreads) void lm_row_kernel(
+    const __bf16* __restrict__ X, const __bf16* __restrict__ W, int N, int Dm, int V,
+    const float* __restrict__ row_max, const double* __restrict__ row_sum, LmDraft dr,
+    float* __restrict__ rowbuf, double2* __restrict__ tsum) {
+  __shared__ double2 s_t[kLThreads / kWave];
   const int b = blockIdx.y, tile = blockIdx.x;
-  if (plan[3 * b] != 1) return;
-  const int m = plan[3 * b + 2];
-  const int c = threadIdx.x, v = tile * kLRows + (c >> 2), part = c & 3;
+  if (dr.plan[3 * b] != 1) return;
+  const int r = dr.plan[3 * b + 1], m = dr.plan[3 * b + 2];
+  const int c = threadIdx.x, v = tile * kLRows + (c >> 2), part = c & 3, wv = c >> 6;
   float acc32 = 0.f;
   if (v < V) {
     const __bf16* wr = W + (size_t)v * Dm + part * 8;
@@ -633,36 +649,76 @@ __global__ __launch_bounds__(kLThreads) void lm_row_kernel(const __bf16* __restr
   }
   acc32 += __shfl_xor(acc32, 1);
   acc32 += __shfl_xor(acc32, 2);
-  if (part == 0 && v < V) rowbuf[(size_t)b * V + v] = acc32;
+  double wr_ = 0.0, wt_ = 0.0;
+  if (part == 0 && v < V) {
+    rowbuf[(size_t)b * V + v] = acc32;
+    const float M = row_max[(size_t)b * N + m];
+    const double invS = 1.0 / row_sum[(size_t)b * N + m];
+    const float* drow = dr.draft + ((size_t)b * dr.R + r) * dr.Vd;
+    wr_ = draw_weight(acc32, M, invS, drow, dr, v, true);
+    wt_ = draw_weight(acc32, M, invS, drow, dr, v, false);
+  }
+  wr_ = wave_sum(wr_);
+  wt_ = wave_sum(wt_);
+  if ((c & (kWave - 1)) == 0) s_t[wv] = make_double2(wr_, wt_);
+  __syncthreads();
+  if (c == 0) {
+    double2 t = s_t[0];
+    for (int q = 1; q < kLThreads / kWave; ++q) {
+      t.x += s_t[q].x;
+      t.y += s_t[q].y;
+    }
+    tsum[(size_t)b * gridDim.x + tile] = t;
+  }
 }
 
-// The residual draw: q_v = relu(exp(l_v - M) / S - D[v]) over the recomputed row (fp64 weights,
-// M and S the row's statistics), u Q placed by inverse CDF; a residual of zero mass draws from
-// T_m.  One workgroup per sequence; thread t owns a contiguous run of tokens.
+// The residual draw: q_v = relu(T[v] - D[v]) over the recomputed row, u Q placed by inverse CDF
+// (Q the sum of the tiles' residual sums; a residual of zero mass draws from T_m instead).  One
+// workgroup per sequence: a block scan over the tile sums finds the tile holding u Q, then one
+// wave scans that tile's 64 weights, the remainder scaled to the wave's own total of the tile
+// (equal to the stored sum up to the order of the fp64 additions).
 __global__ __launch_bounds__(kLThreads) void lm_residual_kernel(
-    const float* __restrict__ rowbuf, const float* __restrict__ row_max, const double* __restrict__ row_sum,
+    const float* __restrict__ rowbuf, const double2* __restrict__ tsum, int nblk,
+    const float* __restrict__ row_max, const double* __restrict__ row_sum,
     const float* __restrict__ uniforms, int N, int V, LmDraft dr, int32_t* __restrict__ bonus) {
   __shared__ double s_w[kLThreads / kWave];
-  __shared__ int s_tok;
+  __shared__ int s_tile;
+  __shared__ double s_pre;
   const int b = blockIdx.x, t = threadIdx.x, lane = t & (kWave - 1), wv = t >> 6;
   if (dr.plan[3 * b] != 1) return;
   const int r = dr.plan[3 * b + 1], m = dr.plan[3 * b + 2];
-  const float M = row_max[(size_t)b * N + m];
-  const double invS = 1.0 / row_sum[(size_t)b * N + m];
-  const float* row = rowbuf + (size_t)b * V;
-  const float* drow = dr.draft + ((size_t)b * dr.R + r) * dr.Vd;
-  const int per = (V + kLThreads - 1) / kLThreads;
-  const int lo = min(V, t * per), hi = min(V, lo + per);
-  auto weight = [&](int v, bool resid) -> double {
-    const double e = (double)expf(row[v] - M) * invS;
-    if (!resid) return e;
-    int dx = v;
-    if (dr.t2d) dx = dr.t2d[v];
-    const double d = (dx >= 0 && dx < dr.Vd) ? (double)drow[dx] : 0.0;
-    return fmax(e - d, 0.0);
-  };
-  auto block_scan = [&](double mine, double& before, double& total) {
-    double incl = mine;
+  const double2* ts = tsum + (size_t)b * nblk;
+  // total residual mass (fixed order: per-thread strided sums, then the waves in order)
+  double part = 0.0;
+  for (int j = t; j < nblk; j += kLThreads) part += ts[j].x;
+  part = wave_sum(part);
+  if (lane == 0) s_w[wv] = part;
+  if (t == 0) {
+    s_tile = -1;
+    s_pre = -1.0;
+  }
+  __syncthreads();
+  double Q = 0.0;
+  for (int q = 0; q < kLThreads / kWave; ++q) Q += s_w[q];
+  const bool resid = Q > 0.0;
+  if (!resid) {
+    __syncthreads();
+    part = 0.0;
+    for (int j = t; j < nblk; j += kLThreads) part += ts[j].y;
+    part = wave_sum(part);
+    if (lane == 0) s_w[wv] = part;
+    __syncthreads();
+    Q = 0.0;
+    for (int q = 0; q < kLThreads / kWave; ++q) Q += s_w[q];
+  }
+  __syncthreads();
+  const double target = (double)uniforms[(size_t)b * N] * Q;
+  // chunks of kLThreads tiles: each thread's tile weight, a block scan, the first crossing
+  double carry = 0.0;
+  for (int j0 = 0; j0 < nblk; j0 += kLThreads) {
+    const int j = j0 + t;
+    const double wj = j < nblk ? (resid ? ts[j].x : ts[j].y) : 0.0;
+    double incl = wj;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
       const double y = __shfl_up(incl, o);
@@ -670,47 +726,46 @@ __global__ __launch_bounds__(kLThreads) void lm_residual_kernel(
     }
     if (lane == kWave - 1) s_w[wv] = incl;
     __syncthreads();
-    before = incl - mine;
-    total = 0.0;
-    for (int q = 0; q < kLThreads / kWave; ++q) {
-      if (q < wv) before += s_w[q];
-      total += s_w[q];
+    double off = carry;
+    for (int q = 0; q < wv; ++q) off += s_w[q];
+    const double before = off + incl - wj;
+    if (wj > 0.0 && before <= target && target < before + wj) {
+      s_tile = j;                            // one thread at most: the ranges are disjoint
+      s_pre = before;
     }
+    double tot = 0.0;
+    for (int q = 0; q < kLThreads / kWave; ++q) tot += s_w[q];
+    carry += tot;
     __syncthreads();
-  };
-  double mine = 0.0;
-  for (int v = lo; v < hi; ++v) mine += weight(v, true);
-  double before, Q;
-  block_scan(mine, before, Q);
-  const bool resid = Q > 0.0;
-  if (!resid) {                              // zero residual: a draw from T_m
-    mine = 0.0;
-    for (int v = lo; v < hi; ++v) mine += weight(v, false);
-    block_scan(mine, before, Q);
+    if (s_tile >= 0) break;                  // uniform: read after the barrier
   }
-  if (t == 0) s_tok = -1;
-  __syncthreads();
-  const double target = (double)uniforms[(size_t)b * N] * Q;
-  if (mine > 0.0 && before <= target && target < before + mine) {
-    double run = before;
-    int tok = -1;
-    for (int v = lo; v < hi; ++v) {
-      const double w = weight(v, resid);
-      if (w > 0.0) tok = v;
-      run += w;
-      if (run > target && w > 0.0) break;
-    }
-    s_tok = tok;
+  if (wv != 0) return;
+  int tile = s_tile;
+  const bool last = tile < 0;                // u Q at or past the rounded total: the last token
+  if (last) {                                // with weight of the last tile with weight
+    tile = nblk - 1;
+    while (tile > 0 && !((resid ? ts[tile].x : ts[tile].y) > 0.0)) --tile;
   }
-  __syncthreads();
-  if (t == 0) {
-    int tok = s_tok;
-    if (tok < 0) {                           // u Q at the rounded total: the last token with weight
-      for (int v = V - 1; v >= 0 && tok < 0; --v)
-        if (weight(v, resid) > 0.0) tok = v;
-    }
-    bonus[b] = tok;
+  const float M = row_max[(size_t)b * N + m];
+  const double invS = 1.0 / row_sum[(size_t)b * N + m];
+  const float* drow = dr.draft + ((size_t)b * dr.R + r) * dr.Vd;
+  const int v = tile * kLRows + lane;
+  const double w = v < V ? draw_weight(rowbuf[(size_t)b * V + v], M, invS, drow, dr, v, resid) : 0.0;
+  double incl = w;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
   }
+  const double tot = __shfl(incl, kWave - 1);
+  const double stored = resid ? ts[tile].x : ts[tile].y;
+  const double rem = last ? tot : (target - s_pre) / stored * tot;
+  const unsigned long long cross = __ballot(w > 0.0 && incl > rem);
+  const unsigned long long pos = __ballot(w > 0.0);
+  int pick;
+  if (cross) pick = __ffsll((long long)cross) - 1;
+  else pick = pos ? 63 - __clzll((long long)pos) : 0;
+  if (lane == 0) bonus[b] = tile * kLRows + pick;
 }
 
 // Greedy or typical verification straight from the LM head's statistics, with the bonus token.
@@ -1116,7 +1171,7 @@ void launch_lm(const __bf16* X, const __bf16* Wb, const int32_t* parents, const 
 
 // spec_verify_lm_head's own part of the workspace, after the LM head's: the statistics
 struct VlLayout {
-  size_t mx, am, sum, ent, cand, err, plan, rowbuf, total;
+  size_t mx, am, sum, ent, cand, err, plan, rowbuf, tsum, total;
 };
 VlLayout vl_layout(const LmLayout& L, int B, int N, int V) {
   const size_t M = (size_t)B * N;
@@ -1129,7 +1184,8 @@ VlLayout vl_layout(const LmLayout& L, int B, int N, int V) {
   v.err = v.cand + align_up(M * sizeof(float), 256);
   v.plan = v.err + align_up((size_t)B * sizeof(int32_t), 256);
   v.rowbuf = v.plan + align_up((size_t)B * 3 * sizeof(int32_t), 256);
-  v.total = v.rowbuf + align_up((size_t)B * V * sizeof(float), 256);     // row m, residual draws
+  v.tsum = v.rowbuf + align_up((size_t)B * V * sizeof(float), 256);      // row m, residual draws
+  v.total = v.tsum + align_up((size_t)B * L.nblk * sizeof(double2), 256);  // its tile sums
   return v;
 }
 }  // namespace
@@ -1198,10 +1254,11 @@ extern "C" spec_status spec_verify_lm_head(const void* hidden, const void* W, co
          (const LmPart*)reinterpret_cast<LmPart*>(w + L.parts), L.nblk, X, Wb, Dm, tokens, parents, n_nodes,
          uniforms, N, V, max_depth, (int)mode, eps, delta, dr, accept_len, path, bonus_token, node_accept, err);
   if (mode == SPEC_VERIFY_REJECT) {
+    double2* tsum = reinterpret_cast<double2*>(w + VL.tsum);
     launch("verify_lm_row", lm_row_kernel, dim3((unsigned)L.nblk, (unsigned)B), dim3(kLThreads), s, X, Wb, N, Dm, V,
-           (const int32_t*)dr.plan, rowbuf);
+           (const float*)mx, (const double*)sum, dr, rowbuf, tsum);
     launch("verify_lm_residual", lm_residual_kernel, dim3(B), dim3(kLThreads), s, (const float*)rowbuf,
-           (const float*)mx, (const double*)sum, uniforms, N, V, dr, bonus_token);
+           (const double2*)tsum, L.nblk, (const float*)mx, (const double*)sum, uniforms, N, V, dr, bonus_token);
   }
   return launch_status();
 }
