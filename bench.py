@@ -318,7 +318,7 @@ def lm_head_stats_timing(w, reps=20, Dm=4096):
             sb.spec_verify_lm_head(h, W, tok, par, uni, "reject", draft_probs=draft, draft_row=drow, out=vrej)
         torch.cuda.synchronize()
         sb.prof_enable(False)
-        rej = [sb.prof_read(k) for k in ("verify_lm", "verify_lm_row", "verify_lm_residual")]
+        rej = [sb.prof_read(k) for k in ("verify_lm", "verify_lm_tilesum", "verify_lm_residual", "lm_head_stats")]
     finally:
         sb.prof_enable(False)
         sb.prof_reset()
@@ -331,7 +331,8 @@ def lm_head_stats_timing(w, reps=20, Dm=4096):
     return {"shape": f"[{B * N} x {Dm}] x [{Dm} x {V}]", "us": round(us, 3), "merge_us": round(us_merge, 3),
             "xperm_us": round(us_perm, 3), "greedy_verify_us": round(us_greedy, 3),
             "typical_verify_us": round(us_typ, 3),
-            "reject_verify_us": {"decide": round(us_rej[0], 3), "row": round(us_rej[1], 3),
+            "reject_verify_us": {"stats_with_rows": round(us_rej[3], 3), "decide": round(us_rej[0], 3),
+                                 "tile_sums": round(us_rej[1], 3),
                                  "residual": round(us_rej[2], 3)},
             "algorithmic_bytes": nbytes, "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
             "hbm_frac": round(nbytes / (us * 1e-6) / 8e12, 4),
@@ -528,7 +529,7 @@ def main():
         log(f"lm_head_stats (beside the step, not in it): {lmh['shape']}, {lmh['xperm_us']:.2f} us permute + "
             f"{lmh['us']:.2f} us + merge {lmh['merge_us']:.2f} us, {lmh['achieved_GBs']:.0f} GB/s; greedy verify "
             f"from the statistics {lmh['greedy_verify_us']:.2f} us, typical with its bonus draw "
-            f"{lmh['typical_verify_us']:.2f} us")
+            f"{lmh['typical_verify_us']:.2f} us; REJECT {lmh['reject_verify_us']}")
 
     if args.copy_calibration_mb:
         nb = args.copy_calibration_mb * (1 << 20)

@@ -342,8 +342,9 @@ spec_status spec_verify_greedy_stats(const int32_t* row_argmax, const int32_t* t
  * and REJECT when m has no child, a draw from T_m - the 64-token tile holding u Z is found from
  * the per-tile sums of the statistics pass and only that tile's logits are recomputed; REJECT
  * when m has children, a draw from norm(relu(T_m - D)), D the draft row of m's lowest-index
- * child (T_m if that residual is zero) - row m is recomputed whole for it (one more pass over
- * W).  [GUIDE] sections "並列検証：ターゲットモデルの1回のforward passで一括確認する" and
+ * child (T_m if that residual is zero) - in REJECT mode the statistics pass also keeps every
+ * row's fp32 logits in the workspace, and the draw scans row m's 64-token tile sums, then one
+ * tile.  [GUIDE] sections "並列検証：ターゲットモデルの1回のforward passで一括確認する" and
  * "棄却サンプリング：出力品質を保証する"; [GLOSSARY] section "Medusa-1とMedusa-2の違い".
  *
  *   hidden, W, parents, tokens, n_nodes, B, N, Dm, V  as spec_lm_head_stats
@@ -351,12 +352,13 @@ spec_status spec_verify_greedy_stats(const int32_t* row_argmax, const int32_t* t
  *   max_depth, eps, delta  as spec_verify
  * Outputs: accept_len [B], path [B, max_depth + 1], bonus_token [B], node_accept uint8 [B, N]
  *   (optional), err [B]: as spec_verify (SPEC_ERR_NNODES, ROOT, PARENT, DEPTH, TOKEN, DRAFTROW,
- *   MAP).  Workspace: spec_verify_lm_head_workspace bytes.
+ *   MAP).  Workspace: spec_verify_lm_head_workspace(B, N, Dm, V, mode) bytes (REJECT's includes
+ *   B * N * V fp32 logits).
  * Supported: GREEDY, TYPICAL, REJECT (not WALK), N <= 256, B * N <= 4096, Dm a multiple of 128.
  * Errors: SPEC_EINVAL (sizes, NULL pointers, NaN eps or delta, REJECT without draft arrays, t2d
  * NULL with Vd != V), SPEC_EUNSUPPORTED (mode, sizes, alignment), SPEC_EWORKSPACE.
  * ------------------------------------------------------------------------------------ */
-size_t spec_verify_lm_head_workspace(int B, int N, int Dm, int V);
+size_t spec_verify_lm_head_workspace(int B, int N, int Dm, int V, spec_mode mode);
 spec_status spec_verify_lm_head(const void* hidden, const void* W, const int32_t* tokens,
                                 const int32_t* parents, const int32_t* n_nodes, const float* uniforms,
                                 const float* draft_probs, const int32_t* draft_row, const int32_t* t2d,

@@ -158,8 +158,10 @@ def test_verify_greedy_stats_argument_checks(lib):
 
 def test_verify_lm_head_argument_checks(lib):
     fake = ctypes.c_void_p(0x1000)     # never dereferenced: every call below returns before a launch
-    ws = lib.spec_verify_lm_head_workspace(1, 63, 4096, 128256)
+    ws = lib.spec_verify_lm_head_workspace(1, 63, 4096, 128256, 1)
     assert ws > lib.spec_lm_head_stats_workspace(1, 63, 4096, 128256)
+    ws_rej = lib.spec_verify_lm_head_workspace(1, 63, 4096, 128256, 2)
+    assert ws_rej >= ws + 63 * 128256 * 4                # REJECT keeps every row's logits
 
     def call(mode=0, eps=0.09, delta=0.3, uni=fake, wsz=ws, B=1, N=63, Dm=4096, draft=None, drow=None, R=0, Vd=0):
         return lib.spec_verify_lm_head(fake, fake, fake, fake, None, uni, draft, drow, None, B, N, Dm, 128256, R, Vd,
@@ -171,3 +173,4 @@ def test_verify_lm_head_argument_checks(lib):
     assert call(mode=2, draft=fake, drow=fake, R=4, Vd=1000) == 1   # no t2d: Vd must be V
     assert call(mode=1, eps=float("nan")) == 1
     assert call(Dm=4000) == 2 and call(wsz=ws - 1) == 3
+    assert call(mode=2, draft=fake, drow=fake, R=63, Vd=128256, wsz=ws) == 3   # REJECT needs its rows

@@ -48,7 +48,7 @@ def test_graph_replays_match_eager():
     ws_walk = sb.workspace(sb.verify_workspace_bytes(B, N, w.V), "cuda")
     ws_lm = sb.workspace(sb.lm_head_stats_workspace_bytes(2, 40, 256, 3000), "cuda")
     ws_vlm = sb.workspace(sb.verify_lm_head_workspace_bytes(2, 40, 256, 3000), "cuda")
-    ws_vrj = sb.workspace(sb.verify_lm_head_workspace_bytes(2, 40, 256, 3000), "cuda")
+    ws_vrj = sb.workspace(sb.verify_lm_head_workspace_bytes(2, 40, 256, 3000, "reject"), "cuda")
     lg = np.random.default_rng(34)
     lunif = dev(lg.random((2, 40), dtype=np.float32))
     ldraft = lg.random((2, 40, 3000)).astype(np.float32) ** 8

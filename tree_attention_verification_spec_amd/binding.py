@@ -53,7 +53,7 @@ def lib():
     L.spec_verify_greedy_stats.restype = _I
     L.spec_verify_greedy_stats.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
     L.spec_verify_lm_head_workspace.restype = _Z
-    L.spec_verify_lm_head_workspace.argtypes = [_I, _I, _I, _I]
+    L.spec_verify_lm_head_workspace.argtypes = [_I, _I, _I, _I, _I]
     L.spec_verify_lm_head.restype = _I
     L.spec_verify_lm_head.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                                       _F, _F, _P, _P, _P, _P, _P, _P, _Z, _P]
@@ -311,8 +311,8 @@ def spec_verify_greedy_stats(row_argmax, tokens, parents, V, n_nodes=None, max_d
     return out
 
 
-def verify_lm_head_workspace_bytes(B, N, Dm, V):
-    return int(lib().spec_verify_lm_head_workspace(B, N, Dm, V))
+def verify_lm_head_workspace_bytes(B, N, Dm, V, mode="typical"):
+    return int(lib().spec_verify_lm_head_workspace(B, N, Dm, V, int(MODES.get(mode, mode))))
 
 
 def spec_verify_lm_head(hidden, W, tokens, parents, uniforms, mode, n_nodes=None, draft_probs=None, draft_row=None,
@@ -333,7 +333,7 @@ def spec_verify_lm_head(hidden, W, tokens, parents, uniforms, mode, n_nodes=None
                "node_accept": torch.empty((B, N), dtype=torch.uint8, device=dev),
                "err": torch.empty((B,), dtype=torch.int32, device=dev)}
     if ws is None:
-        ws = workspace(verify_lm_head_workspace_bytes(B, N, Dm, V), dev)
+        ws = workspace(verify_lm_head_workspace_bytes(B, N, Dm, V, mode), dev)
     _check(lib().spec_verify_lm_head(
         _ptr(hidden, torch.bfloat16, (B, N, Dm), "hidden"), _ptr(W, torch.bfloat16, (V, Dm), "W"),
         _ptr(tokens, torch.int32, (B, N), "tokens"), _ptr(parents, torch.int32, (B, N), "parents"),

@@ -53,11 +53,23 @@ struct LmPart {       // one 64-token tile of one row
 
 __device__ __forceinline__ bf16x8 ld8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
+// Optional output of the stats kernels (REJECT's residual draw needs the row it stops at): the
+// fp32 logits of a 64-token x 64-column tile held in LDS as [token][column] are written to
+// rows[column][token] (rows of V), lane = token so each store is one 256-byte run; the calling
+// wave takes columns c_begin, c_begin + c_step, ...
+__device__ __forceinline__ void store_tile_rows(const float (*tw)[kLMaxCols + 1], int vrow0, int ccol0,
+                                                int c_begin, int c_step, int M, int V, float* __restrict__ rows) {
+  const int lane = threadIdx.x & 63, v = vrow0 + lane;
+  if (v >= V) return;
+  for (int cc = c_begin; cc < kLMaxCols && ccol0 + cc < M; cc += c_step)
+    rows[(size_t)(ccol0 + cc) * V + v] = tw[lane][cc];
+}
+
 template <int CBN>
 __global__ __launch_bounds__(kLThreads) void lmhead_stats_kernel(
     const __bf16* __restrict__ W, const __bf16* __restrict__ Xp, int M, int Dm, int V, int N,
     int nblk, int ncb, const int32_t* __restrict__ parents, const int32_t* __restrict__ tokens,
-    LmPart* __restrict__ parts, float* __restrict__ gath) {
+    LmPart* __restrict__ parts, float* __restrict__ gath, float* __restrict__ rows) {
   // the K-slice partials and, once they are summed, the logits tile share one LDS block, so
   // two workgroups fit a CU
   constexpr size_t kRedBytes = sizeof(f32x4) * kLKWaves * kLRB * CBN * kWave;
@@ -149,6 +161,7 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_kernel(
     }
   }
   __syncthreads();
+  if (rows) store_tile_rows(tile, row0, col0, wave, kLKWaves, M, V, rows);
 
   // per column: four consecutive threads share the tile's 64 rows, 16 each
   const int col = threadIdx.x >> 2, q = threadIdx.x & 3;
@@ -218,7 +231,8 @@ constexpr int kWRows = kWRowsPerWave * kLKWaves;   // W rows per workgroup
 __global__ __launch_bounds__(kLThreads) void lmhead_stats_wide_kernel(
     const __bf16* __restrict__ W, const __bf16* __restrict__ Xp, int M, int Dm, int V, int N,
     int nblk, int ntile, int ncb, const int32_t* __restrict__ parents,
-    const int32_t* __restrict__ tokens, LmPart* __restrict__ parts, float* __restrict__ gath) {
+    const int32_t* __restrict__ tokens, LmPart* __restrict__ parts, float* __restrict__ gath,
+    float* __restrict__ rows) {
   __shared__ float tile[kLKWaves][kWRowsPerWave][kLMaxCols + 1];
   constexpr int RB = kWRowsPerWave / 16, CBN = kLMaxCols / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -277,6 +291,7 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_wide_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) tw[rb * 16 + 4 * lg + e][cb * 16 + l16] = acc[rb][cb][e];
   __syncthreads();
+  if (rows) store_tile_rows(tw, wrow0, col0, 0, 1, M, V, rows);
   // lane = column: max and lowest argmax over the wave's 64 rows, then fp64 sums
   const int col = lane;
   float m = -INFINITY;
@@ -316,7 +331,8 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_wide_kernel(
 __device__ __forceinline__ void wave_tile_epilogue(float (*tw)[kLMaxCols + 1], int wrow0, int wcol0, int M,
                                                    int V, int N, int nblk, const int32_t* __restrict__ parents,
                                                    const int32_t* __restrict__ tokens, LmPart* __restrict__ parts,
-                                                   float* __restrict__ gath) {
+                                                   float* __restrict__ gath, float* __restrict__ rows) {
+  if (rows) store_tile_rows(tw, wrow0, wcol0, 0, 1, M, V, rows);
   const int lane = threadIdx.x & 63;
   const int col = lane;
   float m = -INFINITY;
@@ -363,7 +379,8 @@ constexpr int kGS = 40;                  // LDS row stride in bf16 (32 + 8: rows
 __global__ __launch_bounds__(kLThreads) void lmhead_stats_gemm_kernel(
     const __bf16* __restrict__ W, const __bf16* __restrict__ Xp, int M, int Dm, int V, int N,
     int nblk, int ntile, int ncb, const int32_t* __restrict__ parents,
-    const int32_t* __restrict__ tokens, LmPart* __restrict__ parts, float* __restrict__ gath) {
+    const int32_t* __restrict__ tokens, LmPart* __restrict__ parts, float* __restrict__ gath,
+    float* __restrict__ rows) {
   constexpr size_t kStageBytes = sizeof(__bf16) * 2 * 2 * kGT * kGS;               // [buf][A|B]
   constexpr size_t kTileBytes = sizeof(float) * 2 * 64 * (kLMaxCols + 1);          // two waves at a time
   __shared__ __attribute__((aligned(16))) unsigned char lds[kStageBytes > kTileBytes ? kStageBytes : kTileBytes];
@@ -452,7 +469,7 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_gemm_kernel(
     }
     __syncthreads();
     if ((wave >> 1) == half) wave_tile_epilogue(tw, row0 + wr * 64, col0 + wc * 64, M, V, N, nblk, parents,
-                                                tokens, parts, gath);
+                                                tokens, parts, gath, rows);
     __syncthreads();
   }
 }
@@ -615,70 +632,38 @@ __device__ __forceinline__ double draw_weight(float l, float M, double invS, con
   return fmax(e - d, 0.0);
 }
 
-// Row m of a sequence whose bonus is a residual draw, recomputed: grid (64-token tile, sequence),
-// four threads per token, eight 16-byte pairs in flight per thread.  Besides the row, each tile
-// leaves its fp64 (residual, target) weight sums for the draw's scan.
-__global__ __launch_bounds__(kLThreads) void lm_row_kernel(
-    const __bf16* __restrict__ X, const __bf16* __restrict__ W, int N, int Dm, int V,
-    const float* __restrict__ row_max, const double* __restrict__ row_sum, LmDraft dr,
-    float* __restrict__ rowbuf, double2* __restrict__ tsum) {
-  __shared__ double2 s_t[kLThreads / kWave];
-  const int b = blockIdx.y, tile = blockIdx.x;
-  if (dr.plan[3 * b] != 1) return;
+// Tile sums of row m for a sequence whose bonus is a residual draw: grid (four 64-token tiles,
+// sequence), one wave per tile, lane = token; row m's logits were stored by the stats kernel.
+// Each tile leaves its fp64 (residual, target) weight sums for the draw's scan.
+__global__ __launch_bounds__(kLThreads) void lm_tilesum_kernel(
+    const float* __restrict__ rows, int N, int V, int nblk, const float* __restrict__ row_max,
+    const double* __restrict__ row_sum, LmDraft dr, double2* __restrict__ tsum) {
+  const int b = blockIdx.y, lane = threadIdx.x & (kWave - 1);
+  const int tile = blockIdx.x * (kLThreads / kWave) + (threadIdx.x >> 6);
+  if (dr.plan[3 * b] != 1 || tile >= nblk) return;
   const int r = dr.plan[3 * b + 1], m = dr.plan[3 * b + 2];
-  const int c = threadIdx.x, v = tile * kLRows + (c >> 2), part = c & 3, wv = c >> 6;
-  float acc32 = 0.f;
+  const int v = tile * kLRows + lane;
+  double wr = 0.0, wt = 0.0;
   if (v < V) {
-    const __bf16* wr = W + (size_t)v * Dm + part * 8;
-    const __bf16* hr = X + ((size_t)b * N + m) * Dm + part * 8;
-    const int nk = Dm / 32;
-    for (int k0 = 0; k0 < nk; k0 += 8) {
-      bf16x8 a8[8], h8[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int k = (k0 + i < nk ? k0 + i : 0) * 32;
-        a8[i] = ld8(wr + k);
-        h8[i] = ld8(hr + k);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (k0 + i < nk)
-#pragma unroll
-          for (int e2 = 0; e2 < 8; ++e2) acc32 = fmaf((float)a8[i][e2], (float)h8[i][e2], acc32);
-    }
-  }
-  acc32 += __shfl_xor(acc32, 1);
-  acc32 += __shfl_xor(acc32, 2);
-  double wr_ = 0.0, wt_ = 0.0;
-  if (part == 0 && v < V) {
-    rowbuf[(size_t)b * V + v] = acc32;
+    const float l = rows[((size_t)b * N + m) * V + v];
     const float M = row_max[(size_t)b * N + m];
     const double invS = 1.0 / row_sum[(size_t)b * N + m];
     const float* drow = dr.draft + ((size_t)b * dr.R + r) * dr.Vd;
-    wr_ = draw_weight(acc32, M, invS, drow, dr, v, true);
-    wt_ = draw_weight(acc32, M, invS, drow, dr, v, false);
+    wr = draw_weight(l, M, invS, drow, dr, v, true);
+    wt = draw_weight(l, M, invS, drow, dr, v, false);
   }
-  wr_ = wave_sum(wr_);
-  wt_ = wave_sum(wt_);
-  if ((c & (kWave - 1)) == 0) s_t[wv] = make_double2(wr_, wt_);
-  __syncthreads();
-  if (c == 0) {
-    double2 t = s_t[0];
-    for (int q = 1; q < kLThreads / kWave; ++q) {
-      t.x += s_t[q].x;
-      t.y += s_t[q].y;
-    }
-    tsum[(size_t)b * gridDim.x + tile] = t;
-  }
+  wr = wave_sum(wr);
+  wt = wave_sum(wt);
+  if (lane == 0) tsum[(size_t)b * nblk + tile] = make_double2(wr, wt);
 }
 
-// The residual draw: q_v = relu(T[v] - D[v]) over the recomputed row, u Q placed by inverse CDF
+// The residual draw: q_v = relu(T[v] - D[v]) over row m, u Q placed by inverse CDF
 // (Q the sum of the tiles' residual sums; a residual of zero mass draws from T_m instead).  One
 // workgroup per sequence: a block scan over the tile sums finds the tile holding u Q, then one
 // wave scans that tile's 64 weights, the remainder scaled to the wave's own total of the tile
 // (equal to the stored sum up to the order of the fp64 additions).
 __global__ __launch_bounds__(kLThreads) void lm_residual_kernel(
-    const float* __restrict__ rowbuf, const double2* __restrict__ tsum, int nblk,
+    const float* __restrict__ rows, const double2* __restrict__ tsum, int nblk,
     const float* __restrict__ row_max, const double* __restrict__ row_sum,
     const float* __restrict__ uniforms, int N, int V, LmDraft dr, int32_t* __restrict__ bonus) {
   __shared__ double s_w[kLThreads / kWave];
@@ -750,7 +735,7 @@ __global__ __launch_bounds__(kLThreads) void lm_residual_kernel(
   const double invS = 1.0 / row_sum[(size_t)b * N + m];
   const float* drow = dr.draft + ((size_t)b * dr.R + r) * dr.Vd;
   const int v = tile * kLRows + lane;
-  const double w = v < V ? draw_weight(rowbuf[(size_t)b * V + v], M, invS, drow, dr, v, resid) : 0.0;
+  const double w = v < V ? draw_weight(rows[((size_t)b * N + m) * V + v], M, invS, drow, dr, v, resid) : 0.0;
   double incl = w;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
@@ -876,7 +861,7 @@ __global__ __launch_bounds__(SPEC_MAX_NODES) void verify_lm_kernel(
   if (mode == SPEC_VERIFY_REJECT && c == 0) dr.plan[3 * b] = 0;
   if (!ok || mode == SPEC_VERIFY_GREEDY) return;            // uniform across the workgroup
   if (mode == SPEC_VERIFY_REJECT) {
-    // m with children: a residual draw over the whole row (lm_row_kernel, lm_residual_kernel)
+    // m with children: a residual draw over the whole row (lm_tilesum_kernel, lm_residual_kernel)
     if (c < n && c > 0 && s_par[c] == m) atomicMin(&s_kid, c);
     __syncthreads();
     if (s_kid != INT_MAX) {
@@ -1141,7 +1126,7 @@ spec_status check_lm(const void* hidden, const void* W, int B, int N, int Dm, in
 void launch_lm(const __bf16* X, const __bf16* Wb, const int32_t* parents, const int32_t* tokens,
                const int32_t* n_nodes, int B, int N, int Dm, int V, const LmLayout& L, char* w,
                float* row_max, int32_t* row_argmax, double* row_sum, double* row_ent, float* cand_logit,
-               int32_t* err, hipStream_t s) {
+               int32_t* err, float* rows, hipStream_t s) {
   const int M = B * N;
   LmPart* parts = reinterpret_cast<LmPart*>(w + L.parts);
   float* gath = reinterpret_cast<float*>(w + L.gath);
@@ -1156,24 +1141,24 @@ void launch_lm(const __bf16* X, const __bf16* Wb, const int32_t* parents, const 
   if (M > 2 * kLMaxCols) {
     const int ntile = (V + kGT - 1) / kGT, ncb2 = (M + kGT - 1) / kGT;
     const dim3 gg((unsigned)((ntile + 7) / 8 * 8 * ncb2));
-    launch(nm, lmhead_stats_gemm_kernel, gg, blk, s, Wb, Xp, M, Dm, V, N, nb, ntile, ncb2, parents, tokens, parts, gath);
+    launch(nm, lmhead_stats_gemm_kernel, gg, blk, s, Wb, Xp, M, Dm, V, N, nb, ntile, ncb2, parents, tokens, parts, gath, rows);
   } else if (M > kLMaxCols) {
     const int ntile = (V + kWRows - 1) / kWRows;
     const dim3 gw((unsigned)((ntile + 7) / 8 * 8 * ncb));
-    launch(nm, lmhead_stats_wide_kernel, gw, blk, s, Wb, Xp, M, Dm, V, N, nb, ntile, ncb, parents, tokens, parts, gath);
-  } else if (M <= 16) launch(nm, lmhead_stats_kernel<1>, g1, blk, s, Wb, Xp, M, Dm, V, N, nb, ncb, parents, tokens, parts, gath);
-  else if (M <= 32) launch(nm, lmhead_stats_kernel<2>, g1, blk, s, Wb, Xp, M, Dm, V, N, nb, ncb, parents, tokens, parts, gath);
-  else if (M <= 48) launch(nm, lmhead_stats_kernel<3>, g1, blk, s, Wb, Xp, M, Dm, V, N, nb, ncb, parents, tokens, parts, gath);
-  else launch(nm, lmhead_stats_kernel<4>, g1, blk, s, Wb, Xp, M, Dm, V, N, nb, ncb, parents, tokens, parts, gath);
+    launch(nm, lmhead_stats_wide_kernel, gw, blk, s, Wb, Xp, M, Dm, V, N, nb, ntile, ncb, parents, tokens, parts, gath, rows);
+  } else if (M <= 16) launch(nm, lmhead_stats_kernel<1>, g1, blk, s, Wb, Xp, M, Dm, V, N, nb, ncb, parents, tokens, parts, gath, rows);
+  else if (M <= 32) launch(nm, lmhead_stats_kernel<2>, g1, blk, s, Wb, Xp, M, Dm, V, N, nb, ncb, parents, tokens, parts, gath, rows);
+  else if (M <= 48) launch(nm, lmhead_stats_kernel<3>, g1, blk, s, Wb, Xp, M, Dm, V, N, nb, ncb, parents, tokens, parts, gath, rows);
+  else launch(nm, lmhead_stats_kernel<4>, g1, blk, s, Wb, Xp, M, Dm, V, N, nb, ncb, parents, tokens, parts, gath, rows);
   launch("lm_head_merge", lmhead_merge_kernel, dim3((unsigned)M), blk, s, parts, gath, L.nblk, N, V,
          parents, tokens, n_nodes, row_max, row_argmax, row_sum, row_ent, cand_logit, err);
 }
 
 // spec_verify_lm_head's own part of the workspace, after the LM head's: the statistics
 struct VlLayout {
-  size_t mx, am, sum, ent, cand, err, plan, rowbuf, tsum, total;
+  size_t mx, am, sum, ent, cand, err, plan, rows, tsum, total;
 };
-VlLayout vl_layout(const LmLayout& L, int B, int N, int V) {
+VlLayout vl_layout(const LmLayout& L, int B, int N, int V, bool reject) {
   const size_t M = (size_t)B * N;
   VlLayout v{};
   v.mx = L.total;
@@ -1183,9 +1168,10 @@ VlLayout vl_layout(const LmLayout& L, int B, int N, int V) {
   v.cand = v.ent + align_up(M * sizeof(double), 256);
   v.err = v.cand + align_up(M * sizeof(float), 256);
   v.plan = v.err + align_up((size_t)B * sizeof(int32_t), 256);
-  v.rowbuf = v.plan + align_up((size_t)B * 3 * sizeof(int32_t), 256);
-  v.tsum = v.rowbuf + align_up((size_t)B * V * sizeof(float), 256);      // row m, residual draws
-  v.total = v.tsum + align_up((size_t)B * L.nblk * sizeof(double2), 256);  // its tile sums
+  v.rows = v.plan + align_up((size_t)B * 3 * sizeof(int32_t), 256);
+  // REJECT only: every row's logits (the residual draw reads row m) and row m's tile sums
+  v.tsum = v.rows + (reject ? align_up(M * V * sizeof(float), 256) : 0);
+  v.total = v.tsum + (reject ? align_up((size_t)B * L.nblk * sizeof(double2), 256) : 0);
   return v;
 }
 }  // namespace
@@ -1203,13 +1189,13 @@ extern "C" spec_status spec_lm_head_stats(const void* hidden, const void* W, con
   if (!workspace || ws_bytes < L.total) return SPEC_EWORKSPACE;
   launch_lm(static_cast<const __bf16*>(hidden), static_cast<const __bf16*>(W), parents, tokens, n_nodes, B, N, Dm,
             V, L, static_cast<char*>(workspace), row_max, row_argmax, row_sum, row_ent, cand_logit, err,
-            static_cast<hipStream_t>(stream));
+            nullptr, static_cast<hipStream_t>(stream));
   return launch_status();
 }
 
-extern "C" size_t spec_verify_lm_head_workspace(int B, int N, int Dm, int V) {
+extern "C" size_t spec_verify_lm_head_workspace(int B, int N, int Dm, int V, spec_mode mode) {
   if (B < 1 || N < 1 || Dm < 1 || V < 1) return 0;
-  return vl_layout(lm_layout(B, N, V, Dm), B, N, V).total;
+  return vl_layout(lm_layout(B, N, V, Dm), B, N, V, mode == SPEC_VERIFY_REJECT).total;
 }
 
 extern "C" spec_status spec_verify_lm_head(const void* hidden, const void* W, const int32_t* tokens,
@@ -1232,7 +1218,7 @@ extern "C" spec_status spec_verify_lm_head(const void* hidden, const void* W, co
     if (!t2d && Vd != V) return SPEC_EINVAL;
   }
   const LmLayout L = lm_layout(B, N, V, Dm);
-  const VlLayout VL = vl_layout(L, B, N, V);
+  const VlLayout VL = vl_layout(L, B, N, V, mode == SPEC_VERIFY_REJECT);
   if (!workspace || ws_bytes < VL.total) return SPEC_EWORKSPACE;
   char* w = static_cast<char*>(workspace);
   float* mx = reinterpret_cast<float*>(w + VL.mx);
@@ -1244,20 +1230,20 @@ extern "C" spec_status spec_verify_lm_head(const void* hidden, const void* W, co
   LmDraft dr{};
   dr.draft = draft_probs; dr.draft_row = draft_row; dr.t2d = t2d; dr.R = R; dr.Vd = Vd;
   dr.plan = reinterpret_cast<int32_t*>(w + VL.plan);
-  float* rowbuf = reinterpret_cast<float*>(w + VL.rowbuf);
+  float* rows = mode == SPEC_VERIFY_REJECT ? reinterpret_cast<float*>(w + VL.rows) : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const __bf16* X = static_cast<const __bf16*>(hidden);
   const __bf16* Wb = static_cast<const __bf16*>(W);
-  launch_lm(X, Wb, parents, tokens, n_nodes, B, N, Dm, V, L, w, mx, am, sum, ent, cand, lerr, s);
+  launch_lm(X, Wb, parents, tokens, n_nodes, B, N, Dm, V, L, w, mx, am, sum, ent, cand, lerr, rows, s);
   launch("verify_lm", verify_lm_kernel, dim3(B), dim3(SPEC_MAX_NODES), s, (const float*)mx, (const int32_t*)am,
          (const double*)sum, (const double*)ent, (const float*)cand,
          (const LmPart*)reinterpret_cast<LmPart*>(w + L.parts), L.nblk, X, Wb, Dm, tokens, parents, n_nodes,
          uniforms, N, V, max_depth, (int)mode, eps, delta, dr, accept_len, path, bonus_token, node_accept, err);
   if (mode == SPEC_VERIFY_REJECT) {
     double2* tsum = reinterpret_cast<double2*>(w + VL.tsum);
-    launch("verify_lm_row", lm_row_kernel, dim3((unsigned)L.nblk, (unsigned)B), dim3(kLThreads), s, X, Wb, N, Dm, V,
-           (const float*)mx, (const double*)sum, dr, rowbuf, tsum);
-    launch("verify_lm_residual", lm_residual_kernel, dim3(B), dim3(kLThreads), s, (const float*)rowbuf,
+    launch("verify_lm_tilesum", lm_tilesum_kernel, dim3((unsigned)((L.nblk + 3) / 4), (unsigned)B), dim3(kLThreads),
+           s, (const float*)rows, N, V, L.nblk, (const float*)mx, (const double*)sum, dr, tsum);
+    launch("verify_lm_residual", lm_residual_kernel, dim3(B), dim3(kLThreads), s, (const float*)rows,
            (const double2*)tsum, L.nblk, (const float*)mx, (const double*)sum, uniforms, N, V, dr, bonus_token);
   }
   return launch_status();
