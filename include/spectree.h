@@ -330,9 +330,9 @@ spec_status spec_verify_greedy_stats(const int32_t* row_argmax, const int32_t* t
                                      void* stream);
 
 /* --------------------------------------------------------------------------------------
- * spec_verify_lm_head - greedy, typical or rejection-sampling verification straight from the
- * target's hidden states: spec_lm_head_stats' statistics, then spec_verify's rule on them,
- * without the N x V logits.
+ * spec_verify_lm_head - greedy, typical, rejection-sampling or sibling-residual-walk
+ * verification straight from the target's hidden states: spec_lm_head_stats' statistics, then
+ * spec_verify's rule on them (GREEDY and TYPICAL without storing the N x V logits).
  *
  * The rules are spec_verify's: GREEDY accepts node c (parent p, token x) iff x is p's lowest
  * argmax; TYPICAL iff T_p[x] = exp(l_p[x] - max_p) / S_p >= min(eps, delta exp(-H_p)) with
@@ -344,19 +344,22 @@ spec_status spec_verify_greedy_stats(const int32_t* row_argmax, const int32_t* t
  * when m has children, a draw from norm(relu(T_m - D)), D the draft row of m's lowest-index
  * child (T_m if that residual is zero) - in REJECT mode the statistics pass also keeps every
  * row's fp32 logits in the workspace, and the draw scans row m's 64-token tile sums, then one
- * tile.  [GUIDE] sections "並列検証：ターゲットモデルの1回のforward passで一括確認する" and
+ * tile.  WALK: the statistics pass stores every row's fp32 logits in the workspace and
+ * spec_verify(WALK) runs on them (same outputs and errors as spec_verify on those logits).
+ * [GUIDE] sections "並列検証：ターゲットモデルの1回のforward passで一括確認する" and
  * "棄却サンプリング：出力品質を保証する"; [GLOSSARY] section "Medusa-1とMedusa-2の違い".
  *
  *   hidden, W, parents, tokens, n_nodes, B, N, Dm, V  as spec_lm_head_stats
- *   uniforms float [B, N]; draft_probs, draft_row, t2d, R, Vd (REJECT only; else may be NULL),
+ *   uniforms float [B, N]; draft_probs, draft_row, t2d, R, Vd (REJECT, WALK; else may be NULL),
  *   max_depth, eps, delta  as spec_verify
  * Outputs: accept_len [B], path [B, max_depth + 1], bonus_token [B], node_accept uint8 [B, N]
  *   (optional), err [B]: as spec_verify (SPEC_ERR_NNODES, ROOT, PARENT, DEPTH, TOKEN, DRAFTROW,
- *   MAP).  Workspace: spec_verify_lm_head_workspace(B, N, Dm, V, mode) bytes (REJECT's includes
- *   B * N * V fp32 logits).
- * Supported: GREEDY, TYPICAL, REJECT (not WALK), N <= 256, B * N <= 4096, Dm a multiple of 128.
- * Errors: SPEC_EINVAL (sizes, NULL pointers, NaN eps or delta, REJECT without draft arrays, t2d
- * NULL with Vd != V), SPEC_EUNSUPPORTED (mode, sizes, alignment), SPEC_EWORKSPACE.
+ *   MAP, and WALK's NONFINITE).  Workspace: spec_verify_lm_head_workspace(B, N, Dm, V, mode)
+ *   bytes (REJECT's and WALK's include B * N * V fp32 logits; WALK's also spec_verify's own).
+ * Supported: all four modes, N <= 256, B * N <= 4096, Dm a multiple of 128.
+ * Errors: SPEC_EINVAL (sizes, NULL pointers, NaN eps or delta, REJECT or WALK without draft
+ * arrays, t2d NULL with Vd != V), SPEC_EUNSUPPORTED (mode, sizes, alignment), SPEC_EWORKSPACE;
+ * WALK also returns what spec_verify returns for its call (after the statistics pass ran).
  * ------------------------------------------------------------------------------------ */
 size_t spec_verify_lm_head_workspace(int B, int N, int Dm, int V, spec_mode mode);
 spec_status spec_verify_lm_head(const void* hidden, const void* W, const int32_t* tokens,

@@ -168,9 +168,12 @@ def test_verify_lm_head_argument_checks(lib):
                                        N - 1, mode, eps, delta, fake, fake, fake, None, fake, fake, wsz, None)
 
     assert call(uni=None) == 1 and call(B=0) == 1
-    assert call(mode=3) == 2                             # WALK is not supported here
+    assert call(mode=3) == 1                             # WALK without draft arrays
     assert call(mode=2) == 1                             # REJECT without draft arrays
     assert call(mode=2, draft=fake, drow=fake, R=4, Vd=1000) == 1   # no t2d: Vd must be V
     assert call(mode=1, eps=float("nan")) == 1
     assert call(Dm=4000) == 2 and call(wsz=ws - 1) == 3
     assert call(mode=2, draft=fake, drow=fake, R=63, Vd=128256, wsz=ws) == 3   # REJECT needs its rows
+    ws_walk = lib.spec_verify_lm_head_workspace(1, 63, 4096, 128256, 3)
+    assert ws_walk >= ws + 63 * 128256 * 4 + lib.spec_verify_workspace(1, 63, 128256)   # rows + spec_verify's
+    assert call(mode=3, draft=fake, drow=fake, R=63, Vd=128256, wsz=ws_rej) == 3

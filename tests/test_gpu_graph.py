@@ -1,8 +1,9 @@
 """The entry points inside a captured HIP graph: a verification step (tree build, tree attention,
-rejection and walk verification), a tree selection and a fused LM head with greedy, typical and
-rejection verification are captured once with preallocated outputs and workspaces, replayed three times with unrelated
-eager work and synchronisations in between, and every replay's outputs must equal the eager
-call's bit for bit (the kernels are deterministic: no atomics decide a floating-point sum)."""
+rejection and walk verification), a tree selection and a fused LM head with verification from
+hidden states in all four modes are captured once with preallocated outputs and workspaces,
+replayed three times with unrelated eager work and synchronisations in between, and every
+replay's outputs must equal the eager call's bit for bit (the kernels are deterministic: no
+atomics decide a floating-point sum)."""
 
 import numpy as np
 import pytest
@@ -49,6 +50,7 @@ def test_graph_replays_match_eager():
     ws_lm = sb.workspace(sb.lm_head_stats_workspace_bytes(2, 40, 256, 3000), "cuda")
     ws_vlm = sb.workspace(sb.verify_lm_head_workspace_bytes(2, 40, 256, 3000), "cuda")
     ws_vrj = sb.workspace(sb.verify_lm_head_workspace_bytes(2, 40, 256, 3000, "reject"), "cuda")
+    ws_vwk = sb.workspace(sb.verify_lm_head_workspace_bytes(2, 40, 256, 3000, "walk"), "cuda")
     lg = np.random.default_rng(34)
     lunif = dev(lg.random((2, 40), dtype=np.float32))
     ldraft = lg.random((2, 40, 3000)).astype(np.float32) ** 8
@@ -70,6 +72,8 @@ def test_graph_replays_match_eager():
         o["vlm"] = sb.spec_verify_lm_head(h, W, ltok, lpar, lunif, "typical", out=o.get("vlm"), ws=ws_vlm)
         o["vrj"] = sb.spec_verify_lm_head(h, W, ltok, lpar, lunif, "reject", draft_probs=ldraft,
                                           draft_row=ldrow, out=o.get("vrj"), ws=ws_vrj)
+        o["vwk"] = sb.spec_verify_lm_head(h, W, ltok, lpar, lunif, "walk", draft_probs=ldraft,
+                                          draft_row=ldrow, out=o.get("vwk"), ws=ws_vwk)
         return o
 
     eager = run({})

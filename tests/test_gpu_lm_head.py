@@ -192,7 +192,7 @@ def test_greedy_stats_errors():
     assert int(rv["accept_len"][0]) == 4 and int(rv["bonus"][0]) == 4   # path 0 -> 1 -> 3 -> 6 -> 7
 
 
-@pytest.mark.parametrize("mode", ["greedy", "typical", "reject", "reject_row"])
+@pytest.mark.parametrize("mode", ["greedy", "typical", "reject", "reject_row", "walk"])
 @pytest.mark.parametrize("seed,B,N,Dm,V,hscale", [(41, 2, 40, 256, 3000, 8.0), (42, 4, 16, 128, 700, 12.0),
                                                    (43, 1, 63, 4096, 128256, 1.0), (44, 8, 127, 256, 2000, 8.0)])
 def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
@@ -205,7 +205,9 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
     3 delta of u are excused; its bonus must lie within the tolerance of the oracle's residual CDF
     step (or of T_m's at a leaf).  reject_row drafts random tokens with draft rows peaked on them
     and node uniforms in [0.1, 1), so the root's children are rejected and the bonus is a residual
-    draw over a recomputed row."""
+    draw over the stored row.  WALK (spec_verify's walk on the rows the statistics pass stores):
+    sequences with a sibling test within 6 delta (relative) of its boundary are counted, not
+    compared; the bonus must equal the oracle's where its CDF margin exceeds 100 delta."""
     need_gpu()
     inp = wl.lm_head_inputs(seed=seed, B=B, N=N, Dm=Dm, V=V, max_depth=6)
     inp["hidden"] = wl.round_bf16(inp["hidden"] * np.float32(hscale))
@@ -220,7 +222,7 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
     n_nodes = np.array([N - (b % 2) for b in range(B)], dtype=np.int32)
     eps, delta = float(np.float32(0.09)), float(np.float32(0.3))
     draft = drow = None
-    if mode.startswith("reject"):
+    if mode.startswith("reject") or mode == "walk":
         # per-parent draft rows: D_p = softmax(l_p + N(0, 0.5)) of the oracle's logits (inputs only)
         x = np.nan_to_num(ref0["logits"], nan=0.0) + g.standard_normal(ref0["logits"].shape) * 0.5
         e = np.exp(x - x.max(axis=2, keepdims=True))
@@ -243,7 +245,8 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
     got = {k: host(v) for k, v in got.items()}
     ref = oracle.lm_head_stats(inp["hidden"], inp["W"], inp["parents"], tok, n_nodes=n_nodes)
     logits = np.nan_to_num(ref["logits"], nan=0.0)
-    m_id = {"greedy": oracle.MODE_GREEDY, "typical": oracle.MODE_TYPICAL, "reject": oracle.MODE_REJECT}[mode.split("_")[0]]
+    m_id = {"greedy": oracle.MODE_GREEDY, "typical": oracle.MODE_TYPICAL, "reject": oracle.MODE_REJECT,
+            "walk": oracle.MODE_WALK}[mode.split("_")[0]]
     rv = oracle.verify(logits, tok, inp["parents"], unif, m_id, n_nodes=n_nodes, eps=eps, delta=delta,
                        draft_probs=draft, draft_row=drow)
     d = bound(inp["hidden"], inp["W"])
@@ -268,6 +271,9 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
             H = np.log(ref["row_sum"][b, :nb]) - ref["row_ent"][b, :nb] / ref["row_sum"][b, :nb]
             if np.any(rv["margin"][b, 1:nb] < 6 * dmax * (H.max() + 1)):
                 continue
+        elif mode == "walk":
+            if np.any(rv["margin"][b, 1:nb] < 6 * dmax + 1e-9):  # relative distance of each sibling test
+                continue
         elif np.any(rv["margin"][b, 1:nb] < 3 * dmax + 1e-9):     # |u - min(1, T/D)|, T within 2 delta
             continue
         compared += 1
@@ -276,6 +282,13 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
         assert np.array_equal(got["path"][b], rv["path"][b]), f"sequence {b}: path"
         if mode == "greedy":
             assert int(got["bonus"][b]) == int(rv["bonus"][b]), f"sequence {b}: bonus"
+        elif mode == "walk":
+            if rv["bonus_margin"][b] > 100 * dmax:
+                assert int(got["bonus"][b]) == int(rv["bonus"][b]), f"sequence {b}: walk bonus"
+                bonus_checked += 1
+            elif int(got["bonus"][b]) != int(rv["bonus"][b]):
+                print(f"  sequence {b}: walk bonus {int(got['bonus'][b])} vs oracle {int(rv['bonus'][b])} "
+                      f"(CDF margin {rv['bonus_margin'][b]:.1e})")
         else:
             m = int(rv["m"][b])
             row = logits[b, m]

@@ -1156,9 +1156,10 @@ void launch_lm(const __bf16* X, const __bf16* Wb, const int32_t* parents, const 
 
 // spec_verify_lm_head's own part of the workspace, after the LM head's: the statistics
 struct VlLayout {
-  size_t mx, am, sum, ent, cand, err, plan, rows, tsum, total;
+  size_t mx, am, sum, ent, cand, err, plan, rows, tsum, sub, total;
 };
-VlLayout vl_layout(const LmLayout& L, int B, int N, int V, bool reject) {
+VlLayout vl_layout(const LmLayout& L, int B, int N, int V, spec_mode mode) {
+  const bool reject = mode == SPEC_VERIFY_REJECT, walk = mode == SPEC_VERIFY_WALK;
   const size_t M = (size_t)B * N;
   VlLayout v{};
   v.mx = L.total;
@@ -1169,9 +1170,11 @@ VlLayout vl_layout(const LmLayout& L, int B, int N, int V, bool reject) {
   v.err = v.cand + align_up(M * sizeof(float), 256);
   v.plan = v.err + align_up((size_t)B * sizeof(int32_t), 256);
   v.rows = v.plan + align_up((size_t)B * 3 * sizeof(int32_t), 256);
-  // REJECT only: every row's logits (the residual draw reads row m) and row m's tile sums
-  v.tsum = v.rows + (reject ? align_up(M * V * sizeof(float), 256) : 0);
-  v.total = v.tsum + (reject ? align_up((size_t)B * L.nblk * sizeof(double2), 256) : 0);
+  // REJECT and WALK: every row's logits (REJECT's residual draw reads row m; WALK runs
+  // spec_verify on them); REJECT: row m's tile sums; WALK: spec_verify's own workspace
+  v.tsum = v.rows + (reject || walk ? align_up(M * V * sizeof(float), 256) : 0);
+  v.sub = v.tsum + (reject ? align_up((size_t)B * L.nblk * sizeof(double2), 256) : 0);
+  v.total = v.sub + (walk ? align_up(spec_verify_workspace(B, N, V), 256) : 0);
   return v;
 }
 }  // namespace
@@ -1195,7 +1198,7 @@ extern "C" spec_status spec_lm_head_stats(const void* hidden, const void* W, con
 
 extern "C" size_t spec_verify_lm_head_workspace(int B, int N, int Dm, int V, spec_mode mode) {
   if (B < 1 || N < 1 || Dm < 1 || V < 1) return 0;
-  return vl_layout(lm_layout(B, N, V, Dm), B, N, V, mode == SPEC_VERIFY_REJECT).total;
+  return vl_layout(lm_layout(B, N, V, Dm), B, N, V, mode).total;
 }
 
 extern "C" spec_status spec_verify_lm_head(const void* hidden, const void* W, const int32_t* tokens,
@@ -1210,15 +1213,16 @@ extern "C" spec_status spec_verify_lm_head(const void* hidden, const void* W, co
   if (st != SPEC_OK) return st;
   if (!tokens || !parents || !uniforms || !accept_len || !path || !bonus_token || !err || max_depth < 0)
     return SPEC_EINVAL;
-  if (mode != SPEC_VERIFY_GREEDY && mode != SPEC_VERIFY_TYPICAL && mode != SPEC_VERIFY_REJECT)
+  if (mode != SPEC_VERIFY_GREEDY && mode != SPEC_VERIFY_TYPICAL && mode != SPEC_VERIFY_REJECT &&
+      mode != SPEC_VERIFY_WALK)
     return SPEC_EUNSUPPORTED;
   if (mode == SPEC_VERIFY_TYPICAL && (!(eps == eps) || !(delta == delta))) return SPEC_EINVAL;
-  if (mode == SPEC_VERIFY_REJECT) {
+  if (mode == SPEC_VERIFY_REJECT || mode == SPEC_VERIFY_WALK) {
     if (!draft_probs || !draft_row || R < 1 || Vd < 1) return SPEC_EINVAL;
     if (!t2d && Vd != V) return SPEC_EINVAL;
   }
   const LmLayout L = lm_layout(B, N, V, Dm);
-  const VlLayout VL = vl_layout(L, B, N, V, mode == SPEC_VERIFY_REJECT);
+  const VlLayout VL = vl_layout(L, B, N, V, mode);
   if (!workspace || ws_bytes < VL.total) return SPEC_EWORKSPACE;
   char* w = static_cast<char*>(workspace);
   float* mx = reinterpret_cast<float*>(w + VL.mx);
@@ -1230,11 +1234,20 @@ extern "C" spec_status spec_verify_lm_head(const void* hidden, const void* W, co
   LmDraft dr{};
   dr.draft = draft_probs; dr.draft_row = draft_row; dr.t2d = t2d; dr.R = R; dr.Vd = Vd;
   dr.plan = reinterpret_cast<int32_t*>(w + VL.plan);
-  float* rows = mode == SPEC_VERIFY_REJECT ? reinterpret_cast<float*>(w + VL.rows) : nullptr;
+  const bool keep_rows = mode == SPEC_VERIFY_REJECT || mode == SPEC_VERIFY_WALK;
+  float* rows = keep_rows ? reinterpret_cast<float*>(w + VL.rows) : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const __bf16* X = static_cast<const __bf16*>(hidden);
   const __bf16* Wb = static_cast<const __bf16*>(W);
   launch_lm(X, Wb, parents, tokens, n_nodes, B, N, Dm, V, L, w, mx, am, sum, ent, cand, lerr, rows, s);
+  if (mode == SPEC_VERIFY_WALK) {
+    // the sibling-residual walk visits every sibling's residual over whole rows: it runs as
+    // spec_verify's WALK on the logits rows the statistics pass just stored
+    if (launch_status() != SPEC_OK) return SPEC_EHIP;
+    return spec_verify(rows, draft_probs, draft_row, t2d, tokens, parents, n_nodes, uniforms, B, N, V, R, Vd,
+                       max_depth, SPEC_VERIFY_WALK, eps, delta, accept_len, path, bonus_token, node_accept, err,
+                       w + VL.sub, VL.total - VL.sub, stream);
+  }
   launch("verify_lm", verify_lm_kernel, dim3(B), dim3(SPEC_MAX_NODES), s, (const float*)mx, (const int32_t*)am,
          (const double*)sum, (const double*)ent, (const float*)cand,
          (const LmPart*)reinterpret_cast<LmPart*>(w + L.parts), L.nblk, X, Wb, Dm, tokens, parents, n_nodes,
