@@ -295,9 +295,11 @@ def lm_head_stats_timing(w, reps=20, Dm=4096):
     draft[bi[:, 1:], drow[:, 1:].long(), tok[:, 1:].long()] += 1e4
     draft /= draft.sum(dim=2, keepdim=True)
     vrej = sb.spec_verify_lm_head(h, W, tok, par, uni, "reject", draft_probs=draft, draft_row=drow)
+    vwalk = sb.spec_verify_lm_head(h, W, tok, par, uni, "walk", draft_probs=draft, draft_row=drow)
     torch.cuda.synchronize()
     assert int(out["err"].abs().sum()) == 0 and int(ver["err"].abs().sum()) == 0
     assert int(vtyp["err"].abs().sum()) == 0 and int(vrej["err"].abs().sum()) == 0
+    assert int(vwalk["err"].abs().sum()) == 0
     try:
         sb.prof_reset()
         sb.prof_enable(True)
@@ -319,18 +321,30 @@ def lm_head_stats_timing(w, reps=20, Dm=4096):
         torch.cuda.synchronize()
         sb.prof_enable(False)
         rej = [sb.prof_read(k) for k in ("verify_lm", "verify_lm_tilesum", "verify_lm_residual", "lm_head_stats")]
+        sb.prof_reset()
+        sb.prof_enable(True)
+        for _ in range(reps):
+            sb.spec_verify_lm_head(h, W, tok, par, uni, "walk", draft_probs=draft, draft_row=drow, out=vwalk)
+        torch.cuda.synchronize()
+        sb.prof_enable(False)
+        wk_names = ("lm_head_stats", "verify_rows", "verify_rows_list", "verify_walk_chain", "verify_decide_bonus",
+                    "verify_select")
+        walk = {k: sb.prof_read(k) for k in wk_names}
     finally:
         sb.prof_enable(False)
         sb.prof_reset()
     us, us_merge, us_perm, us_greedy = ms / cnt * 1e3, ms2 / cnt2 * 1e3, ms3 / cnt3 * 1e3, ms4 / cnt4 * 1e3
     us_typ = ms5 / cnt5 * 1e3
     us_rej = [m / c * 1e3 for m, c in rej]
+    us_walk = {("stats_with_rows" if k == "lm_head_stats" else k): round(m / c * 1e3, 3)
+               for k, (m, c) in walk.items() if c}
     nbytes = V * Dm * 2 + B * N * Dm * 2
     flops = 2 * B * N * Dm * V
     del W, draft
     return {"shape": f"[{B * N} x {Dm}] x [{Dm} x {V}]", "us": round(us, 3), "merge_us": round(us_merge, 3),
             "xperm_us": round(us_perm, 3), "greedy_verify_us": round(us_greedy, 3),
             "typical_verify_us": round(us_typ, 3),
+            "walk_verify_us": us_walk,
             "reject_verify_us": {"stats_with_rows": round(us_rej[3], 3), "decide": round(us_rej[0], 3),
                                  "tile_sums": round(us_rej[1], 3),
                                  "residual": round(us_rej[2], 3)},
@@ -529,7 +543,7 @@ def main():
         log(f"lm_head_stats (beside the step, not in it): {lmh['shape']}, {lmh['xperm_us']:.2f} us permute + "
             f"{lmh['us']:.2f} us + merge {lmh['merge_us']:.2f} us, {lmh['achieved_GBs']:.0f} GB/s; greedy verify "
             f"from the statistics {lmh['greedy_verify_us']:.2f} us, typical with its bonus draw "
-            f"{lmh['typical_verify_us']:.2f} us; REJECT {lmh['reject_verify_us']}")
+            f"{lmh['typical_verify_us']:.2f} us; REJECT {lmh['reject_verify_us']}; WALK {lmh['walk_verify_us']}")
 
     if args.copy_calibration_mb:
         nb = args.copy_calibration_mb * (1 << 20)
