@@ -192,7 +192,7 @@ def test_greedy_stats_errors():
     assert int(rv["accept_len"][0]) == 4 and int(rv["bonus"][0]) == 4   # path 0 -> 1 -> 3 -> 6 -> 7
 
 
-@pytest.mark.parametrize("mode", ["greedy", "typical", "reject", "reject_row", "walk"])
+@pytest.mark.parametrize("mode", ["greedy", "typical", "reject", "reject_row", "walk", "reject_t2d", "walk_t2d"])
 @pytest.mark.parametrize("seed,B,N,Dm,V,hscale", [(41, 2, 40, 256, 3000, 8.0), (42, 4, 16, 128, 700, 12.0),
                                                    (43, 1, 63, 4096, 128256, 1.0), (44, 8, 127, 256, 2000, 8.0)])
 def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
@@ -207,7 +207,9 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
     and node uniforms in [0.1, 1), so the root's children are rejected and the bonus is a residual
     draw over the stored row.  WALK (spec_verify's walk on the rows the statistics pass stores):
     sequences with a sibling test within 6 delta (relative) of its boundary are counted, not
-    compared; the bonus must equal the oracle's where its CDF margin exceeds 100 delta."""
+    compared; the bonus must equal the oracle's where its CDF margin exceeds 100 delta.  *_t2d:
+    the draft rows live on a smaller vocabulary, reached through a random map t2d in which about
+    a third of the target tokens have no draft id (-1: no draft mass)."""
     need_gpu()
     inp = wl.lm_head_inputs(seed=seed, B=B, N=N, Dm=Dm, V=V, max_depth=6)
     inp["hidden"] = wl.round_bf16(inp["hidden"] * np.float32(hscale))
@@ -221,8 +223,8 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
     unif = g.random((B, N), dtype=np.float32)
     n_nodes = np.array([N - (b % 2) for b in range(B)], dtype=np.int32)
     eps, delta = float(np.float32(0.09)), float(np.float32(0.3))
-    draft = drow = None
-    if mode.startswith("reject") or mode == "walk":
+    draft = drow = t2d = None
+    if mode.startswith(("reject", "walk")):
         # per-parent draft rows: D_p = softmax(l_p + N(0, 0.5)) of the oracle's logits (inputs only)
         x = np.nan_to_num(ref0["logits"], nan=0.0) + g.standard_normal(ref0["logits"].shape) * 0.5
         e = np.exp(x - x.max(axis=2, keepdims=True))
@@ -235,12 +237,24 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
                     draft[b, drow[b, c], tok[b, c]] += 1.0
             draft /= draft.sum(axis=2, keepdims=True)
         draft = draft.astype(np.float32)
+        draft_t = draft                                  # the draft rows on the target vocabulary
+        if mode.endswith("_t2d"):
+            Vd = 2 * V // 3 + 1
+            perm = g.permutation(V)
+            t2d = np.where(perm < Vd, perm, -1).astype(np.int32)
+            dd = np.zeros((B, N, Vd), np.float64)
+            on = t2d >= 0
+            dd[:, :, t2d[on]] = draft[:, :, on]
+            dd /= dd.sum(axis=2, keepdims=True)
+            draft = dd.astype(np.float32)
+            draft_t = np.where(on[None, None, :], draft[:, :, np.maximum(t2d, 0)], 0.0).astype(np.float32)
     print(f"verify_lm_head {mode} B={B} N={N} Dm={Dm} V={V}", flush=True)
     got = sb.spec_verify_lm_head(dev(inp["hidden"], torch.bfloat16), dev(inp["W"], torch.bfloat16), dev(tok),
                                  dev(inp["parents"]), dev(unif), mode.split("_")[0], n_nodes=dev(n_nodes),
                                  eps=eps, delta=delta,
                                  draft_probs=None if draft is None else dev(draft),
-                                 draft_row=None if drow is None else dev(drow))
+                                 draft_row=None if drow is None else dev(drow),
+                                 t2d=None if t2d is None else dev(t2d))
     torch.cuda.synchronize()
     got = {k: host(v) for k, v in got.items()}
     ref = oracle.lm_head_stats(inp["hidden"], inp["W"], inp["parents"], tok, n_nodes=n_nodes)
@@ -248,7 +262,7 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
     m_id = {"greedy": oracle.MODE_GREEDY, "typical": oracle.MODE_TYPICAL, "reject": oracle.MODE_REJECT,
             "walk": oracle.MODE_WALK}[mode.split("_")[0]]
     rv = oracle.verify(logits, tok, inp["parents"], unif, m_id, n_nodes=n_nodes, eps=eps, delta=delta,
-                       draft_probs=draft, draft_row=drow)
+                       draft_probs=draft, draft_row=drow, t2d=t2d)
     d = bound(inp["hidden"], inp["W"])
     # greedy outcomes depend on the row arg-maxima only: the GPU's (same kernels) are read here
     st = sb.spec_lm_head_stats(dev(inp["hidden"], torch.bfloat16), dev(inp["W"], torch.bfloat16), dev(inp["parents"]),
@@ -271,7 +285,7 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
             H = np.log(ref["row_sum"][b, :nb]) - ref["row_ent"][b, :nb] / ref["row_sum"][b, :nb]
             if np.any(rv["margin"][b, 1:nb] < 6 * dmax * (H.max() + 1)):
                 continue
-        elif mode == "walk":
+        elif mode.startswith("walk"):
             if np.any(rv["margin"][b, 1:nb] < 6 * dmax + 1e-9):  # relative distance of each sibling test
                 continue
         elif np.any(rv["margin"][b, 1:nb] < 3 * dmax + 1e-9):     # |u - min(1, T/D)|, T within 2 delta
@@ -282,7 +296,7 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
         assert np.array_equal(got["path"][b], rv["path"][b]), f"sequence {b}: path"
         if mode == "greedy":
             assert int(got["bonus"][b]) == int(rv["bonus"][b]), f"sequence {b}: bonus"
-        elif mode == "walk":
+        elif mode.startswith("walk"):
             if rv["bonus_margin"][b] > 100 * dmax:
                 assert int(got["bonus"][b]) == int(rv["bonus"][b]), f"sequence {b}: walk bonus"
                 bonus_checked += 1
@@ -297,7 +311,7 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
             q, tol = T, 4 * float(d[b, m]) + 1e-12
             kids = [c for c in range(1, nb) if inp["parents"][b, c] == m]
             if mode.startswith("reject") and kids:
-                res = np.maximum(T - draft[b, drow[b, kids[0]]].astype(np.float64), 0.0)
+                res = np.maximum(T - draft_t[b, drow[b, kids[0]]].astype(np.float64), 0.0)
                 if res.sum() > 0:
                     q, tol = res, 4 * float(d[b, m]) / res.sum() + 1e-12
                     resid_checked += 1
