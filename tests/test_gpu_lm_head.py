@@ -331,3 +331,52 @@ def test_verify_from_hidden_states(mode, seed, B, N, Dm, V, hscale):
     if mode == "reject_row":
         print(f"  residual draws checked: {resid_checked}", flush=True)
         assert resid_checked >= 1
+
+
+@pytest.mark.parametrize("mode", ["reject", "walk"])
+def test_verify_from_hidden_states_draft_errors(mode):
+    """Error words of REJECT and WALK from hidden states equal the oracle's: a draft row out of
+    range, a t2d entry outside [-1, Vd), and (WALK only) siblings drafted from different rows.
+    Sequences without an error must still match wherever no decision is within the bound."""
+    need_gpu()
+    B, N, Dm, V, Vd = 5, 12, 128, 500, 400
+    inp = wl.lm_head_inputs(seed=77, B=B, N=N, Dm=Dm, V=V, max_depth=4)
+    g = np.random.default_rng(77)
+    tok = inp["tokens"].copy()
+    par = inp["parents"]
+    tok[:, 1:] = g.integers(0, V - 1, size=(B, N - 1))          # token V - 1 is kept for sequence 2
+    t2d = np.where(np.arange(V) < Vd, np.arange(V), -1).astype(np.int32)
+    t2d[V - 1] = Vd + 3                                           # a map entry out of range
+    tok[2, 5] = V - 1
+    draft = g.random((B, N, Vd)).astype(np.float32)
+    draft /= draft.sum(axis=2, keepdims=True)
+    drow = np.maximum(par, 0).astype(np.int32)
+    drow[1, 3] = N                                                # a draft row out of range
+    kids0 = [c for c in range(1, N) if par[3, c] == 0]
+    if len(kids0) > 1:
+        drow[3, kids0[1]] = (drow[3, kids0[0]] + 1) % N          # siblings from different rows
+    unif = g.random((B, N), dtype=np.float32)
+    print(f"verify_lm_head {mode} draft errors", flush=True)
+    got = sb.spec_verify_lm_head(dev(inp["hidden"], torch.bfloat16), dev(inp["W"], torch.bfloat16), dev(tok),
+                                 dev(par), dev(unif), mode, draft_probs=dev(draft), draft_row=dev(drow),
+                                 t2d=dev(t2d))
+    torch.cuda.synchronize()
+    got = {k: host(v) for k, v in got.items()}
+    ref = oracle.lm_head_stats(inp["hidden"], inp["W"], par, tok)
+    logits = np.nan_to_num(ref["logits"], nan=0.0)
+    m_id = oracle.MODE_REJECT if mode == "reject" else oracle.MODE_WALK
+    rv = oracle.verify(logits, tok, par, unif, m_id, draft_probs=draft, draft_row=drow, t2d=t2d)
+    assert np.array_equal(got["err"], rv["err"]), f"err {got['err']} vs {rv['err']}"
+    codes = [oracle.decode_err(int(e)) for e in rv["err"]]
+    assert codes[1] == (3, oracle.ERR_DRAFTROW) and codes[2] == (5, oracle.ERR_MAP)
+    if mode == "walk" and len(kids0) > 1:
+        assert codes[3][1] == oracle.ERR_DRAFTROW
+    d = bound(inp["hidden"], inp["W"])
+    for b in range(B):
+        if rv["err"][b] != 0:
+            continue
+        if np.any(rv["margin"][b, 1:] < 6 * float(d[b].max()) + 1e-9):
+            continue
+        assert int(got["accept_len"][b]) == int(rv["accept_len"][b]), f"sequence {b}: accept_len"
+        assert np.array_equal(got["path"][b], rv["path"][b]), f"sequence {b}: path"
+    print(f"  err words {[hex(int(e)) for e in got['err']]}", flush=True)
