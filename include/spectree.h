@@ -429,18 +429,6 @@ spec_status spec_medusa_heads(const void* h, const void* W_res, const void* W_lm
                               float* draft_probs, void* workspace, size_t ws_bytes,
                               void* stream);
 
-/* --------------------------------------------------------------------------------------
- * Kernel timing.  When enabled, the library launches each kernel through hipExtLaunchKernelGGL
- * with a start/stop HIP event pair that the kernel's own dispatch stamps on the launch stream,
- * so each pair brackets exactly one kernel execution; elapsed times accumulate per kernel name.
- * spec_prof_read() waits for the recorded events.  Timing must be off while a stream is being
- * captured into a graph.  It changes nothing in what the kernels compute.
- * ------------------------------------------------------------------------------------ */
-void spec_prof_enable(int on);
-void spec_prof_reset(void);
-/* Total milliseconds and launch count recorded for kernel `name` since the last reset.
- * Returns 0 on success, -1 if the name was never launched while enabled. */
-int spec_prof_read(const char* name, double* total_ms, int64_t* launches);
 
 #ifdef __cplusplus
 }

@@ -20,3 +20,19 @@ def _gpu_guard(request):
         import torch
         if not torch.cuda.is_available():
             pytest.skip("no GPU")
+
+
+@pytest.fixture
+def tune():
+    """Force launch shapes of the library for one test (``tune(attn_cb=2, attn_splits=3)``);
+    the overrides are removed when the test ends."""
+    from tree_attention_verification_spec_amd import binding
+    names = []
+
+    def force(**knobs):
+        for k, v in knobs.items():
+            binding.tune(k, v)
+            names.append(k)
+    yield force
+    for k in names:
+        binding.tune(k, None)

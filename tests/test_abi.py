@@ -32,14 +32,42 @@ def test_header_declares_the_entry_points():
               "spec_verify", "spec_verify_workspace", "spec_medusa_heads", "spec_medusa_heads_workspace",
               "spec_kv_compact", "spec_tree_select", "spec_lm_head_stats", "spec_lm_head_stats_workspace",
               "spec_verify_greedy_stats", "spec_verify_lm_head", "spec_verify_lm_head_workspace",
-              "spec_strerror", "spec_prof_enable", "spec_prof_reset",
-              "spec_prof_read"):
+              "spec_strerror"):
         assert n in names, n
+    for n in ("spec_prof_enable", "spec_prof_reset", "spec_prof_read", "spec_internal_tune"):
+        assert n not in names, f"{n} is internal and must not be in the public header"
 
 
 def test_every_declared_symbol_is_exported(lib):
     for n in declared_functions():
         assert hasattr(lib, n), f"{n} is declared but not exported"
+    for n in internal_functions():
+        assert hasattr(lib, n), f"{n} is declared in internal.h but not exported"
+
+
+def internal_functions():
+    text = open(os.path.join(ROOT, "tree_attention_verification_spec_amd", "csrc", "internal.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(spec_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_tuning_overrides(lib):
+    """Launch-shape overrides are explicit calls (never environment variables); unknown names
+    are refused, and a workspace query without an override depends on its arguments alone."""
+    from tree_attention_verification_spec_amd import binding
+    assert set(internal_functions()) == {"spec_prof_enable", "spec_prof_reset", "spec_prof_read",
+                                         "spec_internal_tune"}
+    assert lib.spec_internal_tune(b"no_such_knob", 1) == -1
+    base = lib.spec_verify_workspace(4, 63, 128256)
+    with binding.tuned(verify_chunk=16384, verify_store_w=0, verify_rows_list=1):
+        assert lib.spec_verify_workspace(4, 63, 128256) == base
+    a0 = lib.spec_tree_attn_workspace(1, 63, 32, 8, 128, 2111, 1)
+    with binding.tuned(attn_splits=2):
+        a2 = lib.spec_tree_attn_workspace(1, 63, 32, 8, 128, 2111, 1)
+    assert lib.spec_tree_attn_workspace(1, 63, 32, 8, 128, 2111, 1) == a0 and a2 > 0
+    src = os.path.join(ROOT, "tree_attention_verification_spec_amd", "csrc")
+    for f in os.listdir(src):
+        assert "getenv" not in open(os.path.join(src, f)).read(), f"{f} reads the environment"
 
 
 def test_status_strings(lib):

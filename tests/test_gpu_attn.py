@@ -76,18 +76,16 @@ def test_shapes(case):
     _check_full(w)
 
 
-# Every launch shape the library can pick, forced through its tuning variables (read at each
-# call): rows per wave (CB), waves per workgroup and key splits, on head dims 64 and 128, with
+# Every launch shape the library can pick, forced through its internal tuning overrides: rows
+# per wave (CB), waves per workgroup and key splits, on head dims 64 and 128, with
 # ragged prefixes, padding nodes and poisoned slots.
 SHAPE_CASES = [(2, 8, 1), (2, 8, 3), (1, 8, 1), (1, 8, 5), (2, 4, 1), (2, 4, 7), (1, 4, 2), (1, 4, 9)]
 
 
 @pytest.mark.parametrize("cb,waves,splits", SHAPE_CASES)
 @pytest.mark.parametrize("d", [64, 128])
-def test_launch_shapes(monkeypatch, cb, waves, splits, d):
-    monkeypatch.setenv("SPECTREE_ATTN_CB", str(cb))
-    monkeypatch.setenv("SPECTREE_ATTN_WAVES", str(waves))
-    monkeypatch.setenv("SPECTREE_ATTN_SPLITS", str(splits))
+def test_launch_shapes(tune, cb, waves, splits, d):
+    tune(attn_cb=cb, attn_waves=waves, attn_splits=splits)
     w = wl.custom(seed=2500 + cb * 100 + waves * 10 + splits, B=3, N=45, Hq=16, Hkv=4, d=d,
                   prefix=("uniform", 1, 900), tree=("random", 5), n_nodes_range=(20, 45), dtype="bf16",
                   extra_slots=17)

@@ -62,14 +62,14 @@ def test_small(case):
     _compare_heads(got, ref)
 
 
-# Every launch shape of the two weight-streaming kernels, forced through their tuning variables:
+# Every launch shape of the two weight-streaming kernels, forced through the library's tuning overrides:
 # ResBlock row blocks per workgroup and LM-head row blocks per wave (which also switches the
 # prefetch ring depth), on shapes with ragged vocabularies and odd column counts.
 @pytest.mark.parametrize("res_rb", ["1", "2", "4"])
 @pytest.mark.parametrize("lm_rb", ["4", "8"])
-def test_launch_shapes(monkeypatch, res_rb, lm_rb):
-    monkeypatch.setenv("SPECTREE_RES_ROWBLOCKS", res_rb)
-    monkeypatch.setenv("SPECTREE_LM_ROWBLOCKS", lm_rb)
+def test_launch_shapes(tune, res_rb, lm_rb):
+    tune(res_rowblocks=int(res_rb))
+    tune(lm_rowblocks=int(lm_rb))
     for case, c in enumerate([dict(B=3, H=3, Dm=512, V=2077, k=7), dict(B=8, H=4, Dm=256, V=1000, k=3)]):
         w = wl.custom(seed=4300 + case, B=c["B"], V=c["V"], heads={"H": c["H"], "Dm": c["Dm"], "k": c["k"]})
         hi = wl.heads_inputs(w)

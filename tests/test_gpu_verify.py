@@ -78,9 +78,9 @@ def test_small(case, mode):
 
 @pytest.mark.parametrize("chunk", ["4096", "16384"])
 @pytest.mark.parametrize("case", [0, 2, 6])
-def test_row_chunk_sizes(monkeypatch, chunk, case):
-    """The row pass at each chunk size its tuning variable allows (8192 is the default)."""
-    monkeypatch.setenv("SPECTREE_VERIFY_CHUNK", chunk)
+def test_row_chunk_sizes(tune, chunk, case):
+    """The row pass at each chunk size its tuning override allows (8192 is the default)."""
+    tune(verify_chunk=int(chunk))
     w = wl.custom(seed=3000 + case, **SMALL[case])
     parents, n_nodes, vi = _case(w)
     for mode in ("greedy", "typical", "reject"):
@@ -90,11 +90,11 @@ def test_row_chunk_sizes(monkeypatch, chunk, case):
 
 @pytest.mark.parametrize("listed", ["0", "1"])
 @pytest.mark.parametrize("case", [0, 2, 3, 4, 6])
-def test_row_pass_listed_or_per_chunk(monkeypatch, listed, case):
+def test_row_pass_listed_or_per_chunk(tune, listed, case):
     """The row pass as one workgroup per (sequence, node, chunk), or as a listing of the rows
     with children followed by one workgroup per listed (row, chunk) item (large problems by
     default): both, forced, on every mode."""
-    monkeypatch.setenv("SPECTREE_VERIFY_ROWS_LIST", listed)
+    tune(verify_rows_list=int(listed))
     w = wl.custom(seed=3000 + case, **SMALL[case])
     parents, n_nodes, vi = _case(w)
     for mode in ("greedy", "typical", "reject"):
@@ -104,10 +104,10 @@ def test_row_pass_listed_or_per_chunk(monkeypatch, listed, case):
 
 @pytest.mark.parametrize("store", ["0", "1"])
 @pytest.mark.parametrize("case", [0, 1, 3, 6])
-def test_draw_weights_stored_or_recomputed(monkeypatch, store, case):
+def test_draw_weights_stored_or_recomputed(tune, store, case):
     """The bonus draw scans weights stored by the bonus pass (small batches by default) or
     recomputes them (large batches): both paths, forced, on every mode."""
-    monkeypatch.setenv("SPECTREE_VERIFY_STORE_W", store)
+    tune(verify_store_w=int(store))
     w = wl.custom(seed=3000 + case, **SMALL[case])
     parents, n_nodes, vi = _case(w)
     for mode in ("greedy", "typical", "reject"):
@@ -116,11 +116,11 @@ def test_draw_weights_stored_or_recomputed(monkeypatch, store, case):
 
 
 @pytest.mark.parametrize("store", ["0", "1"])
-def test_zero_residual_draws_from_target(monkeypatch, store):
+def test_zero_residual_draws_from_target(tune, store):
     """Draft probabilities of 2 everywhere: each node test accepts with T/D <= 1/2 and every
     residual relu(T - D) is zero, so a rejection's bonus token is drawn from T at the kept node
     (the zero-mass reading), on both draw kernels."""
-    monkeypatch.setenv("SPECTREE_VERIFY_STORE_W", store)
+    tune(verify_store_w=int(store))
     w = wl.custom(seed=3100, B=6, N=40, V=9000, tree=("random", 5))
     parents, n_nodes, vi = _case(w)
     vi = dict(vi)
@@ -131,9 +131,9 @@ def test_zero_residual_draws_from_target(monkeypatch, store):
 
 
 @pytest.mark.parametrize("listed", ["0", "1"])
-def test_max_depth_and_errors(monkeypatch, listed):
+def test_max_depth_and_errors(tune, listed):
     need_gpu()
-    monkeypatch.setenv("SPECTREE_VERIFY_ROWS_LIST", listed)
+    tune(verify_rows_list=int(listed))
     w = wl.custom(seed=41, B=8, N=20, V=64, tree=("random", 6))
     parents, n_nodes, vi = _case(w)
     vi = dict(vi)

@@ -80,6 +80,8 @@ def lib():
     L.spec_prof_read.restype = _I
     L.spec_prof_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                  ctypes.POINTER(ctypes.c_int64)]
+    L.spec_internal_tune.restype = _I
+    L.spec_internal_tune.argtypes = [ctypes.c_char_p, _I]
     _lib = L
     return L
 
@@ -109,10 +111,14 @@ def _stream(stream=None):
     return s.cuda_stream
 
 
-def workspace(nbytes, device):
-    """A workspace buffer of ``nbytes`` bytes on ``device`` (zero-filled, although the library
-    needs no initialisation: every call writes each workspace byte it later reads)."""
-    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+def workspace(nbytes, device, fill=None):
+    """A workspace buffer of ``nbytes`` bytes on ``device``.  The library needs no
+    initialisation (every call writes each workspace byte it later reads), so by default the
+    bytes are whatever the allocator hands out; ``fill`` sets every byte to that value."""
+    t = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    if fill is not None:
+        t.fill_(int(fill))
+    return t
 
 
 # ----------------------------------------------------------------------------- tree
@@ -424,3 +430,28 @@ def prof_read(name):
     n = ctypes.c_int64(0)
     lib().spec_prof_read(name.encode(), ctypes.byref(ms), ctypes.byref(n))
     return ms.value, n.value
+
+
+def tune(name, value):
+    """Force a launch-shape choice of the library (internal; tests cover every shape it can
+    pick).  ``value`` None removes the override.  Results do not depend on it."""
+    if lib().spec_internal_tune(name.encode(), -1 if value is None else int(value)) != 0:
+        raise SpecError(f"unknown tuning override {name!r}")
+
+
+class tuned:
+    """Context manager: ``with tuned(attn_cb=2, attn_splits=3): ...`` forces those launch
+    shapes inside the block and removes the overrides on exit."""
+
+    def __init__(self, **knobs):
+        self.knobs = knobs
+
+    def __enter__(self):
+        for k, v in self.knobs.items():
+            tune(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k in self.knobs:
+            tune(k, None)
+        return False

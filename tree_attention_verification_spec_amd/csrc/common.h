@@ -5,7 +5,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <type_traits>
+#include <utility>
+
 #include "spectree.h"
+#include "internal.h"
 
 namespace spectree {
 
@@ -47,24 +52,51 @@ __device__ __forceinline__ int wave_max(int v) {
 // ---------------------------------------------------------------- host side
 
 // Kernel timing (runtime.hip).  When timing is on, prof_pair() creates a start/stop event pair
-// registered under `name` and returns true; the launch then goes through
-// hipExtLaunchKernelGGL, whose events are stamped by the kernel's own dispatch, so they bracket
-// exactly that kernel's execution on `stream`.
+// registered under `name` and returns true; the launch then goes through hipExtLaunchKernel,
+// whose events are stamped by the kernel's own dispatch, so they bracket exactly that kernel's
+// execution on `stream`.
 bool prof_pair(const char* name, hipEvent_t* start, hipEvent_t* stop);
 
-template <typename F, typename... Args>
-inline void launch(const char* name, F kernel, dim3 grid, dim3 block, hipStream_t stream, Args... args) {
+// Launch status of the calling thread's current library call: the first failed launch since
+// the last launch_status() (runtime.hip).
+void note_launch(hipError_t r);
+
+// Launches `kernel` with its arguments converted to the kernel's parameter types; the
+// launch's own return code is recorded (an error left pending by an earlier, unrelated HIP
+// call is not reported against this one).
+template <typename... KArgs, typename... Args>
+inline void launch(const char* name, void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                   Args&&... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+  std::tuple<std::decay_t<KArgs>...> vals(std::forward<Args>(args)...);
+  void* argv[sizeof...(KArgs)];
+  std::apply([&argv](auto&... v) {
+    int i = 0;
+    ((argv[i++] = static_cast<void*>(&v)), ...);
+  }, vals);
   hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t r;
   if (prof_pair(name, &e0, &e1)) {
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, e0, e1, 0, args...);
+    r = hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, stream, e0, e1, 0);
   } else {
-    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+    r = hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, stream);
   }
+  note_launch(r);
 }
 
-inline spec_status launch_status() {
-  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
-}
+// SPEC_OK unless a launch of this call failed; clears the record for the next call.
+spec_status launch_status();
+
+// Tuning overrides (runtime.hip): launch-shape choices that tests force through
+// spec_internal_tune() (internal.h), never read from the environment.  Results do not depend
+// on them.  tuning() returns the forced value, or `fallback` when none is set.
+enum Knob {
+  kKnobAttnCB, kKnobAttnWaves, kKnobAttnSplits, kKnobAttnLpt, kKnobAttnPrio, kKnobAttnKeyGroups,
+  kKnobVerifyChunk, kKnobVerifyStoreW, kKnobVerifyRowsList,
+  kKnobResRowBlocks, kKnobLmRowBlocks,
+  kKnobCount
+};
+int tuning(Knob k, int fallback);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -483,19 +483,17 @@ extern "C" spec_status spec_medusa_heads(const void* h, const void* W_res, const
   float* logits = reinterpret_cast<float*>(w + L.logits);
   const int NC = B * H;
   const dim3 blk(kThreads);
-  // Row blocks per ResBlock workgroup: 2 (Dm % 32 == 0 always holds here), or as set by
-  // SPECTREE_RES_ROWBLOCKS (1, 2 or 4; tuning).
-  const char* rre = std::getenv("SPECTREE_RES_ROWBLOCKS");
-  int rrb = rre && *rre ? std::atoi(rre) : 2;
+  // Row blocks per ResBlock workgroup: 2 (Dm % 32 == 0 always holds here), or as forced by the
+  // tuning override res_rowblocks (1, 2 or 4).
+  int rrb = tuning(kKnobResRowBlocks, 2);
   if (rrb != 1 && rrb != 2 && rrb != 4) rrb = 2;
   const __bf16* hb = static_cast<const __bf16*>(h);
   const __bf16* wr = static_cast<const __bf16*>(W_res);
   if (rrb == 4) launch("medusa_resblock", resblock_kernel<4>, dim3(H * (Dm / 64)), blk, s, hb, wr, B, H, Dm, zsplit);
   else if (rrb == 2) launch("medusa_resblock", resblock_kernel<2>, dim3(H * (Dm / 32)), blk, s, hb, wr, B, H, Dm, zsplit);
   else launch("medusa_resblock", resblock_kernel<1>, dim3(H * (Dm / 16)), blk, s, hb, wr, B, H, Dm, zsplit);
-  // 16-row blocks of W_lm per wave (RB): 8 by default, 4 with SPECTREE_LM_ROWBLOCKS=4 (tuning).
-  const char* rbe = std::getenv("SPECTREE_LM_ROWBLOCKS");
-  const int RBv = (rbe && std::atoi(rbe) == 4) ? 4 : 8;
+  // 16-row blocks of W_lm per wave (RB): 8 by default, 4 with the tuning override lm_rowblocks.
+  const int RBv = tuning(kKnobLmRowBlocks, 8) == 4 ? 4 : 8;
   const dim3 grid_lm((V + 16 * RBv - 1) / (16 * RBv));
   const __bf16* wl = static_cast<const __bf16*>(W_lm);
   const __bf16* zs = zsplit;

@@ -1,5 +1,7 @@
-// Status strings and per-kernel event timing for libspectree.
-#include <map>
+// Status strings, launch status, tuning overrides and per-kernel event timing for libspectree.
+#include <atomic>
+#include <climits>
+#include <cstring>
 #include <mutex>
 #include <string>
 #include <utility>
@@ -31,7 +33,40 @@ std::mutex g_mu;
 bool g_enabled = false;
 std::vector<Record> g_records;
 
+thread_local hipError_t t_launch = hipSuccess;
+
+std::atomic<int> g_knobs[kKnobCount];
+bool init_knobs() {
+  for (auto& k : g_knobs) k.store(INT_MIN);
+  return true;
+}
+const bool g_knobs_ready = init_knobs();
+
+const char* const kKnobNames[kKnobCount] = {
+  "attn_cb", "attn_waves", "attn_splits", "attn_lpt", "attn_prio", "attn_keygroups",
+  "verify_chunk", "verify_store_w", "verify_rows_list",
+  "res_rowblocks", "lm_rowblocks",
+};
+
 }  // namespace
+
+void note_launch(hipError_t r) {
+  if (r != hipSuccess) {
+    if (t_launch == hipSuccess) t_launch = r;
+    (void)hipGetLastError();     // the error is reported through this call's status
+  }
+}
+
+spec_status launch_status() {
+  const hipError_t r = t_launch;
+  t_launch = hipSuccess;
+  return r == hipSuccess ? SPEC_OK : SPEC_EHIP;
+}
+
+int tuning(Knob k, int fallback) {
+  const int v = g_knobs[k].load(std::memory_order_relaxed);
+  return v == INT_MIN ? fallback : v;
+}
 
 bool prof_pair(const char* name, hipEvent_t* start, hipEvent_t* stop) {
   std::lock_guard<std::mutex> lock(g_mu);
@@ -81,4 +116,15 @@ extern "C" int spec_prof_read(const char* name, double* total_ms, int64_t* launc
   if (total_ms) *total_ms = total;
   if (launches) *launches = n;
   return n > 0 ? 0 : -1;
+}
+
+extern "C" int spec_internal_tune(const char* name, int value) {
+  if (!name) return -1;
+  for (int k = 0; k < spectree::kKnobCount; ++k) {
+    if (std::strcmp(name, spectree::kKnobNames[k]) == 0) {
+      spectree::g_knobs[k].store(value < 0 ? INT_MIN : value);
+      return 0;
+    }
+  }
+  return -1;
 }

@@ -37,7 +37,6 @@
 //
 // fp32 path: a plain exact-fp32 kernel (one workgroup per query row) for small fp32 inputs.
 #include <climits>
-#include <cstdlib>
 
 #include "common.h"
 
@@ -616,26 +615,21 @@ struct Plan {
   int CB, WAVES, RBS, R, S, Mpad, units, wgs, lpt;
 };
 
-int env_int(const char* name, int fallback) {
-  const char* v = std::getenv(name);
-  return (v && *v) ? std::atoi(v) : fallback;
-}
-
 // Launch shape.  Few (sequence, KV head) units -> 64-row workgroups (4 waves of 16 rows) and
 // more key splits so that all CUs work; many units -> 256-row workgroups (8 waves of 32 rows:
 // the K/V tile in LDS serves 4x more rows per read) and few splits.  Splits are chosen for
 // about 256 workgroups (one round; an unsplit problem needs no merge), at least two for a large
 // batch (its sequences may differ in length), and every split keeps at least two tiles.
-// SPECTREE_ATTN_LPT=0/1 turns the longest-first order off or on (tuning).  SPECTREE_ATTN_CB, SPECTREE_ATTN_WAVES and SPECTREE_ATTN_SPLITS override the
-// choice (tuning knobs; results do not depend on them).
+// The tuning overrides attn_cb, attn_waves, attn_splits and attn_lpt force the choice (tests;
+// results do not depend on them).
 Plan make_plan(int B, int N, int Hq, int Hkv, int D, int S_max) {
   Plan p{};
   const int G = Hq / Hkv;
   const int M = N * G;
   p.units = B * Hkv;
   const int big = p.units * ((M + 255) / 256) >= 64;
-  p.CB = env_int("SPECTREE_ATTN_CB", big ? 2 : 1);
-  p.WAVES = env_int("SPECTREE_ATTN_WAVES", big ? 8 : 4);
+  p.CB = tuning(kKnobAttnCB, big ? 2 : 1);
+  p.WAVES = tuning(kKnobAttnWaves, big ? 8 : 4);
   if (p.CB != 1 && p.CB != 2) p.CB = 1;
   if (p.WAVES != 4 && p.WAVES != 8) p.WAVES = 4;
   p.RBS = p.WAVES * 16 * p.CB;
@@ -648,8 +642,8 @@ Plan make_plan(int B, int N, int Hq, int Hkv, int D, int S_max) {
   // the halves of long sequences are not left running alone at the end.
   p.lpt = B >= 2 && B <= kMaxLptSeqs;
   if (big && p.lpt && S < 2) S = 2;
-  S = env_int("SPECTREE_ATTN_SPLITS", S);
-  p.lpt = env_int("SPECTREE_ATTN_LPT", p.lpt) != 0 && B >= 2 && B <= kMaxLptSeqs;
+  S = tuning(kKnobAttnSplits, S);
+  p.lpt = tuning(kKnobAttnLpt, p.lpt) != 0 && B >= 2 && B <= kMaxLptSeqs;
   if (S > tiles / 2) S = tiles / 2;
   if (S < 1) S = 1;
   p.S = S;
@@ -720,7 +714,7 @@ extern "C" spec_status spec_tree_attn(const void* q, const void* k_cache, const 
   const size_t need = workspace_bytes(p, head_dim);
   if (need > 0 && (!workspace || ws_bytes < need)) return SPEC_EWORKSPACE;
   a.R = p.R; a.S = p.S; a.Mpad = p.Mpad;
-  a.prio = env_int("SPECTREE_ATTN_PRIO", 1);
+  a.prio = tuning(kKnobAttnPrio, 1);
   a.lpt = p.lpt;
   if (p.S > 1) {
     char* w = static_cast<char*>(workspace);

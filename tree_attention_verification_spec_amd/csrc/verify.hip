@@ -31,7 +31,6 @@
 #include <algorithm>
 #include <cfloat>
 #include <climits>
-#include <cstdlib>
 
 #include "common.h"
 
@@ -1313,20 +1312,15 @@ struct VerifyLayout {
 };
 
 // The listed row pass pays one more launch, so it is used from this many (sequence, node,
-// chunk) items of the plain grid up (SPECTREE_VERIFY_ROWS_LIST=0/1 forces either path; a
-// tuning knob).
+// chunk) items of the plain grid up (the tuning override verify_rows_list forces either path).
 constexpr size_t kListMinItems = 8192;
 
-// Row-pass chunk: 8K logits (measured faster than 4K and 16K at batch 1 and 16).
-// SPECTREE_VERIFY_CHUNK (4096, 8192 or 16384) overrides the choice (a tuning knob).
-int row_chunk(int B, int N, int V) {
-  int rc = 8192;
-  const char* e = std::getenv("SPECTREE_VERIFY_CHUNK");
-  if (e && *e) {
-    const int v = std::atoi(e);
-    if (v == 4096 || v == 8192 || v == 16384) rc = v;
-  }
-  return rc;
+// Row-pass chunk: 8K logits (measured faster than 4K and 16K at batch 1 and 16); the tuning
+// override verify_chunk (4096, 8192 or 16384) forces another.
+constexpr int kRowChunkMin = 4096;
+int row_chunk() {
+  const int v = tuning(kKnobVerifyChunk, 8192);
+  return (v == 4096 || v == 8192 || v == 16384) ? v : 8192;
 }
 
 // The decision + bonus pass and the draw, for chunks of CS logits.
@@ -1339,7 +1333,7 @@ void launch_tail(const VerifyArgs& a, int B, bool wave_draw, hipStream_t s) {
 
 VerifyLayout layout(int B, int N, int V) {
   VerifyLayout L{};
-  L.RC = row_chunk(B, N, V);
+  L.RC = row_chunk();
   L.CR = (V + L.RC - 1) / L.RC;
   const int c_small = (V + kChunkSmall - 1) / kChunkSmall;
   const int c_large = (V + kChunkLarge - 1) / kChunkLarge;
@@ -1347,23 +1341,22 @@ VerifyLayout layout(int B, int N, int V) {
   L.C = L.CS == kChunkSmall ? c_small : c_large;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t at = off; off += align_up(bytes, 256); return at; };
-  L.rowparts = take((size_t)B * N * L.CR * sizeof(RowPart));
+  // sized for the smallest chunk, so the size depends on the arguments alone
+  L.rowparts = take((size_t)B * N * ((V + kRowChunkMin - 1) / kRowChunkMin) * sizeof(RowPart));
   L.plans = take((size_t)B * sizeof(BonusPlan));
   // the chunk parts and weights regions are sized for either chunking (the more chunks, the
   // longer padded row), so the workspace size grows with B whichever chunk size B selects
   L.bparts = take((size_t)B * c_small * sizeof(BonusPart));
-  // Stored draw weights are used for batches up to kStoreWeightsMaxB (SPECTREE_VERIFY_STORE_W=0/1
-  // overrides); their region is always reserved, so that the workspace size grows with B and a
-  // workspace sized for a batch also serves every smaller one.
-  const char* sw = std::getenv("SPECTREE_VERIFY_STORE_W");
-  L.store_w = (sw && *sw) ? std::atoi(sw) != 0 : B <= kStoreWeightsMaxB;
+  // Stored draw weights are used for batches up to kStoreWeightsMaxB (the tuning override
+  // verify_store_w forces either way); their region is always reserved, so that the workspace
+  // size grows with B and a workspace sized for a batch also serves every smaller one.
+  L.store_w = tuning(kKnobVerifyStoreW, B <= kStoreWeightsMaxB ? 1 : 0) != 0;
   L.weights = take((size_t)B * c_large * kChunkLarge * sizeof(double));
   L.row_list = take((size_t)B * N * sizeof(int32_t));
   L.row_count = take(sizeof(int32_t));
   L.walk = take((size_t)3 * B * N * sizeof(double));
-  const char* rl = std::getenv("SPECTREE_VERIFY_ROWS_LIST");
   const bool fits = (size_t)B * N <= (size_t)kListMax;
-  L.listed = fits && ((rl && *rl) ? std::atoi(rl) != 0 : (size_t)B * N * L.CR >= kListMinItems);
+  L.listed = fits && tuning(kKnobVerifyRowsList, (size_t)B * N * L.CR >= kListMinItems ? 1 : 0) != 0;
   L.total = off;
   return L;
 }
