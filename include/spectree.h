@@ -22,10 +22,13 @@
  *     a sequence has several problems the smallest word is reported (lowest node index, then
  *     lowest code); sequence-level problems (node count, prefix length) take node 0 and are
  *     checked first.  A sequence with an error gets the documented neutral outputs.
- *   - Workspaces: query the size with the matching *_workspace() function.  A workspace needs
+ *   - Workspaces: query the size with the matching *_workspace() function (0 for a shape the
+ *     call does not support: the query applies the call's size checks).  A workspace needs
  *     no initialisation: every call writes each workspace byte it later reads (no call keeps
  *     cross-workgroup counters), so one workspace can be reused by back-to-back calls on one
  *     stream.  Calls that run concurrently need distinct workspaces.
+ *   - Codes of the spec_dtype and spec_mode enumerations are passed as plain int arguments
+ *     (`dtype`, `mode`), so that any value a caller passes is checked, never assumed valid.
  *   - Limits: N (tree nodes per sequence, padding included) <= 256.
  */
 #ifndef SPECTREE_H
@@ -74,7 +77,7 @@ enum {
 #define SPEC_MAX_CANDIDATES 4096
 
 /* Human-readable name of a status code (static storage, never NULL). */
-const char* spec_strerror(spec_status s);
+const char* spec_strerror(int status);
 
 /* --------------------------------------------------------------------------------------
  * spec_tree_build - ancestor mask, depths and positions of a batch of candidate trees.
@@ -155,11 +158,11 @@ spec_status spec_tree_assemble(const int32_t* topk_idx, const int32_t* parents,
  * SPEC_EUNSUPPORTED (head_dim, dtype), SPEC_EWORKSPACE.
  * ------------------------------------------------------------------------------------ */
 size_t spec_tree_attn_workspace(int B, int N, int Hq, int Hkv, int head_dim, int S_max,
-                                spec_dtype dtype);
+                                int dtype);
 spec_status spec_tree_attn(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* prefix_len, const uint64_t* tree_mask,
                            const int32_t* n_nodes, int B, int N, int Hq, int Hkv, int head_dim,
-                           int S_max, float scale, spec_dtype dtype, void* out, float* lse,
+                           int S_max, float scale, int dtype, void* out, float* lse,
                            int32_t* err, void* workspace, size_t ws_bytes, void* stream);
 
 /* --------------------------------------------------------------------------------------
@@ -222,7 +225,7 @@ size_t spec_verify_workspace(int B, int N, int V);
 spec_status spec_verify(const float* target_logits, const float* draft_probs,
                         const int32_t* draft_row, const int32_t* t2d, const int32_t* tokens,
                         const int32_t* parents, const int32_t* n_nodes, const float* uniforms,
-                        int B, int N, int V, int R, int Vd, int max_depth, spec_mode mode,
+                        int B, int N, int V, int R, int Vd, int max_depth, int mode,
                         float eps, float delta, int32_t* accept_len, int32_t* path,
                         int32_t* bonus_token, uint8_t* node_accept, int32_t* err,
                         void* workspace, size_t ws_bytes, void* stream);
@@ -361,12 +364,12 @@ spec_status spec_verify_greedy_stats(const int32_t* row_argmax, const int32_t* t
  * arrays, t2d NULL with Vd != V), SPEC_EUNSUPPORTED (mode, sizes, alignment), SPEC_EWORKSPACE;
  * WALK also returns what spec_verify returns for its call (after the statistics pass ran).
  * ------------------------------------------------------------------------------------ */
-size_t spec_verify_lm_head_workspace(int B, int N, int Dm, int V, spec_mode mode);
+size_t spec_verify_lm_head_workspace(int B, int N, int Dm, int V, int mode);
 spec_status spec_verify_lm_head(const void* hidden, const void* W, const int32_t* tokens,
                                 const int32_t* parents, const int32_t* n_nodes, const float* uniforms,
                                 const float* draft_probs, const int32_t* draft_row, const int32_t* t2d,
                                 int B, int N, int Dm, int V, int R, int Vd, int max_depth,
-                                spec_mode mode, float eps, float delta, int32_t* accept_len,
+                                int mode, float eps, float delta, int32_t* accept_len,
                                 int32_t* path, int32_t* bonus_token, uint8_t* node_accept,
                                 int32_t* err, void* workspace, size_t ws_bytes, void* stream);
 
@@ -400,7 +403,7 @@ spec_status spec_kv_compact(void* k_cache, void* v_cache, size_t layer_stride, i
                             const int32_t* prefix_len, int32_t* prefix_len_out,
                             const int32_t* path, const int32_t* accept_len, const int32_t* err,
                             int B, int Hkv, int S_max, int head_dim, int max_depth,
-                            spec_dtype dtype, void* stream);
+                            int dtype, void* stream);
 
 /* --------------------------------------------------------------------------------------
  * spec_medusa_heads - Medusa heads on the last hidden state, shared LM head, per-head top-k.

@@ -205,3 +205,54 @@ def test_verify_lm_head_argument_checks(lib):
     ws_walk = lib.spec_verify_lm_head_workspace(1, 63, 4096, 128256, 3)
     assert ws_walk >= ws + 63 * 128256 * 4 + lib.spec_verify_workspace(1, 63, 128256)   # rows + spec_verify's
     assert call(mode=3, draft=fake, drow=fake, R=63, Vd=128256, wsz=ws_rej) == 3
+
+
+def test_status_strings_cover_every_code(lib):
+    for code in (-1, 5, 99, 1 << 30):
+        assert lib.spec_strerror(code).decode() == "unknown status"
+
+
+# Checks that need no torch: run again against the host-sanitised build below.
+HOST_CHECKS = ["test_every_declared_symbol_is_exported", "test_status_strings", "test_host_argument_checks",
+               "test_kv_compact_host_checks", "test_workspace_sizes_are_monotone", "test_tree_select_argument_checks",
+               "test_lm_head_stats_argument_checks", "test_verify_greedy_stats_argument_checks",
+               "test_verify_lm_head_argument_checks", "test_status_strings_cover_every_code"]
+
+
+def _host_check_script(path):
+    return (
+        "import sys\n"
+        f"sys.path[:0] = [{ROOT!r}, {os.path.join(ROOT, 'tests')!r}]\n"
+        "from tree_attention_verification_spec_amd import abi\n"
+        "import test_abi\n"
+        f"L = abi.load({path!r})\n"
+        f"for name in {HOST_CHECKS!r}:\n"
+        "    getattr(test_abi, name)(L)\n"
+        "for B in (1, 7, 16, 4096, 1 << 20, 2**31 - 1):\n"
+        "    for N in (1, 63, 255, 256, 257, 2**31 - 1):\n"
+        "        for V in (1, 4096, 128256, 2**31 - 1):\n"
+        "            L.spec_verify_workspace(B, N, V)\n"
+        "            L.spec_tree_attn_workspace(B, N, 32, 8, 128, V, 1)\n"
+        "            L.spec_lm_head_stats_workspace(B, N, 4096, V)\n"
+        "            L.spec_medusa_heads_workspace(B, 4, 4096, V, 8)\n"
+        "            for m in range(4): L.spec_verify_lm_head_workspace(B, N, 4096, V, m)\n"
+        "assert L.spec_internal_tune(None, 1) == -1 and L.spec_internal_tune(b'attn_cb', -1) == 0\n"
+        "print('HOST_CHECKS_OK')\n")
+
+
+@pytest.mark.slow
+def test_host_checks_under_address_and_ub_sanitizers():
+    """The host side of the C ABI (argument checks, workspace sizing including extreme sizes,
+    status strings, the tuning setter) under AddressSanitizer + UndefinedBehaviorSanitizer: a
+    build whose host pass is instrumented (device code unchanged), loaded in a child process
+    with clang's ASan runtime preloaded.  Any report aborts the child."""
+    import subprocess
+    import sys
+    from tree_attention_verification_spec_amd import asan_build
+    path = asan_build.build()
+    env = dict(os.environ, LD_PRELOAD=asan_build.runtime(),
+               ASAN_OPTIONS="detect_leaks=0:halt_on_error=1:abort_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    r = subprocess.run([sys.executable, "-c", _host_check_script(path)], env=env, capture_output=True, text=True,
+                       timeout=600)
+    assert r.returncode == 0 and "HOST_CHECKS_OK" in r.stdout, (r.returncode, r.stdout[-3000:], r.stderr[-6000:])

@@ -122,18 +122,24 @@ def test_medusa_round_end_to_end():
     # --- oracle, on its own intermediate results
     rh = oracle.medusa_heads(hi["h"], hi["W_res"], hi["W_lm"], hi["k"])
     ra = oracle.tree_assemble(rh["topk_idx"], topo)
-    if not np.array_equal(host(heads["topk_idx"]), rh["topk_idx"]):
-        _compare_heads({k: host(v) for k, v in heads.items()}, rh)   # only near-ties may differ
-        pytest.skip("a near-tie in the top-k ranking flipped; the downstream steps are excused")
-    assert np.array_equal(host(asm["tokens"]), ra["tokens"])
-    assert np.array_equal(host(asm["draft_row"]), ra["draft_row"])
+    gk = host(heads["topk_idx"])
+    # a sequence whose top-k ranking flipped at a near-tie (checked by _compare_heads) gets other
+    # candidate tokens, so its assembly and verification are counted, not compared
+    _compare_heads({k: host(v) for k, v in heads.items()}, rh)
+    same = np.array([np.array_equal(gk[b], rh["topk_idx"][b]) for b in range(w.B)])
+    assert same.any(), "every sequence's top-k flipped at a near-tie"
+    gt, gr = host(asm["tokens"]), host(asm["draft_row"])
+    assert np.array_equal(gt[same], ra["tokens"][same])
+    assert np.array_equal(gr, ra["draft_row"])          # the rows depend on the topology only
     rtb = oracle.tree_build(np.tile(topo, (w.B, 1)), prefix_len=a["prefix_len"])
     ratt = oracle.tree_attention(a["q"], a["k_cache"], a["v_cache"], a["prefix_len"], rtb["dense"])
     out = host(att["out"].float())
     assert np.abs(out - ratt["out"]).max() <= 2e-2 * np.abs(ratt["out"]).max()
     rv = oracle.verify(ti["target_logits"], ra["tokens"], np.tile(topo, (w.B, 1)), ti["uniforms"],
                        oracle.MODE_REJECT, draft_probs=rh["probs"], draft_row=ra["draft_row"], max_depth=w.N - 1)
-    got = {k: host(v) for k, v in ver.items()}
+    got = {k: host(v)[same] for k, v in ver.items()}
+    rv = {k: (v[same] if isinstance(v, np.ndarray) and v.shape[:1] == (w.B,) else v) for k, v in rv.items()}
     # draft probabilities differ from the oracle's by fp32 rounding (~1e-7 relative), so the
     # residual draw is compared with a margin of 1e-6 instead of the fp64-only 1e-12
-    compare_verify(got, rv, np.full(w.B, w.N), bonus_margin=1e-6, max_excused_frac=0.25)
+    ex = compare_verify(got, rv, np.full(int(same.sum()), w.N), bonus_margin=1e-6, max_excused_frac=0.25)
+    print(f"medusa round: {int(same.sum())} of {w.B} sequences with the oracle's top-k, {ex} excused at a margin")

@@ -40,7 +40,7 @@ def _check(w, max_depth=None):
     vi = wl.verify_inputs(w, parents)
     md = w.N - 1 if max_depth is None else max_depth
     got, ref = _run(vi, parents, n_nodes, md)
-    ex = compare_verify(got, ref, n_nodes, bonus_margin=WALK_BONUS_MARGIN)
+    ex = compare_verify(got, ref, n_nodes, bonus_margin=WALK_BONUS_MARGIN, walk=True)
     return ref, ex
 
 
@@ -90,7 +90,7 @@ def test_max_depth_and_errors():
         got, ref = _run(vi, par, n_nodes, md)
         assert oracle.decode_err(ref["err"][3]) == (kids[1], oracle.ERR_DRAFTROW)
         assert (ref["err"] != 0).sum() >= 5
-        compare_verify(got, ref, n_nodes, bonus_margin=WALK_BONUS_MARGIN)
+        compare_verify(got, ref, n_nodes, bonus_margin=WALK_BONUS_MARGIN, walk=True)
 
 
 def test_chi_square_gpu():
@@ -131,4 +131,4 @@ def test_chi_square_gpu():
     ref = oracle.verify(logits[sl], tokens[sl], parents[sl], u[sl], oracle.MODE_WALK,
                         draft_probs=draft[sl], draft_row=dr[sl])
     gsl = {k: host(v)[sl] for k, v in got.items()}
-    compare_verify(gsl, ref, np.full(3000, N), bonus_margin=WALK_BONUS_MARGIN)
+    compare_verify(gsl, ref, np.full(3000, N), bonus_margin=WALK_BONUS_MARGIN, walk=True)

@@ -11,6 +11,8 @@ import os
 
 import torch
 
+from . import abi
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libspectree.so")
 
@@ -19,10 +21,6 @@ GREEDY, TYPICAL, REJECT, WALK = 0, 1, 2, 3
 MODES = {"greedy": GREEDY, "typical": TYPICAL, "reject": REJECT, "walk": WALK}
 
 _lib = None
-_P = ctypes.c_void_p
-_I = ctypes.c_int
-_F = ctypes.c_float
-_Z = ctypes.c_size_t
 
 
 class SpecError(RuntimeError):
@@ -37,53 +35,8 @@ def lib():
     if not os.path.exists(LIB_PATH):
         raise SpecError(f"{LIB_PATH} is missing: build it with "
                         "`python -m tree_attention_verification_spec_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
-    L.spec_strerror.restype = ctypes.c_char_p
-    L.spec_strerror.argtypes = [_I]
-    L.spec_tree_build.restype = _I
-    L.spec_tree_build.argtypes = [_P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P]
-    L.spec_tree_assemble.restype = _I
-    L.spec_tree_assemble.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P]
-    L.spec_tree_select.restype = _I
-    L.spec_tree_select.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]
-    L.spec_lm_head_stats_workspace.restype = _Z
-    L.spec_lm_head_stats_workspace.argtypes = [_I, _I, _I, _I]
-    L.spec_lm_head_stats.restype = _I
-    L.spec_lm_head_stats.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P]
-    L.spec_verify_greedy_stats.restype = _I
-    L.spec_verify_greedy_stats.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
-    L.spec_verify_lm_head_workspace.restype = _Z
-    L.spec_verify_lm_head_workspace.argtypes = [_I, _I, _I, _I, _I]
-    L.spec_verify_lm_head.restype = _I
-    L.spec_verify_lm_head.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
-                                      _F, _F, _P, _P, _P, _P, _P, _P, _Z, _P]
-    L.spec_tree_attn_workspace.restype = _Z
-    L.spec_tree_attn_workspace.argtypes = [_I, _I, _I, _I, _I, _I, _I]
-    L.spec_tree_attn.restype = _I
-    L.spec_tree_attn.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P,
-                                 _P, _Z, _P]
-    L.spec_verify_workspace.restype = _Z
-    L.spec_verify_workspace.argtypes = [_I, _I, _I]
-    L.spec_verify.restype = _I
-    L.spec_verify.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _F,
-                              _P, _P, _P, _P, _P, _P, _Z, _P]
-    L.spec_medusa_heads_workspace.restype = _Z
-    L.spec_medusa_heads_workspace.argtypes = [_I, _I, _I, _I, _I]
-    L.spec_medusa_heads.restype = _I
-    L.spec_medusa_heads.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _Z, _P]
-    L.spec_kv_compact.restype = _I
-    L.spec_kv_compact.argtypes = [_P, _P, _Z, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
-    L.spec_prof_enable.restype = None
-    L.spec_prof_enable.argtypes = [_I]
-    L.spec_prof_reset.restype = None
-    L.spec_prof_reset.argtypes = []
-    L.spec_prof_read.restype = _I
-    L.spec_prof_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
-                                 ctypes.POINTER(ctypes.c_int64)]
-    L.spec_internal_tune.restype = _I
-    L.spec_internal_tune.argtypes = [ctypes.c_char_p, _I]
-    _lib = L
-    return L
+    _lib = abi.load(LIB_PATH)
+    return _lib
 
 
 def _check(status, what):

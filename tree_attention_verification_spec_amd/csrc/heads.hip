@@ -465,6 +465,7 @@ using namespace spectree;
 
 extern "C" size_t spec_medusa_heads_workspace(int B, int H, int Dm, int V, int k) {
   if (B < 1 || H < 1 || Dm < 1 || V < 1 || k < 1) return 0;
+  if (B > 16 || H > kMaxCols || B * H > kMaxCols || Dm % 128 != 0 || k > 64 || k > V) return 0;
   return heads_layout(B, H, Dm, V).total;
 }
 
@@ -474,7 +475,7 @@ extern "C" spec_status spec_medusa_heads(const void* h, const void* W_res, const
                                          void* stream) {
   if (B < 1 || H < 1 || Dm < 1 || V < 1 || k < 1) return SPEC_EINVAL;
   if (!h || !W_res || !W_lm || !topk_idx || !topk_prob) return SPEC_EINVAL;
-  if (B > 16 || B * H > kMaxCols || Dm % 128 != 0 || k > 64 || k > V) return SPEC_EUNSUPPORTED;
+  if (B > 16 || H > kMaxCols || B * H > kMaxCols || Dm % 128 != 0 || k > 64 || k > V) return SPEC_EUNSUPPORTED;
   const HeadsLayout L = heads_layout(B, H, Dm, V);
   if (!workspace || ws_bytes < L.total) return SPEC_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -83,7 +83,7 @@ extern "C" spec_status spec_kv_compact(void* k_cache, void* v_cache, size_t laye
                                        const int32_t* prefix_len, int32_t* prefix_len_out,
                                        const int32_t* path, const int32_t* accept_len,
                                        const int32_t* err, int B, int Hkv, int S_max, int head_dim,
-                                       int max_depth, spec_dtype dtype, void* stream) {
+                                       int max_depth, int dtype, void* stream) {
   if (!k_cache || !v_cache || !prefix_len || !path || !accept_len) return SPEC_EINVAL;
   if (L < 1 || B < 1 || Hkv < 1 || S_max < 1 || head_dim < 1 || max_depth < 0) return SPEC_EINVAL;
   if (prefix_len_out && prefix_len_out == prefix_len) return SPEC_EINVAL;

@@ -1106,17 +1106,28 @@ LmLayout lm_layout(int B, int N, int V, int Dm) {
 }
 }  // namespace
 
+namespace {
+constexpr int kLMaxVocab = 1 << 24;
+
+// Sizes the statistics pass supports (shared by the workspace queries and the calls).
+spec_status check_lm_shape(int B, int N, int Dm, int V) {
+  if (B < 1 || N < 1 || Dm < 1 || V < 1) return SPEC_EINVAL;
+  if (N > SPEC_MAX_NODES || (size_t)B * N > (size_t)kLMaxRows) return SPEC_EUNSUPPORTED;
+  if (Dm % 128 != 0 || V > kLMaxVocab) return SPEC_EUNSUPPORTED;
+  return SPEC_OK;
+}
+}  // namespace
+
 extern "C" size_t spec_lm_head_stats_workspace(int B, int N, int Dm, int V) {
-  if (B < 1 || N < 1 || Dm < 1 || V < 1) return 0;
+  if (check_lm_shape(B, N, Dm, V) != SPEC_OK) return 0;
   return lm_layout(B, N, V, Dm).total;
 }
 
 namespace {
 spec_status check_lm(const void* hidden, const void* W, int B, int N, int Dm, int V) {
-  if (B < 1 || N < 1 || Dm < 1 || V < 1) return SPEC_EINVAL;
+  const spec_status shape = check_lm_shape(B, N, Dm, V);
+  if (shape != SPEC_OK) return shape;
   if (!hidden || !W) return SPEC_EINVAL;
-  if (N > SPEC_MAX_NODES || (size_t)B * N > (size_t)kLMaxRows) return SPEC_EUNSUPPORTED;
-  if (Dm % 128 != 0) return SPEC_EUNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(hidden) & 15) || (reinterpret_cast<uintptr_t>(W) & 15))
     return SPEC_EUNSUPPORTED;
   return SPEC_OK;
@@ -1158,7 +1169,7 @@ void launch_lm(const __bf16* X, const __bf16* Wb, const int32_t* parents, const 
 struct VlLayout {
   size_t mx, am, sum, ent, cand, err, plan, rows, tsum, sub, total;
 };
-VlLayout vl_layout(const LmLayout& L, int B, int N, int V, spec_mode mode) {
+VlLayout vl_layout(const LmLayout& L, int B, int N, int V, int mode) {
   const bool reject = mode == SPEC_VERIFY_REJECT, walk = mode == SPEC_VERIFY_WALK;
   const size_t M = (size_t)B * N;
   VlLayout v{};
@@ -1196,8 +1207,8 @@ extern "C" spec_status spec_lm_head_stats(const void* hidden, const void* W, con
   return launch_status();
 }
 
-extern "C" size_t spec_verify_lm_head_workspace(int B, int N, int Dm, int V, spec_mode mode) {
-  if (B < 1 || N < 1 || Dm < 1 || V < 1) return 0;
+extern "C" size_t spec_verify_lm_head_workspace(int B, int N, int Dm, int V, int mode) {
+  if (check_lm_shape(B, N, Dm, V) != SPEC_OK) return 0;
   return vl_layout(lm_layout(B, N, V, Dm), B, N, V, mode).total;
 }
 
@@ -1205,7 +1216,7 @@ extern "C" spec_status spec_verify_lm_head(const void* hidden, const void* W, co
                                            const int32_t* parents, const int32_t* n_nodes,
                                            const float* uniforms, const float* draft_probs,
                                            const int32_t* draft_row, const int32_t* t2d, int B, int N,
-                                           int Dm, int V, int R, int Vd, int max_depth, spec_mode mode,
+                                           int Dm, int V, int R, int Vd, int max_depth, int mode,
                                            float eps, float delta, int32_t* accept_len, int32_t* path,
                                            int32_t* bonus_token, uint8_t* node_accept, int32_t* err,
                                            void* workspace, size_t ws_bytes, void* stream) {

@@ -9,7 +9,7 @@
 
 #include "common.h"
 
-extern "C" const char* spec_strerror(spec_status s) {
+extern "C" const char* spec_strerror(int s) {
   switch (s) {
     case SPEC_OK: return "ok";
     case SPEC_EINVAL: return "invalid argument";

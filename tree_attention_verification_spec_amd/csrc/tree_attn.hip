@@ -622,6 +622,22 @@ struct Plan {
 // batch (its sequences may differ in length), and every split keeps at least two tiles.
 // The tuning overrides attn_cb, attn_waves, attn_splits and attn_lpt force the choice (tests;
 // results do not depend on them).
+// Shapes both paths accept: sizes in range and a grid that fits (checked in 64-bit before any
+// 32-bit arithmetic of the plan).  Shared by the workspace query and the call.
+spec_status check_shape(int B, int N, int Hq, int Hkv, int head_dim, int S_max, int dtype) {
+  if (B < 1 || N < 1 || N > SPEC_MAX_NODES || Hq < 1 || Hkv < 1 || S_max < 1) return SPEC_EINVAL;
+  if (Hq % Hkv != 0) return SPEC_EUNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return SPEC_EUNSUPPORTED;
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EUNSUPPORTED;
+  // fp32: one workgroup per query row; bf16: at most (units rounded to 8) x row blocks x splits
+  // with splits <= S_max / 128 + 1 and row blocks <= N * G / 64 + 1
+  const long long units = (long long)B * Hkv;
+  const long long rows = (long long)N * (Hq / Hkv);
+  if ((long long)B * N * Hq > INT_MAX / 2 || units > INT_MAX / 8) return SPEC_EUNSUPPORTED;
+  if ((units + 8) * (rows / 64 + 1) * ((long long)S_max / 128 + 1) > INT_MAX / 2) return SPEC_EUNSUPPORTED;
+  return SPEC_OK;
+}
+
 Plan make_plan(int B, int N, int Hq, int Hkv, int D, int S_max) {
   Plan p{};
   const int G = Hq / Hkv;
@@ -636,7 +652,7 @@ Plan make_plan(int B, int N, int Hq, int Hkv, int D, int S_max) {
   p.R = (M + p.RBS - 1) / p.RBS;
   p.Mpad = p.R * p.RBS;
   const int target = 256;   // one workgroup per CU, all in one round (measured best)
-  const int tiles = (S_max + kKT - 1) / kKT;
+  const int tiles = S_max / kKT + (S_max % kKT != 0);
   int S = (target + p.units * p.R - 1) / (p.units * p.R);
   // Batches may mix prefix lengths: at least two splits, taken longest sequence first, so that
   // the halves of long sequences are not left running alone at the end.
@@ -678,22 +694,21 @@ size_t workspace_bytes(const Plan& p, int D) {
 using namespace spectree;
 
 extern "C" size_t spec_tree_attn_workspace(int B, int N, int Hq, int Hkv, int head_dim, int S_max,
-                                           spec_dtype dtype) {
-  if (dtype != SPEC_BF16 || B < 1 || N < 1 || Hkv < 1 || Hq < Hkv || S_max < 1) return 0;
+                                           int dtype) {
+  if (check_shape(B, N, Hq, Hkv, head_dim, S_max, dtype) != SPEC_OK || dtype != SPEC_BF16) return 0;
   return workspace_bytes(make_plan(B, N, Hq, Hkv, head_dim, S_max), head_dim);
 }
 
 extern "C" spec_status spec_tree_attn(const void* q, const void* k_cache, const void* v_cache,
                                       const int32_t* prefix_len, const uint64_t* tree_mask,
                                       const int32_t* n_nodes, int B, int N, int Hq, int Hkv,
-                                      int head_dim, int S_max, float scale, spec_dtype dtype,
+                                      int head_dim, int S_max, float scale, int dtype,
                                       void* out, float* lse, int32_t* err, void* workspace,
                                       size_t ws_bytes, void* stream) {
   if (B < 1 || N < 1 || N > SPEC_MAX_NODES || Hq < 1 || Hkv < 1 || S_max < 1) return SPEC_EINVAL;
   if (!q || !k_cache || !v_cache || !prefix_len || !tree_mask || !out) return SPEC_EINVAL;
-  if (Hq % Hkv != 0) return SPEC_EUNSUPPORTED;
-  if (head_dim != 64 && head_dim != 128) return SPEC_EUNSUPPORTED;
-  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EUNSUPPORTED;
+  const spec_status shape = check_shape(B, N, Hq, Hkv, head_dim, S_max, dtype);
+  if (shape != SPEC_OK) return shape;
   if (!(scale > 0.f) || !(scale < INFINITY)) return SPEC_EINVAL;   // positive and finite
   hipStream_t s = static_cast<hipStream_t>(stream);
 

@@ -1318,6 +1318,7 @@ constexpr size_t kListMinItems = 8192;
 // Row-pass chunk: 8K logits (measured faster than 4K and 16K at batch 1 and 16); the tuning
 // override verify_chunk (4096, 8192 or 16384) forces another.
 constexpr int kRowChunkMin = 4096;
+constexpr int kMaxVocab = 1 << 20;     // 256 chunks of 4096 logits in the bonus draw
 int row_chunk() {
   const int v = tuning(kKnobVerifyChunk, 8192);
   return (v == 4096 || v == 8192 || v == 16384) ? v : 8192;
@@ -1367,7 +1368,7 @@ VerifyLayout layout(int B, int N, int V) {
 using namespace spectree;
 
 extern "C" size_t spec_verify_workspace(int B, int N, int V) {
-  if (B < 1 || N < 1 || V < 1) return 0;
+  if (B < 1 || N < 1 || V < 1 || V > kMaxVocab) return 0;
   return layout(B, N, V).total;
 }
 
@@ -1375,7 +1376,7 @@ extern "C" spec_status spec_verify(const float* target_logits, const float* draf
                                    const int32_t* draft_row, const int32_t* t2d,
                                    const int32_t* tokens, const int32_t* parents,
                                    const int32_t* n_nodes, const float* uniforms, int B, int N,
-                                   int V, int R, int Vd, int max_depth, spec_mode mode, float eps,
+                                   int V, int R, int Vd, int max_depth, int mode, float eps,
                                    float delta, int32_t* accept_len, int32_t* path,
                                    int32_t* bonus_token, uint8_t* node_accept, int32_t* err,
                                    void* workspace, size_t ws_bytes, void* stream) {
@@ -1390,6 +1391,7 @@ extern "C" spec_status spec_verify(const float* target_logits, const float* draf
     if (!t2d && Vd != V) return SPEC_EINVAL;
   }
   if (mode == SPEC_VERIFY_TYPICAL && (!(eps == eps) || !(delta == delta))) return SPEC_EINVAL;
+  if (V > kMaxVocab) return SPEC_EUNSUPPORTED;
   const VerifyLayout L = layout(B, N, V);
   if (L.C > kThreads || (size_t)L.CR * N * B > (size_t)INT_MAX) return SPEC_EUNSUPPORTED;
   if (!workspace || ws_bytes < L.total) return SPEC_EWORKSPACE;
