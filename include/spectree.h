@@ -46,7 +46,8 @@ typedef enum {
   SPEC_EINVAL = 1,        /* bad argument: NULL required pointer, size out of range     */
   SPEC_EUNSUPPORTED = 2,  /* well-formed but unsupported: head_dim, dtype, group size   */
   SPEC_EWORKSPACE = 3,    /* workspace NULL or smaller than the *_workspace() size      */
-  SPEC_EHIP = 4           /* a HIP runtime call or a kernel launch failed               */
+  SPEC_EHIP = 4,          /* a HIP runtime call or a kernel launch failed               */
+  SPEC_ESCRATCH = 5       /* the call needs more scratch than spec_verify_static's array */
 } spec_status;
 
 typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
@@ -229,6 +230,34 @@ spec_status spec_verify(const float* target_logits, const float* draft_probs,
                         float eps, float delta, int32_t* accept_len, int32_t* path,
                         int32_t* bonus_token, uint8_t* node_accept, int32_t* err,
                         void* workspace, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------------------------------
+ * spec_verify_static - spec_verify without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph capture, serving loops
+ * and harnesses that forbid hipMalloc).
+ *
+ * Arguments, outputs, rules and data errors are exactly spec_verify's (same kernels).  The
+ * scratch lives in a fixed device array of the library, SPEC_VERIFY_STATIC_MAX_BYTES per GPU,
+ * which each GPU the library runs on holds until the process ends; this call allocates and
+ * frees nothing.  spec_verify_static_bytes() gives the scratch a call of that size needs (it
+ * is at most spec_verify_workspace()).  Every call on one GPU uses that GPU's array and leaves
+ * its own contents there: calls that overlap on one GPU (on different streams, or from
+ * different host threads) race and give undefined results.  No call relies on the array's
+ * previous contents (every byte read is written earlier in the same call).  `stream` must
+ * belong to the current device (NULL: the current device's null stream).
+ * Errors: as spec_verify, plus SPEC_ESCRATCH when spec_verify_static_bytes() exceeds
+ * SPEC_VERIFY_STATIC_MAX_BYTES (e.g. batch 8 at a vocabulary near 10^6), SPEC_EINVAL when
+ * `stream` belongs to another device, SPEC_EHIP when the array's address cannot be found.
+ * ------------------------------------------------------------------------------------ */
+#define SPEC_VERIFY_STATIC_MAX_BYTES ((size_t)16 << 20)
+size_t spec_verify_static_bytes(int B, int N, int V);
+spec_status spec_verify_static(const float* target_logits, const float* draft_probs,
+                               const int32_t* draft_row, const int32_t* t2d, const int32_t* tokens,
+                               const int32_t* parents, const int32_t* n_nodes, const float* uniforms,
+                               int B, int N, int V, int R, int Vd, int max_depth, int mode,
+                               float eps, float delta, int32_t* accept_len, int32_t* path,
+                               int32_t* bonus_token, uint8_t* node_accept, int32_t* err,
+                               void* stream);
 
 /* --------------------------------------------------------------------------------------
  * spec_tree_select - dynamic tree: keep the best N-node subtree of a drafted candidate tree.

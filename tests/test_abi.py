@@ -208,15 +208,39 @@ def test_verify_lm_head_argument_checks(lib):
 
 
 def test_status_strings_cover_every_code(lib):
-    for code in (-1, 5, 99, 1 << 30):
+    assert lib.spec_strerror(5).decode() == "request exceeds the fixed scratch array"
+    for code in (-1, 6, 99, 1 << 30):
         assert lib.spec_strerror(code).decode() == "unknown status"
+
+
+def test_verify_static_host_checks(lib):
+    """spec_verify_static refuses, before any device call, arguments spec_verify refuses and a
+    request larger than its fixed scratch array."""
+    fake = ctypes.c_void_p(0x1000)
+    limit = 16 << 20
+    assert lib.spec_verify_static_bytes(1, 63, 128256) <= lib.spec_verify_workspace(1, 63, 128256)
+    assert lib.spec_verify_static_bytes(16, 127, 128256) < lib.spec_verify_workspace(16, 127, 128256)
+    for B, N, V in ((1, 63, 128256), (16, 127, 128256), (4, 255, 128256), (8, 127, 32000)):
+        assert lib.spec_verify_static_bytes(B, N, V) <= limit, (B, N, V)
+    assert lib.spec_verify_static_bytes(8, 256, 1_000_000) > limit
+    assert lib.spec_verify_static_bytes(0, 10, 10) == 0
+
+    def call(B=2, N=10, V=100, mode=0, R=0, Vd=0, draft=None, drow=None, logits=fake, acc=fake):
+        return lib.spec_verify_static(logits, draft, drow, None, fake, fake, None, fake, B, N, V, R, Vd, N - 1, mode,
+                                      0.09, 0.3, acc, fake, fake, None, fake, None)
+
+    assert call(logits=None) == 1 and call(acc=None) == 1 and call(B=0) == 1 and call(N=257) == 1
+    assert call(mode=2) == 1 and call(mode=9) == 1                 # REJECT without drafts; bad mode
+    assert call(mode=2, R=3, Vd=50, draft=fake, drow=fake) == 1     # Vd != V without t2d
+    assert call(B=8, N=256, V=1_000_000) == 5
 
 
 # Checks that need no torch: run again against the host-sanitised build below.
 HOST_CHECKS = ["test_every_declared_symbol_is_exported", "test_status_strings", "test_host_argument_checks",
                "test_kv_compact_host_checks", "test_workspace_sizes_are_monotone", "test_tree_select_argument_checks",
                "test_lm_head_stats_argument_checks", "test_verify_greedy_stats_argument_checks",
-               "test_verify_lm_head_argument_checks", "test_status_strings_cover_every_code"]
+               "test_verify_lm_head_argument_checks", "test_status_strings_cover_every_code",
+               "test_verify_static_host_checks"]
 
 
 def _host_check_script(path):
@@ -231,7 +255,7 @@ def _host_check_script(path):
         "for B in (1, 7, 16, 4096, 1 << 20, 2**31 - 1):\n"
         "    for N in (1, 63, 255, 256, 257, 2**31 - 1):\n"
         "        for V in (1, 4096, 128256, 2**31 - 1):\n"
-        "            L.spec_verify_workspace(B, N, V)\n"
+        "            L.spec_verify_workspace(B, N, V); L.spec_verify_static_bytes(B, N, V)\n"
         "            L.spec_tree_attn_workspace(B, N, 32, 8, 128, V, 1)\n"
         "            L.spec_lm_head_stats_workspace(B, N, 4096, V)\n"
         "            L.spec_medusa_heads_workspace(B, 4, 4096, V, 8)\n"

@@ -36,6 +36,11 @@ def declare(L):
     L.spec_tree_attn.restype = _I
     L.spec_tree_attn.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P,
                                  _P, _Z, _P]
+    L.spec_verify_static_bytes.restype = _Z
+    L.spec_verify_static_bytes.argtypes = [_I, _I, _I]
+    L.spec_verify_static.restype = _I
+    L.spec_verify_static.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _F,
+                                     _P, _P, _P, _P, _P, _P]
     L.spec_verify_workspace.restype = _Z
     L.spec_verify_workspace.argtypes = [_I, _I, _I]
     L.spec_verify.restype = _I

@@ -214,6 +214,43 @@ def spec_verify(target_logits, tokens, parents, uniforms, mode, draft_probs=None
     return out
 
 
+def verify_static_bytes(B, N, V):
+    return int(lib().spec_verify_static_bytes(B, N, V))
+
+
+def spec_verify_static(target_logits, tokens, parents, uniforms, mode, draft_probs=None, draft_row=None,
+                       t2d=None, n_nodes=None, eps=0.09, delta=0.3, max_depth=None, out=None, stream=None):
+    """spec_verify with the library's fixed scratch array instead of a workspace (no device
+    allocation inside the call when ``out`` is given)."""
+    B, N, V = target_logits.shape
+    dev = target_logits.device
+    mode = MODES.get(mode, mode)
+    if max_depth is None:
+        max_depth = N - 1
+    R = Vd = 0
+    if draft_probs is not None:
+        _, R, Vd = draft_probs.shape
+    if out is None:
+        out = {"accept_len": torch.empty((B,), dtype=torch.int32, device=dev),
+               "path": torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev),
+               "bonus": torch.empty((B,), dtype=torch.int32, device=dev),
+               "node_accept": torch.empty((B, N), dtype=torch.uint8, device=dev),
+               "err": torch.empty((B,), dtype=torch.int32, device=dev)}
+    _check(lib().spec_verify_static(
+        _ptr(target_logits, torch.float32, (B, N, V), "target_logits"),
+        _ptr(draft_probs, torch.float32, (B, R, Vd), "draft_probs"),
+        _ptr(draft_row, torch.int32, (B, N), "draft_row"), _ptr(t2d, torch.int32, (V,), "t2d"),
+        _ptr(tokens, torch.int32, (B, N), "tokens"), _ptr(parents, torch.int32, (B, N), "parents"),
+        _ptr(n_nodes, torch.int32, (B,), "n_nodes"), _ptr(uniforms, torch.float32, (B, N), "uniforms"),
+        B, N, V, R, Vd, int(max_depth), int(mode), float(eps), float(delta),
+        _ptr(out["accept_len"], torch.int32, (B,), "accept_len"),
+        _ptr(out["path"], torch.int32, (B, max_depth + 1), "path"),
+        _ptr(out["bonus"], torch.int32, (B,), "bonus"),
+        _ptr(out["node_accept"], torch.uint8, (B, N), "node_accept"),
+        _ptr(out["err"], torch.int32, (B,), "err"), _stream(stream)), "spec_verify_static")
+    return out
+
+
 # ----------------------------------------------------------------------------- target LM head + row statistics
 
 def lm_head_stats_workspace_bytes(B, N, Dm, V):

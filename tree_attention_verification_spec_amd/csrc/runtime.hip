@@ -16,6 +16,7 @@ extern "C" const char* spec_strerror(int s) {
     case SPEC_EUNSUPPORTED: return "unsupported configuration";
     case SPEC_EWORKSPACE: return "workspace missing or too small";
     case SPEC_EHIP: return "HIP runtime error";
+    case SPEC_ESCRATCH: return "request exceeds the fixed scratch array";
   }
   return "unknown status";
 }

@@ -31,6 +31,7 @@
 #include <algorithm>
 #include <cfloat>
 #include <climits>
+#include <mutex>
 
 #include "common.h"
 
@@ -1332,7 +1333,9 @@ void launch_tail(const VerifyArgs& a, int B, bool wave_draw, hipStream_t s) {
   else launch("verify_select", select_kernel<VEC, CS>, dim3(B), dim3(kThreads), s, a);
 }
 
-VerifyLayout layout(int B, int N, int V) {
+// `packed`: the layout of spec_verify_static, whose scratch array holds one call at a time, so
+// the draw-weight region is taken only when this call stores weights.
+VerifyLayout layout(int B, int N, int V, bool packed = false) {
   VerifyLayout L{};
   L.RC = row_chunk();
   L.CR = (V + L.RC - 1) / L.RC;
@@ -1352,7 +1355,7 @@ VerifyLayout layout(int B, int N, int V) {
   // verify_store_w forces either way); their region is always reserved, so that the workspace
   // size grows with B and a workspace sized for a batch also serves every smaller one.
   L.store_w = tuning(kKnobVerifyStoreW, B <= kStoreWeightsMaxB ? 1 : 0) != 0;
-  L.weights = take((size_t)B * c_large * kChunkLarge * sizeof(double));
+  L.weights = take(packed && !L.store_w ? 0 : (size_t)B * c_large * kChunkLarge * sizeof(double));
   L.row_list = take((size_t)B * N * sizeof(int32_t));
   L.row_count = take(sizeof(int32_t));
   L.walk = take((size_t)3 * B * N * sizeof(double));
@@ -1362,24 +1365,12 @@ VerifyLayout layout(int B, int N, int V) {
   return L;
 }
 
-}  // namespace
-}  // namespace spectree
-
-using namespace spectree;
-
-extern "C" size_t spec_verify_workspace(int B, int N, int V) {
-  if (B < 1 || N < 1 || V < 1 || V > kMaxVocab) return 0;
-  return layout(B, N, V).total;
-}
-
-extern "C" spec_status spec_verify(const float* target_logits, const float* draft_probs,
-                                   const int32_t* draft_row, const int32_t* t2d,
-                                   const int32_t* tokens, const int32_t* parents,
-                                   const int32_t* n_nodes, const float* uniforms, int B, int N,
-                                   int V, int R, int Vd, int max_depth, int mode, float eps,
-                                   float delta, int32_t* accept_len, int32_t* path,
-                                   int32_t* bonus_token, uint8_t* node_accept, int32_t* err,
-                                   void* workspace, size_t ws_bytes, void* stream) {
+// Host-checkable arguments of spec_verify and spec_verify_static.
+spec_status check_verify(const float* target_logits, const float* draft_probs, const int32_t* draft_row,
+                         const int32_t* t2d, const int32_t* tokens, const int32_t* parents,
+                         const float* uniforms, int B, int N, int V, int R, int Vd, int max_depth,
+                         int mode, float eps, float delta, const int32_t* accept_len,
+                         const int32_t* path, const int32_t* bonus_token, const int32_t* err) {
   if (B < 1 || N < 1 || N > SPEC_MAX_NODES || V < 1 || max_depth < 0) return SPEC_EINVAL;
   if (!target_logits || !tokens || !parents || !uniforms || !accept_len || !path || !bonus_token || !err)
     return SPEC_EINVAL;
@@ -1394,16 +1385,22 @@ extern "C" spec_status spec_verify(const float* target_logits, const float* draf
   if (V > kMaxVocab) return SPEC_EUNSUPPORTED;
   const VerifyLayout L = layout(B, N, V);
   if (L.C > kThreads || (size_t)L.CR * N * B > (size_t)INT_MAX) return SPEC_EUNSUPPORTED;
-  if (!workspace || ws_bytes < L.total) return SPEC_EWORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  return SPEC_OK;
+}
 
+// The kernels of one verification, with the scratch regions of layout L at `w`.
+spec_status run_verify(const float* target_logits, const float* draft_probs, const int32_t* draft_row,
+                       const int32_t* t2d, const int32_t* tokens, const int32_t* parents,
+                       const int32_t* n_nodes, const float* uniforms, int B, int N, int V, int R, int Vd,
+                       int max_depth, int mode, float eps, float delta, int32_t* accept_len,
+                       int32_t* path, int32_t* bonus_token, uint8_t* node_accept, int32_t* err,
+                       const VerifyLayout& L, char* w, hipStream_t s) {
   VerifyArgs a{};
   a.logits = target_logits; a.draft = draft_probs; a.draft_row = draft_row; a.t2d = t2d;
   a.tokens = tokens; a.parents = parents; a.n_nodes = n_nodes; a.uniforms = uniforms;
   a.B = B; a.N = N; a.V = V; a.R = R; a.Vd = Vd; a.max_depth = max_depth; a.mode = mode;
   a.eps = eps; a.delta = delta; a.accept_len = accept_len; a.path = path; a.bonus = bonus_token;
   a.node_accept = node_accept; a.err = err; a.CR = L.CR; a.RC = L.RC; a.CS = L.CS; a.C = L.C;
-  char* w = static_cast<char*>(workspace);
   a.rowparts = reinterpret_cast<RowPart*>(w + L.rowparts);
   a.plans = reinterpret_cast<BonusPlan*>(w + L.plans);
   a.bparts = reinterpret_cast<BonusPart*>(w + L.bparts);
@@ -1456,4 +1453,97 @@ extern "C" spec_status spec_verify(const float* target_logits, const float* draf
     else launch_tail<1, kChunkLarge>(a, B, wave_draw, s);
   }
   return launch_status();
+}
+
+// Scratch of spec_verify_static: one fixed array per GPU, held until the process ends.  Host
+// code never passes `scratch` itself (its host-side name is a stand-in, not a device address):
+// static_scratch() looks up each device's address once, with that device current, and the
+// kernels get that address.
+constexpr size_t kStaticScratchBytes = SPEC_VERIFY_STATIC_MAX_BYTES;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// This GPU's address of `scratch`; `dev` must be the current device.
+spec_status static_scratch(int dev, char** out) {
+  if (dev < 0 || dev >= kMaxDevices) return SPEC_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return SPEC_EHIP;
+    }
+    g_scratch[dev] = p;
+  }
+  *out = static_cast<char*>(g_scratch[dev]);
+  return SPEC_OK;
+}
+
+}  // namespace
+}  // namespace spectree
+
+using namespace spectree;
+
+extern "C" size_t spec_verify_workspace(int B, int N, int V) {
+  if (B < 1 || N < 1 || V < 1 || V > kMaxVocab) return 0;
+  return layout(B, N, V).total;
+}
+
+extern "C" spec_status spec_verify(const float* target_logits, const float* draft_probs,
+                                   const int32_t* draft_row, const int32_t* t2d,
+                                   const int32_t* tokens, const int32_t* parents,
+                                   const int32_t* n_nodes, const float* uniforms, int B, int N,
+                                   int V, int R, int Vd, int max_depth, int mode, float eps,
+                                   float delta, int32_t* accept_len, int32_t* path,
+                                   int32_t* bonus_token, uint8_t* node_accept, int32_t* err,
+                                   void* workspace, size_t ws_bytes, void* stream) {
+  const spec_status st = check_verify(target_logits, draft_probs, draft_row, t2d, tokens, parents, uniforms, B, N,
+                                      V, R, Vd, max_depth, mode, eps, delta, accept_len, path, bonus_token, err);
+  if (st != SPEC_OK) return st;
+  const VerifyLayout L = layout(B, N, V);
+  if (!workspace || ws_bytes < L.total) return SPEC_EWORKSPACE;
+  return run_verify(target_logits, draft_probs, draft_row, t2d, tokens, parents, n_nodes, uniforms, B, N, V, R,
+                    Vd, max_depth, mode, eps, delta, accept_len, path, bonus_token, node_accept, err, L,
+                    static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+extern "C" size_t spec_verify_static_bytes(int B, int N, int V) {
+  if (B < 1 || N < 1 || V < 1 || V > kMaxVocab) return 0;
+  return layout(B, N, V, true).total;
+}
+
+extern "C" spec_status spec_verify_static(const float* target_logits, const float* draft_probs,
+                                          const int32_t* draft_row, const int32_t* t2d,
+                                          const int32_t* tokens, const int32_t* parents,
+                                          const int32_t* n_nodes, const float* uniforms, int B, int N,
+                                          int V, int R, int Vd, int max_depth, int mode,
+                                          float eps, float delta, int32_t* accept_len, int32_t* path,
+                                          int32_t* bonus_token, uint8_t* node_accept, int32_t* err,
+                                          void* stream) {
+  const spec_status st = check_verify(target_logits, draft_probs, draft_row, t2d, tokens, parents, uniforms, B, N,
+                                      V, R, Vd, max_depth, mode, eps, delta, accept_len, path, bonus_token, err);
+  if (st != SPEC_OK) return st;
+  const VerifyLayout L = layout(B, N, V, true);
+  if (L.total > kStaticScratchBytes) return SPEC_ESCRATCH;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int cur = -1, sdev = -1;
+  if (hipGetDevice(&cur) != hipSuccess) {
+    (void)hipGetLastError();
+    return SPEC_EHIP;
+  }
+  if (s != nullptr) {
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess) {
+      (void)hipGetLastError();
+      return SPEC_EHIP;
+    }
+    if (sdev != cur) return SPEC_EINVAL;      // the scratch address is the current device's
+  }
+  char* w = nullptr;
+  const spec_status sc = static_scratch(cur, &w);
+  if (sc != SPEC_OK) return sc;
+  return run_verify(target_logits, draft_probs, draft_row, t2d, tokens, parents, n_nodes, uniforms, B, N, V, R,
+                    Vd, max_depth, mode, eps, delta, accept_len, path, bonus_token, node_accept, err, L, w, s);
 }
