@@ -26,7 +26,7 @@ from .attention import tree_attention, tree_attention_row
 from .verify import (verify, MODE_GREEDY, MODE_TYPICAL, MODE_REJECT, MODE_WALK,
                      sample_inverse_cdf, residual_after_rejections)
 from .heads import medusa_heads
-from .assemble import tree_assemble
+from .assemble import tree_assemble, tree_assemble_rows
 from .kv import kv_compact
 from .select import tree_select, path_value
 from .lm_head import lm_head_stats, row_statistics
@@ -37,5 +37,5 @@ __all__ = [
     "tree_build", "pack_mask", "unpack_mask", "tree_attention", "tree_attention_row",
     "verify", "MODE_GREEDY", "MODE_TYPICAL", "MODE_REJECT", "MODE_WALK", "sample_inverse_cdf",
     "residual_after_rejections",
-    "medusa_heads", "tree_assemble", "kv_compact", "tree_select", "path_value", "lm_head_stats", "row_statistics",
+    "medusa_heads", "tree_assemble", "tree_assemble_rows", "kv_compact", "tree_select", "path_value", "lm_head_stats", "row_statistics",
 ]
