@@ -4,6 +4,8 @@
 A step is one pass of every hot-path stage the workload defines, on one batch of synthetic
 input already resident in HBM:
     [Medusa-head workload only: heads -> tree assembly ->] tree build -> tree attention -> verify
+(the 63/127/255-node workloads start from a drafted tree whose tokens are given; their
+EAGLE-style assembly from the draft rows is timed beside the step, under next_rows)
 The default workload is the 63-node Llama-3-8B-shaped one (batch 1, 32 query / 8 key-value
 heads, head_dim 128, prefix 2048, vocabulary 128256, rejection-sampling verify).
 
@@ -83,6 +85,7 @@ def upload(w, a, vi, hi, ti):
                  draft=dev(vi["draft_probs"]), draft_row=dev(vi["draft_row"]))
         if vi["t2d"] is not None:
             s["t2d"] = dev(vi["t2d"])
+            s["d2t"] = dev(vi["d2t"])
     return s
 
 
@@ -133,6 +136,7 @@ class Stepper:
         if w.heads:
             self.ws_heads = sb.workspace(sb.medusa_heads_workspace_bytes(B, w.heads["H"], w.heads["Dm"], w.V,
                                                                          w.heads["k"]), "cuda")
+
         self.scale = d ** -0.5
 
     def step(self, i):
@@ -184,6 +188,7 @@ def algorithmic(w, a, parents, depths, mode):
         branching += int((kids > 1).sum())
     # the bonus pass reads the kept row once more, and a residual draw the draft row beside it
     kept = B * V * 4 * (2 if mode in ("reject", "walk") else 1)
+
     out = {("tree_attn_bf16" if w.dtype == "bf16" else "tree_attn_f32"): (attn_bytes, attn_flops),
            "verify_rows": (internal * V * 4, 0),
            "verify_decide_bonus": (kept, 0)}
@@ -235,6 +240,43 @@ def kv_compact_timing(st, layers_max=32, cap_bytes=8 << 30, reps=50):
     us = ms / cnt * 1e3
     return {"layers": layers, "us": round(us, 3), "algorithmic_bytes": nbytes,
             "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 2) if us > 0 else None}
+
+
+def assemble_rows_timing(st, reps=50):
+    """EAGLE-style tree assembly (a row before the step, measured outside it): the workload's
+    own tree and draft rows, each node's children taking the top candidates of their row; the
+    tokens must equal the ones the step verifies."""
+    import torch
+    from tree_attention_verification_spec_amd import binding as sb
+    w, s0 = st.w, st.sets[0]
+    B, N = w.B, w.N
+    Vd = s0["draft"].shape[2]
+    ws = sb.workspace(sb.tree_assemble_rows_workspace_bytes(B, N, Vd), "cuda")
+    call = lambda out=None: sb.spec_tree_assemble_rows(s0["draft"], s0["parents"], s0["draft_row"], d2t=s0.get("d2t"),
+                                                        V=w.V, n_nodes=s0["n_nodes"], out=out, ws=ws)
+    out = call()
+    torch.cuda.synchronize()
+    assert int(out["err"].abs().sum()) == 0
+    assert torch.equal(out["tokens"][:, 1:], s0["tokens"][:, 1:]), "assembled tokens differ from the step's"
+    try:
+        sb.prof_reset()
+        sb.prof_enable(True)
+        for _ in range(reps):
+            call(out)
+        torch.cuda.synchronize()
+        sb.prof_enable(False)
+        ms1, c1 = sb.prof_read("assemble_chunks")
+        ms2, c2 = sb.prof_read("assemble_merge")
+    finally:
+        sb.prof_enable(False)
+        sb.prof_reset()
+    parents = s0["parents"].cpu()
+    internal = sum(int(torch.unique(parents[b, 1:]).numel()) for b in range(B))
+    nbytes = internal * Vd * 4
+    us1, us2 = ms1 / c1 * 1e3, ms2 / c2 * 1e3
+    return {"shape": f"B{B} x {internal // B}-ish nodes with children x Vd {Vd}", "chunks_us": round(us1, 3),
+            "merge_us": round(us2, 3), "algorithmic_bytes": nbytes,
+            "chunks_GBs": round(nbytes / (us1 * 1e-6) / 1e9, 1)}
 
 
 def tree_select_timing(w, C=1024, reps=50):
@@ -493,7 +535,7 @@ def main():
 
     # per-kernel durations: the same K steps launched eagerly with the library's kernel timing
     # on (each launch carries a start/stop event pair stamped by its own dispatch)
-    names = ("tree_build", "tree_assemble", "tree_attn_bf16", "tree_attn_merge", "tree_attn_f32", "verify_rows_list", "verify_rows",
+    names = ("tree_build", "tree_assemble", "assemble_chunks", "assemble_merge", "tree_attn_bf16", "tree_attn_merge", "tree_attn_f32", "verify_rows_list", "verify_rows",
              "verify_walk_chain", "verify_decide_bonus", "verify_select", "medusa_resblock", "medusa_lm_head",
              "medusa_softmax_topk")
     kernels = {}
@@ -529,12 +571,15 @@ def main():
     log(f"step {ms_step * 1e3:.2f} us; kernels sum {sum(kernels.values()) * 1e3:.2f} us")
     # the rows beside the step; skipped in a counter run, whose copy calibration must be the
     # largest copy of the run (the LM head's weight is built by a 1 GB conversion kernel)
-    kvc = tsel = lmh = None
+    kvc = tsel = lmh = asm = None
     side = not args.copy_calibration_mb
     if w.dtype == "bf16" and side:
         kvc = kv_compact_timing(st)
         log(f"kv_compact (after the step, not in it): {kvc['layers']} layers, {kvc['us']:.2f} us, "
             f"{kvc['algorithmic_bytes']} bytes moved")
+    if side and not w.heads:
+        asm = assemble_rows_timing(st)
+        log(f"assemble_rows (before the step, not in it): {asm}")
     if side:
         tsel = tree_select_timing(w)
         log(f"tree_select (before the step, not in it): {tsel['pool']}, {tsel['us']:.2f} us")
@@ -579,7 +624,7 @@ def main():
         "roofline": roof,
         "kernels_us": {k: round(v * 1e3, 3) for k, v in kernels.items()},
         "cpu_baseline": cpu,
-        "next_rows": {"kv_compact": kvc, "tree_select": tsel, "lm_head_stats": lmh},
+        "next_rows": {"kv_compact": kvc, "tree_select": tsel, "lm_head_stats": lmh, "assemble_rows": asm},
     }
     print(json.dumps(line), flush=True)
 

@@ -132,6 +132,51 @@ spec_status spec_tree_assemble(const int32_t* topk_idx, const int32_t* parents,
                                int32_t* tokens, int32_t* draft_row, int32_t* err, void* stream);
 
 /* --------------------------------------------------------------------------------------
+ * spec_tree_assemble_rows - candidate tokens of a draft tree from per-node draft distributions
+ * (EAGLE style): each node's children take the top candidates of the distribution computed at
+ * that node.
+ *
+ * [MTP] section "EAGLE：token ではなく「特徴量」を先読みする": each drafted step gives a
+ * candidate distribution through the LM head, and the steps are repeated into a draft tree;
+ * [GUIDE] section "Tree Attention：候補を木構造で探索する": several candidates are proposed for
+ * one position.  The children of node p, in node order c_0 < c_1 < ..., share the draft row
+ * r = draft_row[b, c_0]; child c_j takes the j-th entry of row r ranked by probability, highest
+ * first, ties to the lower draft id (-0.0 equals 0.0): tokens[b, c_j] = d2t[id],
+ * cand_prob[b, c_j] = draft_probs[b, r, id].
+ *
+ *   draft_probs float [B, R, Vd]  draft distributions (e.g. one per expanded node)
+ *   parents     int32 [B, N]      the tree (rules as in spec_tree_build)
+ *   draft_row   int32 [B, N]      row of draft_probs holding node c's distribution's source
+ *                                 (the row computed at c's parent; root entry ignored)
+ *   d2t         int32 [Vd]        optional (NULL: identity, requires V == Vd): draft id ->
+ *                                 target id
+ *   n_nodes     int32 [B]         optional (NULL = N); root_tokens int32 [B] optional (NULL: -1)
+ *   V                             target vocabulary: every mapped token must lie in [0, V)
+ * Outputs:
+ *   tokens     int32 [B, N]  candidate token of each node (root: root_tokens[b] or -1)
+ *   cand_prob  float [B, N]  draft probability of each node's token (root: 1); it feeds
+ *                            spec_tree_select as cand_prob
+ *   err        int32 [B]     error word: SPEC_ERR_NNODES, SPEC_ERR_ROOT, SPEC_ERR_PARENT,
+ *                            SPEC_ERR_DRAFTROW (row outside [0, R), or a sibling's row differs
+ *                            from the first sibling's), SPEC_ERR_RANK (a child ranked past Vd),
+ *                            SPEC_ERR_NONFINITE (a NaN in a ranked row, at the first child),
+ *                            SPEC_ERR_MAP (d2t gives a token outside [0, V))
+ * A sequence with an error, and padding nodes, get token -1 and cand_prob NaN.
+ * Workspace: spec_tree_assemble_rows_workspace(B, N, Vd) bytes (per chunk of 8192 draft ids,
+ * the chunk's ranked candidates of every node and a NaN flag).
+ * Supported: N <= 256, Vd <= 262144.
+ * Errors: SPEC_EINVAL (sizes, NULL required pointers, d2t NULL with V != Vd), SPEC_EUNSUPPORTED
+ * (Vd), SPEC_EWORKSPACE.
+ * ------------------------------------------------------------------------------------ */
+size_t spec_tree_assemble_rows_workspace(int B, int N, int Vd);
+spec_status spec_tree_assemble_rows(const float* draft_probs, const int32_t* parents,
+                                    const int32_t* draft_row, const int32_t* d2t,
+                                    const int32_t* n_nodes, const int32_t* root_tokens, int B,
+                                    int N, int R, int Vd, int V, int32_t* tokens,
+                                    float* cand_prob, int32_t* err, void* workspace,
+                                    size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------------------------------
  * spec_tree_attn - tree attention: every node's query attends to the shared committed prefix
  * and to its own ancestors (and itself) under the ancestor mask.
  *

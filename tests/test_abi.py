@@ -235,12 +235,29 @@ def test_verify_static_host_checks(lib):
     assert call(B=8, N=256, V=1_000_000) == 5
 
 
+def test_tree_assemble_rows_argument_checks(lib):
+    fake = ctypes.c_void_p(0x1000)     # never dereferenced: every call below returns before a launch
+    ws = lib.spec_tree_assemble_rows_workspace(4, 255, 32000)
+    assert ws >= 4 * 4 * 255 * 12                        # per chunk and slot: a key and a NaN flag
+    assert lib.spec_tree_assemble_rows_workspace(1, 10, 262145) == 0
+
+    def call(d=fake, par=fake, row=fake, d2t=None, B=4, N=255, R=60, Vd=32000, V=32000, tok=fake, wsz=ws):
+        return lib.spec_tree_assemble_rows(d, par, row, d2t, None, None, B, N, R, Vd, V, tok, fake, fake, fake,
+                                           wsz, None)
+
+    assert call(d=None) == 1 and call(par=None) == 1 and call(row=None) == 1 and call(tok=None) == 1
+    assert call(B=0) == 1 and call(N=257) == 1 and call(R=0) == 1 and call(Vd=0) == 1
+    assert call(V=128256) == 1                           # a larger target vocabulary needs d2t
+    assert call(Vd=262145, V=262145) == 2
+    assert call(wsz=ws - 1) == 3
+
+
 # Checks that need no torch: run again against the host-sanitised build below.
 HOST_CHECKS = ["test_every_declared_symbol_is_exported", "test_status_strings", "test_host_argument_checks",
                "test_kv_compact_host_checks", "test_workspace_sizes_are_monotone", "test_tree_select_argument_checks",
                "test_lm_head_stats_argument_checks", "test_verify_greedy_stats_argument_checks",
                "test_verify_lm_head_argument_checks", "test_status_strings_cover_every_code",
-               "test_verify_static_host_checks"]
+               "test_verify_static_host_checks", "test_tree_assemble_rows_argument_checks"]
 
 
 def _host_check_script(path):
@@ -256,7 +273,7 @@ def _host_check_script(path):
         "    for N in (1, 63, 255, 256, 257, 2**31 - 1):\n"
         "        for V in (1, 4096, 128256, 2**31 - 1):\n"
         "            L.spec_verify_workspace(B, N, V); L.spec_verify_static_bytes(B, N, V)\n"
-        "            L.spec_tree_attn_workspace(B, N, 32, 8, 128, V, 1)\n"
+        "            L.spec_tree_attn_workspace(B, N, 32, 8, 128, V, 1); L.spec_tree_assemble_rows_workspace(B, N, V)\n"
         "            L.spec_lm_head_stats_workspace(B, N, 4096, V)\n"
         "            L.spec_medusa_heads_workspace(B, 4, 4096, V, 8)\n"
         "            for m in range(4): L.spec_verify_lm_head_workspace(B, N, 4096, V, m)\n"

@@ -1,0 +1,175 @@
+"""GPU parity: spec_tree_assemble_rows (EAGLE-style assembly: each node's children take the top
+candidates of their draft row) against oracle.tree_assemble_rows.  Both sides rank the same
+float32 values, so tokens, draft probabilities and error words are compared bit for bit (no
+margin): the workloads' own trees and draft rows at full size, and small cases that reach every
+path of the kernels - ties and -0.0, chunk boundaries, a node with 200 children (the sorted
+candidate path), rows of one repeated value, an odd vocabulary (scalar loads), ragged and empty
+sequences, NaNs, and every error rule."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tree_attention_verification_spec_amd import binding as sb
+from tree_attention_verification_spec_amd import workloads as wl
+
+from gpu_util import dev, host, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(draft, parents, draft_row, d2t=None, V=None, n_nodes=None, root_tokens=None, what=""):
+    need_gpu()
+    B, R, Vd = draft.shape
+    print(f"assemble_rows {what}: B={B} N={parents.shape[1]} R={R} Vd={Vd}", flush=True)
+    got = sb.spec_tree_assemble_rows(dev(draft), dev(parents.astype(np.int32)), dev(draft_row.astype(np.int32)),
+                                     d2t=None if d2t is None else dev(d2t.astype(np.int32)), V=V,
+                                     n_nodes=None if n_nodes is None else dev(n_nodes.astype(np.int32)),
+                                     root_tokens=None if root_tokens is None else dev(root_tokens.astype(np.int32)))
+    torch.cuda.synchronize()
+    got = {k: host(v) for k, v in got.items()}
+    ref = oracle.tree_assemble_rows(draft, parents, draft_row, d2t=d2t, V=V, n_nodes=n_nodes, root_tokens=root_tokens)
+    assert np.array_equal(got["err"], ref["err"]), f"{what}: err {got['err']} vs {ref['err']}"
+    assert np.array_equal(got["tokens"], ref["tokens"]), f"{what}: tokens differ"
+    assert np.array_equal(np.isnan(got["cand_prob"]), np.isnan(ref["cand_prob"])), f"{what}: cand_prob NaN pattern"
+    ok = ~np.isnan(ref["cand_prob"])
+    assert np.array_equal(got["cand_prob"][ok], ref["cand_prob"][ok]), f"{what}: cand_prob differs"
+    return got, ref
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_workloads(cfg):
+    """The 63-, 127- and 255-node workloads (per-parent draft rows; the 255-node one over a
+    32000-token draft vocabulary mapped by d2t) at full size."""
+    w = wl.config(cfg)
+    parents, n_nodes = wl.trees(w)
+    vi = wl.verify_inputs(w, parents)
+    got, ref = _run(vi["draft_probs"], parents, vi["draft_row"], d2t=vi["d2t"], V=w.V, n_nodes=n_nodes,
+                    what=f"cfg{cfg}")
+    assert (ref["err"] == 0).all()
+    assert np.array_equal(got["tokens"][:, 1:], vi["tokens"][:, 1:])
+
+
+def _tree(g, B, N, depth):
+    return np.stack([wl.random_tree(np.random.default_rng([int(g.integers(1 << 30)), b]), N, depth)
+                     for b in range(B)]).astype(np.int32)
+
+
+def _per_parent(parents):
+    row = np.full(parents.shape, -1, np.int32)
+    row[:, 1:] = parents[:, 1:]
+    return row
+
+
+CASES = [
+    # (B, N, Vd, depth, levels, d2t, note)
+    (3, 40, 5000, 5, None, False, "plain"),
+    (2, 63, 8192, 4, 3, False, "one chunk, heavy ties"),
+    (2, 63, 8193, 4, None, True, "a one-entry second chunk, mapped"),
+    (4, 30, 777, 3, 2, True, "odd vocabulary: scalar loads"),
+    (1, 127, 40000, 6, 5, True, "five chunks, ties"),
+    (2, 256, 20000, 8, None, False, "256 nodes"),
+    (1, 100, 262144, 4, None, False, "the largest draft vocabulary"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_small(case):
+    B, N, Vd, depth, levels, mapped, note = CASES[case]
+    g = np.random.default_rng(700 + case)
+    parents = _tree(g, B, N, depth)
+    D = g.random((B, N, Vd))
+    if levels:
+        D = np.floor(D * levels) / levels
+    D = (D / D.sum(axis=2, keepdims=True)).astype(np.float32)
+    D[:, ::3, ::7] = -0.0                                  # equal to 0.0
+    d2t = V = None
+    if mapped:
+        V = 3 * Vd
+        d2t = g.permutation(V)[:Vd].astype(np.int32)
+    n_nodes = np.array([N - 3 * b for b in range(B)], np.int32)
+    _run(D, parents, _per_parent(parents), d2t=d2t, V=V, n_nodes=n_nodes,
+         root_tokens=np.arange(B, dtype=np.int32) + 11, what=note)
+
+
+def test_wide_node_and_constant_rows():
+    """A root with 200 children (the candidates are sorted rather than counted) and rows that
+    hold one repeated value (every entry of a chunk is a candidate; the ranks are the ids)."""
+    g = np.random.default_rng(720)
+    N = 230
+    parents = np.zeros((3, N), np.int32)
+    parents[:, 0] = -1
+    parents[:, 201:] = g.integers(1, 201, size=(3, N - 201))
+    D = g.random((3, N, 30000)).astype(np.float32)
+    D[1] = np.float32(1.0 / 30000)                          # constant rows
+    D[2, :, :] = np.float32(0.5)
+    D[2, :, 100:20000] = np.float32(0.25)                   # two levels across chunks
+    got, ref = _run(D, parents, _per_parent(parents), what="wide")
+    assert (ref["err"] == 0).all()
+    assert ref["tokens"][1, 1:201].tolist() == list(range(200))
+
+
+def test_per_depth_rows_and_small_vocabulary():
+    """Rows shared by all nodes of one depth (the Medusa layout) and a draft vocabulary smaller
+    than a node's child count (SPEC_ERR_RANK at the first child past it)."""
+    topo = wl.bfs_tree((6, 3, 2), 60)
+    depth = np.zeros(60, np.int64)
+    for c in range(1, 60):
+        depth[c] = depth[topo[c]] + 1
+    row = np.where(np.arange(60) == 0, -1, depth - 1).astype(np.int32)
+    g = np.random.default_rng(730)
+    D = g.random((2, 3, 1000)).astype(np.float32)
+    _run(D, np.tile(topo, (2, 1)), np.tile(row, (2, 1)), what="per depth")
+    D5 = g.random((1, 3, 5)).astype(np.float32)
+    got, ref = _run(D5, topo[None], row[None], what="rank past the vocabulary")
+    assert oracle.decode_err(ref["err"][0]) == (6, oracle.ERR_RANK)
+
+
+def test_errors():
+    g = np.random.default_rng(740)
+    B, N, Vd = 8, 20, 3000
+    parents = _tree(g, B, N, 4)
+    row = _per_parent(parents)
+    D = g.random((B, N, Vd)).astype(np.float32)
+    d2t = g.permutation(9000)[:Vd].astype(np.int32)
+    n_nodes = np.full(B, N, np.int32)
+    n_nodes[1] = 21                                          # node count beyond N
+    parents[2, 0] = 0                                        # root with a parent
+    parents[3, 7] = 9                                        # parent not earlier
+    p4 = next(p for p in range(N) if sum(parents[4, 1:] == p) >= 2)
+    kids = [c for c in range(1, N) if parents[4, c] == p4]
+    row[4, kids[-1]] = (row[4, kids[0]] + 1) % N             # a sibling on another row
+    row[5, 4] = N + 3                                        # row out of range
+    top = int(np.argmax(D[6, 0]))
+    d2t[top] = 9000                                          # a selected id maps out of range
+    D[7, parents[7, 5], 17] = np.nan                         # a NaN in a ranked row
+    got, ref = _run(D, parents, row, d2t=d2t, V=9000, n_nodes=n_nodes, what="errors")
+    codes = [oracle.decode_err(e)[1] for e in ref["err"]]
+    assert codes == [0, oracle.ERR_NNODES, oracle.ERR_ROOT, oracle.ERR_PARENT, oracle.ERR_DRAFTROW,
+                     oracle.ERR_DRAFTROW, oracle.ERR_MAP, oracle.ERR_NONFINITE]
+    # empty sequences
+    _run(D[:2], parents[:2], row[:2], d2t=d2t, V=9000, n_nodes=np.array([0, 1], np.int32), what="empty")
+
+
+def test_assembled_tokens_feed_selection_and_verification():
+    """The 255-node workload end to end on the device: assembly -> tree build -> REJECT verify,
+    and the assembly's cand_prob as the pool of a dynamic tree selection, against the oracle."""
+    w = wl.config(4)
+    parents, n_nodes = wl.trees(w)
+    vi = wl.verify_inputs(w, parents)
+    need_gpu()
+    par = dev(parents)
+    asm = sb.spec_tree_assemble_rows(dev(vi["draft_probs"]), par, dev(vi["draft_row"]), d2t=dev(vi["d2t"]), V=w.V)
+    ver = sb.spec_verify(dev(vi["target_logits"]), asm["tokens"], par, dev(vi["uniforms"]), "reject",
+                         draft_probs=dev(vi["draft_probs"]), draft_row=dev(vi["draft_row"]), t2d=dev(vi["t2d"]))
+    sel = sb.spec_tree_select(par, asm["cand_prob"], 127, cand_tokens=asm["tokens"], cand_row=dev(vi["draft_row"]))
+    torch.cuda.synchronize()
+    ra = oracle.tree_assemble_rows(vi["draft_probs"], parents, vi["draft_row"], d2t=vi["d2t"], V=w.V)
+    rv = oracle.verify(vi["target_logits"], ra["tokens"], parents, vi["uniforms"], oracle.MODE_REJECT,
+                       draft_probs=vi["draft_probs"], draft_row=vi["draft_row"], t2d=vi["t2d"])
+    from gpu_util import compare_verify
+    compare_verify({k: host(v) for k, v in ver.items()}, rv, n_nodes)
+    rs = oracle.tree_select(parents, ra["cand_prob"], 127, cand_tokens=ra["tokens"], cand_row=vi["draft_row"])
+    for key in ("sel", "parents", "tokens", "draft_row", "n_nodes", "err"):
+        assert np.array_equal(host(sel[key]), rs[key]), f"selection {key} differs"

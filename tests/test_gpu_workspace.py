@@ -153,3 +153,16 @@ def test_lm_head(mode):
         g_outs = sb.spec_verify_greedy_stats(st["row_argmax"], tok, par, 3000, n_nodes=nn)
         _twice(lambda ws, o: sb.spec_verify_greedy_stats(st["row_argmax"], tok, par, 3000, n_nodes=nn, out=o), 1,
                g_outs, "verify_greedy_stats")
+
+
+@pytest.mark.parametrize("Vd,mapped", [(20000, True), (777, False)])
+def test_assemble_rows(Vd, mapped):
+    w = wl.custom(seed=660, B=4, N=50, V=3 * Vd if mapped else Vd, Vd=Vd if mapped else None, tree=("random", 5),
+                  n_nodes_range=(0, 50))
+    parents, n_nodes = wl.trees(w)
+    vi = wl.verify_inputs(w, parents)
+    draft, par, row, nn = dev(vi["draft_probs"]), dev(parents), dev(vi["draft_row"]), dev(n_nodes)
+    d2t = dev(vi["d2t"]) if vi["d2t"] is not None else None
+    outs = sb.spec_tree_assemble_rows(draft, par, row, d2t=d2t, V=w.V, n_nodes=nn)
+    _twice(lambda ws, o: sb.spec_tree_assemble_rows(draft, par, row, d2t=d2t, V=w.V, n_nodes=nn, out=o, ws=ws),
+           sb.tree_assemble_rows_workspace_bytes(4, 50, Vd), outs, f"tree_assemble_rows Vd={Vd}")

@@ -18,6 +18,10 @@ def declare(L):
     L.spec_tree_build.argtypes = [_P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P]
     L.spec_tree_assemble.restype = _I
     L.spec_tree_assemble.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P]
+    L.spec_tree_assemble_rows_workspace.restype = _Z
+    L.spec_tree_assemble_rows_workspace.argtypes = [_I, _I, _I]
+    L.spec_tree_assemble_rows.restype = _I
+    L.spec_tree_assemble_rows.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _Z, _P]
     L.spec_tree_select.restype = _I
     L.spec_tree_select.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]
     L.spec_lm_head_stats_workspace.restype = _Z

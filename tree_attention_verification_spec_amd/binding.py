@@ -112,6 +112,34 @@ def spec_tree_assemble(topk_idx, parents, root_tokens=None, out=None, stream=Non
     return out
 
 
+def tree_assemble_rows_workspace_bytes(B, N, Vd):
+    return int(lib().spec_tree_assemble_rows_workspace(B, N, Vd))
+
+
+def spec_tree_assemble_rows(draft_probs, parents, draft_row, d2t=None, V=None, n_nodes=None, root_tokens=None,
+                            out=None, ws=None, stream=None):
+    """EAGLE-style assembly: each node's children take the top candidates of their draft row."""
+    B, R, Vd = draft_probs.shape
+    N = parents.shape[1]
+    dev = draft_probs.device
+    if V is None:
+        V = Vd
+    if out is None:
+        out = {"tokens": torch.empty((B, N), dtype=torch.int32, device=dev),
+               "cand_prob": torch.empty((B, N), dtype=torch.float32, device=dev),
+               "err": torch.empty((B,), dtype=torch.int32, device=dev)}
+    if ws is None:
+        ws = workspace(tree_assemble_rows_workspace_bytes(B, N, Vd), dev)
+    _check(lib().spec_tree_assemble_rows(
+        _ptr(draft_probs, torch.float32, (B, R, Vd), "draft_probs"), _ptr(parents, torch.int32, (B, N), "parents"),
+        _ptr(draft_row, torch.int32, (B, N), "draft_row"), _ptr(d2t, torch.int32, (Vd,), "d2t"),
+        _ptr(n_nodes, torch.int32, (B,), "n_nodes"), _ptr(root_tokens, torch.int32, (B,), "root_tokens"),
+        B, N, R, Vd, int(V), _ptr(out["tokens"], torch.int32, (B, N), "tokens"),
+        _ptr(out["cand_prob"], torch.float32, (B, N), "cand_prob"), _ptr(out["err"], torch.int32, (B,), "err"),
+        _ptr(ws, None, None, "workspace"), ws.numel(), _stream(stream)), "spec_tree_assemble_rows")
+    return out
+
+
 def spec_tree_select(cand_parents, cand_prob, N, n_cand=None, cand_tokens=None, cand_row=None, out=None,
                      stream=None):
     B, C = cand_parents.shape
