@@ -44,6 +44,9 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, help="workload 1-5 (default 2: 63-node tree)")
+    ap.add_argument("--also", type=int, nargs="*", default=None,
+                    help="further workloads timed into the same line (default: the 127-node batch-16 one "
+                         "beside the 63-node default)")
     ap.add_argument("--mode", default=None, help="verify mode (default: the workload's last listed)")
     ap.add_argument("--rotate-gb", type=float, default=1.2, help="total size of rotating input copies")
     ap.add_argument("--cpu-seconds", type=float, default=24.0, help="budget of the CPU-oracle sample")
@@ -51,7 +54,10 @@ def parse_args():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of from HIP graphs")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run a plain device copy of this size (for scaling --pmc byte counters)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.also is None:
+        args.also = [3] if args.config == 2 and not args.copy_calibration_mb else []
+    return args
 
 
 # --------------------------------------------------------------------------- inputs
@@ -410,7 +416,7 @@ def roofline_entry(name, nbytes, flops, avg_ms, traffic):
 
 # --------------------------------------------------------------------------- CPU oracle
 
-def cpu_baseline(w, a, vi, hi, ti, mode, budget_s):
+def cpu_baseline(w, a, vi, hi, ti, mode, budget_s, threads):
     import numpy as np
     from threadpoolctl import threadpool_limits
     import oracle
@@ -435,7 +441,7 @@ def cpu_baseline(w, a, vi, hi, ti, mode, budget_s):
         oracle.verify(logits, tokens, par, unif, modes[mode], draft_probs=draft, draft_row=drow, t2d=t2d,
                       n_nodes=nn, max_depth=ns - 1)
 
-    with threadpool_limits(1):
+    with threadpool_limits(threads):
         # size the sample from two probe rounds (1 and 2 nodes): fixed cost + cost per node
         t0 = time.perf_counter()
         one_round(1)
@@ -453,37 +459,29 @@ def cpu_baseline(w, a, vi, hi, ti, mode, budget_s):
             if el >= budget_s / 2.0 or rounds >= 50:
                 break
     value = rounds * ns / el
-    return {"value": round(value, 3), "unit": "tree-nodes/s", "cores": 1, "kind": "oracle",
+    return {"value": round(value, 3), "unit": "tree-nodes/s", "cores": threads, "kind": "oracle",
             "sample": (f"sequence 0 of '{w.name}': first {ns} of {w.N} tree nodes, full prefix "
                        f"{int(a['prefix_len'][0])}; {rounds} oracle round(s) of "
                        f"{'heads + assembly + ' if w.heads else ''}tree build + attention over all "
-                       f"{ns}x{w.Hq} query rows + {mode} verify; NumPy float64, 1 BLAS thread; "
+                       f"{ns}x{w.Hq} query rows + {mode} verify; NumPy float64, {threads} BLAS thread(s); "
                        f"{el:.1f} s"),
             "host_cpus": os.cpu_count()}
 
 
 # --------------------------------------------------------------------------- main
 
-def main():
-    args = parse_args()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only (the tree-verification step of one GPU's "
-              "share); multi-GPU runs are not part of it.", file=sys.stderr)
-        sys.exit(2)
+def measure(args, cfg, K, warmup, side, log_prefix=""):
+    """Time K steps of workload `cfg` (graph replays over rotating input copies), then the
+    per-kernel durations, the rows beside the step (when `side`), and the roofline entry."""
     import numpy as np
     import torch
     from tree_attention_verification_spec_amd import binding as sb
     from tree_attention_verification_spec_amd import profiling
     from tree_attention_verification_spec_amd import workloads as wl
 
-    if not torch.cuda.is_available():
-        print("bench.py: no GPU visible", file=sys.stderr)
-        sys.exit(1)
-    sb.lib()
-    w = wl.config(args.config)
-    mode = args.mode or w.modes[-1]
-    log(f"workload: {w.name}; verify mode {mode}")
+    w = wl.config(cfg)
+    mode = (args.mode if cfg == args.config else None) or w.modes[-1]
+    log(f"{log_prefix}workload: {w.name}; verify mode {mode}")
     t0 = time.time()
     a, vi, hi, ti = host_inputs(w)
     base = upload(w, a, vi, hi, ti)
@@ -494,13 +492,12 @@ def main():
     st = Stepper(w, mode, sets)
 
     # eager warm-up and a reference result for the graph check
-    for i in range(args.warmup):
+    for i in range(warmup):
         st.step(i % nsets)
     torch.cuda.synchronize()
     ref = {k: v.clone() for k, v in st.outs[0]["ver"].items()}
     ref_attn = st.outs[0]["attn_out"].clone()
 
-    K = args.steps
     use_graph = not args.no_graph
     if use_graph:
         cyc = capture(st, range(nsets))
@@ -535,9 +532,9 @@ def main():
 
     # per-kernel durations: the same K steps launched eagerly with the library's kernel timing
     # on (each launch carries a start/stop event pair stamped by its own dispatch)
-    names = ("tree_build", "tree_assemble", "assemble_chunks", "assemble_merge", "tree_attn_bf16", "tree_attn_merge", "tree_attn_f32", "verify_rows_list", "verify_rows",
-             "verify_walk_chain", "verify_decide_bonus", "verify_select", "medusa_resblock", "medusa_lm_head",
-             "medusa_softmax_topk")
+    names = ("tree_build", "tree_assemble", "tree_attn_bf16", "tree_attn_merge", "tree_attn_f32", "verify_rows_list",
+             "verify_rows", "verify_walk_chain", "verify_decide_bonus", "verify_select", "medusa_resblock",
+             "medusa_lm_head", "medusa_softmax_topk")
     kernels = {}
     try:
         sb.prof_reset()
@@ -559,7 +556,7 @@ def main():
     work = algorithmic(w, a, a["parents"], depths, mode)
     dom = max((k for k in kernels if k in work), key=lambda k: kernels[k])
     nbytes, flops = work[dom]
-    short = {1: "tiny", 2: "tree63", 3: "tree127_b16", 4: "tree255_b4", 5: "medusa_tree127_b8"}[args.config]
+    short = {1: "tiny", 2: "tree63", 3: "tree127_b16", 4: "tree255_b4", 5: "medusa_tree127_b8"}[cfg]
     tr = profiling.read_traffic(os.path.join(ROOT, "profiles", f"traffic_{dom}_{short}.md"))
     roof = roofline_entry(dom, nbytes, flops, kernels[dom], None if tr is None else int(tr[0]))
     for k in sorted(kernels, key=lambda k: -kernels[k]):
@@ -569,10 +566,16 @@ def main():
             extra = f"  {b_ / (kernels[k] * 1e-3) / 1e9:8.1f} GB/s  {f_ / (kernels[k] * 1e-3) / 1e12:8.1f} TFLOP/s"
         log(f"  {k:22s} {kernels[k] * 1e3:9.2f} us{extra}")
     log(f"step {ms_step * 1e3:.2f} us; kernels sum {sum(kernels.values()) * 1e3:.2f} us")
+    # the whole step against the HBM roofline: every kernel's algorithmic bytes in one step
+    step_bytes = sum(b_ for b_, _ in work.values())
+    step_flops = sum(f_ for _, f_ in work.values())
+    step_roof = {"algorithmic_bytes": step_bytes, "algorithmic_flops": step_flops,
+                 "hbm_frac": round(step_bytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                 "bound_us": round(max(step_bytes / (HBM_PEAK_GBS * 1e9), step_flops / (BF16_PEAK_TFLOPS * 1e12)) * 1e6, 3)}
+    log(f"step: {step_bytes / 1e6:.1f} MB algorithmic, {step_roof['hbm_frac'] * 100:.1f} % of the HBM roofline")
     # the rows beside the step; skipped in a counter run, whose copy calibration must be the
     # largest copy of the run (the LM head's weight is built by a 1 GB conversion kernel)
     kvc = tsel = lmh = asm = None
-    side = not args.copy_calibration_mb
     if w.dtype == "bf16" and side:
         kvc = kv_compact_timing(st)
         log(f"kv_compact (after the step, not in it): {kvc['layers']} layers, {kvc['us']:.2f} us, "
@@ -589,6 +592,47 @@ def main():
             f"{lmh['us']:.2f} us + merge {lmh['merge_us']:.2f} us, {lmh['achieved_GBs']:.0f} GB/s; greedy verify "
             f"from the statistics {lmh['greedy_verify_us']:.2f} us, typical with its bonus draw "
             f"{lmh['typical_verify_us']:.2f} us; REJECT {lmh['reject_verify_us']}; WALK {lmh['walk_verify_us']}")
+    res = {"w": w, "mode": mode, "a": a, "vi": vi, "hi": hi, "ti": ti, "ms_step": ms_step, "kernels": kernels,
+           "roofline": roof, "step_roofline": step_roof, "nsets": nsets, "use_graph": use_graph,
+           "next_rows": {"kv_compact": kvc, "tree_select": tsel, "lm_head_stats": lmh, "assemble_rows": asm}}
+    del st, sets, base
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (the tree-verification step of one GPU's "
+              "share); multi-GPU runs are not part of it.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from tree_attention_verification_spec_amd import binding as sb
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    sb.lib()
+    side = not args.copy_calibration_mb
+    r = measure(args, args.config, args.steps, args.warmup, side)
+    w, mode, ms_step = r["w"], r["mode"], r["ms_step"]
+
+    # the other configuration the headline metric names (127 nodes at batch 16 beside the
+    # 63-node batch-1 one), timed the same way, as an extra key of the same line
+    also = {}
+    for cfg in args.also:
+        if cfg == args.config:
+            continue
+        ra = measure(args, cfg, max(20, args.steps // 4), min(args.warmup, 10), False, log_prefix="also: ")
+        wa = ra["w"]
+        also[wa.name] = {"value": round(wa.B * wa.N / (ra["ms_step"] * 1e-3), 1), "unit": "tree-nodes/s",
+                         "ms_per_step": round(ra["ms_step"], 6), "rounds_per_s": round(1.0 / (ra["ms_step"] * 1e-3), 1),
+                         "steps": max(20, args.steps // 4), "verify_mode": ra["mode"], "roofline": ra["roofline"],
+                         "step_roofline": ra["step_roofline"],
+                         "kernels_us": {k: round(v * 1e3, 3) for k, v in ra["kernels"].items()}}
+        del ra
 
     if args.copy_calibration_mb:
         nb = args.copy_calibration_mb * (1 << 20)
@@ -601,7 +645,10 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, a, vi, hi, ti, mode, args.cpu_seconds)
+        threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+        cpu = cpu_baseline(w, r["a"], r["vi"], r["hi"], r["ti"], mode, args.cpu_seconds / 2, threads)
+        cpu["single_thread"] = cpu_baseline(w, r["a"], r["vi"], r["hi"], r["ti"], mode, args.cpu_seconds / 2, 1)
+        log(f"cpu oracle: {cpu['value']} nodes/s on {threads} threads, {cpu['single_thread']['value']} on 1")
 
     nodes = w.B * w.N
     line = {
@@ -609,7 +656,7 @@ def main():
         "value": round(nodes / (ms_step * 1e-3), 1),
         "unit": "tree-nodes/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 6),
         "higher_is_better": True,
@@ -619,12 +666,14 @@ def main():
         "data": "synthetic (seeded; shapes of the pages' Llama-3-8B-class GQA, tree sizes, vocabularies)",
         "config": {"workload": w.name, "batch": w.B, "tree_nodes": w.N, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": w.d, "prefix": list(w.prefix), "vocab": w.V, "verify_mode": mode,
-                   "medusa_heads": w.heads, "rotating_copies": nsets, "hip_graphs": use_graph},
+                   "medusa_heads": w.heads, "rotating_copies": r["nsets"], "hip_graphs": r["use_graph"]},
         "rounds_per_s": round(1.0 / (ms_step * 1e-3), 1),
-        "roofline": roof,
-        "kernels_us": {k: round(v * 1e3, 3) for k, v in kernels.items()},
+        "roofline": r["roofline"],
+        "step_roofline": r["step_roofline"],
+        "kernels_us": {k: round(v * 1e3, 3) for k, v in r["kernels"].items()},
+        "also": also,
         "cpu_baseline": cpu,
-        "next_rows": {"kv_compact": kvc, "tree_select": tsel, "lm_head_stats": lmh, "assemble_rows": asm},
+        "next_rows": r["next_rows"],
     }
     print(json.dumps(line), flush=True)
 
