@@ -1,14 +1,23 @@
 """rocprofv3 output -> short text summaries, and the HBM traffic figures those summaries record.
 
     python -m tree_attention_verification_spec_amd.profiling stats <kernel_stats.csv> <out.md> "<command>"
-    python -m tree_attention_verification_spec_amd.profiling traffic <fetch.csv> <write.csv> <kernel> \
-        <copy_bytes> <out.md> "<commands>"
+    python -m tree_attention_verification_spec_amd.profiling ea <reads.csv> <writes.csv> <kernel> \
+        <copy_bytes> <algorithmic_bytes> <out.md> "<commands>"
+    python -m tree_attention_verification_spec_amd.profiling mfma <mfma.csv> <kernel> \
+        <algorithmic_flops> <out.md> "<command>"
 
-``traffic`` reads two ``rocprofv3 --pmc`` runs (FETCH_SIZE, then WRITE_SIZE; both KiB per
-dispatch), scales each by what the same counter read for a plain device copy of known size
-(the copy kernel's dispatches are those whose name contains "copy" or "elementwise"), and
-records the per-launch HBM bytes of ``kernel`` together with a hash of the kernel sources,
-so a later benchmark can tell whether the figure still describes the current kernels.
+``ea`` reads two ``rocprofv3 --pmc`` runs: the L2-to-memory read requests by size
+(TCC_EA0_RDREQ_32B_sum, _64B_sum, _128B_sum) and the write requests (TCC_EA0_WRREQ_sum,
+TCC_EA0_WRREQ_64B_sum; the rest are 32 bytes).  Bytes = 32 n32 + 64 n64 + 128 n128 read and
+32 (n - n64) + 64 n64 written, per dispatch.  (FETCH_SIZE's expression takes 128-byte reads from
+TCC_BUBBLE, which on this GPU does not count them, so it reads low.)  The same counters on a
+plain device copy of known size are reported beside the figure as a check (no scaling is
+applied).  The per-launch bytes of ``kernel`` are recorded with a hash of the kernel sources, so
+a later benchmark can tell whether the figure still describes the current kernels.
+
+``mfma`` reads SQ_VALU_MFMA_BUSY_CYCLES (summed over every SIMD) and
+SQ_INSTS_VALU_MFMA_MOPS_BF16 (x 512 = bf16 FLOPs) per dispatch, and the dispatch's duration:
+busy fraction = busy cycles / SIMDs / (duration x clock).
 """
 
 import csv
@@ -106,24 +115,63 @@ def _is_copy(name):
     return "copy" in n or "elementwise" in n
 
 
-def write_traffic_summary(fetch_csv, write_csv, kernel, copy_bytes, out_md, commands):
-    fetch = read_counter(fetch_csv, "FETCH_SIZE")
-    wr = read_counter(write_csv, "WRITE_SIZE")
-    kname = next(k for k in fetch if k.startswith(kernel))
-    copy_f = max((v for k, vs in fetch.items() if _is_copy(k) for v in vs), default=None)
-    copy_w = max((v for k, vs in wr.items() if _is_copy(k) for v in vs), default=None)
-    f_kib = sum(fetch[kname]) / len(fetch[kname])
-    w_kib = sum(wr[kname]) / len(wr[kname])
-    f_scale = copy_bytes / (copy_f * 1024.0) if copy_f else 1.0
-    w_scale = copy_bytes / (copy_w * 1024.0) if copy_w else 1.0
-    fetch_b = f_kib * 1024.0 * f_scale
-    write_b = w_kib * 1024.0 * w_scale
-    lines = ["# HBM traffic per launch (rocprofv3 --pmc)", "",
-             f"kernel: {kname}", f"source_hash: {source_hash()}",
-             f"fetch_kib_per_dispatch: {f_kib:.1f}", f"write_kib_per_dispatch: {w_kib:.1f}",
-             f"copy_bytes: {copy_bytes}", f"copy_fetch_kib: {copy_f}", f"copy_write_kib: {copy_w}",
-             f"fetch_scale: {f_scale:.4f}", f"write_scale: {w_scale:.4f}",
-             f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}", "", "Commands:", "", "```", commands, "```"]
+def read_counters(path):
+    """{dispatch id: (kernel short name, {counter: value}, duration ns)} of a --pmc run."""
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = out.setdefault(r["Dispatch_Id"], [short_name(r["Kernel_Name"]), defaultdict(float), 0])
+            d[1][r["Counter_Name"]] += float(r["Counter_Value"])
+            d[2] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    return out
+
+
+def _ea_reads(c):
+    return 32 * c["TCC_EA0_RDREQ_32B_sum"] + 64 * c["TCC_EA0_RDREQ_64B_sum"] + 128 * c["TCC_EA0_RDREQ_128B_sum"]
+
+
+def _ea_writes(c):
+    return 32 * (c["TCC_EA0_WRREQ_sum"] - c["TCC_EA0_WRREQ_64B_sum"]) + 64 * c["TCC_EA0_WRREQ_64B_sum"]
+
+
+def write_ea_summary(reads_csv, writes_csv, kernel, copy_bytes, alg_bytes, out_md, commands):
+    rd, wr = read_counters(reads_csv), read_counters(writes_csv)
+    rk = [_ea_reads(c) for n, c, _ in rd.values() if n.startswith(kernel)]
+    wk = [_ea_writes(c) for n, c, _ in wr.values() if n.startswith(kernel)]
+    kname = next(n for n, _, _ in rd.values() if n.startswith(kernel))
+    # the copy of known size: the copy dispatch whose byte count is nearest to it
+    copy_r = min((_ea_reads(c) for n, c, _ in rd.values() if _is_copy(n)), key=lambda v: abs(v - copy_bytes),
+                 default=0.0)
+    copy_w = min((_ea_writes(c) for n, c, _ in wr.values() if _is_copy(n)), key=lambda v: abs(v - copy_bytes),
+                 default=0.0)
+    r_b, w_b = sum(rk) / len(rk), sum(wk) / len(wk)
+    lines = ["# HBM traffic per launch (rocprofv3 --pmc, L2-to-memory requests by size)", "",
+             f"kernel: {kname}", f"source_hash: {source_hash()}", f"launches: {len(rk)}",
+             f"read_bytes_per_launch: {r_b:.0f}", f"write_bytes_per_launch: {w_b:.0f}",
+             f"algorithmic_bytes_per_launch: {alg_bytes:.0f}",
+             f"traffic_over_algorithmic: {(r_b + w_b) / alg_bytes:.3f}" if alg_bytes else "traffic_over_algorithmic: -",
+             f"copy_check: a {copy_bytes:.0f}-byte device copy read {copy_r:.0f} and wrote {copy_w:.0f} bytes",
+             f"traffic_bytes_per_launch: {r_b + w_b:.0f}", "", "Commands:", "", "```", commands, "```"]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def write_mfma_summary(mfma_csv, kernel, alg_flops, out_md, command, simds=1024, clock_ghz=2.4):
+    mf = read_counters(mfma_csv)
+    rows = [(c, d) for n, c, d in mf.values() if n.startswith(kernel)]
+    kname = next(n for n, _, _ in mf.values() if n.startswith(kernel))
+    busy = sum(c["SQ_VALU_MFMA_BUSY_CYCLES"] for c, _ in rows) / len(rows)
+    flops = sum(c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for c, _ in rows) / len(rows) * 512
+    dur_ns = sum(d for _, d in rows) / len(rows)
+    frac = busy / simds / (dur_ns * clock_ghz)
+    lines = ["# MFMA use per launch (rocprofv3 --pmc)", "",
+             f"kernel: {kname}", f"source_hash: {source_hash()}", f"launches: {len(rows)}",
+             f"mfma_busy_cycles_per_simd: {busy / simds:.0f}",
+             f"duration_us (serialised under the profiler): {dur_ns / 1e3:.2f}",
+             f"mfma_busy_fraction: {frac:.3f}  (busy cycles per SIMD / (duration x {clock_ghz} GHz))",
+             f"bf16_flops_executed: {flops:.4e}  (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)",
+             f"algorithmic_flops: {alg_flops:.4e}",
+             f"executed_tflops: {flops / dur_ns / 1e3:.1f}", "", "Command:", "", "```", command, "```"]
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -149,7 +197,10 @@ def read_traffic(path):
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         write_stats_summary(sys.argv[2], sys.argv[3], sys.argv[4])
-    elif sys.argv[1] == "traffic":
-        write_traffic_summary(sys.argv[2], sys.argv[3], sys.argv[4], float(sys.argv[5]), sys.argv[6], sys.argv[7])
+    elif sys.argv[1] == "ea":
+        write_ea_summary(sys.argv[2], sys.argv[3], sys.argv[4], float(sys.argv[5]), float(sys.argv[6]), sys.argv[7],
+                         sys.argv[8])
+    elif sys.argv[1] == "mfma":
+        write_mfma_summary(sys.argv[2], sys.argv[3], float(sys.argv[4]), sys.argv[5], sys.argv[6])
     else:
         raise SystemExit(__doc__)
