@@ -12,8 +12,9 @@ TCC_EA0_WRREQ_64B_sum; the rest are 32 bytes).  Bytes = 32 n32 + 64 n64 + 128 n1
 32 (n - n64) + 64 n64 written, per dispatch.  (FETCH_SIZE's expression takes 128-byte reads from
 TCC_BUBBLE, which on this GPU does not count them, so it reads low.)  The same counters on a
 plain device copy of known size are reported beside the figure as a check (no scaling is
-applied).  The per-launch bytes of ``kernel`` are recorded with a hash of the kernel sources, so
-a later benchmark can tell whether the figure still describes the current kernels.
+applied).  The per-launch bytes of ``kernel`` are recorded with a hash of the file defining the
+kernel and the shared header, so a later benchmark can tell whether the figure still describes
+the current kernel.
 
 ``mfma`` reads SQ_VALU_MFMA_BUSY_CYCLES (summed over every SIMD) and
 SQ_INSTS_VALU_MFMA_MOPS_BF16 (x 512 = bf16 FLOPs) per dispatch, and the dispatch's duration:
@@ -23,23 +24,46 @@ busy fraction = busy cycles / SIMDs / (duration x clock).
 import csv
 import hashlib
 import os
+import re
 import sys
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 
-def source_hash():
-    """Hash of the HIP sources and the public header (the kernels the figures describe)."""
-    h = hashlib.sha256()
+def kernel_sources(kname):
+    """The HIP files a kernel's code comes from: the file defining it and the shared header."""
+    base = kname.split("<")[0].strip()
     csrc = os.path.join(PKG, "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + fh.read())
-    with open(os.path.join(os.path.dirname(PKG), "include", "spectree.h"), "rb") as fh:
-        h.update(fh.read())
+        if f.endswith(".hip"):
+            with open(os.path.join(csrc, f)) as fh:
+                if re.search(r"__global__[^;{]*\b" + re.escape(base) + r"\s*\(", fh.read()):
+                    return [f, "common.h"]
+    raise KeyError(f"no source defines kernel {base}")
+
+
+def source_hash(files=None):
+    """Hash of the given csrc files (default: every HIP source and header, and the public header)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(PKG, "csrc")
+    if files is None:
+        files = [f for f in sorted(os.listdir(csrc)) if f.endswith((".hip", ".h"))]
+        extra = [os.path.join(os.path.dirname(PKG), "include", "spectree.h")]
+    else:
+        extra = []
+    for f in files:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    for f in extra:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def _hash_lines(kname):
+    src = kernel_sources(kname)
+    return [f"sources: {' '.join(src)}", f"source_hash: {source_hash(src)}"]
 
 
 def _col(header, *names):
@@ -146,7 +170,7 @@ def write_ea_summary(reads_csv, writes_csv, kernel, copy_bytes, alg_bytes, out_m
                  default=0.0)
     r_b, w_b = sum(rk) / len(rk), sum(wk) / len(wk)
     lines = ["# HBM traffic per launch (rocprofv3 --pmc, L2-to-memory requests by size)", "",
-             f"kernel: {kname}", f"source_hash: {source_hash()}", f"launches: {len(rk)}",
+             f"kernel: {kname}", *_hash_lines(kname), f"launches: {len(rk)}",
              f"read_bytes_per_launch: {r_b:.0f}", f"write_bytes_per_launch: {w_b:.0f}",
              f"algorithmic_bytes_per_launch: {alg_bytes:.0f}",
              f"traffic_over_algorithmic: {(r_b + w_b) / alg_bytes:.3f}" if alg_bytes else "traffic_over_algorithmic: -",
@@ -165,7 +189,7 @@ def write_mfma_summary(mfma_csv, kernel, alg_flops, out_md, command, simds=1024,
     dur_ns = sum(d for _, d in rows) / len(rows)
     frac = busy / simds / (dur_ns * clock_ghz)
     lines = ["# MFMA use per launch (rocprofv3 --pmc)", "",
-             f"kernel: {kname}", f"source_hash: {source_hash()}", f"launches: {len(rows)}",
+             f"kernel: {kname}", *_hash_lines(kname), f"launches: {len(rows)}",
              f"mfma_busy_cycles_per_simd: {busy / simds:.0f}",
              f"duration_us (serialised under the profiler): {dur_ns / 1e3:.2f}",
              f"mfma_busy_fraction: {frac:.3f}  (busy cycles per SIMD / (duration x {clock_ghz} GHz))",
@@ -186,7 +210,12 @@ def read_traffic(path):
             if ":" in line and not line.startswith(("#", "`")):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("source_hash") != source_hash():
+    files = kv["sources"].split() if "sources" in kv else None
+    try:
+        current = source_hash(files)
+    except OSError:
+        return None
+    if kv.get("source_hash") != current:
         return None
     try:
         return float(kv["traffic_bytes_per_launch"]), kv.get("kernel")
