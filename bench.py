@@ -54,6 +54,8 @@ def parse_args():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of from HIP graphs")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run a plain device copy of this size (for scaling --pmc byte counters)")
+    ap.add_argument("--side-rows", action="store_true",
+                    help="time the rows beside the step also in a counter run (--copy-calibration-mb)")
     args = ap.parse_args()
     if args.also is None:
         args.also = [3] if args.config == 2 and not args.copy_calibration_mb else []
@@ -615,7 +617,7 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     sb.lib()
-    side = not args.copy_calibration_mb
+    side = not args.copy_calibration_mb or args.side_rows
     r = measure(args, args.config, args.steps, args.warmup, side)
     w, mode, ms_step = r["w"], r["mode"], r["ms_step"]
 

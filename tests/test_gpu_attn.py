@@ -77,19 +77,48 @@ def test_shapes(case):
 
 
 # Every launch shape the library can pick, forced through its internal tuning overrides: rows
-# per wave (CB), waves per workgroup and key splits, on head dims 64 and 128, with
+# per wave (CB), waves per workgroup and key splits, with the softmax reference max exact or
+# lazy (moved only past a slack of 2^8), on head dims 64 and 128, with
 # ragged prefixes, padding nodes and poisoned slots.
 SHAPE_CASES = [(2, 8, 1), (2, 8, 3), (1, 8, 1), (1, 8, 5), (2, 4, 1), (2, 4, 7), (1, 4, 2), (1, 4, 9)]
 
 
+@pytest.mark.parametrize("lazy", [0, 8])
 @pytest.mark.parametrize("cb,waves,splits", SHAPE_CASES)
 @pytest.mark.parametrize("d", [64, 128])
-def test_launch_shapes(tune, cb, waves, splits, d):
-    tune(attn_cb=cb, attn_waves=waves, attn_splits=splits)
+def test_launch_shapes(tune, cb, waves, splits, d, lazy):
+    tune(attn_cb=cb, attn_waves=waves, attn_splits=splits, attn_lazy=lazy)
     w = wl.custom(seed=2500 + cb * 100 + waves * 10 + splits, B=3, N=45, Hq=16, Hkv=4, d=d,
                   prefix=("uniform", 1, 900), tree=("random", 5), n_nodes_range=(20, 45), dtype="bf16",
                   extra_slots=17)
     _check_full(w)
+
+
+@pytest.mark.parametrize("lazy", [0, 8])
+def test_growing_scores(tune, lazy):
+    """Keys whose scores grow along the cache (K scaled up by 1 + s / 150 for slot s, and 8x on
+    the tree slots), so the softmax reference max must move well past the lazy slack many times
+    over a split: every row against the oracle, with the reference exact or lazy, one split and
+    several."""
+    need_gpu()
+    for splits in (1, 4):
+        tune(attn_lazy=lazy, attn_splits=splits)
+        w = wl.custom(seed=2600 + splits, B=2, N=40, Hq=16, Hkv=4, d=128, prefix=("uniform", 600, 1200),
+                      tree=("random", 5), n_nodes_range=(30, 40), dtype="bf16")
+        a = wl.attention_inputs(w, poison=False)
+        S = a["k_cache"].shape[2]
+        grow = (1.0 + np.arange(S, dtype=np.float32) / 150.0)[None, None, :, None]
+        k = a["k_cache"] * grow
+        for b in range(w.B):
+            P = int(a["prefix_len"][b])
+            k[b, :, P:] *= 8.0
+        a["k_cache"] = wl.round_bf16(k.astype(np.float32))
+        got = _gpu_attn(w, a)
+        ref = _full_oracle(a)
+        assert_attn_close(got["out"], ref["out"], "bf16", f"growing scores, splits {splits}")
+        live = np.isfinite(ref["lse"])
+        assert np.array_equal(np.isfinite(got["lse"]), live)
+        np.testing.assert_allclose(got["lse"][live], ref["lse"][live], rtol=2e-4, atol=2e-3)
 
 
 def test_errors_zero_rows():

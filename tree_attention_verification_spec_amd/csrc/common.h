@@ -91,7 +91,7 @@ spec_status launch_status();
 // spec_internal_tune() (internal.h), never read from the environment.  Results do not depend
 // on them.  tuning() returns the forced value, or `fallback` when none is set.
 enum Knob {
-  kKnobAttnCB, kKnobAttnWaves, kKnobAttnSplits, kKnobAttnLpt, kKnobAttnPrio,
+  kKnobAttnCB, kKnobAttnWaves, kKnobAttnSplits, kKnobAttnLpt, kKnobAttnPrio, kKnobAttnLazy,
   kKnobVerifyChunk, kKnobVerifyStoreW, kKnobVerifyRowsList,
   kKnobResRowBlocks, kKnobLmRowBlocks,
   kKnobCount

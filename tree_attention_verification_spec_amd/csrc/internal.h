@@ -22,8 +22,10 @@ void spec_prof_reset(void);
 int spec_prof_read(const char* name, double* total_ms, int64_t* launches);
 
 /* Forces a launch-shape choice for the calls that follow (tests cover every shape the library
- * can pick).  `name` is one of "attn_cb" (1, 2), "attn_waves" (4, 8), "attn_splits" (>= 1),
- * "attn_lpt" (0, 1), "attn_prio" (0, 1), "verify_chunk" (4096, 8192,
+ * can pick).  `name` is one of "attn_cb" (1, 2), "attn_waves" (4, 8),
+ * "attn_splits" (>= 1), "attn_lpt" (0, 1), "attn_prio" (0, 1), "attn_lazy" (0: move the softmax
+ * reference max with every new row maximum; > 0: only when it grows by more than that many
+ * log2 units), "verify_chunk" (4096, 8192,
  * 16384), "verify_store_w" (0, 1), "verify_rows_list" (0, 1), "res_rowblocks" (1, 2, 4),
  * "lm_rowblocks" (4, 8); a negative value removes the override.  Workspace queries made while
  * an override is set size the workspace for the forced shape.  Returns 0, or -1 for an unknown

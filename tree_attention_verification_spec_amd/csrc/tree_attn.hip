@@ -49,6 +49,7 @@ constexpr int kMaxLptSeqs = 256;  // longest-first ordering for batches up to th
 constexpr int kMaxWords = (SPEC_MAX_NODES + 63) / 64;   // ancestor words per tree node
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kLazy = 8;       // reference-max slack (log2 units): weights below 256
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
@@ -71,6 +72,7 @@ struct AttnArgs {
   __bf16* part_o;              // [U, S, Mpad, D]: each split's output normalised by its own sum
   int R, S, Mpad;
   int prio;                    // raise wave priority around the MFMA blocks
+  float lazy;                  // reference-max slack in log2 units (0: exact running max)
   int lpt;                     // dispatch sequences longest first (batches of 2..256)
 };
 
@@ -134,9 +136,9 @@ __device__ __forceinline__ bf16x8 v_fragment(const __bf16* vt, int d0, int c32, 
   return __builtin_bit_cast(bf16x8, both);
 }
 
-// WAVES waves per workgroup, 16 * CB query rows per wave.  Two waves per SIMD are requested
-// (at most 256 registers per lane): while one wave runs its softmax on the VALU the other
-// keeps the matrix cores busy.
+// WAVES waves per workgroup, 16 * CB query rows per wave.  Two waves per SIMD are requested (at
+// most 256 registers per lane): while one wave runs its softmax on the VALU the other keeps the
+// matrix cores busy.
 template <int D, int CB, int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void tree_attn_bf16_kernel(AttnArgs a) {
@@ -154,6 +156,7 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   constexpr int PASSES = kKT / KPP;
   __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][kKT * KS];
   __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][kKT * VS];
+  __shared__ uint64_t s_mask[RBS * kMaxWords];   // ancestor words of the workgroup's rows
   int u, rb, split;
   if (!decode_wg(a, u, rb, split)) return;
   const int b = u / a.Hkv;
@@ -210,15 +213,18 @@ void tree_attn_bf16_kernel(AttnArgs a) {
     for (int ds = 0; ds < DS; ++ds)
       qf[cb][ds] = row_ok[cb] ? *reinterpret_cast<const bf16x8*>(src + ds * 32) : bf16x8{};
   }
-  // The ancestor words of this lane's rows (W <= kMaxWords), requested with Q so that no tile
-  // loads mask words behind the prefetch (the memory counter drains in issue order).  Word
-  // indices are clamped into the row; a clamped word is never selected below.
-  uint64_t mw[CB][kMaxWords];
+  // The ancestor words of the workgroup's rows (W <= kMaxWords per row), requested with Q so
+  // that no tile loads mask words behind the prefetch (the memory counter drains in issue
+  // order), and kept in LDS: only tiles that reach the tree slots read them.  Word indices are
+  // clamped into the row; a clamped word is never selected below.
+  constexpr int MW_PER = (RBS * kMaxWords + THREADS - 1) / THREADS;
+  uint64_t mw[MW_PER];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    const uint64_t* mrow = a.mask + ((size_t)b * a.N + min(row_node[cb], a.N - 1)) * a.W;
-#pragma unroll
-    for (int w = 0; w < kMaxWords; ++w) mw[cb][w] = mrow[min(w, a.W - 1)];
+  for (int k = 0; k < MW_PER; ++k) {
+    const int e = min(k * THREADS + tid, RBS * kMaxWords - 1);
+    const int r = rb * RBS + e / kMaxWords;
+    const int node = min(r / a.G, a.N - 1);
+    mw[k] = a.mask[((size_t)b * a.N + node) * a.W + min(e % kMaxWords, a.W - 1)];
   }
 
   f32x4 o_acc[DB][CB];
@@ -273,11 +279,13 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   // also drains the prefetch.
   auto settle = [&]() {
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) asm volatile("" : "+v"(qf[cb][ds]));
 #pragma unroll
-      for (int w = 0; w < kMaxWords; ++w) asm volatile("" : "+v"(mw[cb][w]));
+    for (int k = 0; k < MW_PER; ++k) {
+      const int e = k * THREADS + tid;
+      if (e < RBS * kMaxWords) s_mask[e] = mw[k];
     }
   };
   if (k0 < k1) {
@@ -286,33 +294,13 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   } else {
     settle();
   }
-  int buf = 0;
-  for (int t0 = k0; t0 < k1; t0 += kKT) {
-    stage(buf);
-    __syncthreads();
-    fetch(t0 + kKT);   // unconditional (past the split it reloads its last key) so no branch
-                       // leaves the compiler unsure how many loads are still in flight
-    // Ancestor words of tree keys j = s - P in this tile: word jw or jw + 1 (j < n <= 64 W).
-    const int jw = (t0 - P) >> 6;                 // floor division (t0 - P may be negative)
-    uint64_t wlo[CB], whi[CB];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      wlo[cb] = mw[cb][0];
-      whi[cb] = mw[cb][0];
-#pragma unroll
-      for (int w = 1; w < kMaxWords; ++w) {
-        wlo[cb] = jw == w ? mw[cb][w] : wlo[cb];
-        whi[cb] = jw + 1 == w ? mw[cb][w] : whi[cb];
-      }
-    }
-    const __bf16* kt = k_lds[buf];
-    const __bf16* vt = v_lds[buf];
 
-    // ---- S^T = K Q^T for the 64 keys of the tile.  The MFMA blocks run at raised wave
-    // priority: a wave that reaches one gets the issue slot first, so the two waves of a SIMD
-    // drift apart and one's softmax (VALU) overlaps the other's products.
+  // ---- S^T = K Q^T for the 64 keys of the tile in buffer `buf`.  The MFMA blocks run at
+  // raised wave priority: a wave that reaches one gets the issue slot first, so the two waves
+  // of a SIMD drift apart and one's softmax (VALU) overlaps the other's products.
+  auto qk = [&](int buf, f32x4 (&s_acc)[4][CB]) {
+    const __bf16* kt = k_lds[buf];
     if (a.prio) __builtin_amdgcn_s_setprio(1);
-    f32x4 s_acc[4][CB];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
@@ -325,14 +313,22 @@ void tree_attn_bf16_kernel(AttnArgs a) {
           s_acc[kb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[cb][ds], s_acc[kb][cb], 0, 0, 0);
       }
     }
-
     if (a.prio) __builtin_amdgcn_s_setprio(0);
-    // ---- mask (only where needed), online softmax in base 2, P^T packed as bf16.  The max is
-    // taken on raw scores (the scale is positive, so it commutes with the max) and each weight
-    // is exp2(s * scale_log2 - m) with one FMA.  Rows past the workload have Q = 0 and are
-    // discarded at the end, so wholly-prefix tiles need no per-score select.
-    const bool plain = t0 + kKT <= k1 && t0 + kKT <= P;   // wholly prefix, wholly in the split
-    bf16x8 pb[2][CB];
+  };
+
+  // ---- mask (MASKED tiles only), online softmax in base 2, P^T packed as bf16, for the tile
+  // starting at key t0.  The max is taken on raw scores (the scale is positive, so it commutes
+  // with the max) and each weight is exp2(s * scale_log2 - m) with one FMA.  Rows past the
+  // workload have Q = 0 and are discarded at the end, so wholly-prefix tiles need no per-score
+  // select.  The reference max m_run moves only when a score exceeds it by more than a.lazy
+  // (log2 units): softmax is the same for any reference, weights stay below 2^lazy, and the O
+  // rescale is rarely needed.  alpha[cb] receives the factor the output accumulated so far must
+  // take (1 where the reference did not move); returns whether any row of the wave moved.
+  auto softmax = [&](auto masked, int t0, f32x4 (&s_acc)[4][CB], bf16x8 (&pb)[2][CB], float (&alpha)[CB]) {
+    constexpr bool MASKED = decltype(masked)::value;
+    // ancestor words of tree keys j = s - P in this tile: word jw or jw + 1 (j < n <= 64 W)
+    const int jw = (t0 - P) >> 6;               // floor division (t0 - P may be negative)
+    bool moved = false;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       float x[4][4];
@@ -340,7 +336,10 @@ void tree_attn_bf16_kernel(AttnArgs a) {
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[kb][e] = s_acc[kb][cb][e];
-      if (!plain) {
+      if constexpr (MASKED) {
+        const uint64_t* mrow = s_mask + (wave * ROWS_WAVE + cb * 16 + l16) * kMaxWords;
+        const uint64_t wlo = mrow[min(max(jw, 0), kMaxWords - 1)];
+        const uint64_t whi = mrow[min(max(jw + 1, 0), kMaxWords - 1)];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -349,7 +348,7 @@ void tree_attn_bf16_kernel(AttnArgs a) {
             bool vis = row_ok[cb] && s < k1;
             if (vis && s >= P) {
               const int j = s - P;
-              const uint64_t word = ((j >> 6) == jw) ? wlo[cb] : whi[cb];
+              const uint64_t word = ((j >> 6) == jw) ? wlo : whi;
               vis = (word >> (j & 63)) & 1ull;
             }
             if (!vis) x[kb][e] = -INFINITY;
@@ -362,33 +361,40 @@ void tree_attn_bf16_kernel(AttnArgs a) {
         for (int e = 0; e < 4; ++e) mloc = fmaxf(mloc, x[kb][e]);
       mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const float m_new = fmaxf(m_run[cb], mloc * a.scale_log2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      if (__ballot(m_new > m_run[cb])) {         // some row's max moved: rescale
-        const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_use);
-        o_sum[cb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o_acc[db][cb] *= alpha;
-        m_run[cb] = m_new;
-      }
+      const float m_tile = mloc * a.scale_log2;
+      const bool grow = m_tile > m_run[cb] + a.lazy;   // false while both are -inf
+      alpha[cb] = grow ? __builtin_amdgcn_exp2f(m_run[cb] - m_tile) : 1.f;   // 0 from -inf
+      m_run[cb] = grow ? m_tile : m_run[cb];
+      moved = moved || __ballot(grow) != 0;
+      const float m_use = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[kb][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][e], a.scale_log2, -m_use));
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        bf16x8 p;
+        bf16x8 pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          p[e] = (__bf16)x[2 * c][e];
-          p[4 + e] = (__bf16)x[2 * c + 1][e];
+          pk[e] = (__bf16)x[2 * c][e];
+          pk[4 + e] = (__bf16)x[2 * c + 1][e];
         }
-        pb[c][cb] = p;
+        pb[c][cb] = pk;
       }
     }
-
-    // ---- O^T += V^T P^T.
-    if (a.prio) __builtin_amdgcn_s_setprio(1);
+    return moved;
+  };
+  auto rescale = [&](const float (&alpha)[CB]) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      o_sum[cb] *= alpha[cb];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o_acc[db][cb] *= alpha[cb];
+    }
+  };
+  // ---- O^T += V^T P^T with the tile in buffer `buf`.
+  auto pv = [&](int buf, const bf16x8 (&pb)[2][CB]) {
+    const __bf16* vt = v_lds[buf];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -404,6 +410,25 @@ void tree_attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
         o_sum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_frag, pb[c][cb], o_sum[cb], 0, 0, 0);
+  };
+  // wholly prefix and wholly inside the split: no mask
+  auto is_plain = [&](int t0) { return t0 + kKT <= k1 && t0 + kKT <= P; };
+
+  int buf = 0;
+  for (int t0 = k0; t0 < k1; t0 += kKT) {
+    stage(buf);
+    __syncthreads();
+    fetch(t0 + kKT);   // unconditional (past the split it reloads its last key) so no branch
+                       // leaves the compiler unsure how many loads are still in flight
+    f32x4 s_acc[4][CB];
+    qk(buf, s_acc);
+    bf16x8 pb[2][CB];
+    float alpha[CB];
+    const bool moved = is_plain(t0) ? softmax(std::false_type{}, t0, s_acc, pb, alpha)
+                                    : softmax(std::true_type{}, t0, s_acc, pb, alpha);
+    if (moved) rescale(alpha);
+    if (a.prio) __builtin_amdgcn_s_setprio(1);
+    pv(buf, pb);
     if (a.prio) __builtin_amdgcn_s_setprio(0);
     buf ^= 1;
   }
@@ -730,6 +755,7 @@ extern "C" spec_status spec_tree_attn(const void* q, const void* k_cache, const 
   if (need > 0 && (!workspace || ws_bytes < need)) return SPEC_EWORKSPACE;
   a.R = p.R; a.S = p.S; a.Mpad = p.Mpad;
   a.prio = tuning(kKnobAttnPrio, 1);
+  a.lazy = (float)std::max(0, tuning(kKnobAttnLazy, kLazy));
   a.lpt = p.lpt;
   if (p.S > 1) {
     char* w = static_cast<char*>(workspace);
