@@ -673,44 +673,46 @@ __device__ __forceinline__ double draft_at(const VerifyArgs& a, int b, int r, in
 // decision, all nodes at once: the workgroup of node p writes (c_(j-1), f(c_(j-1))) for its
 // j-th child and c_k (k children) for a residual bonus draw at p.
 //
-// Each f is a pass over the row with T = fp32 exp(x - M) / S (as in the row pass) reduced against
-// c D in fp64; the passes are sequential, so one 1024-thread workgroup per node streams the row
-// with 32 elements per thread in flight.  Tokens with D = 0 add T at every c (their sum is kept
-// apart), and a token with D > 0 that adds nothing at c adds nothing at any larger c, since
-// exp(x - M) / S - c D only falls as c grows.  So each streaming pass also collects, in LDS, the
-// tokens with D != 0 that still add something; once they fit (the chain's c grows by f each step
-// and the set shrinks fast), every later pass reads only that list.  Grid (seq, node); nodes with
-// fewer than two children need no pass.
-constexpr int kChainThreads = 512;
-constexpr int kChainWaves = kChainThreads / kWave;
-constexpr int kChainPer = 24;                 // elements per thread per streaming step
+// Each f is a pass over the row, one 1024-thread workgroup per node (the passes are sequential).
+// The test is done in units of S: relu(T - c D) = relu(e - cS D) / S with e = fp32 exp(x - M) (as
+// in the row pass) and cS = c S, one fp64 FMA per token.  Tokens with D = 0 add T at every c:
+// their sum is taken in the first pass only.  A token with D > 0 that adds nothing at c adds
+// nothing at any larger c, since e - cS D only falls as c grows; so each streaming pass also
+// collects, in LDS, the tokens with D != 0 that still add something, and once they fit (the
+// chain's c grows by f each step and the set shrinks), every later pass reads only that list.
+// Every thread keeps two register sets of 8 tokens in flight (the next set's loads are issued
+// before the current one is reduced), and the way the draft row is read (DM: 0 one value at a
+// time, 1 16-byte loads, 2 through t2d) is fixed per launch.  Grid (seq, node); nodes with fewer
+// than two children need no pass.
 constexpr int kChainCap = 16384;              // LDS list: (exp(x - M), D) pairs, 128 KB
 
-__device__ __forceinline__ double chain_sum(double v, double* red) {
-  v = wave_sum(v);
-  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x >> 6;
-  if (lane == 0) red[wv] = v;
-  __syncthreads();
-  double r = 0.0;
-#pragma unroll
-  for (int q = 0; q < kChainWaves; ++q) r += red[q];
-  __syncthreads();
-  return r;
-}
+template <int THREADS, int PER, int VEC, int DM>
+struct Chain {
+  static constexpr int kWaves = THREADS / kWave;
+  static constexpr int kStep = THREADS * PER;
 
-// One streaming pass of a chain at c: fp = sum over tokens with D != 0 of relu(T - c D), z = sum
-// of T over tokens with D = 0, cnt = this thread's tokens with D != 0 and T - c D > 0; with BUILD
-// they are also appended to the LDS list as (exp(x - M), D) (one LDS atomic per wave and step).
-template <int VEC, bool BUILD>
-__device__ __forceinline__ void chain_stream(const VerifyArgs& a, const float* row, const float* drow,
-                                             bool dvec, float M, double invS, double cj, double& fp,
-                                             double& z, int& cnt, float2* list, int* list_n) {
-  const int t = threadIdx.x, lane = t & (kWave - 1);
-  for (int v0 = 0; v0 < a.V; v0 += kChainThreads * kChainPer) {
-    float x[kChainPer], d[kChainPer];
+  // token index of slot u of the set starting at v0 (VEC consecutive tokens per load)
+  static __device__ __forceinline__ int index(int v0, int u) {
+    return v0 + ((u / VEC) * THREADS + (int)threadIdx.x) * VEC + u % VEC;
+  }
+
+  static __device__ __forceinline__ double sum(double v, double* red) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x >> 6;
+    if (lane == 0) red[wv] = v;
+    __syncthreads();
+    double r = 0.0;
 #pragma unroll
-    for (int u = 0; u < kChainPer / VEC; ++u) {
-      const int vb = v0 + (u * kChainThreads + t) * VEC;
+    for (int q = 0; q < kWaves; ++q) r += red[q];
+    __syncthreads();
+    return r;
+  }
+
+  static __device__ __forceinline__ void load(const VerifyArgs& a, const float* row, const float* drow, int v0,
+                                              float (&x)[PER], float (&d)[PER]) {
+#pragma unroll
+    for (int u = 0; u < PER / VEC; ++u) {
+      const int vb = index(v0, u * VEC);
       const int at = vb < a.V ? vb : 0;
       if (VEC == 4) {
         const float4 x4 = *reinterpret_cast<const float4*>(row + at);
@@ -718,50 +720,54 @@ __device__ __forceinline__ void chain_stream(const VerifyArgs& a, const float* r
         x[u * VEC + (VEC > 1 ? 1 : 0)] = x4.y;
         x[u * VEC + (VEC > 2 ? 2 : 0)] = x4.z;
         x[u * VEC + (VEC > 3 ? 3 : 0)] = x4.w;
+        if (DM == 1) {
+          const float4 d4 = *reinterpret_cast<const float4*>(drow + at);
+          d[u * VEC] = d4.x;
+          d[u * VEC + (VEC > 1 ? 1 : 0)] = d4.y;
+          d[u * VEC + (VEC > 2 ? 2 : 0)] = d4.z;
+          d[u * VEC + (VEC > 3 ? 3 : 0)] = d4.w;
+        }
       } else {
         x[u] = row[at];
       }
     }
-    if (a.t2d) {
+    if (DM == 2) {
 #pragma unroll
-      for (int u = 0; u < kChainPer; ++u) {
-        const int v = v0 + ((u / VEC) * kChainThreads + t) * VEC + u % VEC;
+      for (int u = 0; u < PER; ++u) {
+        const int v = index(v0, u);
         const int dx = a.t2d[v < a.V ? v : 0];
         const bool mapped = dx >= 0 && dx < a.Vd;
         const float dv = drow[mapped ? dx : 0];
         d[u] = mapped ? dv : 0.f;
       }
-    } else if (dvec) {
+    } else if (DM == 0) {
 #pragma unroll
-      for (int u = 0; u < kChainPer / VEC; ++u) {
-        const int vb = v0 + (u * kChainThreads + t) * VEC;
-        const float4 d4 = *reinterpret_cast<const float4*>(drow + (vb < a.V ? vb : 0));
-        d[u * VEC] = d4.x;
-        d[u * VEC + (VEC > 1 ? 1 : 0)] = d4.y;
-        d[u * VEC + (VEC > 2 ? 2 : 0)] = d4.z;
-        d[u * VEC + (VEC > 3 ? 3 : 0)] = d4.w;
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < kChainPer; ++u) {
-        const int v = v0 + ((u / VEC) * kChainThreads + t) * VEC + u % VEC;
+      for (int u = 0; u < PER; ++u) {
+        const int v = index(v0, u);
         d[u] = drow[v < a.V ? v : 0];
       }
     }
+  }
+
+  // fp += relu(e - cS D) over tokens with D != 0, z += e over tokens with D = 0 (FIRST), cnt =
+  // tokens with D != 0 that add something; BUILD appends those to the LDS list as (e, D)
+  template <bool FIRST, bool BUILD>
+  static __device__ __forceinline__ void reduce(const VerifyArgs& a, int v0, const float (&x)[PER],
+                                                const float (&d)[PER], float M, double cS, double& fp, double& z,
+                                                int& cnt, float2* list, int* list_n) {
+    const int lane = threadIdx.x & (kWave - 1);
+    float e[PER], dk[PER];
     int mine = 0;
 #pragma unroll
-    for (int u = 0; u < kChainPer; ++u) x[u] = __expf(x[u] - M);    // x now holds exp(x - M)
-#pragma unroll
-    for (int u = 0; u < kChainPer; ++u) {
-      const int v = v0 + ((u / VEC) * kChainThreads + t) * VEC + u % VEC;
-      const bool in = v < a.V;
-      const double tv = (double)x[u] * invS;
-      const double q = tv - cj * (double)d[u];
-      z += (in && d[u] == 0.f) ? tv : 0.0;
+    for (int u = 0; u < PER; ++u) {
+      const bool in = index(v0, u) < a.V;
+      e[u] = __expf(x[u] - M);
+      if (FIRST) z += (in && d[u] == 0.f) ? (double)e[u] : 0.0;
+      const double q = __builtin_fma(-cS, (double)d[u], (double)e[u]);
       const bool keep = in && d[u] != 0.f && q > 0.0;
       fp += keep ? q : 0.0;
       mine += keep ? 1 : 0;
-      d[u] = keep ? d[u] : 0.f;            // 0 marks a token that is not appended
+      dk[u] = keep ? d[u] : 0.f;               // 0 marks a token that is not appended
     }
     cnt += mine;
     if (BUILD) {
@@ -775,31 +781,46 @@ __device__ __forceinline__ void chain_stream(const VerifyArgs& a, const float* r
       if (lane == kWave - 1 && incl) at = atomicAdd(list_n, incl);
       int pos = __shfl(at, kWave - 1) + incl - mine;
 #pragma unroll
-      for (int u = 0; u < kChainPer; ++u) {
-        if (d[u] != 0.f) {
-          if (pos < kChainCap) list[pos] = make_float2(x[u], d[u]);
+      for (int u = 0; u < PER; ++u) {
+        if (dk[u] != 0.f) {
+          if (pos < kChainCap) list[pos] = make_float2(e[u], dk[u]);
           ++pos;
         }
       }
     }
   }
-}
 
-template <int VEC>
-__global__ __launch_bounds__(kChainThreads) void walk_chain_kernel(VerifyArgs a) {
+  template <bool FIRST, bool BUILD>
+  static __device__ void stream(const VerifyArgs& a, const float* row, const float* drow, float M, double cS,
+                                double& fp, double& z, int& cnt, float2* list, int* list_n) {
+    float xa[PER], da[PER], xb[PER], db[PER];
+    load(a, row, drow, 0, xa, da);
+    for (int v0 = 0; v0 < a.V; v0 += 2 * kStep) {
+      load(a, row, drow, v0 + kStep, xb, db);   // in flight during the reduce
+      reduce<FIRST, BUILD>(a, v0, xa, da, M, cS, fp, z, cnt, list, list_n);
+      if (v0 + kStep >= a.V) break;
+      load(a, row, drow, v0 + 2 * kStep, xa, da);
+      reduce<FIRST, BUILD>(a, v0 + kStep, xb, db, M, cS, fp, z, cnt, list, list_n);
+    }
+  }
+};
+
+template <int THREADS, int PER, int VEC, int DM>
+__global__ __launch_bounds__(THREADS) void walk_chain_kernel(VerifyArgs a) {
+  using CH = Chain<THREADS, PER, VEC, DM>;
   __shared__ float2 s_list[kChainCap];
   __shared__ int s_kids[SPEC_MAX_NODES];
-  __shared__ int s_wcnt[kChainWaves];
-  __shared__ double s_red[kChainWaves];
+  __shared__ int s_wcnt[CH::kWaves];
+  __shared__ double s_red[CH::kWaves];
   __shared__ int s_n;
   __shared__ float s_M;
-  __shared__ double s_invS;
+  __shared__ double s_S;
   const int b = blockIdx.x / a.N, p = blockIdx.x - b * a.N;
   const int t = threadIdx.x, lane = t & (kWave - 1), wv = t >> 6;
   const int n = a.n_nodes ? a.n_nodes[b] : a.N;
   if (n < 1 || n > a.N || p >= n) return;
   const size_t base = (size_t)b * a.N;
-  // the children of p in index order (one candidate node per thread)
+  // the children of p in index order (one candidate node per thread; THREADS >= N)
   const int i = p + 1 + t;
   const bool kid = i < n && a.parents[base + i] == p;
   const unsigned long long bal = __ballot(kid);
@@ -807,7 +828,7 @@ __global__ __launch_bounds__(kChainThreads) void walk_chain_kernel(VerifyArgs a)
   __syncthreads();
   int off = 0, k = 0;
 #pragma unroll
-  for (int q = 0; q < kChainWaves; ++q) {
+  for (int q = 0; q < CH::kWaves; ++q) {
     off += q < wv ? s_wcnt[q] : 0;
     k += s_wcnt[q];
   }
@@ -828,44 +849,47 @@ __global__ __launch_bounds__(kChainThreads) void walk_chain_kernel(VerifyArgs a)
     for (int q = 0; q < a.CR; ++q)
       if (rp[q].m != -INFINITY) S += rp[q].S * exp((double)rp[q].m - (double)M);
     s_M = M;
-    s_invS = 1.0 / S;
+    s_S = S;
   }
   __syncthreads();
   const float M = s_M;
-  const double invS = s_invS;
+  const double S = s_S, invS = 1.0 / S;
   const int r = min(max(a.draft_row[base + s_kids[0]], 0), a.R - 1);
   const float* row = a.logits + (base + p) * a.V;
   const float* drow = a.draft + ((size_t)b * a.R + r) * a.Vd;
-  // 16-byte draft loads when the draft row is the target vocabulary and aligned like the logits
-  const bool dvec = VEC == 4 && !a.t2d && (reinterpret_cast<uintptr_t>(drow) & 15) == 0;
-  double cj = 1.0, zero_part = 0.0;
+  double cj = 1.0, zS = 0.0;               // zS: sum of e over tokens with D = 0
   int listed = -1;        // entries of s_list once it holds every token that can still add
   int prev = INT_MAX;     // tokens with D != 0 that added something in the previous pass
   for (int j = 1; j < k; ++j) {
-    double f;
+    const double cS = cj * S;
+    double fS;
     if (listed < 0) {
-      // the contributors at c_j are a subset of those at c_(j-1): collect them only when their
-      // previous count shows that they fit
       const bool build = prev <= kChainCap;
       if (t == 0) s_n = 0;
       __syncthreads();
       double fp = 0.0, z = 0.0;
       int cnt = 0;
-      if (build) chain_stream<VEC, true>(a, row, drow, dvec, M, invS, cj, fp, z, cnt, s_list, &s_n);
-      else chain_stream<VEC, false>(a, row, drow, dvec, M, invS, cj, fp, z, cnt, s_list, &s_n);
-      zero_part = chain_sum(z, s_red);
-      f = zero_part + chain_sum(fp, s_red);
-      prev = (int)chain_sum((double)cnt, s_red);
+      if (j == 1) {
+        if (build) CH::template stream<true, true>(a, row, drow, M, cS, fp, z, cnt, s_list, &s_n);
+        else CH::template stream<true, false>(a, row, drow, M, cS, fp, z, cnt, s_list, &s_n);
+        zS = CH::sum(z, s_red);
+      } else {
+        if (build) CH::template stream<false, true>(a, row, drow, M, cS, fp, z, cnt, s_list, &s_n);
+        else CH::template stream<false, false>(a, row, drow, M, cS, fp, z, cnt, s_list, &s_n);
+      }
+      fS = zS + CH::sum(fp, s_red);
+      prev = (int)CH::sum((double)cnt, s_red);
       if (build) listed = prev;
     } else {
       double fp = 0.0;
-      for (int e = t; e < listed; e += kChainThreads) {
+      for (int e = t; e < listed; e += THREADS) {
         const float2 ed = s_list[e];
-        const double q = (double)ed.x * invS - cj * (double)ed.y;
+        const double q = __builtin_fma(-cS, (double)ed.y, (double)ed.x);
         fp += q > 0.0 ? q : 0.0;
       }
-      f = zero_part + chain_sum(fp, s_red);
+      fS = zS + CH::sum(fp, s_red);
     }
+    const double f = fS * invS;
     if (t == 0) {
       a.wc[base + s_kids[j]] = cj;
       a.wf[base + s_kids[j]] = f;
@@ -873,6 +897,22 @@ __global__ __launch_bounds__(kChainThreads) void walk_chain_kernel(VerifyArgs a)
     cj += f;
   }
   if (t == 0) a.wend[base + p] = cj;
+}
+
+template <int THREADS, int PER>
+void launch_chain(const VerifyArgs& a, dim3 grid, bool vec4, bool dvec, hipStream_t s) {
+  const char* nm = "verify_walk_chain";
+  const dim3 blk(THREADS);
+  if (a.t2d) {
+    if (vec4) launch(nm, walk_chain_kernel<THREADS, PER, 4, 2>, grid, blk, s, a);
+    else launch(nm, walk_chain_kernel<THREADS, PER, 1, 2>, grid, blk, s, a);
+  } else if (vec4 && dvec) {
+    launch(nm, walk_chain_kernel<THREADS, PER, 4, 1>, grid, blk, s, a);
+  } else if (vec4) {
+    launch(nm, walk_chain_kernel<THREADS, PER, 4, 0>, grid, blk, s, a);
+  } else {
+    launch(nm, walk_chain_kernel<THREADS, PER, 1, 0>, grid, blk, s, a);
+  }
 }
 
 template <int VEC, int CS>
@@ -1439,9 +1479,9 @@ spec_status run_verify(const float* target_logits, const float* draft_probs, con
     else launch(nr, rows_kernel<1, 16>, grid_rows, blk, s, a);
   }
   if (mode == SPEC_VERIFY_WALK) {
-    const dim3 gw((unsigned)((size_t)B * N)), bw(kChainThreads);
-    if (vec4) launch("verify_walk_chain", walk_chain_kernel<4>, gw, bw, s, a);
-    else launch("verify_walk_chain", walk_chain_kernel<1>, gw, bw, s, a);
+    // 16-byte draft loads when the draft rows are the target vocabulary and aligned like the logits
+    const bool dvec = draft_probs && !t2d && Vd % 4 == 0 && (reinterpret_cast<uintptr_t>(draft_probs) & 15) == 0;
+    launch_chain<1024, 8>(a, dim3((unsigned)((size_t)B * N)), vec4, dvec, s);
   }
   // the draw: one wave per sequence when the weights are stored and a wave holds the chunks
   const bool wave_draw = a.weights && L.C <= kWave;
