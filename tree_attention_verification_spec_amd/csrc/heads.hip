@@ -165,44 +165,50 @@ __global__ __launch_bounds__(kThreads) void lm_head_kernel(const __bf16* __restr
   // stored).  All fragments of the next step (W_lm from HBM, z from L2) are requested before
   // this step's products: the memory counter drains in issue order, so a load issued after
   // the prefetch could only be waited for together with it.
+  // Two K steps per fetch, so both 64-byte halves of each 128-byte W_lm line are requested
+  // back to back (one step per fetch left the second half to a later request that often
+  // missed L2: 363 MB read per launch for 262 MB of weights, now 299 MB); two slots, one pair
+  // of steps in flight while the other's products run.  Step indices are clamped, so the loads
+  // past the last step re-read it (L2 hits) and stay inside the slice.
   const int steps = kslice / 32;
   struct Frags {
-    bf16x8 a[RB];
-    bf16x8 b[3][CBN];
+    bf16x8 a[RB][2];
+    bf16x8 b[3][CBN][2];
   };
-  auto fetch = [&](Frags& f, int s) {
+  auto fetch = [&](Frags& g, int s) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) f.a[rb] = load8(arow[rb] + s * 32);
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) g.a[rb][h] = load8(arow[rb] + min(s + h, steps - 1) * 32);
 #pragma unroll
     for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
-      for (int cb = 0; cb < CBN; ++cb) f.b[sp][cb] = load8(bptr[sp][cb] + (size_t)s * 32 * NC);
+      for (int cb = 0; cb < CBN; ++cb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) g.b[sp][cb][h] = load8(bptr[sp][cb] + (size_t)min(s + h, steps - 1) * 32 * NC);
   };
-  auto products = [&](const Frags& f) {
+  auto products = [&](const Frags& g, int s) {
 #pragma unroll
-    for (int cb = 0; cb < CBN; ++cb)
+    for (int h = 0; h < 2; ++h) {
+      if (s + h >= steps) break;
 #pragma unroll
-      for (int sp = 0; sp < 3; ++sp)
+      for (int cb = 0; cb < CBN; ++cb)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[rb], f.b[sp][cb], acc[rb][cb], 0, 0, 0);
-  };
-  // A ring of NB buffers, NB - 1 steps requested ahead of the products: three with 8 row
-  // blocks (one wave per SIMD, so the registers cost no occupancy), two otherwise (deeper rings
-  // measured slower there).  The ring index is static inside the unrolled body (a register
-  // copy would wait for the loads it copies).  Step indices are
-  // clamped, so the loads past the last step re-read it (L2 hits) and stay inside the slice.
-  constexpr int NB = (RB == 8 && CBN <= 2) ? 3 : 2;
-  Frags f[NB];
+        for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
-  for (int u = 0; u < NB - 1; ++u) fetch(f[u], min(u, steps - 1));
-  for (int s = 0; s < steps; s += NB) {
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      fetch(f[(u + NB - 1) % NB], min(s + u + NB - 1, steps - 1));
-      __builtin_amdgcn_sched_barrier(0);    // keep the prefetch ahead of the products
-      if (s + u < steps) products(f[u]);
+          for (int rb = 0; rb < RB; ++rb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g.a[rb][h], g.b[sp][cb][h], acc[rb][cb], 0, 0, 0);
     }
+  };
+  Frags g[2];
+  fetch(g[0], 0);
+  for (int s = 0; s < steps; s += 4) {
+    fetch(g[1], s + 2);
+    __builtin_amdgcn_sched_barrier(0);    // keep the prefetch ahead of the products
+    products(g[0], s);
+    fetch(g[0], s + 4);
+    __builtin_amdgcn_sched_barrier(0);
+    products(g[1], s + 2);
   }
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -444,6 +450,15 @@ __global__ __launch_bounds__(kThreads) void softmax_topk_big_kernel(const float*
     for (int v = t; v < V; v += kThreads) probs[(size_t)col * V + v] = weight(row[v], mL) * invS;
 }
 
+template <int RB>
+void launch_lm_head(int cbn, const char* nm, dim3 grid, dim3 blk, hipStream_t s, const __bf16* wl, const __bf16* zs,
+                    int NC, int Dm, int V, float* logits) {
+  if (cbn == 1) launch(nm, lm_head_kernel<1, RB>, grid, blk, s, wl, zs, NC, Dm, V, logits);
+  else if (cbn == 2) launch(nm, lm_head_kernel<2, RB>, grid, blk, s, wl, zs, NC, Dm, V, logits);
+  else if (cbn == 3) launch(nm, lm_head_kernel<3, RB>, grid, blk, s, wl, zs, NC, Dm, V, logits);
+  else launch(nm, lm_head_kernel<4, RB>, grid, blk, s, wl, zs, NC, Dm, V, logits);
+}
+
 struct HeadsLayout {
   size_t zsplit, logits, total;
 };
@@ -500,17 +515,8 @@ extern "C" spec_status spec_medusa_heads(const void* h, const void* W_res, const
   const __bf16* zs = zsplit;
   const char* nm = "medusa_lm_head";
   const int cbn = (NC + 15) / 16;
-  if (RBv == 8) {
-    if (cbn == 1) launch(nm, lm_head_kernel<1, 8>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
-    else if (cbn == 2) launch(nm, lm_head_kernel<2, 8>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
-    else if (cbn == 3) launch(nm, lm_head_kernel<3, 8>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
-    else launch(nm, lm_head_kernel<4, 8>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
-  } else {
-    if (cbn == 1) launch(nm, lm_head_kernel<1, 4>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
-    else if (cbn == 2) launch(nm, lm_head_kernel<2, 4>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
-    else if (cbn == 3) launch(nm, lm_head_kernel<3, 4>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
-    else launch(nm, lm_head_kernel<4, 4>, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
-  }
+  if (RBv == 8) launch_lm_head<8>(cbn, nm, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
+  else launch_lm_head<4>(cbn, nm, grid_lm, blk, s, wl, zs, NC, Dm, V, logits);
   const float* lg = logits;
   const char* nt = "medusa_softmax_topk";
   // logits rows start on 16-byte boundaries when V % 4 == 0 (the workspace is 256-byte aligned)

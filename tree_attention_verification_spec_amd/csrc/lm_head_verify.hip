@@ -103,38 +103,46 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_kernel(
   for (int rb = 0; rb < kLRB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < CBN; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Two K steps per fetch, so both 64-byte halves of each 128-byte weight line are requested
+  // back to back (one step per fetch left the second half to a later request, and a quarter of
+  // the weight lines had left L2 by then: 1.36 GB read per launch for 1.05 GB of weights); two
+  // slots, one pair of steps in flight while the other's products run.  Step indices are
+  // clamped, so the loads past the last step re-read it inside the slice.
+  const int steps = kslice / 32;
   struct Frags {
-    bf16x8 a[kLRB];
-    bf16x8 b[CBN];
+    bf16x8 a[kLRB][2];
+    bf16x8 b[CBN][2];
   };
-  auto fetch = [&](Frags& f, int s) {
+  auto fetch = [&](Frags& g, int s) {
 #pragma unroll
-    for (int rb = 0; rb < kLRB; ++rb) f.a[rb] = ld8(arow[rb] + s * 32);
+    for (int rb = 0; rb < kLRB; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < CBN; ++cb) f.b[cb] = ld8(bptr[cb] + (size_t)s * 32 * M);
-  };
-  auto products = [&](const Frags& f) {
+      for (int h = 0; h < 2; ++h) g.a[rb][h] = ld8(arow[rb] + min(s + h, steps - 1) * 32);
 #pragma unroll
     for (int cb = 0; cb < CBN; ++cb)
 #pragma unroll
-      for (int rb = 0; rb < kLRB; ++rb)
-        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[rb], f.b[cb], acc[rb][cb], 0, 0, 0);
+      for (int h = 0; h < 2; ++h) g.b[cb][h] = ld8(bptr[cb] + (size_t)min(s + h, steps - 1) * 32 * M);
   };
-  // a three-slot ring: two steps' fragments are in flight while a step's products run (the
-  // ring index is static inside the unrolled body); step indices are clamped, so the loads past
-  // the last step re-read it inside the slice
-  constexpr int NB = 3;
-  const int steps = kslice / 32;
-  Frags f[NB];
+  auto products = [&](const Frags& g, int s) {
 #pragma unroll
-  for (int u = 0; u < NB - 1; ++u) fetch(f[u], min(u, steps - 1));
-  for (int s = 0; s < steps; s += NB) {
+    for (int h = 0; h < 2; ++h) {
+      if (s + h >= steps) break;
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      fetch(f[(u + NB - 1) % NB], min(s + u + NB - 1, steps - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      if (s + u < steps) products(f[u]);
+      for (int cb = 0; cb < CBN; ++cb)
+#pragma unroll
+        for (int rb = 0; rb < kLRB; ++rb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g.a[rb][h], g.b[cb][h], acc[rb][cb], 0, 0, 0);
     }
+  };
+  Frags g[2];
+  fetch(g[0], 0);
+  for (int s = 0; s < steps; s += 4) {
+    fetch(g[1], s + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    products(g[0], s);
+    fetch(g[0], s + 4);
+    __builtin_amdgcn_sched_barrier(0);
+    products(g[1], s + 2);
   }
 #pragma unroll
   for (int rb = 0; rb < kLRB; ++rb)
@@ -253,35 +261,43 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_wide_kernel(
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < CBN; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // two K steps per fetch (both halves of each 128-byte weight line back to back), two slots,
+  // as in lmhead_stats_kernel
+  const int steps = Dm / 32;
   struct Frags {
-    bf16x8 a[RB];
-    bf16x8 b[CBN];
+    bf16x8 a[RB][2];
+    bf16x8 b[CBN][2];
   };
-  auto fetch = [&](Frags& f, int s) {
+  auto fetch = [&](Frags& g, int s) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) f.a[rb] = ld8(arow[rb] + s * 32);
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < CBN; ++cb) f.b[cb] = ld8(bptr[cb] + (size_t)s * 32 * M);
-  };
-  auto products = [&](const Frags& f) {
+      for (int h = 0; h < 2; ++h) g.a[rb][h] = ld8(arow[rb] + min(s + h, steps - 1) * 32);
 #pragma unroll
     for (int cb = 0; cb < CBN; ++cb)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[rb], f.b[cb], acc[rb][cb], 0, 0, 0);
+      for (int h = 0; h < 2; ++h) g.b[cb][h] = ld8(bptr[cb] + (size_t)min(s + h, steps - 1) * 32 * M);
   };
-  constexpr int NB = 3;
-  const int steps = Dm / 32;
-  Frags f[NB];
+  auto products = [&](const Frags& g, int s) {
 #pragma unroll
-  for (int u = 0; u < NB - 1; ++u) fetch(f[u], min(u, steps - 1));
-  for (int s = 0; s < steps; s += NB) {
+    for (int h = 0; h < 2; ++h) {
+      if (s + h >= steps) break;
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      fetch(f[(u + NB - 1) % NB], min(s + u + NB - 1, steps - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      if (s + u < steps) products(f[u]);
+      for (int cb = 0; cb < CBN; ++cb)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g.a[rb][h], g.b[cb][h], acc[rb][cb], 0, 0, 0);
     }
+  };
+  Frags g[2];
+  fetch(g[0], 0);
+  for (int s = 0; s < steps; s += 4) {
+    fetch(g[1], s + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    products(g[0], s);
+    fetch(g[0], s + 4);
+    __builtin_amdgcn_sched_barrier(0);
+    products(g[1], s + 2);
   }
   float (*tw)[kLMaxCols + 1] = tile[wave];
 #pragma unroll
