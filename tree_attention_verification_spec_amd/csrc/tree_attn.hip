@@ -18,8 +18,9 @@
 // A-operand fragments (one output dimension per lane, 8 keys in the slots) come from the LDS
 // transpose read ds_read_b64_tr_b16: within each 16-lane group, lane L reads 4 dimensions of
 // key key0 + L / 4 and lane j receives dimension j of those 4 keys.  Every per-row quantity
-// (running max, sum, rescale) lives in the lanes of that row; the O rescale is skipped for a
-// tile in which no row's max moved.
+// (running max, sum, rescale) lives in the lanes of that row.  The reference max of the
+// exponentials moves only when a tile's max exceeds it by more than a slack of 2^8, so the O
+// rescale is rare (softmax does not depend on the reference).
 //
 // Tiles are double-buffered: the next tile's global loads are issued into registers before
 // the current tile is computed and written to the other LDS buffer afterwards, so there is

@@ -43,8 +43,19 @@ def kernel_sources(kname):
     raise KeyError(f"no source defines kernel {base}")
 
 
+def _code(path):
+    """A source file's code with comments removed and whitespace collapsed: an edited comment
+    does not change the kernel a figure describes."""
+    with open(path, encoding="utf-8") as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split()).encode()
+
+
 def source_hash(files=None):
-    """Hash of the given csrc files (default: every HIP source and header, and the public header)."""
+    """Hash of the code of the given csrc files (default: every HIP source and header, and the
+    public header)."""
     h = hashlib.sha256()
     csrc = os.path.join(PKG, "csrc")
     if files is None:
@@ -53,11 +64,9 @@ def source_hash(files=None):
     else:
         extra = []
     for f in files:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        h.update(f.encode() + _code(os.path.join(csrc, f)))
     for f in extra:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        h.update(_code(f))
     return h.hexdigest()[:16]
 
 
