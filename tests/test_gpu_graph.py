@@ -1,9 +1,11 @@
-"""The entry points inside a captured HIP graph: a verification step (tree build, tree attention,
-rejection and walk verification), a tree selection and a fused LM head with verification from
-hidden states in all four modes are captured once with preallocated outputs and workspaces,
-replayed three times with unrelated eager work and synchronisations in between, and every
-replay's outputs must equal the eager call's bit for bit (the kernels are deterministic: no
-atomics decide a floating-point sum)."""
+"""Every entry point inside a captured HIP graph: a verification step (tree build, tree attention,
+rejection and walk verification, the allocation-free verification, KV compaction of the result),
+Medusa heads and their assembly, the EAGLE-style assembly, a tree selection and a fused LM head
+with verification from hidden states in all four modes are captured once with preallocated
+outputs and workspaces, replayed three times with unrelated eager work and synchronisations in
+between, and every replay's outputs must equal the eager call's bit for bit (the kernels are
+deterministic: no atomics decide a floating-point sum).  The compacted KV cache is restored from
+a pristine copy before every run, since compaction works in place."""
 
 import numpy as np
 import pytest
@@ -34,6 +36,10 @@ def test_graph_replays_match_eager():
     vi = wl.verify_inputs(w, a["parents"])
     pool = wl.random_pool(seed=32, B=2, C=300)
     lm = wl.lm_head_inputs(seed=33, B=2, N=40, Dm=256, V=3000)
+    hw = wl.custom(seed=35, B=3, V=3001, heads={"H": 3, "Dm": 384, "k": 6})
+    hi = wl.heads_inputs(hw)
+    hh, Wr, Wl = (dev(hi[x], torch.bfloat16) for x in ("h", "W_res", "W_lm"))
+    topo = dev(wl.bfs_tree((6, 3, 2), 40))
 
     P, par, nn = dev(a["prefix_len"]), dev(a["parents"]), dev(a["n_nodes"])
     q, k, v = (dev(a[x], torch.bfloat16) for x in ("q", "k_cache", "v_cache"))
@@ -51,6 +57,10 @@ def test_graph_replays_match_eager():
     ws_vlm = sb.workspace(sb.verify_lm_head_workspace_bytes(2, 40, 256, 3000), "cuda")
     ws_vrj = sb.workspace(sb.verify_lm_head_workspace_bytes(2, 40, 256, 3000, "reject"), "cuda")
     ws_vwk = sb.workspace(sb.verify_lm_head_workspace_bytes(2, 40, 256, 3000, "walk"), "cuda")
+    ws_heads = sb.workspace(sb.medusa_heads_workspace_bytes(3, 3, 384, 3001, 6), "cuda")
+    ws_asmr = sb.workspace(sb.tree_assemble_rows_workspace_bytes(B, N, w.V), "cuda")
+    k0, v0 = k.clone(), v.clone()       # pristine cache; k2 / v2 are compacted in place
+    k2, v2 = k.clone(), v.clone()
     lg = np.random.default_rng(34)
     lunif = dev(lg.random((2, 40), dtype=np.float32))
     ldraft = lg.random((2, 40, 3000)).astype(np.float32) ** 8
@@ -66,6 +76,16 @@ def test_graph_replays_match_eager():
                                   n_nodes=nn, out=o.get("rej"), ws=ws_ver)
         o["walk"] = sb.spec_verify(logits, toks, par, unif, "walk", draft_probs=draft, draft_row=drow,
                                    n_nodes=nn, out=o.get("walk"), ws=ws_walk)
+        o["static"] = sb.spec_verify_static(logits, toks, par, unif, "reject", draft_probs=draft, draft_row=drow,
+                                            n_nodes=nn, out=o.get("static"))
+        kv = o.get("kv", {})
+        kv["P"] = sb.spec_kv_compact(k2, v2, P, o["rej"]["path"], o["rej"]["accept_len"], err=o["rej"]["err"],
+                                     prefix_len_out=kv.get("P"))
+        kv["k"], kv["v"] = k2, v2
+        o["kv"] = kv
+        o["heads"] = sb.spec_medusa_heads(hh, Wr, Wl, 6, out=o.get("heads"), ws=ws_heads)
+        o["asm"] = sb.spec_tree_assemble(o["heads"]["topk_idx"], topo, out=o.get("asm"))
+        o["asmr"] = sb.spec_tree_assemble_rows(draft, par, drow, V=w.V, n_nodes=nn, out=o.get("asmr"), ws=ws_asmr)
         o["sel"] = sb.spec_tree_select(cp, cprob, 64, cand_tokens=ct, cand_row=cr, out=o.get("sel"))
         o["lm"] = sb.spec_lm_head_stats(h, W, lpar, ltok, out=o.get("lm"), ws=ws_lm)
         o["gr"] = sb.spec_verify_greedy_stats(o["lm"]["row_argmax"], ltok, lpar, 3000, out=o.get("gr"))
@@ -80,6 +100,8 @@ def test_graph_replays_match_eager():
     torch.cuda.synchronize()
     ref = snapshot({k: v for k, v in eager.items() if isinstance(v, dict)})
 
+    k2.copy_(k0)
+    v2.copy_(v0)
     outs = run({})                      # the graph's own output buffers, allocated eagerly
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -99,6 +121,8 @@ def test_graph_replays_match_eager():
                         t.fill_(float("nan"))
                     elif isinstance(t, torch.Tensor):
                         t.fill_(-7)
+        k2.copy_(k0)                    # the cache the compaction starts from
+        v2.copy_(v0)
         scratch.uniform_()              # unrelated eager work between replays
         torch.cuda.synchronize()
         g.replay()
