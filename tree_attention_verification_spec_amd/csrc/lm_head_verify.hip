@@ -17,9 +17,10 @@
 // the candidates whose token falls in the tile pick their parent's logit.  Partials go to the
 // workspace, one per (row, 64 W rows).
 // lmhead_stats_wide_kernel (65-128) and lmhead_stats_gemm_kernel (129-4096): every W tile must
-// meet all hidden states, so these cover 256 W rows x 64 columns, or 128 x 128 tiles staged
-// through LDS; the column blocks of one W tile get workgroup ids with the same residue mod 8, so
-// they run on one XCD and read the tile through its L2.  Same partials and gathers.
+// meet all hidden states, so these cover 256 W rows x 64 columns, or 256 W rows x 128 columns
+// with W staged through LDS; the column blocks of one W tile get workgroup ids with the same
+// residue mod 8, so they run on one XCD and read the tile through its L2.  Same partials and
+// gathers.
 // lmhead_merge_kernel: one workgroup per row; block max first, then the partials' sums rescaled
 // by exp(m_j - max) in fp64 (no sequential rescaling), validation of the sequence's tree, and
 // the outputs.
@@ -52,6 +53,16 @@ struct LmPart {       // one 64-token tile of one row
 };
 
 __device__ __forceinline__ bf16x8 ld8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// Raw buffer loads (bounds-checked against the descriptor's byte count; the kernels keep every
+// offset inside it): the descriptor is wave-uniform and lives in scalar registers.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+__device__ __forceinline__ BufRsrc buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ bf16x8 buf_ld8(BufRsrc r, uint32_t lane_off, uint32_t wave_off) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, wave_off, 0));
+}
 
 // Optional output of the stats kernels (REJECT's residual draw needs the row it stops at): the
 // fp32 logits of a 64-token x 64-column tile held in LDS as [token][column] are written to
@@ -384,108 +395,136 @@ __device__ __forceinline__ void wave_tile_epilogue(float (*tw)[kLMaxCols + 1], i
   }
 }
 
-// More than 128 hidden states: a 128 x 128 tile per workgroup (waves in 2 x 2, each 64 W rows x
-// 64 columns), both operands staged through LDS once per workgroup and K step (16-byte global
-// loads for the next step requested before this step's products, two LDS buffers in turn, one
-// barrier per step).  Per 32-wide K step a workgroup moves 16 KB for 64 products instead of the
-// 32 KB the 256-row kernel's waves fetch separately.
-constexpr int kGT = 128;                 // tile edge (W rows and columns)
-constexpr int kGS = 40;                  // LDS row stride in bf16 (32 + 8: rows 80 bytes apart)
+// More than 128 hidden states: 256 W rows x 128 columns per workgroup, waves in 2 x 2, each 128
+// W rows x 64 columns (per 32-wide K step a wave reads 12 fragments for 32 products), two
+// workgroups per CU.  W goes through LDS, the hidden states straight to registers: a fragment
+// load of W puts 16 different rows in each 16 lanes, so each group of four lanes would meet four
+// cache lines and take the load unit four times as long, while the staging loads give each group
+// of four lanes one row's 64 bytes, and the permuted hidden states are already in fragment
+// order.  The staged W tile is stored unpadded, each row's four 16-byte chunks permuted by
+// w_swz(row) so that a fragment read (16 rows, one chunk each) meets distinct banks whether the
+// LDS serves 8 or 16 lanes of a 16-byte read per clock.  Three LDS buffers: the fragments of
+// step s + 1 are read while step s's products run, and one barrier per step separates every
+// write from the reads of the same buffer.
+constexpr int kGT = 128;                 // columns per workgroup
+constexpr int kG2Rows = 256;             // W rows per workgroup
+__device__ __forceinline__ int w_swz(int r) { return ((r >> 2) + 2 * ((r >> 1) & 1)) & 3; }
 
-__global__ __launch_bounds__(kLThreads) void lmhead_stats_gemm_kernel(
+__global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lmhead_stats_gemm_kernel(
     const __bf16* __restrict__ W, const __bf16* __restrict__ Xp, int M, int Dm, int V, int N,
     int nblk, int ntile, int ncb, const int32_t* __restrict__ parents,
     const int32_t* __restrict__ tokens, LmPart* __restrict__ parts, float* __restrict__ gath,
     float* __restrict__ rows) {
-  constexpr size_t kStageBytes = sizeof(__bf16) * 2 * 2 * kGT * kGS;               // [buf][A|B]
-  constexpr size_t kTileBytes = sizeof(float) * 2 * 64 * (kLMaxCols + 1);          // two waves at a time
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kStageBytes > kTileBytes ? kStageBytes : kTileBytes];
-  auto stage = reinterpret_cast<__bf16 (*)[2][kGT][kGS]>(lds);                        // [buf][0 A / 1 B]
+  constexpr int kBufs = 3;
+  constexpr int kStageBytes1 = kG2Rows * 64;                                        // one step's W tile
+  constexpr size_t kTileBytes = sizeof(float) * kLKWaves * 64 * (kLMaxCols + 1);  // a tile per wave
+  constexpr size_t kLds = (size_t)kBufs * kStageBytes1 > kTileBytes ? (size_t)kBufs * kStageBytes1 : kTileBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
   auto tiles = reinterpret_cast<float (*)[64][kLMaxCols + 1]>(lds);
-  constexpr int RB = 4, CBN = 4;
+  constexpr int RB = 8, CBN = 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int wr = wave >> 1, wc = wave & 1;
   const int grp = blockIdx.x / (8 * ncb), rem = blockIdx.x - grp * 8 * ncb;
   const int tidx = grp * 8 + (rem & 7), cblk = rem >> 3;
   if (tidx >= ntile) return;
-  const int row0 = tidx * kGT, col0 = cblk * kGT;
-  // staging: thread t moves chunks q = t and t + 256 of A (row q / 4, k chunk q % 4) and of B
-  // (k chunk q / 128, column q % 128), 16 bytes each
-  const __bf16* ga[2];
-  const __bf16* gb[2];
-  int ar[2], ak[2], bc[2], bk[2];
+  const int row0 = tidx * kG2Rows, col0 = cblk * kGT;
+  const uint32_t row_bytes = (uint32_t)Dm * sizeof(__bf16);
+  const int arow0 = min(row0, V - 1);
+  const BufRsrc wrs = buf_rsrc(W + (size_t)arow0 * Dm, (uint32_t)min(kG2Rows, V - arow0) * row_bytes);
+  const BufRsrc xr = buf_rsrc(Xp, (uint32_t)M * row_bytes);
+  // staging: thread t moves 16-byte slots q = t + 256 j (row q / 4, slot q % 4, which holds the
+  // row's chunk (q % 4) ^ w_swz(row)); LDS address of slot q: 16 q
+  uint32_t aoff[4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int q = threadIdx.x + j * kLThreads;
-    ar[j] = q >> 2;
-    ak[j] = (q & 3) * 8;
-    ga[j] = W + (size_t)min(row0 + ar[j], V - 1) * Dm + ak[j];
-    bk[j] = q >> 7;
-    bc[j] = q & 127;
-    gb[j] = Xp + ((size_t)bk[j] * M + min(col0 + bc[j], M - 1)) * 8;
+  for (int j = 0; j < 4; ++j) {
+    const int q = threadIdx.x + j * kLThreads, r = q >> 2;
+    aoff[j] = (uint32_t)(min(row0 + r, V - 1) - arow0) * row_bytes + 16 * ((q & 3) ^ w_swz(r));
   }
-  bf16x8 ra[2], rb[2];
-  auto load = [&](int s) {
+  // B fragments of this wave's column block cb: 16 bytes at Xp[(4 s + lg) M + column]
+  uint32_t boff[CBN];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      ra[j] = ld8(ga[j] + (size_t)s * 32);
-      rb[j] = ld8(gb[j] + (size_t)s * 4 * M * 8);
-    }
+  for (int cb = 0; cb < CBN; ++cb) boff[cb] = (uint32_t)(lg * M + min(col0 + wc * 64 + cb * 16 + l16, M - 1)) * 16;
+  const int steps = Dm / 32;
+  bf16x8 rav[4];
+  auto load_a = [&](int s) {
+    const uint32_t so = (uint32_t)min(s, steps - 1) * 64;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rav[j] = buf_ld8(wrs, aoff[j], so);
   };
-  auto store = [&](int buf) {
+  auto store_a = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      *reinterpret_cast<bf16x8*>(&stage[buf][0][ar[j]][ak[j]]) = ra[j];
-      *reinterpret_cast<bf16x8*>(&stage[buf][1][bc[j]][bk[j] * 8]) = rb[j];
-    }
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<bf16x8*>(lds + buf * kStageBytes1 + (threadIdx.x + j * kLThreads) * 16) = rav[j];
+  };
+  bf16x8 fa[RB], fb[2][CBN];
+  auto fetch_b = [&](int slot, int s) {
+    const uint32_t so = (uint32_t)min(s, steps - 1) * 64 * (uint32_t)M;
+#pragma unroll
+    for (int cb = 0; cb < CBN; ++cb) fb[slot][cb] = buf_ld8(xr, boff[cb], so);
+  };
+  auto read_a = [&](int rb, int buf) {
+    const int r = wr * 128 + rb * 16 + l16;
+    fa[rb] = *reinterpret_cast<const bf16x8*>(lds + buf * kStageBytes1 + r * 64 + 16 * (lg ^ w_swz(r)));
   };
   f32x4 acc[RB][CBN];
 #pragma unroll
-  for (int i = 0; i < RB; ++i)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < CBN; ++cb) acc[i][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Step s: the registers (step s + 1, requested a whole step earlier) go to the other LDS
-  // buffer first, then step s + 2 is requested, then step s's products run.  Storing before
-  // requesting keeps the wait for the stored loads exact (the memory counter drains in issue
-  // order, so a wait issued behind newer loads would wait for those too).
-  const int steps = Dm / 32;
-  load(0);
-  store(0);
-  load(min(1, steps - 1));
-  __syncthreads();
-  for (int s = 0; s < steps; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < steps) store(buf ^ 1);
-    if (s + 2 < steps) load(s + 2);
-    bf16x8 fa[RB], fb[CBN];
+    for (int cb = 0; cb < CBN; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Step s (LDS buffer of step t: t % 3): W of step s + 2 (in registers since step s - 1) to its
+  // buffer, W of step s + 3 and the B fragments of step s + 1 requested, then step s's products,
+  // row block by row block, each followed by the read of that block's fragment for step s + 1
+  // into the register it frees.  The buffer written at step s was last read during step s - 2,
+  // before the barrier that ends step s - 1; the one read at step s was written at step s - 1,
+  // before that same barrier.  Past the last step the loads and LDS traffic repeat in-bounds data
+  // that is never used.
+  auto step = [&](int s, int slot) __attribute__((always_inline)) {
+    store_a((s + 2) % kBufs);
+    load_a(s + 3);
+    fetch_b(slot ^ 1, s + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const int nb = (s + 1) % kBufs;
 #pragma unroll
-    for (int i = 0; i < RB; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(&stage[buf][0][wr * 64 + i * 16 + l16][8 * lg]);
+    for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-    for (int cb = 0; cb < CBN; ++cb)
-      fb[cb] = *reinterpret_cast<const bf16x8*>(&stage[buf][1][wc * 64 + cb * 16 + l16][8 * lg]);
+      for (int cb = 0; cb < CBN; ++cb)
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[rb], fb[slot][cb], acc[rb][cb], 0, 0, 0);
+      read_a(rb, nb);
+    }
 #pragma unroll
-    for (int cb = 0; cb < CBN; ++cb)
-#pragma unroll
-      for (int i = 0; i < RB; ++i)
-        acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[cb], acc[i][cb], 0, 0, 0);
-    __syncthreads();
-  }
-  // each wave's 64 x 64 tile to LDS (over the staging buffers, after the last barrier), two
-  // waves at a time so that the block stays at the staging size (three workgroups per CU)
-  float (*tw)[kLMaxCols + 1] = tiles[wave & 1];
-  for (int half = 0; half < 2; ++half) {
-    if ((wave >> 1) == half) {
-#pragma unroll
-      for (int i = 0; i < RB; ++i)
-#pragma unroll
-        for (int cb = 0; cb < CBN; ++cb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) tw[i * 16 + 4 * lg + e][cb * 16 + l16] = acc[i][cb][e];
+    for (int i = 0; i < RB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);    // four products
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // one LDS read
     }
     __syncthreads();
-    if ((wave >> 1) == half) wave_tile_epilogue(tw, row0 + wr * 64, col0 + wc * 64, M, V, N, nblk, parents,
-                                                tokens, parts, gath, rows);
+  };
+  load_a(0);
+  store_a(0);
+  load_a(1);
+  store_a(1);
+  load_a(2);
+  fetch_b(0, 0);
+  __syncthreads();
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) read_a(rb, 0);
+  for (int s = 0; s < steps; s += 2) {
+    step(s, 0);
+    step(s + 1, 1);
+  }
+  // the wave's 128 x 64 tile to LDS (over the staging buffers) and reduced 64 rows at a time
+  float (*tw)[kLMaxCols + 1] = tiles[wave];
+#pragma unroll
+  for (int hr = 0; hr < 2; ++hr) {
+#pragma unroll
+    for (int rb = 0; rb < RB / 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < CBN; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tw[rb * 16 + 4 * lg + e][cb * 16 + l16] = acc[hr * RB / 2 + rb][cb][e];
+    __syncthreads();
+    wave_tile_epilogue(tw, row0 + wr * 128 + hr * 64, col0 + wc * 64, M, V, N, nblk, parents, tokens, parts,
+                       gath, rows);
     __syncthreads();
   }
 }
@@ -1166,7 +1205,7 @@ void launch_lm(const __bf16* X, const __bf16* Wb, const int32_t* parents, const 
   const char* nm = "lm_head_stats";
   const int nb = L.nblk;
   if (M > 2 * kLMaxCols) {
-    const int ntile = (V + kGT - 1) / kGT, ncb2 = (M + kGT - 1) / kGT;
+    const int ntile = (V + kG2Rows - 1) / kG2Rows, ncb2 = (M + kGT - 1) / kGT;
     const dim3 gg((unsigned)((ntile + 7) / 8 * 8 * ncb2));
     launch(nm, lmhead_stats_gemm_kernel, gg, blk, s, Wb, Xp, M, Dm, V, N, nb, ntile, ncb2, parents, tokens, parts, gath, rows);
   } else if (M > kLMaxCols) {
