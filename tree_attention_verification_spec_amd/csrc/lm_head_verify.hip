@@ -54,6 +54,12 @@ struct LmPart {       // one 64-token tile of one row
 
 __device__ __forceinline__ bf16x8 ld8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
+// Column stride of the fragment-ordered hidden states: M rounded up to 8 columns, so that every
+// 16-lane run of a B fragment load starts on a 128-byte line (with a stride of M = 63 columns
+// three of the four runs straddled lines; 243 -> 235 us at 63 rows).  The pad columns are never
+// written or read.
+__host__ __device__ constexpr int xp_stride(int M) { return (M + 7) & ~7; }
+
 // Raw buffer loads (bounds-checked against the descriptor's byte count; the kernels keep every
 // offset inside it): the descriptor is wave-uniform and lives in scalar registers.
 typedef __amdgpu_buffer_rsrc_t BufRsrc;
@@ -103,12 +109,14 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_kernel(
 #pragma unroll
   for (int rb = 0; rb < kLRB; ++rb)
     arow[rb] = W + (size_t)min(row0 + rb * 16 + l16, V - 1) * Dm + kbeg + 8 * lg;
-  // Xp is the hidden states in fragment order, element (col, k) at ((k / 8) M + col) 8 + k % 8:
-  // a B fragment (lane l: column l % 16, k = 8 (l / 16) + [0, 8)) is four 256-byte runs
+  // Xp is the hidden states in fragment order, element (col, k) at ((k / 8) Mp + col) 8 + k % 8
+  // with Mp = xp_stride(M): a B fragment (lane l: column l % 16, k = 8 (l / 16) + [0, 8)) is four
+  // 256-byte runs
+  const int Mp = xp_stride(M);
   const __bf16* bptr[CBN];
 #pragma unroll
   for (int cb = 0; cb < CBN; ++cb)
-    bptr[cb] = Xp + ((size_t)(kbeg / 8 + lg) * M + min(col0 + cb * 16 + l16, M - 1)) * 8;
+    bptr[cb] = Xp + ((size_t)(kbeg / 8 + lg) * Mp + min(col0 + cb * 16 + l16, M - 1)) * 8;
   f32x4 acc[kLRB][CBN];
 #pragma unroll
   for (int rb = 0; rb < kLRB; ++rb)
@@ -132,7 +140,7 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_kernel(
 #pragma unroll
     for (int cb = 0; cb < CBN; ++cb)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) g.b[cb][h] = ld8(bptr[cb] + (size_t)min(s + h, steps - 1) * 32 * M);
+      for (int h = 0; h < 2; ++h) g.b[cb][h] = ld8(bptr[cb] + (size_t)min(s + h, steps - 1) * 32 * Mp);
   };
   auto products = [&](const Frags& g, int s) {
 #pragma unroll
@@ -264,9 +272,10 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_wide_kernel(
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
     arow[rb] = W + (size_t)min(wrow0 + rb * 16 + l16, V - 1) * Dm + 8 * lg;
+  const int Mp = xp_stride(M);
   const __bf16* bptr[CBN];
 #pragma unroll
-  for (int cb = 0; cb < CBN; ++cb) bptr[cb] = Xp + ((size_t)lg * M + min(col0 + cb * 16 + l16, M - 1)) * 8;
+  for (int cb = 0; cb < CBN; ++cb) bptr[cb] = Xp + ((size_t)lg * Mp + min(col0 + cb * 16 + l16, M - 1)) * 8;
   f32x4 acc[RB][CBN];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -287,7 +296,7 @@ __global__ __launch_bounds__(kLThreads) void lmhead_stats_wide_kernel(
 #pragma unroll
     for (int cb = 0; cb < CBN; ++cb)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) g.b[cb][h] = ld8(bptr[cb] + (size_t)min(s + h, steps - 1) * 32 * M);
+      for (int h = 0; h < 2; ++h) g.b[cb][h] = ld8(bptr[cb] + (size_t)min(s + h, steps - 1) * 32 * Mp);
   };
   auto products = [&](const Frags& g, int s) {
 #pragma unroll
@@ -402,13 +411,15 @@ __device__ __forceinline__ void wave_tile_epilogue(float (*tw)[kLMaxCols + 1], i
 // cache lines and take the load unit four times as long, while the staging loads give each group
 // of four lanes one row's 64 bytes, and the permuted hidden states are already in fragment
 // order.  The staged W tile is stored unpadded, each row's four 16-byte chunks permuted by
-// w_swz(row) so that a fragment read (16 rows, one chunk each) meets distinct banks whether the
-// LDS serves 8 or 16 lanes of a 16-byte read per clock.  Three LDS buffers: the fragments of
+// w_swz(row) = (row / 2) % 4, with which a fragment read (16 rows, one chunk each) takes the
+// LDS's minimum of four clocks per instruction (measured with the bank-conflict counter; rows
+// 80 bytes apart, unpermuted 64-byte rows and the other XOR permutations of the chunk index by
+// two row bits take eight).  Three LDS buffers: the fragments of
 // step s + 1 are read while step s's products run, and one barrier per step separates every
 // write from the reads of the same buffer.
 constexpr int kGT = 128;                 // columns per workgroup
 constexpr int kG2Rows = 256;             // W rows per workgroup
-__device__ __forceinline__ int w_swz(int r) { return ((r >> 2) + 2 * ((r >> 1) & 1)) & 3; }
+__device__ __forceinline__ int w_swz(int r) { return (r >> 1) & 3; }
 
 __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lmhead_stats_gemm_kernel(
     const __bf16* __restrict__ W, const __bf16* __restrict__ Xp, int M, int Dm, int V, int N,
@@ -432,7 +443,8 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   const uint32_t row_bytes = (uint32_t)Dm * sizeof(__bf16);
   const int arow0 = min(row0, V - 1);
   const BufRsrc wrs = buf_rsrc(W + (size_t)arow0 * Dm, (uint32_t)min(kG2Rows, V - arow0) * row_bytes);
-  const BufRsrc xr = buf_rsrc(Xp, (uint32_t)M * row_bytes);
+  const int Mp = xp_stride(M);
+  const BufRsrc xr = buf_rsrc(Xp, (uint32_t)Mp * row_bytes);
   // staging: thread t moves 16-byte slots q = t + 256 j (row q / 4, slot q % 4, which holds the
   // row's chunk (q % 4) ^ w_swz(row)); LDS address of slot q: 16 q
   uint32_t aoff[4];
@@ -441,10 +453,10 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     const int q = threadIdx.x + j * kLThreads, r = q >> 2;
     aoff[j] = (uint32_t)(min(row0 + r, V - 1) - arow0) * row_bytes + 16 * ((q & 3) ^ w_swz(r));
   }
-  // B fragments of this wave's column block cb: 16 bytes at Xp[(4 s + lg) M + column]
+  // B fragments of this wave's column block cb: 16 bytes at Xp[(4 s + lg) Mp + column]
   uint32_t boff[CBN];
 #pragma unroll
-  for (int cb = 0; cb < CBN; ++cb) boff[cb] = (uint32_t)(lg * M + min(col0 + wc * 64 + cb * 16 + l16, M - 1)) * 16;
+  for (int cb = 0; cb < CBN; ++cb) boff[cb] = (uint32_t)(lg * Mp + min(col0 + wc * 64 + cb * 16 + l16, M - 1)) * 16;
   const int steps = Dm / 32;
   bf16x8 rav[4];
   auto load_a = [&](int s) {
@@ -459,7 +471,7 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   };
   bf16x8 fa[RB], fb[2][CBN];
   auto fetch_b = [&](int slot, int s) {
-    const uint32_t so = (uint32_t)min(s, steps - 1) * 64 * (uint32_t)M;
+    const uint32_t so = (uint32_t)min(s, steps - 1) * 64 * (uint32_t)Mp;
 #pragma unroll
     for (int cb = 0; cb < CBN; ++cb) fb[slot][cb] = buf_ld8(xr, boff[cb], so);
   };
@@ -529,14 +541,15 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   }
 }
 
-// The hidden states [M, Dm] into fragment order (see lmhead_stats_kernel), 16 bytes per thread.
+// The hidden states [M, Dm] into fragment order (see lmhead_stats_kernel; column stride
+// xp_stride(M)), 16 bytes per thread.
 __global__ __launch_bounds__(kLThreads) void lmhead_xperm_kernel(const __bf16* __restrict__ X, int M, int Dm,
                                                                  __bf16* __restrict__ Xp) {
   const int id = blockIdx.x * kLThreads + threadIdx.x;     // (k / 8) * M + col
   const int K8 = Dm / 8;
   if (id >= K8 * M) return;
   const int k8 = id / M, col = id - k8 * M;
-  *reinterpret_cast<bf16x8*>(Xp + (size_t)id * 8) = ld8(X + (size_t)col * Dm + (size_t)k8 * 8);
+  *reinterpret_cast<bf16x8*>(Xp + ((size_t)k8 * xp_stride(M) + col) * 8) = ld8(X + (size_t)col * Dm + (size_t)k8 * 8);
 }
 
 __global__ __launch_bounds__(kLThreads) void lmhead_merge_kernel(
@@ -1156,7 +1169,7 @@ LmLayout lm_layout(int B, int N, int V, int Dm) {
   L.parts = 0;
   L.gath = align_up(M * L.nblk * sizeof(LmPart), 256);
   L.xperm = L.gath + align_up(M * sizeof(float), 256);
-  L.total = L.xperm + align_up(M * (size_t)Dm * 2, 256);
+  L.total = L.xperm + align_up((size_t)xp_stride((int)M) * Dm * 2, 256);
   return L;
 }
 }  // namespace
