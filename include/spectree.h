@@ -24,8 +24,9 @@
  *     checked first.  A sequence with an error gets the documented neutral outputs.
  *   - Workspaces: query the size with the matching *_workspace() function (0 for a shape the
  *     call does not support: the query applies the call's size checks).  A workspace needs
- *     no initialisation: every call writes each workspace byte it later reads (no call keeps
- *     cross-workgroup counters), so one workspace can be reused by back-to-back calls on one
+ *     no initialisation: every call writes each workspace byte it later reads (the only
+ *     cross-workgroup counters, those of spec_verify's WALK mode, are zeroed by an earlier
+ *     kernel of the same call), so one workspace can be reused by back-to-back calls on one
  *     stream.  Calls that run concurrently need distinct workspaces.
  *   - Codes of the spec_dtype and spec_mode enumerations are passed as plain int arguments
  *     (`dtype`, `mode`), so that any value a caller passes is checked, never assumed valid.

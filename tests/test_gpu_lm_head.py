@@ -77,7 +77,8 @@ def run_both(inp, n_nodes=None, what=""):
 @pytest.mark.parametrize("B,N,Dm,V", [(1, 1, 128, 1), (1, 5, 128, 37), (1, 16, 128, 64), (1, 17, 256, 65),
                                       (2, 16, 256, 1000), (3, 11, 128, 5000), (4, 16, 384, 2048),
                                       (1, 64, 512, 4099), (1, 65, 128, 700), (2, 256, 256, 1500),
-                                      (8, 127, 512, 4099), (16, 127, 256, 3000)])
+                                      (8, 127, 512, 4099), (16, 127, 256, 3000), (3, 43, 128, 1000),
+                                      (16, 256, 128, 700)])
 def test_small(B, N, Dm, V):
     inp = wl.lm_head_inputs(seed=40 + B + N + V, B=B, N=N, Dm=Dm, V=V)
     run_both(inp, what=f"small {B}x{N} Dm{Dm} V{V}")

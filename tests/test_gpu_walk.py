@@ -70,6 +70,18 @@ def test_small(case):
     _check(wl.custom(seed=6000 + case, **SMALL[case]))
 
 
+@pytest.mark.parametrize("parts,spin", [(2, None), (5, None), (16, None), (7, 1), (16, 1)])
+def test_split_chain(tune, parts, spin):
+    """A node's chain split over several workgroups (forced counts; at 16 some workgroups of a
+    70000-token row have no step of it), and with a one-poll wait, on which workgroup 0 finishes
+    the chain alone: the same decisions as the oracle.  Wide sibling sets (6, 3, 1 per level)
+    give 14 nodes with several children, so 16 workgroups each still fit the GPU at once."""
+    tune(walk_parts=parts, **({"walk_spin": spin} if spin else {}))
+    w = wl.custom(seed=6200 + parts + (spin or 0), B=2, N=40, V=70000, tree=("bfs", (6, 3, 1)), sigma_logits=0.5)
+    ref, ex = _check(w)
+    print(f"walk_parts={parts} walk_spin={spin}: mean accept_len {ref['accept_len'].mean():.2f}, excused {ex}")
+
+
 def test_max_depth_and_errors():
     """Structural errors, a sibling on another draft row, and a tight max_depth."""
     w = wl.custom(seed=6100, B=12, N=30, V=900, tree=("random", 4))

@@ -93,7 +93,7 @@ spec_status launch_status();
 enum Knob {
   kKnobAttnCB, kKnobAttnWaves, kKnobAttnSplits, kKnobAttnLpt, kKnobAttnPrio, kKnobAttnLazy,
   kKnobVerifyChunk, kKnobVerifyStoreW, kKnobVerifyRowsList,
-  kKnobResRowBlocks, kKnobLmRowBlocks,
+  kKnobResRowBlocks, kKnobLmRowBlocks, kKnobWalkParts, kKnobWalkSpin,
   kKnobCount
 };
 int tuning(Knob k, int fallback);

@@ -27,7 +27,10 @@ int spec_prof_read(const char* name, double* total_ms, int64_t* launches);
  * reference max with every new row maximum; > 0: only when it grows by more than that many
  * log2 units), "verify_chunk" (4096, 8192,
  * 16384), "verify_store_w" (0, 1), "verify_rows_list" (0, 1), "res_rowblocks" (1, 2, 4),
- * "lm_rowblocks" (4, 8); a negative value removes the override.  Workspace queries made while
+ * "lm_rowblocks" (4, 8), "walk_parts" (1-16 workgroups per node of the
+ * WALK chain), "walk_spin" (>= 1 polls of a node's counter before a workgroup of a split chain
+ * stops waiting; a small value exercises the path on which workgroup 0 finishes alone); a
+ * negative value removes the override.  Workspace queries made while
  * an override is set size the workspace for the forced shape.  Returns 0, or -1 for an unknown
  * name.  Not thread-safe with respect to calls in flight on other host threads. */
 int spec_internal_tune(const char* name, int value);

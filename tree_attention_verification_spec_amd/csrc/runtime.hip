@@ -46,7 +46,7 @@ const bool g_knobs_ready = init_knobs();
 const char* const kKnobNames[kKnobCount] = {
   "attn_cb", "attn_waves", "attn_splits", "attn_lpt", "attn_prio", "attn_lazy",
   "verify_chunk", "verify_store_w", "verify_rows_list",
-  "res_rowblocks", "lm_rowblocks",
+  "res_rowblocks", "lm_rowblocks", "walk_parts", "walk_spin",
 };
 
 }  // namespace

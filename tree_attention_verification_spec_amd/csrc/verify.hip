@@ -105,6 +105,10 @@ struct VerifyArgs {
   double* wc;           // [B, N] walk: child c is tested against relu(T_p - wc D) / wf
   double* wf;           // [B, N]
   double* wend;         // [B, N] walk: residual scale after every child of node p is rejected
+  int wk;               // walk: workgroups per node (1: one workgroup does the whole chain)
+  int wspin;            // walk, wk > 1: polls of a node's counter before a workgroup stops waiting
+  int32_t* wsync;       // [B, N] walk, wk > 1: arrivals per node (zeroed by the row pass)
+  double* wpart;        // [B, N, wk, 2] walk, wk > 1: each workgroup's partial sums of a pass
 };
 
 // ------------------------------------------------------------------ reductions
@@ -280,6 +284,7 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(VerifyArgs a) {
   // only rows of nodes that some node names as its parent are read
   const int named = (t >= 1 && t < n && par == p) ? 1 : 0;
   if (!__syncthreads_or(named)) return;
+  if (a.wsync && c == 0 && t == 0) a.wsync[(size_t)b * a.N + p] = 0;
   float x[PER];
   row_load<VEC>(a, b, p, c, x);
   row_reduce<VEC>(a, b, p, c, x);
@@ -348,6 +353,7 @@ __global__ __launch_bounds__(kThreads) void rows_listed_kernel(VerifyArgs a) {
   const int b = idx / a.N;
   const int p = idx - b * a.N;
   const int c = it - (it / a.CR) * a.CR;
+  if (a.wsync && c == 0 && threadIdx.x == 0) a.wsync[idx] = 0;
   float x[PER];
   row_load<VEC>(a, b, p, c, x);
   row_reduce<VEC>(a, b, p, c, x);
@@ -790,20 +796,33 @@ struct Chain {
     }
   }
 
+  // the steps s0, s0 + ds, s0 + 2 ds, ... of kStep tokens each
   template <bool FIRST, bool BUILD>
   static __device__ void stream(const VerifyArgs& a, const float* row, const float* drow, float M, double cS,
-                                double& fp, double& z, int& cnt, float2* list, int* list_n) {
+                                double& fp, double& z, int& cnt, float2* list, int* list_n, int s0, int ds) {
     float xa[PER], da[PER], xb[PER], db[PER];
-    load(a, row, drow, 0, xa, da);
-    for (int v0 = 0; v0 < a.V; v0 += 2 * kStep) {
-      load(a, row, drow, v0 + kStep, xb, db);   // in flight during the reduce
+    const int v1 = ds * kStep;
+    load(a, row, drow, s0 * kStep, xa, da);
+    for (int v0 = s0 * kStep; v0 < a.V; v0 += 2 * v1) {
+      load(a, row, drow, v0 + v1, xb, db);   // in flight during the reduce
       reduce<FIRST, BUILD>(a, v0, xa, da, M, cS, fp, z, cnt, list, list_n);
-      if (v0 + kStep >= a.V) break;
-      load(a, row, drow, v0 + 2 * kStep, xa, da);
-      reduce<FIRST, BUILD>(a, v0 + kStep, xb, db, M, cS, fp, z, cnt, list, list_n);
+      if (v0 + v1 >= a.V) break;
+      load(a, row, drow, v0 + 2 * v1, xa, da);
+      reduce<FIRST, BUILD>(a, v0 + v1, xb, db, M, cS, fp, z, cnt, list, list_n);
     }
   }
 };
+
+// Several workgroups per node (a.wk > 1, chosen on the host so that every workgroup that can
+// have work is resident at once, one per CU): workgroup q of node p streams the steps q, q + wk,
+// ... of each pass, keeps its own LDS list, and after every pass adds its partial sums to the
+// node's slots and its arrival to the node's counter (release); each then waits for all wk
+// arrivals (acquire) and sums the partials in workgroup order, so every workgroup of the node
+// derives the same c_(j+1).  The wait is bounded: a workgroup that runs out of it (a sibling
+// that is not resident) leaves, except workgroup 0, which finishes the chain alone over the
+// whole row; the results are the same up to the order of the fp64 sums.
+constexpr int kWalkSpinMax = 1 << 14;   // polls of the counter (each followed by a short sleep);
+                                        // the tuning override walk_spin sets another
 
 template <int THREADS, int PER, int VEC, int DM>
 __global__ __launch_bounds__(THREADS) void walk_chain_kernel(VerifyArgs a) {
@@ -815,7 +834,11 @@ __global__ __launch_bounds__(THREADS) void walk_chain_kernel(VerifyArgs a) {
   __shared__ int s_n;
   __shared__ float s_M;
   __shared__ double s_S;
-  const int b = blockIdx.x / a.N, p = blockIdx.x - b * a.N;
+  __shared__ double s_fp, s_z;
+  __shared__ int s_ok;
+  const int K = a.wk;
+  const int node = blockIdx.x / K, part = blockIdx.x - node * K;
+  const int b = node / a.N, p = node - b * a.N;
   const int t = threadIdx.x, lane = t & (kWave - 1), wv = t >> 6;
   const int n = a.n_nodes ? a.n_nodes[b] : a.N;
   if (n < 1 || n > a.N || p >= n) return;
@@ -835,7 +858,7 @@ __global__ __launch_bounds__(THREADS) void walk_chain_kernel(VerifyArgs a) {
   if (kid) s_kids[off + __popcll(bal & ((1ull << lane) - 1))] = i;
   __syncthreads();
   if (k == 0) return;
-  if (t == 0) {
+  if (t == 0 && part == 0) {
     a.wc[base + s_kids[0]] = 0.0;
     a.wf[base + s_kids[0]] = 1.0;
     if (k == 1) a.wend[base + p] = 1.0;
@@ -857,46 +880,89 @@ __global__ __launch_bounds__(THREADS) void walk_chain_kernel(VerifyArgs a) {
   const int r = min(max(a.draft_row[base + s_kids[0]], 0), a.R - 1);
   const float* row = a.logits + (base + p) * a.V;
   const float* drow = a.draft + ((size_t)b * a.R + r) * a.Vd;
+  int parts = K;          // workgroups sharing the passes (1 once this one works alone)
   double cj = 1.0, zS = 0.0;               // zS: sum of e over tokens with D = 0
-  int listed = -1;        // entries of s_list once it holds every token that can still add
-  int prev = INT_MAX;     // tokens with D != 0 that added something in the previous pass
+  int listed = -1;        // entries of s_list once it holds every token (of this workgroup's
+                          // steps) that can still add
+  int prev = INT_MAX;     // this workgroup's tokens with D != 0 that added in the previous pass
+  bool zdone = false;     // zS holds the whole row's sum
   for (int j = 1; j < k; ++j) {
     const double cS = cj * S;
-    double fS;
+    double fp = 0.0, z = 0.0;
     if (listed < 0) {
       const bool build = prev <= kChainCap;
       if (t == 0) s_n = 0;
       __syncthreads();
-      double fp = 0.0, z = 0.0;
       int cnt = 0;
-      if (j == 1) {
-        if (build) CH::template stream<true, true>(a, row, drow, M, cS, fp, z, cnt, s_list, &s_n);
-        else CH::template stream<true, false>(a, row, drow, M, cS, fp, z, cnt, s_list, &s_n);
-        zS = CH::sum(z, s_red);
+      const int s0 = parts > 1 ? part : 0;
+      if (!zdone) {
+        if (build) CH::template stream<true, true>(a, row, drow, M, cS, fp, z, cnt, s_list, &s_n, s0, parts);
+        else CH::template stream<true, false>(a, row, drow, M, cS, fp, z, cnt, s_list, &s_n, s0, parts);
+        z = CH::sum(z, s_red);
       } else {
-        if (build) CH::template stream<false, true>(a, row, drow, M, cS, fp, z, cnt, s_list, &s_n);
-        else CH::template stream<false, false>(a, row, drow, M, cS, fp, z, cnt, s_list, &s_n);
+        if (build) CH::template stream<false, true>(a, row, drow, M, cS, fp, z, cnt, s_list, &s_n, s0, parts);
+        else CH::template stream<false, false>(a, row, drow, M, cS, fp, z, cnt, s_list, &s_n, s0, parts);
       }
-      fS = zS + CH::sum(fp, s_red);
+      fp = CH::sum(fp, s_red);
       prev = (int)CH::sum((double)cnt, s_red);
       if (build) listed = prev;
     } else {
-      double fp = 0.0;
       for (int e = t; e < listed; e += THREADS) {
         const float2 ed = s_list[e];
         const double q = __builtin_fma(-cS, (double)ed.y, (double)ed.x);
         fp += q > 0.0 ? q : 0.0;
       }
-      fS = zS + CH::sum(fp, s_red);
+      fp = CH::sum(fp, s_red);
     }
-    const double f = fS * invS;
-    if (t == 0) {
+    if (parts > 1) {
+      if (t == 0) {
+        double* slot = a.wpart + ((size_t)node * K + part) * 2;
+        __hip_atomic_store(slot, fp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(slot + 1, z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(a.wsync + node, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        const int target = j * K;
+        int polls = 0;
+        bool ok = false;
+        while (!(ok = __hip_atomic_load(a.wsync + node, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) &&
+               ++polls < a.wspin)
+          __builtin_amdgcn_s_sleep(8);
+        double sf = 0.0, sz = 0.0;
+        if (ok) {
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+          for (int q = 0; q < K; ++q) {
+            const double* o = a.wpart + ((size_t)node * K + q) * 2;
+            sf += __hip_atomic_load(o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sz += __hip_atomic_load(o + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+        s_fp = sf;
+        s_z = sz;
+        s_ok = ok;
+      }
+      __syncthreads();
+      if (!s_ok) {
+        if (part != 0) return;
+        parts = 1;            // workgroup 0 redoes this pass, and the rest, over the whole row
+        listed = -1;
+        prev = INT_MAX;
+        --j;
+        continue;
+      }
+      fp = s_fp;
+      z = s_z;
+    }
+    if (!zdone) {
+      zS = z;
+      zdone = true;
+    }
+    const double f = (zS + fp) * invS;
+    if (t == 0 && part == 0) {
       a.wc[base + s_kids[j]] = cj;
       a.wf[base + s_kids[j]] = f;
     }
     cj += f;
   }
-  if (t == 0) a.wend[base + p] = cj;
+  if (t == 0 && part == 0) a.wend[base + p] = cj;
 }
 
 template <int THREADS, int PER>
@@ -1348,9 +1414,24 @@ __global__ __launch_bounds__(kWave) void select_wave_kernel(VerifyArgs a) {
 
 struct VerifyLayout {
   int RC, CR, CS, C;
+  int wk;               // WALK: workgroups per node
   bool store_w, listed;
-  size_t rowparts, plans, bparts, weights, row_list, row_count, walk, total;
+  size_t rowparts, plans, bparts, weights, row_list, row_count, walk, wsync, wpart, total;
 };
+
+// WALK: workgroups per node.  Several only when every workgroup that can have work is resident
+// at once (one 1024-thread workgroup per CU, kWalkResident of the 256 CUs), counting the most
+// nodes that can have two children, (N - 1) / 2 per sequence; at most one per 8K-token step of
+// the row.  The tuning override walk_parts forces a count (1-16).
+constexpr int kWalkMaxParts = 16;
+constexpr int kWalkResident = 240;
+constexpr int kWalkStep = 1024 * 8;     // tokens per streaming step of the chain
+int walk_parts(int B, int N, int V) {
+  const long long multi = (long long)B * std::max(1, (N - 1) / 2);
+  const int steps = (V + kWalkStep - 1) / kWalkStep;
+  const int k = (int)std::min<long long>(std::min<long long>(kWalkMaxParts, kWalkResident / multi), steps);
+  return std::max(1, std::min(tuning(kKnobWalkParts, k), kWalkMaxParts));
+}
 
 // The listed row pass pays one more launch, so it is used from this many (sequence, node,
 // chunk) items of the plain grid up (the tuning override verify_rows_list forces either path).
@@ -1399,6 +1480,10 @@ VerifyLayout layout(int B, int N, int V, bool packed = false) {
   L.row_list = take((size_t)B * N * sizeof(int32_t));
   L.row_count = take(sizeof(int32_t));
   L.walk = take((size_t)3 * B * N * sizeof(double));
+  L.wk = walk_parts(B, N, V);
+  // sized for kWalkMaxParts whatever wk is, so that the size grows with B
+  L.wsync = take((size_t)B * N * sizeof(int32_t));
+  L.wpart = take((size_t)B * N * kWalkMaxParts * 2 * sizeof(double));
   const bool fits = (size_t)B * N <= (size_t)kListMax;
   L.listed = fits && tuning(kKnobVerifyRowsList, (size_t)B * N * L.CR >= kListMinItems ? 1 : 0) != 0;
   L.total = off;
@@ -1450,6 +1535,12 @@ spec_status run_verify(const float* target_logits, const float* draft_probs, con
   a.wc = reinterpret_cast<double*>(w + L.walk);
   a.wf = a.wc + (size_t)B * N;
   a.wend = a.wf + (size_t)B * N;
+  a.wk = L.wk;
+  a.wspin = std::max(1, tuning(kKnobWalkSpin, kWalkSpinMax));
+  const bool split = mode == SPEC_VERIFY_WALK && L.wk > 1;
+  a.wsync = split ? reinterpret_cast<int32_t*>(w + L.wsync) : nullptr;
+  a.wpart = split ? reinterpret_cast<double*>(w + L.wpart) : nullptr;
+  if (!split) a.wk = 1;
 
   const dim3 blk(kThreads);
   const dim3 grid_rows((unsigned)((size_t)L.CR * N * B));
@@ -1481,7 +1572,7 @@ spec_status run_verify(const float* target_logits, const float* draft_probs, con
   if (mode == SPEC_VERIFY_WALK) {
     // 16-byte draft loads when the draft rows are the target vocabulary and aligned like the logits
     const bool dvec = draft_probs && !t2d && Vd % 4 == 0 && (reinterpret_cast<uintptr_t>(draft_probs) & 15) == 0;
-    launch_chain<1024, 8>(a, dim3((unsigned)((size_t)B * N)), vec4, dvec, s);
+    launch_chain<1024, 8>(a, dim3((unsigned)((size_t)B * N * a.wk)), vec4, dvec, s);
   }
   // the draw: one wave per sequence when the weights are stored and a wave holds the chunks
   const bool wave_draw = a.weights && L.C <= kWave;
