@@ -884,7 +884,11 @@ __global__ __launch_bounds__(THREADS) void walk_chain_kernel(VerifyArgs a) {
   double cj = 1.0, zS = 0.0;               // zS: sum of e over tokens with D = 0
   int listed = -1;        // entries of s_list once it holds every token (of this workgroup's
                           // steps) that can still add
-  int prev = INT_MAX;     // this workgroup's tokens with D != 0 that added in the previous pass
+  // this workgroup's tokens with D != 0 that added in the previous pass; before the first, the
+  // tokens of its steps, so the list is built at once when it can hold all of them
+  const int row_steps = (a.V + CH::kStep - 1) / CH::kStep;
+  const int my_steps = K > 1 ? (part < row_steps ? (row_steps - part + K - 1) / K : 0) : row_steps;
+  int prev = (long long)my_steps * CH::kStep <= kChainCap ? my_steps * CH::kStep : INT_MAX;
   bool zdone = false;     // zS holds the whole row's sum
   for (int j = 1; j < k; ++j) {
     const double cS = cj * S;
@@ -915,29 +919,37 @@ __global__ __launch_bounds__(THREADS) void walk_chain_kernel(VerifyArgs a) {
       fp = CH::sum(fp, s_red);
     }
     if (parts > 1) {
-      if (t == 0) {
-        double* slot = a.wpart + ((size_t)node * K + part) * 2;
-        __hip_atomic_store(slot, fp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(slot + 1, z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_add(a.wsync + node, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        const int target = j * K;
-        int polls = 0;
-        bool ok = false;
-        while (!(ok = __hip_atomic_load(a.wsync + node, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) &&
-               ++polls < a.wspin)
-          __builtin_amdgcn_s_sleep(8);
+      if (wv == 0) {
+        int ok = 0;
+        if (lane == 0) {
+          double* slot = a.wpart + ((size_t)node * K + part) * 2;
+          __hip_atomic_store(slot, fp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(slot + 1, z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_add(a.wsync + node, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+          const int target = j * K;
+          int polls = 0;
+          while (!(ok = __hip_atomic_load(a.wsync + node, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) &&
+                 ++polls < a.wspin)
+            __builtin_amdgcn_s_sleep(8);
+        }
+        ok = __shfl(ok, 0);
+        // lane q loads workgroup q's partials (all at once), summed in a fixed lane order
         double sf = 0.0, sz = 0.0;
         if (ok) {
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-          for (int q = 0; q < K; ++q) {
-            const double* o = a.wpart + ((size_t)node * K + q) * 2;
-            sf += __hip_atomic_load(o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            sz += __hip_atomic_load(o + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (lane < K) {
+            const double* o = a.wpart + ((size_t)node * K + lane) * 2;
+            sf = __hip_atomic_load(o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sz = __hip_atomic_load(o + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
+          sf = wave_sum(sf);
+          sz = wave_sum(sz);
         }
-        s_fp = sf;
-        s_z = sz;
-        s_ok = ok;
+        if (lane == 0) {
+          s_fp = sf;
+          s_z = sz;
+          s_ok = ok;
+        }
       }
       __syncthreads();
       if (!s_ok) {
