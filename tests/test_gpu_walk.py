@@ -82,6 +82,27 @@ def test_split_chain(tune, parts, spin):
     print(f"walk_parts={parts} walk_spin={spin}: mean accept_len {ref['accept_len'].mean():.2f}, excused {ex}")
 
 
+def test_split_chain_repeats(tune):
+    """Twenty back-to-back runs of a split chain give bit-identical outputs: the partials of a
+    pass are summed in a fixed order, and a workgroup one pass ahead writes the slots of the other
+    parity (with one set of slots, a fast workgroup could overwrite a partial a sibling had not
+    read yet, and the bonus token then moved)."""
+    tune(walk_parts=16)
+    w = wl.custom(seed=6216, B=2, N=40, V=70000, tree=("bfs", (6, 3, 1)), sigma_logits=0.5)
+    parents, n_nodes = wl.trees(w)
+    vi = wl.verify_inputs(w, parents)
+    first, ref = _run(vi, parents, n_nodes, w.N - 1)
+    compare_verify(first, ref, n_nodes, bonus_margin=WALK_BONUS_MARGIN, walk=True)
+    for it in range(20):
+        got = sb.spec_verify(dev(vi["target_logits"]), dev(vi["tokens"]), dev(parents.astype(np.int32)),
+                             dev(vi["uniforms"]), "walk", draft_probs=dev(vi["draft_probs"]),
+                             draft_row=dev(vi["draft_row"]), n_nodes=dev(n_nodes.astype(np.int32)),
+                             max_depth=w.N - 1)
+        torch.cuda.synchronize()
+        for k, v in got.items():
+            assert np.array_equal(host(v), first[k]), (it, k)
+
+
 def test_max_depth_and_errors():
     """Structural errors, a sibling on another draft row, and a tight max_depth."""
     w = wl.custom(seed=6100, B=12, N=30, V=900, tree=("random", 4))

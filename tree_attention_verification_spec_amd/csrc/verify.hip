@@ -30,6 +30,7 @@
 //           one wave does all of it with shuffles; otherwise a 256-thread workgroup.
 #include <algorithm>
 #include <cfloat>
+#include <atomic>
 #include <climits>
 #include <mutex>
 
@@ -108,7 +109,8 @@ struct VerifyArgs {
   int wk;               // walk: workgroups per node (1: one workgroup does the whole chain)
   int wspin;            // walk, wk > 1: polls of a node's counter before a workgroup stops waiting
   int32_t* wsync;       // [B, N] walk, wk > 1: arrivals per node (zeroed by the row pass)
-  double* wpart;        // [B, N, wk, 2] walk, wk > 1: each workgroup's partial sums of a pass
+  double* wpart;        // [B, N, wk, 2, 2] walk, wk > 1: each workgroup's partial sums of a pass
+                        // (fp, z), in the slot of the pass's parity
 };
 
 // ------------------------------------------------------------------ reductions
@@ -816,8 +818,9 @@ struct Chain {
 // Several workgroups per node (a.wk > 1, chosen on the host so that every workgroup that can
 // have work is resident at once, one per CU): workgroup q of node p streams the steps q, q + wk,
 // ... of each pass, keeps its own LDS list, and after every pass adds its partial sums to the
-// node's slots and its arrival to the node's counter (release); each then waits for all wk
-// arrivals (acquire) and sums the partials in workgroup order, so every workgroup of the node
+// node's slots of that pass's parity and its arrival to the node's counter (release; a
+// workgroup can be one pass ahead of a sibling still reading, never two); each then waits for all wk
+// arrivals (acquire) and sums the partials in a fixed order, so every workgroup of the node
 // derives the same c_(j+1).  The wait is bounded: a workgroup that runs out of it (a sibling
 // that is not resident) leaves, except workgroup 0, which finishes the chain alone over the
 // whole row; the results are the same up to the order of the fp64 sums.
@@ -922,7 +925,9 @@ __global__ __launch_bounds__(THREADS) void walk_chain_kernel(VerifyArgs a) {
       if (wv == 0) {
         int ok = 0;
         if (lane == 0) {
-          double* slot = a.wpart + ((size_t)node * K + part) * 2;
+          // the slot of this pass's parity: a workgroup may run one pass ahead of a sibling
+          // still reading this pass's partials, never two
+          double* slot = a.wpart + (((size_t)node * K + part) * 2 + (j & 1)) * 2;
           __hip_atomic_store(slot, fp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           __hip_atomic_store(slot + 1, z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           __hip_atomic_fetch_add(a.wsync + node, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
@@ -938,7 +943,7 @@ __global__ __launch_bounds__(THREADS) void walk_chain_kernel(VerifyArgs a) {
         if (ok) {
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
           if (lane < K) {
-            const double* o = a.wpart + ((size_t)node * K + lane) * 2;
+            const double* o = a.wpart + (((size_t)node * K + lane) * 2 + (j & 1)) * 2;
             sf = __hip_atomic_load(o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             sz = __hip_atomic_load(o + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
@@ -1432,16 +1437,34 @@ struct VerifyLayout {
 };
 
 // WALK: workgroups per node.  Several only when every workgroup that can have work is resident
-// at once (one 1024-thread workgroup per CU, kWalkResident of the 256 CUs), counting the most
-// nodes that can have two children, (N - 1) / 2 per sequence; at most one per 8K-token step of
-// the row.  The tuning override walk_parts forces a count (1-16).
+// at once (one 1024-thread workgroup per CU; all CUs of the current device but 16), counting the
+// most nodes that can have two children, (N - 1) / 2 per sequence; at most one per 8K-token step
+// of the row.  The tuning override walk_parts forces a count (1-16).
 constexpr int kWalkMaxParts = 16;
-constexpr int kWalkResident = 240;
 constexpr int kWalkStep = 1024 * 8;     // tokens per streaming step of the chain
+constexpr int kMaxWalkDevices = 64;
+int walk_resident() {
+  static std::atomic<int> cached[kMaxWalkDevices];   // 0: not looked up yet
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxWalkDevices) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    v = std::max(1, cus - 16);
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
 int walk_parts(int B, int N, int V) {
   const long long multi = (long long)B * std::max(1, (N - 1) / 2);
   const int steps = (V + kWalkStep - 1) / kWalkStep;
-  const int k = (int)std::min<long long>(std::min<long long>(kWalkMaxParts, kWalkResident / multi), steps);
+  const int k = (int)std::min<long long>(std::min<long long>(kWalkMaxParts, walk_resident() / multi), steps);
   return std::max(1, std::min(tuning(kKnobWalkParts, k), kWalkMaxParts));
 }
 
@@ -1495,7 +1518,7 @@ VerifyLayout layout(int B, int N, int V, bool packed = false) {
   L.wk = walk_parts(B, N, V);
   // sized for kWalkMaxParts whatever wk is, so that the size grows with B
   L.wsync = take((size_t)B * N * sizeof(int32_t));
-  L.wpart = take((size_t)B * N * kWalkMaxParts * 2 * sizeof(double));
+  L.wpart = take((size_t)B * N * kWalkMaxParts * 4 * sizeof(double));
   const bool fits = (size_t)B * N <= (size_t)kListMax;
   L.listed = fits && tuning(kKnobVerifyRowsList, (size_t)B * N * L.CR >= kListMinItems ? 1 : 0) != 0;
   L.total = off;
