@@ -928,9 +928,15 @@ __global__ __launch_bounds__(THREADS) void walk_chain_kernel(VerifyArgs a) {
           // the slot of this pass's parity: a workgroup may run one pass ahead of a sibling
           // still reading this pass's partials, never two
           double* slot = a.wpart + (((size_t)node * K + part) * 2 + (j & 1)) * 2;
+          // Everything exchanged here is an agent-scope atomic (performed coherently across the
+          // XCDs' caches), so no cache write-back or invalidation is needed; the wait makes the
+          // two stores complete before the arrival is counted.
           __hip_atomic_store(slot, fp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           __hip_atomic_store(slot + 1, z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_fetch_add(a.wsync + node, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          __builtin_amdgcn_s_waitcnt(0);
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          __hip_atomic_fetch_add(a.wsync + node, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           const int target = j * K;
           int polls = 0;
           while (!(ok = __hip_atomic_load(a.wsync + node, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) &&
@@ -941,7 +947,7 @@ __global__ __launch_bounds__(THREADS) void walk_chain_kernel(VerifyArgs a) {
         // lane q loads workgroup q's partials (all at once), summed in a fixed lane order
         double sf = 0.0, sz = 0.0;
         if (ok) {
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
           if (lane < K) {
             const double* o = a.wpart + (((size_t)node * K + lane) * 2 + (j & 1)) * 2;
             sf = __hip_atomic_load(o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
