@@ -817,11 +817,11 @@ struct Chain {
 
 // Several workgroups per node (a.wk > 1, chosen on the host so that every workgroup that can
 // have work is resident at once, one per CU): workgroup q of node p streams the steps q, q + wk,
-// ... of each pass, keeps its own LDS list, and after every pass adds its partial sums to the
-// node's slots of that pass's parity and its arrival to the node's counter (release; a
-// workgroup can be one pass ahead of a sibling still reading, never two); each then waits for all wk
-// arrivals (acquire) and sums the partials in a fixed order, so every workgroup of the node
-// derives the same c_(j+1).  The wait is bounded: a workgroup that runs out of it (a sibling
+// ... of each pass, keeps its own LDS list, and after every pass stores its partial sums in the
+// node's slots of that pass's parity (a workgroup can be one pass ahead of a sibling still
+// reading, never two) and, once the stores are complete, adds its arrival to the node's
+// counter; each then waits for all wk arrivals and sums the partials in a fixed order, so every
+// workgroup of the node derives the same c_(j+1).  The wait is bounded: a workgroup that runs out of it (a sibling
 // that is not resident) leaves, except workgroup 0, which finishes the chain alone over the
 // whole row; the results are the same up to the order of the fp64 sums.
 constexpr int kWalkSpinMax = 1 << 14;   // polls of the counter (each followed by a short sleep);
