@@ -54,6 +54,9 @@ constexpr int kLazy = 8;       // reference-max slack (log2 units): weights belo
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 struct AttnArgs {
   const void* q;
@@ -74,6 +77,7 @@ struct AttnArgs {
   int R, S, Mpad;
   int prio;                    // raise wave priority around the MFMA blocks
   float lazy;                  // reference-max slack in log2 units (0: exact running max)
+  uint32_t lazy_bits;          // bf16 bit pattern of 2^lazy (positive bf16 order as integers)
   int lpt;                     // dispatch sequences longest first (batches of 2..256)
 };
 
@@ -325,18 +329,25 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   // (log2 units): softmax is the same for any reference, weights stay below 2^lazy, and the O
   // rescale is rarely needed.  alpha[cb] receives the factor the output accumulated so far must
   // take (1 where the reference did not move); returns whether any row of the wave moved.
-  auto softmax = [&](auto masked, int t0, f32x4 (&s_acc)[4][CB], bf16x8 (&pb)[2][CB], float (&alpha)[CB]) {
+  //
+  // Fast path, once every live row of the wave has a reference: the weights are formed against
+  // the current references straight away, and one integer max over their bf16 bit patterns
+  // (non-negative bf16 values order like their bits; NaN sorts above every number) tells
+  // whether any of them passed 2^lazy.  If none did, no reference moves and the tile needs no
+  // row max at all; otherwise the tile takes the general path below, which forms the weights
+  // again.  `ready` (wave-uniform) records that every live row has a finite reference.
+  auto softmax = [&](auto masked, int t0, f32x4 (&s_acc)[4][CB], bf16x8 (&pb)[2][CB], float (&alpha)[CB],
+                     bool& ready) {
     constexpr bool MASKED = decltype(masked)::value;
     // ancestor words of tree keys j = s - P in this tile: word jw or jw + 1 (j < n <= 64 W)
     const int jw = (t0 - P) >> 6;               // floor division (t0 - P may be negative)
-    bool moved = false;
+    float x[CB][4][4];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      float x[4][4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[kb][e] = s_acc[kb][cb][e];
+        for (int e = 0; e < 4; ++e) x[cb][kb][e] = s_acc[kb][cb][e];
       if constexpr (MASKED) {
         const uint64_t* mrow = s_mask + (wave * ROWS_WAVE + cb * 16 + l16) * kMaxWords;
         const uint64_t wlo = mrow[min(max(jw, 0), kMaxWords - 1)];
@@ -352,14 +363,49 @@ void tree_attn_bf16_kernel(AttnArgs a) {
               const uint64_t word = ((j >> 6) == jw) ? wlo : whi;
               vis = (word >> (j & 63)) & 1ull;
             }
-            if (!vis) x[kb][e] = -INFINITY;
+            if (!vis) x[cb][kb][e] = -INFINITY;
           }
       }
+    }
+    auto pack = [&](int cb, const float (&w)[4][4]) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        bf16x8 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pk[e] = (__bf16)w[2 * c][e];
+          pk[4 + e] = (__bf16)w[2 * c + 1][e];
+        }
+        pb[c][cb] = pk;
+      }
+    };
+    if (ready) {
+      u16x8 top = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const float m_use = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb];   // rows past the workload
+        float w[4][4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[kb][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[cb][kb][e], a.scale_log2, -m_use));
+        pack(cb, w);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) top = __builtin_elementwise_max(top, __builtin_bit_cast(u16x8, pb[c][cb]));
+      }
+      const u16x4 t4 = __builtin_elementwise_max(top.lo, top.hi);
+      const u16x2 t2 = __builtin_elementwise_max(t4.lo, t4.hi);
+      const uint32_t t1 = t2.x > t2.y ? t2.x : t2.y;
+      if (__ballot(t1 > a.lazy_bits) == 0) return false;
+    }
+    bool moved = false, unset = false;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
       float mloc = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mloc = fmaxf(mloc, x[kb][e]);
+        for (int e = 0; e < 4; ++e) mloc = fmaxf(mloc, x[cb][kb][e]);
       mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
       const float m_tile = mloc * a.scale_log2;
@@ -367,22 +413,16 @@ void tree_attn_bf16_kernel(AttnArgs a) {
       alpha[cb] = grow ? __builtin_amdgcn_exp2f(m_run[cb] - m_tile) : 1.f;   // 0 from -inf
       m_run[cb] = grow ? m_tile : m_run[cb];
       moved = moved || __ballot(grow) != 0;
+      unset = unset || (row_ok[cb] && m_run[cb] == -INFINITY);
       const float m_use = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb];
+      float w[4][4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[kb][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][e], a.scale_log2, -m_use));
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        bf16x8 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pk[e] = (__bf16)x[2 * c][e];
-          pk[4 + e] = (__bf16)x[2 * c + 1][e];
-        }
-        pb[c][cb] = pk;
-      }
+        for (int e = 0; e < 4; ++e) w[kb][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[cb][kb][e], a.scale_log2, -m_use));
+      pack(cb, w);
     }
+    ready = __ballot(unset) == 0;
     return moved;
   };
   auto rescale = [&](const float (&alpha)[CB]) {
@@ -416,6 +456,7 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   auto is_plain = [&](int t0) { return t0 + kKT <= k1 && t0 + kKT <= P; };
 
   int buf = 0;
+  bool ready = false;
   for (int t0 = k0; t0 < k1; t0 += kKT) {
     stage(buf);
     __syncthreads();
@@ -425,8 +466,8 @@ void tree_attn_bf16_kernel(AttnArgs a) {
     qk(buf, s_acc);
     bf16x8 pb[2][CB];
     float alpha[CB];
-    const bool moved = is_plain(t0) ? softmax(std::false_type{}, t0, s_acc, pb, alpha)
-                                    : softmax(std::true_type{}, t0, s_acc, pb, alpha);
+    const bool moved = is_plain(t0) ? softmax(std::false_type{}, t0, s_acc, pb, alpha, ready)
+                                    : softmax(std::true_type{}, t0, s_acc, pb, alpha, ready);
     if (moved) rescale(alpha);
     if (a.prio) __builtin_amdgcn_s_setprio(1);
     pv(buf, pb);
@@ -756,7 +797,9 @@ extern "C" spec_status spec_tree_attn(const void* q, const void* k_cache, const 
   if (need > 0 && (!workspace || ws_bytes < need)) return SPEC_EWORKSPACE;
   a.R = p.R; a.S = p.S; a.Mpad = p.Mpad;
   a.prio = tuning(kKnobAttnPrio, 1);
-  a.lazy = (float)std::max(0, tuning(kKnobAttnLazy, kLazy));
+  const int lazy = std::max(0, tuning(kKnobAttnLazy, kLazy));
+  a.lazy = (float)lazy;
+  a.lazy_bits = lazy < 128 ? (uint32_t)(127 + lazy) << 7 : 0x7F80u;   // 2^lazy, or +inf
   a.lpt = p.lpt;
   if (p.S > 1) {
     char* w = static_cast<char*>(workspace);
