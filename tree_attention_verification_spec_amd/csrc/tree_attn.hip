@@ -339,8 +339,11 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   auto softmax = [&](auto masked, int t0, f32x4 (&s_acc)[4][CB], bf16x8 (&pb)[2][CB], float (&alpha)[CB],
                      bool& ready) {
     constexpr bool MASKED = decltype(masked)::value;
-    // ancestor words of tree keys j = s - P in this tile: word jw or jw + 1 (j < n <= 64 W)
-    const int jw = (t0 - P) >> 6;               // floor division (t0 - P may be negative)
+    // tree index of the tile's first key (negative inside the prefix); the ancestor words of
+    // the tile's tree keys are word jw and jw + 1 (tree keys j < n <= 64 W)
+    const int j0 = t0 - P;
+    const int jw = j0 >> 6;                     // floor division
+    const int lim = k1 - t0;                    // keys of the tile inside the split (>= 1)
     float x[CB][4][4];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
@@ -349,22 +352,35 @@ void tree_attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[cb][kb][e] = s_acc[kb][cb][e];
       if constexpr (MASKED) {
+        // Visibility of the tile's 64 keys for this row, bit i for key t0 + i: prefix keys
+        // always, tree key j when bit j of the row's ancestor words is set, nothing past the
+        // split or in a row past the workload.  Each lane then takes the 4 bits of each of its
+        // key groups and turns a score into -inf with one bit-insert.
         const uint64_t* mrow = s_mask + (wave * ROWS_WAVE + cb * 16 + l16) * kMaxWords;
         const uint64_t wlo = mrow[min(max(jw, 0), kMaxWords - 1)];
         const uint64_t whi = mrow[min(max(jw + 1, 0), kMaxWords - 1)];
+        uint64_t vis;
+        if (j0 >= 0) {
+          const int sh = j0 & 63;
+          vis = sh ? (wlo >> sh) | (whi << (64 - sh)) : wlo;
+        } else if (j0 > -64) {                  // jw = -1: whi is word 0, keys i < -j0 prefix
+          const int sh = -j0;
+          vis = (whi << sh) | ((1ull << sh) - 1);
+        } else {
+          vis = ~0ull;
+        }
+        if (lim < 64) vis &= (1ull << lim) - 1;
+        if (!row_ok[cb]) vis = 0;
+        const uint64_t mine = vis >> (4 * lg);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb) {
+          const uint32_t q = (uint32_t)(mine >> (16 * kb));
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int s = t0 + kb * 16 + 4 * lg + e;
-            bool vis = row_ok[cb] && s < k1;
-            if (vis && s >= P) {
-              const int j = s - P;
-              const uint64_t word = ((j >> 6) == jw) ? wlo : whi;
-              vis = (word >> (j & 63)) & 1ull;
-            }
-            if (!vis) x[cb][kb][e] = -INFINITY;
+            const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe((int)q, e, 1);   // 0 or ~0
+            x[cb][kb][e] = __uint_as_float((__float_as_uint(x[cb][kb][e]) & keep) | (0xff800000u & ~keep));
           }
+        }
       }
     }
     auto pack = [&](int cb, const float (&w)[4][4]) {
