@@ -200,7 +200,8 @@ spec_status spec_tree_assemble_rows(const float* draft_probs, const int32_t* par
  *              visible slots (-inf for a row that sees nothing)
  *   err        int32 [B]            optional (NULL): SPEC_ERR_NNODES / SPEC_ERR_PREFIX
  * Rows of padding nodes, rows that see no slot and all rows of a sequence with an error are 0.
- * Supported: head_dim 64 or 128; Hq % Hkv == 0; N <= 256.
+ * Supported: head_dim 64 or 128; Hq % Hkv == 0; N <= 256; S_max * head_dim * 2 < 2^31 (the
+ * K and V cache of one sequence and KV head below 2 GiB each).
  * Errors: SPEC_EINVAL (sizes, NULL pointers, scale not positive and finite),
  * SPEC_EUNSUPPORTED (head_dim, dtype), SPEC_EWORKSPACE.
  * ------------------------------------------------------------------------------------ */

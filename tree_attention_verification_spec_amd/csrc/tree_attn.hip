@@ -55,6 +55,17 @@ constexpr int kLazy = 8;       // reference-max slack (log2 units): weights belo
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+// Buffer loads: a per-workgroup descriptor (scalar registers) and 32-bit byte offsets per lane.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+__device__ __forceinline__ BufRsrc buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ bf16x8 buf_ld8(BufRsrc r, uint32_t lane_off) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, 0, 0));
+}
+// Largest K or V cache of one (sequence, KV head) in bytes that the bf16 kernel addresses
+// with 32-bit offsets.
+constexpr long long kMaxHeadCacheBytes = 1ll << 31;
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
@@ -252,6 +263,9 @@ void tree_attn_bf16_kernel(AttnArgs a) {
   for (int e = 0; e < 8; ++e) ones_frag[e] = (__bf16)(l16 == 0 ? 1.f : 0.f);
 
   const size_t kv_base = ((size_t)b * a.Hkv + g) * (size_t)a.S_max * D;
+  const uint32_t head_bytes = (uint32_t)a.S_max * (D * 2);   // < 2^31 (checked on the host)
+  const BufRsrc krs = buf_rsrc(kp + kv_base, head_bytes);
+  const BufRsrc vrs = buf_rsrc(vp + kv_base, head_bytes);
   const int ld_key = tid / CPK;
   const int ld_chunk = tid % CPK;
   // Next tile into registers, consumed only by the next stage(), so the loads stay in flight
@@ -263,9 +277,9 @@ void tree_attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
       const int s = min(t0 + pass * KPP + ld_key, k1 - 1);
-      const size_t at = kv_base + (size_t)s * D + ld_chunk * 8;
-      kreg[pass] = *reinterpret_cast<const bf16x8*>(kp + at);
-      vreg[pass] = *reinterpret_cast<const bf16x8*>(vp + at);
+      const uint32_t at = (uint32_t)s * (D * 2) + ld_chunk * 16;
+      kreg[pass] = buf_ld8(krs, at);
+      vreg[pass] = buf_ld8(vrs, at);
     }
   };
   auto stage = [&](int buf) {
@@ -711,6 +725,7 @@ spec_status check_shape(int B, int N, int Hq, int Hkv, int head_dim, int S_max, 
   if (B < 1 || N < 1 || N > SPEC_MAX_NODES || Hq < 1 || Hkv < 1 || S_max < 1) return SPEC_EINVAL;
   if (Hq % Hkv != 0) return SPEC_EUNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return SPEC_EUNSUPPORTED;
+  if ((long long)S_max * head_dim * 2 >= kMaxHeadCacheBytes) return SPEC_EUNSUPPORTED;
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EUNSUPPORTED;
   // fp32: one workgroup per query row; bf16: at most (units rounded to 8) x row blocks x splits
   // with splits <= S_max / 128 + 1 and row blocks <= N * G / 64 + 1
