@@ -137,6 +137,11 @@ def test_workspace_sizes_are_monotone(lib):
     assert 0 < small < big
     assert lib.spec_medusa_heads_workspace(8, 4, 4096, 32000, 8) > 8 * 4 * 32000 * 4
     assert lib.spec_tree_attn_workspace(1, 10, 4, 1, 64, 266, 0) == 0   # fp32 path needs none
+    # the bf16 kernel addresses one (sequence, KV head) cache with 32-bit offsets: below 2 GiB
+    assert lib.spec_tree_attn_workspace(1, 63, 32, 8, 128, (1 << 23) - 1, 1) > 0
+    assert lib.spec_tree_attn_workspace(1, 63, 32, 8, 128, 1 << 23, 1) == 0
+    assert lib.spec_tree_attn_workspace(1, 63, 32, 8, 64, (1 << 24) - 1, 1) > 0
+    assert lib.spec_tree_attn_workspace(1, 63, 32, 8, 64, 1 << 24, 1) == 0
 
 
 def test_tree_select_argument_checks(lib):
