@@ -116,12 +116,26 @@ def test_draw_weights_stored_or_recomputed(tune, store, case):
 
 
 @pytest.mark.parametrize("store", ["0", "1"])
-def test_zero_residual_draws_from_target(tune, store):
+def test_wide_vocabulary_workgroup_draw(tune, store):
+    """A vocabulary of 300000 tokens is more than 64 bonus chunks of 4096, so the draw runs on a
+    workgroup with block scans (stored weights or recomputed ones) instead of one wave."""
+    tune(verify_store_w=int(store))
+    w = wl.custom(seed=3050, B=2, N=20, V=300_000, sigma_logits=0.5, tree=("random", 4))
+    parents, n_nodes, vi = _case(w)
+    for mode in ("typical", "reject"):
+        got, ref = _run(w, mode, vi, parents, n_nodes)
+        compare_verify(got, ref, n_nodes)
+
+
+@pytest.mark.parametrize("store", ["0", "1"])
+@pytest.mark.parametrize("V", [9000, 300_000])
+def test_zero_residual_draws_from_target(tune, store, V):
     """Draft probabilities of 2 everywhere: each node test accepts with T/D <= 1/2 and every
     residual relu(T - D) is zero, so a rejection's bonus token is drawn from T at the kept node
-    (the zero-mass reading), on both draw kernels."""
+    (the zero-mass reading), on every draw kernel: one wave over stored weights or over group
+    sums (9000 tokens), a workgroup over stored or recomputed weights (300000 tokens)."""
     tune(verify_store_w=int(store))
-    w = wl.custom(seed=3100, B=6, N=40, V=9000, tree=("random", 5))
+    w = wl.custom(seed=3100, B=6 if V < 100_000 else 3, N=40, V=V, tree=("random", 5))
     parents, n_nodes, vi = _case(w)
     vi = dict(vi)
     vi["draft_probs"] = np.full_like(vi["draft_probs"], 2.0)

@@ -49,7 +49,7 @@ def _both(w, mode, parents, n_nodes, vi):
 
 def test_static_scratch_matches_workspace_twice():
     need_gpu()
-    big = wl.config(3)                         # 16 x 127 nodes, vocabulary 128256: ~2 MB of scratch
+    big = wl.config(3)                         # 16 x 127 nodes, vocabulary 128256: ~3.6 MB of scratch
     small = wl.custom(seed=901, B=3, N=37, V=5000, tree=("random", 5), n_nodes_range=(20, 37))
     assert sb.verify_static_bytes(small.B, small.N, small.V) < sb.verify_static_bytes(big.B, big.N, big.V)
     _both(big, "reject", *_inputs(big))

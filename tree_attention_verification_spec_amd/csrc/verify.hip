@@ -103,6 +103,10 @@ struct VerifyArgs {
   BonusPart* bparts;    // [B, C]
   double* weights;      // [B, C * CS]: the bonus pass's per-token weights (kinds 2 and 3),
                         // kept only for small batches (NULL otherwise)
+  double* gsum;         // [B, C, CS / 64, 2]: per 64-token group, the sums of the bonus pass's
+                        // weights (kind 2: exp(x - chunk max); kind 3: relu(T - cs D)) and, for
+                        // kind 3, of exp(x - M); when the weights are not kept and one wave
+                        // holds the chunks (NULL otherwise)
   double* wc;           // [B, N] walk: child c is tested against relu(T_p - wc D) / wf
   double* wf;           // [B, N]
   double* wend;         // [B, N] walk: residual scale after every child of node p is rejected
@@ -1004,6 +1008,26 @@ void launch_chain(const VerifyArgs& a, dim3 grid, bool vec4, bool dvec, hipStrea
   }
 }
 
+// Sum over aligned groups of LANES lanes (4, 8, 16, 32 or 64), in every lane of the group: DPP
+// moves inside a row of 16 (swap neighbours, swap pairs, mirror each half, mirror the row),
+// shuffles across rows.
+template <int CTRL>
+__device__ __forceinline__ double dpp_move(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+template <int LANES>
+__device__ __forceinline__ double lane_group_sum(double v) {
+  v += dpp_move<0xB1>(v);                      // quad_perm [1, 0, 3, 2]
+  v += dpp_move<0x4E>(v);                      // quad_perm [2, 3, 0, 1]
+  if (LANES >= 8) v += dpp_move<0x141>(v);     // row_half_mirror
+  if (LANES >= 16) v += dpp_move<0x140>(v);    // row_mirror
+  if (LANES >= 32) v += __shfl_xor(v, 16);
+  if (LANES >= 64) v += __shfl_xor(v, 32);
+  return v;
+}
+
 template <int VEC, int CS>
 __device__ void bonus_chunk(const VerifyArgs& a, int b, int c, const BonusPlan& pl) {
   constexpr int kPer = CS / kThreads;
@@ -1035,18 +1059,18 @@ __device__ void bonus_chunk(const VerifyArgs& a, int b, int c, const BonusPlan& 
   // re-gathering and recomputing them (one dependent round trip less on a latency-bound path;
   // for large batches writing B x V fp64 weights costs more than it saves).
   double S = 0.0, Q = 0.0;
-  double w[kPer];
+  double w[kPer], ex[kPer];
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) w[k] = 0.0;
+  for (int k = 0; k < kPer; ++k) w[k] = ex[k] = 0.0;
   if (!nf && pl.kind == 3) {
     // exp(x - M) with the row max, and relu(T - D) with T normalised by the row statistics
     const double inv = 1.0 / pl.S;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       if (chunk_index<VEC>(lo, k) < hi) {
-        const double e = exp((double)x[k] - (double)pl.M);
-        S += e;
-        w[k] = fmax(e * inv - pl.cs * dr[k], 0.0);
+        ex[k] = exp((double)x[k] - (double)pl.M);
+        S += ex[k];
+        w[k] = fmax(ex[k] * inv - pl.cs * dr[k], 0.0);
         Q += w[k];
       }
     }
@@ -1067,6 +1091,30 @@ __device__ void bonus_chunk(const VerifyArgs& a, int b, int c, const BonusPlan& 
       } else {
         wrow[v] = w[k];
         wrow[chunk_index<VEC>(lo, k + 1)] = w[k + 1];
+      }
+    }
+  }
+  if (a.gsum && pl.kind >= 2) {
+    // Group sums for the one-wave draw: this thread's VEC consecutive tokens of register group
+    // g lie in 64-token group (g * kThreads + t) * VEC / 64, shared by kWave / VEC aligned lanes
+    // of one wave, which add their parts; the first of them stores the sums (the exp(x - M)
+    // sums only for residual draws).
+    constexpr int kLanes = kWave / VEC;
+    double* gs = a.gsum + ((size_t)b * a.C + c) * (CS / 64) * 2;
+    const bool resid = pl.kind == 3;
+#pragma unroll
+    for (int g = 0; g < kPer / VEC; ++g) {
+      double pw = 0.0, pe = 0.0;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        pw += w[g * VEC + e];
+        pe += ex[g * VEC + e];
+      }
+      pw = lane_group_sum<kLanes>(pw);
+      if (resid) pe = lane_group_sum<kLanes>(pe);
+      if ((threadIdx.x & (kLanes - 1)) == 0) {
+        const int grp = (chunk_index<VEC>(lo, g * VEC) - lo) / 64;
+        *reinterpret_cast<double2*>(gs + grp * 2) = make_double2(pw, pe);
       }
     }
   }
@@ -1433,13 +1481,107 @@ __global__ __launch_bounds__(kWave) void select_wave_kernel(VerifyArgs a) {
   if (t == 0) a.bonus[b] = tok;
 }
 
+// One-wave draw when the weights are not kept (large batches) and at most 64 chunks: lane t
+// holds chunk t's part; the chunk holding u * Z is found as in select_wave_kernel, then the
+// 64-token group inside it from the group sums the bonus pass left, then the token inside the
+// group, each lane recomputing one token's weight exactly as the bonus pass formed it.  Three
+// dependent rounds of loads and one exponential per lane, against a workgroup that recomputes
+// the whole chunk.  Rounding fallbacks as in the other draws: past the end of the chosen
+// chunk or group, its last element of positive weight.
+template <int VEC, int CS>
+__global__ __launch_bounds__(kWave) void select_groups_kernel(VerifyArgs a) {
+  constexpr int kG = CS / 64;                  // groups per chunk (<= 64)
+  const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  const BonusPlan pl = a.plans[b];
+  const BonusPart bp = a.bparts[(size_t)b * a.C + (t < a.C ? t : 0)];
+  const float u = a.uniforms[(size_t)b * a.N];
+  if (pl.kind == 0) return;
+  double Sc = 0.0, Qc = 0.0;
+  float mc = -INFINITY;
+  int amc = INT_MAX, nf = 0;
+  if (t < a.C) {
+    Sc = bp.S; Qc = bp.Q; mc = bp.m; amc = bp.argmax; nf = bp.nonfinite;
+  }
+  float m = mc;
+  int am = amc;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {           // row max / lowest argmax / nonfinite
+    const float m2 = __shfl_xor(m, o);
+    const int am2 = __shfl_xor(am, o), nf2 = __shfl_xor(nf, o);
+    if (m2 > m || (m2 == m && am2 < am)) { m = m2; am = am2; }
+    nf |= nf2;
+  }
+  if (nf) {
+    write_neutral_wave(a, b, err_word(pl.m, SPEC_ERR_NONFINITE));
+    return;
+  }
+  if (pl.kind == 1) {
+    if (t == 0) a.bonus[b] = am;
+    return;
+  }
+  // chunk weights: as in select_wave_kernel; `slot` picks the group sums that match them
+  double q, scale = 1.0;
+  int what = 2;                                // 2: T (kind 2), 3: residual, 4: T_m (zero residual)
+  if (pl.kind == 2) {
+    scale = (mc == -INFINITY) ? 0.0 : exp((double)mc - (double)m);
+    q = Sc * scale;
+  } else if (wave_sum(Qc) > 0.0) {
+    q = Qc;
+    what = 3;
+  } else {
+    q = Sc;                                    // relative to the row max pl.M
+    what = 4;
+  }
+  if (t >= a.C) q = 0.0;
+  const double incl = wave_scan(q);
+  const double thr = (double)u * __shfl(incl, kWave - 1);
+  const unsigned long long over = __ballot(t < a.C && incl > thr);
+  const unsigned long long mass = __ballot(t < a.C && q > 0.0);
+  const int cs = over ? __ffsll(over) - 1 : (mass ? 63 - __clzll(mass) : 0);
+  const double base = (over || mass) ? __shfl(incl - q, cs) : 0.0;
+  const double sc = (over || mass) ? __shfl(scale, cs) : 1.0;
+  const float mcs = __shfl(mc, cs);            // chunk max (kind 2 weights are relative to it)
+  const int lo = cs * a.CS, hi = min(a.V, lo + a.CS);
+  // the group
+  const double* gs = a.gsum + ((size_t)b * a.C + cs) * kG * 2;
+  const bool gin = t < kG && lo + t * 64 < hi;
+  const double qg = gin ? gs[t * 2 + (what == 4 ? 1 : 0)] * sc : 0.0;
+  const double inclg = wave_scan(qg);
+  const unsigned long long overg = __ballot(gin && base + inclg > thr);
+  const unsigned long long massg = __ballot(gin && qg > 0.0);
+  const int gsel = overg ? __ffsll(overg) - 1 : (massg ? 63 - __clzll(massg) : 0);
+  const double baseg = (overg || massg) ? base + __shfl(inclg - qg, gsel) : base;
+  // the token: lane t recomputes the weight of token lo + 64 gsel + t
+  const int v = lo + gsel * 64 + t;
+  const bool tin = v < hi;
+  const int at = tin ? v : lo;
+  const float* row = a.logits + ((size_t)b * a.N + pl.m) * a.V;
+  const float x = row[at];
+  double w;
+  if (what == 2) {
+    w = (x == -INFINITY) ? 0.0 : exp((double)x - (double)mcs);
+  } else if (what == 3) {
+    const double inv = 1.0 / pl.S;
+    w = fmax(exp((double)x - (double)pl.M) * inv - pl.cs * draft_at(a, b, pl.r, at), 0.0);
+  } else {
+    w = exp((double)x - (double)pl.M);
+  }
+  w = tin ? w * sc : 0.0;
+  const double inclw = wave_scan(w);
+  const unsigned long long overw = __ballot(tin && baseg + inclw > thr);
+  const unsigned long long massw = __ballot(tin && w > 0.0);
+  const int lane = overw ? __ffsll(overw) - 1 : (massw ? 63 - __clzll(massw) : -1);
+  if (t == 0) a.bonus[b] = lane >= 0 ? lo + gsel * 64 + lane : -1;
+}
+
 // ------------------------------------------------------------------ host
 
 struct VerifyLayout {
   int RC, CR, CS, C;
   int wk;               // WALK: workgroups per node
   bool store_w, listed;
-  size_t rowparts, plans, bparts, weights, row_list, row_count, walk, wsync, wpart, total;
+  size_t rowparts, plans, bparts, weights, gsum, row_list, row_count, walk, wsync, wpart, total;
 };
 
 // WALK: workgroups per node.  Several only when every workgroup that can have work is resident
@@ -1492,6 +1634,7 @@ template <int VEC, int CS>
 void launch_tail(const VerifyArgs& a, int B, bool wave_draw, hipStream_t s) {
   launch("verify_decide_bonus", decide_bonus_kernel<VEC, CS>, dim3((unsigned)((size_t)a.C * B)), dim3(kThreads), s, a);
   if (wave_draw) launch("verify_select", select_wave_kernel<VEC, CS>, dim3(B), dim3(kWave), s, a);
+  else if (a.gsum) launch("verify_select", select_groups_kernel<VEC, CS>, dim3(B), dim3(kWave), s, a);
   else launch("verify_select", select_kernel<VEC, CS>, dim3(B), dim3(kThreads), s, a);
 }
 
@@ -1518,6 +1661,9 @@ VerifyLayout layout(int B, int N, int V, bool packed = false) {
   // size grows with B and a workspace sized for a batch also serves every smaller one.
   L.store_w = tuning(kKnobVerifyStoreW, B <= kStoreWeightsMaxB ? 1 : 0) != 0;
   L.weights = take(packed && !L.store_w ? 0 : (size_t)B * c_large * kChunkLarge * sizeof(double));
+  // group sums of the one-wave draw without stored weights (reserved like the weights)
+  const size_t groups = std::max((size_t)c_large * (kChunkLarge / 64), (size_t)c_small * (kChunkSmall / 64));
+  L.gsum = take(packed && L.store_w ? 0 : (size_t)B * groups * 2 * sizeof(double));
   L.row_list = take((size_t)B * N * sizeof(int32_t));
   L.row_count = take(sizeof(int32_t));
   L.walk = take((size_t)3 * B * N * sizeof(double));
@@ -1571,6 +1717,7 @@ spec_status run_verify(const float* target_logits, const float* draft_probs, con
   a.plans = reinterpret_cast<BonusPlan*>(w + L.plans);
   a.bparts = reinterpret_cast<BonusPart*>(w + L.bparts);
   a.weights = L.store_w ? reinterpret_cast<double*>(w + L.weights) : nullptr;
+  a.gsum = (!L.store_w && L.C <= kWave) ? reinterpret_cast<double*>(w + L.gsum) : nullptr;
   a.row_list = reinterpret_cast<int32_t*>(w + L.row_list);
   a.row_count = reinterpret_cast<int32_t*>(w + L.row_count);
   a.wc = reinterpret_cast<double*>(w + L.walk);
