@@ -224,7 +224,9 @@ def test_verify_static_host_checks(lib):
     fake = ctypes.c_void_p(0x1000)
     limit = 16 << 20
     assert lib.spec_verify_static_bytes(1, 63, 128256) <= lib.spec_verify_workspace(1, 63, 128256)
-    assert lib.spec_verify_static_bytes(16, 127, 128256) < lib.spec_verify_workspace(16, 127, 128256)
+    assert lib.spec_verify_static_bytes(16, 127, 128256) <= lib.spec_verify_workspace(16, 127, 128256)
+    # above 64 bonus chunks the workspace reserves stored draw weights that batch 16 does not use
+    assert lib.spec_verify_static_bytes(16, 127, 300_000) < lib.spec_verify_workspace(16, 127, 300_000)
     for B, N, V in ((1, 63, 128256), (16, 127, 128256), (4, 255, 128256), (8, 127, 32000)):
         assert lib.spec_verify_static_bytes(B, N, V) <= limit, (B, N, V)
     assert lib.spec_verify_static_bytes(8, 256, 1_000_000) > limit

@@ -46,7 +46,8 @@ constexpr int kThreads = 256;
 constexpr int kChunkSmall = 2048;
 constexpr int kChunkLarge = 4096;
 constexpr int kSmallChunkMaxB = 8;
-constexpr int kStoreWeightsMaxB = 8;          // batches that keep the bonus pass's weights
+constexpr int kStoreWeightsMaxB = 8;          // batches that keep the bonus pass's weights when
+                                              // the row has more chunks than a wave has lanes
 constexpr int kPartsPerLane = 8;             // row-chunk partials per merging lane and batch
 
 struct RowPart {      // one chunk of one logits row
@@ -1054,10 +1055,10 @@ __device__ void bonus_chunk(const VerifyArgs& a, int b, int c, const BonusPlan& 
     }
   }
   block_argmax(m, am, nf);                 // chunk max / argmax / nonfinite, in every thread
-  // For small batches each token's weight of the draw (kind 3: relu(T - D); kind 2:
-  // exp(x - chunk max)) is also stored, so that the draw scans exactly these values instead of
-  // re-gathering and recomputing them (one dependent round trip less on a latency-bound path;
-  // for large batches writing B x V fp64 weights costs more than it saves).
+  // Each token's weight of the draw (kind 3: relu(T - D); kind 2: exp(x - chunk max)) is
+  // either summed per 64-token group for the one-wave draw (rows of at most 64 chunks) or, for
+  // small batches with longer rows, stored so that the workgroup draw scans exactly these
+  // values instead of recomputing the chunk.
   double S = 0.0, Q = 0.0;
   double w[kPer], ex[kPer];
 #pragma unroll
@@ -1351,10 +1352,10 @@ __global__ __launch_bounds__(kThreads) void select_kernel(VerifyArgs a) {
   if (t == 0) a.bonus[b] = tok;
 }
 
-// One-wave draw for the common case of stored weights and at most 64 chunks: lane t holds
-// chunk t's part, and inside the chosen chunk lane t owns a contiguous run of CS / 64 tokens, so
-// every reduction and scan is a wave shuffle and the kernel has no barrier.  Same chunk choice,
-// token choice and rounding fallbacks as select_kernel.
+// One-wave draw over stored weights (when the tuning override stores them for a row of at most
+// 64 chunks): lane t holds chunk t's part, and inside the chosen chunk lane t owns a contiguous
+// run of CS / 64 tokens, so every reduction and scan is a wave shuffle and the kernel has no
+// barrier.  Same chunk choice, token choice and rounding fallbacks as select_kernel.
 
 // Inclusive prefix sum over the wave in lane order (fp64).
 __device__ __forceinline__ double wave_scan(double v) {
@@ -1656,11 +1657,15 @@ VerifyLayout layout(int B, int N, int V, bool packed = false) {
   // the chunk parts and weights regions are sized for either chunking (the more chunks, the
   // longer padded row), so the workspace size grows with B whichever chunk size B selects
   L.bparts = take((size_t)B * c_small * sizeof(BonusPart));
-  // Stored draw weights are used for batches up to kStoreWeightsMaxB (the tuning override
-  // verify_store_w forces either way); their region is always reserved, so that the workspace
-  // size grows with B and a workspace sized for a batch also serves every smaller one.
-  L.store_w = tuning(kKnobVerifyStoreW, B <= kStoreWeightsMaxB ? 1 : 0) != 0;
-  L.weights = take(packed && !L.store_w ? 0 : (size_t)B * c_large * kChunkLarge * sizeof(double));
+  // Rows of at most 64 chunks are drawn by one wave from the 64-token group sums (measured
+  // faster than scanning stored weights at every batch).  Longer rows are drawn by a
+  // workgroup, over stored weights for batches up to kStoreWeightsMaxB; the tuning override
+  // verify_store_w forces either way.  The weights region is reserved whenever a batch of this
+  // vocabulary may store (or the override forces it), so that the workspace size grows with B
+  // and a workspace sized for a batch also serves every smaller one.
+  L.store_w = tuning(kKnobVerifyStoreW, (L.C > kWave && B <= kStoreWeightsMaxB) ? 1 : 0) != 0;
+  const bool reserve_w = packed ? L.store_w : (L.store_w || c_large > kWave);
+  L.weights = take(reserve_w ? (size_t)B * c_large * kChunkLarge * sizeof(double) : 0);
   // group sums of the one-wave draw without stored weights (reserved like the weights)
   const size_t groups = std::max((size_t)c_large * (kChunkLarge / 64), (size_t)c_small * (kChunkSmall / 64));
   L.gsum = take(packed && L.store_w ? 0 : (size_t)B * groups * 2 * sizeof(double));
