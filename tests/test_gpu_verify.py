@@ -105,8 +105,9 @@ def test_row_pass_listed_or_per_chunk(tune, listed, case):
 @pytest.mark.parametrize("store", ["0", "1"])
 @pytest.mark.parametrize("case", [0, 1, 3, 6])
 def test_draw_weights_stored_or_recomputed(tune, store, case):
-    """The bonus draw scans weights stored by the bonus pass (small batches by default) or
-    recomputes them (large batches): both paths, forced, on every mode."""
+    """The one-wave bonus draw either scans per-token weights stored by the bonus pass (forced)
+    or picks a 64-token group from the group sums and recomputes one weight per lane (the
+    default): both paths on every mode."""
     tune(verify_store_w=int(store))
     w = wl.custom(seed=3000 + case, **SMALL[case])
     parents, n_nodes, vi = _case(w)
