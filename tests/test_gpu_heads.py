@@ -48,8 +48,12 @@ def _compare_heads(got, ref):
     return swapped
 
 
+# Rows held in registers (V up to 32768; V = 9001: rows without 16-byte alignment) and rows
+# re-read from L2 (V = 40000).
 SMALL = [dict(B=4, H=3, Dm=256, V=1000, k=8), dict(B=1, H=1, Dm=128, V=77, k=5),
-         dict(B=16, H=4, Dm=512, V=4099, k=64), dict(B=5, H=2, Dm=1024, V=130, k=1)]
+         dict(B=16, H=4, Dm=512, V=4099, k=64), dict(B=5, H=2, Dm=1024, V=130, k=1),
+         dict(B=2, H=3, Dm=256, V=9001, k=16), dict(B=3, H=2, Dm=128, V=12288, k=64),
+         dict(B=2, H=2, Dm=128, V=40000, k=64)]
 
 
 @pytest.mark.parametrize("case", range(len(SMALL)))
@@ -85,6 +89,20 @@ def test_zero_resblock_reduces_to_lm_head():
     got = _heads(hi)
     ref = oracle.medusa_heads(hi["h"], hi["W_res"], hi["W_lm"], hi["k"])
     _compare_heads(got, ref)
+
+
+@pytest.mark.parametrize("V", [9001, 40000])
+def test_all_logits_tied(V):
+    """Identical rows of W_lm make every logit of a column equal: the top-k must be ids 0..k-1
+    (lower id first on ties) and every probability 1 / V.  Every logit is then a candidate, more
+    than the candidate list holds, so the top-k comes from the selection rounds."""
+    w = wl.custom(seed=4200, B=2, V=V, heads={"H": 2, "Dm": 128, "k": 12})
+    hi = dict(wl.heads_inputs(w))
+    hi["W_lm"] = np.repeat(hi["W_lm"][:1], V, axis=0)
+    got = _heads(hi)
+    assert (got["topk_idx"] == np.arange(12)).all()
+    np.testing.assert_allclose(got["topk_prob"], 1.0 / V, rtol=1e-5)
+    np.testing.assert_allclose(got["probs"], 1.0 / V, rtol=1e-5)
 
 
 def test_full_size_heads():
