@@ -20,12 +20,14 @@
 // key key0 + L / 4 and lane j receives dimension j of those 4 keys.  Every per-row quantity
 // (running max, sum, rescale) lives in the lanes of that row.  The reference max of the
 // exponentials moves only when a tile's max exceeds it by more than a slack of 2^8, so the O
-// rescale is rare (softmax does not depend on the reference).
+// rescale is rare (softmax does not depend on the reference); a tile whose weights all stay
+// below 2^8 against the current references needs no row max at all.
 //
-// Tiles are double-buffered: the next tile's global loads are issued into registers before
-// the current tile is computed and written to the other LDS buffer afterwards, so there is
-// one barrier per tile and the HBM latency hides behind the MFMA work.  Tiles that lie wholly
-// in the prefix and inside the split skip all masking.
+// Tiles are double-buffered: the next tile's global loads (buffer loads with 32-bit offsets
+// into the head's K and V) are issued into registers before the current tile is computed and
+// written to the other LDS buffer afterwards, so there is one barrier per tile and the HBM
+// latency hides behind the MFMA work.  Tiles that lie wholly in the prefix and inside the
+// split skip all masking; the others mask with one 64-bit visibility word per row.
 //
 // Work split: grid = units x row blocks x key splits.  A split covers a contiguous key range
 // of the unit (prefix and tree slots alike), computed on the device from prefix_len and
