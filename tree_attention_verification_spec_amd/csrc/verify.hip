@@ -1482,7 +1482,7 @@ __global__ __launch_bounds__(kWave) void select_wave_kernel(VerifyArgs a) {
   if (t == 0) a.bonus[b] = tok;
 }
 
-// One-wave draw when the weights are not kept (large batches) and at most 64 chunks: lane t
+// One-wave draw from the group sums (the default for rows of at most 64 chunks): lane t
 // holds chunk t's part; the chunk holding u * Z is found as in select_wave_kernel, then the
 // 64-token group inside it from the group sums the bonus pass left, then the token inside the
 // group, each lane recomputing one token's weight exactly as the bonus pass formed it.  Three
