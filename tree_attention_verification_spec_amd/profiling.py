@@ -133,9 +133,14 @@ def read_counter(path, counter):
     return {k: list(v.values()) for k, v in vals.items()}
 
 
+# How the commands in the summaries are run: from any directory, with REPO set to the
+# repository root (the package built in place) and TMPDIR=/tmp.
+RUN_NOTE = "`$REPO` is the repository root, with the library built in place; run with `TMPDIR=/tmp`."
+
+
 def write_stats_summary(stats_csv, out_md, command):
     st = read_kernel_stats(stats_csv)
-    lines = ["# rocprofv3 kernel statistics", "", "Command:", "", "```", command, "```", "",
+    lines = ["# rocprofv3 kernel statistics", "", "Command:", "", "```", command, "```", "", RUN_NOTE, "",
              "| kernel | calls | avg us | total us |", "|---|---|---|---|"]
     for name, (calls, avg, tot) in sorted(st.items(), key=lambda kv: -kv[1][2]):
         lines.append(f"| {name} | {calls} | {avg / 1e3:.2f} | {tot / 1e3:.1f} |")
@@ -184,7 +189,8 @@ def write_ea_summary(reads_csv, writes_csv, kernel, copy_bytes, alg_bytes, out_m
              f"algorithmic_bytes_per_launch: {alg_bytes:.0f}",
              f"traffic_over_algorithmic: {(r_b + w_b) / alg_bytes:.3f}" if alg_bytes else "traffic_over_algorithmic: -",
              f"copy_check: a {copy_bytes:.0f}-byte device copy read {copy_r:.0f} and wrote {copy_w:.0f} bytes",
-             f"traffic_bytes_per_launch: {r_b + w_b:.0f}", "", "Commands:", "", "```", commands, "```"]
+             f"traffic_bytes_per_launch: {r_b + w_b:.0f}", "", "Commands:", "", "```", commands, "```", "",
+             RUN_NOTE]
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -204,7 +210,8 @@ def write_mfma_summary(mfma_csv, kernel, alg_flops, out_md, command, simds=1024,
              f"mfma_busy_fraction: {frac:.3f}  (busy cycles per SIMD / (duration x {clock_ghz} GHz))",
              f"bf16_flops_executed: {flops:.4e}  (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)",
              f"algorithmic_flops: {alg_flops:.4e}",
-             f"executed_tflops: {flops / dur_ns / 1e3:.1f}", "", "Command:", "", "```", command, "```"]
+             f"executed_tflops: {flops / dur_ns / 1e3:.1f}", "", "Command:", "", "```", command, "```", "",
+             RUN_NOTE]
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
