@@ -275,6 +275,7 @@ def assemble_rows_timing(st, reps=50):
         sb.prof_enable(False)
         ms1, c1 = sb.prof_read("assemble_chunks")
         ms2, c2 = sb.prof_read("assemble_merge")
+        ms0, c0 = sb.prof_read("assemble_list")     # large grids list the nodes with children first
     finally:
         sb.prof_enable(False)
         sb.prof_reset()
@@ -282,8 +283,9 @@ def assemble_rows_timing(st, reps=50):
     internal = sum(int(torch.unique(parents[b, 1:]).numel()) for b in range(B))
     nbytes = internal * Vd * 4
     us1, us2 = ms1 / c1 * 1e3, ms2 / c2 * 1e3
-    return {"shape": f"B{B} x {internal // B}-ish nodes with children x Vd {Vd}", "chunks_us": round(us1, 3),
-            "merge_us": round(us2, 3), "algorithmic_bytes": nbytes,
+    us0 = ms0 / c0 * 1e3 if c0 else 0.0
+    return {"shape": f"B{B} x {internal // B}-ish nodes with children x Vd {Vd}", "list_us": round(us0, 3),
+            "chunks_us": round(us1, 3), "merge_us": round(us2, 3), "algorithmic_bytes": nbytes,
             "chunks_GBs": round(nbytes / (us1 * 1e-6) / 1e9, 1)}
 
 

@@ -71,6 +71,9 @@ CASES = [
     (1, 127, 40000, 6, 5, True, "five chunks, ties"),
     (2, 256, 20000, 8, None, False, "256 nodes"),
     (1, 100, 262144, 4, None, False, "the largest draft vocabulary"),
+    # grids of at least 8192 (node, chunk) items with B * N <= 4096: nodes listed first
+    (16, 128, 25000, 6, 4, True, "listed: 16 x 128 nodes, ties, mapped"),
+    (5, 256, 49153, 8, None, False, "listed: 256 nodes, seven chunks"),
 ]
 
 

@@ -8,7 +8,8 @@
 // of a row gets a unique 64-bit key, (order-preserving bits of the probability) << 32 |
 // (~id), so "better" is simply "larger key" and no two entries tie.
 //
-// Two kernels in stream order (the kernel boundary orders them; no workgroup waits on another):
+// Two kernels in stream order (the kernel boundary orders them; no workgroup waits on another;
+// large grids first list the nodes with children, see assemble_list_kernel):
 //   chunks  grid (j, sequence, chunk of 8192 draft ids), j slowest: workgroup (j, b, c) finds
 //           (from the parent array, one load per thread) the j-th node of sequence b that has
 //           children (k of them) and ranks chunk c of that node's draft row: 32 entries per
@@ -52,7 +53,19 @@ struct RowsArgs {
   int32_t* err;
   uint64_t* keys;            // [B, CA, N]: slot s of a chunk's list
   int32_t* nonfinite;        // [B, CA, N]: per (chunk, node with children)
+  int4* list;                // [B * N]: (b N + node, children, first slot, draft row) of each node
+                             // with children, in (sequence, node) order (listed path)
+  int32_t* list_count;       // [1]: entries of list
 };
+
+// The listed path: one workgroup first lists the nodes with children, then workgroup i of the
+// chunk pass takes the i-th listed (node, chunk) item, so that the workgroups with work come
+// first and start their chunk loads after one lookup.  Used for B * N <= kAListMax and grids of
+// at least kAListMinItems (node, chunk) items.
+constexpr int kAListMax = 4096;
+constexpr int kAListThreads = 1024;
+constexpr int kAListPer = kAListMax / kAListThreads;
+constexpr size_t kAListMinItems = 8192;
 
 // Order-preserving bits of a float (-0.0 folded into 0.0): larger float, larger bits; a NaN
 // gets 0, below every number.
@@ -70,58 +83,20 @@ __device__ __forceinline__ uint64_t make_key(uint32_t o, int id) {
   return ((uint64_t)o << 32) | (uint64_t)(0xffffffffu - (uint32_t)id);
 }
 
-__global__ __launch_bounds__(kAT) void assemble_chunks_kernel(RowsArgs a) {
+// Chunk c of the draft row r of node p of sequence b, which has k children whose keys go to slots
+// off .. off + k - 1 of the chunk's list: the chunk's best min(k, chunk length) keys, in order,
+// and its NaN flag.
+__device__ void rank_chunk(const RowsArgs& a, int b, int p, int k, int off, int r, int c) {
   constexpr int kWavesA = kAT / kWave;
   __shared__ uint32_t s_max[kAT];
   __shared__ uint64_t s_cand[kACand];
   __shared__ uint64_t s_wmax[kWavesA];
   __shared__ uint32_t s_wtau[kWavesA];
-  __shared__ int s_rows[SPEC_MAX_NODES];
-  __shared__ int s_has[SPEC_MAX_NODES];
-  __shared__ int s_wtot[kWavesA];
   __shared__ uint32_t s_tau;
-  __shared__ int s_count, s_first, s_p;
-  // workgroup -> (j-th node with children of sequence b, chunk c), j slowest: the workgroups
-  // with work are dispatched first, and the ones past a sequence's last such node leave early
-  const int c = blockIdx.x % a.CA;
-  const int rest = blockIdx.x / a.CA;
-  const int b = rest % a.B;
-  const int jn = rest / a.B;
+  __shared__ int s_count;
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
-  // first round of loads, all independent: n, this thread's parent entry and draft row
-  const int n = a.n_nodes ? a.n_nodes[b] : a.N;
-  const size_t ti = (size_t)b * a.N + min(t, a.N - 1);
-  const int par_t = a.parents[ti];
-  const int row_t = a.draft_row[ti];
-  if (n < 1 || n > a.N || jn >= n) return;
-  // valid node t (t < n, parent in [0, t)); nodes named by a valid node have children
-  const bool valid = t >= 1 && t < n && par_t >= 0 && par_t < t;
-  if (t < a.N) { s_rows[t] = row_t; s_has[t] = 0; }
-  if (t == 0) { s_first = INT_MAX; s_count = 0; s_p = -1; }
-  __syncthreads();
-  if (valid) s_has[par_t] = 1;
-  __syncthreads();
-  const bool has = t < n && s_has[t];
-  const uint64_t bal = __ballot(has);
-  if (lane == 0) s_wtot[w] = __popcll(bal);
-  __syncthreads();
-  int before = __popcll(bal & ((1ull << lane) - 1ull)), total = 0;
-#pragma unroll
-  for (int q = 0; q < kWavesA; ++q) {
-    before += q < w ? s_wtot[q] : 0;
-    total += s_wtot[q];
-  }
-  if (jn >= total) return;                        // past the last node with children
-  if (has && before == jn) s_p = t;
-  __syncthreads();
-  const int p = s_p;
-  const bool mine = valid && par_t == p;
-  if (mine) atomicMin(&s_first, t);
-  const int k = __syncthreads_count(mine);
-  const int off = __syncthreads_count(valid && par_t < p);
-  const int r = s_rows[s_first];
-  if (r < 0 || r >= a.R) return;                  // the merge reports it
+  if (t == 0) s_count = 0;                        // read after the barriers below
   const int lo = c * kAChunk;
   const int len = min(kAChunk, a.Vd - lo);
   const int kk = min(k, len);
@@ -237,6 +212,166 @@ __global__ __launch_bounds__(kAT) void assemble_chunks_kernel(RowsArgs a) {
     }
   }
   if (t == 0) a.nonfinite[((size_t)b * a.CA + c) * a.N + p] = nan;
+}
+
+__global__ __launch_bounds__(kAT) void assemble_chunks_kernel(RowsArgs a) {
+  constexpr int kWavesA = kAT / kWave;
+  __shared__ int s_rows[SPEC_MAX_NODES];
+  __shared__ int s_has[SPEC_MAX_NODES];
+  __shared__ int s_wtot[kWavesA];
+  __shared__ int s_first, s_p;
+  // workgroup -> (j-th node with children of sequence b, chunk c), j slowest: the workgroups
+  // with work are dispatched first, and the ones past a sequence's last such node leave early
+  const int c = blockIdx.x % a.CA;
+  const int rest = blockIdx.x / a.CA;
+  const int b = rest % a.B;
+  const int jn = rest / a.B;
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  // first round of loads, all independent: n, this thread's parent entry and draft row
+  const int n = a.n_nodes ? a.n_nodes[b] : a.N;
+  const size_t ti = (size_t)b * a.N + min(t, a.N - 1);
+  const int par_t = a.parents[ti];
+  const int row_t = a.draft_row[ti];
+  if (n < 1 || n > a.N || jn >= n) return;
+  // valid node t (t < n, parent in [0, t)); nodes named by a valid node have children
+  const bool valid = t >= 1 && t < n && par_t >= 0 && par_t < t;
+  if (t < a.N) { s_rows[t] = row_t; s_has[t] = 0; }
+  if (t == 0) { s_first = INT_MAX; s_p = -1; }
+  __syncthreads();
+  if (valid) s_has[par_t] = 1;
+  __syncthreads();
+  const bool has = t < n && s_has[t];
+  const uint64_t bal = __ballot(has);
+  if (lane == 0) s_wtot[w] = __popcll(bal);
+  __syncthreads();
+  int before = __popcll(bal & ((1ull << lane) - 1ull)), total = 0;
+#pragma unroll
+  for (int q = 0; q < kWavesA; ++q) {
+    before += q < w ? s_wtot[q] : 0;
+    total += s_wtot[q];
+  }
+  if (jn >= total) return;                        // past the last node with children
+  if (has && before == jn) s_p = t;
+  __syncthreads();
+  const int p = s_p;
+  const bool mine = valid && par_t == p;
+  if (mine) atomicMin(&s_first, t);
+  const int k = __syncthreads_count(mine);
+  const int off = __syncthreads_count(valid && par_t < p);
+  const int r = s_rows[s_first];
+  if (r < 0 || r >= a.R) return;                  // the merge reports it
+  rank_chunk(a, b, p, k, off, r, c);
+}
+
+// Exclusive prefix over the workgroup of two counts (thread order); the totals to every thread.
+__device__ __forceinline__ int2 list_scan(int x, int y, int2& total) {
+  constexpr int kW = kAListThreads / kWave;
+  __shared__ int2 s_w[kW];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int ix = x, iy = y;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int ux = __shfl_up(ix, o), uy = __shfl_up(iy, o);
+    if (lane >= o) { ix += ux; iy += uy; }
+  }
+  if (lane == kWave - 1) s_w[w] = make_int2(ix, iy);
+  __syncthreads();
+  int bx = 0, by = 0, tx = 0, ty = 0;
+#pragma unroll
+  for (int q = 0; q < kW; ++q) {
+    const int2 v = s_w[q];
+    if (q < w) { bx += v.x; by += v.y; }
+    tx += v.x; ty += v.y;
+  }
+  total = make_int2(tx, ty);
+  return make_int2(bx + ix - x, by + iy - y);
+}
+
+// Lists the nodes with children of every sequence, in (sequence, node) order: thread t owns the
+// contiguous (sequence, node) entries [t per, t per + per); their parent, draft row and n_nodes
+// loads are requested at once.  A node's entry: its children count k, its first slot (the
+// children of lower-index nodes of the sequence) and the draft row of its lowest-index child;
+// nodes whose row is out of range are left out (the merge reports them), as are sequences with
+// an invalid n_nodes (they have no valid children).
+__global__ __launch_bounds__(kAListThreads) void assemble_list_kernel(RowsArgs a) {
+  __shared__ int s_cnt[kAListMax];
+  __shared__ int s_first[kAListMax];
+  __shared__ int s_drow[kAListMax];
+  __shared__ int s_base[kAListMax];             // first slot of each entry's sequence
+  const int t = threadIdx.x;
+  const int total = a.B * a.N;
+  const int per = (total + kAListThreads - 1) / kAListThreads;   // <= kAListPer
+  const int i0 = t * per;
+  int par[kAListPer], nn[kAListPer], dr[kAListPer];
+#pragma unroll
+  for (int k = 0; k < kAListPer; ++k) {
+    const int i = min(i0 + k, total - 1);
+    par[k] = a.parents[i];
+    dr[k] = a.draft_row[i];
+    nn[k] = a.n_nodes ? a.n_nodes[i / a.N] : a.N;
+  }
+#pragma unroll
+  for (int k = 0; k < kAListPer; ++k)
+    if (k < per && i0 + k < total) { s_cnt[i0 + k] = 0; s_first[i0 + k] = INT_MAX; s_drow[i0 + k] = dr[k]; }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kAListPer; ++k) {
+    const int i = i0 + k;
+    if (k < per && i < total) {
+      const int b = i / a.N, c = i - b * a.N, n = nn[k], p = par[k];
+      if (n >= 1 && n <= a.N && c >= 1 && c < n && p >= 0 && p < c) {
+        atomicAdd(&s_cnt[b * a.N + p], 1);
+        atomicMin(&s_first[b * a.N + p], c);
+      }
+    }
+  }
+  __syncthreads();
+  int cnt[kAListPer], row[kAListPer];
+  int sc = 0, sl = 0;
+#pragma unroll
+  for (int k = 0; k < kAListPer; ++k) {
+    const int i = i0 + k;
+    const bool in = k < per && i < total;
+    cnt[k] = in ? s_cnt[i] : 0;
+    row[k] = cnt[k] > 0 ? s_drow[(i / a.N) * a.N + s_first[i]] : -1;
+    sc += cnt[k];
+    sl += (cnt[k] > 0 && row[k] >= 0 && row[k] < a.R) ? 1 : 0;
+  }
+  int2 all;
+  const int2 ex = list_scan(sc, sl, all);
+  // the first slot of each sequence: the running count at its node 0
+  int rc = ex.x;
+#pragma unroll
+  for (int k = 0; k < kAListPer; ++k) {
+    const int i = i0 + k;
+    if (k < per && i < total && i % a.N == 0) s_base[i / a.N] = rc;
+    rc += cnt[k];
+  }
+  __syncthreads();
+  rc = ex.x;
+  int at = ex.y;
+#pragma unroll
+  for (int k = 0; k < kAListPer; ++k) {
+    const int i = i0 + k;
+    if (k < per && i < total && cnt[k] > 0 && row[k] >= 0 && row[k] < a.R)
+      a.list[at++] = make_int4(i, cnt[k], rc - s_base[i / a.N], row[k]);
+    rc += cnt[k];
+  }
+  if (t == 0) *a.list_count = all.y;
+}
+
+// Workgroup it takes chunk it % CA of the (it / CA)-th listed node; the rest leave after one
+// look at the count.  The count and the entry are requested together (the entry's index is
+// clamped into the list).
+__global__ __launch_bounds__(kAT) void assemble_listed_kernel(RowsArgs a) {
+  const int it = blockIdx.x;
+  const int c = it % a.CA, i = it / a.CA;
+  const int count = *a.list_count;
+  const int4 e = a.list[min(i, a.B * a.N - 1)];
+  if (i >= count) return;
+  const int b = e.x / a.N;
+  rank_chunk(a, b, e.x - b * a.N, e.y, e.z, e.w, c);
 }
 
 // One workgroup per sequence: bookkeeping one thread per node, the chunk lists staged in LDS
@@ -415,7 +550,8 @@ spec_status check_rows_shape(int B, int N, int R, int Vd, int V) {
 extern "C" size_t spec_tree_assemble_rows_workspace(int B, int N, int Vd) {
   if (check_rows_shape(B, N, 1, Vd, 1) != SPEC_OK) return 0;
   const size_t CA = (size_t)(Vd + kAChunk - 1) / kAChunk;
-  return align_up((size_t)B * CA * N * sizeof(uint64_t), 256) + align_up((size_t)B * CA * N * sizeof(int32_t), 256);
+  return align_up((size_t)B * CA * N * sizeof(uint64_t), 256) + align_up((size_t)B * CA * N * sizeof(int32_t), 256) +
+         align_up((size_t)B * N * sizeof(int4), 256) + align_up(sizeof(int32_t), 256);
 }
 
 extern "C" spec_status spec_tree_assemble_rows(const float* draft_probs, const int32_t* parents,
@@ -437,9 +573,20 @@ extern "C" spec_status spec_tree_assemble_rows(const float* draft_probs, const i
   a.tokens = tokens; a.cand_prob = cand_prob; a.err = err;
   char* w = static_cast<char*>(workspace);
   a.keys = reinterpret_cast<uint64_t*>(w);
-  a.nonfinite = reinterpret_cast<int32_t*>(w + align_up((size_t)B * a.CA * N * sizeof(uint64_t), 256));
+  size_t off = align_up((size_t)B * a.CA * N * sizeof(uint64_t), 256);
+  a.nonfinite = reinterpret_cast<int32_t*>(w + off);
+  off += align_up((size_t)B * a.CA * N * sizeof(int32_t), 256);
+  a.list = reinterpret_cast<int4*>(w + off);
+  off += align_up((size_t)B * N * sizeof(int4), 256);
+  a.list_count = reinterpret_cast<int32_t*>(w + off);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  launch("assemble_chunks", assemble_chunks_kernel, dim3((unsigned)((size_t)B * N * a.CA)), dim3(kAT), s, a);
+  const dim3 grid((unsigned)((size_t)B * N * a.CA));
+  if ((size_t)B * N <= (size_t)kAListMax && (size_t)B * N * a.CA >= kAListMinItems) {
+    launch("assemble_list", assemble_list_kernel, dim3(1), dim3(kAListThreads), s, a);
+    launch("assemble_chunks", assemble_listed_kernel, grid, dim3(kAT), s, a);
+  } else {
+    launch("assemble_chunks", assemble_chunks_kernel, grid, dim3(kAT), s, a);
+  }
   launch("assemble_merge", assemble_merge_kernel, dim3(B), dim3(kMT), s, a);
   return launch_status();
 }
