@@ -845,8 +845,11 @@ __global__ __launch_bounds__(THREADS) void walk_chain_kernel(VerifyArgs a) {
   __shared__ double s_fp, s_z;
   __shared__ int s_ok;
   const int K = a.wk;
-  const int node = blockIdx.x / K, part = blockIdx.x - node * K;
-  const int b = node / a.N, p = node - b * a.N;
+  const int wg_node = blockIdx.x / K, part = blockIdx.x - wg_node * K;
+  // node-major over the batch (every sequence's node 0 first, then node 1, ...): low-index
+  // nodes, nearest the root, tend to have the most children and so the longest chains
+  const int p = wg_node / a.B, b = wg_node - p * a.B;
+  const size_t node = (size_t)b * a.N + p;       // (sequence, node) index of the counters and slots
   const int t = threadIdx.x, lane = t & (kWave - 1), wv = t >> 6;
   const int n = a.n_nodes ? a.n_nodes[b] : a.N;
   if (n < 1 || n > a.N || p >= n) return;
@@ -932,7 +935,7 @@ __global__ __launch_bounds__(THREADS) void walk_chain_kernel(VerifyArgs a) {
         if (lane == 0) {
           // the slot of this pass's parity: a workgroup may run one pass ahead of a sibling
           // still reading this pass's partials, never two
-          double* slot = a.wpart + (((size_t)node * K + part) * 2 + (j & 1)) * 2;
+          double* slot = a.wpart + ((node * K + part) * 2 + (j & 1)) * 2;
           // Everything exchanged here is an agent-scope atomic (performed coherently across the
           // XCDs' caches), so no cache write-back or invalidation is needed; the wait makes the
           // two stores complete before the arrival is counted.
@@ -954,7 +957,7 @@ __global__ __launch_bounds__(THREADS) void walk_chain_kernel(VerifyArgs a) {
         if (ok) {
           __atomic_signal_fence(__ATOMIC_SEQ_CST);
           if (lane < K) {
-            const double* o = a.wpart + (((size_t)node * K + lane) * 2 + (j & 1)) * 2;
+            const double* o = a.wpart + ((node * K + lane) * 2 + (j & 1)) * 2;
             sf = __hip_atomic_load(o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             sz = __hip_atomic_load(o + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
